@@ -1,0 +1,232 @@
+/*
+ * csa.h - C ABI of the MI355X (gfx950) Compressed Sparse Attention / Heavily Compressed
+ * Attention library (libcsa.so).
+ *
+ * The method is DeepSeek-V4's long-context attention as described in
+ * "DeepSeek V4 模型技术大全" (wineandchord.com book), chapter "Attention", sections
+ * "CSA 的完整路径", "HCA 的完整路径" and "注意力实现细节", and in
+ * "DeepSeek-V4 技术报告深度解读" (chang-wenbin.github.io), sections 2.1-2.3.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every call returns an int status: CSA_OK (0) or a negative CSA_ERR_* code.  On error
+ *    nothing has been enqueued and csa_last_error() (per calling thread) describes why.
+ *  - No call allocates device memory and no call synchronizes: work is enqueued on the HIP
+ *    stream passed as `stream` (a hipStream_t, NULL = the default stream) and the call returns.
+ *  - Every tensor argument is a caller-owned DEVICE pointer to contiguous row-major memory,
+ *    unless marked "host".  The library keeps no pointer after a call returns.
+ *  - Scratch memory comes from the caller's `workspace` (device, 256-byte aligned) of
+ *    `ws_bytes` bytes; csa_workspace_size() returns the bytes an operation needs.  Workspace
+ *    contents on entry are irrelevant and are clobbered.
+ *  - Element types: bf16 = uint16_t bit patterns, e4m3 = uint8_t OCP FP8 E4M3 ("fn": bias 7,
+ *    no infinities, max 448), fp32 = float, indices and positions = int32_t.
+ *  - Token positions are 0-based.  Token u's window row lives in row (u % win_slots) of the
+ *    window buffer; compressed entry i (covering tokens m*i .. m*i+m-1) lives in row i.
+ *  - Calls on the same stream are ordered; calls that share a cache or workspace must not
+ *    overlap on different streams.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_OK 0
+#define CSA_ERR_INVALID_ARG (-1) /* NULL pointer, bad shape or unsupported parameter */
+#define CSA_ERR_UNSUPPORTED (-2) /* valid request outside what the kernels implement */
+#define CSA_ERR_WORKSPACE (-3)   /* ws_bytes smaller than csa_workspace_size() */
+#define CSA_ERR_HIP (-4)         /* a HIP runtime call failed (message in csa_last_error) */
+
+#define CSA_MODE_CSA 0 /* overlapping m-token compressor + lightning indexer + top-k */
+#define CSA_MODE_HCA 1 /* non-overlapping m'-token compressor, dense over closed entries */
+
+/* Operation ids for csa_workspace_size(). */
+#define CSA_OP_COMPRESS 0
+#define CSA_OP_INDEX_TOPK 1
+#define CSA_OP_SPARSE_MQA 2
+#define CSA_OP_HCA_MQA 3
+#define CSA_OP_DECODE 4
+#define CSA_OP_PREFILL 5
+
+/* Layer configuration, passed by pointer (read during the call only).
+ * Supported set (CSA_ERR_INVALID_ARG otherwise):
+ *   head_dim in {64, 128, 192, ..., 512} (multiple of 64, <= 512);
+ *   rope_dim even, 2 <= rope_dim <= min(head_dim, 128);
+ *   1 <= n_heads <= 128;  n_win in 1..1024;
+ *   CSA: idx_dim in {32, 64, 128}, 1 <= idx_heads <= 64, 1 <= top_k <= 4096, m >= 1;
+ *   HCA: m >= 1;  hidden (compressor only) a positive multiple of 32. */
+typedef struct csa_config {
+  int32_t mode;       /* CSA_MODE_CSA or CSA_MODE_HCA */
+  int32_t m;          /* compression ratio: 4 in CSA layers, 128 (m') in HCA layers */
+  int32_t top_k;      /* k: compressed entries selected per query (CSA) */
+  int32_t n_win;      /* sliding-window length n_win (128) */
+  int32_t n_heads;    /* query heads n_h sharing the single K=V head */
+  int32_t head_dim;   /* entry / head width c = d_h */
+  int32_t rope_dim;   /* r: trailing dims that carry RoPE */
+  int32_t idx_heads;  /* indexer heads n_h^I (CSA) */
+  int32_t idx_dim;    /* indexer dim d_I (CSA) */
+  int32_t hidden;     /* hidden size D of the compressor input */
+  float softmax_scale; /* logit scale (1/sqrt(d_h)) */
+  float rms_eps;       /* RMSNorm epsilon (1e-6) */
+  const float* rope_inv_freq; /* device fp32 [rope_dim/2]: angle of pair i at position p is
+                                 p * rope_inv_freq[i] (base 160000 for compressed layers; any
+                                 table, e.g. YaRN-scaled, may be passed) */
+} csa_config_t;
+
+/* Caller-owned per-sequence attention state for B sequences (all device pointers).
+ *  entries   bf16 [B, n_max, head_dim]  compressed entries, RMS-normalised and rotated
+ *  idx_keys  e4m3 [B, n_max, idx_dim]   indexer keys K^IComp (CSA; NULL for HCA)
+ *  idx_scale fp32 [B, n_max]            per-entry scale of idx_keys (CSA; NULL for HCA)
+ *  window    bf16 [B, win_slots, head_dim]  uncompressed window KV, token u in row u%win_slots
+ *  tail      fp32 [B, tail_rows, tail_cols] compressor projections of the last tail_rows tokens
+ *            (row u % tail_rows); only used by the compressor (csa_tail_shape gives the shape)
+ *  n_entries int32 [B]                   closed entries per sequence (read; the compressor
+ *                                        updates it) */
+typedef struct csa_cache {
+  int32_t n_max;
+  int32_t win_slots;
+  uint16_t* entries;
+  uint8_t* idx_keys;
+  float* idx_scale;
+  uint16_t* window;
+  float* tail;
+  int32_t* n_entries;
+} csa_cache_t;
+
+/* Compressor parameters (device pointers).
+ *  w_cat  bf16 [n_cols, hidden], one row per projection output column (csa_weight_cols):
+ *         CSA: [W^a_KV c | W^b_KV c | W^a_Z c | W^b_Z c | W^a_I dI | W^b_I dI | W^a_IZ dI |
+ *               W^b_IZ dI | W_win c];   HCA: [W_KV c | W_Z c | W_win c]
+ *  bias_a fp32 [m, c]   B^a (CSA) or B (HCA), the compressor's position bias
+ *  bias_b fp32 [m, c]   B^b (CSA; NULL for HCA)
+ *  bias_ia, bias_ib fp32 [m, dI]  position biases of the indexer-key compressor (CSA)
+ *  gamma, gamma_win fp32 [c]      RMSNorm gains of compressed entries and of window KV */
+typedef struct csa_weights {
+  const uint16_t* w_cat;
+  const float* bias_a;
+  const float* bias_b;
+  const float* bias_ia;
+  const float* bias_ib;
+  const float* gamma;
+  const float* gamma_win;
+} csa_weights_t;
+
+/* Library version: major*10000 + minor*100 + patch. */
+int csa_version(void);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char* csa_last_error(void);
+
+/* Host-side shape helpers (no device work). */
+int csa_weight_cols(const csa_config_t* cfg, int32_t* n_cols /* host out */);
+int csa_tail_shape(const csa_config_t* cfg, int32_t* rows /* host out */,
+                   int32_t* cols /* host out */);
+
+/* Bytes of workspace operation `op` (CSA_OP_*) needs for B sequences, nq queries (or tokens)
+ * per sequence and caches of n_max entries.  *bytes is a host pointer. */
+int csa_workspace_size(const csa_config_t* cfg, int32_t op, int32_t B, int32_t nq,
+                       int32_t n_max, size_t* bytes);
+
+/* csa_compress - token-level compressor (CSA: overlapping 2m-token windows with streams
+ * C^a/C^b weighted by a per-channel softmax of Z^a+B^a / Z^b+B^b, plus the indexer keys
+ * K^IComp from the same operation; HCA: m'-token windows of C weighted by softmax(Z+B)).
+ * Book "DeepSeek V4 模型技术大全", chapter "Attention", section "CSA 的完整路径" (first three
+ * equations and the K^IComp sentence) and section "HCA 的完整路径" (first two equations);
+ * entries are RMS-normalised and carry partial RoPE at position m*i (section "注意力实现细节").
+ *
+ *  H     bf16 [B, T, hidden]: T new tokens of each sequence, sequence b's at positions
+ *        pos0[b] .. pos0[b]+T-1.
+ *  pos0  int32 [B] device: first new position per sequence; n_entries[b] must equal
+ *        floor(pos0[b]/m) and the tail ring must hold the previous call's last tokens.
+ *  Effects per sequence: every block i that closes inside the call (m(i+1)-1 within the new
+ *  tokens) is written to entries[b,i] (bf16, RMSNorm*gamma, RoPE at m*i) and, for CSA, to
+ *  idx_keys/idx_scale[b,i] (E4M3 with per-entry scale max|x|/448, no norm, no RoPE);
+ *  window rows of the new tokens (RMSNorm(h W_win)*gamma_win, RoPE at u); the tail ring;
+ *  n_entries[b] = floor((pos0[b]+T)/m).  Requires floor((pos0[b]+T)/m) <= n_max.
+ */
+int csa_compress(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,
+                 const int32_t* pos0, const csa_weights_t* w, const csa_cache_t* cache,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/* csa_index_topk - lightning-indexer scores I_{t,s} = sum_h w_{t,h} ReLU(q^I_{t,h} . K^I_s)
+ * over the closed entries s < min(n_entries[b], floor((t+1)/m)), then TopK_k.
+ * Book "DeepSeek V4 模型技术大全", chapter "Attention", section "CSA 的完整路径" (indexer
+ * score and TopK equations).
+ *
+ *  qi        e4m3 [B, nq, idx_heads, idx_dim]   indexer queries
+ *  qi_scale  fp32 [B, nq, idx_heads]            per-(token, head) scale of qi
+ *  wi        fp32 [B, nq, idx_heads]            head weights w^I
+ *  pos       int32 [B, nq]                      query positions t
+ *  idx_out   int32 [B, nq, top_k]  selected entry indices in ascending order; when fewer
+ *            than top_k entries are visible all of them are selected and the rest is -1.
+ *            Ties at the k-th score go to the lower index.
+ *  score_out fp32 [B, nq, top_k] or NULL: I_{t,s} of each selected index (-inf for -1 pads).
+ */
+int csa_index_topk(const csa_config_t* cfg, int32_t B, int32_t nq, const uint8_t* qi,
+                   const float* qi_scale, const float* wi, const csa_cache_t* cache,
+                   const int32_t* pos, int32_t* idx_out, float* score_out, void* workspace,
+                   size_t ws_bytes, void* stream);
+
+/* csa_sparse_mqa - shared-KV multi-query attention of each query over its selected entries
+ * plus its sliding window, with a per-head sink logit in the softmax denominator:
+ * p_j = exp(z_j) / (exp(a_h) + sum_u exp(z_u)), z_j = scale * RoPE(q_h, t) . e_j, o_h =
+ * sum_j p_j e_j, whose last rope_dim dims are rotated back by -t.
+ * Book "DeepSeek V4 模型技术大全", chapter "Attention": component table (shared K=V MQA,
+ * attention sink, window W_t = {t-n_win+1..t}), section "注意力实现细节" (partial RoPE with
+ * reverse rotation of the core-attention output).
+ *
+ *  q       bf16 [B, nq, n_heads, head_dim]  RMS-normalised queries, not rotated
+ *  idx     int32 [B, nq, top_k]             entry indices (any order; -1 entries skipped)
+ *  pos     int32 [B, nq]                    query positions t (window = max(0,t-n_win+1)..t;
+ *                                           those rows must be present in cache->window)
+ *  sink    fp32 [n_heads]                   sink logits a_h
+ *  out     bf16 [B, nq, n_heads, head_dim]
+ *  lse_out fp32 [B, nq, n_heads] or NULL:   log sum_j exp(z_j) without the sink
+ */
+int csa_sparse_mqa(const csa_config_t* cfg, int32_t B, int32_t nq, const uint16_t* q,
+                   const csa_cache_t* cache, const int32_t* idx, const int32_t* pos,
+                   const float* sink, uint16_t* out, float* lse_out, void* workspace,
+                   size_t ws_bytes, void* stream);
+
+/* hca_dense_mqa - as csa_sparse_mqa but over every closed entry j < min(n_entries[b],
+ * floor((t+1)/m')) (no indexer), plus the window and the sink.
+ * Book "DeepSeek V4 模型技术大全", chapter "Attention", section "HCA 的完整路径" (visible set
+ * J_t and K_attn(t) = entries[J_t] U window).  Arguments as csa_sparse_mqa without idx. */
+int hca_dense_mqa(const csa_config_t* cfg, int32_t B, int32_t nq, const uint16_t* q,
+                  const csa_cache_t* cache, const int32_t* pos, const float* sink, uint16_t* out,
+                  float* lse_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* csa_decode - one decode step for B sequences at positions pos[b]:
+ *  1. if h_new != NULL: csa_compress of the new token (T=1, pos0=pos) with weights w;
+ *  2. CSA mode: csa_index_topk (nq=1) then csa_sparse_mqa; HCA mode: hca_dense_mqa.
+ *  h_new bf16 [B, hidden] or NULL (then w may be NULL and the cache must already hold the
+ *  token's window row); q bf16 [B, n_heads, head_dim]; qi/qi_scale/wi as csa_index_topk
+ *  with nq=1 (ignored in HCA mode); out bf16 [B, n_heads, head_dim];
+ *  idx_out int32 [B, top_k] or NULL (CSA: the selected indices). */
+int csa_decode(const csa_config_t* cfg, int32_t B, const uint16_t* h_new,
+               const csa_weights_t* w, const csa_cache_t* cache, const int32_t* pos,
+               const uint16_t* q, const uint8_t* qi, const float* qi_scale, const float* wi,
+               const float* sink, uint16_t* out, int32_t* idx_out, void* workspace,
+               size_t ws_bytes, void* stream);
+
+/* csa_prefill - causal layer over the first T tokens of B sequences (positions 0..T-1):
+ * csa_compress (pos0 = 0; n_entries must be 0), then for every token t as a query the
+ * causal csa_index_topk and csa_sparse_mqa (HCA mode: hca_dense_mqa).
+ * Requires cache->win_slots >= T.  q bf16 [B, T, n_heads, head_dim]; qi/qi_scale/wi as
+ * csa_index_topk with nq=T; out bf16 [B, T, n_heads, head_dim]; idx_out int32
+ * [B, T, top_k] or NULL. */
+int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,
+                const csa_weights_t* w, const csa_cache_t* cache, const uint16_t* q,
+                const uint8_t* qi, const float* qi_scale, const float* wi, const float* sink,
+                uint16_t* out, int32_t* idx_out, void* workspace, size_t ws_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H_ */

@@ -1,0 +1,212 @@
+"""Python binding of libcsa.so, the MI355X CSA/HCA library.
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind the C ABI
+declared in include/csa.h.  Tensors are torch tensors on the GPU (torch provides device memory
+and streams); bf16 arguments may be torch.bfloat16 or int16/uint16 bit patterns, E4M3
+arguments torch.uint8 or torch.float8_e4m3fn.  Every call enqueues on the current torch stream
+(or the stream passed) and raises CsaError with the library's message on a non-zero status.
+There is no fallback: if libcsa.so is missing or fails to load, every call raises.
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+
+MODE_CSA, MODE_HCA = 0, 1
+OP_COMPRESS, OP_INDEX_TOPK, OP_SPARSE_MQA, OP_HCA_MQA, OP_DECODE, OP_PREFILL = range(6)
+
+
+class CsaError(RuntimeError):
+    pass
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("m", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_win", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+                ("idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("rms_eps", ctypes.c_float), ("rope_inv_freq", ctypes.c_void_p)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("n_max", ctypes.c_int32), ("win_slots", ctypes.c_int32),
+                ("entries", ctypes.c_void_p), ("idx_keys", ctypes.c_void_p),
+                ("idx_scale", ctypes.c_void_p), ("window", ctypes.c_void_p),
+                ("tail", ctypes.c_void_p), ("n_entries", ctypes.c_void_p)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("w_cat", ctypes.c_void_p), ("bias_a", ctypes.c_void_p),
+                ("bias_b", ctypes.c_void_p), ("bias_ia", ctypes.c_void_p),
+                ("bias_ib", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("gamma_win", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "csa_version": ([], ctypes.c_int),
+    "csa_last_error": ([], ctypes.c_char_p),
+    "csa_weight_cols": ([_P, _P], ctypes.c_int),
+    "csa_tail_shape": ([_P, _P, _P], ctypes.c_int),
+    "csa_workspace_size": ([_P, _I, _I, _I, _I, _P], ctypes.c_int),
+    "csa_compress": ([_P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "csa_index_topk": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "csa_sparse_mqa": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "hca_dense_mqa": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "csa_decode": ([_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+                   ctypes.c_int),
+    "csa_prefill": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+                    ctypes.c_int),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libcsa.so (raises CsaError if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CsaError("libcsa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def version():
+    return lib().csa_version()
+
+
+def last_error():
+    return lib().csa_last_error().decode()
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise CsaError("%s failed (%d): %s" % (what, rc, last_error()))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise CsaError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise CsaError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_config(mode, m, n_heads, head_dim, rope_dim, inv_freq, top_k=0, n_win=128,
+                idx_heads=0, idx_dim=0, hidden=0, softmax_scale=None, rms_eps=1e-6):
+    """A Config; keeps a reference to the device inv_freq tensor for the config's lifetime."""
+    cfg = Config(mode, m, top_k, n_win, n_heads, head_dim, rope_dim, idx_heads, idx_dim, hidden,
+                 float(softmax_scale if softmax_scale is not None else head_dim ** -0.5),
+                 float(rms_eps), _ptr(inv_freq).value)
+    cfg._keep = inv_freq
+    return cfg
+
+
+def make_cache(n_max, win_slots, entries, window, n_entries, idx_keys=None, idx_scale=None,
+               tail=None):
+    c = Cache(n_max, win_slots, _ptr(entries).value, _ptr(idx_keys) and _ptr(idx_keys).value,
+              _ptr(idx_scale) and _ptr(idx_scale).value, _ptr(window).value,
+              _ptr(tail) and _ptr(tail).value, _ptr(n_entries).value)
+    c._keep = (entries, window, n_entries, idx_keys, idx_scale, tail)
+    return c
+
+
+def make_weights(w_cat, bias_a, gamma, gamma_win, bias_b=None, bias_ia=None, bias_ib=None):
+    v = lambda t: _ptr(t) and _ptr(t).value
+    w = Weights(v(w_cat), v(bias_a), v(bias_b), v(bias_ia), v(bias_ib), v(gamma), v(gamma_win))
+    w._keep = (w_cat, bias_a, bias_b, bias_ia, bias_ib, gamma, gamma_win)
+    return w
+
+
+def weight_cols(cfg):
+    n = ctypes.c_int32()
+    _check(lib().csa_weight_cols(ctypes.byref(cfg), ctypes.byref(n)), "csa_weight_cols")
+    return n.value
+
+
+def tail_shape(cfg):
+    r, c = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().csa_tail_shape(ctypes.byref(cfg), ctypes.byref(r), ctypes.byref(c)),
+           "csa_tail_shape")
+    return r.value, c.value
+
+
+def workspace_size(cfg, op, B, nq, n_max):
+    b = ctypes.c_size_t()
+    _check(lib().csa_workspace_size(ctypes.byref(cfg), op, B, nq, n_max, ctypes.byref(b)),
+           "csa_workspace_size")
+    return b.value
+
+
+def _ws(ws):
+    return (_ptr(ws), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+
+
+def compress(cfg, H, pos0, weights, cache, ws, stream=None):
+    B, T = H.shape[0], H.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib().csa_compress(ctypes.byref(cfg), B, T, _ptr(H), _ptr(pos0),
+                              ctypes.byref(weights), ctypes.byref(cache), wp, wn,
+                              _stream(stream)), "csa_compress")
+
+
+def index_topk(cfg, qi, qi_scale, wi, cache, pos, idx_out, ws, score_out=None, stream=None):
+    B, nq = qi.shape[0], qi.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib().csa_index_topk(ctypes.byref(cfg), B, nq, _ptr(qi), _ptr(qi_scale), _ptr(wi),
+                                ctypes.byref(cache), _ptr(pos), _ptr(idx_out), _ptr(score_out),
+                                wp, wn, _stream(stream)), "csa_index_topk")
+
+
+def sparse_mqa(cfg, q, cache, idx, pos, sink, out, ws, lse_out=None, stream=None):
+    B, nq = q.shape[0], q.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib().csa_sparse_mqa(ctypes.byref(cfg), B, nq, _ptr(q), ctypes.byref(cache),
+                                _ptr(idx), _ptr(pos), _ptr(sink), _ptr(out), _ptr(lse_out),
+                                wp, wn, _stream(stream)), "csa_sparse_mqa")
+
+
+def hca_dense_mqa(cfg, q, cache, pos, sink, out, ws, lse_out=None, stream=None):
+    B, nq = q.shape[0], q.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib().hca_dense_mqa(ctypes.byref(cfg), B, nq, _ptr(q), ctypes.byref(cache),
+                               _ptr(pos), _ptr(sink), _ptr(out), _ptr(lse_out), wp, wn,
+                               _stream(stream)), "hca_dense_mqa")
+
+
+def decode(cfg, cache, pos, q, sink, out, ws, h_new=None, weights=None, qi=None, qi_scale=None,
+           wi=None, idx_out=None, stream=None):
+    B = q.shape[0]
+    wp, wn = _ws(ws)
+    _check(lib().csa_decode(ctypes.byref(cfg), B, _ptr(h_new),
+                            ctypes.byref(weights) if weights is not None else None,
+                            ctypes.byref(cache), _ptr(pos), _ptr(q), _ptr(qi), _ptr(qi_scale),
+                            _ptr(wi), _ptr(sink), _ptr(out), _ptr(idx_out), wp, wn,
+                            _stream(stream)), "csa_decode")
+
+
+def prefill(cfg, H, weights, cache, q, sink, out, ws, qi=None, qi_scale=None, wi=None,
+            idx_out=None, stream=None):
+    B, T = H.shape[0], H.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib().csa_prefill(ctypes.byref(cfg), B, T, _ptr(H), ctypes.byref(weights),
+                             ctypes.byref(cache), _ptr(q), _ptr(qi), _ptr(qi_scale), _ptr(wi),
+                             _ptr(sink), _ptr(out), _ptr(idx_out), wp, wn, _stream(stream)),
+           "csa_prefill")

@@ -1,0 +1,430 @@
+// C ABI of libcsa.so: argument validation, workspace layout and kernel sequencing.
+// The operations and their definitions are documented in include/csa.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/csa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(CSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+bool is_csa(const csa_config_t* c) { return c->mode == CSA_MODE_CSA; }
+
+int check_config(const csa_config_t* c, bool need_compressor) {
+  if (!c) return fail(CSA_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->mode != CSA_MODE_CSA && c->mode != CSA_MODE_HCA)
+    return fail(CSA_ERR_INVALID_ARG, "mode %d is neither CSA nor HCA", c->mode);
+  if (c->m < 1) return fail(CSA_ERR_INVALID_ARG, "m=%d < 1", c->m);
+  if (c->head_dim != 128 && c->head_dim != 256 && c->head_dim != 512)
+    return fail(CSA_ERR_INVALID_ARG, "head_dim=%d not in {128, 256, 512}", c->head_dim);
+  if (c->rope_dim < 2 || (c->rope_dim & 1) || c->rope_dim > c->head_dim || c->rope_dim > 128)
+    return fail(CSA_ERR_INVALID_ARG, "rope_dim=%d must be even, 2..min(head_dim,128)",
+                c->rope_dim);
+  if (c->n_heads < 1 || c->n_heads > 128)
+    return fail(CSA_ERR_INVALID_ARG, "n_heads=%d not in 1..128", c->n_heads);
+  if (c->n_win < 1 || c->n_win > 1024)
+    return fail(CSA_ERR_INVALID_ARG, "n_win=%d not in 1..1024", c->n_win);
+  if (!(c->softmax_scale > 0.f) || !std::isfinite(c->softmax_scale))
+    return fail(CSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (!(c->rms_eps >= 0.f)) return fail(CSA_ERR_INVALID_ARG, "rms_eps must be >= 0");
+  if (!c->rope_inv_freq) return fail(CSA_ERR_INVALID_ARG, "rope_inv_freq is NULL");
+  if (is_csa(c)) {
+    if (c->idx_dim != 32 && c->idx_dim != 64 && c->idx_dim != 128)
+      return fail(CSA_ERR_INVALID_ARG, "idx_dim=%d not in {32, 64, 128}", c->idx_dim);
+    if (c->idx_heads < 1 || c->idx_heads > 64)
+      return fail(CSA_ERR_INVALID_ARG, "idx_heads=%d not in 1..64", c->idx_heads);
+    if (c->top_k < 1 || c->top_k > csa::kMaxTopK)
+      return fail(CSA_ERR_INVALID_ARG, "top_k=%d not in 1..%d", c->top_k, csa::kMaxTopK);
+  }
+  if (need_compressor) {
+    if (c->hidden < 32 || (c->hidden % 32))
+      return fail(CSA_ERR_INVALID_ARG, "hidden=%d must be a positive multiple of 32", c->hidden);
+  }
+  return CSA_OK;
+}
+
+int weight_cols(const csa_config_t* c) {
+  return is_csa(c) ? 5 * c->head_dim + 4 * c->idx_dim : 3 * c->head_dim;
+}
+void tail_shape(const csa_config_t* c, int* rows, int* cols) {
+  if (is_csa(c)) {
+    *rows = 2 * c->m;
+    *cols = 4 * c->head_dim + 4 * c->idx_dim;
+  } else {
+    *rows = c->m;
+    *cols = 2 * c->head_dim;
+  }
+}
+
+int check_cache(const csa_config_t* c, const csa_cache_t* k, bool need_keys, bool need_tail) {
+  if (!k) return fail(CSA_ERR_INVALID_ARG, "cache is NULL");
+  if (k->n_max < 1) return fail(CSA_ERR_INVALID_ARG, "cache n_max=%d < 1", k->n_max);
+  if (k->win_slots < c->n_win)
+    return fail(CSA_ERR_INVALID_ARG, "cache win_slots=%d < n_win=%d", k->win_slots, c->n_win);
+  if (!k->entries || !k->window || !k->n_entries)
+    return fail(CSA_ERR_INVALID_ARG, "cache entries/window/n_entries is NULL");
+  if (need_keys && (!k->idx_keys || !k->idx_scale))
+    return fail(CSA_ERR_INVALID_ARG, "cache idx_keys/idx_scale is NULL");
+  if (need_tail && !k->tail) return fail(CSA_ERR_INVALID_ARG, "cache tail is NULL");
+  return CSA_OK;
+}
+
+int check_weights(const csa_config_t* c, const csa_weights_t* w) {
+  if (!w) return fail(CSA_ERR_INVALID_ARG, "weights are NULL");
+  if (!w->w_cat || !w->bias_a || !w->gamma || !w->gamma_win)
+    return fail(CSA_ERR_INVALID_ARG, "w_cat/bias_a/gamma/gamma_win is NULL");
+  if (is_csa(c) && (!w->bias_b || !w->bias_ia || !w->bias_ib))
+    return fail(CSA_ERR_INVALID_ARG, "CSA needs bias_b, bias_ia and bias_ib");
+  return CSA_OK;
+}
+
+// --- workspace layouts ----------------------------------------------------------------------
+bool index_multi(int rows) { return rows <= 1024; }
+
+size_t ws_compress(const csa_config_t* c, int B, int T) {
+  return csa::compress_workspace(B, T, weight_cols(c));
+}
+size_t ws_index(const csa_config_t* c, int rows, int n_max) {
+  return csa::index_topk_workspace(rows, n_max, c->top_k, index_multi(rows));
+}
+size_t ws_mqa(const csa_config_t* c, int rows, int max_list) {
+  const csa::MqaPlan p = csa::plan_mqa(rows, c->n_heads, c->head_dim, max_list);
+  return csa::mqa_workspace(p, rows, c->n_heads, c->head_dim);
+}
+int max_list_sparse(const csa_config_t* c) { return c->top_k + c->n_win; }
+int max_list_dense(const csa_config_t* c, int n_max) { return n_max + c->n_win; }
+
+size_t ws_attend(const csa_config_t* c, int rows, int n_max) {
+  return is_csa(c) ? ws_mqa(c, rows, max_list_sparse(c)) : ws_mqa(c, rows, max_list_dense(c, n_max));
+}
+
+// decode / prefill: [idx buffer (CSA)] + union(compress, index, attend)
+size_t ws_layer(const csa_config_t* c, int B, int T, int n_max, bool prefill, bool compress) {
+  const int rows = B * T;
+  size_t idx = is_csa(c) ? align256(static_cast<size_t>(rows) * c->top_k * 4) : 0;
+  size_t u = ws_attend(c, rows, n_max);
+  if (is_csa(c)) u = std::max(u, ws_index(c, rows, n_max));
+  if (compress) u = std::max(u, ws_compress(c, B, prefill ? T : 1));
+  return idx + u;
+}
+
+void fill_index_args(csa::IndexArgs& a, const csa_config_t* c, int B, int nq, const uint8_t* qi,
+                     const float* qi_scale, const float* wi, const csa_cache_t* k,
+                     const int32_t* pos, int32_t* idx_out, float* score_out, void* ws) {
+  a.qi = qi;
+  a.qi_scale = qi_scale;
+  a.wi = wi;
+  a.keys = k->idx_keys;
+  a.kscale = k->idx_scale;
+  a.n_entries = k->n_entries;
+  a.pos = pos;
+  a.B = B;
+  a.nq = nq;
+  a.n_max = k->n_max;
+  a.H_I = c->idx_heads;
+  a.d_I = c->idx_dim;
+  a.m = c->m;
+  a.k = c->top_k;
+  a.idx_out = idx_out;
+  a.score_out = score_out;
+  const int rows = B * nq;
+  a.sstride = (k->n_max + 63) & ~63;
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  a.scores = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(rows) * a.sstride * sizeof(float));
+  a.hist = reinterpret_cast<uint32_t*>(p);
+  p += align256(static_cast<size_t>(rows) * csa::kHistBins * 4);
+  a.counters = reinterpret_cast<uint32_t*>(p);
+  p += align256(static_cast<size_t>(rows) * 2 * 4);
+  a.sel = reinterpret_cast<int32_t*>(p);
+  p += align256(static_cast<size_t>(rows) * c->top_k * 4);
+  a.cand = reinterpret_cast<uint64_t*>(p);
+}
+
+void fill_mqa_args(csa::MqaArgs& a, const csa_config_t* c, int B, int nq, const uint16_t* q,
+                   const csa_cache_t* k, const int32_t* idx, const int32_t* pos,
+                   const float* sink, uint16_t* out, float* lse_out, void* ws) {
+  a.q = q;
+  a.entries = k->entries;
+  a.window = k->window;
+  a.idx = idx;
+  a.n_entries = k->n_entries;
+  a.pos = pos;
+  a.sink = sink;
+  a.inv_freq = c->rope_inv_freq;
+  a.B = B;
+  a.nq = nq;
+  a.n_heads = c->n_heads;
+  a.c = c->head_dim;
+  a.r = c->rope_dim;
+  a.k = c->top_k;
+  a.m = c->m;
+  a.n_win = c->n_win;
+  a.win_slots = k->win_slots;
+  a.n_max = k->n_max;
+  a.scale = c->softmax_scale;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.part = static_cast<float*>(ws);
+}
+
+int run_compress(const csa_config_t* c, int B, int T, const uint16_t* H, const int32_t* pos0,
+                 const csa_weights_t* w, const csa_cache_t* k, void* ws, hipStream_t s) {
+  csa::CompressArgs a;
+  a.mode = c->mode;
+  a.B = B;
+  a.T = T;
+  a.D = c->hidden;
+  a.c = c->head_dim;
+  a.d_I = is_csa(c) ? c->idx_dim : 0;
+  a.m = c->m;
+  a.r = c->rope_dim;
+  a.n_cols = weight_cols(c);
+  tail_shape(c, &a.tail_rows, &a.tail_cols);
+  a.win_slots = k->win_slots;
+  a.n_max = k->n_max;
+  a.H = H;
+  a.pos0 = pos0;
+  a.W = w->w_cat;
+  a.bias_a = w->bias_a;
+  a.bias_b = w->bias_b;
+  a.bias_ia = w->bias_ia;
+  a.bias_ib = w->bias_ib;
+  a.gamma = w->gamma;
+  a.gamma_win = w->gamma_win;
+  a.inv_freq = c->rope_inv_freq;
+  a.eps = c->rms_eps;
+  a.entries = k->entries;
+  a.ikeys = k->idx_keys;
+  a.iscale = k->idx_scale;
+  a.window = k->window;
+  a.tail = k->tail;
+  a.n_entries = k->n_entries;
+  a.proj = static_cast<float*>(ws);
+  hipError_t e = csa::launch_compress(a, s);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "compress launch");
+}
+
+int run_index(const csa_config_t* c, int B, int nq, const uint8_t* qi, const float* qi_scale,
+              const float* wi, const csa_cache_t* k, const int32_t* pos, int32_t* idx_out,
+              float* score_out, void* ws, hipStream_t s) {
+  csa::IndexArgs a;
+  fill_index_args(a, c, B, nq, qi, qi_scale, wi, k, pos, idx_out, score_out, ws);
+  hipError_t e = csa::launch_index_topk(a, index_multi(B * nq), s);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "index_topk launch");
+}
+
+int run_attend(const csa_config_t* c, int B, int nq, const uint16_t* q, const csa_cache_t* k,
+               const int32_t* idx, const int32_t* pos, const float* sink, uint16_t* out,
+               float* lse_out, void* ws, hipStream_t s) {
+  csa::MqaArgs a;
+  fill_mqa_args(a, c, B, nq, q, k, idx, pos, sink, out, lse_out, ws);
+  const int max_list = idx ? max_list_sparse(c) : max_list_dense(c, k->n_max);
+  const csa::MqaPlan p = csa::plan_mqa(B * nq, c->n_heads, c->head_dim, max_list);
+  hipError_t e = csa::launch_mqa(a, p, s);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+const char* csa_last_error(void) { return g_last_error.c_str(); }
+
+int csa_weight_cols(const csa_config_t* cfg, int32_t* n_cols) {
+  int rc = check_config(cfg, false);
+  if (rc) return rc;
+  if (!n_cols) return fail(CSA_ERR_INVALID_ARG, "n_cols is NULL");
+  *n_cols = weight_cols(cfg);
+  return CSA_OK;
+}
+
+int csa_tail_shape(const csa_config_t* cfg, int32_t* rows, int32_t* cols) {
+  int rc = check_config(cfg, false);
+  if (rc) return rc;
+  if (!rows || !cols) return fail(CSA_ERR_INVALID_ARG, "rows/cols is NULL");
+  int r, c;
+  tail_shape(cfg, &r, &c);
+  *rows = r;
+  *cols = c;
+  return CSA_OK;
+}
+
+int csa_workspace_size(const csa_config_t* cfg, int32_t op, int32_t B, int32_t nq, int32_t n_max,
+                       size_t* bytes) {
+  int rc = check_config(cfg, op == CSA_OP_COMPRESS || op == CSA_OP_PREFILL);
+  if (rc) return rc;
+  if (!bytes) return fail(CSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 1 || nq < 1 || n_max < 1) return fail(CSA_ERR_INVALID_ARG, "B, nq, n_max must be >= 1");
+  switch (op) {
+    case CSA_OP_COMPRESS: *bytes = ws_compress(cfg, B, nq); break;
+    case CSA_OP_INDEX_TOPK:
+      if (!is_csa(cfg)) return fail(CSA_ERR_INVALID_ARG, "index_topk needs CSA mode");
+      *bytes = ws_index(cfg, B * nq, n_max);
+      break;
+    case CSA_OP_SPARSE_MQA: *bytes = ws_mqa(cfg, B * nq, max_list_sparse(cfg)); break;
+    case CSA_OP_HCA_MQA: *bytes = ws_mqa(cfg, B * nq, max_list_dense(cfg, n_max)); break;
+    case CSA_OP_DECODE: *bytes = ws_layer(cfg, B, 1, n_max, false, true); break;
+    case CSA_OP_PREFILL: *bytes = ws_layer(cfg, B, nq, n_max, true, true); break;
+    default: return fail(CSA_ERR_INVALID_ARG, "unknown op %d", op);
+  }
+  return CSA_OK;
+}
+
+int csa_compress(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,
+                 const int32_t* pos0, const csa_weights_t* w, const csa_cache_t* cache,
+                 void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg, true);
+  if (rc) return rc;
+  if ((rc = check_cache(cfg, cache, is_csa(cfg), true))) return rc;
+  if ((rc = check_weights(cfg, w))) return rc;
+  if (B < 1 || T < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, T=%d must be >= 1", B, T);
+  if (!H || !pos0) return fail(CSA_ERR_INVALID_ARG, "H or pos0 is NULL");
+  const size_t need = ws_compress(cfg, B, T);
+  if (!workspace || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return run_compress(cfg, B, T, H, pos0, w, cache, workspace,
+                      reinterpret_cast<hipStream_t>(stream));
+}
+
+int csa_index_topk(const csa_config_t* cfg, int32_t B, int32_t nq, const uint8_t* qi,
+                   const float* qi_scale, const float* wi, const csa_cache_t* cache,
+                   const int32_t* pos, int32_t* idx_out, float* score_out, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg, false);
+  if (rc) return rc;
+  if (!is_csa(cfg)) return fail(CSA_ERR_INVALID_ARG, "csa_index_topk needs CSA mode");
+  if ((rc = check_cache(cfg, cache, true, false))) return rc;
+  if (B < 1 || nq < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, nq=%d must be >= 1", B, nq);
+  if (!qi || !qi_scale || !wi || !pos || !idx_out)
+    return fail(CSA_ERR_INVALID_ARG, "qi/qi_scale/wi/pos/idx_out is NULL");
+  const size_t need = ws_index(cfg, B * nq, cache->n_max);
+  if (!workspace || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return run_index(cfg, B, nq, qi, qi_scale, wi, cache, pos, idx_out, score_out, workspace,
+                   reinterpret_cast<hipStream_t>(stream));
+}
+
+int csa_sparse_mqa(const csa_config_t* cfg, int32_t B, int32_t nq, const uint16_t* q,
+                   const csa_cache_t* cache, const int32_t* idx, const int32_t* pos,
+                   const float* sink, uint16_t* out, float* lse_out, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg, false);
+  if (rc) return rc;
+  if ((rc = check_cache(cfg, cache, false, false))) return rc;
+  if (B < 1 || nq < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, nq=%d must be >= 1", B, nq);
+  if (!q || !idx || !pos || !sink || !out)
+    return fail(CSA_ERR_INVALID_ARG, "q/idx/pos/sink/out is NULL");
+  if (cfg->top_k < 1 || cfg->top_k > csa::kMaxTopK)
+    return fail(CSA_ERR_INVALID_ARG, "top_k=%d not in 1..%d", cfg->top_k, csa::kMaxTopK);
+  const size_t need = ws_mqa(cfg, B * nq, max_list_sparse(cfg));
+  if (need && (!workspace || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return run_attend(cfg, B, nq, q, cache, idx, pos, sink, out, lse_out, workspace,
+                    reinterpret_cast<hipStream_t>(stream));
+}
+
+int hca_dense_mqa(const csa_config_t* cfg, int32_t B, int32_t nq, const uint16_t* q,
+                  const csa_cache_t* cache, const int32_t* pos, const float* sink, uint16_t* out,
+                  float* lse_out, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg, false);
+  if (rc) return rc;
+  if ((rc = check_cache(cfg, cache, false, false))) return rc;
+  if (B < 1 || nq < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, nq=%d must be >= 1", B, nq);
+  if (!q || !pos || !sink || !out) return fail(CSA_ERR_INVALID_ARG, "q/pos/sink/out is NULL");
+  const size_t need = ws_mqa(cfg, B * nq, max_list_dense(cfg, cache->n_max));
+  if (need && (!workspace || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return run_attend(cfg, B, nq, q, cache, nullptr, pos, sink, out, lse_out, workspace,
+                    reinterpret_cast<hipStream_t>(stream));
+}
+
+int csa_decode(const csa_config_t* cfg, int32_t B, const uint16_t* h_new, const csa_weights_t* w,
+               const csa_cache_t* cache, const int32_t* pos, const uint16_t* q, const uint8_t* qi,
+               const float* qi_scale, const float* wi, const float* sink, uint16_t* out,
+               int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+  const bool comp = h_new != nullptr;
+  int rc = check_config(cfg, comp);
+  if (rc) return rc;
+  if ((rc = check_cache(cfg, cache, is_csa(cfg), comp))) return rc;
+  if (comp && (rc = check_weights(cfg, w))) return rc;
+  if (B < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (!pos || !q || !sink || !out) return fail(CSA_ERR_INVALID_ARG, "pos/q/sink/out is NULL");
+  if (is_csa(cfg) && (!qi || !qi_scale || !wi))
+    return fail(CSA_ERR_INVALID_ARG, "CSA decode needs qi, qi_scale and wi");
+  const size_t need = ws_layer(cfg, B, 1, cache->n_max, false, comp);
+  if (!workspace || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* p = static_cast<unsigned char*>(workspace);
+  int32_t* idx = nullptr;
+  if (is_csa(cfg)) {
+    idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p);
+    p += align256(static_cast<size_t>(B) * cfg->top_k * 4);
+  }
+  if (comp && (rc = run_compress(cfg, B, 1, h_new, pos, w, cache, p, s))) return rc;
+  if (is_csa(cfg)) {
+    if ((rc = run_index(cfg, B, 1, qi, qi_scale, wi, cache, pos, idx, nullptr, p, s))) return rc;
+    return run_attend(cfg, B, 1, q, cache, idx, pos, sink, out, nullptr, p, s);
+  }
+  return run_attend(cfg, B, 1, q, cache, nullptr, pos, sink, out, nullptr, p, s);
+}
+
+int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,
+                const csa_weights_t* w, const csa_cache_t* cache, const uint16_t* q,
+                const uint8_t* qi, const float* qi_scale, const float* wi, const float* sink,
+                uint16_t* out, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg, true);
+  if (rc) return rc;
+  if ((rc = check_cache(cfg, cache, is_csa(cfg), true))) return rc;
+  if ((rc = check_weights(cfg, w))) return rc;
+  if (B < 1 || T < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, T=%d must be >= 1", B, T);
+  if (!H || !q || !sink || !out) return fail(CSA_ERR_INVALID_ARG, "H/q/sink/out is NULL");
+  if (is_csa(cfg) && (!qi || !qi_scale || !wi))
+    return fail(CSA_ERR_INVALID_ARG, "CSA prefill needs qi, qi_scale and wi");
+  if (cache->win_slots < T)
+    return fail(CSA_ERR_INVALID_ARG, "prefill needs win_slots=%d >= T=%d", cache->win_slots, T);
+  if (T / cfg->m > cache->n_max)
+    return fail(CSA_ERR_INVALID_ARG, "T/m=%d entries exceed n_max=%d", T / cfg->m, cache->n_max);
+  const size_t need = ws_layer(cfg, B, T, cache->n_max, true, true);
+  if (!workspace || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* p = static_cast<unsigned char*>(workspace);
+  int32_t* idx = nullptr;
+  if (is_csa(cfg)) {
+    idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p);
+    p += align256(static_cast<size_t>(B) * T * cfg->top_k * 4);
+  }
+  if ((rc = run_compress(cfg, B, T, H, nullptr, w, cache, p, s))) return rc;
+  if (is_csa(cfg)) {
+    if ((rc = run_index(cfg, B, T, qi, qi_scale, wi, cache, nullptr, idx, nullptr, p, s)))
+      return rc;
+    return run_attend(cfg, B, T, q, cache, idx, nullptr, sink, out, nullptr, p, s);
+  }
+  return run_attend(cfg, B, T, q, cache, nullptr, nullptr, sink, out, nullptr, p, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Device helpers shared by the CSA/HCA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// bf16 <-> fp32.  fp32 -> bf16 rounds to nearest, ties to even (finite inputs).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Order-preserving map fp32 -> uint32 (larger float <=> larger key; -0 is folded to +0).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// RoPE angle p * inv_freq reduced to [-pi, pi] in fp64 before the fp32 sin/cos, so positions
+// up to 2^31 keep an absolute angle error far below the fp32 rounding of the result.
+__device__ __forceinline__ void rope_cos_sin(int pos, float inv_freq, float& c, float& s) {
+  const double two_pi = 6.283185307179586476925;
+  double a = static_cast<double>(pos) * static_cast<double>(inv_freq);
+  a -= two_pi * rint(a / two_pi);
+  sincosf(static_cast<float>(a), &s, &c);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int from_mask) {
+  // reduce over lanes that differ only in the bits of from_mask (16 and/or 32)
+  if (from_mask & 16) v = fmaxf(v, __shfl_xor(v, 16, 64));
+  if (from_mask & 32) v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_xor(float v, int from_mask) {
+  if (from_mask & 16) v += __shfl_xor(v, 16, 64);
+  if (from_mask & 32) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// MFMA wrappers.  16x16 outputs: lane l holds D[row = 4*(l/16) + i][col = l%16], i = 0..3.
+// A operand: lane l supplies row l%16 and a K slice chosen by l/16; B operand: column l%16 and
+// the same K slice.  Any fixed assignment of K values to (lane/16, element) works as long as
+// A and B use the same one, which every caller below does.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x32(long a, long b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+// 16x16x128 with both operands E4M3 (format code 0) and unit block scales (E8M0 127 = 2^0).
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+}  // namespace csa

@@ -1,0 +1,364 @@
+// Token-level compressor of CSA / HCA for gfx950.
+//
+// Method: "DeepSeek V4 模型技术大全", chapter "Attention".
+//  - section "CSA 的完整路径": C^a = H W^a_KV, C^b = H W^b_KV, Z^a = H W^a_Z, Z^b = H W^b_Z;
+//    block i's weights are a softmax over the 2m rows [Z^a_{mi..m(i+1)-1} + B^a;
+//    Z^b_{m(i-1)..mi-1} + B^b], taken per channel, and C^Comp_i = sum S^a (.) C^a + sum S^b (.) C^b.
+//    The indexer keys K^IComp come from the same operation with their own weights.
+//  - section "HCA 的完整路径": m'-row blocks, C^Comp_i = sum S (.) C with S = softmax(Z + B).
+//  - section "注意力实现细节": compressed entries are RMS-normalised and carry partial RoPE.
+// Block 0 of the overlapping compressor has no b-rows.  Entry i sits at position m*i; the
+// window KV of token u is RMSNorm(h_u W_win) * gamma_win with RoPE at u.  Indexer keys are not
+// normalised or rotated and are stored as E4M3 with one fp32 scale (max|x|/448) per entry.
+//
+// Pipeline: one bf16 MFMA GEMM computes every projection of the new tokens into an fp32
+// staging buffer (projections of tokens from earlier calls come from the per-sequence tail
+// ring); a pooling kernel per closed block; a window kernel per token; a tail-ring update.
+#include "common.h"
+#include "kernels.h"
+
+namespace csa {
+
+// ============================================================================ GEMM
+// Cst[M, N] (fp32) = A[M, K] (bf16, row-major) . Bw[N, K]^T (bf16, row-major), K % 32 == 0.
+// 128x128 tile per workgroup, 4 waves each owning 64x64 (4x4 MFMA 16x16x32 tiles).
+constexpr int GBM = 128, GBN = 128, GBK = 32, GLD = GBK + 8;
+
+__global__ __launch_bounds__(256) void gemm_tn_bf16_kernel(const uint16_t* __restrict__ A,
+                                                          const uint16_t* __restrict__ Bw,
+                                                          float* __restrict__ Cst, int M, int N,
+                                                          int K, int tiles_n) {
+  __shared__ __align__(16) uint16_t sa[2][GBM * GLD];
+  __shared__ __align__(16) uint16_t sb[2][GBN * GLD];
+  const int tid = threadIdx.x;
+  const int l = lane_id(), g = l >> 4, c16 = l & 15, wave = tid >> 6;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int m0 = tm * GBM, n0 = tn * GBN;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+
+  // each thread stages 2 x 16 bytes of A and of B per K step
+  u32x4 ra[2], rb[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = tid + i * 256;      // 512 chunks = 128 rows x 4 chunks of 8 bf16
+      const int rr = ch >> 2, cc = (ch & 3) * 8;
+      const int am = m0 + rr, bn = n0 + rr;
+      ra[i] = am < M ? *reinterpret_cast<const u32x4*>(A + static_cast<size_t>(am) * K + k0 + cc)
+                     : u32x4{0, 0, 0, 0};
+      rb[i] = bn < N ? *reinterpret_cast<const u32x4*>(Bw + static_cast<size_t>(bn) * K + k0 + cc)
+                     : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = tid + i * 256;
+      const int rr = ch >> 2, cc = (ch & 3) * 8;
+      *reinterpret_cast<u32x4*>(&sa[buf][rr * GLD + cc]) = ra[i];
+      *reinterpret_cast<u32x4*>(&sb[buf][rr * GLD + cc]) = rb[i];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / GBK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * GBK);
+    bf16x8 af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sa[buf][(wm + i * 16 + c16) * GLD + g * 8]));
+      bfr[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sb[buf][(wn + i * 16 + c16) * GLD + g * 8]));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16_16x16x32(af[i], bfr[j], acc[i][j]);
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + j * 16 + c16;
+      if (n >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm + i * 16 + g * 4 + e;
+        if (m < M) Cst[static_cast<size_t>(m) * N + n] = acc[i][j][e];
+      }
+    }
+}
+
+// ============================================================================ helpers
+// E4M3 ("fn") encoding with round-to-nearest-even and saturation to +-448, from the format's
+// bit fields (bias 7, 3 mantissa bits, subnormal quantum 2^-9).
+__device__ __forceinline__ uint8_t e4m3_rne(float x) {
+  const uint8_t sign = (__float_as_uint(x) >> 24) & 0x80;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (!(a < 448.f)) {
+    code = 0x7e;
+  } else if (a < 0.015625f) {  // below 2^-6: subnormal quantum 2^-9
+    code = static_cast<uint32_t>(rintf(a * 512.f));  // 8 -> 0x08 = 2^-6, still correct
+  } else {
+    int ex;
+    const float f = frexpf(a, &ex);  // a = f * 2^ex, f in [0.5, 1)
+    uint32_t mant = static_cast<uint32_t>(rintf((f * 2.f - 1.f) * 8.f));
+    uint32_t field = static_cast<uint32_t>(ex + 6);
+    if (mant == 8) {
+      mant = 0;
+      ++field;
+    }
+    code = (field << 3) | mant;
+    if (code > 0x7e) code = 0x7e;
+  }
+  return static_cast<uint8_t>(code | sign);
+}
+
+__device__ float block_sum(float v, float* s_red) {
+  const int tid = threadIdx.x;
+  v = wave_sum_xor(v, 48);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((tid & 63) == 0) s_red[tid >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) t += s_red[w];
+  __syncthreads();
+  return t;
+}
+__device__ float block_max(float v, float* s_red) {
+  const int tid = threadIdx.x;
+  v = wave_max_xor(v, 48);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  if ((tid & 63) == 0) s_red[tid >> 6] = v;
+  __syncthreads();
+  float t = -INFINITY;
+  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) t = fmaxf(t, s_red[w]);
+  __syncthreads();
+  return t;
+}
+
+struct PoolParams {
+  int mode, B, T, c, d_I, m, r, n_cols, tail_rows, tail_cols, n_max, nblk;
+  const int32_t* pos0;
+  const float* proj;
+  const float* tail;
+  const float *bias_a, *bias_b, *bias_ia, *bias_ib, *gamma;
+  const float* inv_freq;
+  float eps;
+  uint16_t* entries;
+  uint8_t* ikeys;
+  float* iscale;
+};
+
+__device__ __forceinline__ const float* proj_row(const PoolParams& p, int b, int p0, int u) {
+  if (u >= p0) return p.proj + (static_cast<size_t>(b) * p.T + (u - p0)) * p.n_cols;
+  return p.tail + (static_cast<size_t>(b) * p.tail_rows + (u % p.tail_rows)) * p.tail_cols;
+}
+
+// Softmax-weighted pooling of one channel over the block's rows.  a-rows: tokens ma..ma+m-1
+// using value column cv_a, logit column cz_a and bias ba; b-rows (if has_b): tokens mb..mb+m-1.
+__device__ float pool_channel(const PoolParams& p, int b, int p0, int ma, int mb, bool has_b,
+                              int cv_a, int cz_a, const float* ba, int cv_b, int cz_b,
+                              const float* bb, int width, int ch) {
+  float mx = -INFINITY;
+  for (int r = 0; r < p.m; ++r) mx = fmaxf(mx, proj_row(p, b, p0, ma + r)[cz_a + ch] + ba[r * width + ch]);
+  if (has_b)
+    for (int r = 0; r < p.m; ++r)
+      mx = fmaxf(mx, proj_row(p, b, p0, mb + r)[cz_b + ch] + bb[r * width + ch]);
+  float den = 0.f, num = 0.f;
+  for (int r = 0; r < p.m; ++r) {
+    const float* rowp = proj_row(p, b, p0, ma + r);
+    const float w = expf(rowp[cz_a + ch] + ba[r * width + ch] - mx);
+    den += w;
+    num += w * rowp[cv_a + ch];
+  }
+  if (has_b)
+    for (int r = 0; r < p.m; ++r) {
+      const float* rowp = proj_row(p, b, p0, mb + r);
+      const float w = expf(rowp[cz_b + ch] + bb[r * width + ch] - mx);
+      den += w;
+      num += w * rowp[cv_b + ch];
+    }
+  return num / den;
+}
+
+__global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
+  __shared__ float s_val[512];
+  __shared__ float s_red[8];
+  const int b = blockIdx.x / p.nblk;
+  const int p0 = p.pos0 ? p.pos0[b] : 0;
+  const int i = p0 / p.m + blockIdx.x % p.nblk;
+  if (i > (p0 + p.T) / p.m - 1) return;  // block does not close in this call
+  if (i >= p.n_max) return;               // never write past the cache
+  const int tid = threadIdx.x;
+  const int c = p.c;
+  const bool csa = p.mode == 0;
+  const int ma = p.m * i, mb = p.m * (i - 1);
+  const bool has_b = csa && i >= 1;
+  float ss = 0.f;
+  for (int ch = tid; ch < c; ch += 256) {
+    float v;
+    if (csa)
+      v = pool_channel(p, b, p0, ma, mb, has_b, 0, 2 * c, p.bias_a, c, 3 * c, p.bias_b, c, ch);
+    else
+      v = pool_channel(p, b, p0, ma, mb, false, 0, c, p.bias_a, 0, 0, nullptr, c, ch);
+    s_val[ch] = v;
+    ss += v * v;
+  }
+  const float tot = block_sum(ss, s_red);  // includes the barrier that publishes s_val
+  const float inv_rms = rsqrtf(tot / c + p.eps);
+  uint16_t* dst = p.entries + (static_cast<size_t>(b) * p.n_max + i) * c;
+  const int pos = p.m * i;
+  for (int pp = tid; pp < c / 2; pp += 256) {
+    const int d = 2 * pp;
+    float x0 = s_val[d] * inv_rms * p.gamma[d];
+    float x1 = s_val[d + 1] * inv_rms * p.gamma[d + 1];
+    if (d >= c - p.r) {
+      float cs, sn;
+      rope_cos_sin(pos, p.inv_freq[(d - (c - p.r)) >> 1], cs, sn);
+      const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+      x0 = y0;
+      x1 = y1;
+    }
+    *reinterpret_cast<uint32_t*>(dst + d) = pack_bf16x2(x0, x1);
+  }
+  if (!csa) return;
+  // indexer keys: same pooling on their own streams, then per-entry E4M3 quantisation
+  const int dI = p.d_I;
+  const int base = 4 * c;
+  float amax = 0.f;
+  __syncthreads();
+  for (int ch = tid; ch < dI; ch += 256) {
+    const float v = pool_channel(p, b, p0, ma, mb, has_b, base, base + 2 * dI, p.bias_ia,
+                                 base + dI, base + 3 * dI, p.bias_ib, dI, ch);
+    s_val[ch] = v;
+    amax = fmaxf(amax, fabsf(v));
+  }
+  amax = block_max(amax, s_red);
+  const float scale = amax > 0.f ? amax / 448.f : 1.f;
+  uint8_t* kd = p.ikeys + (static_cast<size_t>(b) * p.n_max + i) * dI;
+  for (int ch = tid; ch < dI; ch += 256) kd[ch] = e4m3_rne(s_val[ch] / scale);
+  if (tid == 0) p.iscale[static_cast<size_t>(b) * p.n_max + i] = scale;
+}
+
+// Window KV of every new token: RMSNorm(h_u W_win) * gamma_win, RoPE at u.
+__global__ __launch_bounds__(256) void window_kernel(const float* __restrict__ proj, int T,
+                                                     int n_cols, int c, int r, const int32_t* pos0,
+                                                     const float* __restrict__ gamma_win,
+                                                     const float* __restrict__ inv_freq, float eps,
+                                                     uint16_t* __restrict__ window,
+                                                     int win_slots) {
+  __shared__ float s_red[8];
+  const int bt = blockIdx.x;
+  const int b = bt / T, tt = bt % T;
+  const int u = (pos0 ? pos0[b] : 0) + tt;
+  const float* src = proj + static_cast<size_t>(bt) * n_cols + (n_cols - c);
+  const int tid = threadIdx.x;
+  float x[4];  // c <= 512: two pairs per thread at most
+  float ss = 0.f;
+  int np = 0;
+  for (int pp = tid; pp < c / 2; pp += 256, ++np) {
+    x[2 * np] = src[2 * pp];
+    x[2 * np + 1] = src[2 * pp + 1];
+    ss += x[2 * np] * x[2 * np] + x[2 * np + 1] * x[2 * np + 1];
+  }
+  const float inv_rms = rsqrtf(block_sum(ss, s_red) / c + eps);
+  uint16_t* dst = window + (static_cast<size_t>(b) * win_slots + (u % win_slots)) * c;
+  np = 0;
+  for (int pp = tid; pp < c / 2; pp += 256, ++np) {
+    const int d = 2 * pp;
+    float x0 = x[2 * np] * inv_rms * gamma_win[d];
+    float x1 = x[2 * np + 1] * inv_rms * gamma_win[d + 1];
+    if (d >= c - r) {
+      float cs, sn;
+      rope_cos_sin(u, inv_freq[(d - (c - r)) >> 1], cs, sn);
+      const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+      x0 = y0;
+      x1 = y1;
+    }
+    *reinterpret_cast<uint32_t*>(dst + d) = pack_bf16x2(x0, x1);
+  }
+}
+
+// Copy the projections of the last tail_rows new tokens into the tail ring; update n_entries.
+__global__ __launch_bounds__(256) void tail_kernel(const float* __restrict__ proj, int T, int n_cols,
+                                                   int tail_rows, int tail_cols, int m,
+                                                   const int32_t* pos0, float* __restrict__ tail,
+                                                   int32_t* __restrict__ n_entries, int nrows) {
+  const int b = blockIdx.x / nrows;
+  const int j = blockIdx.x % nrows;
+  const int p0 = pos0 ? pos0[b] : 0;
+  const int tt = T - nrows + j;  // new-token index
+  const int u = p0 + tt;
+  const float* src = proj + (static_cast<size_t>(b) * T + tt) * n_cols;
+  float* dst = tail + (static_cast<size_t>(b) * tail_rows + (u % tail_rows)) * tail_cols;
+  for (int cc = threadIdx.x; cc < tail_cols; cc += 256) dst[cc] = src[cc];
+  if (j == 0 && threadIdx.x == 0) n_entries[b] = (p0 + T) / m;
+}
+
+// ============================================================================ launch
+size_t compress_workspace(int B, int T, int n_cols) {
+  return (static_cast<size_t>(B) * T * n_cols * sizeof(float) + 255) & ~static_cast<size_t>(255);
+}
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
+  const int M = a.B * a.T;
+  const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (a.n_cols + GBN - 1) / GBN;
+  gemm_tn_bf16_kernel<<<tiles_m * tiles_n, 256, 0, s>>>(a.H, a.W, a.proj, M, a.n_cols, a.D,
+                                                        tiles_n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PoolParams p;
+  p.mode = a.mode;
+  p.B = a.B;
+  p.T = a.T;
+  p.c = a.c;
+  p.d_I = a.d_I;
+  p.m = a.m;
+  p.r = a.r;
+  p.n_cols = a.n_cols;
+  p.tail_rows = a.tail_rows;
+  p.tail_cols = a.tail_cols;
+  p.n_max = a.n_max;
+  p.nblk = a.T / a.m + 1;
+  p.pos0 = a.pos0;
+  p.proj = a.proj;
+  p.tail = a.tail;
+  p.bias_a = a.bias_a;
+  p.bias_b = a.bias_b;
+  p.bias_ia = a.bias_ia;
+  p.bias_ib = a.bias_ib;
+  p.gamma = a.gamma;
+  p.inv_freq = a.inv_freq;
+  p.eps = a.eps;
+  p.entries = a.entries;
+  p.ikeys = a.ikeys;
+  p.iscale = a.iscale;
+  pool_kernel<<<a.B * p.nblk, 256, 0, s>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  window_kernel<<<M, 256, 0, s>>>(a.proj, a.T, a.n_cols, a.c, a.r, a.pos0, a.gamma_win,
+                                  a.inv_freq, a.eps, a.window, a.win_slots);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nrows = a.T < a.tail_rows ? a.T : a.tail_rows;
+  tail_kernel<<<a.B * nrows, 256, 0, s>>>(a.proj, a.T, a.n_cols, a.tail_rows, a.tail_cols, a.m,
+                                          a.pos0, a.tail, a.n_entries, nrows);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,89 @@
+// Internal launcher interface between the C ABI layer (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+constexpr int kHistBins = 4096;     // first-level top-k histogram: top 12 bits of the key
+constexpr int kCandCap = 4096;      // candidates kept for the exact refinement of one row
+constexpr int kMaxTopK = 4096;
+constexpr int kRowTopkMaxN = 16384; // visible entries a single-workgroup row select holds in LDS
+
+// ---------------------------------------------------------------- indexer + top-k
+struct IndexArgs {
+  const uint8_t* qi;      // [rows, H_I, d_I]
+  const float* qi_scale;  // [rows, H_I]
+  const float* wi;        // [rows, H_I]
+  const uint8_t* keys;    // [B, n_max, d_I]
+  const float* kscale;    // [B, n_max]
+  const int32_t* n_entries;  // [B]
+  const int32_t* pos;     // [rows] or nullptr (t = query index within its sequence)
+  int B, nq, n_max, H_I, d_I, m, k;
+  float* scores;          // workspace [rows, sstride]
+  int sstride;
+  uint32_t* hist;         // workspace [rows, kHistBins]
+  uint32_t* counters;     // workspace [rows, 2]
+  int32_t* sel;           // workspace [rows, k]
+  uint64_t* cand;         // workspace [rows, kCandCap]
+  int32_t* idx_out;       // [rows, k]
+  float* score_out;       // [rows, k] or nullptr
+};
+size_t index_topk_workspace(int rows, int n_max, int k, bool multi);
+hipError_t launch_index_topk(const IndexArgs& a, bool multi, hipStream_t s);
+// Causal prefill indexer: queries are tokens 0..nq-1 of each sequence.
+hipError_t launch_index_prefill(const IndexArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct MqaArgs {
+  const uint16_t* q;        // [rows, n_heads, c]
+  const uint16_t* entries;  // [B, n_max, c]
+  const uint16_t* window;   // [B, win_slots, c]
+  const int32_t* idx;       // [rows, k] (sparse) or nullptr (dense: all visible entries)
+  const int32_t* n_entries; // [B]
+  const int32_t* pos;       // [rows] or nullptr
+  const float* sink;        // [n_heads]
+  const float* inv_freq;    // [r/2]
+  int B, nq, n_heads, c, r, k, m, n_win, win_slots, n_max;
+  float scale;
+  uint16_t* out;            // [rows, n_heads, c]
+  float* lse_out;           // [rows, n_heads] or nullptr
+  float* part;              // workspace partials
+};
+struct MqaPlan {
+  int heads_per_wg;   // 16 * waves
+  int head_groups;
+  int split_rows;     // rows of the key list per workgroup (multiple of 32)
+  int n_splits;
+};
+MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list);
+size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c);
+hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& p, hipStream_t s);
+
+// ---------------------------------------------------------------- compressor
+struct CompressArgs {
+  int mode;                 // 0 CSA, 1 HCA
+  int B, T, D, c, d_I, m, r, n_cols, tail_rows, tail_cols, win_slots, n_max;
+  const uint16_t* H;        // [B, T, D]
+  const int32_t* pos0;      // [B] or nullptr (all 0)
+  const uint16_t* W;        // [n_cols, D]
+  const float *bias_a, *bias_b, *bias_ia, *bias_ib, *gamma, *gamma_win;
+  const float* inv_freq;
+  float eps;
+  uint16_t* entries;
+  uint8_t* ikeys;
+  float* iscale;
+  uint16_t* window;
+  float* tail;
+  int32_t* n_entries;
+  float* proj;              // workspace [B*T, n_cols]
+};
+size_t compress_workspace(int B, int T, int n_cols);
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- misc
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
+
+}  // namespace csa

@@ -1,0 +1,150 @@
+"""GPU parity of the whole layer on the tiny workloads: csa_prefill (compressor, causal indexer,
+per-query top-k, sparse MQA + window + sink) followed by csa_decode steps that append tokens
+through the compressor tail, for CSA (m=4) and HCA (m'=128).  Stage-wise comparison with the
+oracle: compressor outputs against the oracle's, the selection against the oracle's scores on
+the GPU's stored keys, attention against the oracle on the GPU's stored rows."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_15_amd as csa
+import oracle as O
+from synth import inputs as S
+from gpu_common import (DEV, bf16_f64, check_close, check_selection, config_for, dev, host_bits,
+                        say, workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+def _e4m3_steps(a, b):
+    """Distance in representable steps between two E4M3 code arrays of the same sign."""
+    a = a.astype(np.int32)
+    b = b.astype(np.int32)
+    mag = lambda c: np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+    return np.abs(mag(a) - mag(b))
+
+
+def _build(w, x, T_total):
+    d = {k: dev(x[k]) for k in x if isinstance(x[k], np.ndarray)}
+    cfg = config_for(w, d["inv_freq"])
+    n_max = T_total // w.m + 1
+    win_slots = 1 << (T_total - 1).bit_length()
+    tr, tc = csa.tail_shape(cfg)
+    B = w.B
+    cache_t = dict(
+        entries=torch.zeros((B, n_max, w.c), dtype=torch.int16, device=DEV),
+        window=torch.zeros((B, win_slots, w.c), dtype=torch.int16, device=DEV),
+        n_entries=torch.zeros(B, dtype=torch.int32, device=DEV),
+        tail=torch.zeros((B, tr, tc), dtype=torch.float32, device=DEV))
+    if w.mode == "csa":
+        cache_t["idx_keys"] = torch.zeros((B, n_max, w.d_I), dtype=torch.uint8, device=DEV)
+        cache_t["idx_scale"] = torch.zeros((B, n_max), dtype=torch.float32, device=DEV)
+        weights = csa.make_weights(d["W"], d["Ba"], d["gamma"], d["gamma_win"], bias_b=d["Bb"],
+                                   bias_ia=d["BIa"], bias_ib=d["BIb"])
+    else:
+        weights = csa.make_weights(d["W"], d["B"], d["gamma"], d["gamma_win"])
+    cache = csa.make_cache(n_max, win_slots, **cache_t)
+    return cfg, cache, cache_t, weights, d, n_max, win_slots
+
+
+@pytest.mark.parametrize("name,T", [("tiny_csa", 2048), ("tiny_csa", 2046), ("tiny_hca", 2040)])
+def test_layer_prefill_then_decode(name, T):
+    say("layer", name, "prefill", T)
+    w = S.WORKLOADS[name]
+    x = S.layer_inputs(w, T=T)
+    TT = x["T_total"]
+    cfg, cache, ct, weights, d, n_max, slots = _build(w, x, TT)
+    csa_mode = w.mode == "csa"
+    ws = workspace(max(csa.workspace_size(cfg, csa.OP_PREFILL, 1, T, n_max),
+                       csa.workspace_size(cfg, csa.OP_DECODE, 1, 1, n_max)))
+    out = torch.empty((1, TT, w.n_h, w.c), dtype=torch.bfloat16, device=DEV)
+    idx = torch.full((1, TT, max(w.k, 1)), -7, dtype=torch.int32, device=DEV)
+    H, q = d["H"], d["q"]
+    kw = {}
+    if csa_mode:
+        kw = dict(qi=d["qi"][:, :T].contiguous(), qi_scale=d["qi_scale"][:, :T].contiguous(),
+                  wi=d["wi"][:, :T].contiguous(), idx_out=idx[:, :T])
+    csa.prefill(cfg, H[:, :T].contiguous(), weights, cache, q[:, :T].contiguous(), d["sink"],
+                out[:, :T], ws, **kw)
+    torch.cuda.synchronize()
+    assert int(ct["n_entries"][0]) == T // w.m
+    say("layer", name, "decode", TT - T, "steps")
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for t in range(T, TT):
+        pos.fill_(t)
+        dk = {}
+        if csa_mode:
+            dk = dict(qi=d["qi"][:, t].contiguous(), qi_scale=d["qi_scale"][:, t].contiguous(),
+                      wi=d["wi"][:, t].contiguous(), idx_out=idx[:, t])
+        csa.decode(cfg, cache, pos, q[:, t].contiguous(), d["sink"], out[:, t], ws,
+                   h_new=H[:, t].contiguous(), weights=weights, **dk)
+    torch.cuda.synchronize()
+    n_ent = TT // w.m
+    assert int(ct["n_entries"][0]) == n_ent
+
+    # ---- compressor outputs vs the oracle's compressor on the whole prefix
+    params = {k: x[k] for k in (("Ba", "Bb", "BIa", "BIb") if csa_mode else ("B",)) +
+              ("gamma", "gamma_win")}
+    comp = O.compress_tokens(x["H"][0], x["W"], params, w.mode, w.m, w.c, w.d_I, x["inv_freq"],
+                             1e-6)
+    ent = host_bits(ct["entries"][0])
+    win = host_bits(ct["window"][0])
+    check_close(O.bf16_bits_to_f64(ent[:n_ent]), O.bf16_bits_to_f64(comp["entries"]), "entries")
+    check_close(O.bf16_bits_to_f64(win[:TT]), O.bf16_bits_to_f64(comp["win"]), "window rows")
+    if csa_mode:
+        keys = ct["idx_keys"][0].cpu().numpy()
+        ksc = ct["idx_scale"][0].cpu().numpy()
+        check_close(ksc[:n_ent], comp["iscale"], "key scales", atol=0, rtol=1e-5)
+        steps = _e4m3_steps(keys[:n_ent], comp["ikeys"])
+        assert steps.max() <= 1, "indexer key codes differ by more than one step"
+
+    # ---- per-query selection and attention, stage-wise on the GPU's stored state
+    rng = np.random.default_rng(0)
+    qs = sorted(set([0, 1, 2, 3, 4, 5, 127, 128, 129, T - 1] + list(range(T, TT)) +
+                    list(rng.integers(0, T, 24))))
+    out_h = bf16_f64(out.view(torch.int16)[0])
+    idx_h = idx[0].cpu().numpy()
+    for t in qs:
+        n_vis = O.visible_entries(t, w.m, n_ent)
+        if csa_mode:
+            sc = O.index_scores(x["qi"][0, t], x["qi_scale"][0, t], x["wi"][0, t], keys, ksc, n_vis)
+            check_selection(idx_h[t], sc, w.k, "query %d selection" % t)
+            sel = idx_h[t][:min(w.k, n_vis)]
+        else:
+            sel = np.arange(n_vis)
+        rows = np.concatenate([ent[sel], win[O.window_tokens(t, w.n_win) % slots]])
+        ref, _ = O.attend(x["q"][0, t], rows, x["sink"], w.scale, t, x["inv_freq"])
+        check_close(out_h[t], ref, "query %d output" % t)
+
+
+def test_compress_ragged_batch_positions():
+    """csa_compress with per-sequence start positions: sequence 0 continues a prefix of 37
+    tokens, sequence 1 starts at 0; both append 19 tokens.  Entries, keys, window rows, the
+    tail and n_entries must match the oracle's compressor on each sequence's whole prefix."""
+    say("compress ragged positions")
+    w = S.shrink(S.WORKLOADS["tiny_csa"], B=2)
+    x = S.layer_inputs(w, T=56)
+    cfg, cache, ct, weights, d, n_max, slots = _build(w, x, 56 + 16)
+    ws = workspace(csa.workspace_size(cfg, csa.OP_COMPRESS, 2, 37, n_max))
+    # first call: sequence 0 takes tokens 0..36, sequence 1 tokens 0..36 as well (same T)
+    pos0 = torch.zeros(2, dtype=torch.int32, device=DEV)
+    csa.compress(cfg, d["H"][:, :37].contiguous(), pos0, weights, cache, ws)
+    # second call: sequence 0 continues at 37; sequence 1 restarts its own stream at 0 with
+    # new tokens (its cache entries are overwritten from block 0 on)
+    ct["n_entries"][1] = 0
+    pos0 = torch.tensor([37, 0], dtype=torch.int32, device=DEV)
+    Hn = torch.stack([d["H"][0, 37:56], d["H"][1, 37:56]]).contiguous()
+    csa.compress(cfg, Hn, pos0, weights, cache, ws)
+    torch.cuda.synchronize()
+    params = {k: x[k] for k in ("Ba", "Bb", "BIa", "BIb", "gamma", "gamma_win")}
+    seqs = [x["H"][0, :56], x["H"][1, 37:56]]
+    for b, Hs in enumerate(seqs):
+        comp = O.compress_tokens(Hs, x["W"], params, "csa", w.m, w.c, w.d_I, x["inv_freq"], 1e-6)
+        n = Hs.shape[0] // w.m
+        assert int(ct["n_entries"][b]) == n
+        ent = host_bits(ct["entries"][b])[:n]
+        check_close(O.bf16_bits_to_f64(ent), O.bf16_bits_to_f64(comp["entries"]), "seq %d" % b)
+        keys = ct["idx_keys"][b].cpu().numpy()[:n]
+        assert _e4m3_steps(keys, comp["ikeys"]).max() <= 1
+        win = host_bits(ct["window"][b])[:Hs.shape[0]]
+        check_close(O.bf16_bits_to_f64(win), O.bf16_bits_to_f64(comp["win"]), "seq %d win" % b)
