@@ -54,7 +54,7 @@ extern "C" {
 
 /* Layer configuration, passed by pointer (read during the call only).
  * Supported set (CSA_ERR_INVALID_ARG otherwise):
- *   head_dim in {64, 128, 192, ..., 512} (multiple of 64, <= 512);
+ *   head_dim in {128, 256, 512};
  *   rope_dim even, 2 <= rope_dim <= min(head_dim, 128);
  *   1 <= n_heads <= 128;  n_win in 1..1024;
  *   CSA: idx_dim in {32, 64, 128}, 1 <= idx_heads <= 64, 1 <= top_k <= 4096, m >= 1;
@@ -120,6 +120,20 @@ int csa_version(void);
 
 /* Message describing the last error returned on the calling thread ("" if none). */
 const char* csa_last_error(void);
+
+/* Opt-in launch timing, for measurement tools.  Between csa_profile_start() and
+ * csa_profile_stop() every kernel the library launches is bracketed by two hipEvents recorded on
+ * its launch stream.  csa_profile_stop() waits for those events and fills out[0..*n_out) with
+ * one record per kernel name: launches and summed event time in milliseconds.  Not for use while
+ * another thread is launching through the library. */
+typedef struct csa_kernel_time {
+  char name[40];
+  int32_t launches;
+  double total_ms;
+} csa_kernel_time_t;
+int csa_profile_start(void);
+int csa_profile_stop(csa_kernel_time_t* out /* host */, int32_t max_out,
+                     int32_t* n_out /* host */);
 
 /* Host-side shape helpers (no device work). */
 int csa_weight_cols(const csa_config_t* cfg, int32_t* n_cols /* host out */);

@@ -36,6 +36,11 @@ class Cache(ctypes.Structure):
                 ("tail", ctypes.c_void_p), ("n_entries", ctypes.c_void_p)]
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 40), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
+
+
 class Weights(ctypes.Structure):
     _fields_ = [("w_cat", ctypes.c_void_p), ("bias_a", ctypes.c_void_p),
                 ("bias_b", ctypes.c_void_p), ("bias_ia", ctypes.c_void_p),
@@ -49,6 +54,8 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "csa_version": ([], ctypes.c_int),
     "csa_last_error": ([], ctypes.c_char_p),
+    "csa_profile_start": ([], ctypes.c_int),
+    "csa_profile_stop": ([_P, _I, _P], ctypes.c_int),
     "csa_weight_cols": ([_P, _P], ctypes.c_int),
     "csa_tail_shape": ([_P, _P, _P], ctypes.c_int),
     "csa_workspace_size": ([_P, _I, _I, _I, _I, _P], ctypes.c_int),
@@ -86,6 +93,19 @@ def version():
 
 def last_error():
     return lib().csa_last_error().decode()
+
+
+def profile_start():
+    """Start bracketing every kernel launch of the library with hipEvents."""
+    _check(lib().csa_profile_start(), "csa_profile_start")
+
+
+def profile_stop():
+    """Stop; returns {kernel name: (launches, summed event milliseconds)}."""
+    buf = (KernelTime * 64)()
+    n = ctypes.c_int32()
+    _check(lib().csa_profile_stop(buf, 64, ctypes.byref(n)), "csa_profile_stop")
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n.value)}
 
 
 def _check(rc, what):

@@ -99,13 +99,11 @@ int check_weights(const csa_config_t* c, const csa_weights_t* w) {
 }
 
 // --- workspace layouts ----------------------------------------------------------------------
-bool index_multi(int rows) { return rows <= 1024; }
-
 size_t ws_compress(const csa_config_t* c, int B, int T) {
   return csa::compress_workspace(B, T, weight_cols(c));
 }
 size_t ws_index(const csa_config_t* c, int rows, int n_max) {
-  return csa::index_topk_workspace(rows, n_max, c->top_k, index_multi(rows));
+  return csa::index_topk_workspace(rows, n_max, c->top_k);
 }
 size_t ws_mqa(const csa_config_t* c, int rows, int max_list) {
   const csa::MqaPlan p = csa::plan_mqa(rows, c->n_heads, c->head_dim, max_list);
@@ -147,18 +145,7 @@ void fill_index_args(csa::IndexArgs& a, const csa_config_t* c, int B, int nq, co
   a.k = c->top_k;
   a.idx_out = idx_out;
   a.score_out = score_out;
-  const int rows = B * nq;
-  a.sstride = (k->n_max + 63) & ~63;
-  unsigned char* p = static_cast<unsigned char*>(ws);
-  a.scores = reinterpret_cast<float*>(p);
-  p += align256(static_cast<size_t>(rows) * a.sstride * sizeof(float));
-  a.hist = reinterpret_cast<uint32_t*>(p);
-  p += align256(static_cast<size_t>(rows) * csa::kHistBins * 4);
-  a.counters = reinterpret_cast<uint32_t*>(p);
-  p += align256(static_cast<size_t>(rows) * 2 * 4);
-  a.sel = reinterpret_cast<int32_t*>(p);
-  p += align256(static_cast<size_t>(rows) * c->top_k * 4);
-  a.cand = reinterpret_cast<uint64_t*>(p);
+  csa::index_topk_layout(a, ws, B * nq);
 }
 
 void fill_mqa_args(csa::MqaArgs& a, const csa_config_t* c, int B, int nq, const uint16_t* q,
@@ -230,7 +217,7 @@ int run_index(const csa_config_t* c, int B, int nq, const uint8_t* qi, const flo
               float* score_out, void* ws, hipStream_t s) {
   csa::IndexArgs a;
   fill_index_args(a, c, B, nq, qi, qi_scale, wi, k, pos, idx_out, score_out, ws);
-  hipError_t e = csa::launch_index_topk(a, index_multi(B * nq), s);
+  hipError_t e = csa::launch_index_topk(a, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "index_topk launch");
 }
 
@@ -250,6 +237,20 @@ int run_attend(const csa_config_t* c, int B, int nq, const uint16_t* q, const cs
 extern "C" {
 
 int csa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+int csa_profile_start(void) {
+  csa::profile_start();
+  return CSA_OK;
+}
+
+int csa_profile_stop(csa_kernel_time_t* out, int32_t max_out, int32_t* n_out) {
+  if (!out || !n_out || max_out < 0) return fail(CSA_ERR_INVALID_ARG, "out/n_out is NULL");
+  static_assert(sizeof(csa_kernel_time_t) == sizeof(csa::ProfTotal), "layout");
+  int n = 0;
+  const int rc = csa::profile_stop(reinterpret_cast<csa::ProfTotal*>(out), max_out, &n);
+  *n_out = n;
+  return rc == 0 ? CSA_OK : fail(CSA_ERR_HIP, "waiting for timing events failed");
+}
 
 const char* csa_last_error(void) { return g_last_error.c_str(); }
 

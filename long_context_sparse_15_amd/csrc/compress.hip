@@ -318,8 +318,11 @@ size_t compress_workspace(int B, int T, int n_cols) {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   const int M = a.B * a.T;
   const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (a.n_cols + GBN - 1) / GBN;
-  gemm_tn_bf16_kernel<<<tiles_m * tiles_n, 256, 0, s>>>(a.H, a.W, a.proj, M, a.n_cols, a.D,
-                                                        tiles_n);
+  {
+    ProfScope ps("compress_gemm", s);
+    gemm_tn_bf16_kernel<<<tiles_m * tiles_n, 256, 0, s>>>(a.H, a.W, a.proj, M, a.n_cols, a.D,
+                                                          tiles_n);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PoolParams p;
@@ -348,14 +351,21 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   p.entries = a.entries;
   p.ikeys = a.ikeys;
   p.iscale = a.iscale;
-  pool_kernel<<<a.B * p.nblk, 256, 0, s>>>(p);
+  {
+    ProfScope ps("compress_pool", s);
+    pool_kernel<<<a.B * p.nblk, 256, 0, s>>>(p);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  window_kernel<<<M, 256, 0, s>>>(a.proj, a.T, a.n_cols, a.c, a.r, a.pos0, a.gamma_win,
-                                  a.inv_freq, a.eps, a.window, a.win_slots);
+  {
+    ProfScope ps("compress_window", s);
+    window_kernel<<<M, 256, 0, s>>>(a.proj, a.T, a.n_cols, a.c, a.r, a.pos0, a.gamma_win,
+                                    a.inv_freq, a.eps, a.window, a.win_slots);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nrows = a.T < a.tail_rows ? a.T : a.tail_rows;
+  ProfScope ps("compress_tail", s);
   tail_kernel<<<a.B * nrows, 256, 0, s>>>(a.proj, a.T, a.n_cols, a.tail_rows, a.tail_cols, a.m,
                                           a.pos0, a.tail, a.n_entries, nrows);
   return hipGetLastError();

@@ -148,98 +148,74 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     }
   }
 }
-
 // ============================================================================ block helpers
-// Threshold bin of a row: the bin tb such that (#keys in bins > tb) < kk <= (#keys in bins >= tb).
-__device__ int find_threshold_bin(const uint32_t* __restrict__ h, int kk, uint32_t* s_sum,
-                                  int* s_out) {
-  const int tid = threadIdx.x;  // 256 threads, 16 bins each
-  uint32_t loc[16];
-  uint32_t tot = 0;
+// Block-wide search over a histogram of `nbins` counts for the bin d with
+//   sum(bins > d) < remaining <= sum(bins >= d).
+// Writes d to s_res[0] and remaining - sum(bins > d) to s_res[1].  All THREADS threads call it.
+template <int THREADS>
+__device__ void block_find_crossing(const uint32_t* bins, int nbins, uint32_t remaining,
+                                    uint32_t* s_tmp, int* s_res) {
+  constexpr int NWAVE = THREADS / 64;
+  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
+  const int per = nbins / THREADS;  // nbins is a multiple of THREADS
+  uint32_t own = 0;
+  for (int j = 0; j < per; ++j) own += bins[tid * per + j];
+  // inclusive suffix scan inside the wave (lane l: sum over lanes >= l)
+  uint32_t suf = own;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    loc[j] = h[tid * 16 + j];
-    tot += loc[j];
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_down(suf, off, 64);
+    if (l + off < 64) suf += v;
   }
-  s_sum[tid] = tot;
+  if (l == 0) s_tmp[wave] = suf;  // wave total
   __syncthreads();
-  // reverse inclusive scan: s_sum[t] = sum over t' >= t
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t v = (tid + off < 256) ? s_sum[tid + off] : 0u;
-    __syncthreads();
-    s_sum[tid] += v;
-    __syncthreads();
-  }
-  const uint32_t above = s_sum[tid] - tot;
-  if (above < static_cast<uint32_t>(kk) && static_cast<uint32_t>(kk) <= above + tot) {
+  uint32_t later = 0;
+  for (int w2 = wave + 1; w2 < NWAVE; ++w2) later += s_tmp[w2];
+  const uint32_t above = suf - own + later;
+  if (above < remaining && remaining <= above + own) {
     uint32_t cum = above;
-    for (int j = 15; j >= 0; --j) {
-      if (cum + loc[j] >= static_cast<uint32_t>(kk)) {
-        *s_out = tid * 16 + j;
+    for (int j = per - 1; j >= 0; --j) {
+      const uint32_t c = bins[tid * per + j];
+      if (cum + c >= remaining) {
+        s_res[0] = tid * per + j;
+        s_res[1] = static_cast<int>(remaining - cum);
         break;
       }
-      cum += loc[j];
+      cum += c;
     }
   }
   __syncthreads();
-  return *s_out;
 }
 
-// wave-aggregated append: returns the slot of this lane (valid only if pred)
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
-  const unsigned long long mask = __ballot(pred);
-  if (!mask) return 0;
-  const int l = lane_id();
-  const int leader = __ffsll(static_cast<long long>(mask)) - 1;
-  uint32_t base = 0;
-  if (l == leader) base = atomicAdd(counter, static_cast<uint32_t>(__popcll(mask)));
-  base = __shfl(base, leader, 64);
-  const unsigned long long lower = (l == 0) ? 0ull : (mask & ((1ull << l) - 1ull));
-  return base + static_cast<uint32_t>(__popcll(lower));
-}
-
-// ============================================================================ multi-WG top-k
-__global__ __launch_bounds__(256) void topk_collect_kernel(
-    const float* __restrict__ scores, int sstride, const uint32_t* __restrict__ hist,
-    const int32_t* __restrict__ n_entries, const int32_t* __restrict__ pos, int nq, int m, int k,
-    int n_max, int chunk, int nchunks, uint32_t* __restrict__ counters, int32_t* __restrict__ sel,
-    uint64_t* __restrict__ cand) {
-  __shared__ uint32_t s_sum[256];
-  __shared__ int s_tb;
-  const int row = blockIdx.x / nchunks;
-  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
-  if (threadIdx.x == 0) s_tb = -1;
-  if (n_vis <= k) return;  // everything is selected; finalize handles it
-  const int e0 = (blockIdx.x % nchunks) * chunk;
-  const int e1 = min(n_vis, e0 + chunk);
-  if (e0 >= e1) return;
-  const int tb = find_threshold_bin(hist + static_cast<size_t>(row) * kHistBins, k, s_sum, &s_tb);
-  const float* srow = scores + static_cast<size_t>(row) * sstride;
-  uint32_t* cnt = counters + 2 * row;
-  for (int base = e0; base < e1; base += 256) {
-    const int e = base + threadIdx.x;
-    uint32_t key = 0;
-    int bin = -1;
-    if (e < e1) {
-      key = order_key(srow[e]);
-      bin = static_cast<int>(key >> 20);
-    }
-    const bool is_sel = bin > tb;
-    const bool is_cand = bin == tb;
-    const uint32_t ps = wave_append(is_sel, cnt + 0);
-    if (is_sel && ps < static_cast<uint32_t>(k)) sel[static_cast<size_t>(row) * k + ps] = e;
-    const uint32_t pc = wave_append(is_cand, cnt + 1);
-    if (is_cand && pc < static_cast<uint32_t>(kCandCap))
-      cand[static_cast<size_t>(row) * kCandCap + pc] =
-          (static_cast<uint64_t>(key) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
+// Exclusive block scan of one uint32 per thread; returns the thread's prefix, *total the sum.
+template <int THREADS>
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
+  constexpr int NWAVE = THREADS / 64;
+  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
+  uint32_t inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_up(inc, off, 64);
+    if (l >= off) inc += u;
   }
+  if (l == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+  for (int w2 = 0; w2 < NWAVE; ++w2) {
+    const uint32_t x = s_tmp[w2];
+    if (w2 < wave) before += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + inc - v;
 }
 
-template <typename T, bool kDescending>
-__device__ void bitonic_sort(T* a, int n) {  // n power of two, 256 threads
+template <typename T, bool kDescending, int THREADS>
+__device__ void bitonic_sort(T* a, int n) {  // n power of two
   for (int k2 = 2; k2 <= n; k2 <<= 1) {
     for (int j = k2 >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += 256) {
+      for (int i = threadIdx.x; i < n; i += THREADS) {
         const int ixj = i ^ j;
         if (ixj > i) {
           const bool up = ((i & k2) == 0) == kDescending;  // this pair wants a[i] >= a[ixj]
@@ -261,153 +237,236 @@ __device__ __forceinline__ int next_pow2(int x) {
   return p;
 }
 
-// Exact selection of one row by a single workgroup streaming the row (used when a row's
-// threshold bin holds more candidates than kCandCap, e.g. massive ties).  Radix select over
-// the 32-bit keys finds the kk-th largest key T; an index-ordered pass then takes every key > T
-// and the first (lowest-index) keys == T, emitting indices in ascending order.
-__device__ void select_row_exact(const float* __restrict__ srow, int n_vis, int kk, int k,
-                                 int32_t* __restrict__ out, float* __restrict__ sout,
-                                 uint32_t* s_hist /*256*/, int* s_misc /*8*/) {
+// Index-ordered emission of a row's selection: every key > T, then the first need_eq keys == T
+// in index order; indices come out ascending.  key(e) reads the row's key of entry e.
+template <int THREADS, typename KeyFn>
+__device__ void ordered_emit(KeyFn key, int n, uint32_t T, int need_eq, int kk, int k,
+                             const float* __restrict__ srow, int32_t* __restrict__ out,
+                             float* __restrict__ sout, uint32_t* s_tmp) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
-  int remaining = kk;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    s_hist[tid] = 0;
-    __syncthreads();
-    for (int e = tid; e < n_vis; e += 256) {
-      const uint32_t key = order_key(srow[e]);
-      if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int cum = 0;
-      for (int d = 255; d >= 0; --d) {
-        const int c = static_cast<int>(s_hist[d]);
-        if (cum + c >= remaining) {
-          s_misc[0] = d;
-          s_misc[1] = remaining - cum;
-          break;
-        }
-        cum += c;
-      }
-    }
-    __syncthreads();
-    prefix |= static_cast<uint32_t>(s_misc[0]) << shift;
-    mask |= 255u << shift;
-    remaining = s_misc[1];
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  const int need_eq = remaining;
-  // index-ordered compaction
-  __shared__ int s_wcnt[2][4];
   int taken = 0, eq_seen = 0;
-  const int wave = tid >> 6, l = lane_id();
-  for (int base = 0; base < n_vis; base += 256) {
+  for (int base = 0; base < n; base += THREADS) {
     const int e = base + tid;
-    uint32_t key = 0;
-    if (e < n_vis) key = order_key(srow[e]);
-    const bool eq = (e < n_vis) && key == T;
-    const unsigned long long meq = __ballot(eq);
-    const unsigned long long lower = (l == 0) ? 0ull : ((1ull << l) - 1ull);
-    if (l == 0) s_wcnt[0][wave] = __popcll(meq);
-    __syncthreads();
-    int eq_before = eq_seen;
-    for (int w = 0; w < wave; ++w) eq_before += s_wcnt[0][w];
-    eq_before += __popcll(meq & lower);
-    const bool take = (e < n_vis) && (key > T || (eq && eq_before < need_eq));
-    const unsigned long long mt = __ballot(take);
-    if (l == 0) s_wcnt[1][wave] = __popcll(mt);
-    __syncthreads();
-    int slot = taken;
-    for (int w = 0; w < wave; ++w) slot += s_wcnt[1][w];
-    slot += __popcll(mt & lower);
-    if (take && slot < k) {
+    const uint32_t kv = e < n ? key(e) : 0u;
+    const bool eq = (e < n) && kv == T;
+    const bool gt = (e < n) && kv > T;
+    uint32_t tot_eq;
+    const uint32_t eq_before = block_excl_scan<THREADS>(eq ? 1u : 0u, s_tmp, &tot_eq);
+    const bool take = gt || (eq && eq_seen + static_cast<int>(eq_before) < need_eq);
+    uint32_t tot_take;
+    const uint32_t slot = taken + block_excl_scan<THREADS>(take ? 1u : 0u, s_tmp, &tot_take);
+    if (take && slot < static_cast<uint32_t>(k)) {
       out[slot] = e;
       if (sout) sout[slot] = srow[e];
     }
-    int add_eq = 0, add_t = 0;
-    for (int w = 0; w < 4; ++w) {
-      add_eq += s_wcnt[0][w];
-      add_t += s_wcnt[1][w];
-    }
-    eq_seen += add_eq;
-    taken += add_t;
-    __syncthreads();
+    eq_seen += static_cast<int>(tot_eq);
+    taken += static_cast<int>(tot_take);
   }
-  for (int j = kk + tid; j < k; j += 256) {
+  for (int j = kk + tid; j < k; j += THREADS) {
     out[j] = -1;
     if (sout) sout[j] = -INFINITY;
   }
 }
 
-__global__ __launch_bounds__(256) void topk_finalize_kernel(
-    const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
-    const int32_t* __restrict__ pos, int nq, int m, int k, int n_max,
-    const uint32_t* __restrict__ counters,
-    const int32_t* __restrict__ sel, const uint64_t* __restrict__ cand,
-    int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint64_t* cbuf = reinterpret_cast<uint64_t*>(smem);                  // kCandCap
-  int32_t* list = reinterpret_cast<int32_t*>(cbuf + kCandCap);         // kMaxTopK
-  __shared__ uint32_t s_hist[256];
-  __shared__ int s_misc[8];
-  const int row = blockIdx.x;
+// Radix select of the kk-th largest key among n keys with 12 + 12 + 8 bit passes over a 4096-bin
+// histogram.  Returns T (the kk-th largest key) and need_eq (how many keys == T are taken).
+template <int THREADS, typename KeyFn>
+__device__ void radix_select(KeyFn key, int n, int kk, uint32_t* hist /*4096*/, uint32_t* s_tmp,
+                             int* s_res, uint32_t& T, int& need_eq) {
   const int tid = threadIdx.x;
-  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
-  const int kk = min(k, n_vis);
-  int32_t* out = idx_out + static_cast<size_t>(row) * k;
-  float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
-  const float* srow = scores + static_cast<size_t>(row) * sstride;
-  if (n_vis <= k) {
-    for (int j = tid; j < k; j += 256) {
-      out[j] = j < n_vis ? j : -1;
-      if (sout) sout[j] = j < n_vis ? srow[j] : -INFINITY;
+  uint32_t prefix = 0, mask = 0;
+  uint32_t remaining = static_cast<uint32_t>(kk);
+  const int shifts[3] = {20, 8, 0};
+  const int widths[3] = {12, 12, 8};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = shifts[pass];
+    const int nb = 1 << widths[pass];
+    for (int i = tid; i < nb; i += THREADS) hist[i] = 0;
+    __syncthreads();
+    for (int e = tid; e < n; e += THREADS) {
+      const uint32_t kv = key(e);
+      if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & (nb - 1)], 1u);
     }
-    return;
+    __syncthreads();
+    if (nb >= THREADS) {
+      block_find_crossing<THREADS>(hist, nb, remaining, s_tmp, s_res);
+    } else {  // 256 bins with more than 256 threads: first 256 threads only
+      if (tid < 64) {
+        const int l = tid;
+        uint32_t c4[4], own = 0;
+        for (int j = 0; j < 4; ++j) {
+          c4[j] = hist[l * 4 + j];
+          own += c4[j];
+        }
+        uint32_t suf = own;
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t v = __shfl_down(suf, off, 64);
+          if (l + off < 64) suf += v;
+        }
+        const uint32_t above = suf - own;
+        if (above < remaining && remaining <= above + own) {
+          uint32_t cum = above;
+          for (int j = 3; j >= 0; --j) {
+            if (cum + c4[j] >= remaining) {
+              s_res[0] = l * 4 + j;
+              s_res[1] = static_cast<int>(remaining - cum);
+              break;
+            }
+            cum += c4[j];
+          }
+        }
+      }
+      __syncthreads();
+    }
+    const uint32_t d = static_cast<uint32_t>(s_res[0]);
+    remaining = static_cast<uint32_t>(s_res[1]);
+    prefix |= d << shift;
+    mask |= static_cast<uint32_t>(nb - 1) << shift;
+    __syncthreads();
   }
-  const int n_gt = static_cast<int>(counters[2 * row]);
-  const int nc = static_cast<int>(counters[2 * row + 1]);
-  // the candidate path needs n_gt < kk <= n_gt + nc <= n_gt + kCandCap; anything else (massive
-  // ties in the threshold bin) takes the exact streaming path
-  if (nc > kCandCap || n_gt >= kk || n_gt + nc < kk) {
-    select_row_exact(srow, n_vis, kk, k, out, sout, s_hist, s_misc);
-    return;
-  }
-  const int need = kk - n_gt;
-  const int p2c = next_pow2(nc);
-  for (int j = tid; j < p2c; j += 256)
-    cbuf[j] = j < nc ? cand[static_cast<size_t>(row) * kCandCap + j] : 0ull;
-  __syncthreads();
-  bitonic_sort<uint64_t, true>(cbuf, p2c);
-  const int p2k = next_pow2(kk);
-  for (int j = tid; j < p2k; j += 256) {
-    int32_t v = 0x7fffffff;
-    if (j < n_gt)
-      v = sel[static_cast<size_t>(row) * k + j];
-    else if (j < kk)
-      v = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(cbuf[j - n_gt] & 0xffffffffu));
-    list[j] = v;
-  }
-  __syncthreads();
-  bitonic_sort<int32_t, false>(list, p2k);
-  for (int j = tid; j < k; j += 256) {
-    const int v = j < kk ? list[j] : -1;
-    out[j] = v;
-    if (sout) sout[j] = j < kk ? srow[v] : -INFINITY;
-  }
+  T = prefix;
+  need_eq = static_cast<int>(remaining);
 }
 
 // ============================================================================ per-row top-k
-__global__ __launch_bounds__(256) void topk_row_kernel(
+// One workgroup per query row; the row's keys live in LDS when n_vis <= CAP, otherwise they are
+// re-read from the score row in global memory on every pass (exact, slower).
+template <int THREADS, int CAP>
+__global__ __launch_bounds__(THREADS) void topk_row_kernel(
     const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
   extern __shared__ __align__(16) unsigned char smem[];
-  uint32_t* keys = reinterpret_cast<uint32_t*>(smem);  // kRowTopkMaxN
-  __shared__ uint32_t s_hist[256];
-  __shared__ int s_misc[8];
-  __shared__ int s_wcnt[2][4];
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem);  // CAP
+  uint32_t* hist = keys + CAP;                          // 4096
+  __shared__ uint32_t s_tmp[THREADS / 64];
+  __shared__ int s_res[2];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  const int kk = min(k, n_vis);
+  int32_t* out = idx_out + static_cast<size_t>(row) * k;
+  float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
+  const float* srow = scores + static_cast<size_t>(row) * sstride;
+  if (n_vis <= k) {
+    for (int j = tid; j < k; j += THREADS) {
+      out[j] = j < n_vis ? j : -1;
+      if (sout) sout[j] = j < n_vis ? srow[j] : -INFINITY;
+    }
+    return;
+  }
+  uint32_t T;
+  int need_eq;
+  if (n_vis <= CAP) {
+    const int n4 = n_vis >> 2;
+    const float4* s4 = reinterpret_cast<const float4*>(srow);
+    for (int i = tid; i < n4; i += THREADS) {
+      const float4 v = s4[i];
+      keys[4 * i + 0] = order_key(v.x);
+      keys[4 * i + 1] = order_key(v.y);
+      keys[4 * i + 2] = order_key(v.z);
+      keys[4 * i + 3] = order_key(v.w);
+    }
+    for (int e = 4 * n4 + tid; e < n_vis; e += THREADS) keys[e] = order_key(srow[e]);
+    __syncthreads();
+    auto kf = [&](int e) { return keys[e]; };
+    radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
+    ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+  } else {
+    auto kf = [&](int e) { return order_key(srow[e]); };
+    radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
+    ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+  }
+}
+
+// ============================================================================ multi-WG top-k
+// For long rows: the scoring kernel has accumulated a 4096-bin histogram of the top 12 key bits
+// per row.  Each collect workgroup takes kCollectChunk entries of one row, finds the threshold bin
+// tb (the bin holding the kk-th largest key), and writes the indices of its entries above tb and
+// the (key, index) pairs inside tb into its own region of the workspace, at offsets from a block
+// prefix sum (no global atomics, deterministic).  The finalize workgroup of the row concatenates
+// the regions, sorts the candidates by (key desc, index asc), takes what is needed and emits the
+// selection in ascending index order.
+constexpr int kCollectChunk = 4096;
+constexpr int kCandPerChunk = 1024;
+
+__device__ int find_threshold_bin(const uint32_t* __restrict__ h, int kk, uint32_t* s_tmp,
+                                  int* s_res) {
+  if (threadIdx.x == 0) s_res[0] = -1;
+  __syncthreads();
+  block_find_crossing<256>(h, kHistBins, static_cast<uint32_t>(kk), s_tmp, s_res);
+  return s_res[0];
+}
+
+__global__ __launch_bounds__(256) void topk_collect_kernel(
+    const float* __restrict__ scores, int sstride, const uint32_t* __restrict__ hist,
+    const int32_t* __restrict__ n_entries, const int32_t* __restrict__ pos, int nq, int m, int k,
+    int n_max, int nchunks, int selcap, uint32_t* __restrict__ ccount, int32_t* __restrict__ sel,
+    uint64_t* __restrict__ cand) {
+  constexpr int PER = kCollectChunk / 256;
+  __shared__ uint32_t s_tmp[4];
+  __shared__ int s_res[2];
+  const int row = blockIdx.x / nchunks;
+  const int chunk = blockIdx.x % nchunks;
+  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  const int tid = threadIdx.x;
+  const size_t rc = static_cast<size_t>(row) * nchunks + chunk;
+  if (n_vis <= k) return;  // everything is selected; finalize does not read the regions
+  const int e0 = chunk * kCollectChunk;
+  if (e0 >= n_vis) {
+    if (tid == 0) ccount[rc] = 0;
+    return;
+  }
+  const int tb = find_threshold_bin(hist + static_cast<size_t>(row) * kHistBins, k, s_tmp, s_res);
+  const float* srow = scores + static_cast<size_t>(row) * sstride;
+  uint32_t key[PER];
+  uint32_t nsel = 0, ncand = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = e0 + i * 256 + tid;
+    key[i] = e < n_vis ? order_key(srow[e]) : 0u;
+    const int bin = e < n_vis ? static_cast<int>(key[i] >> 20) : -2;
+    nsel += bin > tb;
+    ncand += bin == tb;
+  }
+  uint32_t total;
+  const uint32_t off = block_excl_scan<256>((nsel << 16) | ncand, s_tmp, &total);
+  uint32_t os = off >> 16, oc = off & 0xffff;
+  int32_t* sdst = sel + rc * selcap;
+  uint64_t* cdst = cand + rc * kCandPerChunk;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = e0 + i * 256 + tid;
+    if (e >= n_vis) continue;
+    const int bin = static_cast<int>(key[i] >> 20);
+    if (bin > tb) {
+      if (os < static_cast<uint32_t>(selcap)) sdst[os] = e;
+      ++os;
+    } else if (bin == tb) {
+      if (oc < static_cast<uint32_t>(kCandPerChunk))
+        cdst[oc] = (static_cast<uint64_t>(key[i]) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
+      ++oc;
+    }
+  }
+  if (tid == 0) ccount[rc] = total;
+}
+
+// Exact selection by one workgroup streaming the row from global memory (fallback for rows whose
+// threshold bin overflows the candidate regions, e.g. massive ties).
+__global__ __launch_bounds__(256) void topk_finalize_kernel(
+    const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int nchunks, int selcap,
+    const uint32_t* __restrict__ ccount, const int32_t* __restrict__ sel,
+    const uint64_t* __restrict__ cand, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint64_t* cbuf = reinterpret_cast<uint64_t*>(smem);            // kCandCap
+  int32_t* list = reinterpret_cast<int32_t*>(cbuf + kCandCap);   // kMaxTopK
+  uint32_t* hist = reinterpret_cast<uint32_t*>(list + kMaxTopK);  // kHistBins (fallback)
+  __shared__ uint32_t s_tmp[4];
+  __shared__ int s_res[2];
+  __shared__ uint32_t s_soff[1025], s_coff[1025];
+  __shared__ int s_bad;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
@@ -422,93 +481,62 @@ __global__ __launch_bounds__(256) void topk_row_kernel(
     }
     return;
   }
-  if (n_vis > kRowTopkMaxN) {
-    select_row_exact(srow, n_vis, kk, k, out, sout, s_hist, s_misc);
+  const int used = (n_vis + kCollectChunk - 1) / kCollectChunk;  // <= nchunks
+  if (tid == 0) s_bad = used > 1024 ? 1 : 0;
+  __syncthreads();
+  if (!s_bad) {
+    // exclusive prefix over the chunks' (sel, cand) counts; one thread walks them (<= 1024)
+    if (tid == 0) {
+      uint32_t so = 0, co = 0;
+      int bad = 0;
+      for (int j = 0; j < used; ++j) {
+        const uint32_t c = ccount[static_cast<size_t>(row) * nchunks + j];
+        s_soff[j] = so;
+        s_coff[j] = co;
+        const uint32_t ns = c >> 16, nc = c & 0xffff;
+        if (ns > static_cast<uint32_t>(selcap) || nc > static_cast<uint32_t>(kCandPerChunk)) bad = 1;
+        so += ns;
+        co += nc;
+      }
+      s_soff[used] = so;
+      s_coff[used] = co;
+      const int n_gt = static_cast<int>(so), nc = static_cast<int>(co);
+      if (n_gt >= kk || n_gt + nc < kk || nc > kCandCap) bad = 1;
+      s_bad = bad;
+    }
+    __syncthreads();
+  }
+  if (s_bad) {
+    uint32_t T;
+    int need_eq;
+    auto kf = [&](int e) { return order_key(srow[e]); };
+    radix_select<256>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
+    ordered_emit<256>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
     return;
   }
-  for (int e = tid; e < n_vis; e += 256) keys[e] = order_key(srow[e]);
+  const int n_gt = static_cast<int>(s_soff[used]);
+  const int nc = static_cast<int>(s_coff[used]);
+  const int need = kk - n_gt;
+  const int p2c = next_pow2(nc);
+  for (int j = 0; j < used; ++j) {
+    const size_t rc = static_cast<size_t>(row) * nchunks + j;
+    const uint32_t ns = s_soff[j + 1] - s_soff[j], ncj = s_coff[j + 1] - s_coff[j];
+    for (uint32_t i = tid; i < ns; i += 256) list[s_soff[j] + i] = sel[rc * selcap + i];
+    for (uint32_t i = tid; i < ncj; i += 256) cbuf[s_coff[j] + i] = cand[rc * kCandPerChunk + i];
+  }
+  for (int j = nc + tid; j < p2c; j += 256) cbuf[j] = 0ull;
   __syncthreads();
-  uint32_t prefix = 0, mask = 0;
-  int remaining = kk;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    s_hist[tid] = 0;
-    __syncthreads();
-    for (int e = tid; e < n_vis; e += 256) {
-      const uint32_t key = keys[e];
-      if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // digit search by one wave: suffix sums over 256 digits, 4 per lane
-      const int l = tid;
-      uint32_t c4[4];
-      uint32_t tot = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c4[j] = s_hist[l * 4 + j];
-        tot += c4[j];
-      }
-      // inclusive suffix scan of tot across lanes (lane l gets sum over lanes >= l)
-      uint32_t suf = tot;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_down(suf, off, 64);
-        if (l + off < 64) suf += v;
-      }
-      const uint32_t above = suf - tot;
-      if (above < static_cast<uint32_t>(remaining) &&
-          static_cast<uint32_t>(remaining) <= above + tot) {
-        uint32_t cum = above;
-        for (int j = 3; j >= 0; --j) {
-          if (cum + c4[j] >= static_cast<uint32_t>(remaining)) {
-            s_misc[0] = l * 4 + j;
-            s_misc[1] = remaining - static_cast<int>(cum);
-            break;
-          }
-          cum += c4[j];
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= static_cast<uint32_t>(s_misc[0]) << shift;
-    mask |= 255u << shift;
-    remaining = s_misc[1];
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  const int need_eq = remaining;
-  int taken = 0, eq_seen = 0;
-  const int wave = tid >> 6, l = lane_id();
-  const unsigned long long lower = (l == 0) ? 0ull : ((1ull << l) - 1ull);
-  for (int base = 0; base < n_vis; base += 256) {
-    const int e = base + tid;
-    const uint32_t key = e < n_vis ? keys[e] : 0u;
-    const bool eq = (e < n_vis) && key == T;
-    const unsigned long long meq = __ballot(eq);
-    const bool gt = (e < n_vis) && key > T;
-    if (l == 0) s_wcnt[0][wave] = __popcll(meq);
-    __syncthreads();
-    int eq_before = eq_seen + __popcll(meq & lower);
-    for (int w = 0; w < wave; ++w) eq_before += s_wcnt[0][w];
-    const bool take = gt || (eq && eq_before < need_eq);
-    const unsigned long long mt = __ballot(take);
-    if (l == 0) s_wcnt[1][wave] = __popcll(mt);
-    __syncthreads();
-    int slot = taken + __popcll(mt & lower);
-    for (int w = 0; w < wave; ++w) slot += s_wcnt[1][w];
-    if (take && slot < k) {
-      out[slot] = e;
-      if (sout) sout[slot] = srow[e];
-    }
-    for (int w = 0; w < 4; ++w) {
-      eq_seen += s_wcnt[0][w];
-      taken += s_wcnt[1][w];
-    }
-    __syncthreads();
-  }
-  for (int j = kk + tid; j < k; j += 256) {
-    out[j] = -1;
-    if (sout) sout[j] = -INFINITY;
+  bitonic_sort<uint64_t, true, 256>(cbuf, p2c);
+  const int p2k = next_pow2(kk);
+  for (int j = n_gt + tid; j < p2k; j += 256)
+    list[j] = j < kk ? static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(cbuf[j - n_gt] & 0xffffffffu))
+                     : 0x7fffffff;
+  __syncthreads();
+  bitonic_sort<int32_t, false, 256>(list, p2k);
+  for (int j = tid; j < k; j += 256) {
+    const int v = j < kk ? list[j] : -1;
+    out[j] = v;
+    if (sout) sout[j] = j < kk ? srow[v] : -INFINITY;
   }
 }
 
@@ -523,6 +551,7 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const size_t blocks = (n + 255) / 256;
   const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
+  ProfScope ps("fill_u32", s);
   fill_u32_kernel<<<grid, 256, 0, s>>>(p, v, n);
   return hipGetLastError();
 }
@@ -532,21 +561,49 @@ static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 static int score_stride(int n_max) { return (n_max + 63) & ~63; }
 
-size_t index_topk_workspace(int rows, int n_max, int k, bool multi) {
+bool index_use_multi(int rows, int n_max) { return n_max > kRowTopkBigN && rows <= 4096; }
+
+static int collect_chunks(int n_max) { return (n_max + kCollectChunk - 1) / kCollectChunk; }
+static int sel_cap(int k) { return k < kCollectChunk ? k : kCollectChunk; }
+
+size_t index_topk_workspace(int rows, int n_max, int k) {
   size_t b = align256(static_cast<size_t>(rows) * score_stride(n_max) * sizeof(float));
-  if (multi) {
+  if (index_use_multi(rows, n_max)) {
+    const size_t rc = static_cast<size_t>(rows) * collect_chunks(n_max);
     b += align256(static_cast<size_t>(rows) * kHistBins * 4);
-    b += align256(static_cast<size_t>(rows) * 2 * 4);
-    b += align256(static_cast<size_t>(rows) * k * 4);
-    b += align256(static_cast<size_t>(rows) * kCandCap * 8);
+    b += align256(rc * 4);
+    b += align256(rc * sel_cap(k) * 4);
+    b += align256(rc * kCandPerChunk * 8);
   }
   return b;
+}
+
+void index_topk_layout(IndexArgs& a, void* ws, int rows) {
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  a.sstride = score_stride(a.n_max);
+  a.scores = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(rows) * a.sstride * sizeof(float));
+  a.hist = nullptr;
+  a.counters = nullptr;
+  a.sel = nullptr;
+  a.cand = nullptr;
+  if (index_use_multi(rows, a.n_max)) {
+    const size_t rc = static_cast<size_t>(rows) * collect_chunks(a.n_max);
+    a.hist = reinterpret_cast<uint32_t*>(p);
+    p += align256(static_cast<size_t>(rows) * kHistBins * 4);
+    a.counters = reinterpret_cast<uint32_t*>(p);
+    p += align256(rc * 4);
+    a.sel = reinterpret_cast<int32_t*>(p);
+    p += align256(rc * sel_cap(a.k) * 4);
+    a.cand = reinterpret_cast<uint64_t*>(p);
+  }
 }
 
 template <int DI, int HT>
 static void launch_scores_t(const IndexArgs& a, int chunk, int nchunks, uint32_t* hist,
                             hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(nchunks) * static_cast<unsigned>(a.B * a.nq);
+  ProfScope ps("index_score", s);
   index_score_kernel<DI, HT><<<grid, 256, 0, s>>>(a.qi, a.qi_scale, a.wi, a.keys, a.kscale,
                                                   a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
                                                   chunk, a.scores, a.sstride, hist, nchunks);
@@ -555,10 +612,10 @@ static void launch_scores_t(const IndexArgs& a, int chunk, int nchunks, uint32_t
 static hipError_t launch_scores(const IndexArgs& a, int chunk, uint32_t* hist, hipStream_t s) {
   const int nchunks = (a.n_max + chunk - 1) / chunk;
   const int ht = (a.H_I + 15) / 16;
-#define CSA_SCORE_CASE(DI_, HT_)                        \
-  if (a.d_I == DI_ && ht == HT_) {                     \
+#define CSA_SCORE_CASE(DI_, HT_)                            \
+  if (a.d_I == DI_ && ht == HT_) {                         \
     launch_scores_t<DI_, HT_>(a, chunk, nchunks, hist, s); \
-    return hipGetLastError();                          \
+    return hipGetLastError();                              \
   }
   CSA_SCORE_CASE(128, 4)
   CSA_SCORE_CASE(128, 3)
@@ -576,49 +633,61 @@ static hipError_t launch_scores(const IndexArgs& a, int chunk, uint32_t* hist, h
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_index_topk(const IndexArgs& a, bool multi, hipStream_t s) {
-  const int rows = a.B * a.nq;
-  hipError_t e;
-  if (multi) {
-    // histogram + counters must start at zero
-    e = launch_fill_u32(a.hist, 0u, static_cast<size_t>(rows) * kHistBins, s);
-    if (e != hipSuccess) return e;
-    e = launch_fill_u32(a.counters, 0u, static_cast<size_t>(rows) * 2, s);
-    if (e != hipSuccess) return e;
-  }
-  const int chunk = 2048;
-  e = launch_scores(a, chunk, multi ? a.hist : nullptr, s);
-  if (e != hipSuccess) return e;
-  if (multi) {
-    const int cchunk = 4096;
-    const int ncc = (a.n_max + cchunk - 1) / cchunk;
-    const unsigned grid = static_cast<unsigned>(ncc) * static_cast<unsigned>(rows);
-    topk_collect_kernel<<<grid, 256, 0, s>>>(a.scores, a.sstride, a.hist, a.n_entries, a.pos,
-                                             a.nq, a.m, a.k, a.n_max, cchunk, ncc, a.counters,
-                                             a.sel, a.cand);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const size_t lds = kCandCap * 8 + kMaxTopK * 4;
-    topk_finalize_kernel<<<rows, 256, lds, s>>>(a.scores, a.sstride, a.n_entries, a.pos, a.nq,
-                                                a.m, a.k, a.n_max, a.counters, a.sel, a.cand,
-                                                a.idx_out, a.score_out);
-    return hipGetLastError();
-  }
-  const size_t lds = kRowTopkMaxN * 4;
+template <int THREADS, int CAP>
+static hipError_t launch_row_topk(const IndexArgs& a, int rows, hipStream_t s) {
+  const size_t lds = (static_cast<size_t>(CAP) + kHistBins) * 4;
   static bool attr_set = false;
   if (!attr_set) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_row_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_row_kernel<THREADS, CAP>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  ProfScope ps("topk_row", s);
+  topk_row_kernel<THREADS, CAP><<<rows, THREADS, lds, s>>>(a.scores, a.sstride, a.n_entries,
+                                                           a.pos, a.nq, a.m, a.k, a.n_max,
+                                                           a.idx_out, a.score_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
+  const int rows = a.B * a.nq;
+  const bool multi = index_use_multi(rows, a.n_max);
+  hipError_t e;
+  if (multi) {
+    e = launch_fill_u32(a.hist, 0u, static_cast<size_t>(rows) * kHistBins, s);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_scores(a, 2048, multi ? a.hist : nullptr, s);
+  if (e != hipSuccess) return e;
+  if (!multi) {
+    if (a.n_max <= kRowTopkMaxN) return launch_row_topk<256, kRowTopkMaxN>(a, rows, s);
+    return launch_row_topk<1024, kRowTopkBigN>(a, rows, s);
+  }
+  const int ncc = collect_chunks(a.n_max);
+  const int scap = sel_cap(a.k);
+  {
+    ProfScope ps("topk_collect", s);
+    topk_collect_kernel<<<static_cast<unsigned>(ncc) * rows, 256, 0, s>>>(
+        a.scores, a.sstride, a.hist, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, ncc, scap,
+        a.counters, a.sel, a.cand);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = static_cast<size_t>(kCandCap) * 8 + kMaxTopK * 4 + kHistBins * 4;
+  static bool attr_set = false;
+  if (!attr_set) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_finalize_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  topk_row_kernel<<<rows, 256, lds, s>>>(a.scores, a.sstride, a.n_entries, a.pos, a.nq, a.m,
-                                         a.k, a.n_max, a.idx_out, a.score_out);
+  ProfScope ps("topk_finalize", s);
+  topk_finalize_kernel<<<rows, 256, lds, s>>>(a.scores, a.sstride, a.n_entries, a.pos, a.nq, a.m,
+                                              a.k, a.n_max, ncc, scap, a.counters, a.sel, a.cand,
+                                              a.idx_out, a.score_out);
   return hipGetLastError();
-}
-
-hipError_t launch_index_prefill(const IndexArgs& a, hipStream_t s) {
-  return launch_index_topk(a, false, s);
 }
 
 }  // namespace csa

@@ -10,7 +10,8 @@ namespace csa {
 constexpr int kHistBins = 4096;     // first-level top-k histogram: top 12 bits of the key
 constexpr int kCandCap = 4096;      // candidates kept for the exact refinement of one row
 constexpr int kMaxTopK = 4096;
-constexpr int kRowTopkMaxN = 16384; // visible entries a single-workgroup row select holds in LDS
+constexpr int kRowTopkMaxN = 16384; // row select with 256 threads holds this many keys in LDS
+constexpr int kRowTopkBigN = 32768; // row select with 1024 threads holds this many keys in LDS
 
 // ---------------------------------------------------------------- indexer + top-k
 struct IndexArgs {
@@ -24,17 +25,18 @@ struct IndexArgs {
   int B, nq, n_max, H_I, d_I, m, k;
   float* scores;          // workspace [rows, sstride]
   int sstride;
-  uint32_t* hist;         // workspace [rows, kHistBins]
-  uint32_t* counters;     // workspace [rows, 2]
-  int32_t* sel;           // workspace [rows, k]
-  uint64_t* cand;         // workspace [rows, kCandCap]
+  uint32_t* hist;         // workspace [rows, kHistBins] (multi-workgroup select only)
+  uint32_t* counters;     // workspace [rows, chunks] packed (selected << 16 | candidates)
+  int32_t* sel;           // workspace [rows, chunks, min(k, chunk)]
+  uint64_t* cand;         // workspace [rows, chunks, candidates per chunk]
   int32_t* idx_out;       // [rows, k]
   float* score_out;       // [rows, k] or nullptr
 };
-size_t index_topk_workspace(int rows, int n_max, int k, bool multi);
-hipError_t launch_index_topk(const IndexArgs& a, bool multi, hipStream_t s);
-// Causal prefill indexer: queries are tokens 0..nq-1 of each sequence.
-hipError_t launch_index_prefill(const IndexArgs& a, hipStream_t s);
+// Rows longer than kRowTopkBigN (and not too many) use the multi-workgroup select.
+bool index_use_multi(int rows, int n_max);
+size_t index_topk_workspace(int rows, int n_max, int k);
+void index_topk_layout(IndexArgs& a, void* ws, int rows);  // needs a.n_max and a.k set
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 struct MqaArgs {
@@ -85,5 +87,26 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- misc
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- launch timing (opt-in)
+struct ProfTotal {
+  char name[40];
+  int32_t launches;
+  double total_ms;
+};
+class ProfScope {  // brackets one kernel launch with hipEvents when timing is on
+ public:
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  void* a_;
+};
+int profile_start();
+int profile_stop(ProfTotal* out, int max, int* n);
 
 }  // namespace csa

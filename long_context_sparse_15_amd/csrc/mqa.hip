@@ -33,7 +33,7 @@ struct MqaParams {
   const float* inv_freq;
   int nq, n_heads, r, k, m, n_win, win_slots, n_max;
   float scale_log2;
-  int split_rows, n_splits, head_groups;
+  int split_rows, n_splits, head_groups, n_work;
   float* part;  // [rows, n_splits, n_heads, C + 4]: C unnormalised sums, (max, sum), pad
   uint16_t* out;
   float* lse_out;
@@ -83,11 +83,14 @@ __global__ __launch_bounds__(64 * NW) void mqa_kernel(MqaParams p) {
 
   const int tid = threadIdx.x;
   const int l = lane_id(), g = l >> 4, c16 = l & 15, wave = tid >> 6;
-  int bid = blockIdx.x;
-  const int split = bid % p.n_splits;
-  bid /= p.n_splits;
-  const int hg = bid % p.head_groups;
-  const int row = bid / p.head_groups;
+  // Work item w = (row, split); its head groups run as blocks 8 apart so that, with blocks
+  // dealt round-robin over the 8 XCDs, all groups of one work item share an XCD and its L2.
+  const int bid = blockIdx.x;
+  const int w = (bid / (8 * p.head_groups)) * 8 + (bid & 7);
+  const int hg = (bid >> 3) % p.head_groups;
+  if (w >= p.n_work) return;
+  const int split = w % p.n_splits;
+  const int row = w / p.n_splits;
   const int b = row / p.nq;
   const int t = p.pos ? p.pos[row] : (row % p.nq);
   const int n_ent = max(0, min(p.n_entries[b], p.n_max));
@@ -357,11 +360,12 @@ static int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
 MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list) {
   MqaPlan pl;
+  // at most 4 waves (64 heads) per workgroup: 16 heads x 512 dims of fp32 accumulator per wave
+  // plus the query fragments already fill most of a wave's registers
   int nw = (n_heads + 15) / 16;
-  if (nw > 8) nw = 8;
+  if (nw > 4) nw = 4;
   if (nw == 3) nw = 4;
-  if (nw > 4 && nw < 8) nw = 8;
-  if (c >= 512 && nw < 2) nw = 2;  // one wave would need 2x the staging registers and spill
+  if (c >= 512 && nw < 2) nw = 2;  // one wave would need 2x the staging registers
   pl.heads_per_wg = 16 * nw;
   pl.head_groups = (n_heads + pl.heads_per_wg - 1) / pl.heads_per_wg;
   const long base = static_cast<long>(rows) * pl.head_groups;
@@ -392,10 +396,16 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const unsigned grid = static_cast<unsigned>(rows) * prm.head_groups * prm.n_splits;
-  mqa_kernel<C, NW><<<grid, 64 * NW, lds, s>>>(prm);
+  MqaParams q = prm;
+  q.n_work = rows * prm.n_splits;
+  const unsigned grid = static_cast<unsigned>((q.n_work + 7) / 8 * 8) * prm.head_groups;
+  {
+    ProfScope ps(prm.idx ? "mqa_sparse" : "mqa_dense", s);
+    mqa_kernel<C, NW><<<grid, 64 * NW, lds, s>>>(q);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || prm.n_splits == 1) return e;
+  ProfScope ps("mqa_combine", s);
   mqa_combine_kernel<C><<<static_cast<unsigned>(rows) * prm.n_heads, 64, 0, s>>>(prm);
   return hipGetLastError();
 }
@@ -406,7 +416,6 @@ static hipError_t launch_c(const MqaParams& prm, int nw, int rows, hipStream_t s
     case 1: return launch_t<C, 1>(prm, rows, s);
     case 2: return launch_t<C, 2>(prm, rows, s);
     case 4: return launch_t<C, 4>(prm, rows, s);
-    case 8: return launch_t<C, 8>(prm, rows, s);
   }
   return hipErrorInvalidValue;
 }

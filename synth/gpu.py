@@ -1,0 +1,98 @@
+"""Full-size seeded inputs generated on the GPU with torch, for timing runs.
+
+Same recipe as synth.inputs (bf16 = normal draws truncated to their upper 16 bits; E4M3 codes
+assembled from sign/exponent of a normal draw plus uniform mantissa bits; uniform scales),
+drawn from torch's device generator instead of numpy PCG64 so that gigabyte-sized workloads
+are produced in milliseconds.  Parity tests use synth.inputs; these tensors are only timed.
+"""
+import torch
+
+from .inputs import rope_inv_freq, weight_cols
+
+
+def _gen(seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def bf16_normal(g, shape, device, std=1.0, chunk=1 << 26):
+    n = 1
+    for s in shape:
+        n *= s
+    out = torch.empty(n, dtype=torch.int16, device=device)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        x = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x *= std
+        out[s:e] = (x.view(torch.int32) >> 16).to(torch.int16)
+    return out.view(*shape)
+
+
+def e4m3_normalish(g, shape, device, chunk=1 << 26):
+    n = 1
+    for s in shape:
+        n *= s
+    out = torch.empty(n, dtype=torch.uint8, device=device)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        x = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+        _, ex = torch.frexp(x)
+        field = torch.clamp(ex + 6, 0, 14).to(torch.int32)
+        mant = torch.randint(0, 8, (e - s,), generator=g, device=device, dtype=torch.int32)
+        sign = (x < 0).to(torch.int32)
+        out[s:e] = ((sign << 7) | (field << 3) | mant).to(torch.uint8)
+    return out.view(*shape)
+
+
+def _uniform(g, shape, device, lo, hi):
+    return torch.rand(*shape, generator=g, device=device) * (hi - lo) + lo
+
+
+def decode_cache_inputs(w, device="cuda", seed=None):
+    """As synth.inputs.decode_cache_inputs, on the device."""
+    g = _gen(w.seed if seed is None else seed, device)
+    B, N = w.B, w.N
+    out = {"B": B, "N": N}
+    out["entries"] = bf16_normal(g, (B, N, w.c), device)
+    if w.mode == "csa":
+        out["ikeys"] = e4m3_normalish(g, (B, N, w.d_I), device)
+        out["iscale"] = _uniform(g, (B, N), device, 0.5, 1.5) / 16
+    out["window"] = bf16_normal(g, (B, w.n_win, w.c), device)
+    out["inv_freq"] = torch.from_numpy(rope_inv_freq(w.r, w.rope_base)).to(device)
+    out["pos"] = torch.full((B,), w.t, dtype=torch.int32, device=device)
+    out["n_entries"] = torch.full((B,), N, dtype=torch.int32, device=device)
+    _queries(g, w, 1, out, device)
+    return out
+
+
+def _queries(g, w, nq, out, device):
+    out["q"] = bf16_normal(g, (w.B, nq, w.n_h, w.c), device)
+    if w.mode == "csa":
+        out["qi"] = e4m3_normalish(g, (w.B, nq, w.H_I, w.d_I), device)
+        out["qi_scale"] = _uniform(g, (w.B, nq, w.H_I), device, 0.5, 1.5) / 16
+        out["wi"] = torch.randn(w.B, nq, w.H_I, generator=g, device=device) / 8
+    if w.sink is None:
+        out["sink"] = torch.randn(w.n_h, generator=g, device=device)
+    else:
+        out["sink"] = torch.full((w.n_h,), w.sink, device=device)
+
+
+def layer_inputs(w, device="cuda", seed=None):
+    """As synth.inputs.layer_inputs (prefill of w.T tokens, no decode tokens), on the device."""
+    g = _gen(w.seed if seed is None else seed, device)
+    T = w.T
+    out = {"T": T, "T_total": T}
+    out["H"] = bf16_normal(g, (w.B, T, w.D), device)
+    out["W"] = bf16_normal(g, (weight_cols(w), w.D), device, std=1.0 / w.D ** 0.5)
+    if w.mode == "csa":
+        for k, width in (("Ba", w.c), ("Bb", w.c), ("BIa", w.d_I), ("BIb", w.d_I)):
+            out[k] = torch.randn(w.m, width, generator=g, device=device)
+    else:
+        out["B"] = torch.randn(w.m, w.c, generator=g, device=device)
+    out["gamma"] = 1.0 + 0.1 * torch.randn(w.c, generator=g, device=device)
+    out["gamma_win"] = 1.0 + 0.1 * torch.randn(w.c, generator=g, device=device)
+    out["inv_freq"] = torch.from_numpy(rope_inv_freq(w.r, w.rope_base)).to(device)
+    _queries(g, w, T, out, device)
+    return out

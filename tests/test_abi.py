@@ -36,7 +36,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
         assert n in csa._SIGS, n

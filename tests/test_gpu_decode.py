@@ -89,6 +89,10 @@ def _w(name, **kw):
     ("csa_decode_1m", 2, 9000, [4 * 9000 + 7, 4 * 4500]),
     ("tiny_csa", 2, 700, [2063, 2]),
     ("tiny_csa", 1, 64, [300]),
+    # one 1024-thread workgroup per row with every key in LDS (16K < n_vis <= 32K)
+    ("csa_decode_128k", 2, 20000, [4 * 20000, 4 * 17000 + 3]),
+    # multi-workgroup select (n_vis > 32K): threshold bin, per-chunk regions, finalize
+    ("csa_decode_1m", 2, 40000, [4 * 40000 + 1, 4 * 33000]),
 ])
 def test_csa_decode_parity(case):
     name, B, N, positions = case
@@ -117,6 +121,16 @@ def test_csa_decode_massive_ties_exact_fallback():
     x["ikeys"][:] = x["ikeys"][:, :1]
     x["iscale"][:] = x["iscale"][:, :1]
     x["pos"] = np.array([4 * 6000], dtype=np.int32)
+    run_csa_case(w, x, exact_ties=True)
+
+
+def test_csa_decode_massive_ties_multi_workgroup_fallback():
+    say("csa decode massive ties, multi-workgroup select")
+    w = _w("csa_decode_128k")
+    x = S.decode_cache_inputs(w, B=1, N=40000)
+    x["ikeys"][:, 5000:] = x["ikeys"][:, 5000:5001]
+    x["iscale"][:, 5000:] = x["iscale"][:, 5000:5001]
+    x["pos"] = np.array([4 * 40000], dtype=np.int32)
     run_csa_case(w, x, exact_ties=True)
 
 
