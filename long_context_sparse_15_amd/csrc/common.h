@@ -8,6 +8,7 @@ namespace csa {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -76,5 +77,13 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane 4*i0+q points
+// at 4 consecutive 16-bit values (row i0, columns 4q..4q+3) of a 4x16 block; lane j receives
+// column j of that block, rows 0..3 in order.  p must point into LDS, 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
 
 }  // namespace csa

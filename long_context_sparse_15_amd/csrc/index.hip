@@ -238,34 +238,67 @@ __device__ __forceinline__ int next_pow2(int x) {
 }
 
 // Index-ordered emission of a row's selection: every key > T, then the first need_eq keys == T
-// in index order; indices come out ascending.  key(e) reads the row's key of entry e.
+// in index order; indices come out ascending.  key(e) reads the row's key of entry e.  Each wave
+// owns a contiguous segment of the row: a counting pass (ballots), one exchange of per-wave
+// counts, and an emitting pass whose slots come from ballot prefix counts.
+template <int THREADS, typename KeyFn, typename EmitFn>
+__device__ void ordered_emit_fn(KeyFn key, int n, uint32_t T, int need_eq, int cap, EmitFn emit) {
+  constexpr int NWAVE = THREADS / 64;
+  __shared__ uint32_t s_gt[NWAVE], s_eq[NWAVE];
+  const int l = lane_id(), wave = threadIdx.x >> 6;
+  const unsigned long long lower = (l == 0) ? 0ull : ((1ull << l) - 1ull);
+  const int seg = ((n + NWAVE - 1) / NWAVE + 63) & ~63;
+  const int s0 = min(n, wave * seg), s1 = min(n, s0 + seg);
+  uint32_t cgt = 0, ceq = 0;
+  for (int base = s0; base < s1; base += 64) {
+    const int e = base + l;
+    const uint32_t kv = e < s1 ? key(e) : 0u;
+    cgt += __popcll(__ballot(e < s1 && kv > T));
+    ceq += __popcll(__ballot(e < s1 && kv == T));
+  }
+  if (l == 0) {
+    s_gt[wave] = cgt;
+    s_eq[wave] = ceq;
+  }
+  __syncthreads();
+  int eq_seen = 0, slot_base = 0;
+  for (int w2 = 0; w2 < wave; ++w2) {
+    const int eqb = eq_seen;
+    int take_eq = need_eq - eqb;
+    take_eq = take_eq < 0 ? 0 : (take_eq > static_cast<int>(s_eq[w2]) ? static_cast<int>(s_eq[w2]) : take_eq);
+    slot_base += static_cast<int>(s_gt[w2]) + take_eq;
+    eq_seen += static_cast<int>(s_eq[w2]);
+  }
+  for (int base = s0; base < s1; base += 64) {
+    const int e = base + l;
+    const uint32_t kv = e < s1 ? key(e) : 0u;
+    const bool eq = e < s1 && kv == T;
+    const bool gt = e < s1 && kv > T;
+    const unsigned long long meq = __ballot(eq);
+    const bool take = gt || (eq && eq_seen + __popcll(meq & lower) < need_eq);
+    const unsigned long long mt = __ballot(take);
+    const int slot = slot_base + __popcll(mt & lower);
+    if (take && slot < cap) emit(slot, e);
+    slot_base += __popcll(mt);
+    eq_seen += __popcll(meq);
+  }
+  __syncthreads();  // s_gt / s_eq are reused by the next call
+}
+
+// Emission straight into a row of the output (and its scores), padded with -1 / -inf.
 template <int THREADS, typename KeyFn>
 __device__ void ordered_emit(KeyFn key, int n, uint32_t T, int need_eq, int kk, int k,
                              const float* __restrict__ srow, int32_t* __restrict__ out,
                              float* __restrict__ sout, uint32_t* s_tmp) {
-  const int tid = threadIdx.x;
-  int taken = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += THREADS) {
-    const int e = base + tid;
-    const uint32_t kv = e < n ? key(e) : 0u;
-    const bool eq = (e < n) && kv == T;
-    const bool gt = (e < n) && kv > T;
-    uint32_t tot_eq;
-    const uint32_t eq_before = block_excl_scan<THREADS>(eq ? 1u : 0u, s_tmp, &tot_eq);
-    const bool take = gt || (eq && eq_seen + static_cast<int>(eq_before) < need_eq);
-    uint32_t tot_take;
-    const uint32_t slot = taken + block_excl_scan<THREADS>(take ? 1u : 0u, s_tmp, &tot_take);
-    if (take && slot < static_cast<uint32_t>(k)) {
-      out[slot] = e;
-      if (sout) sout[slot] = srow[e];
-    }
-    eq_seen += static_cast<int>(tot_eq);
-    taken += static_cast<int>(tot_take);
-  }
-  for (int j = kk + tid; j < k; j += THREADS) {
+  ordered_emit_fn<THREADS>(key, n, T, need_eq, k, [&](int slot, int e) {
+    out[slot] = e;
+    if (sout) sout[slot] = srow[e];
+  });
+  for (int j = kk + threadIdx.x; j < k; j += THREADS) {
     out[j] = -1;
     if (sout) sout[j] = -INFINITY;
   }
+  (void)s_tmp;
 }
 
 // Radix select of the kk-th largest key among n keys with 12 + 12 + 8 bit passes over a 4096-bin
@@ -421,9 +454,11 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(
   const float* srow = scores + static_cast<size_t>(row) * sstride;
   uint32_t key[PER];
   uint32_t nsel = 0, ncand = 0;
+  // thread t owns entries e0 + t*PER .. e0 + t*PER + PER-1, so a block prefix over threads
+  // writes every region in ascending entry order
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = e0 + i * 256 + tid;
+    const int e = e0 + tid * PER + i;
     key[i] = e < n_vis ? order_key(srow[e]) : 0u;
     const int bin = e < n_vis ? static_cast<int>(key[i] >> 20) : -2;
     nsel += bin > tb;
@@ -436,7 +471,7 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(
   uint64_t* cdst = cand + rc * kCandPerChunk;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = e0 + i * 256 + tid;
+    const int e = e0 + tid * PER + i;
     if (e >= n_vis) continue;
     const int bin = static_cast<int>(key[i] >> 20);
     if (bin > tb) {
@@ -444,7 +479,7 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(
       ++os;
     } else if (bin == tb) {
       if (oc < static_cast<uint32_t>(kCandPerChunk))
-        cdst[oc] = (static_cast<uint64_t>(key[i]) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
+        cdst[oc] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(e);
       ++oc;
     }
   }
@@ -485,24 +520,38 @@ __global__ __launch_bounds__(256) void topk_finalize_kernel(
   if (tid == 0) s_bad = used > 1024 ? 1 : 0;
   __syncthreads();
   if (!s_bad) {
-    // exclusive prefix over the chunks' (sel, cand) counts; one thread walks them (<= 1024)
-    if (tid == 0) {
-      uint32_t so = 0, co = 0;
-      int bad = 0;
-      for (int j = 0; j < used; ++j) {
-        const uint32_t c = ccount[static_cast<size_t>(row) * nchunks + j];
-        s_soff[j] = so;
-        s_coff[j] = co;
-        const uint32_t ns = c >> 16, nc = c & 0xffff;
-        if (ns > static_cast<uint32_t>(selcap) || nc > static_cast<uint32_t>(kCandPerChunk)) bad = 1;
-        so += ns;
-        co += nc;
+    // per-chunk counts -> exclusive prefix sums (4 chunks per thread, one block scan each)
+    uint32_t ls = 0, lc = 0;
+    uint32_t cs[4], cc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ch = tid * 4 + j;
+      const uint32_t c = ch < used ? ccount[static_cast<size_t>(row) * nchunks + ch] : 0u;
+      cs[j] = c >> 16;
+      cc[j] = c & 0xffff;
+      if (cs[j] > static_cast<uint32_t>(selcap) || cc[j] > static_cast<uint32_t>(kCandPerChunk))
+        s_bad = 1;
+      ls += cs[j];
+      lc += cc[j];
+    }
+    uint32_t tot_s, tot_c;
+    uint32_t ps = block_excl_scan<256>(ls, s_tmp, &tot_s);
+    uint32_t pc = block_excl_scan<256>(lc, s_tmp, &tot_c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ch = tid * 4 + j;
+      if (ch <= used) {
+        s_soff[ch] = ps;
+        s_coff[ch] = pc;
       }
-      s_soff[used] = so;
-      s_coff[used] = co;
-      const int n_gt = static_cast<int>(so), nc = static_cast<int>(co);
-      if (n_gt >= kk || n_gt + nc < kk || nc > kCandCap) bad = 1;
-      s_bad = bad;
+      ps += cs[j];
+      pc += cc[j];
+    }
+    if (tid == 0) {
+      const int n_gt = static_cast<int>(tot_s), nc = static_cast<int>(tot_c);
+      if (n_gt >= kk || n_gt + nc < kk || nc > kCandCap) s_bad = 1;
+      s_soff[used] = tot_s;
+      s_coff[used] = tot_c;
     }
     __syncthreads();
   }
@@ -517,26 +566,62 @@ __global__ __launch_bounds__(256) void topk_finalize_kernel(
   const int n_gt = static_cast<int>(s_soff[used]);
   const int nc = static_cast<int>(s_coff[used]);
   const int need = kk - n_gt;
-  const int p2c = next_pow2(nc);
-  for (int j = 0; j < used; ++j) {
-    const size_t rc = static_cast<size_t>(row) * nchunks + j;
-    const uint32_t ns = s_soff[j + 1] - s_soff[j], ncj = s_coff[j + 1] - s_coff[j];
-    for (uint32_t i = tid; i < ns; i += 256) list[s_soff[j] + i] = sel[rc * selcap + i];
-    for (uint32_t i = tid; i < ncj; i += 256) cbuf[s_coff[j] + i] = cand[rc * kCandPerChunk + i];
+  // LDS: list[0..n_gt) = entries above the threshold bin (ascending); ckey/cidx[0..nc) = the
+  // threshold bin's candidates (ascending index); chosen[0..need) = the candidates taken
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(cbuf);
+  int32_t* cidx = reinterpret_cast<int32_t*>(ckey + kCandCap);
+  int32_t* chosen = list + n_gt;  // directly after the above-threshold list
+  auto chunk_of = [&](const uint32_t* off, int j) {
+    int lo = 0, hi = used;  // off[lo] <= j < off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= static_cast<uint32_t>(j)) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  for (int j = tid; j < n_gt; j += 256) {
+    const int ch = chunk_of(s_soff, j);
+    list[j] = sel[(static_cast<size_t>(row) * nchunks + ch) * selcap + (j - s_soff[ch])];
   }
-  for (int j = nc + tid; j < p2c; j += 256) cbuf[j] = 0ull;
+  for (int j = tid; j < nc; j += 256) {
+    const int ch = chunk_of(s_coff, j);
+    const uint64_t v = cand[(static_cast<size_t>(row) * nchunks + ch) * kCandPerChunk + (j - s_coff[ch])];
+    ckey[j] = static_cast<uint32_t>(v >> 32);
+    cidx[j] = static_cast<int32_t>(v & 0xffffffffu);
+  }
   __syncthreads();
-  bitonic_sort<uint64_t, true, 256>(cbuf, p2c);
-  const int p2k = next_pow2(kk);
-  for (int j = n_gt + tid; j < p2k; j += 256)
-    list[j] = j < kk ? static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(cbuf[j - n_gt] & 0xffffffffu))
-                     : 0x7fffffff;
+  // the need largest candidates (lower index first among equal keys), in ascending index order
+  uint32_t T2;
+  int need_eq2;
+  auto ck = [&](int j) { return ckey[j]; };
+  radix_select<256>(ck, nc, need, hist, s_tmp, s_res, T2, need_eq2);
+  ordered_emit_fn<256>(ck, nc, T2, need_eq2, need, [&](int slot, int j) { chosen[slot] = cidx[j]; });
   __syncthreads();
-  bitonic_sort<int32_t, false, 256>(list, p2k);
-  for (int j = tid; j < k; j += 256) {
-    const int v = j < kk ? list[j] : -1;
-    out[j] = v;
-    if (sout) sout[j] = j < kk ? srow[v] : -INFINITY;
+  // merge the two ascending lists by rank: an element's output slot is its own index plus the
+  // number of elements of the other list that are smaller (the lists are disjoint)
+  auto rank_in = [&](const int32_t* a, int n, int v) {
+    int lo = 0, hi = n;  // first position with a[pos] > v
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a[mid] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  for (int j = tid; j < n_gt; j += 256) {
+    const int v = list[j];
+    const int slot = j + rank_in(chosen, need, v);
+    out[slot] = v;
+    if (sout) sout[slot] = srow[v];
+  }
+  for (int j = tid; j < need; j += 256) {
+    const int v = chosen[j];
+    const int slot = j + rank_in(list, n_gt, v);
+    out[slot] = v;
+    if (sout) sout[slot] = srow[v];
+  }
+  for (int j = kk + tid; j < k; j += 256) {
+    out[j] = -1;
+    if (sout) sout[j] = -INFINITY;
   }
 }
 
@@ -659,7 +744,7 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
     e = launch_fill_u32(a.hist, 0u, static_cast<size_t>(rows) * kHistBins, s);
     if (e != hipSuccess) return e;
   }
-  e = launch_scores(a, 2048, multi ? a.hist : nullptr, s);
+  e = launch_scores(a, 1024, multi ? a.hist : nullptr, s);
   if (e != hipSuccess) return e;
   if (!multi) {
     if (a.n_max <= kRowTopkMaxN) return launch_row_topk<256, kRowTopkMaxN>(a, rows, s);

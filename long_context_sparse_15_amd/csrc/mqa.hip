@@ -247,7 +247,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_kernel(MqaParams p) {
       }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    if (alpha != 1.f) {
+    if (__ballot(alpha != 1.f)) {  // wave-uniform: skip once the running maxima have settled
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
@@ -257,17 +257,19 @@ __global__ __launch_bounds__(64 * NW) void mqa_kernel(MqaParams p) {
     pr[2] = pack_bf16x2(pv[1][0], pv[1][1]);
     pr[3] = pack_bf16x2(pv[1][2], pv[1][3]);
     const bf16x8 bp = as_bf16x8(pr);
-    // O^T += E^T . P^T ; K slots of lane group g are rows 4g..4g+3 and 16+4g..16+4g+3
-    const uint16_t* ec = E + (g * 4) * TL::kStride + c16;
+    // O^T += E^T . P^T.  The K slots of lane group g are rows 4g..4g+3 and 16+4g..16+4g+3 (the
+    // S^T accumulator layout); the A operand (dims x rows) comes from two LDS transpose reads:
+    // within each 16-lane group, lane 4*i0+q addresses row (base+i0), dims dt*16+4q..+3 of a
+    // 4x16 block, and lane j receives dim dt*16+j of rows base..base+3.
+    const int i0 = c16 >> 2, q4 = c16 & 3;
+    const uint16_t* ta = E + (g * 4 + i0) * TL::kStride + 4 * q4;
+    const uint16_t* tb = ta + 16 * TL::kStride;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* e0 = ec + dt * 16;
-      u32x4 a;
-      a[0] = static_cast<uint32_t>(e0[0 * TL::kStride]) | (static_cast<uint32_t>(e0[1 * TL::kStride]) << 16);
-      a[1] = static_cast<uint32_t>(e0[2 * TL::kStride]) | (static_cast<uint32_t>(e0[3 * TL::kStride]) << 16);
-      a[2] = static_cast<uint32_t>(e0[16 * TL::kStride]) | (static_cast<uint32_t>(e0[17 * TL::kStride]) << 16);
-      a[3] = static_cast<uint32_t>(e0[18 * TL::kStride]) | (static_cast<uint32_t>(e0[19 * TL::kStride]) << 16);
-      acc[dt] = mfma_bf16_16x16x32(as_bf16x8(a), bp, acc[dt]);
+      const bf16x4 lo = lds_read_tr16(ta + dt * 16);
+      const bf16x4 hi = lds_read_tr16(tb + dt * 16);
+      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[dt] = mfma_bf16_16x16x32(a, bp, acc[dt]);
     }
     __syncthreads();  // everyone is done with this buffer and with s_valid[buf]
     if (more) {
@@ -372,7 +374,7 @@ MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list) {
   const long target = 512;
   int splits = base >= target ? 1 : static_cast<int>((target + base - 1) / base);
   int sr = round_up((max_list + splits - 1) / splits, 32);
-  if (sr < 128 && max_list > 128) sr = 128;
+  if (sr < 64 && max_list > 64) sr = 64;
   if (sr < 32) sr = 32;
   pl.split_rows = sr;
   pl.n_splits = (max_list + sr - 1) / sr;

@@ -1,0 +1,159 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times (the same
+entry points, shapes and workspace plans), checked against the oracle on sampled outputs:
+
+* CSA decode, batch 32, 32768 entries (128K context), 64 heads, indexer 64x128, k=512;
+* CSA decode, batch 4, 262144 entries (1M context), 128 heads, k=2048;
+* HCA dense decode, batch 16, 8192 entries (1M context), 128 heads;
+* CSA prefill of 65536 tokens with hidden size 4096 (compressor, causal indexer, per-query
+  top-k 512, sparse MQA with window and sink), checked stage-wise on sampled tokens.
+
+Inputs come from the seeded device generator (synth.gpu); the oracle receives host copies of the
+same tensors."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_15_amd as csa
+import oracle as O
+from synth import inputs as S
+from synth import gpu as G
+from gpu_common import (DEV, check_close, check_selection, say, workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+def h16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def _decode_full(name, sample):
+    w = S.WORKLOADS[name]
+    say("full-size decode", name, "B=%d N=%d" % (w.B, w.N))
+    x = G.decode_cache_inputs(w, DEV)
+    csa_mode = w.mode == "csa"
+    cfg = csa.make_config(csa.MODE_CSA if csa_mode else csa.MODE_HCA, w.m, w.n_h, w.c, w.r,
+                          x["inv_freq"], top_k=w.k, n_win=w.n_win, idx_heads=w.H_I,
+                          idx_dim=w.d_I, softmax_scale=w.scale)
+    cache = csa.make_cache(w.N, w.n_win, x["entries"], x["window"], x["n_entries"],
+                           idx_keys=x.get("ikeys"), idx_scale=x.get("iscale"))
+    ws = workspace(csa.workspace_size(cfg, csa.OP_DECODE, w.B, 1, w.N))
+    out = torch.empty((w.B, w.n_h, w.c), dtype=torch.bfloat16, device=DEV)
+    q = x["q"][:, 0].contiguous()
+    idx = torch.full((w.B, max(w.k, 1)), -7, dtype=torch.int32, device=DEV)
+    if csa_mode:
+        csa.decode(cfg, cache, x["pos"], q, x["sink"], out, ws, qi=x["qi"],
+                   qi_scale=x["qi_scale"], wi=x["wi"], idx_out=idx)
+    else:
+        csa.decode(cfg, cache, x["pos"], q, x["sink"], out, ws)
+    torch.cuda.synchronize()
+    out_h = O.bf16_bits_to_f64(h16(out.view(torch.int16)))
+    idx_h = idx.cpu().numpy()
+    inv = x["inv_freq"].cpu().numpy()
+    sink = x["sink"].cpu().numpy()
+    for b in sample:
+        t = int(w.t)
+        n_vis = O.visible_entries(t, w.m, w.N)
+        ent = h16(x["entries"][b])
+        win = h16(x["window"][b])
+        win_rows = win[[u % w.n_win for u in O.window_tokens(t, w.n_win)]]
+        if csa_mode:
+            sc = O.index_scores(x["qi"][b, 0].cpu().numpy(), x["qi_scale"][b, 0].cpu().numpy(),
+                                x["wi"][b, 0].cpu().numpy(), x["ikeys"][b].cpu().numpy(),
+                                x["iscale"][b].cpu().numpy(), n_vis)
+            check_selection(idx_h[b], sc, w.k, "%s seq %d selection" % (name, b))
+            rows = np.concatenate([ent[idx_h[b][:min(w.k, n_vis)]], win_rows])
+        else:
+            rows = np.concatenate([ent[:n_vis], win_rows])
+        ref, _ = O.attend(h16(x["q"][b, 0]), rows, sink, w.scale, t, inv)
+        check_close(out_h[b], ref, "%s seq %d output" % (name, b))
+
+
+def test_full_csa_decode_128k():
+    _decode_full("csa_decode_128k", [0, 13, 31])
+
+
+def test_full_csa_decode_1m():
+    _decode_full("csa_decode_1m", [0, 3])
+
+
+def test_full_hca_decode_1m():
+    _decode_full("hca_decode_1m", [0, 9, 15])
+
+
+def test_full_csa_prefill_64k():
+    w = S.WORKLOADS["csa_prefill_64k"]
+    say("full-size prefill", w.name, "T=%d D=%d" % (w.T, w.D))
+    x = G.layer_inputs(w, DEV)
+    T, B = w.T, w.B
+    n_max = T // w.m
+    cfg = csa.make_config(csa.MODE_CSA, w.m, w.n_h, w.c, w.r, x["inv_freq"], top_k=w.k,
+                          n_win=w.n_win, idx_heads=w.H_I, idx_dim=w.d_I, hidden=w.D,
+                          softmax_scale=w.scale)
+    tr, tc = csa.tail_shape(cfg)
+    ct = dict(entries=torch.zeros((B, n_max, w.c), dtype=torch.int16, device=DEV),
+              window=torch.zeros((B, T, w.c), dtype=torch.int16, device=DEV),
+              n_entries=torch.zeros(B, dtype=torch.int32, device=DEV),
+              tail=torch.zeros((B, tr, tc), dtype=torch.float32, device=DEV),
+              idx_keys=torch.zeros((B, n_max, w.d_I), dtype=torch.uint8, device=DEV),
+              idx_scale=torch.zeros((B, n_max), dtype=torch.float32, device=DEV))
+    cache = csa.make_cache(n_max, T, **ct)
+    weights = csa.make_weights(x["W"], x["Ba"], x["gamma"], x["gamma_win"], bias_b=x["Bb"],
+                               bias_ia=x["BIa"], bias_ib=x["BIb"])
+    ws = workspace(csa.workspace_size(cfg, csa.OP_PREFILL, B, T, n_max))
+    out = torch.empty((B, T, w.n_h, w.c), dtype=torch.bfloat16, device=DEV)
+    idx = torch.full((B, T, w.k), -7, dtype=torch.int32, device=DEV)
+    csa.prefill(cfg, x["H"], weights, cache, x["q"], x["sink"], out, ws, qi=x["qi"],
+                qi_scale=x["qi_scale"], wi=x["wi"], idx_out=idx)
+    torch.cuda.synchronize()
+    assert int(ct["n_entries"][0]) == n_max
+    inv = x["inv_freq"].cpu().numpy()
+    sink = x["sink"].cpu().numpy()
+    Wh = h16(x["W"])
+    params = {k: x[k].cpu().numpy() for k in ("Ba", "Bb", "BIa", "BIb", "gamma", "gamma_win")}
+    keys = ct["idx_keys"][0].cpu().numpy()
+    ksc = ct["idx_scale"][0].cpu().numpy()
+    ent = h16(ct["entries"][0])
+    rng = np.random.default_rng(5)
+
+    # compressor: sampled blocks i (tokens 4i-4 .. 4i+3 feed block i) and window rows
+    say("prefill compressor sample")
+    for i in [0, 1, 2, 1000, 8191, n_max - 1] + list(rng.integers(3, n_max, 3)):
+        lo = max(0, w.m * (i - 1))
+        Hs = h16(x["H"][0, lo:w.m * (i + 1)])
+        P = O.project(Hs, Wh)
+        sc_ = O.split_columns(P, "csa", w.c, w.d_I)
+        blk = (i * w.m - lo) // w.m  # block index inside the slice (0 for i = 0, else 1)
+        pre = O.pool_overlap(sc_["Ca"], sc_["Cb"], sc_["Za"], sc_["Zb"], params["Ba"],
+                             params["Bb"], w.m, blk + 1)[blk]
+        e_ref = O.rope_rotate(O.rms_norm(pre, params["gamma"], 1e-6), w.m * i, inv)
+        check_close(O.bf16_bits_to_f64(ent[i]), e_ref, "entry %d" % i)
+        ipre = O.pool_overlap(sc_["Ia"], sc_["Ib"], sc_["IZa"], sc_["IZb"], params["BIa"],
+                              params["BIb"], w.m, blk + 1)[blk]
+        dec = O.e4m3_decode(keys[i]) * np.float64(ksc[i])
+        check_close(ksc[i], np.max(np.abs(ipre)) / 448.0, "key scale %d" % i, atol=0, rtol=1e-5)
+        # one E4M3 step: 2^-3 relative in the normal range, 2^-9 * scale for subnormals
+        check_close(dec, ipre, "indexer key %d" % i, atol=ksc[i] * 2.0 ** -8, rtol=2.0 ** -3)
+    win_all = ct["window"][0]
+    for u in [0, 5, 4095, T - 1] + list(rng.integers(0, T, 3)):
+        P = O.project(h16(x["H"][0, u:u + 1]), Wh)
+        wr = O.rope_rotate(O.rms_norm(P[:, 4 * w.c + 4 * w.d_I:], params["gamma_win"], 1e-6), u,
+                           inv)
+        check_close(O.bf16_bits_to_f64(h16(win_all[u])), wr[0], "window row %d" % u)
+
+    # indexer + top-k + attention on sampled query tokens, stage-wise on the GPU's state
+    say("prefill query sample")
+    qs = [0, 1, 2, 3, 4, 127, 128, 2047, 2048, 16383, 40000, T - 1] + list(
+        rng.integers(0, T, 6))
+    win_h = None
+    for t in qs:
+        n_vis = O.visible_entries(t, w.m, n_max)
+        sc = O.index_scores(x["qi"][0, t].cpu().numpy(), x["qi_scale"][0, t].cpu().numpy(),
+                            x["wi"][0, t].cpu().numpy(), keys, ksc, n_vis)
+        row = idx[0, t].cpu().numpy()
+        check_selection(row, sc, w.k, "query %d selection" % t)
+        sel = row[:min(w.k, n_vis)]
+        wt = O.window_tokens(t, w.n_win)
+        rows = np.concatenate([ent[sel], h16(win_all[wt[0]:wt[-1] + 1])])
+        ref, _ = O.attend(h16(x["q"][0, t]), rows, sink, w.scale, t, inv)
+        got = O.bf16_bits_to_f64(h16(out[0, t].view(torch.int16)))
+        check_close(got, ref, "query %d output" % t)
