@@ -17,6 +17,10 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef CSA_STREAM_LOAD
+#define CSA_STREAM_LOAD(p) __builtin_nontemporal_load(p)
+#endif
+
 namespace csa {
 
 // Visible entries of a query row: min(n_entries[b], floor((t+1)/m)), clamped to [0, n_max]
@@ -35,7 +39,7 @@ __device__ __forceinline__ int visible(const int32_t* n_entries, const int32_t* 
 // One workgroup scores `chunk` consecutive entries of one query row.  Each wave takes 16-entry
 // tiles; a tile is an MFMA with the indexer heads as the M dimension (A operand, resident in
 // registers for the whole chunk) and 16 entries as N (B operand, streamed from HBM).
-template <int DI, int HT>
+template <int DI, int HT, int TPW>
 __global__ __launch_bounds__(256) void index_score_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ wi, const uint8_t* __restrict__ keys,
@@ -86,22 +90,19 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     const uint8_t* kbase = keys + static_cast<size_t>(b) * n_max * DI + g * KB;
     const float* sbase = kscale + static_cast<size_t>(b) * n_max;
     float* srow = scores + static_cast<size_t>(row) * sstride;
-    const int ntile = (e1 - e0 + 15) >> 4;
 
-    auto load = [&](int tile, long (&bk)[KK], float& ks) {
-      const int e = e0 + tile * 16 + c16;
-      if (e < e1) {
-        const long* src = reinterpret_cast<const long*>(kbase + static_cast<size_t>(e) * DI);
+    // Wave `wave` scores tiles wave, wave+4, ... (TPW tiles of 16 entries).  The sequence is
+    // fully unrolled straight-line code with PD tiles in flight; loads are unconditional (past
+    // the end they re-read entry e1-1, whose extra scores are never stored), so the compiler
+    // waits for exactly the tile it is about to use.
+    auto load = [&](int t, long (&bk)[KK], float& ks) {
+      const int e = min(e0 + (wave + 4 * t) * 16 + c16, e1 - 1);
+      const long* src = reinterpret_cast<const long*>(kbase + static_cast<size_t>(e) * DI);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) bk[kk] = __builtin_nontemporal_load(src + kk);
-        ks = sbase[e];
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) bk[kk] = 0;
-        ks = 0.f;
-      }
+      for (int kk = 0; kk < KK; ++kk) bk[kk] = CSA_STREAM_LOAD(src + kk);
+      ks = sbase[e];
     };
-    auto compute = [&](int tile, const long (&bk)[KK], float ks) {
+    auto compute = [&](int t, const long (&bk)[KK], float ks) {
       f32x4 acc[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -115,27 +116,22 @@ __global__ __launch_bounds__(256) void index_score_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) part += wq[ht][i] * fmaxf(acc[ht][i], 0.f);
       part = wave_sum_xor(part, 48);
-      const int e = e0 + tile * 16 + c16;
+      const int e = e0 + (wave + 4 * t) * 16 + c16;
       if (g == 0 && e < e1) {
-        const float s = part * ks;
-        srow[e] = s;
-        if (hist) atomicAdd(&lhist[order_key(s) >> 20], 1u);
+        const float sc = part * ks;
+        srow[e] = sc;
+        if (hist) atomicAdd(&lhist[order_key(sc) >> 20], 1u);
       }
     };
-
-    // two tiles in flight per wave: tile j+4 loads while tile j computes
-    long k0[KK], k1[KK];
-    float s0 = 0.f, s1 = 0.f;
-    int tile = wave;
-    if (tile < ntile) load(tile, k0, s0);
-    while (tile < ntile) {
-      if (tile + 4 < ntile) load(tile + 4, k1, s1);
-      compute(tile, k0, s0);
-      tile += 4;
-      if (tile >= ntile) break;
-      if (tile + 4 < ntile) load(tile + 4, k0, s0);
-      compute(tile, k1, s1);
-      tile += 4;
+    constexpr int PD = 3;
+    long kb[PD][KK];
+    float ksv[PD];
+#pragma unroll
+    for (int t = 0; t < PD; ++t) load(t, kb[t], ksv[t]);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      compute(t, kb[t % PD], ksv[t % PD]);
+      if (t + PD < TPW) load(t + PD, kb[t % PD], ksv[t % PD]);
     }
   }
 
@@ -684,12 +680,18 @@ void index_topk_layout(IndexArgs& a, void* ws, int rows) {
   }
 }
 
+#ifndef CSA_SCORE_TPW
+#define CSA_SCORE_TPW 32
+#endif
+constexpr int kScoreTPW = CSA_SCORE_TPW;       // tiles of 16 entries per wave
+constexpr int kScoreChunk = 4 * kScoreTPW * 16;  // entries per workgroup
+
 template <int DI, int HT>
 static void launch_scores_t(const IndexArgs& a, int chunk, int nchunks, uint32_t* hist,
                             hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(nchunks) * static_cast<unsigned>(a.B * a.nq);
   ProfScope ps("index_score", s);
-  index_score_kernel<DI, HT><<<grid, 256, 0, s>>>(a.qi, a.qi_scale, a.wi, a.keys, a.kscale,
+  index_score_kernel<DI, HT, kScoreTPW><<<grid, 256, 0, s>>>(a.qi, a.qi_scale, a.wi, a.keys, a.kscale,
                                                   a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
                                                   chunk, a.scores, a.sstride, hist, nchunks);
 }
@@ -744,7 +746,7 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
     e = launch_fill_u32(a.hist, 0u, static_cast<size_t>(rows) * kHistBins, s);
     if (e != hipSuccess) return e;
   }
-  e = launch_scores(a, 1024, multi ? a.hist : nullptr, s);
+  e = launch_scores(a, kScoreChunk, multi ? a.hist : nullptr, s);
   if (e != hipSuccess) return e;
   if (!multi) {
     if (a.n_max <= kRowTopkMaxN) return launch_row_topk<256, kRowTopkMaxN>(a, rows, s);

@@ -55,7 +55,9 @@ struct MqaArgs {
   float* part;              // workspace partials
 };
 struct MqaPlan {
-  int heads_per_wg;   // 16 * waves
+  int head_tiles;     // 16-head tiles per workgroup
+  int slices;         // dim slices per head tile (waves per head tile)
+  int heads_per_wg;   // 16 * head_tiles
   int head_groups;
   int split_rows;     // rows of the key list per workgroup (multiple of 32)
   int n_splits;
