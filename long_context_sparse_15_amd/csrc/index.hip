@@ -408,6 +408,108 @@ __global__ __launch_bounds__(THREADS) void topk_row_kernel(
   }
 }
 
+// ============================================================================ sampled row top-k
+// One workgroup per row; thread t keeps the keys of entries t*PER .. t*PER+PER-1 in registers.
+//  1. every 16th key is a sample; the r-th largest sample (r a little above kk/16, with a margin
+//     of 4 standard deviations) is a lower threshold T_lo that almost surely has between kk and
+//     kCandCap keys at or above it;
+//  2. one block prefix sum over per-thread counts writes those candidates to LDS in index order;
+//  3. an exact radix select among the candidates finds the kk-th key and an index-ordered pass
+//     emits the selection in ascending order.
+// If the count misses [kk, kCandCap] (ties, adversarial data) the exact streaming select runs.
+template <int THREADS, int PER>
+__global__ __launch_bounds__(THREADS) void topk_sample_kernel(
+    const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
+  constexpr int NS = THREADS * (PER / 16);  // samples
+  __shared__ uint32_t s_samp[NS];
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_ckey[kCandCap];
+  __shared__ int32_t s_cidx[kCandCap];
+  __shared__ uint32_t s_tmp[THREADS / 64];
+  __shared__ int s_res[2];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  const int kk = min(k, n_vis);
+  int32_t* out = idx_out + static_cast<size_t>(row) * k;
+  float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
+  const float* srow = scores + static_cast<size_t>(row) * sstride;
+  if (n_vis <= k) {
+    for (int j = tid; j < k; j += THREADS) {
+      out[j] = j < n_vis ? j : -1;
+      if (sout) sout[j] = j < n_vis ? srow[j] : -INFINITY;
+    }
+    return;
+  }
+  const int e0 = tid * PER;
+  uint32_t kr[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    if (e0 + i + 3 < n_vis) {
+      const float4 v = *reinterpret_cast<const float4*>(srow + e0 + i);
+      kr[i] = order_key(v.x);
+      kr[i + 1] = order_key(v.y);
+      kr[i + 2] = order_key(v.z);
+      kr[i + 3] = order_key(v.w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kr[i + j] = (e0 + i + j < n_vis) ? order_key(srow[e0 + i + j]) : 0u;
+    }
+  }
+  // samples: keys at offsets 0, 16, 32, ... of each thread's segment (only visible entries)
+#pragma unroll
+  for (int i = 0; i < PER; i += 16) s_samp[tid * (PER / 16) + i / 16] = e0 + i < n_vis ? kr[i] : 0u;
+  // the sample array holds the visible samples first: thread segments are in entry order and the
+  // invisible tail is contiguous, so the number of visible samples is simply ceil(n_vis / 16)
+  const int ns = (n_vis + 15) / 16;
+  __syncthreads();
+  const float expect = static_cast<float>(kk) * static_cast<float>(ns) / static_cast<float>(n_vis);
+  int r = static_cast<int>(ceilf(expect + 4.f * sqrtf(expect) + 4.f));
+  if (r > ns) r = ns;
+  uint32_t Tlo;
+  int dummy;
+  auto sf = [&](int j) { return s_samp[j]; };
+  radix_select<THREADS>(sf, ns, r, s_hist, s_tmp, s_res, Tlo, dummy);
+  // count and compact the candidates (keys >= Tlo) in entry order
+  uint32_t own = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) own += (e0 + i < n_vis && kr[i] >= Tlo) ? 1u : 0u;
+  uint32_t cnt;
+  uint32_t off = block_excl_scan<THREADS>(own, s_tmp, &cnt);
+  if (cnt >= static_cast<uint32_t>(kk) && cnt <= static_cast<uint32_t>(kCandCap)) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (e0 + i < n_vis && kr[i] >= Tlo) {
+        s_ckey[off] = kr[i];
+        s_cidx[off] = e0 + i;
+        ++off;
+      }
+    }
+    __syncthreads();
+    uint32_t T;
+    int need_eq;
+    auto cf = [&](int j) { return s_ckey[j]; };
+    radix_select<THREADS>(cf, static_cast<int>(cnt), kk, s_hist, s_tmp, s_res, T, need_eq);
+    ordered_emit_fn<THREADS>(cf, static_cast<int>(cnt), T, need_eq, k, [&](int slot, int j) {
+      const int e = s_cidx[j];
+      out[slot] = e;
+      if (sout) sout[slot] = srow[e];
+    });
+    for (int j = kk + tid; j < k; j += THREADS) {
+      out[j] = -1;
+      if (sout) sout[j] = -INFINITY;
+    }
+    return;
+  }
+  uint32_t T;
+  int need_eq;
+  auto gk = [&](int e) { return order_key(srow[e]); };
+  radix_select<THREADS>(gk, n_vis, kk, s_hist, s_tmp, s_res, T, need_eq);
+  ordered_emit<THREADS>(gk, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+}
+
 // ============================================================================ multi-WG top-k
 // For long rows: the scoring kernel has accumulated a 4096-bin histogram of the top 12 key bits
 // per row.  Each collect workgroup takes kCollectChunk entries of one row, finds the threshold bin
@@ -749,8 +851,19 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
   e = launch_scores(a, kScoreChunk, multi ? a.hist : nullptr, s);
   if (e != hipSuccess) return e;
   if (!multi) {
-    if (a.n_max <= kRowTopkMaxN) return launch_row_topk<256, kRowTopkMaxN>(a, rows, s);
-    return launch_row_topk<1024, kRowTopkBigN>(a, rows, s);
+    if (a.n_max <= 4096) return launch_row_topk<256, kRowTopkMaxN>(a, rows, s);
+    if (a.n_max <= 16384) {
+      ProfScope ps("topk_sample", s);
+      topk_sample_kernel<256, 64><<<rows, 256, 0, s>>>(a.scores, a.sstride, a.n_entries, a.pos,
+                                                      a.nq, a.m, a.k, a.n_max, a.idx_out,
+                                                      a.score_out);
+      return hipGetLastError();
+    }
+    ProfScope ps("topk_sample", s);
+    topk_sample_kernel<1024, 32><<<rows, 1024, 0, s>>>(a.scores, a.sstride, a.n_entries, a.pos,
+                                                      a.nq, a.m, a.k, a.n_max, a.idx_out,
+                                                      a.score_out);
+    return hipGetLastError();
   }
   const int ncc = collect_chunks(a.n_max);
   const int scap = sel_cap(a.k);
