@@ -55,9 +55,9 @@ struct MqaArgs {
   float* part;              // workspace partials
 };
 struct MqaPlan {
-  int head_tiles;     // 16-head tiles per workgroup
-  int slices;         // dim slices per head tile (waves per head tile)
-  int heads_per_wg;   // 16 * head_tiles
+  int head_pairs;     // 32-head groups per workgroup (one wave each per dim slice)
+  int slices;         // dim slices (waves) per head pair
+  int heads_per_wg;   // 32 * head_pairs
   int head_groups;
   int split_rows;     // rows of the key list per workgroup (multiple of 32)
   int n_splits;

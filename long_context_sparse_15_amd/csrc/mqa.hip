@@ -6,21 +6,30 @@
 // core-attention output rotated back).  CSA attends the top-k selected entries, HCA every closed
 // entry j < floor((t+1)/m') ("HCA 的完整路径"); both add the window rows and share one softmax.
 //
-// Layout of the work: a workgroup owns one query row, 16*NW heads (16 per wave) and a span of
-// the query's key list (selected or visible entries, then window tokens).  Key rows are staged
-// through LDS 32 at a time and shared by all waves.  Per wave and 32-row tile:
-//   S^T[32 rows x 16 heads] = E . Q^T        (A = entry rows from LDS, B = query in registers)
-//   online softmax per head in the log2 domain (rows spread over the 4 lane groups)
-//   O^T[C dims x 16 heads] += E^T . P^T      (A = entry columns from LDS, B = P^T straight from
-//                                             the S^T accumulator layout, no LDS round trip)
-// With several spans per query each workgroup writes (max, sum, unnormalised O) and a combine
-// kernel merges them in a fixed order, adds the sink and normalises; with one span the same
-// epilogue runs in place.  Spans are fixed by the plan, not by timing, so results are
-// run-to-run deterministic.
+// Layout of the work.  A workgroup owns one query row, 32*HP heads and a span of the query's
+// key list (selected or visible entries, then window tokens).  Key rows are gathered 32 at a
+// time into LDS and shared by all waves; while one tile is computed the next two are in flight
+// in registers.  Wave (hp, s) owns heads hp*32..hp*32+31 and, for C = 512, the dim slice
+// s*256..s*256+255 (DS = 2 slices; one slice for C <= 256).  Per wave and tile, with 32x32x16
+// bf16 MFMAs:
+//   S^T[32 rows x 32 heads] = E . Q^T over the slice  (A = entry rows from LDS, B = q in regs);
+//   the DS slice partials are summed through LDS;
+//   online softmax per head in the log2 domain (lane l: head l%32, 16 of the 32 rows);
+//   O^T[slice dims x 32 heads] += E^T . P^T  (A = transposed LDS reads, B = P^T taken straight
+//   from the S^T accumulator layout).
+// LDS rows are unpadded with 16-byte chunks XOR-swizzled by row, which keeps both the row reads
+// of the S phase and the transposed reads of the PV phase free of bank conflicts.  With several
+// spans per query each workgroup writes (max, sum, unnormalised O) and a combine kernel merges
+// them in a fixed order, adds the sink and normalises; with one span the same epilogue runs in
+// place.  Spans are fixed by the plan, not by timing, so results are run-to-run deterministic.
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace csa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct MqaParams {
   const uint16_t* q;
@@ -39,12 +48,21 @@ struct MqaParams {
   float* lse_out;
 };
 
-template <int C>
-struct Tile {
-  static constexpr int kRows = 32;
-  static constexpr int kStride = C + 8;  // bf16 elements per LDS row (16-byte pad)
-  static constexpr int kElems = kRows * kStride;
-};
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Physical 16-byte chunk of logical chunk c in LDS row `row`: the low four bits of the chunk
+// index are XORed with a permutation of row % 16 (bits of row&3 and (row>>2)&3 swapped).
+// 16 consecutive rows at one logical chunk land in 16 distinct bank groups, and so do the
+// 4 rows x 4 chunks addressed by 32 lanes of a transposed read.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // RNE
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // Epilogue shared by the in-place path and the combine kernel: o (4 consecutive dims d0..d0+3
 // of one head) is rotated back by -t on the RoPE dims and stored as bf16.
@@ -63,37 +81,46 @@ __device__ __forceinline__ void store_out4(uint16_t* dst, float o0, float o1, fl
     }
   }
   uint2 v;
-  v.x = pack_bf16x2(o[0], o[1]);
-  v.y = pack_bf16x2(o[2], o[3]);
+  v.x = pack2(o[0], o[1]);
+  v.y = pack2(o[2], o[3]);
   *reinterpret_cast<uint2*>(dst) = v;
 }
 
-// One workgroup: one query row, HT head tiles of 16 heads, DS dim slices per head tile
-// (NW = HT*DS waves).  Wave (h, s) owns heads h*16..h*16+15 and dims s*C/DS..(s+1)*C/DS-1:
-// it computes the partial logits of its dim slice, the DS partials of a head tile are summed
-// through LDS (every slice then runs the identical softmax), and it accumulates the output
-// of its own dims only.  Rows are staged through a single LDS tile of 32 rows whose global
-// loads for the next tile are in flight (in registers) while the current tile is computed.
-template <int C, int HT, int DS>
-__global__ __launch_bounds__(64 * HT * DS) void mqa_kernel(MqaParams p) {
-  using TL = Tile<C>;
-  constexpr int NW = HT * DS;
-  constexpr int NT = 64 * NW;
-  constexpr int CH = C / 8;                             // 16-byte chunks per row
-  constexpr int LOADS = (TL::kRows * CH + NT - 1) / NT;
-  constexpr int CS = C / DS;                            // dims per slice
-  constexpr int KSL = CS / 32;                          // MFMA K steps of a slice
-  constexpr int DTL = CS / 16;                          // output dim tiles of a slice
+template <int C, int HP>
+struct MqaShape {
+  static constexpr int DS = C == 512 ? 2 : 1;   // dim slices
+  static constexpr int NW = HP * DS;            // waves
+  static constexpr int NT = 64 * NW;
+  static constexpr int CS = C / DS;             // dims per slice (256 or 128)
+  static constexpr int KK = CS / 16;            // S^T MFMA steps over the slice
+  static constexpr int DT = CS / 32;            // 32-dim output tiles of the slice
+  static constexpr int CPR = C / 8;             // 16-byte chunks per row
+  static constexpr int LOADS = 32 * CPR / NT;   // chunks per thread per tile
+  static constexpr int TILE = 32 * C;           // bf16 elements per LDS tile
+  static constexpr size_t lds_sx() { return 2 * TILE * sizeof(uint16_t); }
+  static constexpr size_t lds_freq() { return lds_sx() + (DS > 1 ? NW * 1024 * sizeof(float) : 0); }
+  static constexpr size_t lds_fixed() { return lds_freq() + (C / 2) * sizeof(float); }
+};
+
+template <int C, int HP>
+__global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p) {
+  using SH = MqaShape<C, HP>;
+  constexpr int DS = SH::DS, NW = SH::NW, NT = SH::NT, CS = SH::CS, KK = SH::KK, DT = SH::DT;
+  constexpr int CPR = SH::CPR, LOADS = SH::LOADS, TILE = SH::TILE;
+  static_assert(LOADS * NT == 32 * CPR, "tile chunks must split evenly over the threads");
+  static_assert(CPR == 64 || 64 % CPR == 0, "a load step covers whole rows");
+  static_assert(C / 2 <= NT, "one thread per RoPE frequency");
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* E = reinterpret_cast<uint16_t*>(smem);                          // [32][C+8]
-  float* SX = reinterpret_cast<float*>(smem + TL::kElems * sizeof(uint16_t));  // [NW][8][64]
-  int* s_idx = reinterpret_cast<int*>(SX + NW * 8 * 64);                     // [split_rows]
-  __shared__ long s_off[3][TL::kRows];
-  __shared__ int s_valid[3][TL::kRows];
+  uint16_t* E = reinterpret_cast<uint16_t*>(smem);                         // [2][32][C] swizzled
+  float* SX = reinterpret_cast<float*>(smem + SH::lds_sx());       // [NW][4][64][4]
+  float* s_freq = reinterpret_cast<float*>(smem + SH::lds_freq());  // [r/2] RoPE frequencies
+  int* s_idx = reinterpret_cast<int*>(smem + SH::lds_fixed());      // [split_rows]
 
   const int tid = threadIdx.x;
-  const int l = lane_id(), g = l >> 4, c16 = l & 15, wave = tid >> 6;
-  const int hsub = wave % HT, slice = wave / HT;
+  const int l = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hp = wave % HP, slice = wave / HP;
+  const int h = l >> 5, n32 = l & 31;
   // Work item w = (row, split); head groups of one work item are blocks 8 apart (same XCD).
   const int bid = blockIdx.x;
   const int w = (bid / (8 * p.head_groups)) * 8 + (bid & 7);
@@ -116,224 +143,343 @@ __global__ __launch_bounds__(64 * HT * DS) void mqa_kernel(MqaParams p) {
   const int R = n_sel + n_w;
   const int j0 = split * p.split_rows;
   const int j1 = min(R, j0 + p.split_rows);
-  const int head = (hg * HT + hsub) * 16 + c16;
+  const int head = (hg * HP + hp) * 32 + n32;
   const bool head_ok = head < p.n_heads;
   const int dbase = slice * CS;
 
-  // the span's selected entry indices go to LDS first, so that the tile loop issues no global
-  // load other than the row gathers (whose completion the compiler then tracks exactly)
-  if (p.idx) {
-    const int e1 = min(j1, n_sel);
-    for (int j = j0 + tid; j < e1; j += NT) s_idx[j - j0] = p.idx[static_cast<size_t>(row) * p.k + j];
+  // Row pointers of the tile starting at list row jt, computed by lanes 0..31 (one row each).
+  // Rows that are masked (past the span, an index outside the visible entries) point at the
+  // window row of token t, which every call holds, and are excluded through the valid mask,
+  // so every lane always issues its loads and no gathered value is ever undefined.
+  const uint16_t* const safe_row =
+      p.window + (static_cast<size_t>(b) * p.win_slots + (t % p.win_slots)) * C;
+  auto resolve = [&](int jt, bool idx_from_global, const uint16_t*& ptr, uint32_t& mask) {
+    const int j = jt + l;
+    const uint16_t* pr = safe_row;
+    bool ok = false;
+    if (l < 32 && j < j1) {
+      if (j < n_sel) {
+        const int e = p.idx ? (idx_from_global ? p.idx[static_cast<size_t>(row) * p.k + j]
+                                               : s_idx[j - j0])
+                            : j;
+        ok = e >= 0 && e < n_ent;
+        if (ok) pr = p.entries + (static_cast<size_t>(b) * p.n_max + e) * C;
+      } else {
+        const int u = wlo + (j - n_sel);
+        ok = true;
+        pr = p.window + (static_cast<size_t>(b) * p.win_slots + (u % p.win_slots)) * C;
+      }
+    }
+    ptr = pr;
+    mask = static_cast<uint32_t>(__ballot(ok));
+  };
+  auto gload = [&](const uint16_t* ptr, u32x4 (&st)[LOADS]) {
+    const uint64_t pv = reinterpret_cast<uint64_t>(ptr);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int ch = tid + i * NT;
+      const int cc = ch % CPR;
+      uint64_t rp;
+      if constexpr (CPR == 64) {  // one row per wave and load step: a wave-uniform pointer
+        const int rr = wave + i * NW;
+        const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv), rr);
+        const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv >> 32), rr);
+        rp = (static_cast<uint64_t>(hi) << 32) | lo;
+      } else {
+        const int rr = ch / CPR;
+        const uint32_t lo = __shfl(static_cast<uint32_t>(pv), rr, 64);
+        const uint32_t hi = __shfl(static_cast<uint32_t>(pv >> 32), rr, 64);
+        rp = (static_cast<uint64_t>(hi) << 32) | lo;
+      }
+      st[i] = *(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(rp) + cc);
+    }
+  };
+
+  // The tile count is odd (padded with a masked tile): the first tile is peeled, the rest run
+  // in pairs with static register stages and LDS buffers.  Every tile step prefetches two tiles
+  // ahead unconditionally (tiles past the span resolve to masked rows), so both register stages
+  // are always in flight in the same order.  The first two tiles are issued before anything
+  // else, with their indices read straight from global memory.
+  const int ntiles = j1 > j0 ? (((j1 - j0 + 31) / 32) | 1) : 0;
+  u32x4 stage0[LOADS], stage1[LOADS];
+  uint32_t mask0 = 0, mask1 = 0;
+  if (ntiles > 0) {
+    const uint16_t* p0;
+    const uint16_t* p1;
+    resolve(j0, true, p0, mask0);
+    resolve(j0 + 32, true, p1, mask1);
+    gload(p0, stage0);
+    gload(p1, stage1);
   }
 
-  // ---- query fragments of this slice (B operand of S^T), rotated at t on the RoPE dims
-  bf16x8 bq[KSL];
+  // All other global loads of the prologue follow right behind, so that their latencies overlap
+  // with the gathers': the query fragments, the sink, the RoPE frequencies and the span's
+  // selected entry indices (the last two go to LDS: the tile loop then issues no global load
+  // but the row gathers, and the epilogue does not read frequencies behind its own stores).
+  u32x4 qraw[KK];
   {
     const uint16_t* qrow = p.q + (static_cast<size_t>(row) * p.n_heads + (head_ok ? head : 0)) * C;
 #pragma unroll
-    for (int kk = 0; kk < KSL; ++kk) {
-      const int d0 = dbase + kk * 32 + g * 8;
-      u32x4 raw = head_ok ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0, 0, 0, 0};
-      if (d0 + 8 > C - p.r) {
+    for (int kk = 0; kk < KK; ++kk)
+      qraw[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qrow + dbase + kk * 16 + h * 8)
+                         : u32x4{0, 0, 0, 0};
+  }
+  const float sink_v = (p.sink && head_ok) ? p.sink[head] : 0.f;
+  const float freq_v = tid < (p.r >> 1) ? p.inv_freq[tid] : 0.f;  // r/2 <= C/2 <= NT
+  if (p.idx) {
+    constexpr int IPT = 8;  // indices per thread and pass, all loaded before any is stored
+    const int e1 = min(j1, n_sel);
+    for (int base = j0; base < e1; base += NT * IPT) {
+      int v[IPT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = d0 + 2 * j;
-          if (d >= C - p.r) {
-            float cs, sn;
-            rope_cos_sin(t, p.inv_freq[(d - (C - p.r)) >> 1], cs, sn);
-            const float x0 = bf16_to_f32(static_cast<uint16_t>(raw[j] & 0xffff));
-            const float x1 = bf16_to_f32(static_cast<uint16_t>(raw[j] >> 16));
-            raw[j] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
-          }
-        }
+      for (int i = 0; i < IPT; ++i) {
+        const int j = base + tid + i * NT;
+        v[i] = j < e1 ? p.idx[static_cast<size_t>(row) * p.k + j] : 0;
       }
-      bq[kk] = as_bf16x8(raw);
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        const int j = base + tid + i * NT;
+        if (j < e1) s_idx[j - j0] = v[i];
+      }
     }
   }
+  if (tid < (p.r >> 1)) s_freq[tid] = freq_v;
+  __syncthreads();  // s_idx, s_freq
 
-  f32x4 acc[DTL];
+  // ---- query fragments (B operand of S^T): head l%32, dims dbase + 16kk + 8h .. +7, rotated
+  // at t on the RoPE dims
+  bf16x8 bq[KK];
 #pragma unroll
-  for (int dt = 0; dt < DTL; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // m_ref: the reference maximum the probabilities are taken against (log2 domain); it moves
-  // only when a logit exceeds it by more than 8, so the accumulators are rarely rescaled and
-  // every probability stays below 2^8.
+  for (int kk = 0; kk < KK; ++kk) {
+    const int d0 = dbase + kk * 16 + h * 8;
+    u32x4 raw = qraw[kk];
+    if (d0 + 8 > C - p.r) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = d0 + 2 * j;
+        if (d >= C - p.r) {
+          float cs, sn;
+          rope_cos_sin(t, s_freq[(d - (C - p.r)) >> 1], cs, sn);
+          const float x0 = bf16_to_f32(static_cast<uint16_t>(raw[j] & 0xffff));
+          const float x1 = bf16_to_f32(static_cast<uint16_t>(raw[j] >> 16));
+          raw[j] = pack2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+        }
+      }
+    }
+    bq[kk] = as_bf16x8(raw);
+  }
+  // the query fragments are complete before the tile loop (otherwise the first use inside the
+  // loop would wait for every load in flight, on every iteration)
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(bq[kk]) : "memory");
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  // m_ref: the reference maximum the probabilities are taken against (log2 domain, scaled); it
+  // moves only when a scaled logit exceeds it by more than 8, so the accumulators are rarely
+  // rescaled and every probability stays below 2^8.
   float m_ref = -INFINITY, l_run = 0.f;
 
-  auto resolve = [&](int slot, int jt) {  // row offsets of the tile starting at list row jt
-    if (tid < TL::kRows) {
-      const int j = jt + tid;
-      long off = static_cast<long>(b) * p.n_max * C;  // safe in-bounds row for masked slots
-      int ok = 0;
-      if (j < j1) {
-        if (j < n_sel) {
-          const int e = p.idx ? s_idx[j - j0] : j;
-          ok = (e >= 0 && e < n_ent) ? 1 : 0;
-          off = (static_cast<long>(b) * p.n_max + (ok ? e : 0)) * C;
-        } else {
-          const int u = wlo + (j - n_sel);
-          ok = 1;
-          off = -1 - (static_cast<long>(b) * p.win_slots + (u % p.win_slots)) * C;  // window
-        }
-      }
-      s_off[slot][tid] = off;
-      s_valid[slot][tid] = ok;
-    }
-  };
-  // two register stages: while tile `it` is computed, tiles it+1 and it+2 are in flight
-  u32x4 stage0[LOADS], stage1[LOADS];
-  // Every lane always issues its loads (an invalid row reads a valid row of the cache and is
-  // zeroed when stored to LDS), so the instruction stream does not branch and the compiler waits
-  // for exactly the stage being stored while the other stage stays in flight.
-  static_assert(LOADS * NT == TL::kRows * CH, "tile chunks must split evenly over the threads");
-  auto gload = [&](int slot, u32x4 (&st)[LOADS]) {
+  // LDS byte offsets that do not change from tile to tile (the buffer, the upper 16-chunk block
+  // of a row and the second 16-row half are added as immediates)
+  uint32_t st_off[LOADS];  // store of load step i: row ch / CPR, chunk ch % CPR
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int ch = tid + i * NT;
-      const int rr = ch / CH, cc = ch % CH;
-      const long off = s_off[slot][rr];
-      const uint16_t* src = off >= 0 ? p.entries + off : p.window + (-1 - off);
-      st[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + cc);
-    }
-  };
-  auto sstore = [&](int slot, const u32x4 (&st)[LOADS]) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int ch = tid + i * NT;
-      const int rr = ch / CH, cc = ch % CH;
-      const u32x4 v = s_valid[slot][rr] ? st[i] : u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(E + rr * TL::kStride + cc * 8) = v;
-    }
-  };
-
-  const int ntiles = j1 > j0 ? (j1 - j0 + TL::kRows - 1) / TL::kRows : 0;
-  __syncthreads();  // s_idx
-  if (ntiles > 0) {
-    resolve(0, j0);
-    if (ntiles > 1) resolve(1, j0 + TL::kRows);
-    __syncthreads();
-    gload(0, stage0);
-    if (ntiles > 1) gload(1, stage1);
+  for (int i = 0; i < LOADS; ++i) {
+    const int ch = tid + i * NT;
+    const int rr = ch / CPR, cc = ch % CPR;
+    st_off[i] = static_cast<uint32_t>(rr * C + ((cc ^ swz(rr)) << 3)) * 2u;
   }
-  const int i0 = c16 >> 2, q4 = c16 & 3;
-  auto tile_step = [&](int it, u32x4 (&st)[LOADS]) {
-    const int slot = it % 3;
-    __syncthreads();  // every wave is done with the previous tile (E and SX)
-    sstore(slot, st);  // waits for this tile's loads only; the next tile's stay in flight
-    if (it + 2 < ntiles) resolve((it + 2) % 3, j0 + (it + 2) * TL::kRows);
-    __syncthreads();  // tile `it` is in LDS; offsets of tile it+2 are known
-    if (it + 2 < ntiles) gload((it + 2) % 3, st);
-    // partial S^T of this slice: rows rt*16 + c16 (A from LDS) x heads (B in registers)
-    f32x4 sacc[2];
+  // S phase (A operand): lane row n32, logical chunk (dbase>>3) + 2kk + h; the swizzle only
+  // touches the low four chunk bits, so kk >= 8 adds 256 bytes to the offset of kk - 8.
+  uint32_t sa_off[8];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* er = E + (rt * 16 + c16) * TL::kStride + dbase + g * 8;
+  for (int k8 = 0; k8 < 8; ++k8)
+    sa_off[k8] = static_cast<uint32_t>(n32 * C + (dbase & ~127) +
+                                       (((((dbase >> 3) & 15) + 2 * k8 + h) ^ swz(n32)) << 3)) * 2u;
+  // PV phase (transposed A operand): rows 16mm + 4h + i0 (first read) and +8 (second read),
+  // logical chunk (dbase>>3) + 4dt + 2(G&1) + q/2, element 4(q&1) in the chunk.  Row swizzles:
+  // (i0<<2)|h and (i0<<2)|(2+h), independent of mm; dt>>2 adds 256 bytes, mm adds 16 rows.
+  const int G = l >> 4, i0 = (l & 15) >> 2, q4 = l & 3;
+  uint32_t ta_off[4], tb_off[4];
 #pragma unroll
-      for (int kk = 0; kk < KSL; ++kk) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(er + kk * 32));
-        sacc[rt] = mfma_bf16_16x16x32(a, bq[kk], sacc[rt]);
+  for (int d3 = 0; d3 < 4; ++d3) {
+    const int low = 4 * d3 + 2 * (G & 1) + (q4 >> 1);
+    const int ra = 4 * h + i0, rb = ra + 8;
+    ta_off[d3] = static_cast<uint32_t>(ra * C + (dbase & ~127) + ((low ^ swz(ra)) << 3) +
+                                       4 * (q4 & 1)) * 2u;
+    tb_off[d3] = static_cast<uint32_t>(rb * C + (dbase & ~127) + ((low ^ swz(rb)) << 3) +
+                                       4 * (q4 & 1)) * 2u;
+  }
+
+  // tile step, front part: tile `it` (held in stage st) goes to LDS buffer buf, tile it+2 is
+  // resolved and its gathers issued into the same stage; returns tile it's valid mask
+  auto front = [&](int it, u32x4 (&st)[LOADS], uint32_t& mask, int buf) -> uint32_t {
+    if constexpr (DS == 1) __syncthreads();  // every wave is done with the buffer's last tile
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      *reinterpret_cast<u32x4*>(smem + st_off[i] + buf * TILE * 2) = st[i];
+    const uint32_t msk = mask;
+    const uint16_t* pn;
+    resolve(j0 + (it + 2) * 32, false, pn, mask);
+    __syncthreads();  // tile `it` is in LDS
+    gload(pn, st);
+    return msk;
+  };
+  // partial S^T of this wave's slice from LDS buffer buf
+  auto s_phase = [&](int buf) -> f32x16 {
+    const unsigned char* Eb = smem + buf * TILE * 2;
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 a =
+          as_bf16x8(*reinterpret_cast<const u32x4*>(Eb + sa_off[kk & 7] + (kk >> 3) * 256));
+      sacc = mfma_bf16_32x32x16(a, bq[kk], sacc);
+    }
+    return sacc;
+  };
+  // O^T += E^T . P^T on this slice's dims from LDS buffer buf.  K slots of lane half h in MFMA
+  // mm: rows 16mm + 4h + 0..3 and 16mm + 8 + 4h + 0..3, read transposed (within each 16-lane
+  // group, lane 4*i0+q addresses row base+i0, dims +4q..+4q+3 of a 4x16 block; lane j receives
+  // dim j of rows base..base+3).
+  auto pv_phase = [&](int buf, const bf16x8 (&bp)[2]) {
+    const unsigned char* Eb = smem + buf * TILE * 2;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const uint32_t imm = (dt >> 2) * 256 + mm * 16 * C * 2;
+        const bf16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Eb + ta_off[dt & 3] + imm));
+        const bf16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Eb + tb_off[dt & 3] + imm));
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[dt] = mfma_bf16_32x32x16(a, bp[mm], acc[dt]);
       }
     }
-    if constexpr (DS > 1) {  // sum the DS slice partials of this head tile
-      float* mine = SX + (wave * 8) * 64 + l;
+    // keep the output accumulators in the accumulation registers across tiles (only the rare
+    // rescale below moves them through VGPRs); the empty asm emits no instruction
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+    for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+a"(acc[dt]));
+  };
+  // slice sum, mask, online softmax of one tile; P^T (bf16, B operand of the PV MFMAs) to bp
+  auto softmax = [&](f32x16 sacc, uint32_t msk, bf16x8 (&bp)[2]) {
+    if constexpr (DS > 1) {  // sum the slice partials of this head pair
+      f32x4* mine = reinterpret_cast<f32x4*>(SX + wave * 1024);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mine[(rt * 4 + i) * 64] = sacc[rt][i];
+      for (int qq = 0; qq < 4; ++qq)
+        mine[qq * 64 + l] = f32x4{sacc[4 * qq], sacc[4 * qq + 1], sacc[4 * qq + 2], sacc[4 * qq + 3]};
       __syncthreads();
+      const f32x4* other = reinterpret_cast<const f32x4*>(SX + (hp + (1 - slice) * HP) * 1024);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x4 v = other[qq * 64 + l];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = 0.f;
-#pragma unroll
-          for (int s2 = 0; s2 < DS; ++s2) v += SX[((s2 * HT + hsub) * 8 + rt * 4 + i) * 64 + l];
-          sacc[rt][i] = v;
-        }
-    }
-    // online softmax (log2 domain); lane holds rows rt*16 + 4g + i for head c16
-    float s[2][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = rt * 16 + g * 4 + i;
-        const bool ok = s_valid[slot][rr] && (j0 + it * TL::kRows + rr < j1);
-        s[rt][i] = ok ? sacc[rt][i] * p.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, s[rt][i]);
+        for (int e = 0; e < 4; ++e) sacc[4 * qq + e] += v[e];
       }
-    tmax = wave_max_xor(tmax, 48);
-    const bool move = tmax > m_ref + 8.f;
-    if (__ballot(move)) {  // wave-uniform: some head's reference has to move up
-      const float m_new = move ? tmax : m_ref;
-      const float alpha = (m_new == m_ref) ? 1.f : exp2f(m_ref - m_new);
-      l_run *= alpha;
+    }
+    // element i of the accumulator holds row 8*(i/4) + 4h + i%4 of the tile, head l%32
+    if (msk != 0xffffffffu) {
 #pragma unroll
-      for (int dt = 0; dt < DTL; ++dt) acc[dt] *= alpha;
+      for (int i = 0; i < 16; ++i) {
+        const int rr = 8 * (i >> 2) + 4 * h + (i & 3);
+        if (!((msk >> rr) & 1u)) sacc[i] = -INFINITY;
+      }
+    }
+    float mx = sacc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;
+    const bool move = mx > m_ref + 8.f;
+    if (__ballot(move)) {  // wave-uniform: some head's reference has to move up
+      const float m_new = move ? mx : m_ref;
+      const float alpha = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
+      // acc *= alpha, element by element in place in the accumulation registers: written as
+      // asm so that the compiler cannot hoist the register copies out of this rare branch
+      // (they would hold 128 VGPRs through every tile)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float x = acc[dt][e], tmp;
+          asm volatile(
+              "v_accvgpr_read_b32 %1, %0\n\t"
+              "v_mul_f32 %1, %1, %2\n\t"
+              "v_accvgpr_write_b32 %0, %1"
+              : "+a"(x), "=&v"(tmp)
+              : "v"(alpha));
+          acc[dt][e] = x;
+        }
       m_ref = m_new;
     }
-    float pv[2][4];
+    const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
     float psum = 0.f;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int mm = 0; mm < 2; ++mm) {
+      u32x4 v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[rt][i] = (s[rt][i] == -INFINITY) ? 0.f : exp2f(s[rt][i] - m_ref);
-        psum += pv[rt][i];
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[8 * mm + 2 * e], p.scale_log2, -mu));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[8 * mm + 2 * e + 1], p.scale_log2, -mu));
+        psum += p0 + p1;
+        v[e] = pack2(p0, p1);
       }
-    l_run += psum;
-    u32x4 pr;
-    pr[0] = pack_bf16x2(pv[0][0], pv[0][1]);
-    pr[1] = pack_bf16x2(pv[0][2], pv[0][3]);
-    pr[2] = pack_bf16x2(pv[1][0], pv[1][1]);
-    pr[3] = pack_bf16x2(pv[1][2], pv[1][3]);
-    const bf16x8 bp = as_bf16x8(pr);
-    // O^T += E^T . P^T on this slice's dims.  K slots of lane group g: rows 4g..4g+3 and
-    // 16+4g..16+4g+3; the A operand comes from two LDS transpose reads (within each 16-lane
-    // group, lane 4*i0+q addresses row base+i0, dims +4q..+4q+3 of a 4x16 block; lane j gets
-    // dim j of rows base..base+3).
-    const uint16_t* ta = E + (g * 4 + i0) * TL::kStride + dbase + 4 * q4;
-    const uint16_t* tb = ta + 16 * TL::kStride;
-#pragma unroll
-    for (int dt = 0; dt < DTL; ++dt) {
-      const bf16x4 lo = lds_read_tr16(ta + dt * 16);
-      const bf16x4 hi = lds_read_tr16(tb + dt * 16);
-      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[dt] = mfma_bf16_16x16x32(a, bp, acc[dt]);
+      bp[mm] = as_bf16x8(v);
     }
+    l_run += psum;
   };
-  for (int it = 0; it < ntiles; it += 2) {  // unrolled by the two stages (static register indexing)
-    tile_step(it, stage0);
-    if (it + 1 < ntiles) tile_step(it + 1, stage1);
+
+  if (ntiles > 0) {
+    bf16x8 bpA[2], bpB[2];
+    {
+      const uint32_t msk = front(0, stage0, mask0, 0);
+      softmax(s_phase(0), msk, bpA);
+    }
+    // step it: S of tile it interleaves with PV of tile it-1 (independent MFMA chains on
+    // different LDS buffers), then the slice sum and softmax of tile it
+    for (int it = 1; it < ntiles; it += 2) {
+      uint32_t msk = front(it, stage1, mask1, 1);
+      f32x16 sacc = s_phase(1);
+      pv_phase(0, bpA);
+      softmax(sacc, msk, bpB);
+      msk = front(it + 1, stage0, mask0, 0);
+      sacc = s_phase(0);
+      pv_phase(1, bpB);
+      softmax(sacc, msk, bpA);
+    }
+    pv_phase(0, bpA);  // the last tile (even index)
   }
 
-  const float l_tot = wave_sum_xor(l_run, 48);
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const size_t orow = static_cast<size_t>(row) * p.n_heads + head;
   if (!head_ok) return;
+  // output element i of acc[dt]: head l%32, dim dbase + 32dt + 8*(i/4) + 4h + i%4
   if (p.n_splits == 1) {
-    const float a2 = p.sink ? p.sink[head] * kLog2e : -INFINITY;
+    const float a2 = p.sink ? sink_v * kLog2e : -INFINITY;
     const float M = fmaxf(m_ref, a2);
     const float f = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - M);
     const float den = l_tot * f + ((a2 == -INFINITY) ? 0.f : exp2f(a2 - M));
     const float inv = den > 0.f ? f / den : 0.f;
     uint16_t* orow_p = p.out + orow * C;
 #pragma unroll
-    for (int dt = 0; dt < DTL; ++dt) {
-      const int d0 = dbase + dt * 16 + g * 4;
-      store_out4(orow_p + d0, acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv,
-                 acc[dt][3] * inv, d0, C, p.r, t, p.inv_freq);
-    }
-    if (p.lse_out && g == 0 && slice == 0)
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = dbase + dt * 32 + g4 * 8 + 4 * h;
+        store_out4(orow_p + d0, acc[dt][4 * g4] * inv, acc[dt][4 * g4 + 1] * inv,
+                   acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv, d0, C, p.r, t, s_freq);
+      }
+    if (p.lse_out && h == 0 && slice == 0)
       p.lse_out[orow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     float* prow = p.part + ((static_cast<size_t>(row) * p.n_splits + split) * p.n_heads + head) *
                                (C + 4);
 #pragma unroll
-    for (int dt = 0; dt < DTL; ++dt)
-      *reinterpret_cast<f32x4*>(prow + dbase + dt * 16 + g * 4) = acc[dt];
-    if (g == 0 && slice == 0) {
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(prow + dbase + dt * 32 + g4 * 8 + 4 * h) =
+            f32x4{acc[dt][4 * g4], acc[dt][4 * g4 + 1], acc[dt][4 * g4 + 2], acc[dt][4 * g4 + 3]};
+    if (h == 0 && slice == 0) {
       prow[C] = m_ref;
       prow[C + 1] = l_tot;
     }
@@ -353,8 +499,8 @@ __global__ __launch_bounds__(64) void mqa_combine_kernel(MqaParams p) {
   for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, base[s * sstride + C]);
   float den = (p.sink && M != -INFINITY) ? exp2f(p.sink[head] * kLog2e - M) : 0.f;
   float lsum = 0.f;
-  constexpr int PER = C / 64;  // dims per thread (multiple of 4 for C >= 256; C=128 -> 2)
-  float o[PER > 0 ? PER : 1];
+  constexpr int PER = C / 64;  // dims per thread (2, 4 or 8)
+  float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
   for (int s = 0; s < p.n_splits; ++s) {
@@ -368,7 +514,9 @@ __global__ __launch_bounds__(64) void mqa_combine_kernel(MqaParams p) {
   den += lsum;
   const float inv = den > 0.f ? 1.f / den : 0.f;
   uint16_t* dst = p.out + (static_cast<size_t>(row) * p.n_heads + head) * C;
-  // each thread owns PER consecutive dims starting at l*PER (even, so RoPE pairs stay local)
+  // each thread owns PER consecutive dims starting at l*PER (even, so RoPE pairs stay local);
+  // all rotations happen before the first store
+  uint32_t packed[PER / 2];
 #pragma unroll
   for (int i = 0; i < PER; i += 2) {
     const int d = l * PER + i;
@@ -380,44 +528,54 @@ __global__ __launch_bounds__(64) void mqa_combine_kernel(MqaParams p) {
       x0 = y0;
       x1 = y1;
     }
-    *reinterpret_cast<uint32_t*>(dst + d) = pack_bf16x2(x0, x1);
+    packed[i / 2] = pack2(x0, x1);
   }
+#pragma unroll
+  for (int i = 0; i < PER; i += 2) *reinterpret_cast<uint32_t*>(dst + l * PER + i) = packed[i / 2];
   if (p.lse_out && l == 0)
     p.lse_out[rh] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- planning and launch
-// ---------------------------------------------------------------- planning and launch
 static int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
-// Shapes: many query rows (prefill) -> 64 heads x 2 slices per workgroup and no spans; few rows
-// over long dense lists (HCA decode) -> 64 heads x 2 slices, spans of >= 512 rows; few rows
-// over short sparse lists (CSA decode) -> 16 heads x 4 slices per workgroup (the head groups of
-// a row share the gathered rows through L2) and spans chosen to fill the chip.
+// Heads: up to 64 per workgroup (two 32-head pairs), more as separate head groups whose
+// workgroups sit on the same XCD and share the gathered rows through its L2.  Spans: chosen by
+// a small cost model with one resident workgroup of four waves per CU (fewer waves: several):
+// rounds of workgroups x (tiles x per-tile time + fixed cost), plus writing and re-reading the
+// fp32 partials when a query's list is split.
 MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list) {
   MqaPlan pl;
-  const int tiles = (n_heads + 15) / 16;
-  const bool many_rows = rows >= 1024;
-  const bool dense_long = max_list > 4096;
-  if (many_rows || dense_long) {
-    pl.head_tiles = tiles < 4 ? tiles : 4;
-    if (pl.head_tiles == 3) pl.head_tiles = 4;
-    pl.slices = 2;
-  } else {
-    pl.head_tiles = 1;
-    pl.slices = c >= 256 ? 4 : 2;
-  }
-  pl.heads_per_wg = 16 * pl.head_tiles;
+  pl.head_pairs = 2;  // one instantiation: 64 heads (fewer heads leave waves idle)
+  pl.slices = c == 512 ? 2 : 1;
+  pl.heads_per_wg = 32 * pl.head_pairs;
   pl.head_groups = (n_heads + pl.heads_per_wg - 1) / pl.heads_per_wg;
-  const long base = static_cast<long>(rows) * pl.head_groups;
-  const long target = dense_long ? 256 : 256;
-  const int min_rows = dense_long ? 512 : 128;
-  int splits = base >= target ? 1 : static_cast<int>((target + base - 1) / base);
-  int sr = round_up((max_list + splits - 1) / splits, 32);
-  if (sr < min_rows) sr = round_up(min_rows < max_list ? min_rows : max_list, 32);
-  pl.split_rows = sr;
-  pl.n_splits = (max_list + sr - 1) / sr;
-  if (pl.n_splits < 1) pl.n_splits = 1;
+  const int waves = pl.head_pairs * pl.slices;
+  const double slots = 256.0 * (waves >= 4 ? 1 : 4 / waves);
+  const double base = static_cast<double>(rows) * pl.head_groups;
+  const int list = max_list > 0 ? max_list : 1;
+  // measured on MI355X: a 32-row tile step, the per-workgroup fixed cost, the partials' round
+  // trip and the combine launch
+  const double t_tile = 1.0e-6 * (c >= 256 ? 1.0 : 0.6), t_fixed = 5.0e-6, bw = 5.0e12,
+               t_comb = 3.0e-6;
+  double best = 1e30;
+  pl.split_rows = round_up(list, 32);
+  pl.n_splits = 1;
+  for (int s = 1; s <= 64; ++s) {
+    const int sr = round_up((list + s - 1) / s, 32);
+    const int ns = (list + sr - 1) / sr;
+    if (ns != s) continue;
+    const int tiles = (sr / 32) | 1;  // the kernel pads to an odd tile count
+    const double rounds = std::ceil(base * ns / slots);
+    double tm = rounds * (tiles * t_tile + t_fixed);
+    if (ns > 1) tm += 2.0 * rows * ns * static_cast<double>(n_heads) * (c + 4) * 4.0 / bw + t_comb;
+    if (tm < best * 0.97) {
+      best = tm;
+      pl.split_rows = sr;
+      pl.n_splits = ns;
+    }
+    if (sr <= 32) break;
+  }
   return pl;
 }
 
@@ -426,13 +584,14 @@ size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c) {
   return static_cast<size_t>(rows) * p.n_splits * n_heads * (c + 4) * sizeof(float);
 }
 
-template <int C, int HT, int DS>
+template <int C, int HP>
 static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
-  const size_t lds = Tile<C>::kElems * sizeof(uint16_t) + HT * DS * 8 * 64 * sizeof(float) +
-                     (prm.idx ? static_cast<size_t>(prm.split_rows) * sizeof(int) : 0);
+  using SH = MqaShape<C, HP>;
+  const size_t lds =
+      SH::lds_fixed() + (prm.idx ? static_cast<size_t>(prm.split_rows) * sizeof(int) : 0);
   static size_t attr = 0;
   if (attr < lds) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_kernel<C, HT, DS>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_kernel<C, HP>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
@@ -443,7 +602,7 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((q.n_work + 7) / 8 * 8) * prm.head_groups;
   {
     ProfScope ps(prm.idx ? "mqa_sparse" : "mqa_dense", s);
-    mqa_kernel<C, HT, DS><<<grid, 64 * HT * DS, lds, s>>>(q);
+    mqa_kernel<C, HP><<<grid, SH::NT, lds, s>>>(q);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || prm.n_splits == 1) return e;
@@ -454,10 +613,7 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
 
 template <int C>
 static hipError_t launch_c(const MqaParams& prm, const MqaPlan& pl, int rows, hipStream_t s) {
-  if (pl.head_tiles == 1 && pl.slices == 4) return launch_t<C, 1, 4>(prm, rows, s);
-  if (pl.head_tiles == 1 && pl.slices == 2) return launch_t<C, 1, 2>(prm, rows, s);
-  if (pl.head_tiles == 2 && pl.slices == 2) return launch_t<C, 2, 2>(prm, rows, s);
-  if (pl.head_tiles == 4 && pl.slices == 2) return launch_t<C, 4, 2>(prm, rows, s);
+  if (pl.head_pairs == 2) return launch_t<C, 2>(prm, rows, s);
   return hipErrorInvalidValue;
 }
 
