@@ -52,6 +52,28 @@ def _score_kernel_bytes(w, n_vis):
     return n_vis * (w.d_I + 4) + w.H_I * (w.d_I + 8)
 
 
+def _profiled_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (profiles/<kernel>_<workload>_counters.txt: FETCH_SIZE and WRITE_SIZE scaled by a plain-copy
+    calibration), or None when there is none or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "%s_%s_counters.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.strip().split(":", 1)
+            vals[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("index.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "long_context_sparse_15_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("source_sha256") != h.hexdigest() or vals.get("kernel") != kernel:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
 def _time_steps(step, K, W, stream):
     import torch
     for i in range(W):
@@ -130,8 +152,9 @@ def decode_workload(name, K, W, rotate):
     launches, tot = prof[kname]
     kdur = tot / launches
     ach = kbytes / (kdur / 1e3) / 1e9
+    traffic = _profiled_traffic(kname, name) if kname == "index_score" else None
     res["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                       "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                       "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                        "bytes_per_launch": kbytes, "avg_launch_ms": kdur}
     del copies, caches, ws
     torch.cuda.empty_cache()
