@@ -23,6 +23,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),
 ]
+# Per-file flags.  The indexer's MFMA results feed VALU epilogues directly, so they are produced
+# in VGPRs; the attention kernels keep their long-lived accumulators in AGPRs.
+FILE_FLAGS = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -41,7 +44,7 @@ def build(jobs=4, verbose=False):
     for s in SOURCES:
         o = os.path.join(BUILD, s.replace(".hip", ".o"))
         objs.append(o)
-        cmds.append([HIPCC] + FLAGS + ["-c", os.path.join(SRC, s), "-o", o])
+        cmds.append([HIPCC] + FLAGS + FILE_FLAGS.get(s, []) + ["-c", os.path.join(SRC, s), "-o", o])
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():

@@ -144,6 +144,160 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     }
   }
 }
+// ============================================================================ scoring, many rows
+// Prefill: many query rows share the keys, so scoring is a batched product over heads.  A
+// workgroup takes 16 consecutive query rows of one sequence and holds their indexer queries
+// (all heads, E4M3 codes) in LDS.  Each wave takes groups of 64 entries, four 16-entry blocks
+// held in registers as A operands, and for every head h reads the 16 queries' codes of h once
+// (B operand) for four 16x16x128 MFMAs, one per block (K = 128: one head's whole product):
+//   D[entry][query] = K_e . Q_{q,h}                    (raw codes, exact in fp32)
+//   acc[entry][query] += max(D, 0) * (w_{q,h} sq_{q,h})
+// then multiplies by the entry scale sk_e.  The next group's keys and scales are loaded while
+// the current one is computed.
+constexpr int kGemmQ = 16;   // query rows per workgroup
+constexpr int kGemmWaves = 8;  // two waves per SIMD: one's epilogue overlaps another's MFMAs
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kGemmH = 64;   // largest head count held in LDS
+constexpr int kGemmDI = 128;
+constexpr size_t kGemmLds = kGemmH * kGemmQ * kGemmDI + kGemmH * kGemmQ * 4 + kGemmQ * 4;
+
+// 16-byte chunk swizzle of the query rows in LDS: the 16 queries read at one chunk position
+// land in 16 distinct bank groups (rows are 128 bytes apart).
+__device__ __forceinline__ int qswz(int q) { return (q >> 1) & 7; }
+
+__global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
+    const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
+    const float* __restrict__ wi, const uint8_t* __restrict__ keys,
+    const float* __restrict__ kscale, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ pos, int nq, int n_max, int H_I, int m, int qtiles,
+    float* __restrict__ scores, int sstride) {
+  constexpr int DI = kGemmDI;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint8_t* s_q = smem;                                                   // [h][q][128] swizzled
+  float* s_c = reinterpret_cast<float*>(smem + kGemmH * kGemmQ * DI);    // [h][q]: w * sq
+  int* s_nv = reinterpret_cast<int*>(s_c + kGemmH * kGemmQ);             // [q]: visible entries
+  // causal rows: the last query tiles carry the most entries and are dispatched first
+  const int b = blockIdx.x / qtiles;
+  const int t0 = (qtiles - 1 - blockIdx.x % qtiles) * kGemmQ;
+  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
+  const int g = l >> 4, c16 = l & 15;
+
+  for (int ch = tid; ch < H_I * kGemmQ * 8; ch += kGemmThreads) {
+    const int h = ch / (kGemmQ * 8), q = (ch / 8) % kGemmQ, c = ch % 8;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (t0 + q < nq)
+      v = *reinterpret_cast<const u32x4*>(
+          qi + (static_cast<size_t>(b * nq + t0 + q) * H_I + h) * DI + c * 16);
+    *reinterpret_cast<u32x4*>(s_q + (h * kGemmQ + q) * DI + ((c ^ qswz(q)) << 4)) = v;
+  }
+  for (int i = tid; i < H_I * kGemmQ; i += kGemmThreads) {
+    const int h = i / kGemmQ, q = i % kGemmQ;
+    const size_t rh = static_cast<size_t>(b * nq + t0 + q) * H_I + h;
+    s_c[i] = (t0 + q < nq) ? wi[rh] * qi_scale[rh] : 0.f;
+  }
+  if (tid < kGemmQ)
+    s_nv[tid] = (t0 + tid < nq) ? visible(n_entries, pos, b * nq + t0 + tid, nq, m, n_max) : 0;
+  __syncthreads();
+  int nv_max = 0;
+#pragma unroll
+  for (int q = 0; q < kGemmQ; ++q) nv_max = max(nv_max, s_nv[q]);
+  const int my_nv = s_nv[c16];
+  const int ngroups = (nv_max + 63) / 64;
+  if (wave >= ngroups) return;
+
+  const uint8_t* kb = keys + static_cast<size_t>(b) * n_max * DI + g * 32;
+  const float* sb = kscale + static_cast<size_t>(b) * n_max;
+  float* srow = scores + static_cast<size_t>(b * nq + t0 + c16) * sstride;
+  const bool row_ok = t0 + c16 < nq;
+  // A operands of group G: entry G*64 + 16blk + c16 (clamped into the visible range), bytes
+  // 32g..32g+31; entry scales of the 4 entries G*64 + 16blk + 4g + i this lane's D holds
+  auto load = [&](int G, i32x8 (&a)[4], f32x4 (&ks)[4]) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int e = min(G * 64 + blk * 16 + c16, nv_max - 1);
+      const u32x4* src = reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(e) * DI);
+      const u32x4 lo = src[0], hi = src[1];
+      a[blk] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                     static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                     static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ks[blk][i] = sb[min(G * 64 + blk * 16 + 4 * g + i, nv_max - 1)];
+    }
+  };
+  const uint8_t* qb = s_q + c16 * DI;
+  const int ch0 = ((2 * g) ^ qswz(c16)) << 4, ch1 = ((2 * g + 1) ^ qswz(c16)) << 4;
+  i32x8 a[4], an[4];
+  f32x4 ks[4], ksn[4];
+  load(wave, a, ks);
+  for (int G = wave; G < ngroups; G += kGemmWaves) {
+    load(min(G + kGemmWaves, ngroups - 1), an, ksn);  // always issued: same order each iteration
+    f32x4 acc[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) acc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // heads are software-pipelined: the four MFMAs of head h+1 are issued before the epilogue
+    // of head h reads its results, and each head's query codes are read from LDS one step
+    // before its MFMAs
+    auto readq = [&](int h, i32x8& bq, float& ch) {
+      const uint8_t* qh = qb + min(h, H_I - 1) * kGemmQ * DI;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(qh + ch0);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(qh + ch1);
+      bq = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                 static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                 static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+      ch = s_c[min(h, H_I - 1) * kGemmQ + c16];
+    };
+    auto issue = [&](const i32x8& bq, f32x4 (&d)[4]) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+        d[blk] = mfma_fp8_16x16x128(a[blk], bq, f32x4{0.f, 0.f, 0.f, 0.f});
+    };
+    // acc += max(d, 0) * ch; the ReLU is a signed integer max of the float's bits with 0
+    // (negative floats have negative integer patterns), one instruction
+    auto epi = [&](const f32x4 (&d)[4], float ch) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[blk][i] = fmaf(__int_as_float(max(__float_as_int(d[blk][i]), 0)), ch, acc[blk][i]);
+    };
+    f32x4 dA[4], dB[4];
+    float cA, cB, cc, cn;
+    i32x8 bc, bn;
+    readq(0, bc, cc);
+    issue(bc, dA);
+    cA = cc;
+    readq(1, bc, cc);
+    int h = 1;
+    for (; h + 1 < H_I; h += 2) {
+      readq(h + 1, bn, cn);
+      issue(bc, dB);  // head h
+      cB = cc;
+      epi(dA, cA);
+      readq(h + 2, bc, cc);
+      issue(bn, dA);  // head h + 1
+      cA = cn;
+      epi(dB, cB);
+    }
+    if (h < H_I) {
+      issue(bc, dB);
+      epi(dA, cA);
+      epi(dB, cc);
+    } else {
+      epi(dA, cA);
+    }
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int e = G * 64 + blk * 16 + 4 * g;
+      if (row_ok && e < my_nv)
+        *reinterpret_cast<f32x4*>(srow + e) =
+            f32x4{acc[blk][0] * ks[blk][0], acc[blk][1] * ks[blk][1], acc[blk][2] * ks[blk][2],
+                  acc[blk][3] * ks[blk][3]};
+      a[blk] = an[blk];
+      ks[blk] = ksn[blk];
+    }
+  }
+}
+
 // ============================================================================ block helpers
 // Block-wide search over a histogram of `nbins` counts for the bin d with
 //   sum(bins > d) < remaining <= sum(bins >= d).
@@ -840,6 +994,29 @@ static hipError_t launch_row_topk(const IndexArgs& a, int rows, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Rows scored as a product over heads (16 query rows of a sequence per workgroup) when every
+// sequence brings at least 16 query rows and the heads fit the LDS tile.
+static bool use_gemm_scores(const IndexArgs& a) {
+  return a.nq >= kGemmQ && a.d_I == kGemmDI && a.H_I <= kGemmH;
+}
+
+static hipError_t launch_gemm_scores(const IndexArgs& a, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(index_gemm_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(kGemmLds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int qtiles = (a.nq + kGemmQ - 1) / kGemmQ;
+  ProfScope ps("index_score", s);
+  index_gemm_kernel<<<static_cast<unsigned>(a.B) * qtiles, kGemmThreads, kGemmLds, s>>>(
+      a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
+      qtiles, a.scores, a.sstride);
+  return hipGetLastError();
+}
+
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
   const int rows = a.B * a.nq;
   const bool multi = index_use_multi(rows, a.n_max);
@@ -848,7 +1025,8 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
     e = launch_fill_u32(a.hist, 0u, static_cast<size_t>(rows) * kHistBins, s);
     if (e != hipSuccess) return e;
   }
-  e = launch_scores(a, kScoreChunk, multi ? a.hist : nullptr, s);
+  e = (!multi && use_gemm_scores(a)) ? launch_gemm_scores(a, s)
+                                     : launch_scores(a, kScoreChunk, multi ? a.hist : nullptr, s);
   if (e != hipSuccess) return e;
   if (!multi) {
     if (a.n_max <= 4096) return launch_row_topk<256, kRowTopkMaxN>(a, rows, s);

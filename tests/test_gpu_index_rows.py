@@ -1,0 +1,81 @@
+"""GPU parity of csa_index_topk with many query rows per sequence (the prefill shape: rows are
+scored 16 at a time as a product over indexer heads) against the oracle's float64 scores:
+ragged row counts, fewer heads than the LDS tile holds, partially filled caches, rows with
+nothing visible, and arbitrary positions."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_15_amd as csa
+import oracle as O
+from synth import inputs as S
+from gpu_common import DEV, check_close, check_selection, dev, say, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, B, nq, n_max, n_ent, H_I, d_I, pos):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = {
+        "ikeys": S.e4m3_normalish(rng, (B, n_max, d_I)),
+        "iscale": (rng.uniform(0.5, 1.5, size=(B, n_max)) / 16).astype(np.float32),
+        "qi": S.e4m3_normalish(rng, (B, nq, H_I, d_I)),
+        "qi_scale": (rng.uniform(0.5, 1.5, size=(B, nq, H_I)) / 16).astype(np.float32),
+        "wi": (rng.standard_normal((B, nq, H_I), dtype=np.float32) / 8),
+        "n_entries": np.asarray(n_ent, dtype=np.int32),
+        "pos": None if pos is None else np.asarray(pos, dtype=np.int32).reshape(B, nq),
+    }
+    return x
+
+
+def _run(x, B, nq, n_max, H_I, d_I, k, m=4):
+    inv = dev(S.rope_inv_freq(64, 160000.0))
+    cfg = csa.make_config(csa.MODE_CSA, m, 64, 512, 64, inv, top_k=k, n_win=128, idx_heads=H_I,
+                          idx_dim=d_I)
+    d = {key: dev(x[key]) for key in ("ikeys", "iscale", "qi", "qi_scale", "wi", "n_entries")}
+    pos = dev(x["pos"]) if x["pos"] is not None else None
+    entries = torch.zeros((B, n_max, 512), dtype=torch.int16, device=DEV)
+    window = torch.zeros((B, 128, 512), dtype=torch.int16, device=DEV)
+    cache = csa.make_cache(n_max, 128, entries, window, d["n_entries"], idx_keys=d["ikeys"],
+                           idx_scale=d["iscale"])
+    idx = torch.full((B, nq, k), -7, dtype=torch.int32, device=DEV)
+    sc = torch.empty((B, nq, k), dtype=torch.float32, device=DEV)
+    ws = workspace(csa.workspace_size(cfg, csa.OP_INDEX_TOPK, B, nq, n_max))
+    csa.index_topk(cfg, d["qi"], d["qi_scale"], d["wi"], cache, pos, idx, ws, score_out=sc)
+    torch.cuda.synchronize()
+    idx_h, sc_h = idx.cpu().numpy(), sc.cpu().numpy()
+    for b in range(B):
+        for q in range(nq):
+            t = int(x["pos"][b, q]) if x["pos"] is not None else q
+            n_vis = O.visible_entries(t, m, int(x["n_entries"][b]))
+            ref = O.index_scores(x["qi"][b, q], x["qi_scale"][b, q], x["wi"][b, q],
+                                 x["ikeys"][b], x["iscale"][b], n_vis)
+            what = "seq %d row %d (t=%d, n_vis=%d)" % (b, q, t, n_vis)
+            check_selection(idx_h[b, q], ref, k, what)
+            kk = min(k, n_vis)
+            sel = idx_h[b, q, :kk]
+            check_close(sc_h[b, q, :kk], ref[sel], what + " scores",
+                        atol=1e-5 * max(1.0, np.abs(ref).max(initial=0.0)), rtol=1e-5)
+            assert np.all(np.isneginf(sc_h[b, q, kk:])), what + " padding scores"
+
+
+@pytest.mark.parametrize("case", [
+    # (seed, B, nq, n_max, n_entries, H_I, k, positions): 100 rows = 6 tiles of 16 + 4
+    (11, 2, 100, 2000, [2000, 1300], 64, 64, "spread"),
+    # 40 heads (not a multiple of 16), 33 rows, k larger than some rows' visible entries
+    (12, 1, 33, 1500, [1500], 40, 128, "spread"),
+    # positions 0..47: early rows see no entry, the rest only a few
+    (13, 1, 48, 512, [512], 64, 16, "prefix"),
+    # one full tile of 16 rows over long rows (several 64-entry groups per wave)
+    (14, 1, 16, 9000, [8800], 64, 256, "spread"),
+])
+def test_index_rows_parity(case):
+    seed, B, nq, n_max, n_ent, H_I, k, posmode = case
+    say("index rows", case)
+    if posmode == "spread":
+        rng = np.random.Generator(np.random.PCG64(seed + 100))
+        pos = rng.integers(0, 4 * n_max + 8, size=(B, nq))
+    else:  # positions 0..nq-1
+        pos = np.tile(np.arange(nq), (B, 1))
+    x = _inputs(seed, B, nq, n_max, n_ent, H_I, 128, pos)
+    _run(x, B, nq, n_max, H_I, 128, k)
