@@ -511,6 +511,78 @@ __device__ void radix_select(KeyFn key, int n, int kk, uint32_t* hist /*4096*/, 
   need_eq = static_cast<int>(remaining);
 }
 
+// One histogram pass of radix select: counts keys matching (prefix, mask) into nb bins of the
+// bits at `shift`, then finds the crossing bin of `remaining` (s_res[0], s_res[1]); returns the
+// crossing bin's count.
+template <int THREADS, typename KeyFn>
+__device__ uint32_t radix_pass(KeyFn key, int n, uint32_t prefix, uint32_t mask, int shift,
+                               int nb, uint32_t remaining, uint32_t* hist, uint32_t* s_tmp,
+                               int* s_res) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nb; i += THREADS) hist[i] = 0;
+  __syncthreads();
+  for (int e = tid; e < n; e += THREADS) {
+    const uint32_t kv = key(e);
+    if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & (nb - 1)], 1u);
+  }
+  __syncthreads();
+  block_find_crossing<THREADS>(hist, nb, remaining, s_tmp, s_res);
+  return hist[s_res[0]];
+}
+
+// Exact kk-th largest key (T) among n keys that all lie in [lo, hi], and how many keys equal
+// to T are taken (need_eq).  One 12-bit histogram over the bits just below the common prefix of
+// lo and hi (so the bins split the keys' actual range); if the crossing bin holds at most 64
+// keys they are gathered into a small list and ranked by pairwise comparison in one wave,
+// otherwise the full radix select runs.
+template <int THREADS, typename KeyFn>
+__device__ void select_kth(KeyFn key, int n, int kk, uint32_t lo, uint32_t hi,
+                           uint32_t* hist /*4096*/, uint32_t* s_tmp, int* s_res, uint32_t& T,
+                           int& need_eq) {
+  __shared__ uint32_t s_bin[64];
+  __shared__ uint32_t s_nb;
+  const int tid = threadIdx.x;
+  const uint32_t diff = lo ^ hi;
+  const int top = diff ? 32 - __clz(diff) : 0;  // bits below the common prefix
+  const int shift = top > 12 ? top - 12 : 0;
+  const uint32_t pmask = top >= 32 ? 0u : ~((1u << top) - 1u);
+  const uint32_t prefix = lo & pmask;
+  const uint32_t c1 = radix_pass<THREADS>(key, n, prefix, pmask, shift, 4096,
+                                          static_cast<uint32_t>(kk), hist, s_tmp, s_res);
+  const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
+  const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
+  __syncthreads();
+  if (c1 > 64) {
+    radix_select<THREADS>(key, n, kk, hist, s_tmp, s_res, T, need_eq);
+    return;
+  }
+  if (tid == 0) s_nb = 0;
+  __syncthreads();
+  for (int e = tid; e < n; e += THREADS) {
+    const uint32_t kv = key(e);
+    if ((kv & pmask) == prefix && ((kv >> shift) & 4095u) == d1) s_bin[atomicAdd(&s_nb, 1u)] = kv;
+  }
+  __syncthreads();
+  if (tid < 64) {  // wave 0: rank the bin's keys; the r1-th largest is T
+    const int nbk = static_cast<int>(s_nb);
+    const uint32_t mine = tid < nbk ? s_bin[tid] : 0u;
+    int gt = 0, eq = 0;
+    for (int j = 0; j < nbk; ++j) {
+      const uint32_t o = s_bin[j];
+      gt += o > mine;
+      eq += o == mine;
+    }
+    if (tid < nbk && gt < static_cast<int>(r1) && static_cast<int>(r1) <= gt + eq) {
+      s_res[0] = static_cast<int>(mine);  // every lane holding T writes the same values
+      s_res[1] = static_cast<int>(r1) - gt;
+    }
+  }
+  __syncthreads();
+  T = static_cast<uint32_t>(s_res[0]);
+  need_eq = s_res[1];
+  __syncthreads();
+}
+
 // ============================================================================ per-row top-k
 // One workgroup per query row; the row's keys live in LDS when n_vis <= CAP, otherwise they are
 // re-read from the score row in global memory on every pass (exact, slower).
@@ -563,26 +635,36 @@ __global__ __launch_bounds__(THREADS) void topk_row_kernel(
 }
 
 // ============================================================================ sampled row top-k
-// One workgroup per row; thread t keeps the keys of entries t*PER .. t*PER+PER-1 in registers.
-//  1. every 16th key is a sample; the r-th largest sample (r a little above kk/16, with a margin
-//     of 4 standard deviations) is a lower threshold T_lo that almost surely has between kk and
-//     kCandCap keys at or above it;
-//  2. one block prefix sum over per-thread counts writes those candidates to LDS in index order;
-//  3. an exact radix select among the candidates finds the kk-th key and an index-ordered pass
-//     emits the selection in ascending order.
+// One workgroup per row; thread t holds in registers the keys of the row's 16-byte chunks
+// i*THREADS + t, i < PER/4 (coalesced loads).
+//  1. the first key of every fourth chunk is a sample (1 in 16); the lower edge of the 12-bit
+//     bin holding the r-th largest sample (r a little above kk/16 with a margin of 4 standard
+//     deviations; refined by a second pass when that bin is crowded) is a threshold T_lo that
+//     almost surely has between kk and kCandCap keys at or above it;
+//  2. one block prefix sum over per-thread counts writes those candidate keys to LDS;
+//  3. select_kth finds the kk-th candidate key T and how many keys equal to T are taken;
+//  4. keys > T and keys == T set bits in two bitmaps of the row in LDS; one block prefix sum
+//     over the counts of each thread's bitmap words gives its output slots, so the selection
+//     comes out in ascending index order with the lowest indices winning ties.
 // If the count misses [kk, kCandCap] (ties, adversarial data) the exact streaming select runs.
 template <int THREADS, int PER>
 __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
     const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
-  constexpr int NS = THREADS * (PER / 16);  // samples
+  constexpr int CH = PER / 4;             // chunks per thread
+  constexpr int SPT = CH / 4;             // samples per thread
+  constexpr int NS = THREADS * SPT;       // sample slots
+  constexpr int NWORD = THREADS * PER / 32;
+  constexpr int WPT = PER / 32;           // bitmap words per thread
+  static_assert(CH % 4 == 0 && PER % 32 == 0, "chunk and word layout");
   __shared__ uint32_t s_samp[NS];
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_ckey[kCandCap];
-  __shared__ int32_t s_cidx[kCandCap];
+  __shared__ uint32_t s_gtw[NWORD], s_eqw[NWORD];
   __shared__ uint32_t s_tmp[THREADS / 64];
   __shared__ int s_res[2];
+  __shared__ uint32_t s_max;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
@@ -597,60 +679,137 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
     }
     return;
   }
-  const int e0 = tid * PER;
+  // keys; every chunk load is issued (clamped into the row) and masked, the row's last partial
+  // chunk is read element by element
   uint32_t kr[PER];
 #pragma unroll
-  for (int i = 0; i < PER; i += 4) {
-    if (e0 + i + 3 < n_vis) {
-      const float4 v = *reinterpret_cast<const float4*>(srow + e0 + i);
-      kr[i] = order_key(v.x);
-      kr[i + 1] = order_key(v.y);
-      kr[i + 2] = order_key(v.z);
-      kr[i + 3] = order_key(v.w);
-    } else {
+  for (int i = 0; i < CH; ++i) {
+    const int base = (i * THREADS + tid) * 4;
+    // the address depends only on the row length, not on n_vis, so the loads need not wait for
+    // the row's position and entry count
+    const float4 v = *reinterpret_cast<const float4*>(srow + min(base, sstride - 4));
+    const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kr[i + j] = (e0 + i + j < n_vis) ? order_key(srow[e0 + i + j]) : 0u;
+    for (int j = 0; j < 4; ++j) kr[i * 4 + j] = (base + j < n_vis) ? order_key(f[j]) : 0u;
+  }
+  {
+    const int last = (n_vis - 1) & ~3;  // start of the chunk holding the last visible entry
+    if (n_vis & 3) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+        if ((i * THREADS + tid) * 4 == last) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (last + j < n_vis) kr[i * 4 + j] = order_key(srow[last + j]);
+        }
     }
   }
-  // samples: keys at offsets 0, 16, 32, ... of each thread's segment (only visible entries)
+  // samples: slot (i/4)*THREADS + t holds the first key of chunk i*THREADS + t (i % 4 == 0);
+  // entries grow with the slot, so the visible samples are a prefix of ns slots
 #pragma unroll
-  for (int i = 0; i < PER; i += 16) s_samp[tid * (PER / 16) + i / 16] = e0 + i < n_vis ? kr[i] : 0u;
-  // the sample array holds the visible samples first: thread segments are in entry order and the
-  // invisible tail is contiguous, so the number of visible samples is simply ceil(n_vis / 16)
-  const int ns = (n_vis + 15) / 16;
+  for (int i = 0; i < CH; i += 4) {
+    const int base = (i * THREADS + tid) * 4;
+    s_samp[(i / 4) * THREADS + tid] = base < n_vis ? kr[i * 4] : 0u;
+  }
+  const int qch = (n_vis + 3) / 4;  // chunks that start below n_vis
+  int ns = 0;
+#pragma unroll
+  for (int g = 0; g < SPT; ++g) ns += max(0, min(THREADS, qch - 4 * g * THREADS));
+  if (tid == 0) s_max = 0u;
   __syncthreads();
   const float expect = static_cast<float>(kk) * static_cast<float>(ns) / static_cast<float>(n_vis);
   int r = static_cast<int>(ceilf(expect + 4.f * sqrtf(expect) + 4.f));
   if (r > ns) r = ns;
-  uint32_t Tlo;
-  int dummy;
+  // T_lo: the lower edge of the 12-bit bin that holds the r-th largest sample (refined by a
+  // second 12-bit pass when that bin holds more than 64 samples)
   auto sf = [&](int j) { return s_samp[j]; };
-  radix_select<THREADS>(sf, ns, r, s_hist, s_tmp, s_res, Tlo, dummy);
-  // count and compact the candidates (keys >= Tlo) in entry order
-  uint32_t own = 0;
+  uint32_t Tlo;
+  {
+    const uint32_t cb = radix_pass<THREADS>(sf, ns, 0u, 0u, 20, 4096, static_cast<uint32_t>(r),
+                                            s_hist, s_tmp, s_res);
+    const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
+    const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
+    __syncthreads();
+    Tlo = d1 << 20;
+    if (cb > 64) {
+      radix_pass<THREADS>(sf, ns, d1 << 20, 0xfff00000u, 8, 4096, r1, s_hist, s_tmp, s_res);
+      Tlo |= static_cast<uint32_t>(s_res[0]) << 8;
+      __syncthreads();
+    }
+  }
+  // count the candidates (visible keys >= T_lo) and their largest key
+  uint32_t own = 0, kmax = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) own += (e0 + i < n_vis && kr[i] >= Tlo) ? 1u : 0u;
+  for (int i = 0; i < CH; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool c = (i * THREADS + tid) * 4 + j < n_vis && kr[i * 4 + j] >= Tlo;
+      own += c ? 1u : 0u;
+      kmax = c ? max(kmax, kr[i * 4 + j]) : kmax;
+    }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), off, 64)));
+  if (lane_id() == 0 && kmax) atomicMax(&s_max, kmax);
   uint32_t cnt;
   uint32_t off = block_excl_scan<THREADS>(own, s_tmp, &cnt);
   if (cnt >= static_cast<uint32_t>(kk) && cnt <= static_cast<uint32_t>(kCandCap)) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (e0 + i < n_vis && kr[i] >= Tlo) {
-        s_ckey[off] = kr[i];
-        s_cidx[off] = e0 + i;
-        ++off;
-      }
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((i * THREADS + tid) * 4 + j < n_vis && kr[i * 4 + j] >= Tlo) s_ckey[off++] = kr[i * 4 + j];
+    for (int w = tid; w < NWORD; w += THREADS) {
+      s_gtw[w] = 0u;
+      s_eqw[w] = 0u;
     }
     __syncthreads();
     uint32_t T;
     int need_eq;
     auto cf = [&](int j) { return s_ckey[j]; };
-    radix_select<THREADS>(cf, static_cast<int>(cnt), kk, s_hist, s_tmp, s_res, T, need_eq);
-    ordered_emit_fn<THREADS>(cf, static_cast<int>(cnt), T, need_eq, k, [&](int slot, int j) {
-      const int e = s_cidx[j];
-      out[slot] = e;
-      if (sout) sout[slot] = srow[e];
-    });
+    select_kth<THREADS>(cf, static_cast<int>(cnt), kk, Tlo, s_max, s_hist, s_tmp, s_res, T,
+                        need_eq);
+    // bitmaps of the keys above T and equal to T
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = (i * THREADS + tid) * 4 + j;
+        const uint32_t kv = kr[i * 4 + j];
+        if (e < n_vis && kv >= T) atomicOr(kv > T ? &s_gtw[e >> 5] : &s_eqw[e >> 5], 1u << (e & 31));
+      }
+    __syncthreads();
+    // thread t emits the entries of words t*WPT .. t*WPT+WPT-1 in index order
+    uint32_t gw[WPT], ew[WPT], ngt = 0, neq = 0;
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      gw[q] = s_gtw[tid * WPT + q];
+      ew[q] = s_eqw[tid * WPT + q];
+      ngt += __popc(gw[q]);
+      neq += __popc(ew[q]);
+    }
+    uint32_t tot;
+    const uint32_t before = block_excl_scan<THREADS>((ngt << 16) | neq, s_tmp, &tot);
+    int eq_seen = static_cast<int>(before & 0xffffu);
+    int slot = static_cast<int>(before >> 16) + min(eq_seen, need_eq);
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      uint32_t bits = gw[q] | ew[q];
+      while (bits) {
+        const int bpos = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        const int e = (tid * WPT + q) * 32 + bpos;
+        bool take = true;
+        if (!((gw[q] >> bpos) & 1u)) {
+          take = eq_seen < need_eq;
+          ++eq_seen;
+        }
+        if (take) {
+          out[slot] = e;
+          if (sout) sout[slot] = srow[e];
+          ++slot;
+        }
+      }
+    }
     for (int j = kk + tid; j < k; j += THREADS) {
       out[j] = -1;
       if (sout) sout[j] = -INFINITY;

@@ -486,7 +486,11 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
   }
 }
 
-// Merge of the spans of one (query row, head): fixed order over spans, sink added once.
+// Merge of the spans of one (query row, head): fixed order over spans, sink added once.  The
+// span loops are unrolled to kCombineMax so that all spans' loads are in flight together (a
+// longer list is merged in further rounds of the same loop).
+constexpr int kCombineMax = 8;
+
 template <int C>
 __global__ __launch_bounds__(64) void mqa_combine_kernel(MqaParams p) {
   const int rh = blockIdx.x;  // row * n_heads + head
@@ -495,21 +499,41 @@ __global__ __launch_bounds__(64) void mqa_combine_kernel(MqaParams p) {
   const int l = threadIdx.x;
   const float* base = p.part + (static_cast<size_t>(row) * p.n_splits * p.n_heads + head) * (C + 4);
   const size_t sstride = static_cast<size_t>(p.n_heads) * (C + 4);
-  float M = p.sink ? p.sink[head] * kLog2e : -INFINITY;
-  for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, base[s * sstride + C]);
-  float den = (p.sink && M != -INFINITY) ? exp2f(p.sink[head] * kLog2e - M) : 0.f;
-  float lsum = 0.f;
   constexpr int PER = C / 64;  // dims per thread (2, 4 or 8)
+  const float sink2 = p.sink ? p.sink[head] * kLog2e : -INFINITY;
+  float M = sink2;
+  for (int s0 = 0; s0 < p.n_splits; s0 += kCombineMax) {
+    float mv[kCombineMax];
+#pragma unroll
+    for (int j = 0; j < kCombineMax; ++j)
+      mv[j] = s0 + j < p.n_splits ? base[(s0 + j) * sstride + C] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kCombineMax; ++j) M = fmaxf(M, mv[j]);
+  }
+  float den = (p.sink && M != -INFINITY) ? exp2f(sink2 - M) : 0.f;
+  float lsum = 0.f;
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  for (int s = 0; s < p.n_splits; ++s) {
-    const float ms = base[s * sstride + C];
-    if (ms == -INFINITY) continue;
-    const float f = exp2f(ms - M);
-    lsum += base[s * sstride + C + 1] * f;
+  for (int s0 = 0; s0 < p.n_splits; s0 += kCombineMax) {
+    float mv[kCombineMax], lv[kCombineMax], ov[kCombineMax][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] += base[s * sstride + l * PER + i] * f;
+    for (int j = 0; j < kCombineMax; ++j) {
+      const int sp = min(s0 + j, p.n_splits - 1);
+      const float* src = base + sp * sstride;
+      mv[j] = s0 + j < p.n_splits ? src[C] : -INFINITY;
+      lv[j] = src[C + 1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ov[j][i] = src[l * PER + i];
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineMax; ++j) {
+      if (mv[j] == -INFINITY) continue;
+      const float f = exp2f(mv[j] - M);
+      lsum += lv[j] * f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] += ov[j][i] * f;
+    }
   }
   den += lsum;
   const float inv = den > 0.f ? 1.f / den : 0.f;
