@@ -43,7 +43,8 @@ struct MqaParams {
   int nq, n_heads, r, k, m, n_win, win_slots, n_max;
   float scale_log2;
   int split_rows, n_splits, head_groups, n_work;
-  float* part;  // [rows, n_splits, n_heads, C + 4]: C unnormalised sums, (max, sum), pad
+  float* part;  // span partials, unnormalised O in the MFMA lane order (see mqa_kernel)
+  float* ml;    // [rows, n_splits, n_heads, 2]: (max, sum) of each span
   uint16_t* out;
   float* lse_out;
 };
@@ -109,7 +110,7 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
   constexpr int CPR = SH::CPR, LOADS = SH::LOADS, TILE = SH::TILE;
   static_assert(LOADS * NT == 32 * CPR, "tile chunks must split evenly over the threads");
   static_assert(CPR == 64 || 64 % CPR == 0, "a load step covers whole rows");
-  static_assert(C / 2 <= NT, "one thread per RoPE frequency");
+  static_assert(NT >= 64, "one thread per RoPE frequency (rope_dim <= 128 is checked at the API)");
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* E = reinterpret_cast<uint16_t*>(smem);                         // [2][32][C] swizzled
   float* SX = reinterpret_cast<float*>(smem + SH::lds_sx());       // [NW][4][64][4]
@@ -129,6 +130,16 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
   const int split = w % p.n_splits;
   const int row = w / p.n_splits;
   const int b = row / p.nq;
+  const int j0 = split * p.split_rows;
+  // the first two tiles' selected indices depend only on (row, split): their loads go out
+  // before the position and entry count they are checked against (two dependent memory round
+  // trips before the first gathers instead of three)
+  int pre0 = 0, pre1 = 0;
+  if (p.idx && l < 32) {
+    const int32_t* ir = p.idx + static_cast<size_t>(row) * p.k;
+    pre0 = ir[min(j0 + l, p.k - 1)];
+    pre1 = ir[min(j0 + 32 + l, p.k - 1)];
+  }
   const int t = p.pos ? p.pos[row] : (row % p.nq);
   const int n_ent = max(0, min(p.n_entries[b], p.n_max));
   const int n_w = min(p.n_win, t + 1);
@@ -141,7 +152,6 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
     n_sel = static_cast<int>(v < n_ent ? v : n_ent);
   }
   const int R = n_sel + n_w;
-  const int j0 = split * p.split_rows;
   const int j1 = min(R, j0 + p.split_rows);
   const int head = (hg * HP + hp) * 32 + n32;
   const bool head_ok = head < p.n_heads;
@@ -153,15 +163,13 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
   // so every lane always issues its loads and no gathered value is ever undefined.
   const uint16_t* const safe_row =
       p.window + (static_cast<size_t>(b) * p.win_slots + (t % p.win_slots)) * C;
-  auto resolve = [&](int jt, bool idx_from_global, const uint16_t*& ptr, uint32_t& mask) {
+  auto resolve = [&](int jt, int pre, const uint16_t*& ptr, uint32_t& mask) {
     const int j = jt + l;
     const uint16_t* pr = safe_row;
     bool ok = false;
     if (l < 32 && j < j1) {
       if (j < n_sel) {
-        const int e = p.idx ? (idx_from_global ? p.idx[static_cast<size_t>(row) * p.k + j]
-                                               : s_idx[j - j0])
-                            : j;
+        const int e = p.idx ? (pre >= -1 ? pre : s_idx[j - j0]) : j;
         ok = e >= 0 && e < n_ent;
         if (ok) pr = p.entries + (static_cast<size_t>(b) * p.n_max + e) * C;
       } else {
@@ -199,15 +207,15 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
   // in pairs with static register stages and LDS buffers.  Every tile step prefetches two tiles
   // ahead unconditionally (tiles past the span resolve to masked rows), so both register stages
   // are always in flight in the same order.  The first two tiles are issued before anything
-  // else, with their indices read straight from global memory.
+  // else, with their indices read straight from global memory (pre0, pre1).
   const int ntiles = j1 > j0 ? (((j1 - j0 + 31) / 32) | 1) : 0;
   u32x4 stage0[LOADS], stage1[LOADS];
   uint32_t mask0 = 0, mask1 = 0;
   if (ntiles > 0) {
     const uint16_t* p0;
     const uint16_t* p1;
-    resolve(j0, true, p0, mask0);
-    resolve(j0 + 32, true, p1, mask1);
+    resolve(j0, pre0 < -1 ? -1 : pre0, p0, mask0);
+    resolve(j0 + 32, pre1 < -1 ? -1 : pre1, p1, mask1);
     gload(p0, stage0);
     gload(p1, stage1);
   }
@@ -321,7 +329,7 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
       *reinterpret_cast<u32x4*>(smem + st_off[i] + buf * TILE * 2) = st[i];
     const uint32_t msk = mask;
     const uint16_t* pn;
-    resolve(j0 + (it + 2) * 32, false, pn, mask);
+    resolve(j0 + (it + 2) * 32, -2, pn, mask);  // -2: read the index from LDS
     __syncthreads();  // tile `it` is in LDS
     gload(pn, st);
     return msk;
@@ -471,60 +479,83 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
     if (p.lse_out && h == 0 && slice == 0)
       p.lse_out[orow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
-    float* prow = p.part + ((static_cast<size_t>(row) * p.n_splits + split) * p.n_heads + head) *
-                               (C + 4);
+    // span partials in the MFMA lane order: per (row, span, head group, wave) DT*4 chunks of
+    // 64 lanes x 4 floats, so every store instruction writes 1 KiB contiguous
+    float* pw = p.part + ((((static_cast<size_t>(row) * p.n_splits + split) * p.head_groups + hg) *
+                            NW + wave) * (DT * 4) * 256);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<f32x4*>(prow + dbase + dt * 32 + g4 * 8 + 4 * h) =
+        *reinterpret_cast<f32x4*>(pw + ((dt * 4 + g4) * 64 + l) * 4) =
             f32x4{acc[dt][4 * g4], acc[dt][4 * g4 + 1], acc[dt][4 * g4 + 2], acc[dt][4 * g4 + 3]};
     if (h == 0 && slice == 0) {
-      prow[C] = m_ref;
-      prow[C + 1] = l_tot;
+      float* mlp = p.ml + ((static_cast<size_t>(row) * p.n_splits + split) * p.n_heads + head) * 2;
+      mlp[0] = m_ref;
+      mlp[1] = l_tot;
     }
   }
 }
 
-// Merge of the spans of one (query row, head): fixed order over spans, sink added once.  The
-// span loops are unrolled to kCombineMax so that all spans' loads are in flight together (a
-// longer list is merged in further rounds of the same loop).
+// Merge of the spans of one (query row, 64-head group): a thread takes 4 of the DT*4 chunks
+// a lane of one wave held (same head, 16 dims), merges the spans in a fixed order, adds the sink
+// once, normalises, rotates back and stores bf16.  Loads of up to kCombineMax spans are in flight
+// together.
 constexpr int kCombineMax = 8;
 
-template <int C>
-__global__ __launch_bounds__(64) void mqa_combine_kernel(MqaParams p) {
-  const int rh = blockIdx.x;  // row * n_heads + head
-  const int row = rh / p.n_heads, head = rh % p.n_heads;
+template <int C, int HP>
+__global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_combine_kernel(MqaParams p) {
+  using SH = MqaShape<C, HP>;
+  constexpr int NW = SH::NW, CS = SH::CS, DT = SH::DT;
+  constexpr int CPT = 4;                 // chunks per thread
+  constexpr int GROUPS = DT * 4 / CPT;   // thread groups per (row, head group)
+  const int bid = blockIdx.x;
+  const int cgp = bid % GROUPS;
+  const int hg = (bid / GROUPS) % p.head_groups;
+  const int row = bid / (GROUPS * p.head_groups);
+  const int tid = threadIdx.x, l = lane_id();
+  const int wave = tid >> 6;
+  const int hp = wave % HP, slice = wave / HP;
+  const int h = l >> 5, n32 = l & 31;
+  const int head = (hg * HP + hp) * 32 + n32;
+  if (head >= p.n_heads) return;
   const int t = p.pos ? p.pos[row] : (row % p.nq);
-  const int l = threadIdx.x;
-  const float* base = p.part + (static_cast<size_t>(row) * p.n_splits * p.n_heads + head) * (C + 4);
-  const size_t sstride = static_cast<size_t>(p.n_heads) * (C + 4);
-  constexpr int PER = C / 64;  // dims per thread (2, 4 or 8)
+  const int dbase = slice * CS;
+  const size_t span_stride = static_cast<size_t>(p.head_groups) * NW * (DT * 4) * 256;
+  const float* pw0 = p.part + (((static_cast<size_t>(row) * p.n_splits) * p.head_groups + hg) * NW +
+                               wave) * (DT * 4) * 256 + (cgp * CPT * 64 + l) * 4;
+  const float* ml0 = p.ml + (static_cast<size_t>(row) * p.n_splits * p.n_heads + head) * 2;
+  const size_t ml_stride = static_cast<size_t>(p.n_heads) * 2;
+
+  // one pass per kCombineMax spans: their (max, sum) and O loads go out together, and the
+  // running reference M moves (rescaling what was merged) only between passes
   const float sink2 = p.sink ? p.sink[head] * kLog2e : -INFINITY;
   float M = sink2;
-  for (int s0 = 0; s0 < p.n_splits; s0 += kCombineMax) {
-    float mv[kCombineMax];
-#pragma unroll
-    for (int j = 0; j < kCombineMax; ++j)
-      mv[j] = s0 + j < p.n_splits ? base[(s0 + j) * sstride + C] : -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kCombineMax; ++j) M = fmaxf(M, mv[j]);
-  }
-  float den = (p.sink && M != -INFINITY) ? exp2f(sink2 - M) : 0.f;
   float lsum = 0.f;
-  float o[PER];
+  f32x4 o[CPT];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  for (int c = 0; c < CPT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < p.n_splits; s0 += kCombineMax) {
-    float mv[kCombineMax], lv[kCombineMax], ov[kCombineMax][PER];
+    float mv[kCombineMax], lv[kCombineMax];
+    f32x4 ov[kCombineMax][CPT];
 #pragma unroll
     for (int j = 0; j < kCombineMax; ++j) {
       const int sp = min(s0 + j, p.n_splits - 1);
-      const float* src = base + sp * sstride;
-      mv[j] = s0 + j < p.n_splits ? src[C] : -INFINITY;
-      lv[j] = src[C + 1];
+      mv[j] = s0 + j < p.n_splits ? ml0[sp * ml_stride] : -INFINITY;
+      lv[j] = ml0[sp * ml_stride + 1];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) ov[j][i] = src[l * PER + i];
+      for (int c = 0; c < CPT; ++c)
+        ov[j][c] = *reinterpret_cast<const f32x4*>(pw0 + sp * span_stride + c * 256);
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < kCombineMax; ++j) Mn = fmaxf(Mn, mv[j]);
+    if (Mn != M) {
+      const float a = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
+      lsum *= a;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) o[c] *= a;
+      M = Mn;
     }
 #pragma unroll
     for (int j = 0; j < kCombineMax; ++j) {
@@ -532,32 +563,40 @@ __global__ __launch_bounds__(64) void mqa_combine_kernel(MqaParams p) {
       const float f = exp2f(mv[j] - M);
       lsum += lv[j] * f;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) o[i] += ov[j][i] * f;
+      for (int c = 0; c < CPT; ++c) o[c] += ov[j][c] * f;
     }
   }
-  den += lsum;
+  const float den = lsum + ((p.sink && M != -INFINITY) ? exp2f(sink2 - M) : 0.f);
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  uint16_t* dst = p.out + (static_cast<size_t>(row) * p.n_heads + head) * C;
-  // each thread owns PER consecutive dims starting at l*PER (even, so RoPE pairs stay local);
-  // all rotations happen before the first store
-  uint32_t packed[PER / 2];
+  // chunk cc = dt*4 + g4 holds dims dbase + 32dt + 8g4 + 4h .. +3; all rotations before stores
+  uint2 packed[CPT];
+  int dpos[CPT];
 #pragma unroll
-  for (int i = 0; i < PER; i += 2) {
-    const int d = l * PER + i;
-    float x0 = o[i] * inv, x1 = o[i + 1] * inv;
-    if (d >= C - p.r) {
-      float cs, sn;
-      rope_cos_sin(t, p.inv_freq[(d - (C - p.r)) >> 1], cs, sn);
-      const float y0 = x0 * cs + x1 * sn, y1 = -x0 * sn + x1 * cs;
-      x0 = y0;
-      x1 = y1;
+  for (int c = 0; c < CPT; ++c) {
+    const int cc = cgp * CPT + c;
+    const int d0 = dbase + (cc >> 2) * 32 + (cc & 3) * 8 + 4 * h;
+    float x[4] = {o[c][0] * inv, o[c][1] * inv, o[c][2] * inv, o[c][3] * inv};
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int d = d0 + 2 * pr;
+      if (d >= C - p.r) {
+        float cs, sn;
+        rope_cos_sin(t, p.inv_freq[(d - (C - p.r)) >> 1], cs, sn);
+        const float x0 = x[2 * pr], x1 = x[2 * pr + 1];
+        x[2 * pr] = x0 * cs + x1 * sn;
+        x[2 * pr + 1] = -x0 * sn + x1 * cs;
+      }
     }
-    packed[i / 2] = pack2(x0, x1);
+    packed[c].x = pack2(x[0], x[1]);
+    packed[c].y = pack2(x[2], x[3]);
+    dpos[c] = d0;
   }
+  uint16_t* dst = p.out + (static_cast<size_t>(row) * p.n_heads + head) * C;
 #pragma unroll
-  for (int i = 0; i < PER; i += 2) *reinterpret_cast<uint32_t*>(dst + l * PER + i) = packed[i / 2];
-  if (p.lse_out && l == 0)
-    p.lse_out[rh] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
+  for (int c = 0; c < CPT; ++c) *reinterpret_cast<uint2*>(dst + dpos[c]) = packed[c];
+  if (p.lse_out && cgp == 0 && h == 0 && slice == 0)
+    p.lse_out[static_cast<size_t>(row) * p.n_heads + head] =
+        lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- planning and launch
@@ -603,9 +642,12 @@ MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list) {
   return pl;
 }
 
+// partials: rows x spans x head groups x (32 * head_pairs heads) x c floats, then (max, sum)
 size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c) {
   if (p.n_splits <= 1) return 0;
-  return static_cast<size_t>(rows) * p.n_splits * n_heads * (c + 4) * sizeof(float);
+  const size_t o = static_cast<size_t>(rows) * p.n_splits * p.head_groups * p.heads_per_wg * c;
+  const size_t ml = static_cast<size_t>(rows) * p.n_splits * n_heads * 2;
+  return (o + ml) * sizeof(float);
 }
 
 template <int C, int HP>
@@ -631,7 +673,8 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || prm.n_splits == 1) return e;
   ProfScope ps("mqa_combine", s);
-  mqa_combine_kernel<C><<<static_cast<unsigned>(rows) * prm.n_heads, 64, 0, s>>>(prm);
+  constexpr int groups = SH::DT * 4 / 4;
+  mqa_combine_kernel<C, HP><<<static_cast<unsigned>(rows) * prm.head_groups * groups, SH::NT, 0, s>>>(prm);
   return hipGetLastError();
 }
 
@@ -664,6 +707,8 @@ hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& pl, hipStream_t s) {
   p.n_splits = pl.n_splits;
   p.head_groups = pl.head_groups;
   p.part = a.part;
+  p.ml = a.part + static_cast<size_t>(a.B) * a.nq * pl.n_splits * pl.head_groups *
+                      pl.heads_per_wg * a.c;
   p.out = a.out;
   p.lse_out = a.lse_out;
   const int rows = a.B * a.nq;
