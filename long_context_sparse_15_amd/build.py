@@ -24,8 +24,9 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 # Per-file flags.  The indexer's MFMA results feed VALU epilogues directly, so they are produced
-# in VGPRs; the attention kernels keep their long-lived accumulators in AGPRs.
-FILE_FLAGS = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# in VGPRs; the attention kernels keep their accumulators in VGPRs too, one register pool.
+FILE_FLAGS = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "mqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):

@@ -87,8 +87,9 @@ __device__ __forceinline__ void store_out4(uint16_t* dst, float o0, float o1, fl
   *reinterpret_cast<uint2*>(dst) = v;
 }
 
-template <int C, int HP>
+template <int C, int HP_>
 struct MqaShape {
+  static constexpr int HP = HP_;
   static constexpr int DS = C == 512 ? 2 : 1;   // dim slices
   static constexpr int NW = HP * DS;            // waves
   static constexpr int NT = 64 * NW;
@@ -363,10 +364,6 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
         acc[dt] = mfma_bf16_32x32x16(a, bp[mm], acc[dt]);
       }
     }
-    // keep the output accumulators in the accumulation registers across tiles (only the rare
-    // rescale below moves them through VGPRs); the empty asm emits no instruction
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+a"(acc[dt]));
   };
   // slice sum, mask, online softmax of one tile; P^T (bf16, B operand of the PV MFMAs) to bp
   auto softmax = [&](f32x16 sacc, uint32_t msk, bf16x8 (&bp)[2]) {
@@ -401,22 +398,8 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
       const float m_new = move ? mx : m_ref;
       const float alpha = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
       l_run *= alpha;
-      // acc *= alpha, element by element in place in the accumulation registers: written as
-      // asm so that the compiler cannot hoist the register copies out of this rare branch
-      // (they would hold 128 VGPRs through every tile)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = acc[dt][e], tmp;
-          asm volatile(
-              "v_accvgpr_read_b32 %1, %0\n\t"
-              "v_mul_f32 %1, %1, %2\n\t"
-              "v_accvgpr_write_b32 %0, %1"
-              : "+a"(x), "=&v"(tmp)
-              : "v"(alpha));
-          acc[dt][e] = x;
-        }
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
       m_ref = m_new;
     }
     const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
@@ -497,16 +480,441 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
   }
 }
 
+// ---------------------------------------------------------------- eight-wave variant, C = 512
+// Wave (hp, s) of eight owns heads hp*32..hp*32+31 and the 128-dim slice s*128..s*128+127: its
+// output accumulators take 64 registers and two waves share each SIMD.  The four slice partials
+// of S^T are summed through LDS with a change of ownership: wave (hp, s) finishes the softmax of
+// heads 8s..8s+7 of its pair over all 32 rows of the tile (lane l: head 8s + l%8, rows
+// 4(l/8)..4(l/8)+3), so the per-head maximum is a reduction across lanes of one wave (DPP and
+// lane-swap instructions, no LDS round trip).  The owner publishes P^T (bf16, in the K-slot
+// order of the PV MFMAs) and the rescale factor of each head.
+//
+// Two barriers per tile, and matrix work on both sides of each:
+//   phase A of step i: P^T(i-1) and rescale factors in, rescale, PV(i-1); S partials of tile i
+//                      out; barrier
+//   phase B of step i: slice sums and softmax of tile i, P^T(i) out; S(i+1); tile i+2 from
+//                      registers into LDS, gathers of tile i+4 resolved; barrier; gathers issued
+// Key tiles live in a ring of three LDS buffers (tile t in buffer t % 3): during step i tile i-1
+// is read by PV in phase A and overwritten by tile i+2 in phase B, tile i+1 is read by S.
+template <int C>
+struct MqaWideShape {
+  static constexpr int HP = 2, DS = 4, NW = HP * DS, NT = 64 * NW;
+  static constexpr int CS = C / DS;             // dims per slice
+  static constexpr int KK = CS / 16;            // S^T MFMA steps over the slice
+  static constexpr int DT = CS / 32;            // 32-dim output tiles of the slice
+  static constexpr int CPR = C / 8;             // 16-byte chunks per row
+  static constexpr int LOADS = 32 * CPR / NT;   // chunks per thread per tile
+  static constexpr int TILE = 32 * C;           // bf16 elements per LDS tile
+  static constexpr int NBUF = 3;
+  static constexpr size_t off_sx = NBUF * TILE * sizeof(uint16_t);  // [HP][DS][4][64] f32x4
+  static constexpr size_t off_sp = off_sx + HP * DS * 4 * 64 * 16;  // [HP][8][32] 4 x bf16
+  static constexpr size_t off_sa = off_sp + HP * 8 * 32 * 8;        // [HP][32] rescale factor
+  static constexpr size_t off_sl = off_sa + HP * 32 * 4;            // [HP][32] (max, sum)
+  static constexpr size_t off_freq = off_sl + HP * 32 * 8;          // [C/2] RoPE frequencies
+  static constexpr size_t lds_fixed() { return off_freq + (C / 2) * sizeof(float); }
+};
+
+// x combined with lane l ^ 8, l ^ 16 and l ^ 32 (a reduction over the eight lanes l % 8 + 8j)
+__device__ __forceinline__ float max_over_xor8_16_32(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf,
+                                                          false)));  // row_ror:8 = lane ^ 8
+  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+}
+__device__ __forceinline__ float sum_over_xor8_16_32(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
+template <int C>
+__global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaParams p) {
+  using SH = MqaWideShape<C>;
+  constexpr int HP = SH::HP, DS = SH::DS, NW = SH::NW, NT = SH::NT, CS = SH::CS, KK = SH::KK,
+                DT = SH::DT, CPR = SH::CPR, LOADS = SH::LOADS, TILE = SH::TILE;
+  constexpr uint32_t TB = TILE * 2;  // bytes per LDS tile
+  static_assert(CPR == 64 && LOADS * NT == 32 * CPR, "one row per wave and load step");
+  static_assert(KK <= 8 && DT <= 4, "offset tables below cover one 128-dim block");
+  static_assert(NT >= C / 2, "one thread per RoPE frequency");
+  extern __shared__ __align__(16) unsigned char smem[];
+  f32x4* SX = reinterpret_cast<f32x4*>(smem + SH::off_sx);
+  uint2* SP = reinterpret_cast<uint2*>(smem + SH::off_sp);
+  float* SA = reinterpret_cast<float*>(smem + SH::off_sa);
+  float2* SL = reinterpret_cast<float2*>(smem + SH::off_sl);
+  float* s_freq = reinterpret_cast<float*>(smem + SH::off_freq);
+  int* s_idx = reinterpret_cast<int*>(smem + SH::lds_fixed());  // [split_rows]
+
+  const int tid = threadIdx.x;
+  const int l = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hp = wave % HP, slice = wave / HP;
+  const int h = l >> 5, n32 = l & 31;
+  const int r4 = l >> 3, hh = 8 * slice + (l & 7);  // softmax share: head hh, rows 4r4..4r4+3
+  const int bid = blockIdx.x;
+  const int w = (bid / (8 * p.head_groups)) * 8 + (bid & 7);
+  const int hg = (bid >> 3) % p.head_groups;
+  if (w >= p.n_work) return;
+  const int split = w % p.n_splits;
+  const int row = w / p.n_splits;
+  const int b = row / p.nq;
+  const int j0 = split * p.split_rows;
+  int pre0 = 0, pre1 = 0;
+  if (p.idx && l < 32) {
+    const int32_t* ir = p.idx + static_cast<size_t>(row) * p.k;
+    pre0 = ir[min(j0 + l, p.k - 1)];
+    pre1 = ir[min(j0 + 32 + l, p.k - 1)];
+  }
+  const int t = p.pos ? p.pos[row] : (row % p.nq);
+  const int n_ent = max(0, min(p.n_entries[b], p.n_max));
+  const int n_w = min(p.n_win, t + 1);
+  const int wlo = t - n_w + 1;
+  int n_sel;
+  if (p.idx) {
+    n_sel = p.k;
+  } else {
+    const long v = (static_cast<long>(t) + 1) / p.m;
+    n_sel = static_cast<int>(v < n_ent ? v : n_ent);
+  }
+  const int R = n_sel + n_w;
+  const int j1 = min(R, j0 + p.split_rows);
+  const int head = (hg * HP + hp) * 32 + n32;
+  const bool head_ok = head < p.n_heads;
+  const int dbase = slice * CS;
+
+  // row pointers of the tile at list row jt (lanes 0..31), masked rows read the window row of t
+  const uint16_t* const safe_row =
+      p.window + (static_cast<size_t>(b) * p.win_slots + (t % p.win_slots)) * C;
+  auto resolve = [&](int jt, int pre, const uint16_t*& ptr, uint32_t& mask) {
+    const int j = jt + l;
+    const uint16_t* pr = safe_row;
+    bool ok = false;
+    if (l < 32 && j < j1) {
+      if (j < n_sel) {
+        const int e = p.idx ? (pre >= -1 ? pre : s_idx[j - j0]) : j;
+        ok = e >= 0 && e < n_ent;
+        if (ok) pr = p.entries + (static_cast<size_t>(b) * p.n_max + e) * C;
+      } else {
+        const int u = wlo + (j - n_sel);
+        ok = true;
+        pr = p.window + (static_cast<size_t>(b) * p.win_slots + (u % p.win_slots)) * C;
+      }
+    }
+    ptr = pr;
+    mask = static_cast<uint32_t>(__ballot(ok));
+  };
+  // wave `wave` loads rows wave, wave+8, wave+16, wave+24 of the tile, 16 bytes per lane
+  auto gload = [&](const uint16_t* ptr, u32x4 (&st)[LOADS]) {
+    const uint64_t pv = reinterpret_cast<uint64_t>(ptr);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int rr = wave + i * NW;
+      const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv), rr);
+      const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv >> 32), rr);
+      const uint64_t rp = (static_cast<uint64_t>(hi) << 32) | lo;
+      st[i] = *(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(rp) + l);
+    }
+  };
+
+  // even tile count (a masked tile pads odd spans); tiles 0 and 1 are gathered first
+  const int ntiles = j1 > j0 ? ((j1 - j0 + 63) / 64) * 2 : 0;
+  u32x4 stage0[LOADS], stage1[LOADS];
+  uint32_t mq0 = 0, mq1 = 0, mq2 = 0, mq3 = 0;  // valid masks of tiles i .. i+3
+  if (ntiles > 0) {
+    const uint16_t* p0;
+    const uint16_t* p1;
+    resolve(j0, pre0 < -1 ? -1 : pre0, p0, mq0);
+    resolve(j0 + 32, pre1 < -1 ? -1 : pre1, p1, mq1);
+    gload(p0, stage0);
+    gload(p1, stage1);
+  }
+
+  u32x4 qraw[KK];
+  {
+    const uint16_t* qrow = p.q + (static_cast<size_t>(row) * p.n_heads + (head_ok ? head : 0)) * C;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qraw[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qrow + dbase + kk * 16 + h * 8)
+                         : u32x4{0, 0, 0, 0};
+  }
+  const float sink_v = (p.sink && head_ok) ? p.sink[head] : 0.f;
+  const float freq_v = tid < (p.r >> 1) ? p.inv_freq[tid] : 0.f;
+  if (p.idx) {
+    constexpr int IPT = 2;
+    const int e1 = min(j1, n_sel);
+    for (int base = j0; base < e1; base += NT * IPT) {
+      int v[IPT];
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        const int j = base + tid + i * NT;
+        v[i] = j < e1 ? p.idx[static_cast<size_t>(row) * p.k + j] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        const int j = base + tid + i * NT;
+        if (j < e1) s_idx[j - j0] = v[i];
+      }
+    }
+  }
+  if (tid < (p.r >> 1)) s_freq[tid] = freq_v;
+  __syncthreads();  // s_idx, s_freq
+
+  bf16x8 bq[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int d0 = dbase + kk * 16 + h * 8;
+    u32x4 raw = qraw[kk];
+    if (d0 + 8 > C - p.r) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = d0 + 2 * j;
+        if (d >= C - p.r) {
+          float cs, sn;
+          rope_cos_sin(t, s_freq[(d - (C - p.r)) >> 1], cs, sn);
+          const float x0 = bf16_to_f32(static_cast<uint16_t>(raw[j] & 0xffff));
+          const float x1 = bf16_to_f32(static_cast<uint16_t>(raw[j] >> 16));
+          raw[j] = pack2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+        }
+      }
+    }
+    bq[kk] = as_bf16x8(raw);
+  }
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(bq[kk]) : "memory");
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  // online softmax state of this lane's share (head hh, four rows): the reference maximum moves
+  // only when a scaled logit exceeds it by more than 8; l_part sums this lane's probabilities
+  float m_ref = -INFINITY, l_part = 0.f;
+
+  uint32_t st_off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int rr = wave + i * NW;
+    st_off[i] = static_cast<uint32_t>(rr * C + ((l ^ swz(rr)) << 3)) * 2u;
+  }
+  // S phase (A operand): row n32, logical chunk (dbase>>3) + 2kk + h; the slice is one 16-chunk
+  // block, so the swizzle stays inside it
+  uint32_t sa_off[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    sa_off[kk] = static_cast<uint32_t>(n32 * C + dbase + (((2 * kk + h) ^ swz(n32)) << 3)) * 2u;
+  // PV phase (transposed A operand): rows 16mm + 4h + i0 and +8, logical chunk
+  // (dbase>>3) + 4dt + 2(G&1) + q/2, element 4(q&1); mm adds 16 rows as an immediate
+  const int G = l >> 4, i0 = (l & 15) >> 2, q4 = l & 3;
+  uint32_t ta_off[DT], tb_off[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int low = 4 * dt + 2 * (G & 1) + (q4 >> 1);
+    const int ra = 4 * h + i0, rb = ra + 8;
+    ta_off[dt] = static_cast<uint32_t>(ra * C + dbase + ((low ^ swz(ra)) << 3) + 4 * (q4 & 1)) * 2u;
+    tb_off[dt] = static_cast<uint32_t>(rb * C + dbase + ((low ^ swz(rb)) << 3) + 4 * (q4 & 1)) * 2u;
+  }
+
+  auto store_tile = [&](const u32x4 (&st)[LOADS], uint32_t bo) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4*>(smem + st_off[i] + bo) = st[i];
+  };
+  // every operand read of a phase is issued before its first MFMA (one LDS round trip per
+  // phase instead of one per MFMA pair)
+  auto s_phase = [&](uint32_t bo) -> f32x16 {
+    const unsigned char* Eb = smem + bo;
+    u32x4 ea[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) ea[kk] = *reinterpret_cast<const u32x4*>(Eb + sa_off[kk]);
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) sacc = mfma_bf16_32x32x16(as_bf16x8(ea[kk]), bq[kk], sacc);
+    __builtin_amdgcn_sched_group_barrier(0x100, KK, 0);  // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, KK, 0);  // then the MFMAs
+    return sacc;
+  };
+  // P^T of a tile for head n32 in the K-slot order of the PV MFMAs (rows 16mm + 4h + 0..3, then
+  // 16mm + 8 + 4h + 0..3)
+  auto read_p = [&](bf16x8 (&bp)[2]) {
+    const uint2* sp = SP + hp * 256 + n32;
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const uint2 lo = sp[(4 * mm + h) * 32];
+      const uint2 hi = sp[(4 * mm + 2 + h) * 32];
+      bp[mm] = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+    }
+  };
+  // accumulators *= the rescale factor head n32's owner published (1 unless its reference moved)
+  auto rescale = [&]() {
+    const float alpha = SA[hp * 32 + n32];
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
+  };
+  auto pv_phase = [&](uint32_t bo, const bf16x8 (&bp)[2]) {
+    const unsigned char* Eb = smem + bo;
+    bf16x8 ev[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const uint32_t imm = mm * 16 * C * 2;
+        const bf16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Eb + ta_off[dt] + imm));
+        const bf16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Eb + tb_off[dt] + imm));
+        ev[dt][mm] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) acc[dt] = mfma_bf16_32x32x16(ev[dt][mm], bp[mm], acc[dt]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * DT, 0);  // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * DT, 0);  // then the MFMAs
+  };
+  // this wave's S^T partial to LDS: element i of sacc holds row 8*(i/4) + 4h + i%4, head n32
+  auto x_write = [&](const f32x16& sacc) {
+    f32x4* mine = SX + (hp * DS + slice) * 256;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      mine[g * 64 + l] = f32x4{sacc[4 * g], sacc[4 * g + 1], sacc[4 * g + 2], sacc[4 * g + 3]};
+  };
+  // slice sums of this lane's share (rows 4r4..4r4+3 of head hh sit in lane 32*(r4&1) + hh,
+  // elements 4*(r4/2)..+3, of each slice's partial), mask, online softmax, P^T and the rescale
+  // factor to LDS
+  auto softmax = [&](uint32_t msk) {
+    const f32x4* src = SX + hp * DS * 256 + (r4 >> 1) * 64 + 32 * (r4 & 1) + hh;
+    f32x4 s = src[0];
+#pragma unroll
+    for (int ss = 1; ss < DS; ++ss) s += src[ss * 256];
+    if (msk != 0xffffffffu) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!((msk >> (4 * r4 + e)) & 1u)) s[e] = -INFINITY;
+    }
+    const float mx =
+        max_over_xor8_16_32(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * p.scale_log2;
+    const bool move = mx > m_ref + 8.f;
+    float alpha = 1.f;
+    if (__ballot(move)) {
+      const float m_new = move ? mx : m_ref;
+      alpha = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_part *= alpha;
+      m_ref = m_new;
+    }
+    const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(s[e], p.scale_log2, -mu));
+    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    SP[(hp * 8 + r4) * 32 + hh] = uint2{pack2(pr[0], pr[1]), pack2(pr[2], pr[3])};
+    if (r4 == 0) SA[hp * 32 + hh] = alpha;
+  };
+
+  if (ntiles > 0) {
+    // tiles 0 and 1 into buffers 0 and 1, gathers of tiles 2 and 3, S(0)
+    store_tile(stage0, 0);
+    store_tile(stage1, TB);
+    {
+      const uint16_t* p2;
+      const uint16_t* p3;
+      resolve(j0 + 64, -2, p2, mq2);
+      resolve(j0 + 96, -2, p3, mq3);
+      __syncthreads();
+      gload(p2, stage0);
+      gload(p3, stage1);
+    }
+    f32x16 sacc = s_phase(0);
+    bf16x8 bp[2];
+    uint32_t bo_prev = 2 * TB, bo_next = TB;  // buffers of tiles i-1 (= i+2) and i+1
+    auto step = [&](int i, u32x4 (&st)[LOADS]) {
+      // phase A
+      if (i > 0) {
+        read_p(bp);
+        rescale();
+        pv_phase(bo_prev, bp);
+      }
+      x_write(sacc);
+      __syncthreads();
+      // phase B
+      softmax(mq0);
+      if (i + 1 < ntiles) sacc = s_phase(bo_next);
+      store_tile(st, bo_prev);  // tile i+2 over tile i-1
+      const uint16_t* pn;
+      uint32_t mn;
+      resolve(j0 + (i + 4) * 32, -2, pn, mn);
+      mq0 = mq1;
+      mq1 = mq2;
+      mq2 = mq3;
+      mq3 = mn;
+      __syncthreads();
+      gload(pn, st);
+      bo_prev = bo_prev == 2 * TB ? 0 : bo_prev + TB;  // tile i, i.e. i-1 of the next step
+      bo_next = bo_next == 2 * TB ? 0 : bo_next + TB;
+    };
+    for (int i = 0; i < ntiles; i += 2) {
+      step(i, stage0);
+      step(i + 1, stage1);
+    }
+    read_p(bp);  // P^T of the last tile (published before the last barrier)
+    rescale();
+    pv_phase(bo_prev, bp);
+  }
+
+  // the owners publish (reference, sum) per head; every wave normalises its own dims
+  {
+    const float l_tot = sum_over_xor8_16_32(l_part);
+    if (r4 == 0) SL[hp * 32 + hh] = float2{m_ref, l_tot};
+  }
+  __syncthreads();
+  const float2 mlv = SL[hp * 32 + n32];
+  const float m_fin = mlv.x, l_fin = mlv.y;
+  if (!head_ok) return;
+  const size_t orow = static_cast<size_t>(row) * p.n_heads + head;
+  // output element i of acc[dt]: head n32, dim dbase + 32dt + 8*(i/4) + 4h + i%4
+  if (p.n_splits == 1) {
+    const float a2 = p.sink ? sink_v * kLog2e : -INFINITY;
+    const float M = fmaxf(m_fin, a2);
+    const float f = (m_fin == -INFINITY) ? 0.f : exp2f(m_fin - M);
+    const float den = l_fin * f + ((a2 == -INFINITY) ? 0.f : exp2f(a2 - M));
+    const float inv = den > 0.f ? f / den : 0.f;
+    uint16_t* orow_p = p.out + orow * C;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = dbase + dt * 32 + g4 * 8 + 4 * h;
+        store_out4(orow_p + d0, acc[dt][4 * g4] * inv, acc[dt][4 * g4 + 1] * inv,
+                   acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv, d0, C, p.r, t, s_freq);
+      }
+    if (p.lse_out && h == 0 && slice == 0)
+      p.lse_out[orow] = l_fin > 0.f ? (m_fin + log2f(l_fin)) * kLn2 : -INFINITY;
+  } else {
+    float* pw = p.part + ((((static_cast<size_t>(row) * p.n_splits + split) * p.head_groups + hg) *
+                            NW + wave) * (DT * 4) * 256);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(pw + ((dt * 4 + g4) * 64 + l) * 4) =
+            f32x4{acc[dt][4 * g4], acc[dt][4 * g4 + 1], acc[dt][4 * g4 + 2], acc[dt][4 * g4 + 3]};
+    if (h == 0 && slice == 0) {
+      float* mlp = p.ml + ((static_cast<size_t>(row) * p.n_splits + split) * p.n_heads + head) * 2;
+      mlp[0] = m_fin;
+      mlp[1] = l_fin;
+    }
+  }
+}
+
 // Merge of the spans of one (query row, 64-head group): a thread takes 4 of the DT*4 chunks
 // a lane of one wave held (same head, 16 dims), merges the spans in a fixed order, adds the sink
 // once, normalises, rotates back and stores bf16.  Loads of up to kCombineMax spans are in flight
 // together.
 constexpr int kCombineMax = 8;
 
-template <int C, int HP>
-__global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_combine_kernel(MqaParams p) {
-  using SH = MqaShape<C, HP>;
-  constexpr int NW = SH::NW, CS = SH::CS, DT = SH::DT;
+template <int C, class SH>
+__global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
+  constexpr int HP = SH::HP, NW = SH::NW, CS = SH::CS, DT = SH::DT;
   constexpr int CPT = 4;                 // chunks per thread
   constexpr int GROUPS = DT * 4 / CPT;   // thread groups per (row, head group)
   const int bid = blockIdx.x;
@@ -610,7 +1018,7 @@ static int round_up(int x, int a) { return (x + a - 1) / a * a; }
 MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list) {
   MqaPlan pl;
   pl.head_pairs = 2;  // one instantiation: 64 heads (fewer heads leave waves idle)
-  pl.slices = c == 512 ? 2 : 1;
+  pl.slices = c == 512 ? 4 : 1;  // eight waves of 128-dim slices for c = 512
   pl.heads_per_wg = 32 * pl.head_pairs;
   pl.head_groups = (n_heads + pl.heads_per_wg - 1) / pl.heads_per_wg;
   const int waves = pl.head_pairs * pl.slices;
@@ -628,7 +1036,8 @@ MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list) {
     const int sr = round_up((list + s - 1) / s, 32);
     const int ns = (list + sr - 1) / sr;
     if (ns != s) continue;
-    const int tiles = (sr / 32) | 1;  // the kernel pads to an odd tile count
+    // tile counts are padded: even for the eight-wave kernel (c = 512), odd otherwise
+    const int tiles = c == 512 ? ((sr + 63) / 64) * 2 : ((sr / 32) | 1);
     const double rounds = std::ceil(base * ns / slots);
     double tm = rounds * (tiles * t_tile + t_fixed);
     if (ns > 1) tm += 2.0 * rows * ns * static_cast<double>(n_heads) * (c + 4) * 4.0 / bw + t_comb;
@@ -650,15 +1059,16 @@ size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c) {
   return (o + ml) * sizeof(float);
 }
 
-template <int C, int HP>
+template <int C, class SH, bool WIDE>
 static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
-  using SH = MqaShape<C, HP>;
   const size_t lds =
       SH::lds_fixed() + (prm.idx ? static_cast<size_t>(prm.split_rows) * sizeof(int) : 0);
   static size_t attr = 0;
   if (attr < lds) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_kernel<C, HP>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+    const void* kfn;
+    if constexpr (WIDE) kfn = reinterpret_cast<const void*>(mqa_wide_kernel<C>);
+    else kfn = reinterpret_cast<const void*>(mqa_kernel<C, SH::HP>);
+    hipError_t e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr = lds;
@@ -668,20 +1078,22 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((q.n_work + 7) / 8 * 8) * prm.head_groups;
   {
     ProfScope ps(prm.idx ? "mqa_sparse" : "mqa_dense", s);
-    mqa_kernel<C, HP><<<grid, SH::NT, lds, s>>>(q);
+    if constexpr (WIDE) mqa_wide_kernel<C><<<grid, SH::NT, lds, s>>>(q);
+    else mqa_kernel<C, SH::HP><<<grid, SH::NT, lds, s>>>(q);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || prm.n_splits == 1) return e;
   ProfScope ps("mqa_combine", s);
   constexpr int groups = SH::DT * 4 / 4;
-  mqa_combine_kernel<C, HP><<<static_cast<unsigned>(rows) * prm.head_groups * groups, SH::NT, 0, s>>>(prm);
+  mqa_combine_kernel<C, SH><<<static_cast<unsigned>(rows) * prm.head_groups * groups, SH::NT, 0, s>>>(prm);
   return hipGetLastError();
 }
 
 template <int C>
 static hipError_t launch_c(const MqaParams& prm, const MqaPlan& pl, int rows, hipStream_t s) {
-  if (pl.head_pairs == 2) return launch_t<C, 2>(prm, rows, s);
-  return hipErrorInvalidValue;
+  if (pl.head_pairs != 2) return hipErrorInvalidValue;
+  if constexpr (C == 512) return launch_t<C, MqaWideShape<C>, true>(prm, rows, s);
+  else return launch_t<C, MqaShape<C, 2>, false>(prm, rows, s);
 }
 
 hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& pl, hipStream_t s) {
