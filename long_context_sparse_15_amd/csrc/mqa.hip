@@ -489,13 +489,14 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
 // lane-swap instructions, no LDS round trip).  The owner publishes P^T (bf16, in the K-slot
 // order of the PV MFMAs) and the rescale factor of each head.
 //
-// Two barriers per tile, and matrix work on both sides of each:
-//   phase A of step i: P^T(i-1) and rescale factors in, rescale, PV(i-1); S partials of tile i
-//                      out; barrier
-//   phase B of step i: slice sums and softmax of tile i, P^T(i) out; S(i+1); tile i+2 from
-//                      registers into LDS, gathers of tile i+4 resolved; barrier; gathers issued
-// Key tiles live in a ring of three LDS buffers (tile t in buffer t % 3): during step i tile i-1
-// is read by PV in phase A and overwritten by tile i+2 in phase B, tile i+1 is read by S.
+// Two barriers per tile step i:
+//   phase A: tile i+1 from registers into LDS, this wave's S partial of tile i out, gathers of
+//            tile i+3 issued; barrier
+//   phase B: rescale by the factors of tile i-1; slice sums and softmax of tile i (P^T and
+//            factors out); PV of tile i-1; S of tile i+1; rows of tile i+4 resolved; barrier
+// Phase B is one branch-free block apart from the rare rescale, so the scheduler can spread
+// its 16 MFMAs over the softmax and address work.  Key tiles live in a ring of three LDS buffers
+// (tile t in buffer t % 3); P^T and the factors alternate between two buffers by tile parity.
 template <int C>
 struct MqaWideShape {
   static constexpr int HP = 2, DS = 4, NW = HP * DS, NT = 64 * NW;
@@ -507,9 +508,9 @@ struct MqaWideShape {
   static constexpr int TILE = 32 * C;           // bf16 elements per LDS tile
   static constexpr int NBUF = 3;
   static constexpr size_t off_sx = NBUF * TILE * sizeof(uint16_t);  // [HP][DS][4][64] f32x4
-  static constexpr size_t off_sp = off_sx + HP * DS * 4 * 64 * 16;  // [HP][8][32] 4 x bf16
-  static constexpr size_t off_sa = off_sp + HP * 8 * 32 * 8;        // [HP][32] rescale factor
-  static constexpr size_t off_sl = off_sa + HP * 32 * 4;            // [HP][32] (max, sum)
+  static constexpr size_t off_sp = off_sx + HP * DS * 4 * 64 * 16;  // [2][HP][8][32] 4 x bf16
+  static constexpr size_t off_sa = off_sp + 2 * HP * 8 * 32 * 8;    // [2][HP][32] factors
+  static constexpr size_t off_sl = off_sa + 2 * HP * 32 * 4;        // [HP][32] (max, sum)
   static constexpr size_t off_freq = off_sl + HP * 32 * 8;          // [C/2] RoPE frequencies
   static constexpr size_t lds_fixed() { return off_freq + (C / 2) * sizeof(float); }
 };
@@ -531,7 +532,7 @@ __device__ __forceinline__ float sum_over_xor8_16_32(float x) {
   return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
 
-template <int C>
+template <int C, bool SPARSE>
 __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaParams p) {
   using SH = MqaWideShape<C>;
   constexpr int HP = SH::HP, DS = SH::DS, NW = SH::NW, NT = SH::NT, CS = SH::CS, KK = SH::KK,
@@ -539,14 +540,14 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   constexpr uint32_t TB = TILE * 2;  // bytes per LDS tile
   static_assert(CPR == 64 && LOADS * NT == 32 * CPR, "one row per wave and load step");
   static_assert(KK <= 8 && DT <= 4, "offset tables below cover one 128-dim block");
-  static_assert(NT >= C / 2, "one thread per RoPE frequency");
+  static_assert(NT >= C / 2 && NT * LOADS * 16 >= TB, "prologue work splits over the threads");
   extern __shared__ __align__(16) unsigned char smem[];
   f32x4* SX = reinterpret_cast<f32x4*>(smem + SH::off_sx);
   uint2* SP = reinterpret_cast<uint2*>(smem + SH::off_sp);
   float* SA = reinterpret_cast<float*>(smem + SH::off_sa);
   float2* SL = reinterpret_cast<float2*>(smem + SH::off_sl);
   float* s_freq = reinterpret_cast<float*>(smem + SH::off_freq);
-  int* s_idx = reinterpret_cast<int*>(smem + SH::lds_fixed());  // [split_rows]
+  int* s_idx = reinterpret_cast<int*>(smem + SH::lds_fixed());  // [split_rows] (sparse)
 
   const int tid = threadIdx.x;
   const int l = lane_id();
@@ -563,7 +564,7 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   const int b = row / p.nq;
   const int j0 = split * p.split_rows;
   int pre0 = 0, pre1 = 0;
-  if (p.idx && l < 32) {
+  if (SPARSE && l < 32) {
     const int32_t* ir = p.idx + static_cast<size_t>(row) * p.k;
     pre0 = ir[min(j0 + l, p.k - 1)];
     pre1 = ir[min(j0 + 32 + l, p.k - 1)];
@@ -573,7 +574,7 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   const int n_w = min(p.n_win, t + 1);
   const int wlo = t - n_w + 1;
   int n_sel;
-  if (p.idx) {
+  if (SPARSE) {
     n_sel = p.k;
   } else {
     const long v = (static_cast<long>(t) + 1) / p.m;
@@ -585,26 +586,29 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   const bool head_ok = head < p.n_heads;
   const int dbase = slice * CS;
 
-  // row pointers of the tile at list row jt (lanes 0..31), masked rows read the window row of t
-  const uint16_t* const safe_row =
-      p.window + (static_cast<size_t>(b) * p.win_slots + (t % p.win_slots)) * C;
-  auto resolve = [&](int jt, int pre, const uint16_t*& ptr, uint32_t& mask) {
-    const int j = jt + l;
-    const uint16_t* pr = safe_row;
-    bool ok = false;
-    if (l < 32 && j < j1) {
-      if (j < n_sel) {
-        const int e = p.idx ? (pre >= -1 ? pre : s_idx[j - j0]) : j;
-        ok = e >= 0 && e < n_ent;
-        if (ok) pr = p.entries + (static_cast<size_t>(b) * p.n_max + e) * C;
-      } else {
-        const int u = wlo + (j - n_sel);
-        ok = true;
-        pr = p.window + (static_cast<size_t>(b) * p.win_slots + (u % p.win_slots)) * C;
-      }
-    }
-    ptr = pr;
+  // Row pointers of the tile at list row jt (lanes 0..31; other lanes' values are unused).
+  // Masked rows (past the span, an index outside the visible entries) read the window row of t.
+  // Branch-free: the index is always read (clamped into the span's index list) and both
+  // candidate pointers are formed, then selected.
+  const uint16_t* const ent_base = p.entries + static_cast<size_t>(b) * p.n_max * C;
+  const uint16_t* const win_base = p.window + static_cast<size_t>(b) * p.win_slots * C;
+  const uint16_t* const safe_row = win_base + static_cast<size_t>(t % p.win_slots) * C;
+  auto resolve_e = [&](int j, int e, const uint16_t*& ptr, uint32_t& mask) {
+    const bool in_span = l < 32 && j < j1;
+    const bool sel = j < n_sel;
+    const bool ok_e = e >= 0 && e < n_ent;
+    const int u = max(wlo + (j - n_sel), 0);
+    const uint16_t* pe = ent_base + static_cast<size_t>(ok_e ? e : 0) * C;
+    const uint16_t* pw = win_base + static_cast<size_t>(u % p.win_slots) * C;
+    const bool ok = in_span && (!sel || ok_e);
+    ptr = ok ? (sel ? pe : pw) : safe_row;
     mask = static_cast<uint32_t>(__ballot(ok));
+  };
+  auto resolve = [&](int jt, const uint16_t*& ptr, uint32_t& mask) {
+    const int j = jt + l;
+    int e = j;
+    if constexpr (SPARSE) e = s_idx[min(max(j - j0, 0), p.split_rows - 1)];
+    resolve_e(j, e, ptr, mask);
   };
   // wave `wave` loads rows wave, wave+8, wave+16, wave+24 of the tile, 16 bytes per lane
   auto gload = [&](const uint16_t* ptr, u32x4 (&st)[LOADS]) {
@@ -619,15 +623,16 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     }
   };
 
-  // even tile count (a masked tile pads odd spans); tiles 0 and 1 are gathered first
+  // even tile count (a masked tile pads odd spans); tiles 0 and 1 are gathered first, their
+  // indices read straight from global memory
   const int ntiles = j1 > j0 ? ((j1 - j0 + 63) / 64) * 2 : 0;
   u32x4 stage0[LOADS], stage1[LOADS];
   uint32_t mq0 = 0, mq1 = 0, mq2 = 0, mq3 = 0;  // valid masks of tiles i .. i+3
   if (ntiles > 0) {
     const uint16_t* p0;
     const uint16_t* p1;
-    resolve(j0, pre0 < -1 ? -1 : pre0, p0, mq0);
-    resolve(j0 + 32, pre1 < -1 ? -1 : pre1, p1, mq1);
+    resolve_e(j0 + l, SPARSE ? pre0 : j0 + l, p0, mq0);
+    resolve_e(j0 + 32 + l, SPARSE ? pre1 : j0 + 32 + l, p1, mq1);
     gload(p0, stage0);
     gload(p1, stage1);
   }
@@ -642,7 +647,7 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   }
   const float sink_v = (p.sink && head_ok) ? p.sink[head] : 0.f;
   const float freq_v = tid < (p.r >> 1) ? p.inv_freq[tid] : 0.f;
-  if (p.idx) {
+  if constexpr (SPARSE) {
     constexpr int IPT = 2;
     const int e1 = min(j1, n_sel);
     for (int base = j0; base < e1; base += NT * IPT) {
@@ -660,7 +665,13 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     }
   }
   if (tid < (p.r >> 1)) s_freq[tid] = freq_v;
-  __syncthreads();  // s_idx, s_freq
+  // the step before tile 0 runs a PV on buffer 2 with P = 0 and factors 1: zero both
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i)
+    reinterpret_cast<u32x4*>(smem + 2 * TB)[tid + i * NT] = u32x4{0, 0, 0, 0};
+  if (tid < HP * 8 * 32) SP[HP * 8 * 32 + tid] = uint2{0, 0};
+  if (tid < HP * 32) SA[HP * 32 + tid] = 1.f;
+  __syncthreads();  // s_idx, s_freq, zeroed buffers
 
   bf16x8 bq[KK];
 #pragma unroll
@@ -720,8 +731,6 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4*>(smem + st_off[i] + bo) = st[i];
   };
-  // every operand read of a phase is issued before its first MFMA (one LDS round trip per
-  // phase instead of one per MFMA pair)
   auto s_phase = [&](uint32_t bo) -> f32x16 {
     const unsigned char* Eb = smem + bo;
     u32x4 ea[KK];
@@ -730,27 +739,17 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) sacc = mfma_bf16_32x32x16(as_bf16x8(ea[kk]), bq[kk], sacc);
-    __builtin_amdgcn_sched_group_barrier(0x100, KK, 0);  // LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, KK, 0);  // then the MFMAs
     return sacc;
   };
   // P^T of a tile for head n32 in the K-slot order of the PV MFMAs (rows 16mm + 4h + 0..3, then
   // 16mm + 8 + 4h + 0..3)
-  auto read_p = [&](bf16x8 (&bp)[2]) {
-    const uint2* sp = SP + hp * 256 + n32;
+  auto read_p = [&](int par, bf16x8 (&bp)[2]) {
+    const uint2* sp = SP + (par * HP + hp) * 256 + n32;
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) {
       const uint2 lo = sp[(4 * mm + h) * 32];
       const uint2 hi = sp[(4 * mm + 2 + h) * 32];
       bp[mm] = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
-    }
-  };
-  // accumulators *= the rescale factor head n32's owner published (1 unless its reference moved)
-  auto rescale = [&]() {
-    const float alpha = SA[hp * 32 + n32];
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
   };
   auto pv_phase = [&](uint32_t bo, const bf16x8 (&bp)[2]) {
@@ -769,8 +768,6 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) acc[dt] = mfma_bf16_32x32x16(ev[dt][mm], bp[mm], acc[dt]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * DT, 0);  // LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * DT, 0);  // then the MFMAs
   };
   // this wave's S^T partial to LDS: element i of sacc holds row 8*(i/4) + 4h + i%4, head n32
   auto x_write = [&](const f32x16& sacc) {
@@ -781,83 +778,86 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   };
   // slice sums of this lane's share (rows 4r4..4r4+3 of head hh sit in lane 32*(r4&1) + hh,
   // elements 4*(r4/2)..+3, of each slice's partial), mask, online softmax, P^T and the rescale
-  // factor to LDS
-  auto softmax = [&](uint32_t msk) {
+  // factor to LDS (buffer par); branch-free
+  auto softmax = [&](uint32_t msk, int par) {
     const f32x4* src = SX + hp * DS * 256 + (r4 >> 1) * 64 + 32 * (r4 & 1) + hh;
     f32x4 s = src[0];
 #pragma unroll
     for (int ss = 1; ss < DS; ++ss) s += src[ss * 256];
-    if (msk != 0xffffffffu) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (!((msk >> (4 * r4 + e)) & 1u)) s[e] = -INFINITY;
-    }
+    for (int e = 0; e < 4; ++e) s[e] = ((msk >> (4 * r4 + e)) & 1u) ? s[e] : -INFINITY;
     const float mx =
         max_over_xor8_16_32(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * p.scale_log2;
     const bool move = mx > m_ref + 8.f;
-    float alpha = 1.f;
-    if (__ballot(move)) {
-      const float m_new = move ? mx : m_ref;
-      alpha = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_part *= alpha;
-      m_ref = m_new;
-    }
+    const float m_new = move ? mx : m_ref;
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+    l_part *= alpha;
+    m_ref = m_new;
     const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
     float pr[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(s[e], p.scale_log2, -mu));
     l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    SP[(hp * 8 + r4) * 32 + hh] = uint2{pack2(pr[0], pr[1]), pack2(pr[2], pr[3])};
-    if (r4 == 0) SA[hp * 32 + hh] = alpha;
+    SP[((par * HP + hp) * 8 + r4) * 32 + hh] = uint2{pack2(pr[0], pr[1]), pack2(pr[2], pr[3])};
+    SA[(par * HP + hp) * 32 + hh] = alpha;  // the eight lanes of a head write the same value
   };
 
   if (ntiles > 0) {
-    // tiles 0 and 1 into buffers 0 and 1, gathers of tiles 2 and 3, S(0)
-    store_tile(stage0, 0);
-    store_tile(stage1, TB);
+    // tile 0 into buffer 0, tile 2 gathered into its registers, S(0); tile 3 is resolved
+    const uint16_t* pnext;
     {
       const uint16_t* p2;
-      const uint16_t* p3;
-      resolve(j0 + 64, -2, p2, mq2);
-      resolve(j0 + 96, -2, p3, mq3);
+      resolve(j0 + 64, p2, mq2);
+      resolve(j0 + 96, pnext, mq3);
+      store_tile(stage0, 0);
       __syncthreads();
       gload(p2, stage0);
-      gload(p3, stage1);
     }
     f32x16 sacc = s_phase(0);
     bf16x8 bp[2];
-    uint32_t bo_prev = 2 * TB, bo_next = TB;  // buffers of tiles i-1 (= i+2) and i+1
+    uint32_t bo_prev = 2 * TB, bo_next = TB;  // buffers of tiles i-1 and i+1
     auto step = [&](int i, u32x4 (&st)[LOADS]) {
-      // phase A
-      if (i > 0) {
-        read_p(bp);
-        rescale();
-        pv_phase(bo_prev, bp);
-      }
+      const int par = i & 1;
+      // phase A: tile i+1 to LDS, S partial of tile i out, gathers of tile i+3
+      store_tile(st, bo_next);
       x_write(sacc);
+      gload(pnext, st);
       __syncthreads();
       // phase B
-      softmax(mq0);
-      if (i + 1 < ntiles) sacc = s_phase(bo_next);
-      store_tile(st, bo_prev);  // tile i+2 over tile i-1
-      const uint16_t* pn;
+      {
+        const float alpha = SA[((par ^ 1) * HP + hp) * 32 + n32];  // factor of tile i-1
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        }
+      }
+      read_p(par ^ 1, bp);
+      softmax(mq0, par);
+      pv_phase(bo_prev, bp);
+      sacc = s_phase(bo_next);
       uint32_t mn;
-      resolve(j0 + (i + 4) * 32, -2, pn, mn);
+      resolve(j0 + (i + 4) * 32, pnext, mn);
       mq0 = mq1;
       mq1 = mq2;
       mq2 = mq3;
       mq3 = mn;
       __syncthreads();
-      gload(pn, st);
       bo_prev = bo_prev == 2 * TB ? 0 : bo_prev + TB;  // tile i, i.e. i-1 of the next step
       bo_next = bo_next == 2 * TB ? 0 : bo_next + TB;
     };
     for (int i = 0; i < ntiles; i += 2) {
-      step(i, stage0);
-      step(i + 1, stage1);
+      step(i, stage1);
+      step(i + 1, stage0);
     }
-    read_p(bp);  // P^T of the last tile (published before the last barrier)
-    rescale();
+    // PV of the last tile (odd index: P^T in buffer 1)
+    {
+      const float alpha = SA[(1 * HP + hp) * 32 + n32];
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      }
+    }
+    read_p(1, bp);
     pv_phase(bo_prev, bp);
   }
 
@@ -1066,10 +1066,17 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   static size_t attr = 0;
   if (attr < lds) {
     const void* kfn;
-    if constexpr (WIDE) kfn = reinterpret_cast<const void*>(mqa_wide_kernel<C>);
-    else kfn = reinterpret_cast<const void*>(mqa_kernel<C, SH::HP>);
-    hipError_t e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
+    hipError_t e;
+    if constexpr (WIDE) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_wide_kernel<C, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_wide_kernel<C, false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    } else {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_kernel<C, SH::HP>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    }
     if (e != hipSuccess) return e;
     attr = lds;
   }
@@ -1078,7 +1085,10 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((q.n_work + 7) / 8 * 8) * prm.head_groups;
   {
     ProfScope ps(prm.idx ? "mqa_sparse" : "mqa_dense", s);
-    if constexpr (WIDE) mqa_wide_kernel<C><<<grid, SH::NT, lds, s>>>(q);
+    if constexpr (WIDE) {
+      if (prm.idx) mqa_wide_kernel<C, true><<<grid, SH::NT, lds, s>>>(q);
+      else mqa_wide_kernel<C, false><<<grid, SH::NT, lds, s>>>(q);
+    }
     else mqa_kernel<C, SH::HP><<<grid, SH::NT, lds, s>>>(q);
   }
   hipError_t e = hipGetLastError();
