@@ -100,6 +100,123 @@ __global__ __launch_bounds__(256) void gemm_tn_bf16_kernel(const uint16_t* __res
     }
 }
 
+// Large-tile variant for K % 64 == 0: 256x256 tile per workgroup of 8 waves (two per SIMD),
+// wave (wm, wn) owning rows wm*128.. and columns wn*64.. with 4x2 MFMA 32x32x16 tiles (128
+// accumulator VGPRs).  K advances 64 at a time through two LDS stages of A and B panels
+// (2 x 64 KiB) filled by direct global->LDS 16-byte loads: one load instruction writes 1 KiB
+// (8 rows of 128 bytes); which chunk a lane fetches sets the layout, so chunk c of row r sits at
+// 16-byte position c ^ g(r), g(r) = (r & 7) ^ ((r >> 3) & 1), which keeps the fragment reads
+// (lane -> row l%32, chunk pair) free of bank conflicts for 8- and 16-lane bank groups.  Tiles
+// are numbered in groups of 8 M-tiles and the numbering is laid out XCD by XCD (workgroup b runs
+// on XCD b % 8), so the 32 workgroups resident on an XCD share 8 A panels and 4 B panels
+// through its L2.
+constexpr int G2M = 256, G2N = 256, G2K = 64, G2_THREADS = 512;
+constexpr size_t kGemm2Lds = 2 * (G2M + G2N) * G2K * sizeof(uint16_t);  // 128 KiB
+
+__device__ __forceinline__ int g2_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__global__ __launch_bounds__(G2_THREADS) void gemm_tn_bf16_256_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, float* __restrict__ Cst,
+    int M, int N, int K, int tiles_m, int tiles_n, int per_xcd) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int bid = blockIdx.x;
+  const int t = (bid & 7) * per_xcd + (bid >> 3);
+  if (t >= tiles_m * tiles_n) return;
+  // grouped order: 8 M-tiles (fewer in the last group) per column sweep
+  const int group = t / (8 * tiles_n);
+  const int gm0 = group * 8;
+  const int gsize = min(8, tiles_m - gm0);
+  const int within = t - group * 8 * tiles_n;
+  const int tm = gm0 + within % gsize, tn = within / gsize;
+  const int m0 = tm * G2M, n0 = tn * G2N;
+
+  const int tid = threadIdx.x, l = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int h = l >> 5, n32 = l & 31;
+
+  // direct loads: instruction q of wave w covers panel rows (4w + q)*8 .. +7; lane i takes row
+  // +i/8, LDS position i%8, global chunk (i%8) ^ g(row)
+  const uint16_t* asrc[4];
+  const uint16_t* bsrc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (4 * wave + q) * 8 + (l >> 3);
+    const int c = (l & 7) ^ g2_swz(r);
+    asrc[q] = A + static_cast<size_t>(min(m0 + r, M - 1)) * K + c * 8;
+    bsrc[q] = Bw + static_cast<size_t>(min(n0 + r, N - 1)) * K + c * 8;
+  }
+  auto issue = [&](int kt, int stage) {
+    unsigned char* sa = smem + stage * 65536 + (4 * wave) * 8 * 128;
+    unsigned char* sb = sa + 32768;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_global_load_lds(asrc[q] + kt * G2K, (lds_void*)(sa + q * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bsrc[q] + kt * G2K, (lds_void*)(sb + q * 1024),
+                                       16, 0, 0);
+    }
+  };
+  // fragment offsets: row l%32 of a 32-row block (g depends on l only), chunk 2ks + h
+  const int gr = g2_swz(n32);
+  uint32_t aoff[4], boff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t pos = static_cast<uint32_t>((2 * ks + h) ^ gr) * 16u;
+    aoff[ks] = static_cast<uint32_t>(wm * 128 + n32) * 128u + pos;
+    boff[ks] = 32768u + static_cast<uint32_t>(wn * 64 + n32) * 128u + pos;
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
+
+  const int nk = K / G2K;
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < nk) issue(kt + 1, stage ^ 1);
+    const unsigned char* base = smem + stage * 65536;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 af[4], bf[2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = *reinterpret_cast<const u32x4*>(base + aoff[ks] + mi * 4096);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        bf[ni] = *reinterpret_cast<const u32x4*>(base + boff[ks] + ni * 4096);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mi]),
+                                                                as_bf16x8(bf[ni]), acc[mi][ni], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next stage has landed
+    __syncthreads();                                   // and every wave is done with this one
+  }
+  // D of a 32x32 tile: lane l holds column l%32, rows 8*(i/4) + 4h + i%4
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int n = n0 + wn * 64 + ni * 32 + n32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + wm * 128 + mi * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (m < M) Cst[static_cast<size_t>(m) * N + n] = acc[mi][ni][i];
+      }
+    }
+}
+
+
 // ============================================================================ helpers
 // E4M3 ("fn") encoding with round-to-nearest-even and saturation to +-448, from the format's
 // bit fields (bias 7, 3 mantissa bits, subnormal quantum 2^-9).
@@ -318,7 +435,21 @@ size_t compress_workspace(int B, int T, int n_cols) {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   const int M = a.B * a.T;
   const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (a.n_cols + GBN - 1) / GBN;
-  {
+  if (a.D % G2K == 0) {
+    static bool attr = false;
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tn_bf16_256_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(kGemm2Lds));
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    const int tm2 = (M + G2M - 1) / G2M, tn2 = (a.n_cols + G2N - 1) / G2N;
+    const int per_xcd = (tm2 * tn2 + 7) / 8;
+    ProfScope ps("compress_gemm", s);
+    gemm_tn_bf16_256_kernel<<<8 * per_xcd, G2_THREADS, kGemm2Lds, s>>>(
+        a.H, a.W, a.proj, M, a.n_cols, a.D, tm2, tn2, per_xcd);
+  } else {
     ProfScope ps("compress_gemm", s);
     gemm_tn_bf16_kernel<<<tiles_m * tiles_n, 256, 0, s>>>(a.H, a.W, a.proj, M, a.n_cols, a.D,
                                                           tiles_n);

@@ -29,7 +29,6 @@
 
 namespace csa {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct MqaParams {
   const uint16_t* q;
