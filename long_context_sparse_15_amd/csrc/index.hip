@@ -8,12 +8,12 @@
 // so the MFMA works on raw codes and the epilogue applies (w_h sq_h) per head and sk_s per entry.
 //
 // Top-k is exact with the lower index winning ties.  Scores become order-preserving 32-bit
-// keys.  Decode rows (few rows, many entries) use a first-level histogram of the top 12 key bits
-// built by the scoring kernel, a multi-workgroup collect of everything above the threshold bin
-// plus the (few) candidates inside it, and a per-row finalize that sorts the candidates and
-// emits the selection in ascending index order.  Prefill rows (many rows, <= 16384 entries
-// each) use one workgroup per row with the keys held in LDS: a 4-pass radix select finds the
-// k-th key, and an index-ordered compaction emits the selection already sorted.
+// keys.  Rows of up to 32768 entries use one workgroup per row with the keys in registers or
+// LDS: a sampled threshold, an exact select among the few candidates above it (or a radix
+// select) and an index-ordered compaction that emits the selection sorted.  Longer rows
+// (decode at long context, few rows) are cut into 4096-entry chunks, one workgroup each,
+// that share a sampled threshold and write their candidates; the last workgroup of a row selects
+// among them and emits the selection in ascending index order.
 #include "common.h"
 #include "kernels.h"
 
@@ -45,10 +45,9 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     const float* __restrict__ wi, const uint8_t* __restrict__ keys,
     const float* __restrict__ kscale, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int n_max, int H_I, int m, int chunk,
-    float* __restrict__ scores, int sstride, uint32_t* __restrict__ hist, int nchunks) {
+    float* __restrict__ scores, int sstride, int nchunks) {
   constexpr int KB = DI / 4;   // key bytes per lane (its lane group's K slice)
   constexpr int KK = DI / 32;  // 8-byte MFMA steps per slice
-  __shared__ uint32_t lhist[kHistBins];
 
   const int row = blockIdx.x / nchunks;
   const int b = row / nq;
@@ -58,10 +57,6 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const int tid = threadIdx.x;
   const int l = lane_id(), g = l >> 4, c16 = l & 15, wave = tid >> 6;
 
-  if (hist) {
-    for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0;
-    __syncthreads();
-  }
 
   if (e0 < e1) {
     // A operand: query codes of head ht*16 + c16, K slice g.  For DI = 128 (one 16x16x128 MFMA
@@ -152,7 +147,6 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       if (g == 0 && e < e1) {
         const float sc = part * kt.ks;
         srow[e] = sc;
-        if (hist) atomicAdd(&lhist[order_key(sc) >> 20], 1u);
       }
     };
     constexpr int PD = 3;
@@ -163,15 +157,6 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     for (int t = 0; t < TPW; ++t) {
       compute(t, kb[t % PD]);
       if (t + PD < TPW) load(t + PD, kb[t % PD]);
-    }
-  }
-
-  if (hist) {
-    __syncthreads();
-    uint32_t* grow = hist + static_cast<size_t>(row) * kHistBins;
-    for (int i = tid; i < kHistBins; i += 256) {
-      const uint32_t v = lhist[i];
-      if (v) atomicAdd(grow + i, v);
     }
   }
 }
@@ -854,219 +839,6 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
   ordered_emit<THREADS>(gk, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
 }
 
-// ============================================================================ multi-WG top-k
-// For long rows: the scoring kernel has accumulated a 4096-bin histogram of the top 12 key bits
-// per row.  Each collect workgroup takes kCollectChunk entries of one row, finds the threshold bin
-// tb (the bin holding the kk-th largest key), and writes the indices of its entries above tb and
-// the (key, index) pairs inside tb into its own region of the workspace, at offsets from a block
-// prefix sum (no global atomics, deterministic).  The finalize workgroup of the row concatenates
-// the regions, sorts the candidates by (key desc, index asc), takes what is needed and emits the
-// selection in ascending index order.
-constexpr int kCollectChunk = 4096;
-constexpr int kCandPerChunk = 1024;
-
-__device__ int find_threshold_bin(const uint32_t* __restrict__ h, int kk, uint32_t* s_tmp,
-                                  int* s_res) {
-  if (threadIdx.x == 0) s_res[0] = -1;
-  __syncthreads();
-  block_find_crossing<256>(h, kHistBins, static_cast<uint32_t>(kk), s_tmp, s_res);
-  return s_res[0];
-}
-
-__global__ __launch_bounds__(256) void topk_collect_kernel(
-    const float* __restrict__ scores, int sstride, const uint32_t* __restrict__ hist,
-    const int32_t* __restrict__ n_entries, const int32_t* __restrict__ pos, int nq, int m, int k,
-    int n_max, int nchunks, int selcap, uint32_t* __restrict__ ccount, int32_t* __restrict__ sel,
-    uint64_t* __restrict__ cand) {
-  constexpr int PER = kCollectChunk / 256;
-  __shared__ uint32_t s_tmp[4];
-  __shared__ int s_res[2];
-  const int row = blockIdx.x / nchunks;
-  const int chunk = blockIdx.x % nchunks;
-  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
-  const int tid = threadIdx.x;
-  const size_t rc = static_cast<size_t>(row) * nchunks + chunk;
-  if (n_vis <= k) return;  // everything is selected; finalize does not read the regions
-  const int e0 = chunk * kCollectChunk;
-  if (e0 >= n_vis) {
-    if (tid == 0) ccount[rc] = 0;
-    return;
-  }
-  const int tb = find_threshold_bin(hist + static_cast<size_t>(row) * kHistBins, k, s_tmp, s_res);
-  const float* srow = scores + static_cast<size_t>(row) * sstride;
-  uint32_t key[PER];
-  uint32_t nsel = 0, ncand = 0;
-  // thread t owns entries e0 + t*PER .. e0 + t*PER + PER-1, so a block prefix over threads
-  // writes every region in ascending entry order
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = e0 + tid * PER + i;
-    key[i] = e < n_vis ? order_key(srow[e]) : 0u;
-    const int bin = e < n_vis ? static_cast<int>(key[i] >> 20) : -2;
-    nsel += bin > tb;
-    ncand += bin == tb;
-  }
-  uint32_t total;
-  const uint32_t off = block_excl_scan<256>((nsel << 16) | ncand, s_tmp, &total);
-  uint32_t os = off >> 16, oc = off & 0xffff;
-  int32_t* sdst = sel + rc * selcap;
-  uint64_t* cdst = cand + rc * kCandPerChunk;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = e0 + tid * PER + i;
-    if (e >= n_vis) continue;
-    const int bin = static_cast<int>(key[i] >> 20);
-    if (bin > tb) {
-      if (os < static_cast<uint32_t>(selcap)) sdst[os] = e;
-      ++os;
-    } else if (bin == tb) {
-      if (oc < static_cast<uint32_t>(kCandPerChunk))
-        cdst[oc] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(e);
-      ++oc;
-    }
-  }
-  if (tid == 0) ccount[rc] = total;
-}
-
-// Exact selection by one workgroup streaming the row from global memory (fallback for rows whose
-// threshold bin overflows the candidate regions, e.g. massive ties).
-__global__ __launch_bounds__(256) void topk_finalize_kernel(
-    const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
-    const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int nchunks, int selcap,
-    const uint32_t* __restrict__ ccount, const int32_t* __restrict__ sel,
-    const uint64_t* __restrict__ cand, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint64_t* cbuf = reinterpret_cast<uint64_t*>(smem);            // kCandCap
-  int32_t* list = reinterpret_cast<int32_t*>(cbuf + kCandCap);   // kMaxTopK
-  uint32_t* hist = reinterpret_cast<uint32_t*>(list + kMaxTopK);  // kHistBins (fallback)
-  __shared__ uint32_t s_tmp[4];
-  __shared__ int s_res[2];
-  __shared__ uint32_t s_soff[1025], s_coff[1025];
-  __shared__ int s_bad;
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
-  const int kk = min(k, n_vis);
-  int32_t* out = idx_out + static_cast<size_t>(row) * k;
-  float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
-  const float* srow = scores + static_cast<size_t>(row) * sstride;
-  if (n_vis <= k) {
-    for (int j = tid; j < k; j += 256) {
-      out[j] = j < n_vis ? j : -1;
-      if (sout) sout[j] = j < n_vis ? srow[j] : -INFINITY;
-    }
-    return;
-  }
-  const int used = (n_vis + kCollectChunk - 1) / kCollectChunk;  // <= nchunks
-  if (tid == 0) s_bad = used > 1024 ? 1 : 0;
-  __syncthreads();
-  if (!s_bad) {
-    // per-chunk counts -> exclusive prefix sums (4 chunks per thread, one block scan each)
-    uint32_t ls = 0, lc = 0;
-    uint32_t cs[4], cc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ch = tid * 4 + j;
-      const uint32_t c = ch < used ? ccount[static_cast<size_t>(row) * nchunks + ch] : 0u;
-      cs[j] = c >> 16;
-      cc[j] = c & 0xffff;
-      if (cs[j] > static_cast<uint32_t>(selcap) || cc[j] > static_cast<uint32_t>(kCandPerChunk))
-        s_bad = 1;
-      ls += cs[j];
-      lc += cc[j];
-    }
-    uint32_t tot_s, tot_c;
-    uint32_t ps = block_excl_scan<256>(ls, s_tmp, &tot_s);
-    uint32_t pc = block_excl_scan<256>(lc, s_tmp, &tot_c);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ch = tid * 4 + j;
-      if (ch <= used) {
-        s_soff[ch] = ps;
-        s_coff[ch] = pc;
-      }
-      ps += cs[j];
-      pc += cc[j];
-    }
-    if (tid == 0) {
-      const int n_gt = static_cast<int>(tot_s), nc = static_cast<int>(tot_c);
-      if (n_gt >= kk || n_gt + nc < kk || nc > kCandCap) s_bad = 1;
-      s_soff[used] = tot_s;
-      s_coff[used] = tot_c;
-    }
-    __syncthreads();
-  }
-  if (s_bad) {
-    uint32_t T;
-    int need_eq;
-    auto kf = [&](int e) { return order_key(srow[e]); };
-    radix_select<256>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
-    ordered_emit<256>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
-    return;
-  }
-  const int n_gt = static_cast<int>(s_soff[used]);
-  const int nc = static_cast<int>(s_coff[used]);
-  const int need = kk - n_gt;
-  // LDS: list[0..n_gt) = entries above the threshold bin (ascending); ckey/cidx[0..nc) = the
-  // threshold bin's candidates (ascending index); chosen[0..need) = the candidates taken
-  uint32_t* ckey = reinterpret_cast<uint32_t*>(cbuf);
-  int32_t* cidx = reinterpret_cast<int32_t*>(ckey + kCandCap);
-  int32_t* chosen = list + n_gt;  // directly after the above-threshold list
-  auto chunk_of = [&](const uint32_t* off, int j) {
-    int lo = 0, hi = used;  // off[lo] <= j < off[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= static_cast<uint32_t>(j)) lo = mid; else hi = mid;
-    }
-    return lo;
-  };
-  for (int j = tid; j < n_gt; j += 256) {
-    const int ch = chunk_of(s_soff, j);
-    list[j] = sel[(static_cast<size_t>(row) * nchunks + ch) * selcap + (j - s_soff[ch])];
-  }
-  for (int j = tid; j < nc; j += 256) {
-    const int ch = chunk_of(s_coff, j);
-    const uint64_t v = cand[(static_cast<size_t>(row) * nchunks + ch) * kCandPerChunk + (j - s_coff[ch])];
-    ckey[j] = static_cast<uint32_t>(v >> 32);
-    cidx[j] = static_cast<int32_t>(v & 0xffffffffu);
-  }
-  __syncthreads();
-  // the need largest candidates (lower index first among equal keys), in ascending index order
-  uint32_t T2;
-  int need_eq2;
-  auto ck = [&](int j) { return ckey[j]; };
-  radix_select<256>(ck, nc, need, hist, s_tmp, s_res, T2, need_eq2);
-  ordered_emit_fn<256>(ck, nc, T2, need_eq2, need, [&](int slot, int j) { chosen[slot] = cidx[j]; });
-  __syncthreads();
-  // merge the two ascending lists by rank: an element's output slot is its own index plus the
-  // number of elements of the other list that are smaller (the lists are disjoint)
-  auto rank_in = [&](const int32_t* a, int n, int v) {
-    int lo = 0, hi = n;  // first position with a[pos] > v
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (a[mid] < v) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-  };
-  for (int j = tid; j < n_gt; j += 256) {
-    const int v = list[j];
-    const int slot = j + rank_in(chosen, need, v);
-    out[slot] = v;
-    if (sout) sout[slot] = srow[v];
-  }
-  for (int j = tid; j < need; j += 256) {
-    const int v = chosen[j];
-    const int slot = j + rank_in(list, n_gt, v);
-    out[slot] = v;
-    if (sout) sout[slot] = srow[v];
-  }
-  for (int j = kk + tid; j < k; j += 256) {
-    out[j] = -1;
-    if (sout) sout[j] = -INFINITY;
-  }
-}
-
 // ============================================================================ fill
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v, size_t n) {
   for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
@@ -1083,25 +855,217 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ============================================================================ multi-WG top-k
+// For rows longer than one workgroup's register file (decode at long context).  A row is cut
+// into chunks of kCollectChunk entries, one 1024-thread workgroup each.  Every workgroup of a row
+// takes the same kRowSamples evenly spaced keys of the row and derives the same threshold T_lo
+// (the lower edge of the bin holding the r-th largest sample, r a little above
+// kk * samples / n_vis with a margin of four standard deviations), so T_lo almost surely has
+// between kk and a few times kk keys at or above it.  Each workgroup writes its chunk's
+// (key, index) pairs >= T_lo in ascending index order into its own region (block prefix sum, no
+// global atomics).  A finalize workgroup per row (a second launch: a device-scope handoff
+// inside one launch costs an L2 write-back per workgroup on this multi-XCD part) concatenates
+// the regions (a list in ascending index order), finds the exact kk-th key among them with one
+// histogram pass over their actual range, and emits the keys above it plus the first ties in
+// index order.  A region overflow or too few candidates (ties, adversarial data) fall back to
+// the exact streaming select of the row.
+constexpr int kCollectChunk = 4096;
+constexpr int kCandPerChunk = 1024;
+constexpr int kRowSamples = 2048;
+constexpr int kSCandCap = 8192;  // candidates of a row held by its finalize workgroup
+constexpr size_t kMultiLds = static_cast<size_t>(kSCandCap) * 8 + kHistBins * 4;
+
+__global__ __launch_bounds__(1024) void topk_collect_kernel(
+    const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int nchunks,
+    uint32_t* __restrict__ ccount, uint64_t* __restrict__ cand) {
+  constexpr int THREADS = 1024, PER = kCollectChunk / THREADS, SPT = kRowSamples / THREADS;
+  static_assert(PER == 4, "one 16-byte load of keys per thread");
+  __shared__ uint32_t s_samp[kRowSamples];
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t s_tmp[THREADS / 64];
+  __shared__ int s_res[2];
+  const int row = blockIdx.x / nchunks;
+  const int chunk = blockIdx.x % nchunks;
+  const int tid = threadIdx.x;
+  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  const int kk = min(k, n_vis);
+  const float* srow = scores + static_cast<size_t>(row) * sstride;
+  if (n_vis <= k) return;  // everything is selected; finalize does not read the regions
+  const int used = (n_vis + kCollectChunk - 1) / kCollectChunk;  // chunks holding visible keys
+  if (chunk >= used) return;
+  const size_t rc = static_cast<size_t>(row) * nchunks + chunk;
+  const int e0 = chunk * kCollectChunk;
+
+  // ---- collect: this chunk's keys (one 16-byte load per thread, clamped into the row)
+  uint32_t key[PER];
+  {
+    const int base = e0 + tid * PER;
+    const float4 v = *reinterpret_cast<const float4*>(srow + min(base, sstride - 4));
+    const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) key[j] = base + j < n_vis ? order_key(f[j]) : 0u;
+  }
+  // samples: sample j is entry floor(j * n_vis / kRowSamples), the same in every workgroup
+#pragma unroll
+  for (int s = 0; s < SPT; ++s) {
+    const int j = s * THREADS + tid;
+    s_samp[j] = order_key(srow[static_cast<int>((static_cast<long long>(j) * n_vis) / kRowSamples)]);
+  }
+  __syncthreads();
+  const float expect = static_cast<float>(kk) * kRowSamples / static_cast<float>(n_vis);
+  int r = static_cast<int>(ceilf(expect + 4.f * sqrtf(expect) + 4.f));
+  if (r > kRowSamples) r = kRowSamples;
+  auto sf = [&](int j) { return s_samp[j]; };
+  uint32_t Tlo;
+  {
+    const uint32_t cb = radix_pass<THREADS>(sf, kRowSamples, 0u, 0u, 20, 4096,
+                                            static_cast<uint32_t>(r), hist, s_tmp, s_res);
+    const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
+    const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
+    __syncthreads();
+    Tlo = d1 << 20;
+    if (cb > 16) {  // crowded bin: refine by the next 12 bits
+      radix_pass<THREADS>(sf, kRowSamples, d1 << 20, 0xfff00000u, 8, 4096, r1, hist, s_tmp,
+                          s_res);
+      Tlo |= static_cast<uint32_t>(s_res[0]) << 8;
+      __syncthreads();
+    }
+  }
+  uint32_t own = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) own += (e0 + tid * PER + i < n_vis && key[i] >= Tlo) ? 1u : 0u;
+  uint32_t total;
+  uint32_t off = block_excl_scan<THREADS>(own, s_tmp, &total);
+  uint64_t* cdst = cand + rc * kCandPerChunk;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = e0 + tid * PER + i;
+    if (e < n_vis && key[i] >= Tlo) {
+      if (off < static_cast<uint32_t>(kCandPerChunk))
+        cdst[off] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(e);
+      ++off;
+    }
+  }
+  if (tid == 0) ccount[rc] = total;
+}
+
+__global__ __launch_bounds__(1024) void topk_finalize_kernel(
+    const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int nchunks,
+    const uint32_t* __restrict__ ccount, const uint64_t* __restrict__ cand,
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+  constexpr int THREADS = 1024;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(smem);              // kSCandCap
+  int32_t* cidx = reinterpret_cast<int32_t*>(ckey + kSCandCap);    // kSCandCap
+  uint32_t* hist = reinterpret_cast<uint32_t*>(cidx + kSCandCap);  // kHistBins
+  __shared__ uint32_t s_off[1025];
+  __shared__ uint32_t s_tmp[THREADS / 64];
+  __shared__ int s_res[2];
+  __shared__ int s_flag;
+  __shared__ uint32_t s_lo, s_hi;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  const int kk = min(k, n_vis);
+  int32_t* out = idx_out + static_cast<size_t>(row) * k;
+  float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
+  const float* srow = scores + static_cast<size_t>(row) * sstride;
+  if (n_vis <= k) {  // everything is selected
+    for (int j = tid; j < k; j += THREADS) {
+      out[j] = j < n_vis ? j : -1;
+      if (sout) sout[j] = j < n_vis ? srow[j] : -INFINITY;
+    }
+    return;
+  }
+  const int used = (n_vis + kCollectChunk - 1) / kCollectChunk;  // <= nchunks
+  if (tid == 0) {
+    s_flag = used > THREADS ? 1 : 0;  // 1 = take the exact fallback
+    s_lo = 0xffffffffu;
+    s_hi = 0u;
+  }
+  __syncthreads();
+  if (!s_flag) {
+    const uint32_t c = tid < used ? ccount[static_cast<size_t>(row) * nchunks + tid] : 0u;
+    if (c > static_cast<uint32_t>(kCandPerChunk)) s_flag = 1;
+    uint32_t tot;
+    const uint32_t o = block_excl_scan<THREADS>(c, s_tmp, &tot);
+    if (tid < used) s_off[tid] = o;
+    if (tid == 0) {
+      s_off[used] = tot;
+      if (tot > static_cast<uint32_t>(kSCandCap) || tot < static_cast<uint32_t>(kk)) s_flag = 1;
+    }
+    __syncthreads();
+  }
+  if (s_flag) {
+    uint32_t T;
+    int need_eq;
+    auto kf = [&](int e) { return order_key(srow[e]); };
+    radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
+    ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+    return;
+  }
+  const int nc = static_cast<int>(s_off[used]);
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int j = tid; j < nc; j += THREADS) {
+    int a = 0, b = used;  // s_off[a] <= j < s_off[b]
+    while (b - a > 1) {
+      const int mid = (a + b) >> 1;
+      if (s_off[mid] <= static_cast<uint32_t>(j)) a = mid; else b = mid;
+    }
+    const uint64_t v =
+        cand[(static_cast<size_t>(row) * nchunks + a) * kCandPerChunk + (j - s_off[a])];
+    const uint32_t kv = static_cast<uint32_t>(v >> 32);
+    ckey[j] = kv;
+    cidx[j] = static_cast<int32_t>(v & 0xffffffffu);
+    lo = min(lo, kv);
+    hi = max(hi, kv);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), o, 64)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), o, 64)));
+  }
+  if (lane_id() == 0) {
+    atomicMin(&s_lo, lo);
+    atomicMax(&s_hi, hi);
+  }
+  __syncthreads();
+  uint32_t T;
+  int need_eq;
+  auto ck = [&](int j) { return ckey[j]; };
+  select_kth<THREADS>(ck, nc, kk, s_lo, s_hi, hist, s_tmp, s_res, T, need_eq);
+  // the candidate list is in ascending index order
+  ordered_emit_fn<THREADS>(ck, nc, T, need_eq, k, [&](int slot, int j) {
+    out[slot] = cidx[j];
+    if (sout) sout[slot] = srow[cidx[j]];
+  });
+  for (int j = kk + tid; j < k; j += THREADS) {
+    out[j] = -1;
+    if (sout) sout[j] = -INFINITY;
+  }
+}
+
 // ============================================================================ launchers
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 static int score_stride(int n_max) { return (n_max + 63) & ~63; }
 
+// Rows longer than the 1024-thread sampled select holds (and not too many of them) use the
+// multi-workgroup select (measured slower than the one-workgroup select at 32K entries).
 bool index_use_multi(int rows, int n_max) { return n_max > kRowTopkBigN && rows <= 4096; }
 
 static int collect_chunks(int n_max) { return (n_max + kCollectChunk - 1) / kCollectChunk; }
-static int sel_cap(int k) { return k < kCollectChunk ? k : kCollectChunk; }
 
 size_t index_topk_workspace(int rows, int n_max, int k) {
   size_t b = align256(static_cast<size_t>(rows) * score_stride(n_max) * sizeof(float));
   if (index_use_multi(rows, n_max)) {
     const size_t rc = static_cast<size_t>(rows) * collect_chunks(n_max);
-    b += align256(static_cast<size_t>(rows) * kHistBins * 4);
     b += align256(rc * 4);
-    b += align256(rc * sel_cap(k) * 4);
     b += align256(rc * kCandPerChunk * 8);
   }
+  (void)k;
   return b;
 }
 
@@ -1110,18 +1074,12 @@ void index_topk_layout(IndexArgs& a, void* ws, int rows) {
   a.sstride = score_stride(a.n_max);
   a.scores = reinterpret_cast<float*>(p);
   p += align256(static_cast<size_t>(rows) * a.sstride * sizeof(float));
-  a.hist = nullptr;
   a.counters = nullptr;
-  a.sel = nullptr;
   a.cand = nullptr;
   if (index_use_multi(rows, a.n_max)) {
     const size_t rc = static_cast<size_t>(rows) * collect_chunks(a.n_max);
-    a.hist = reinterpret_cast<uint32_t*>(p);
-    p += align256(static_cast<size_t>(rows) * kHistBins * 4);
     a.counters = reinterpret_cast<uint32_t*>(p);
     p += align256(rc * 4);
-    a.sel = reinterpret_cast<int32_t*>(p);
-    p += align256(rc * sel_cap(a.k) * 4);
     a.cand = reinterpret_cast<uint64_t*>(p);
   }
 }
@@ -1133,21 +1091,20 @@ constexpr int kScoreTPW = CSA_SCORE_TPW;       // tiles of 16 entries per wave
 constexpr int kScoreChunk = 4 * kScoreTPW * 16;  // entries per workgroup
 
 template <int DI, int HT>
-static void launch_scores_t(const IndexArgs& a, int chunk, int nchunks, uint32_t* hist,
-                            hipStream_t s) {
+static void launch_scores_t(const IndexArgs& a, int chunk, int nchunks, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(nchunks) * static_cast<unsigned>(a.B * a.nq);
   ProfScope ps("index_score", s);
   index_score_kernel<DI, HT, kScoreTPW><<<grid, 256, 0, s>>>(a.qi, a.qi_scale, a.wi, a.keys, a.kscale,
                                                   a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
-                                                  chunk, a.scores, a.sstride, hist, nchunks);
+                                                  chunk, a.scores, a.sstride, nchunks);
 }
 
-static hipError_t launch_scores(const IndexArgs& a, int chunk, uint32_t* hist, hipStream_t s) {
+static hipError_t launch_scores(const IndexArgs& a, int chunk, hipStream_t s) {
   const int nchunks = (a.n_max + chunk - 1) / chunk;
   const int ht = (a.H_I + 15) / 16;
 #define CSA_SCORE_CASE(DI_, HT_)                            \
   if (a.d_I == DI_ && ht == HT_) {                         \
-    launch_scores_t<DI_, HT_>(a, chunk, nchunks, hist, s); \
+    launch_scores_t<DI_, HT_>(a, chunk, nchunks, s);              \
     return hipGetLastError();                              \
   }
   CSA_SCORE_CASE(128, 4)
@@ -1210,13 +1167,8 @@ static hipError_t launch_gemm_scores(const IndexArgs& a, hipStream_t s) {
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
   const int rows = a.B * a.nq;
   const bool multi = index_use_multi(rows, a.n_max);
-  hipError_t e;
-  if (multi) {
-    e = launch_fill_u32(a.hist, 0u, static_cast<size_t>(rows) * kHistBins, s);
-    if (e != hipSuccess) return e;
-  }
-  e = (!multi && use_gemm_scores(a)) ? launch_gemm_scores(a, s)
-                                     : launch_scores(a, kScoreChunk, multi ? a.hist : nullptr, s);
+  hipError_t e = (!multi && use_gemm_scores(a)) ? launch_gemm_scores(a, s)
+                                                : launch_scores(a, kScoreChunk, s);
   if (e != hipSuccess) return e;
   if (!multi) {
     if (a.n_max <= 4096) return launch_row_topk<256, kRowTopkMaxN>(a, rows, s);
@@ -1234,27 +1186,26 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const int ncc = collect_chunks(a.n_max);
-  const int scap = sel_cap(a.k);
   {
     ProfScope ps("topk_collect", s);
-    topk_collect_kernel<<<static_cast<unsigned>(ncc) * rows, 256, 0, s>>>(
-        a.scores, a.sstride, a.hist, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, ncc, scap,
-        a.counters, a.sel, a.cand);
+    topk_collect_kernel<<<static_cast<unsigned>(ncc) * rows, 1024, 0, s>>>(
+        a.scores, a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, ncc, a.counters,
+        a.cand);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = static_cast<size_t>(kCandCap) * 8 + kMaxTopK * 4 + kHistBins * 4;
   static bool attr_set = false;
   if (!attr_set) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_finalize_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(kMultiLds));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   ProfScope ps("topk_finalize", s);
-  topk_finalize_kernel<<<rows, 256, lds, s>>>(a.scores, a.sstride, a.n_entries, a.pos, a.nq, a.m,
-                                              a.k, a.n_max, ncc, scap, a.counters, a.sel, a.cand,
-                                              a.idx_out, a.score_out);
+  topk_finalize_kernel<<<rows, 1024, kMultiLds, s>>>(a.scores, a.sstride, a.n_entries, a.pos,
+                                                     a.nq, a.m, a.k, a.n_max, ncc, a.counters,
+                                                     a.cand, a.idx_out, a.score_out);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ constexpr int kHistBins = 4096;     // first-level top-k histogram: top 12 bits 
 constexpr int kCandCap = 4096;      // candidates kept for the exact refinement of one row
 constexpr int kMaxTopK = 4096;
 constexpr int kRowTopkMaxN = 16384; // row select with 256 threads holds this many keys in LDS
-constexpr int kRowTopkBigN = 32768; // row select with 1024 threads holds this many keys in LDS
+constexpr int kRowTopkBigN = 32768; // row select with 1024 threads holds this many keys
 
 // ---------------------------------------------------------------- indexer + top-k
 struct IndexArgs {
@@ -25,10 +25,8 @@ struct IndexArgs {
   int B, nq, n_max, H_I, d_I, m, k;
   float* scores;          // workspace [rows, sstride]
   int sstride;
-  uint32_t* hist;         // workspace [rows, kHistBins] (multi-workgroup select only)
-  uint32_t* counters;     // workspace [rows, chunks] packed (selected << 16 | candidates)
-  int32_t* sel;           // workspace [rows, chunks, min(k, chunk)]
-  uint64_t* cand;         // workspace [rows, chunks, candidates per chunk]
+  uint32_t* counters;     // workspace [rows, chunks]: candidates of each chunk
+  uint64_t* cand;         // workspace [rows, chunks, candidates per chunk]: (key, index)
   int32_t* idx_out;       // [rows, k]
   float* score_out;       // [rows, k] or nullptr
 };
