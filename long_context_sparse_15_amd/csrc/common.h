@@ -56,6 +56,15 @@ __device__ __forceinline__ float wave_max_xor(float v, int from_mask) {
   if (from_mask & 32) v = fmaxf(v, __shfl_xor(v, 32, 64));
   return v;
 }
+// v summed over the four lanes l, l^16, l^32, l^48 with the lane-swap instructions
+// (v_permlane16_swap / v_permlane32_swap: VALU, no LDS round trip).  Swapping a register with
+// itself leaves, in each lane, its own value in one result and its partner's in the other.
+__device__ __forceinline__ float wave_sum_xor16_32(float v) {
+  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
 __device__ __forceinline__ float wave_sum_xor(float v, int from_mask) {
   if (from_mask & 16) v += __shfl_xor(v, 16, 64);
   if (from_mask & 32) v += __shfl_xor(v, 32, 64);

@@ -51,112 +51,114 @@ __global__ __launch_bounds__(256) void index_score_kernel(
 
   const int row = blockIdx.x / nchunks;
   const int b = row / nq;
-  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
   const int e0 = (blockIdx.x % nchunks) * chunk;
-  const int e1 = min(n_vis, e0 + chunk);
   const int tid = threadIdx.x;
   const int l = lane_id(), g = l >> 4, c16 = l & 15, wave = tid >> 6;
 
-
-  if (e0 < e1) {
-    // A operand: query codes of head ht*16 + c16, K slice g.  For DI = 128 (one 16x16x128 MFMA
-    // per head tile) lane group g holds bytes 16g..16g+15 and 64+16g..64+16g+15 of the row, and
-    // of each key: the four lane groups of an entry then read 64 contiguous bytes per load.
-    // Other DI: bytes 32g.. in 8-byte steps of 16x16x32 MFMAs.
-    constexpr bool kWide = DI == 128;
-    i32x8 aw[HT];
-    long aq[HT][KK];
-    float wq[HT][4];
+  // A operand: query codes of head ht*16 + c16, K slice g.  For DI = 128 (one 16x16x128 MFMA
+  // per head tile) lane group g holds bytes 16g..16g+15 and 64+16g..64+16g+15 of the row, and
+  // of each key: the four lane groups of an entry then read 64 contiguous bytes per load.
+  // Other DI: bytes 32g.. in 8-byte steps of 16x16x32 MFMAs.
+  constexpr bool kWide = DI == 128;
+  i32x8 aw[HT];
+  long aq[HT][KK];
+  float wq[HT][4];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      const int head = ht * 16 + c16;
-      const uint8_t* qrow = qi + (static_cast<size_t>(row) * H_I + (head < H_I ? head : 0)) * DI;
-      const uint8_t* src = qrow + g * KB;
-      if constexpr (kWide) {
-        const u32x4* q16 = reinterpret_cast<const u32x4*>(qrow);
-        const u32x4 lo = head < H_I ? q16[g] : u32x4{0, 0, 0, 0};
-        const u32x4 hi = head < H_I ? q16[4 + g] : u32x4{0, 0, 0, 0};
-        aw[ht] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
-                       static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
-                       static_cast<int>(hi[2]), static_cast<int>(hi[3])};
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          aq[ht][kk] = head < H_I ? reinterpret_cast<const long*>(src)[kk] : 0;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hh = ht * 16 + g * 4 + i;
-        wq[ht][i] = hh < H_I ? wi[static_cast<size_t>(row) * H_I + hh] *
-                                   qi_scale[static_cast<size_t>(row) * H_I + hh]
-                             : 0.f;
-      }
-    }
-
-    const uint8_t* kbase = keys + static_cast<size_t>(b) * n_max * DI + (kWide ? 0 : g * KB);
-    const float* sbase = kscale + static_cast<size_t>(b) * n_max;
-    float* srow = scores + static_cast<size_t>(row) * sstride;
-
-    // Wave `wave` scores tiles wave, wave+4, ... (TPW tiles of 16 entries).  The sequence is
-    // fully unrolled straight-line code with PD tiles in flight; loads are unconditional (past
-    // the end they re-read entry e1-1, whose extra scores are never stored), so the compiler
-    // waits for exactly the tile it is about to use.
-    auto tile_entry = [&](int t) { return e0 + (wave + 4 * t) * 16 + c16; };
-    struct KeyTile {
-      i32x8 w;
-      long n[KK];
-      float ks;
-    };
-    auto load = [&](int t, KeyTile& kt) {
-      const int e = min(tile_entry(t), e1 - 1);
-      if constexpr (kWide) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(e) * DI);
-        const u32x4 lo = CSA_STREAM_LOAD(src + g), hi = CSA_STREAM_LOAD(src + 4 + g);
-        kt.w = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+  for (int ht = 0; ht < HT; ++ht) {
+    const int head = ht * 16 + c16;
+    const uint8_t* qrow = qi + (static_cast<size_t>(row) * H_I + (head < H_I ? head : 0)) * DI;
+    const uint8_t* src = qrow + g * KB;
+    if constexpr (kWide) {
+      const u32x4* q16 = reinterpret_cast<const u32x4*>(qrow);
+      const u32x4 lo = head < H_I ? q16[g] : u32x4{0, 0, 0, 0};
+      const u32x4 hi = head < H_I ? q16[4 + g] : u32x4{0, 0, 0, 0};
+      aw[ht] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
                      static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
                      static_cast<int>(hi[2]), static_cast<int>(hi[3])};
-      } else {
-        const long* src = reinterpret_cast<const long*>(kbase + static_cast<size_t>(e) * DI);
+    } else {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kt.n[kk] = CSA_STREAM_LOAD(src + kk);
-      }
-      kt.ks = sbase[e];
-    };
-    auto compute = [&](int t, const KeyTile& kt) {
-      f32x4 acc[HT];
+      for (int kk = 0; kk < KK; ++kk)
+        aq[ht][kk] = head < H_I ? reinterpret_cast<const long*>(src)[kk] : 0;
+    }
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (kWide) {
+    for (int i = 0; i < 4; ++i) {
+      const int hh = ht * 16 + g * 4 + i;
+      wq[ht][i] = hh < H_I ? wi[static_cast<size_t>(row) * H_I + hh] *
+                                 qi_scale[static_cast<size_t>(row) * H_I + hh]
+                           : 0.f;
+    }
+  }
+
+  const uint8_t* kbase = keys + static_cast<size_t>(b) * n_max * DI + (kWide ? 0 : g * KB);
+  const float* sbase = kscale + static_cast<size_t>(b) * n_max;
+  float* srow = scores + static_cast<size_t>(row) * sstride;
+
+  // Wave `wave` scores tiles wave, wave+4, ... (TPW tiles of 16 entries).  The sequence is
+  // fully unrolled straight-line code with PD tiles in flight; loads are unconditional (past
+  // the end they re-read the last visible entry, whose extra scores are never stored), so the
+  // compiler waits for exactly the tile it is about to use.
+  auto tile_entry = [&](int t) { return e0 + (wave + 4 * t) * 16 + c16; };
+  struct KeyTile {
+    i32x8 w;
+    long n[KK];
+    float ks;
+  };
+  auto load = [&](int t, KeyTile& kt, int emax) {
+    const int e = min(tile_entry(t), emax);
+    if constexpr (kWide) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(e) * DI);
+      const u32x4 lo = CSA_STREAM_LOAD(src + g), hi = CSA_STREAM_LOAD(src + 4 + g);
+      kt.w = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                   static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                   static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+    } else {
+      const long* src = reinterpret_cast<const long*>(kbase + static_cast<size_t>(e) * DI);
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_fp8_16x16x128(aw[ht], kt.w, acc[ht]);
-      } else {
+      for (int kk = 0; kk < KK; ++kk) kt.n[kk] = CSA_STREAM_LOAD(src + kk);
+    }
+    kt.ks = sbase[e];
+  };
+  auto compute = [&](int t, const KeyTile& kt, int e1) {
+    f32x4 acc[HT];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
+    for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kWide) {
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_fp8_16x16x32(aq[ht][kk], kt.n[kk], acc[ht]);
-      }
-      // ReLU as a signed integer max of the float's bits with 0 (one instruction)
-      float part = 0.f;
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_fp8_16x16x128(aw[ht], kt.w, acc[ht]);
+    } else {
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          part = fmaf(wq[ht][i], __int_as_float(max(__float_as_int(acc[ht][i]), 0)), part);
-      part = wave_sum_xor(part, 48);
-      const int e = tile_entry(t);
-      if (g == 0 && e < e1) {
-        const float sc = part * kt.ks;
-        srow[e] = sc;
-      }
-    };
-    constexpr int PD = 3;
-    KeyTile kb[PD];
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_fp8_16x16x32(aq[ht][kk], kt.n[kk], acc[ht]);
+    }
+    // ReLU as a signed integer max of the float's bits with 0 (one instruction)
+    float part = 0.f;
 #pragma unroll
-    for (int t = 0; t < PD; ++t) load(t, kb[t]);
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        part = fmaf(wq[ht][i], __int_as_float(max(__float_as_int(acc[ht][i]), 0)), part);
+    part = wave_sum_xor16_32(part);
+    const int e = tile_entry(t);
+    if (g == 0 && e < e1) {
+      const float sc = part * kt.ks;
+      srow[e] = sc;
+    }
+  };
+  // The first tiles are loaded before the row's visible length is known (clamped to the
+  // allocated entries; scores past the visible end are never stored), so no wave waits for
+  // the position and entry-count loads before its first key loads.
+  constexpr int PD = 3, NB = PD + 1;  // a spare buffer: tile t+PD's loads go out before tile t
+  KeyTile kb[NB];                      // is computed
+#pragma unroll
+  for (int t = 0; t < PD; ++t) load(t, kb[t], n_max - 1);
+  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  const int e1 = min(n_vis, e0 + chunk);
+  if (e0 < e1) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      compute(t, kb[t % PD]);
-      if (t + PD < TPW) load(t + PD, kb[t % PD]);
+      if (t + PD < TPW) load(t + PD, kb[(t + PD) % NB], e1 - 1);
+      compute(t, kb[t % NB], e1);
     }
   }
 }
