@@ -220,7 +220,7 @@ def prefill_workload(name, K, W):
     return res
 
 
-def cpu_baseline(name, budget_s=15.0):
+def cpu_baseline(name, budget_s=10.0):
     """The CPU oracle on a bounded sample of the same workload: decode steps of sampled
     sequences (same shapes and recipe, numpy generator), timed on the host cores."""
     import numpy as np
@@ -249,7 +249,7 @@ def cpu_baseline(name, budget_s=15.0):
                         lambda u: u % w.n_win, w.m, w.n_win, w.scale, x["inv_freq"])
         done += 1
         el = time.time() - t0
-        if el > budget_s or done >= 64:
+        if el > budget_s or done >= 4096:
             break
     return {"value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d decode tokens (sequences of the %s workload, %d distinct) in %.1f s"
