@@ -1176,7 +1176,9 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
     if (a.n_max <= 4096) return launch_row_topk<256, kRowTopkMaxN>(a, rows, s);
     if (a.n_max <= 16384) {
       ProfScope ps("topk_sample", s);
-      topk_sample_kernel<256, 64><<<rows, 256, 0, s>>>(a.scores, a.sstride, a.n_entries, a.pos,
+      // 512 threads x 32 keys (measured 1.83 ms against 2.89 ms for 256 x 64 and 3.68 ms for
+      // 1024 x 32 on the 64K-token prefill rows)
+      topk_sample_kernel<512, 32><<<rows, 512, 0, s>>>(a.scores, a.sstride, a.n_entries, a.pos,
                                                       a.nq, a.m, a.k, a.n_max, a.idx_out,
                                                       a.score_out);
       return hipGetLastError();
