@@ -65,6 +65,44 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v) {
   auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
+// Whole-wave integer scans and reductions from DPP lane moves and the lane-swap instructions,
+// all VALU: no LDS round trip per step.
+// Inclusive prefix sum over lanes 0..l: shifts by 1, 2, 4, 8 inside each 16-lane row (lanes
+// without a source read 0), then row r adds the total of row r-1 (rows 1, 3) and the total of
+// rows 0-1 (rows 2, 3) through the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int v = static_cast<int>(x);
+  int s = v + __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  s += __builtin_amdgcn_update_dpp(0, s, 0x112, 0xf, 0xf, true);          // row_shr:2
+  s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xf, 0xf, true);          // row_shr:4
+  s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xf, 0xf, true);          // row_shr:8
+  s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xa, 0xf, false);         // row_bcast:15
+  s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xc, 0xf, false);         // row_bcast:31
+  return static_cast<uint32_t>(s);
+}
+// x reduced over all 64 lanes: lanes l^1 and l^2 (quad permutes), then the mirrored half-row
+// and row, then l^16 and l^32 (lane swaps).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, Op op) {
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0xb1, 0xf,
+                                                              0xf, false)));  // [1,0,3,2]
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x4e, 0xf,
+                                                              0xf, false)));  // [2,3,0,1]
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x141, 0xf,
+                                                              0xf, false)));  // row_half_mirror
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x140, 0xf,
+                                                              0xf, false)));  // row_mirror
+  auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(s16[0], s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(s32[0], s32[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
 __device__ __forceinline__ float wave_sum_xor(float v, int from_mask) {
   if (from_mask & 16) v += __shfl_xor(v, 16, 64);
   if (from_mask & 32) v += __shfl_xor(v, 32, 64);

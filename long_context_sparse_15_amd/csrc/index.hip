@@ -328,14 +328,11 @@ __device__ void block_find_crossing(const uint32_t* bins, int nbins, uint32_t re
   const int per = nbins / THREADS;  // nbins is a multiple of THREADS
   uint32_t own = 0;
   for (int j = 0; j < per; ++j) own += bins[tid * per + j];
-  // inclusive suffix scan inside the wave (lane l: sum over lanes >= l)
-  uint32_t suf = own;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t v = __shfl_down(suf, off, 64);
-    if (l + off < 64) suf += v;
-  }
-  if (l == 0) s_tmp[wave] = suf;  // wave total
+  // inclusive suffix sum inside the wave (lane l: sum over lanes >= l) from the prefix sum
+  const uint32_t inc = wave_incl_scan(own);
+  const uint32_t wtot = __builtin_amdgcn_readlane(inc, 63);
+  const uint32_t suf = wtot - inc + own;
+  if (l == 0) s_tmp[wave] = wtot;
   __syncthreads();
   uint32_t later = 0;
   for (int w2 = wave + 1; w2 < NWAVE; ++w2) later += s_tmp[w2];
@@ -360,12 +357,7 @@ template <int THREADS>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
   constexpr int NWAVE = THREADS / 64;
   const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t u = __shfl_up(inc, off, 64);
-    if (l >= off) inc += u;
-  }
+  const uint32_t inc = wave_incl_scan(v);
   if (l == 63) s_tmp[wave] = inc;
   __syncthreads();
   uint32_t before = 0, tot = 0;
@@ -499,12 +491,8 @@ __device__ void radix_select(KeyFn key, int n, int kk, uint32_t* hist /*4096*/, 
           c4[j] = hist[l * 4 + j];
           own += c4[j];
         }
-        uint32_t suf = own;
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t v = __shfl_down(suf, off, 64);
-          if (l + off < 64) suf += v;
-        }
-        const uint32_t above = suf - own;
+        const uint32_t inc = wave_incl_scan(own);
+        const uint32_t above = __builtin_amdgcn_readlane(inc, 63) - inc;
         if (above < remaining && remaining <= above + own) {
           uint32_t cum = above;
           for (int j = 3; j >= 0; --j) {
@@ -535,10 +523,12 @@ __device__ void radix_select(KeyFn key, int n, int kk, uint32_t* hist /*4096*/, 
 template <int THREADS, typename KeyFn>
 __device__ uint32_t radix_pass(KeyFn key, int n, uint32_t prefix, uint32_t mask, int shift,
                                int nb, uint32_t remaining, uint32_t* hist, uint32_t* s_tmp,
-                               int* s_res) {
+                               int* s_res, bool zeroed = false) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < nb; i += THREADS) hist[i] = 0;
-  __syncthreads();
+  if (!zeroed) {  // a caller that cleared hist before its last barrier skips this
+    for (int i = tid; i < nb; i += THREADS) hist[i] = 0;
+    __syncthreads();
+  }
   for (int e = tid; e < n; e += THREADS) {
     const uint32_t kv = key(e);
     if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & (nb - 1)], 1u);
@@ -556,7 +546,7 @@ __device__ uint32_t radix_pass(KeyFn key, int n, uint32_t prefix, uint32_t mask,
 template <int THREADS, typename KeyFn>
 __device__ void select_kth(KeyFn key, int n, int kk, uint32_t lo, uint32_t hi,
                            uint32_t* hist /*4096*/, uint32_t* s_tmp, int* s_res, uint32_t& T,
-                           int& need_eq) {
+                           int& need_eq, bool zeroed = false) {
   __shared__ uint32_t s_bin[64];
   __shared__ uint32_t s_nb;
   const int tid = threadIdx.x;
@@ -566,7 +556,7 @@ __device__ void select_kth(KeyFn key, int n, int kk, uint32_t lo, uint32_t hi,
   const uint32_t pmask = top >= 32 ? 0u : ~((1u << top) - 1u);
   const uint32_t prefix = lo & pmask;
   const uint32_t c1 = radix_pass<THREADS>(key, n, prefix, pmask, shift, 4096,
-                                          static_cast<uint32_t>(kk), hist, s_tmp, s_res);
+                                          static_cast<uint32_t>(kk), hist, s_tmp, s_res, zeroed);
   const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
   const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
   __syncthreads();
@@ -654,16 +644,18 @@ __global__ __launch_bounds__(THREADS) void topk_row_kernel(
 
 // ============================================================================ sampled row top-k
 // One workgroup per row; thread t holds in registers the keys of the row's 16-byte chunks
-// i*THREADS + t, i < PER/4 (coalesced loads).
+// i*THREADS + t, i < PER/4 (coalesced loads), so chunk column i of all threads precedes column
+// i+1 in index order.
 //  1. the first key of every fourth chunk is a sample (1 in 16); the lower edge of the 12-bit
 //     bin holding the r-th largest sample (r a little above kk/16 with a margin of 4 standard
 //     deviations; refined by a second pass when that bin is crowded) is a threshold T_lo that
 //     almost surely has between kk and kCandCap keys at or above it;
-//  2. one block prefix sum over per-thread counts writes those candidate keys to LDS;
+//  2. each thread counts its candidates (keys >= T_lo) per chunk column, two 16-bit counts to a
+//     word; one block prefix sum over those words places every candidate (key, index) in LDS in
+//     ascending index order;
 //  3. select_kth finds the kk-th candidate key T and how many keys equal to T are taken;
-//  4. keys > T and keys == T set bits in two bitmaps of the row in LDS; one block prefix sum
-//     over the counts of each thread's bitmap words gives its output slots, so the selection
-//     comes out in ascending index order with the lowest indices winning ties.
+//  4. the index-ordered emission over the candidate list writes the keys above T and the first
+//     ties, so the selection comes out sorted with the lowest indices winning ties.
 // If the count misses [kk, kCandCap] (ties, adversarial data) the exact streaming select runs.
 template <int THREADS, int PER>
 __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
@@ -673,18 +665,20 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
   constexpr int CH = PER / 4;             // chunks per thread
   constexpr int SPT = CH / 4;             // samples per thread
   constexpr int NS = THREADS * SPT;       // sample slots
-  constexpr int NWORD = THREADS * PER / 32;
-  constexpr int WPT = PER / 32;           // bitmap words per thread
-  static_assert(CH % 4 == 0 && PER % 32 == 0, "chunk and word layout");
+  constexpr int NWAVE = THREADS / 64;
+  constexpr int CW = CH / 2;              // count words per thread, two chunk columns each
+  static_assert(CH % 4 == 0 && CW <= 4, "chunk and count layout");
+  static_assert(THREADS * 4 <= 0xffff, "a column's candidate count fits 16 bits");
   __shared__ uint32_t s_samp[NS];
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_ckey[kCandCap];
-  __shared__ uint32_t s_gtw[NWORD], s_eqw[NWORD];
-  __shared__ uint32_t s_tmp[THREADS / 64];
+  __shared__ int32_t s_cidx[kCandCap];
+  __shared__ u32x4 s_wcnt[NWAVE];
+  __shared__ uint32_t s_tmp[NWAVE];
   __shared__ int s_res[2];
   __shared__ uint32_t s_max;
   const int row = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
   const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
   const int kk = min(k, n_vis);
   int32_t* out = idx_out + static_cast<size_t>(row) * k;
@@ -710,6 +704,8 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) kr[i * 4 + j] = (base + j < n_vis) ? order_key(f[j]) : 0u;
   }
+  // the first histogram pass finds it cleared (written while the loads are in flight)
+  for (int i = tid; i < kHistBins; i += THREADS) s_hist[i] = 0u;
   {
     const int last = (n_vis - 1) & ~3;  // start of the chunk holding the last visible entry
     if (n_vis & 3) {
@@ -744,7 +740,7 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
   uint32_t Tlo;
   {
     const uint32_t cb = radix_pass<THREADS>(sf, ns, 0u, 0u, 20, 4096, static_cast<uint32_t>(r),
-                                            s_hist, s_tmp, s_res);
+                                            s_hist, s_tmp, s_res, /*zeroed=*/true);
     const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
     const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
     __syncthreads();
@@ -755,79 +751,82 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
       __syncthreads();
     }
   }
-  // count the candidates (visible keys >= T_lo) and their largest key
-  uint32_t own = 0, kmax = 0;
+  // candidates (visible keys >= T_lo) per chunk column, packed two columns to a word, and the
+  // largest candidate key
+  uint32_t cw[CW], kmax = 0;
 #pragma unroll
-  for (int i = 0; i < CH; ++i)
+  for (int w = 0; w < CW; ++w) cw[w] = 0u;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    uint32_t c = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool c = (i * THREADS + tid) * 4 + j < n_vis && kr[i * 4 + j] >= Tlo;
-      own += c ? 1u : 0u;
-      kmax = c ? max(kmax, kr[i * 4 + j]) : kmax;
+      const bool in = (i * THREADS + tid) * 4 + j < n_vis && kr[i * 4 + j] >= Tlo;
+      c += in ? 1u : 0u;
+      kmax = in ? max(kmax, kr[i * 4 + j]) : kmax;
     }
+    cw[i / 2] += c << (16 * (i & 1));
+  }
+  uint32_t inc[CW];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), off, 64)));
-  if (lane_id() == 0 && kmax) atomicMax(&s_max, kmax);
-  uint32_t cnt;
-  uint32_t off = block_excl_scan<THREADS>(own, s_tmp, &cnt);
+  for (int w = 0; w < CW; ++w) inc[w] = wave_incl_scan(cw[w]);
+  kmax = wave_max_u32(kmax);
+  if (l == 63) {
+    u32x4 t4 = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < CW; ++w) t4[w] = inc[w];
+    s_wcnt[wave] = t4;
+  }
+  if (l == 0 && kmax) atomicMax(&s_max, kmax);
+  // select_kth's histogram pass finds it cleared
+  for (int i = tid; i < kHistBins; i += THREADS) s_hist[i] = 0u;
+  __syncthreads();
+  // lane j < NWAVE takes wave j's totals; a scan across those lanes gives every wave the words
+  // of the waves before it and the block totals
+  uint32_t before[CW], tot[CW];
+  {
+    const int uw = __builtin_amdgcn_readfirstlane(wave);
+    const u32x4 mine = l < NWAVE ? s_wcnt[l] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < CW; ++w) {
+      const uint32_t sc = wave_incl_scan(mine[w]);
+      tot[w] = __builtin_amdgcn_readlane(sc, NWAVE - 1);
+      const uint32_t prev = uw > 0 ? __builtin_amdgcn_readlane(sc, uw > 0 ? uw - 1 : 0) : 0u;
+      before[w] = inc[w] - cw[w] + prev;
+    }
+  }
+  uint32_t cnt = 0;
+  uint32_t slot[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    slot[i] = cnt + ((before[i / 2] >> (16 * (i & 1))) & 0xffffu);
+    cnt += (tot[i / 2] >> (16 * (i & 1))) & 0xffffu;
+  }
   if (cnt >= static_cast<uint32_t>(kk) && cnt <= static_cast<uint32_t>(kCandCap)) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
+    for (int i = 0; i < CH; ++i) {
+      uint32_t sl = slot[i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if ((i * THREADS + tid) * 4 + j < n_vis && kr[i * 4 + j] >= Tlo) s_ckey[off++] = kr[i * 4 + j];
-    for (int w = tid; w < NWORD; w += THREADS) {
-      s_gtw[w] = 0u;
-      s_eqw[w] = 0u;
+      for (int j = 0; j < 4; ++j) {
+        const int e = (i * THREADS + tid) * 4 + j;
+        if (e < n_vis && kr[i * 4 + j] >= Tlo) {
+          s_ckey[sl] = kr[i * 4 + j];
+          s_cidx[sl] = e;
+          ++sl;
+        }
+      }
     }
     __syncthreads();
     uint32_t T;
     int need_eq;
     auto cf = [&](int j) { return s_ckey[j]; };
     select_kth<THREADS>(cf, static_cast<int>(cnt), kk, Tlo, s_max, s_hist, s_tmp, s_res, T,
-                        need_eq);
-    // bitmaps of the keys above T and equal to T
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = (i * THREADS + tid) * 4 + j;
-        const uint32_t kv = kr[i * 4 + j];
-        if (e < n_vis && kv >= T) atomicOr(kv > T ? &s_gtw[e >> 5] : &s_eqw[e >> 5], 1u << (e & 31));
-      }
-    __syncthreads();
-    // thread t emits the entries of words t*WPT .. t*WPT+WPT-1 in index order
-    uint32_t gw[WPT], ew[WPT], ngt = 0, neq = 0;
-#pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      gw[q] = s_gtw[tid * WPT + q];
-      ew[q] = s_eqw[tid * WPT + q];
-      ngt += __popc(gw[q]);
-      neq += __popc(ew[q]);
-    }
-    uint32_t tot;
-    const uint32_t before = block_excl_scan<THREADS>((ngt << 16) | neq, s_tmp, &tot);
-    int eq_seen = static_cast<int>(before & 0xffffu);
-    int slot = static_cast<int>(before >> 16) + min(eq_seen, need_eq);
-#pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      uint32_t bits = gw[q] | ew[q];
-      while (bits) {
-        const int bpos = __ffs(bits) - 1;
-        bits &= bits - 1u;
-        const int e = (tid * WPT + q) * 32 + bpos;
-        bool take = true;
-        if (!((gw[q] >> bpos) & 1u)) {
-          take = eq_seen < need_eq;
-          ++eq_seen;
-        }
-        if (take) {
-          out[slot] = e;
-          if (sout) sout[slot] = srow[e];
-          ++slot;
-        }
-      }
-    }
+                        need_eq, /*zeroed=*/true);
+    ordered_emit_fn<THREADS>(cf, static_cast<int>(cnt), T, need_eq, k, [&](int o, int j) {
+      const int e = s_cidx[j];
+      out[o] = e;
+      if (sout) sout[o] = srow[e];
+    });
     for (int j = kk + tid; j < k; j += THREADS) {
       out[j] = -1;
       if (sout) sout[j] = -INFINITY;
@@ -1024,11 +1023,8 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
     lo = min(lo, kv);
     hi = max(hi, kv);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), o, 64)));
-    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), o, 64)));
-  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   if (lane_id() == 0) {
     atomicMin(&s_lo, lo);
     atomicMax(&s_hi, hi);
