@@ -28,11 +28,15 @@ Readings taken where the pages are silent (also listed in the design notes):
   R13 the sink only adds exp(a_h) to the denominator;
   R14 the attention output's last r dims are rotated back by -t;
   R18 the query arrives RMS-normalised (its projection and norm are upstream) but not
-      rotated: the attention step applies RoPE at the query position t.
+      rotated: the attention step applies RoPE at the query position t;
+  R19 optional FP4 indexer keys are OCP MXFP4: 32 consecutive dims share one E8M0 scale
+      (shared exponent floor(log2 max|v|) - 2, all-zero block -127), elements E2M1 with ties to
+      even and saturation; the query stays E4M3.
 """
 import numpy as np
 
-from .numerics import (bf16_bits_to_f64, f64_to_bf16_bits, e4m3_decode, quantize_rows_e4m3)
+from .numerics import (bf16_bits_to_f64, f64_to_bf16_bits, e4m3_decode, quantize_rows_e4m3,
+                       quantize_rows_mxfp4, mxfp4_decode)
 
 
 # ----------------------------------------------------------------------------- a1 projections
@@ -154,14 +158,15 @@ def rope_rotate(x, positions, inv_freq, sign=1.0):
     return x
 
 
-def compress_tokens(h_bits, w_bits, params, mode, m, c, d_i, inv_freq, eps):
+def compress_tokens(h_bits, w_bits, params, mode, m, c, d_i, inv_freq, eps, idx_format="e4m3"):
     """Run the compressor on a whole token prefix H[0:T] (a1 + a2 + epilogue).
 
     Returns a dict with
       entries  uint16 [floor(T/m), c]  bf16 bits of RoPE(RMSNorm(C^Comp_i) * gamma, m*i)
       pre      float64 [floor(T/m), c] C^Comp before the norm (for stage-wise tests)
-      ikeys    uint8 [floor(T/m), d_I] E4M3 codes of K^IComp (CSA only; reading R5)
-      iscale   float32 [floor(T/m)]
+      ikeys    uint8 [floor(T/m), d_I] E4M3 codes of K^IComp (CSA only; reading R5), or with
+               idx_format "mxfp4" uint8 [floor(T/m), d_I/2] packed MXFP4 codes (reading R19)
+      iscale   float32 [floor(T/m)], or uint8 [floor(T/m), d_I/32] E8M0 block scales (mxfp4)
       ipre     float64 [floor(T/m), d_I]
       win      uint16 [T, c] bf16 bits of RoPE(RMSNorm(h_u W_win) * gamma_win, u) (reading R10)
     params: dict with Ba, Bb, BIa, BIb (CSA) or B (HCA), gamma, gamma_win.
@@ -178,7 +183,10 @@ def compress_tokens(h_bits, w_bits, params, mode, m, c, d_i, inv_freq, eps):
         pre = pool_overlap(s["Ca"], s["Cb"], s["Za"], s["Zb"], params["Ba"], params["Bb"], m, n)
         ipre = pool_overlap(s["Ia"], s["Ib"], s["IZa"], s["IZb"], params["BIa"], params["BIb"],
                             m, n)
-        codes, scale = quantize_rows_e4m3(ipre)
+        if idx_format == "mxfp4":
+            codes, scale = quantize_rows_mxfp4(ipre)
+        else:
+            codes, scale = quantize_rows_e4m3(ipre)
         out.update(ikeys=codes, iscale=scale, ipre=ipre)
     else:
         pre = pool_plain(s["C"], s["Z"], params["B"], m, n)
@@ -222,6 +230,18 @@ def index_scores(qi_codes, qi_scale, wi, ki_codes, ki_scale, n_vis):
     return np.maximum(dots, 0.0) @ np.asarray(wi, np.float64)
 
 
+def index_scores_mxfp4(qi_codes, qi_scale, wi, ki_packed, ki_scales, n_vis):
+    """index_scores with the keys in MXFP4 (reading R19: the pages' FP4 indexer keys, the
+    "FP4 indexer" of the V4 model card, stored as OCP MXFP4; the query stays E4M3 with a
+    per-head scale).  Same formula as index_scores; each key is decoded to its real value
+    (E2M1 code times its block's power-of-two scale) and the sums run in float64.
+    ki_packed [N, d_I/2] u8, ki_scales [N, d_I/32] u8 (E8M0).  Returns float64 [n_vis]."""
+    q = e4m3_decode(qi_codes) * np.asarray(qi_scale, np.float64)[:, None]   # [H_I, d_I]
+    k = mxfp4_decode(ki_packed[:n_vis], ki_scales[:n_vis])                 # [n_vis, d_I]
+    dots = k @ q.T
+    return np.maximum(dots, 0.0) @ np.asarray(wi, np.float64)
+
+
 def topk_select(scores, k):
     """TopK_k over the visible scores (book, chapter "Attention", section "CSA 的完整路径",
     I_t = TopK_k{I_{t,s} | s < floor((t+1)/m)}).  Ties: lower index wins; fewer than k
@@ -262,7 +282,7 @@ def attend(q_bits, rows_bits, sink, scale, t, inv_freq):
 
 
 def csa_query(t, q_bits, qi_codes, qi_scale, wi, sink, entries, ikeys, iscale, n_entries, win,
-              win_pos_to_row, m, k, n_win, scale, inv_freq):
+              win_pos_to_row, m, k, n_win, scale, inv_freq, idx_format="e4m3"):
     """One CSA query token t: score the visible entries, select the top-k, attend over the
     selected entries plus the sliding window plus the sink.
 
@@ -271,7 +291,8 @@ def csa_query(t, q_bits, qi_codes, qi_scale, wi, sink, entries, ikeys, iscale, n
     Returns dict(sel, scores, out, lse).
     """
     n_vis = visible_entries(t, m, n_entries)
-    scores = index_scores(qi_codes, qi_scale, wi, ikeys, iscale, n_vis)
+    score_fn = index_scores_mxfp4 if idx_format == "mxfp4" else index_scores
+    scores = score_fn(qi_codes, qi_scale, wi, ikeys, iscale, n_vis)
     sel = topk_select(scores, k)
     rows = [entries[sel]]
     wt = window_tokens(t, n_win)
@@ -293,19 +314,19 @@ def hca_query(t, q_bits, sink, entries, n_entries, win, win_pos_to_row, m, n_win
 
 
 def csa_layer(h_bits, w_bits, params, q_bits, qi_codes, qi_scale, wi, sink, m, c, d_i, k,
-              n_win, scale, inv_freq, eps, queries):
+              n_win, scale, inv_freq, eps, queries, idx_format="e4m3"):
     """Whole CSA layer from hidden states, for the listed query tokens (prefill rows or decode
     steps alike: a decode step at position t is the prefill row t of the longer prefix, since
     every quantity depends only on tokens <= t).  q_bits etc. are indexed by token.
     Returns (compressed dict, {t: csa_query result})."""
-    comp = compress_tokens(h_bits, w_bits, params, "csa", m, c, d_i, inv_freq, eps)
+    comp = compress_tokens(h_bits, w_bits, params, "csa", m, c, d_i, inv_freq, eps, idx_format)
     res = {}
     for t in queries:
         # entries closed by token t only depend on tokens <= t (causality); the oracle computes
         # them from the whole prefix once and lets visibility mask the rest.
         res[t] = csa_query(t, q_bits[t], qi_codes[t], qi_scale[t], wi[t], sink, comp["entries"],
                            comp["ikeys"], comp["iscale"], comp["entries"].shape[0], comp["win"],
-                           lambda u: u, m, k, n_win, scale, inv_freq)
+                           lambda u: u, m, k, n_win, scale, inv_freq, idx_format)
     return comp, res
 
 

@@ -12,6 +12,12 @@ below are the public format definitions, written out from the bit fields:
 * E4M3 (OCP 8-bit floating point, "fn" variant): 1 sign bit, 4 exponent bits (bias 7), 3
   mantissa bits; no infinities; S.1111.111 is NaN; largest finite magnitude 448; exponent
   field 0 encodes subnormals m/8 * 2^-6.
+* MXFP4 (OCP Microscaling Formats v1.0): blocks of 32 consecutive elements share one E8M0
+  scale (an 8-bit biased exponent, value 2^(byte-127), byte 255 = NaN); each element is E2M1
+  (1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4,
+  6, exponent field 0 = subnormal 0/0.5).  The shared exponent of a block is
+  floor(log2(max|v|)) - 2, 2 being the largest E2M1 exponent, and each element is v / 2^exp
+  rounded to E2M1 with ties to the even code and saturation at 6.
 """
 import numpy as np
 
@@ -116,3 +122,71 @@ def quantize_rows_e4m3(x):
     scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
     codes = e4m3_encode(x / scale.astype(np.float64)[..., None])
     return codes, scale
+
+
+# ----------------------------------------------------------------------------- MXFP4
+
+# E2M1 magnitudes of codes 0..7 (code bit 3 is the sign)
+_E2M1_POS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+_E2M1 = np.concatenate([_E2M1_POS, -_E2M1_POS])
+MX_BLOCK = 32
+
+
+def e2m1_decode(codes):
+    """Decode E2M1 codes (0..15, sign in bit 3) to float64."""
+    return _E2M1[np.asarray(codes, dtype=np.uint8) & np.uint8(0xF)]
+
+
+def e2m1_encode(x):
+    """Round float64 values to E2M1 codes: nearest magnitude, ties to the even code (mantissa
+    bit 0), magnitudes beyond 6 saturate to 6.  The sign bit follows the sign of x, so values
+    that round to zero keep their sign (code 8 for negatives)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 6.0)
+    lo = np.clip(np.searchsorted(_E2M1_POS, a, side="right") - 1, 0, 7)
+    hi = np.clip(lo + 1, 0, 7)
+    dlo = a - _E2M1_POS[lo]
+    dhi = _E2M1_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi != lo) & ((hi & 1) == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | np.uint8(8), code).astype(np.uint8)
+
+
+def mx_shared_exponent(amax):
+    """Shared exponent of an MXFP4 block with largest magnitude amax: floor(log2(amax)) - 2,
+    clamped to the E8M0 range [-127, 127]; an all-zero block takes -127.  floor(log2) comes
+    from the binary exponent of frexp (amax = f * 2^e, 0.5 <= f < 1), so it is exact."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(amax)
+    se = (e.astype(np.int64) - 1) - 2
+    se = np.where(amax > 0, se, -127)
+    return np.clip(se, -127, 127)
+
+
+def quantize_rows_mxfp4(x):
+    """MXFP4 quantization of rows whose length is a multiple of 32 (reading: the indexer keys'
+    FP4 format is OCP MXFP4 with blocks of 32 consecutive dims).  Returns (packed uint8
+    [..., d/2]: element 2i in the low nibble of byte i, element 2i+1 in the high nibble;
+    scales uint8 [..., d/32]: E8M0 byte = shared exponent + 127)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    assert d % MX_BLOCK == 0
+    blocks = x.reshape(x.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
+    se = mx_shared_exponent(np.max(np.abs(blocks), axis=-1))
+    codes = e2m1_encode(blocks / np.exp2(se.astype(np.float64))[..., None]).reshape(x.shape)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << np.uint8(4))).astype(np.uint8)
+    return packed, (se + 127).astype(np.uint8)
+
+
+def mxfp4_decode(packed, scales):
+    """Real values of MXFP4 rows: packed uint8 [..., d/2], scales uint8 [..., d/32]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    codes = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    codes[..., 0::2] = packed & np.uint8(0xF)
+    codes[..., 1::2] = packed >> np.uint8(4)
+    vals = e2m1_decode(codes)
+    d = vals.shape[-1]
+    blocks = vals.reshape(vals.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
+    mult = np.exp2(scales.astype(np.float64) - 127.0)
+    return (blocks * mult[..., None]).reshape(vals.shape)

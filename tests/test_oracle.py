@@ -72,6 +72,98 @@ def test_e4m3_encode_matches_torch_rne():
     assert np.all(O.e4m3_encode(np.array([500.0, 1e6, -1e9])) == np.array([0x7E, 0x7E, 0xFE]))
 
 
+def test_e2m1_table_spec_points():
+    g = _gold("mxfp4_points.json")
+    for code, val in g["e2m1"]:
+        got = float(O.e2m1_decode(np.array([code]))[0])
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), code
+
+
+def test_e2m1_encode_spec_examples():
+    g = _gold("mxfp4_points.json")
+    for x, code in g["encode"]:
+        assert int(O.e2m1_encode(np.array([x]))[0]) == code, x
+
+
+def test_e2m1_encode_is_nearest_with_even_ties_brute_force():
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    xs = np.concatenate([np.linspace(-8, 8, 4001), np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5,
+                                                             5.0, -0.25, -5.0])])
+    got = O.e2m1_encode(xs)
+    for x, c in zip(xs, got):
+        a = min(abs(x), 6.0)
+        d = np.abs(mags - a)
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        assert (int(c) & 7) == want and (int(c) >> 3) == int(np.signbit(x)), x
+
+
+def test_mx_shared_exponent_fixture_and_torch_e8m0():
+    g = _gold("mxfp4_points.json")
+    for b in g["blocks"]:
+        assert int(O.mx_shared_exponent(np.array([b["amax"]]))[0]) + 127 == b["scale_byte"], b
+    # floor(log2(x)) of a normal binary32 is its biased exponent field minus 127; the shared
+    # exponent is that minus 2 (the largest E2M1 exponent), clamped to E8M0's range
+    rng = np.random.default_rng(21)
+    a = np.exp2(rng.uniform(-125, 125, 4000)).astype(np.float32)
+    field = ((a.view(np.uint32) >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int64)
+    want = np.clip(field - 127 - 2, -127, 127)
+    assert np.array_equal(O.mx_shared_exponent(a.astype(np.float64)), want)
+
+
+def test_quantize_rows_mxfp4_packing_hand_example():
+    x = np.zeros((1, 64))
+    x[0, :4] = [1.0, 2.0, 3.0, 4.0]      # block 0: amax 4 -> exponent 0, codes 2, 4, 5, 6
+    x[0, 32:34] = [-0.75, 0.1875]        # block 1: amax 0.75 -> exponent -3, scaled -6, 1.5
+    packed, scales = O.quantize_rows_mxfp4(x)
+    assert list(scales[0]) == [127, 124]
+    assert list(packed[0, :2]) == [0x42, 0x65] and np.all(packed[0, 2:16] == 0)
+    assert list(packed[0, 16:17]) == [0x3F] and np.all(packed[0, 17:] == 0)
+    assert np.array_equal(O.mxfp4_decode(packed, scales), x)
+
+
+def test_quantize_rows_mxfp4_roundtrip_and_error_bound():
+    rng = np.random.default_rng(22)
+    # values already on the grid round-trip exactly
+    codes = rng.integers(0, 16, (8, 128)).astype(np.uint8)
+    codes[:, ::32] = 7                   # every block reaches magnitude 6: exponent = block's
+    se = rng.integers(-10, 10, (8, 4))
+    x = O.e2m1_decode(codes) * np.repeat(np.exp2(se.astype(np.float64)), 32, axis=1)
+    p, s = O.quantize_rows_mxfp4(x)
+    assert np.array_equal(O.mxfp4_decode(p, s), x)
+    # random rows: each element within half a grid step of its scaled value (or clamped to 6)
+    y = rng.standard_normal((64, 128)) * np.exp2(rng.integers(-8, 8, (64, 1)))
+    p, s = O.quantize_rows_mxfp4(y)
+    d = O.mxfp4_decode(p, s)
+    X = np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=1)
+    a = np.abs(y) / X
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    err = np.abs(d - y) / X
+    clamp = np.maximum(a - 6.0, 0.0)
+    assert np.all(err <= 0.5 * step + clamp + 1e-12)
+    assert np.all(np.max(np.abs(d), axis=1) > 0)
+
+
+def test_index_scores_mxfp4_equals_e4m3_path_on_shared_values():
+    # keys whose real values are exact in both formats (E2M1 magnitudes x 2^e, |.| <= 448):
+    # the MXFP4 scorer must give exactly the E4M3 scorer's scores
+    rng = np.random.default_rng(23)
+    H, d, N = 4, 64, 50
+    codes = rng.integers(0, 16, (N, d)).astype(np.uint8)
+    codes[:, ::32] = 7
+    se = rng.integers(-3, 5, (N, d // 32))
+    kv = O.e2m1_decode(codes) * np.repeat(np.exp2(se.astype(np.float64)), 32, axis=1)
+    kp, ks = O.quantize_rows_mxfp4(kv)
+    ke = O.e4m3_encode(kv)
+    assert np.array_equal(O.e4m3_decode(ke), kv)
+    qc = S.e4m3_normalish(rng, (H, d))
+    qs = rng.uniform(0.5, 2.0, H).astype(np.float32)
+    wi = rng.standard_normal(H).astype(np.float32)
+    a = O.index_scores(qc, qs, wi, ke, np.ones(N, np.float32), N - 3)
+    b = O.index_scores_mxfp4(qc, qs, wi, kp, ks, N - 3)
+    assert a.shape == (N - 3,) and np.array_equal(a, b)
+
+
 def test_bf16_rounding_matches_torch():
     rng = np.random.default_rng(12)
     x = np.concatenate([rng.standard_normal(50000) * 10.0 ** rng.integers(-30, 30, 50000),
@@ -456,3 +548,15 @@ def test_compress_epilogue_closed_forms():
     dec = O.e4m3_decode(comp["ikeys"]) * comp["iscale"][:, None].astype(np.float64)
     big = np.abs(comp["ipre"]) > comp["iscale"][:, None] * 2.0 ** -6
     assert np.all(np.abs(dec - comp["ipre"])[big] <= np.abs(comp["ipre"])[big] * 2.0 ** -4 + 1e-12)
+    # the same layer with MXFP4 keys: identical entries and pooled keys; every key element within
+    # half an E2M1 step of its block-scaled value (or clamped at 6)
+    c4 = O.compress_tokens(x["H"][0], x["W"], params, "csa", w.m, w.c, w.d_I, x["inv_freq"],
+                           1e-6, idx_format="mxfp4")
+    assert np.array_equal(c4["entries"], comp["entries"]) and np.array_equal(c4["ipre"],
+                                                                             comp["ipre"])
+    assert c4["ikeys"].shape == (16, w.d_I // 2) and c4["iscale"].shape == (16, w.d_I // 32)
+    X = np.repeat(np.exp2(c4["iscale"].astype(np.float64) - 127), 32, axis=1)
+    a = np.abs(c4["ipre"]) / X
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    err = np.abs(O.mxfp4_decode(c4["ikeys"], c4["iscale"]) - c4["ipre"]) / X
+    assert np.all(err <= 0.5 * step + np.maximum(a - 6.0, 0.0) + 1e-12)
