@@ -44,6 +44,14 @@ extern "C" {
 #define CSA_MODE_CSA 0 /* overlapping m-token compressor + lightning indexer + top-k */
 #define CSA_MODE_HCA 1 /* non-overlapping m'-token compressor, dense over closed entries */
 
+/* Storage of the indexer keys K^IComp (csa_config_t.idx_key_format).  The pages give the
+ * indexer's QK path in FP8 and, for V4's indexer, FP4 ("DeepSeek V4 模型技术大全", chapter
+ * "Attention", section "注意力实现细节"); the bit layouts are the public OCP formats. */
+#define CSA_IDX_E4M3 0  /* e4m3 codes [idx_dim] + one fp32 scale per entry (max|k|/448) */
+#define CSA_IDX_MXFP4 1 /* OCP MXFP4: E2M1 codes packed two per byte [idx_dim/2] (dim 2i in the
+                           low nibble of byte i) + one E8M0 scale byte per 32 dims (shared
+                           exponent floor(log2 max|k|) - 2); the query stays e4m3 */
+
 /* Operation ids for csa_workspace_size(). */
 #define CSA_OP_COMPRESS 0
 #define CSA_OP_INDEX_TOPK 1
@@ -57,7 +65,8 @@ extern "C" {
  *   head_dim in {128, 256, 512};
  *   rope_dim even, 2 <= rope_dim <= min(head_dim, 128);
  *   1 <= n_heads <= 128;  n_win in 1..1024;
- *   CSA: idx_dim in {32, 64, 128}, 1 <= idx_heads <= 64, 1 <= top_k <= 4096, m >= 1;
+ *   CSA: idx_dim in {32, 64, 128}, 1 <= idx_heads <= 64, 1 <= top_k <= 4096, m >= 1,
+ *        idx_key_format CSA_IDX_E4M3 or CSA_IDX_MXFP4;
  *   HCA: m >= 1;  hidden (compressor only) a positive multiple of 32. */
 typedef struct csa_config {
   int32_t mode;       /* CSA_MODE_CSA or CSA_MODE_HCA */
@@ -75,12 +84,16 @@ typedef struct csa_config {
   const float* rope_inv_freq; /* device fp32 [rope_dim/2]: angle of pair i at position p is
                                  p * rope_inv_freq[i] (base 160000 for compressed layers; any
                                  table, e.g. YaRN-scaled, may be passed) */
+  int32_t idx_key_format;     /* CSA_IDX_E4M3 (0) or CSA_IDX_MXFP4 (1); CSA only */
 } csa_config_t;
 
 /* Caller-owned per-sequence attention state for B sequences (all device pointers).
  *  entries   bf16 [B, n_max, head_dim]  compressed entries, RMS-normalised and rotated
- *  idx_keys  e4m3 [B, n_max, idx_dim]   indexer keys K^IComp (CSA; NULL for HCA)
- *  idx_scale fp32 [B, n_max]            per-entry scale of idx_keys (CSA; NULL for HCA)
+ *  idx_keys  e4m3 [B, n_max, idx_dim]   indexer keys K^IComp (CSA; NULL for HCA); with
+ *            CSA_IDX_MXFP4: uint8 [B, n_max, idx_dim/2] packed E2M1 codes
+ *  idx_scale fp32 [B, n_max]            per-entry scale of idx_keys (CSA; NULL for HCA); with
+ *            CSA_IDX_MXFP4 the same 4 bytes per entry hold the idx_dim/32 E8M0 block scales,
+ *            block b in byte b (unused bytes are ignored)
  *  window    bf16 [B, win_slots, head_dim]  uncompressed window KV, token u in row u%win_slots
  *  tail      fp32 [B, tail_rows, tail_cols] compressor projections of the last tail_rows tokens
  *            (row u % tail_rows); only used by the compressor (csa_tail_shape gives the shape)

@@ -55,6 +55,9 @@ int check_config(const csa_config_t* c, bool need_compressor) {
       return fail(CSA_ERR_INVALID_ARG, "idx_heads=%d not in 1..64", c->idx_heads);
     if (c->top_k < 1 || c->top_k > csa::kMaxTopK)
       return fail(CSA_ERR_INVALID_ARG, "top_k=%d not in 1..%d", c->top_k, csa::kMaxTopK);
+    if (c->idx_key_format != CSA_IDX_E4M3 && c->idx_key_format != CSA_IDX_MXFP4)
+      return fail(CSA_ERR_INVALID_ARG, "idx_key_format=%d is neither E4M3 nor MXFP4",
+                  c->idx_key_format);
   }
   if (need_compressor) {
     if (c->hidden < 32 || (c->hidden % 32))
@@ -143,6 +146,7 @@ void fill_index_args(csa::IndexArgs& a, const csa_config_t* c, int B, int nq, co
   a.d_I = c->idx_dim;
   a.m = c->m;
   a.k = c->top_k;
+  a.key_fmt = c->idx_key_format;
   a.idx_out = idx_out;
   a.score_out = score_out;
   csa::index_topk_layout(a, ws, B * nq);
@@ -184,6 +188,7 @@ int run_compress(const csa_config_t* c, int B, int T, const uint16_t* H, const i
   a.D = c->hidden;
   a.c = c->head_dim;
   a.d_I = is_csa(c) ? c->idx_dim : 0;
+  a.key_fmt = is_csa(c) ? c->idx_key_format : 0;
   a.m = c->m;
   a.r = c->rope_dim;
   a.n_cols = weight_cols(c);

@@ -124,6 +124,12 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// 16x16x128 with A E4M3 (unit scale) and B FP4 E2M1 (format code 4) in the low four dwords of
+// b, scaled by 2^(scale_b - 127) per lane: each lane's scale covers the 32 K values it holds.
+__device__ __forceinline__ f32x4 mfma_fp8_fp4_16x16x128(i32x8 a, i32x8 b, f32x4 c, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, 0, scale_b);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane 4*i0+q points

@@ -243,6 +243,21 @@ __device__ __forceinline__ uint8_t e4m3_rne(float x) {
   return static_cast<uint8_t>(code | sign);
 }
 
+// E2M1 (OCP MXFP4 element: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to x, ties to the even
+// code, saturating at 6; the sign bit (bit 3) follows x's sign bit.
+__device__ __forceinline__ uint32_t e2m1_rne(float x) {
+  const float a = fabsf(x);
+  const uint32_t mag = a > 5.f     ? 7u
+                       : a >= 3.5f ? 6u
+                       : a > 2.5f  ? 5u
+                       : a >= 1.75f ? 4u
+                       : a > 1.25f ? 3u
+                       : a >= 0.75f ? 2u
+                       : a > 0.25f ? 1u
+                                   : 0u;
+  return mag | ((__float_as_uint(x) >> 28) & 8u);
+}
+
 __device__ float block_sum(float v, float* s_red) {
   const int tid = threadIdx.x;
   v = wave_sum_xor(v, 48);
@@ -270,6 +285,7 @@ __device__ float block_max(float v, float* s_red) {
 
 struct PoolParams {
   int mode, B, T, c, d_I, m, r, n_cols, tail_rows, tail_cols, n_max, nblk;
+  int key_fmt;  // 0 E4M3 + per-entry scale, 1 MXFP4
   const int32_t* pos0;
   const float* proj;
   const float* tail;
@@ -354,7 +370,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     *reinterpret_cast<uint32_t*>(dst + d) = pack_bf16x2(x0, x1);
   }
   if (!csa) return;
-  // indexer keys: same pooling on their own streams, then per-entry E4M3 quantisation
+  // indexer keys: same pooling on their own streams, then per-entry E4M3 quantisation or
+  // MXFP4 blocks
   const int dI = p.d_I;
   const int base = 4 * c;
   float amax = 0.f;
@@ -364,6 +381,27 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
                                  base + dI, base + 3 * dI, p.bias_ib, dI, ch);
     s_val[ch] = v;
     amax = fmaxf(amax, fabsf(v));
+  }
+  if (p.key_fmt == 1) {
+    // MXFP4: thread ch < dI (<= 128) holds channel ch; the 32 lanes of a half-wave form one
+    // block: shared exponent floor(log2 max|v|) - 2 (frexp: max = f 2^ex, f in [0.5, 1)),
+    // E8M0 byte exponent + 127, elements v / 2^exponent to E2M1, two per byte (even channel in
+    // the low nibble).  Blocks past dI (dI < 128) get the unit scale byte.
+    const bool has = tid < dI;
+    const float v = has ? s_val[tid] : 0.f;
+    float am = fabsf(v);
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+    int ex;
+    (void)frexpf(am, &ex);
+    const int se = am > 0.f ? min(max(ex - 3, -127), 127) : -127;
+    const uint32_t code = e2m1_rne(ldexpf(v, -se));
+    const uint32_t hi = static_cast<uint32_t>(__shfl_down(static_cast<int>(code), 1, 64));
+    uint8_t* kd = p.ikeys + (static_cast<size_t>(b) * p.n_max + i) * (dI / 2);
+    if (has && (tid & 1) == 0) kd[tid >> 1] = static_cast<uint8_t>(code | (hi << 4));
+    uint8_t* sd = reinterpret_cast<uint8_t*>(p.iscale) + (static_cast<size_t>(b) * p.n_max + i) * 4;
+    if (tid < 128 && (tid & 31) == 0) sd[tid >> 5] = static_cast<uint8_t>(has ? se + 127 : 127);
+    return;
   }
   amax = block_max(amax, s_red);
   const float scale = amax > 0.f ? amax / 448.f : 1.f;
@@ -482,6 +520,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   p.entries = a.entries;
   p.ikeys = a.ikeys;
   p.iscale = a.iscale;
+  p.key_fmt = a.key_fmt;
   {
     ProfScope ps("compress_pool", s);
     pool_kernel<<<a.B * p.nblk, 256, 0, s>>>(p);

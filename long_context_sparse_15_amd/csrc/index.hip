@@ -39,7 +39,11 @@ __device__ __forceinline__ int visible(const int32_t* n_entries, const int32_t* 
 // One workgroup scores `chunk` consecutive entries of one query row.  Each wave takes 16-entry
 // tiles; a tile is an MFMA with the indexer heads as the M dimension (A operand, resident in
 // registers for the whole chunk) and 16 entries as N (B operand, streamed from HBM).
-template <int DI, int HT, int TPW>
+// MX = true: the keys are MXFP4 (E2M1 codes, E8M0 scale per 32 dims).  The scaled MFMA takes
+// the query as E4M3 and the keys as FP4 with each lane's block scale; its FP4 operand gives
+// lane group g the 32 dims 32g..32g+31 (16 contiguous bytes of the packed key), while its FP8
+// operand gives lane group g dims 16g..16g+15 and 64+16g..64+16g+15 (both checked on the GPU).
+template <int DI, int HT, int TPW, bool MX = false>
 __global__ __launch_bounds__(256) void index_score_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ wi, const uint8_t* __restrict__ keys,
@@ -59,7 +63,9 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   // per head tile) lane group g holds bytes 16g..16g+15 and 64+16g..64+16g+15 of the row, and
   // of each key: the four lane groups of an entry then read 64 contiguous bytes per load.
   // Other DI: bytes 32g.. in 8-byte steps of 16x16x32 MFMAs.
-  constexpr bool kWide = DI == 128;
+  constexpr bool kWide = DI == 128 || MX;
+  constexpr int KROW = MX ? DI / 2 : DI;  // key bytes per entry
+  constexpr int NBLK = DI / 32;           // MXFP4 blocks per key
   i32x8 aw[HT];
   long aq[HT][KK];
   float wq[HT][4];
@@ -68,10 +74,10 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     const int head = ht * 16 + c16;
     const uint8_t* qrow = qi + (static_cast<size_t>(row) * H_I + (head < H_I ? head : 0)) * DI;
     const uint8_t* src = qrow + g * KB;
-    if constexpr (kWide) {
+    if constexpr (kWide) {  // dims past DI (MXFP4 with DI < 128) are zero
       const u32x4* q16 = reinterpret_cast<const u32x4*>(qrow);
-      const u32x4 lo = head < H_I ? q16[g] : u32x4{0, 0, 0, 0};
-      const u32x4 hi = head < H_I ? q16[4 + g] : u32x4{0, 0, 0, 0};
+      const u32x4 lo = (head < H_I && g < DI / 16) ? q16[g] : u32x4{0, 0, 0, 0};
+      const u32x4 hi = (head < H_I && 4 + g < DI / 16) ? q16[4 + g] : u32x4{0, 0, 0, 0};
       aw[ht] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
                      static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
                      static_cast<int>(hi[2]), static_cast<int>(hi[3])};
@@ -89,8 +95,9 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     }
   }
 
-  const uint8_t* kbase = keys + static_cast<size_t>(b) * n_max * DI + (kWide ? 0 : g * KB);
+  const uint8_t* kbase = keys + static_cast<size_t>(b) * n_max * KROW + (kWide ? 0 : g * KB);
   const float* sbase = kscale + static_cast<size_t>(b) * n_max;
+  const uint32_t* swbase = reinterpret_cast<const uint32_t*>(sbase);  // MXFP4 scale bytes
   float* srow = scores + static_cast<size_t>(row) * sstride;
 
   // Wave `wave` scores tiles wave, wave+4, ... (TPW tiles of 16 entries).  The sequence is
@@ -102,10 +109,18 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     i32x8 w;
     long n[KK];
     float ks;
+    uint32_t sw;
   };
   auto load = [&](int t, KeyTile& kt, int emax) {
     const int e = min(tile_entry(t), emax);
-    if constexpr (kWide) {
+    if constexpr (MX) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(e) * KROW);
+      const u32x4 v = g < NBLK ? CSA_STREAM_LOAD(src + g) : u32x4{0, 0, 0, 0};
+      kt.w = i32x8{static_cast<int>(v[0]), static_cast<int>(v[1]), static_cast<int>(v[2]),
+                   static_cast<int>(v[3]), 0, 0, 0, 0};
+      kt.sw = swbase[e];
+      return;
+    } else if constexpr (kWide) {
       const u32x4* src = reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(e) * DI);
       const u32x4 lo = CSA_STREAM_LOAD(src + g), hi = CSA_STREAM_LOAD(src + 4 + g);
       kt.w = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
@@ -122,7 +137,12 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     f32x4 acc[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (kWide) {
+    if constexpr (MX) {
+      // this lane's block scale (unit for the zero blocks past DI)
+      const int sb = g < NBLK ? static_cast<int>((kt.sw >> (8 * g)) & 0xffu) : 127;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_fp8_fp4_16x16x128(aw[ht], kt.w, acc[ht], sb);
+    } else if constexpr (kWide) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_fp8_16x16x128(aw[ht], kt.w, acc[ht]);
     } else {
@@ -141,7 +161,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     part = wave_sum_xor16_32(part);
     const int e = tile_entry(t);
     if (g == 0 && e < e1) {
-      const float sc = part * kt.ks;
+      const float sc = MX ? part : part * kt.ks;  // MXFP4 scales act inside the MFMA
       srow[e] = sc;
     }
   };
@@ -1092,9 +1112,14 @@ template <int DI, int HT>
 static void launch_scores_t(const IndexArgs& a, int chunk, int nchunks, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(nchunks) * static_cast<unsigned>(a.B * a.nq);
   ProfScope ps("index_score", s);
-  index_score_kernel<DI, HT, kScoreTPW><<<grid, 256, 0, s>>>(a.qi, a.qi_scale, a.wi, a.keys, a.kscale,
-                                                  a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
-                                                  chunk, a.scores, a.sstride, nchunks);
+  if (a.key_fmt == 1)
+    index_score_kernel<DI, HT, kScoreTPW, true><<<grid, 256, 0, s>>>(
+        a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
+        chunk, a.scores, a.sstride, nchunks);
+  else
+    index_score_kernel<DI, HT, kScoreTPW><<<grid, 256, 0, s>>>(
+        a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
+        chunk, a.scores, a.sstride, nchunks);
 }
 
 static hipError_t launch_scores(const IndexArgs& a, int chunk, hipStream_t s) {
@@ -1142,7 +1167,7 @@ static hipError_t launch_row_topk(const IndexArgs& a, int rows, hipStream_t s) {
 // Rows scored as a product over heads (16 query rows of a sequence per workgroup) when every
 // sequence brings at least 16 query rows and the heads fit the LDS tile.
 static bool use_gemm_scores(const IndexArgs& a) {
-  return a.nq >= kGemmQ && a.d_I == kGemmDI && a.H_I <= kGemmH;
+  return a.key_fmt == 0 && a.nq >= kGemmQ && a.d_I == kGemmDI && a.H_I <= kGemmH;
 }
 
 static hipError_t launch_gemm_scores(const IndexArgs& a, hipStream_t s) {

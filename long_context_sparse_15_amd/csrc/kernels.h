@@ -18,11 +18,12 @@ struct IndexArgs {
   const uint8_t* qi;      // [rows, H_I, d_I]
   const float* qi_scale;  // [rows, H_I]
   const float* wi;        // [rows, H_I]
-  const uint8_t* keys;    // [B, n_max, d_I]
-  const float* kscale;    // [B, n_max]
+  const uint8_t* keys;    // [B, n_max, d_I] e4m3, or [B, n_max, d_I/2] packed MXFP4
+  const float* kscale;    // [B, n_max] fp32, or 4 E8M0 block-scale bytes per entry (MXFP4)
   const int32_t* n_entries;  // [B]
   const int32_t* pos;     // [rows] or nullptr (t = query index within its sequence)
   int B, nq, n_max, H_I, d_I, m, k;
+  int key_fmt;            // 0 e4m3 + fp32 scale, 1 MXFP4
   float* scores;          // workspace [rows, sstride]
   int sstride;
   uint32_t* counters;     // workspace [rows, chunks]: candidates of each chunk
@@ -68,6 +69,7 @@ hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& p, hipStream_t s);
 struct CompressArgs {
   int mode;                 // 0 CSA, 1 HCA
   int B, T, D, c, d_I, m, r, n_cols, tail_rows, tail_cols, win_slots, n_max;
+  int key_fmt;              // indexer keys: 0 e4m3 + fp32 scale, 1 MXFP4
   const uint16_t* H;        // [B, T, D]
   const int32_t* pos0;      // [B] or nullptr (all 0)
   const uint16_t* W;        // [n_cols, D]

@@ -7,7 +7,7 @@ are produced in milliseconds.  Parity tests use synth.inputs; these tensors are 
 """
 import torch
 
-from .inputs import rope_inv_freq, weight_cols
+from .inputs import MXFP4_MAG_P, rope_inv_freq, weight_cols
 
 
 def _gen(seed, device):
@@ -50,13 +50,35 @@ def _uniform(g, shape, device, lo, hi):
     return torch.rand(*shape, generator=g, device=device) * (hi - lo) + lo
 
 
-def decode_cache_inputs(w, device="cuda", seed=None):
+def mxfp4_normalish(g, rows_shape, d, device, chunk=1 << 24):
+    """As synth.inputs.mxfp4_normalish, on the device (magnitude codes by inverse CDF)."""
+    n = 1
+    for s in rows_shape:
+        n *= s
+    cdf = torch.cumsum(torch.tensor(MXFP4_MAG_P, dtype=torch.float32, device=device), 0)
+    packed = torch.empty((n, d // 2), dtype=torch.uint8, device=device)
+    for s in range(0, n, chunk // d):
+        e = min(n, s + chunk // d)
+        u = torch.rand((e - s, d), generator=g, device=device)
+        mag = torch.clamp(torch.searchsorted(cdf, u), max=7).to(torch.int32)
+        sign = torch.randint(0, 2, (e - s, d), generator=g, device=device, dtype=torch.int32)
+        codes = mag | (sign << 3)
+        packed[s:e] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).to(torch.uint8)
+    scales = torch.full((n, 4), 127, dtype=torch.uint8, device=device)
+    scales[:, :d // 32] = torch.randint(121, 126, (n, d // 32), generator=g, device=device,
+                                        dtype=torch.int32).to(torch.uint8)
+    return packed.view(*rows_shape, d // 2), scales.view(*rows_shape, 4)
+
+
+def decode_cache_inputs(w, device="cuda", seed=None, key_fmt="e4m3"):
     """As synth.inputs.decode_cache_inputs, on the device."""
     g = _gen(w.seed if seed is None else seed, device)
     B, N = w.B, w.N
     out = {"B": B, "N": N}
     out["entries"] = bf16_normal(g, (B, N, w.c), device)
-    if w.mode == "csa":
+    if w.mode == "csa" and key_fmt == "mxfp4":
+        out["ikeys"], out["iscale"] = mxfp4_normalish(g, (B, N), w.d_I, device)
+    elif w.mode == "csa":
         out["ikeys"] = e4m3_normalish(g, (B, N, w.d_I), device)
         out["iscale"] = _uniform(g, (B, N), device, 0.5, 1.5) / 16
     out["window"] = bf16_normal(g, (B, w.n_win, w.c), device)

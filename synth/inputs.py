@@ -145,17 +145,39 @@ def layer_inputs(w, seed=None, T=None):
     return out
 
 
-def decode_cache_inputs(w, seed=None, B=None, N=None):
+# E2M1 magnitude codes 0..7 in the proportions an N(0,1) block quantised with its shared
+# exponent would show (small magnitudes likelier, 6 rare)
+MXFP4_MAG_P = np.array([0.10, 0.19, 0.17, 0.15, 0.17, 0.13, 0.07, 0.02])
+
+
+def mxfp4_normalish(rng, rows_shape, d):
+    """Packed MXFP4 rows of d dims: E2M1 codes (sign uniform, magnitude code drawn from
+    MXFP4_MAG_P), two per byte with the even dim in the low nibble -> uint8 [..., d/2]; and
+    4 E8M0 scale bytes per row, uniform in 121..125 for the d/32 blocks, 127 for unused bytes
+    -> uint8 [..., 4].  No value is quantised here: the codes are drawn directly."""
+    n = int(np.prod(rows_shape))
+    mag = rng.choice(8, size=(n, d), p=MXFP4_MAG_P).astype(np.uint8)
+    sign = rng.integers(0, 2, size=(n, d), dtype=np.uint8) << np.uint8(3)
+    codes = mag | sign
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    scales = np.full((n, 4), 127, dtype=np.uint8)
+    scales[:, :d // 32] = rng.integers(121, 126, size=(n, d // 32), dtype=np.uint8)
+    return packed.reshape(tuple(rows_shape) + (d // 2,)), scales.reshape(tuple(rows_shape) + (4,))
+
+
+def decode_cache_inputs(w, seed=None, B=None, N=None, key_fmt="e4m3"):
     """Inputs of one decode step over a resident cache: N entries per sequence (bf16 ~N(0,1)),
-    E4M3 indexer keys with per-entry scales (CSA), a 128-row window ring (token u in row
-    u mod 128) and one query per sequence at position w.t."""
+    indexer keys (CSA: E4M3 with per-entry scales, or MXFP4 with key_fmt "mxfp4"), a 128-row
+    window ring (token u in row u mod 128) and one query per sequence at position w.t."""
     rng = _rng(w.seed if seed is None else seed)
     B = w.B if B is None else B
     N = w.N if N is None else N
     w = replace(w, B=B, N=N)
     out = {"N": N, "B": B}
     out["entries"] = bf16_normal(rng, (B, N, w.c))
-    if w.mode == "csa":
+    if w.mode == "csa" and key_fmt == "mxfp4":
+        out["ikeys"], out["iscale"] = mxfp4_normalish(rng, (B, N), w.d_I)
+    elif w.mode == "csa":
         out["ikeys"] = e4m3_normalish(rng, (B, N, w.d_I))
         out["iscale"] = rng.uniform(0.5, 1.5, size=(B, N)).astype(np.float32) / 16
     out["window"] = bf16_normal(rng, (B, w.n_win, w.c))
