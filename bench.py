@@ -34,22 +34,28 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 
 
-def _decode_bytes(w, n_vis):
+def _key_bytes(w, key_fmt):
+    """Indexer-key bytes per entry: E4M3 codes + an fp32 scale, or MXFP4 codes (two per byte)
+    + the 4-byte word of E8M0 block scales."""
+    return (w.d_I // 2 if key_fmt == "mxfp4" else w.d_I) + 4
+
+
+def _decode_bytes(w, n_vis, key_fmt="e4m3"):
     """Algorithmic HBM bytes of one decode token (what the method must move): indexer keys and
     their scales over the visible entries, the top-k gathered entries (CSA) or every visible
     entry (HCA), the window rows, the query and the output, the indexer query."""
     c2 = w.c * 2
     b = w.n_win * c2 + 2 * w.n_h * c2
     if w.mode == "csa":
-        b += n_vis * (w.d_I + 4) + min(w.k, n_vis) * c2 + w.H_I * (w.d_I + 8)
+        b += n_vis * _key_bytes(w, key_fmt) + min(w.k, n_vis) * c2 + w.H_I * (w.d_I + 8)
     else:
         b += n_vis * c2
     return b
 
 
-def _score_kernel_bytes(w, n_vis):
+def _score_kernel_bytes(w, n_vis, key_fmt="e4m3"):
     """Algorithmic bytes of one indexer-scoring launch per sequence: keys + scales + query."""
-    return n_vis * (w.d_I + 4) + w.H_I * (w.d_I + 8)
+    return n_vis * _key_bytes(w, key_fmt) + w.H_I * (w.d_I + 8)
 
 
 def _profiled_traffic(kernel, workload):
@@ -101,14 +107,18 @@ def _profiled(step, K, W):
 
 
 def decode_workload(name, K, W, rotate):
+    """One decode step per iteration of a named workload; a "_mxfp4" suffix runs the same
+    workload with MXFP4 indexer keys (the E4M3 keys are the configured default)."""
     import torch
     import long_context_sparse_15_amd as csa
     from synth import inputs as S
     from synth import gpu as G
 
-    w = S.WORKLOADS[name]
+    key_fmt = "mxfp4" if name.endswith("_mxfp4") else "e4m3"
+    base = name[:-len("_mxfp4")] if key_fmt == "mxfp4" else name
+    w = S.WORKLOADS[base]
     dev = "cuda"
-    x = G.decode_cache_inputs(w, dev)
+    x = G.decode_cache_inputs(w, dev, key_fmt=key_fmt)
     heavy = ["entries", "window"] + (["ikeys", "iscale"] if w.mode == "csa" else [])
     copies = [x]
     for r in range(1, rotate):
@@ -118,7 +128,8 @@ def decode_workload(name, K, W, rotate):
         copies.append(y)
     cfg = csa.make_config(csa.MODE_CSA if w.mode == "csa" else csa.MODE_HCA, w.m, w.n_h, w.c,
                           w.r, x["inv_freq"], top_k=w.k, n_win=w.n_win, idx_heads=w.H_I,
-                          idx_dim=w.d_I, softmax_scale=w.scale)
+                          idx_dim=w.d_I, softmax_scale=w.scale,
+                          idx_key_format=csa.IDX_MXFP4 if key_fmt == "mxfp4" else csa.IDX_E4M3)
     caches = [csa.make_cache(w.N, w.n_win, y["entries"], y["window"], y["n_entries"],
                              idx_keys=y.get("ikeys"), idx_scale=y.get("iscale")) for y in copies]
     ws = torch.empty(csa.workspace_size(cfg, csa.OP_DECODE, w.B, 1, w.N), dtype=torch.uint8,
@@ -138,21 +149,22 @@ def decode_workload(name, K, W, rotate):
     ms = _time_steps(step, K, W, stream)
     prof = _profiled(step, K, W)
     n_vis = min(w.N, (w.t + 1) // w.m)
-    step_bytes = w.B * _decode_bytes(w, n_vis)
+    step_bytes = w.B * _decode_bytes(w, n_vis, key_fmt)
     res = {"workload": name, "value": w.B / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
            "hbm_gbs": step_bytes / (ms / 1e3) / 1e9,
            "hbm_frac": step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
            "kernels_ms_per_step": {k: v[1] / K for k, v in prof.items()}}
     if w.mode == "csa":
         kname = "index_score"
-        kbytes = w.B * _score_kernel_bytes(w, n_vis)
+        kbytes = w.B * _score_kernel_bytes(w, n_vis, key_fmt)
     else:
         kname = "mqa_dense"
         kbytes = w.B * ((n_vis + w.n_win) * w.c * 2 + 2 * w.n_h * w.c * 2)
     launches, tot = prof[kname]
     kdur = tot / launches
     ach = kbytes / (kdur / 1e3) / 1e9
-    traffic = _profiled_traffic(kname, name) if kname == "index_score" else None
+    traffic = (_profiled_traffic(kname, name) if kname == "index_score" and key_fmt == "e4m3"
+               else None)
     res["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                        "bytes_per_launch": kbytes, "avg_launch_ms": kdur}
@@ -262,7 +274,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode_128k")
-    ap.add_argument("--extra", default="csa_decode_1m,hca_decode_1m,csa_prefill_64k",
+    ap.add_argument("--extra", default="csa_decode_1m,hca_decode_1m,csa_prefill_64k,"
+                    "csa_decode_128k_mxfp4,csa_decode_1m_mxfp4",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")

@@ -203,6 +203,10 @@ constexpr size_t kGemmLds = kGemmH * kGemmQ * kGemmDI + kGemmH * kGemmQ * 4 + kG
 // land in 16 distinct bank groups (rows are 128 bytes apart).
 __device__ __forceinline__ int qswz(int q) { return (q >> 1) & 7; }
 
+// MX = true: MXFP4 keys as the FP4 A operand (lane group g: dims 32g..32g+31, the lane's block
+// scale); the query codes then go in the FP8 operand's order (lane group g: dims 16g..16g+15 and
+// 64+16g..64+16g+15, i.e. 16-byte chunks g and 4+g of the query row).
+template <bool MX>
 __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ wi, const uint8_t* __restrict__ keys,
@@ -210,6 +214,7 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
     const int32_t* __restrict__ pos, int nq, int n_max, int H_I, int m, int qtiles,
     float* __restrict__ scores, int sstride) {
   constexpr int DI = kGemmDI;
+  constexpr int KROW = MX ? DI / 2 : DI;  // key bytes per entry
   extern __shared__ __align__(16) unsigned char smem[];
   uint8_t* s_q = smem;                                                   // [h][q][128] swizzled
   float* s_c = reinterpret_cast<float*>(smem + kGemmH * kGemmQ * DI);    // [h][q]: w * sq
@@ -243,16 +248,26 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
   const int ngroups = (nv_max + 63) / 64;
   if (wave >= ngroups) return;
 
-  const uint8_t* kb = keys + static_cast<size_t>(b) * n_max * DI + g * 32;
+  const uint8_t* kb = keys + static_cast<size_t>(b) * n_max * KROW + g * (MX ? 16 : 32);
   const float* sb = kscale + static_cast<size_t>(b) * n_max;
+  const uint32_t* swb = reinterpret_cast<const uint32_t*>(sb);  // MXFP4 scale bytes
   float* srow = scores + static_cast<size_t>(b * nq + t0 + c16) * sstride;
   const bool row_ok = t0 + c16 < nq;
   // A operands of group G: entry G*64 + 16blk + c16 (clamped into the visible range), bytes
   // 32g..32g+31; entry scales of the 4 entries G*64 + 16blk + 4g + i this lane's D holds
-  auto load = [&](int G, i32x8 (&a)[4], f32x4 (&ks)[4]) {
+  auto load = [&](int G, i32x8 (&a)[4], f32x4 (&ks)[4], int (&sa)[4]) {
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const int e = min(G * 64 + blk * 16 + c16, nv_max - 1);
+      if constexpr (MX) {  // 16 bytes of codes and this lane's block scale; no entry scale
+        const u32x4 v = *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(e) * KROW);
+        a[blk] = i32x8{static_cast<int>(v[0]), static_cast<int>(v[1]), static_cast<int>(v[2]),
+                       static_cast<int>(v[3]), 0, 0, 0, 0};
+        sa[blk] = static_cast<int>((swb[e] >> (8 * g)) & 0xffu);
+        ks[blk] = f32x4{1.f, 1.f, 1.f, 1.f};
+        continue;
+      }
+      sa[blk] = 127;
       const u32x4* src = reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(e) * DI);
       const u32x4 lo = src[0], hi = src[1];
       a[blk] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
@@ -263,12 +278,14 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
     }
   };
   const uint8_t* qb = s_q + c16 * DI;
-  const int ch0 = ((2 * g) ^ qswz(c16)) << 4, ch1 = ((2 * g + 1) ^ qswz(c16)) << 4;
+  const int ch0 = ((MX ? g : 2 * g) ^ qswz(c16)) << 4;
+  const int ch1 = ((MX ? 4 + g : 2 * g + 1) ^ qswz(c16)) << 4;
   i32x8 a[4], an[4];
   f32x4 ks[4], ksn[4];
-  load(wave, a, ks);
+  int sa[4], san[4];
+  load(wave, a, ks, sa);
   for (int G = wave; G < ngroups; G += kGemmWaves) {
-    load(min(G + kGemmWaves, ngroups - 1), an, ksn);  // always issued: same order each iteration
+    load(min(G + kGemmWaves, ngroups - 1), an, ksn, san);  // always issued: same order
     f32x4 acc[4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) acc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -286,8 +303,13 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
     };
     auto issue = [&](const i32x8& bq, f32x4 (&d)[4]) {
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
-        d[blk] = mfma_fp8_16x16x128(a[blk], bq, f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int blk = 0; blk < 4; ++blk) {
+        if constexpr (MX)
+          d[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a[blk], bq, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, sa[blk], 0, 127);
+        else
+          d[blk] = mfma_fp8_16x16x128(a[blk], bq, f32x4{0.f, 0.f, 0.f, 0.f});
+      }
     };
     // acc += max(d, 0) * ch; the ReLU is a signed integer max of the float's bits with 0
     // (negative floats have negative integer patterns), one instruction
@@ -332,6 +354,7 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
                   acc[blk][3] * ks[blk][3]};
       a[blk] = an[blk];
       ks[blk] = ksn[blk];
+      sa[blk] = san[blk];
     }
   }
 }
@@ -1167,13 +1190,14 @@ static hipError_t launch_row_topk(const IndexArgs& a, int rows, hipStream_t s) {
 // Rows scored as a product over heads (16 query rows of a sequence per workgroup) when every
 // sequence brings at least 16 query rows and the heads fit the LDS tile.
 static bool use_gemm_scores(const IndexArgs& a) {
-  return a.key_fmt == 0 && a.nq >= kGemmQ && a.d_I == kGemmDI && a.H_I <= kGemmH;
+  return a.nq >= kGemmQ && a.d_I == kGemmDI && a.H_I <= kGemmH;
 }
 
-static hipError_t launch_gemm_scores(const IndexArgs& a, hipStream_t s) {
+template <bool MX>
+static hipError_t launch_gemm_scores_t(const IndexArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(index_gemm_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(index_gemm_kernel<MX>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(kGemmLds));
     if (e != hipSuccess) return e;
@@ -1181,10 +1205,14 @@ static hipError_t launch_gemm_scores(const IndexArgs& a, hipStream_t s) {
   }
   const int qtiles = (a.nq + kGemmQ - 1) / kGemmQ;
   ProfScope ps("index_score", s);
-  index_gemm_kernel<<<static_cast<unsigned>(a.B) * qtiles, kGemmThreads, kGemmLds, s>>>(
+  index_gemm_kernel<MX><<<static_cast<unsigned>(a.B) * qtiles, kGemmThreads, kGemmLds, s>>>(
       a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
       qtiles, a.scores, a.sstride);
   return hipGetLastError();
+}
+
+static hipError_t launch_gemm_scores(const IndexArgs& a, hipStream_t s) {
+  return a.key_fmt == 1 ? launch_gemm_scores_t<true>(a, s) : launch_gemm_scores_t<false>(a, s);
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {

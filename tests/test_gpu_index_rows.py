@@ -1,7 +1,7 @@
 """GPU parity of csa_index_topk with many query rows per sequence (the prefill shape: rows are
 scored 16 at a time as a product over indexer heads) against the oracle's float64 scores:
 ragged row counts, fewer heads than the LDS tile holds, partially filled caches, rows with
-nothing visible, and arbitrary positions."""
+nothing visible, and arbitrary positions; with E4M3 keys and with MXFP4 keys."""
 import numpy as np
 import pytest
 import torch
@@ -14,11 +14,17 @@ from gpu_common import DEV, check_close, check_selection, dev, say, workspace
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(seed, B, nq, n_max, n_ent, H_I, d_I, pos):
+def _inputs(seed, B, nq, n_max, n_ent, H_I, d_I, pos, key_fmt="e4m3"):
     rng = np.random.Generator(np.random.PCG64(seed))
+    if key_fmt == "mxfp4":
+        keys, ksc = S.mxfp4_normalish(rng, (B, n_max), d_I)
+    else:
+        keys = S.e4m3_normalish(rng, (B, n_max, d_I))
+        ksc = (rng.uniform(0.5, 1.5, size=(B, n_max)) / 16).astype(np.float32)
     x = {
-        "ikeys": S.e4m3_normalish(rng, (B, n_max, d_I)),
-        "iscale": (rng.uniform(0.5, 1.5, size=(B, n_max)) / 16).astype(np.float32),
+        "key_fmt": key_fmt,
+        "ikeys": keys,
+        "iscale": ksc,
         "qi": S.e4m3_normalish(rng, (B, nq, H_I, d_I)),
         "qi_scale": (rng.uniform(0.5, 1.5, size=(B, nq, H_I)) / 16).astype(np.float32),
         "wi": (rng.standard_normal((B, nq, H_I), dtype=np.float32) / 8),
@@ -30,8 +36,9 @@ def _inputs(seed, B, nq, n_max, n_ent, H_I, d_I, pos):
 
 def _run(x, B, nq, n_max, H_I, d_I, k, m=4):
     inv = dev(S.rope_inv_freq(64, 160000.0))
+    mx = x["key_fmt"] == "mxfp4"
     cfg = csa.make_config(csa.MODE_CSA, m, 64, 512, 64, inv, top_k=k, n_win=128, idx_heads=H_I,
-                          idx_dim=d_I)
+                          idx_dim=d_I, idx_key_format=csa.IDX_MXFP4 if mx else csa.IDX_E4M3)
     d = {key: dev(x[key]) for key in ("ikeys", "iscale", "qi", "qi_scale", "wi", "n_entries")}
     pos = dev(x["pos"]) if x["pos"] is not None else None
     entries = torch.zeros((B, n_max, 512), dtype=torch.int16, device=DEV)
@@ -48,8 +55,12 @@ def _run(x, B, nq, n_max, H_I, d_I, k, m=4):
         for q in range(nq):
             t = int(x["pos"][b, q]) if x["pos"] is not None else q
             n_vis = O.visible_entries(t, m, int(x["n_entries"][b]))
-            ref = O.index_scores(x["qi"][b, q], x["qi_scale"][b, q], x["wi"][b, q],
-                                 x["ikeys"][b], x["iscale"][b], n_vis)
+            if mx:
+                ref = O.index_scores_mxfp4(x["qi"][b, q], x["qi_scale"][b, q], x["wi"][b, q],
+                                           x["ikeys"][b], x["iscale"][b][:, :d_I // 32], n_vis)
+            else:
+                ref = O.index_scores(x["qi"][b, q], x["qi_scale"][b, q], x["wi"][b, q],
+                                     x["ikeys"][b], x["iscale"][b], n_vis)
             what = "seq %d row %d (t=%d, n_vis=%d)" % (b, q, t, n_vis)
             check_selection(idx_h[b, q], ref, k, what)
             kk = min(k, n_vis)
@@ -69,13 +80,14 @@ def _run(x, B, nq, n_max, H_I, d_I, k, m=4):
     # one full tile of 16 rows over long rows (several 64-entry groups per wave)
     (14, 1, 16, 9000, [8800], 64, 256, "spread"),
 ])
-def test_index_rows_parity(case):
+@pytest.mark.parametrize("key_fmt", ["e4m3", "mxfp4"])
+def test_index_rows_parity(case, key_fmt):
     seed, B, nq, n_max, n_ent, H_I, k, posmode = case
-    say("index rows", case)
+    say("index rows", key_fmt, case)
     if posmode == "spread":
         rng = np.random.Generator(np.random.PCG64(seed + 100))
         pos = rng.integers(0, 4 * n_max + 8, size=(B, nq))
     else:  # positions 0..nq-1
         pos = np.tile(np.arange(nq), (B, 1))
-    x = _inputs(seed, B, nq, n_max, n_ent, H_I, 128, pos)
+    x = _inputs(seed, B, nq, n_max, n_ent, H_I, 128, pos, key_fmt)
     _run(x, B, nq, n_max, H_I, 128, k)
