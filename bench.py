@@ -14,8 +14,10 @@ Infinity Cache.  A second, profiled pass of K steps brackets every kernel launch
 (csa_profile_start/stop) to get the dominant kernel's average duration for the roofline.
 
 Also measured (one line, under "also"): CSA decode at 1M context (B=4, 262144 entries, 128
-heads, k=2048), HCA dense decode at 1M context (B=16, 8192 entries, 128 heads) and the 64K-token
-CSA prefill.  The CPU oracle is timed on a bounded sample of the headline workload.
+heads, k=2048), HCA dense decode at 1M context (B=16, 8192 entries, 128 heads), the 64K-token
+CSA prefill, and the 128K / 1M decodes and the prefill again with MXFP4 indexer keys (E2M1 codes
+with an E8M0 scale per 32 dims instead of E4M3 codes with a per-entry fp32 scale).  The CPU
+oracle is timed on a bounded sample of the headline workload.
 
 Prints ONE JSON line.
 """
@@ -174,25 +176,30 @@ def decode_workload(name, K, W, rotate):
 
 
 def prefill_workload(name, K, W):
+    """The whole prefill (compressor, causal indexer, top-k, sparse MQA) of a named workload; a
+    "_mxfp4" suffix has the compressor write MXFP4 indexer keys."""
     import torch
     import long_context_sparse_15_amd as csa
     from synth import inputs as S
     from synth import gpu as G
 
-    w = S.WORKLOADS[name]
+    mx = name.endswith("_mxfp4")
+    w = S.WORKLOADS[name[:-len("_mxfp4")] if mx else name]
     dev = "cuda"
     x = G.layer_inputs(w, dev)
     T, B = w.T, w.B
     n_max = T // w.m
     cfg = csa.make_config(csa.MODE_CSA, w.m, w.n_h, w.c, w.r, x["inv_freq"], top_k=w.k,
                           n_win=w.n_win, idx_heads=w.H_I, idx_dim=w.d_I, hidden=w.D,
-                          softmax_scale=w.scale)
+                          softmax_scale=w.scale,
+                          idx_key_format=csa.IDX_MXFP4 if mx else csa.IDX_E4M3)
     tr, tc = csa.tail_shape(cfg)
     ct = dict(entries=torch.zeros((B, n_max, w.c), dtype=torch.int16, device=dev),
               window=torch.zeros((B, T, w.c), dtype=torch.int16, device=dev),
               n_entries=torch.zeros(B, dtype=torch.int32, device=dev),
               tail=torch.zeros((B, tr, tc), dtype=torch.float32, device=dev),
-              idx_keys=torch.zeros((B, n_max, w.d_I), dtype=torch.uint8, device=dev),
+              idx_keys=torch.zeros((B, n_max, w.d_I // 2 if mx else w.d_I), dtype=torch.uint8,
+                                   device=dev),
               idx_scale=torch.zeros((B, n_max), dtype=torch.float32, device=dev))
     cache = csa.make_cache(n_max, T, **ct)
     weights = csa.make_weights(x["W"], x["Ba"], x["gamma"], x["gamma_win"], bias_b=x["Bb"],
@@ -275,7 +282,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode_128k")
     ap.add_argument("--extra", default="csa_decode_1m,hca_decode_1m,csa_prefill_64k,"
-                    "csa_decode_128k_mxfp4,csa_decode_1m_mxfp4",
+                    "csa_decode_128k_mxfp4,csa_decode_1m_mxfp4,csa_prefill_64k_mxfp4",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
