@@ -5,7 +5,8 @@ entry points, shapes and workspace plans), checked against the oracle on sampled
 * CSA decode, batch 4, 262144 entries (1M context), 128 heads, k=2048;
 * HCA dense decode, batch 16, 8192 entries (1M context), 128 heads;
 * CSA prefill of 65536 tokens with hidden size 4096 (compressor, causal indexer, per-query
-  top-k 512, sparse MQA with window and sink), checked stage-wise on sampled tokens.
+  top-k 512, sparse MQA with window and sink), checked stage-wise on sampled tokens;
+* the two CSA decodes again with MXFP4 indexer keys.
 
 Inputs come from the seeded device generator (synth.gpu); the oracle receives host copies of the
 same tensors."""
@@ -26,14 +27,16 @@ def h16(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def _decode_full(name, sample):
+def _decode_full(name, sample, key_fmt="e4m3"):
     w = S.WORKLOADS[name]
-    say("full-size decode", name, "B=%d N=%d" % (w.B, w.N))
-    x = G.decode_cache_inputs(w, DEV)
+    say("full-size decode", name, key_fmt, "B=%d N=%d" % (w.B, w.N))
+    x = G.decode_cache_inputs(w, DEV, key_fmt=key_fmt)
     csa_mode = w.mode == "csa"
+    mx = key_fmt == "mxfp4"
     cfg = csa.make_config(csa.MODE_CSA if csa_mode else csa.MODE_HCA, w.m, w.n_h, w.c, w.r,
                           x["inv_freq"], top_k=w.k, n_win=w.n_win, idx_heads=w.H_I,
-                          idx_dim=w.d_I, softmax_scale=w.scale)
+                          idx_dim=w.d_I, softmax_scale=w.scale,
+                          idx_key_format=csa.IDX_MXFP4 if mx else csa.IDX_E4M3)
     cache = csa.make_cache(w.N, w.n_win, x["entries"], x["window"], x["n_entries"],
                            idx_keys=x.get("ikeys"), idx_scale=x.get("iscale"))
     ws = workspace(csa.workspace_size(cfg, csa.OP_DECODE, w.B, 1, w.N))
@@ -57,9 +60,11 @@ def _decode_full(name, sample):
         win = h16(x["window"][b])
         win_rows = win[[u % w.n_win for u in O.window_tokens(t, w.n_win)]]
         if csa_mode:
-            sc = O.index_scores(x["qi"][b, 0].cpu().numpy(), x["qi_scale"][b, 0].cpu().numpy(),
-                                x["wi"][b, 0].cpu().numpy(), x["ikeys"][b].cpu().numpy(),
-                                x["iscale"][b].cpu().numpy(), n_vis)
+            score_fn = O.index_scores_mxfp4 if mx else O.index_scores
+            ksc = x["iscale"][b].cpu().numpy()
+            sc = score_fn(x["qi"][b, 0].cpu().numpy(), x["qi_scale"][b, 0].cpu().numpy(),
+                          x["wi"][b, 0].cpu().numpy(), x["ikeys"][b].cpu().numpy(),
+                          ksc[:, :w.d_I // 32] if mx else ksc, n_vis)
             check_selection(idx_h[b], sc, w.k, "%s seq %d selection" % (name, b))
             rows = np.concatenate([ent[idx_h[b][:min(w.k, n_vis)]], win_rows])
         else:
@@ -78,6 +83,14 @@ def test_full_csa_decode_1m():
 
 def test_full_hca_decode_1m():
     _decode_full("hca_decode_1m", [0, 9, 15])
+
+
+def test_full_csa_decode_128k_mxfp4():
+    _decode_full("csa_decode_128k", [0, 17, 31], "mxfp4")
+
+
+def test_full_csa_decode_1m_mxfp4():
+    _decode_full("csa_decode_1m", [1, 2], "mxfp4")
 
 
 def test_full_csa_prefill_64k():
