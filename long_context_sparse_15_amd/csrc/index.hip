@@ -901,21 +901,21 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s) {
 
 // ============================================================================ multi-WG top-k
 // For rows longer than one workgroup's register file (decode at long context).  A row is cut
-// into chunks of kCollectChunk entries, one 1024-thread workgroup each.  Every workgroup of a row
-// takes the same kRowSamples evenly spaced keys of the row and derives the same threshold T_lo
-// (the lower edge of the bin holding the r-th largest sample, r a little above
-// kk * samples / n_vis with a margin of four standard deviations), so T_lo almost surely has
-// between kk and a few times kk keys at or above it.  Each workgroup writes its chunk's
-// (key, index) pairs >= T_lo in ascending index order into its own region (block prefix sum, no
-// global atomics).  A finalize workgroup per row (a second launch: a device-scope handoff
-// inside one launch costs an L2 write-back per workgroup on this multi-XCD part) concatenates
-// the regions (a list in ascending index order), finds the exact kk-th key among them with one
-// histogram pass over their actual range, and emits the keys above it plus the first ties in
-// index order.  A region overflow or too few candidates (ties, adversarial data) fall back to
-// the exact streaming select of the row.
+// into chunks of kCollectChunk entries, one 1024-thread workgroup each.  A workgroup selects its
+// chunk's candidates with a threshold of its own: T_c, the lower edge of the 12-bit bin (refined
+// by 12 more bits when crowded) holding its r-th largest key, r = the chunk's expected share of
+// the row's top kk plus four standard deviations.  It writes the (key, index) pairs >= T_c in
+// ascending index order into its own region (block prefix sum, no global atomics) with the
+// count and T_c.  A finalize workgroup per row (a second launch: a device-scope handoff inside
+// one launch costs an L2 write-back per workgroup on this multi-XCD part) concatenates the
+// regions (a list in ascending index order), finds the kk-th key T of the list with one
+// histogram pass over its actual range and emits the keys above it plus the first ties in index
+// order.  The list holds every key >= T of the row exactly when T >= every chunk's T_c (a key
+// >= T is then >= its chunk's threshold); otherwise (a chunk holding far more than its share
+// of the top keys), and on a region overflow or too few candidates, the exact streaming select
+// of the row runs instead.
 constexpr int kCollectChunk = 4096;
 constexpr int kCandPerChunk = 1024;
-constexpr int kRowSamples = 2048;
 constexpr int kSCandCap = 8192;  // candidates of a row held by its finalize workgroup
 constexpr size_t kMultiLds = static_cast<size_t>(kSCandCap) * 8 + kHistBins * 4;
 
@@ -923,9 +923,9 @@ __global__ __launch_bounds__(1024) void topk_collect_kernel(
     const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int nchunks,
     uint32_t* __restrict__ ccount, uint64_t* __restrict__ cand) {
-  constexpr int THREADS = 1024, PER = kCollectChunk / THREADS, SPT = kRowSamples / THREADS;
+  constexpr int THREADS = 1024, PER = kCollectChunk / THREADS;
   static_assert(PER == 4, "one 16-byte load of keys per thread");
-  __shared__ uint32_t s_samp[kRowSamples];
+  __shared__ uint32_t s_key[kCollectChunk];
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t s_tmp[THREADS / 64];
   __shared__ int s_res[2];
@@ -940,8 +940,10 @@ __global__ __launch_bounds__(1024) void topk_collect_kernel(
   if (chunk >= used) return;
   const size_t rc = static_cast<size_t>(row) * nchunks + chunk;
   const int e0 = chunk * kCollectChunk;
+  const int len = min(kCollectChunk, n_vis - e0);
 
-  // ---- collect: this chunk's keys (one 16-byte load per thread, clamped into the row)
+  // this chunk's keys (one 16-byte load per thread, clamped into the row), also to LDS for the
+  // histogram pass; the histogram is cleared while the loads are in flight
   uint32_t key[PER];
   {
     const int base = e0 + tid * PER;
@@ -950,48 +952,46 @@ __global__ __launch_bounds__(1024) void topk_collect_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) key[j] = base + j < n_vis ? order_key(f[j]) : 0u;
   }
-  // samples: sample j is entry floor(j * n_vis / kRowSamples), the same in every workgroup
+  for (int i = tid; i < kHistBins; i += THREADS) hist[i] = 0u;
 #pragma unroll
-  for (int s = 0; s < SPT; ++s) {
-    const int j = s * THREADS + tid;
-    s_samp[j] = order_key(srow[static_cast<int>((static_cast<long long>(j) * n_vis) / kRowSamples)]);
-  }
+  for (int j = 0; j < PER; ++j) s_key[tid * PER + j] = key[j];
   __syncthreads();
-  const float expect = static_cast<float>(kk) * kRowSamples / static_cast<float>(n_vis);
-  int r = static_cast<int>(ceilf(expect + 4.f * sqrtf(expect) + 4.f));
-  if (r > kRowSamples) r = kRowSamples;
-  auto sf = [&](int j) { return s_samp[j]; };
-  uint32_t Tlo;
-  {
-    const uint32_t cb = radix_pass<THREADS>(sf, kRowSamples, 0u, 0u, 20, 4096,
-                                            static_cast<uint32_t>(r), hist, s_tmp, s_res);
+  const float expect = static_cast<float>(kk) * static_cast<float>(len) / static_cast<float>(n_vis);
+  const int r = static_cast<int>(ceilf(expect + 4.f * sqrtf(expect) + 4.f));
+  uint32_t Tc = 0u;  // keep the whole chunk when it holds no more than r keys
+  if (r < len) {
+    auto kf = [&](int e) { return s_key[e]; };
+    const uint32_t cb = radix_pass<THREADS>(kf, len, 0u, 0u, 20, 4096, static_cast<uint32_t>(r),
+                                            hist, s_tmp, s_res, /*zeroed=*/true);
     const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
     const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
     __syncthreads();
-    Tlo = d1 << 20;
-    if (cb > 16) {  // crowded bin: refine by the next 12 bits
-      radix_pass<THREADS>(sf, kRowSamples, d1 << 20, 0xfff00000u, 8, 4096, r1, hist, s_tmp,
-                          s_res);
-      Tlo |= static_cast<uint32_t>(s_res[0]) << 8;
+    Tc = d1 << 20;
+    if (cb > 64) {  // crowded bin: refine by the next 12 bits
+      radix_pass<THREADS>(kf, len, d1 << 20, 0xfff00000u, 8, 4096, r1, hist, s_tmp, s_res);
+      Tc |= static_cast<uint32_t>(s_res[0]) << 8;
       __syncthreads();
     }
   }
   uint32_t own = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) own += (e0 + tid * PER + i < n_vis && key[i] >= Tlo) ? 1u : 0u;
+  for (int i = 0; i < PER; ++i) own += (e0 + tid * PER + i < n_vis && key[i] >= Tc) ? 1u : 0u;
   uint32_t total;
   uint32_t off = block_excl_scan<THREADS>(own, s_tmp, &total);
   uint64_t* cdst = cand + rc * kCandPerChunk;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = e0 + tid * PER + i;
-    if (e < n_vis && key[i] >= Tlo) {
+    if (e < n_vis && key[i] >= Tc) {
       if (off < static_cast<uint32_t>(kCandPerChunk))
         cdst[off] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(e);
       ++off;
     }
   }
-  if (tid == 0) ccount[rc] = total;
+  if (tid == 0) {
+    ccount[2 * rc] = total;
+    ccount[2 * rc + 1] = Tc;
+  }
 }
 
 __global__ __launch_bounds__(1024) void topk_finalize_kernel(
@@ -1008,7 +1008,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   __shared__ uint32_t s_tmp[THREADS / 64];
   __shared__ int s_res[2];
   __shared__ int s_flag;
-  __shared__ uint32_t s_lo, s_hi;
+  __shared__ uint32_t s_lo, s_hi, s_tmax;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
@@ -1028,10 +1028,14 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
     s_flag = used > THREADS ? 1 : 0;  // 1 = take the exact fallback
     s_lo = 0xffffffffu;
     s_hi = 0u;
+    s_tmax = 0u;
   }
   __syncthreads();
   if (!s_flag) {
-    const uint32_t c = tid < used ? ccount[static_cast<size_t>(row) * nchunks + tid] : 0u;
+    const size_t rc = static_cast<size_t>(row) * nchunks + tid;
+    const uint32_t c = tid < used ? ccount[2 * rc] : 0u;
+    const uint32_t tc = wave_max_u32(tid < used ? ccount[2 * rc + 1] : 0u);
+    if (lane_id() == 0) atomicMax(&s_tmax, tc);
     if (c > static_cast<uint32_t>(kCandPerChunk)) s_flag = 1;
     uint32_t tot;
     const uint32_t o = block_excl_scan<THREADS>(c, s_tmp, &tot);
@@ -1052,19 +1056,18 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   }
   const int nc = static_cast<int>(s_off[used]);
   uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int j = tid; j < nc; j += THREADS) {
-    int a = 0, b = used;  // s_off[a] <= j < s_off[b]
-    while (b - a > 1) {
-      const int mid = (a + b) >> 1;
-      if (s_off[mid] <= static_cast<uint32_t>(j)) a = mid; else b = mid;
+  // 16 threads per region, each region's pairs to its place in the concatenated list
+  for (int c = tid >> 4; c < used; c += THREADS / 16) {
+    const uint32_t o = s_off[c], n = s_off[c + 1] - o;
+    const uint64_t* src = cand + (static_cast<size_t>(row) * nchunks + c) * kCandPerChunk;
+    for (uint32_t j = tid & 15; j < n; j += 16) {
+      const uint64_t v = src[j];
+      const uint32_t kv = static_cast<uint32_t>(v >> 32);
+      ckey[o + j] = kv;
+      cidx[o + j] = static_cast<int32_t>(v & 0xffffffffu);
+      lo = min(lo, kv);
+      hi = max(hi, kv);
     }
-    const uint64_t v =
-        cand[(static_cast<size_t>(row) * nchunks + a) * kCandPerChunk + (j - s_off[a])];
-    const uint32_t kv = static_cast<uint32_t>(v >> 32);
-    ckey[j] = kv;
-    cidx[j] = static_cast<int32_t>(v & 0xffffffffu);
-    lo = min(lo, kv);
-    hi = max(hi, kv);
   }
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
@@ -1077,6 +1080,12 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   int need_eq;
   auto ck = [&](int j) { return ckey[j]; };
   select_kth<THREADS>(ck, nc, kk, s_lo, s_hi, hist, s_tmp, s_res, T, need_eq);
+  if (T < s_tmax) {  // some chunk's threshold cut keys that reach T: exact streaming select
+    auto kf = [&](int e) { return order_key(srow[e]); };
+    radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
+    ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+    return;
+  }
   // the candidate list is in ascending index order
   ordered_emit_fn<THREADS>(ck, nc, T, need_eq, k, [&](int slot, int j) {
     out[slot] = cidx[j];
@@ -1103,7 +1112,7 @@ size_t index_topk_workspace(int rows, int n_max, int k) {
   size_t b = align256(static_cast<size_t>(rows) * score_stride(n_max) * sizeof(float));
   if (index_use_multi(rows, n_max)) {
     const size_t rc = static_cast<size_t>(rows) * collect_chunks(n_max);
-    b += align256(rc * 4);
+    b += align256(rc * 8);  // (count, threshold) per chunk
     b += align256(rc * kCandPerChunk * 8);
   }
   (void)k;
@@ -1120,7 +1129,7 @@ void index_topk_layout(IndexArgs& a, void* ws, int rows) {
   if (index_use_multi(rows, a.n_max)) {
     const size_t rc = static_cast<size_t>(rows) * collect_chunks(a.n_max);
     a.counters = reinterpret_cast<uint32_t*>(p);
-    p += align256(rc * 4);
+    p += align256(rc * 8);
     a.cand = reinterpret_cast<uint64_t*>(p);
   }
 }

@@ -26,7 +26,7 @@ struct IndexArgs {
   int key_fmt;            // 0 e4m3 + fp32 scale, 1 MXFP4
   float* scores;          // workspace [rows, sstride]
   int sstride;
-  uint32_t* counters;     // workspace [rows, chunks]: candidates of each chunk
+  uint32_t* counters;     // workspace [rows, chunks, 2]: candidates and threshold of each chunk
   uint64_t* cand;         // workspace [rows, chunks, candidates per chunk]: (key, index)
   int32_t* idx_out;       // [rows, k]
   float* score_out;       // [rows, k] or nullptr
