@@ -40,7 +40,7 @@ def _oracle_row(w, x, b, t, sel=None):
     return O.attend(x["q"][b, 0], rows, x["sink"], w.scale, t, x["inv_freq"])
 
 
-def run_csa_case(w, x, exact_ties=False):
+def run_csa_case(w, x, exact_ties=False, score_atol_mult=1.0):
     B, N = x["B"], x["N"]
     cfg, cache, d = _setup(w, x)
     idx = torch.empty((B, 1, w.k), dtype=torch.int32, device=DEV)
@@ -70,8 +70,9 @@ def run_csa_case(w, x, exact_ties=False):
         sel = idx_h[b, 0, :kk]
         if exact_ties:
             assert np.array_equal(sel, O.topk_select(ref_scores, w.k)), "tie order"
-        check_close(sc_h[b, 0, :kk], ref_scores[sel], "seq %d scores" % b, atol=1e-5 * max(
-            1.0, np.abs(ref_scores).max(initial=0.0)), rtol=1e-5)
+        check_close(sc_h[b, 0, :kk], ref_scores[sel], "seq %d scores" % b,
+                    atol=1e-5 * score_atol_mult * max(1.0, np.abs(ref_scores).max(initial=0.0)),
+                    rtol=1e-5)
         assert np.all(np.isneginf(sc_h[b, 0, kk:]))
         ref, ref_lse = _oracle_row(w, x, b, t, sel=sel)
         check_close(out_h[b, 0], ref, "seq %d output" % b)
@@ -132,6 +133,18 @@ def test_csa_decode_massive_ties_multi_workgroup_fallback():
     x["iscale"][:, 5000:] = x["iscale"][:, 5000:5001]
     x["pos"] = np.array([4 * 40000], dtype=np.int32)
     run_csa_case(w, x, exact_ties=True)
+
+
+def test_csa_decode_clustered_top_keys_multi_workgroup_fallback():
+    """The top keys of a long row all sit in its first 4096-entry chunk: that chunk's own
+    threshold cuts keys above the k-th key, the finalize sees it and takes the exact path."""
+    say("csa decode clustered top keys, multi-workgroup select")
+    w = _w("csa_decode_1m")
+    x = S.decode_cache_inputs(w, B=1, N=40000)
+    x["iscale"][:, :4096] *= 16.0
+    x["pos"] = np.array([4 * 40000], dtype=np.int32)
+    # the fp32 sums' rounding scales with their 16x larger terms
+    run_csa_case(w, x, score_atol_mult=16.0)
 
 
 @pytest.mark.parametrize("case", [
