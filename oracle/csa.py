@@ -31,7 +31,13 @@ Readings taken where the pages are silent (also listed in the design notes):
       rotated: the attention step applies RoPE at the query position t;
   R19 optional FP4 indexer keys are OCP MXFP4: 32 consecutive dims share one E8M0 scale
       (shared exponent floor(log2 max|v|) - 2, all-zero block -127), elements E2M1 with ties to
-      even and saturation; the query stays E4M3.
+      even and saturation; the query stays E4M3;
+  R20 query side: c^Q = h W^DQ is stored in bf16 between the two projections; the attention
+      query is c^Q W^UQ RMS-normalised over each head's c dims with one gain vector shared by
+      the heads, stored bf16 and not rotated (R18); q^I = c^Q W^IUQ is stored as R5; w^I = h W_w
+      stays fp32;
+  R21 grouped output projection: group u holds the consecutive heads u*n_h/g .. (u+1)*n_h/g-1,
+      z^[u] is stored in bf16, Proj is a plain linear map from g*r_o to D (no bias), y in bf16.
 """
 import numpy as np
 
@@ -338,3 +344,50 @@ def hca_layer(h_bits, w_bits, params, q_bits, sink, m, c, n_win, scale, inv_freq
         res[t] = hca_query(t, q_bits[t], sink, comp["entries"], comp["entries"].shape[0],
                            comp["win"], lambda u: u, m, n_win, scale, inv_freq)
     return comp, res
+
+
+# ----------------------------------------------------------------------------- query and output
+# projections (the steps on either side of the attention path)
+
+def query_projections(h_bits, w_dq_bits, w_w_bits, w_uq_bits, w_iuq_bits, gamma_q, n_h, c,
+                      H_I, d_I, eps):
+    """Indexer query, indexer head weights and attention query of every token.
+
+    Book, chapter "Attention", section "CSA 的完整路径": c^Q_t = h_t W^DQ,
+    q^I_t = c^Q_t W^IUQ split into n_h^I heads, w^I_t = h_t W_w; section "注意力实现细节":
+    queries are RMS-normalised; readings R5, R18, R20.
+    h_bits [T, D] bf16; weights bf16, one row per output column: w_dq [r_q, D], w_w [H_I, D],
+    w_uq [n_h*c, r_q], w_iuq [H_I*d_I, r_q]; gamma_q [c].
+    Returns dict(cq bf16 [T, r_q], q bf16 [T, n_h, c], qi u8 [T, H_I, d_I], qi_scale f32
+    [T, H_I], wi f32 [T, H_I], qpre f64 [T, n_h, c], qi_pre f64 [T, H_I, d_I]).
+    """
+    H = bf16_bits_to_f64(h_bits)
+    T = H.shape[0]
+    cq = f64_to_bf16_bits(H @ bf16_bits_to_f64(w_dq_bits).T)
+    CQ = bf16_bits_to_f64(cq)
+    wi = (H @ bf16_bits_to_f64(w_w_bits).T).astype(np.float32)
+    qi_pre = (CQ @ bf16_bits_to_f64(w_iuq_bits).T).reshape(T, H_I, d_I)
+    qi, qi_scale = quantize_rows_e4m3(qi_pre)
+    qpre = (CQ @ bf16_bits_to_f64(w_uq_bits).T).reshape(T, n_h, c)
+    q = f64_to_bf16_bits(rms_norm(qpre, gamma_q, eps))
+    return {"cq": cq, "q": q, "qi": qi, "qi_scale": qi_scale, "wi": wi, "qpre": qpre,
+            "qi_pre": qi_pre}
+
+
+def grouped_output_projection(o_bits, w_down_bits, w_proj_bits, g):
+    """Layer output from the attention output of every token.
+
+    Book, chapter "Attention", section "注意力实现细节" and the component table row "Grouped
+    output projection": O = Concat_u O^[u], z^[u] = O^[u] W^[u]_down with
+    W^[u]_down in R^{(n_h/g) d_h x r_o}, y = Proj(Concat_u z^[u]); reading R21.
+    o_bits [T, n_h, c] bf16; w_down_bits [g, r_o, (n_h/g)*c] bf16 (row = output column);
+    w_proj_bits [D, g*r_o] bf16.  Returns (z bf16 [T, g*r_o], y bf16 [T, D]).
+    """
+    O = bf16_bits_to_f64(o_bits)
+    T = O.shape[0]
+    O = O.reshape(T, -1)
+    width = O.shape[1] // g
+    zs = [O[:, u * width:(u + 1) * width] @ bf16_bits_to_f64(w_down_bits[u]).T for u in range(g)]
+    z = f64_to_bf16_bits(np.concatenate(zs, axis=1))
+    y = f64_to_bf16_bits(bf16_bits_to_f64(z) @ bf16_bits_to_f64(w_proj_bits).T)
+    return z, y

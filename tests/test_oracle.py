@@ -560,3 +560,67 @@ def test_compress_epilogue_closed_forms():
     step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
     err = np.abs(O.mxfp4_decode(c4["ikeys"], c4["iscale"]) - c4["ipre"]) / X
     assert np.all(err <= 0.5 * step + np.maximum(a - 6.0, 0.0) + 1e-12)
+
+
+# ----------------------------------------------------------------------------- query / output
+# projections: closed forms with identity and one-hot weights, exact scaling, group isolation
+
+def _bf16(x):
+    return O.f64_to_bf16_bits(np.asarray(x, dtype=np.float64))
+
+
+def test_query_projections_closed_forms():
+    rng = np.random.default_rng(31)
+    T, D, n_h, c, H_I, d_I = 5, 64, 2, 32, 2, 32
+    r_q = n_h * c                       # = 64 = D: identity down-projection possible
+    h = _bf16(rng.standard_normal((T, D)))
+    eye = _bf16(np.eye(D))
+    w_w = _bf16(np.eye(D)[[3, 40]])    # w^I_j = h[:, 3], h[:, 40]
+    w_uq = _bf16(np.eye(r_q))           # qpre = c^Q split into heads
+    w_iuq = _bf16(rng.standard_normal((H_I * d_I, r_q)) / 8)
+    ones = np.ones(c)
+    r = O.query_projections(h, eye, w_w, w_uq, w_iuq, ones, n_h, c, H_I, d_I, 1e-6)
+    hf = O.bf16_bits_to_f64(h)
+    assert np.array_equal(r["cq"], h)                                   # identity W^DQ
+    assert np.array_equal(r["wi"].astype(np.float64), hf[:, [3, 40]])   # one-hot W_w
+    assert np.array_equal(r["qpre"], hf.reshape(T, n_h, c))             # heads in order
+    q = O.bf16_bits_to_f64(r["q"])
+    rms = np.sqrt(np.mean(q * q, axis=-1))
+    assert np.allclose(rms, 1.0, atol=4e-3)                              # gain 1: unit RMS
+    cos = np.sum(q * r["qpre"], -1) / np.linalg.norm(q, axis=-1) / np.linalg.norm(r["qpre"], axis=-1)
+    assert np.all(cos > 1 - 1e-4)                                       # direction kept
+    dec = O.e4m3_decode(r["qi"]) * r["qi_scale"][..., None].astype(np.float64)
+    big = np.abs(r["qi_pre"]) > r["qi_scale"][..., None] * 2.0 ** -6
+    assert np.all(np.abs(dec - r["qi_pre"])[big] <= np.abs(r["qi_pre"])[big] * 2.0 ** -4)
+    # doubling h (exact in bf16) doubles c^Q, q^I's scales and w^I, keeps the codes and q
+    r2 = O.query_projections(_bf16(2 * hf), eye, w_w, w_uq, w_iuq, ones, n_h, c, H_I, d_I, 0.0)
+    r1 = O.query_projections(h, eye, w_w, w_uq, w_iuq, ones, n_h, c, H_I, d_I, 0.0)
+    assert np.array_equal(O.bf16_bits_to_f64(r2["cq"]), 2 * O.bf16_bits_to_f64(r1["cq"]))
+    assert np.array_equal(r2["qi"], r1["qi"]) and np.array_equal(r2["qi_scale"], 2 * r1["qi_scale"])
+    assert np.array_equal(r2["q"], r1["q"]) and np.array_equal(r2["wi"], 2 * r1["wi"])
+
+
+def test_grouped_output_projection_closed_forms():
+    rng = np.random.default_rng(32)
+    T, n_h, c, g = 3, 4, 16, 2
+    width = n_h // g * c                 # 32 dims per group
+    o = _bf16(rng.standard_normal((T, n_h, c)))
+    of = O.bf16_bits_to_f64(o).reshape(T, -1)
+    # identity blocks (r_o = width): z is O itself, concatenated in head order
+    w_down = np.stack([_bf16(np.eye(width))] * g)
+    w_proj = _bf16(np.eye(g * width)[[5, 40, 63]])   # y picks z columns 5, 40, 63
+    z, y = O.grouped_output_projection(o, w_down, w_proj, g)
+    assert np.array_equal(z, o.reshape(T, -1))
+    assert np.array_equal(O.bf16_bits_to_f64(y), of[:, [5, 40, 63]])
+    # random blocks: group u's z depends only on its own heads
+    w_down = _bf16(rng.standard_normal((g, 8, width)) / 4)
+    w_proj = _bf16(rng.standard_normal((6, g * 8)) / 4)
+    z, y = O.grouped_output_projection(o, w_down, w_proj, g)
+    o0 = O.bf16_bits_to_f64(o).copy()
+    o0[:, n_h // g:, :] = 0.0           # silence group 1's heads
+    z0, _ = O.grouped_output_projection(_bf16(o0), w_down, w_proj, g)
+    assert np.array_equal(z0[:, :8], z[:, :8])
+    assert np.all(O.bf16_bits_to_f64(z0[:, 8:]) == 0.0)
+    # one group with identity weights is a plain projection
+    z1, y1 = O.grouped_output_projection(o, _bf16(np.eye(n_h * c))[None], _bf16(np.eye(n_h * c)), 1)
+    assert np.array_equal(z1, o.reshape(T, -1)) and np.array_equal(y1, z1)
