@@ -59,6 +59,8 @@ extern "C" {
 #define CSA_OP_HCA_MQA 3
 #define CSA_OP_DECODE 4
 #define CSA_OP_PREFILL 5
+#define CSA_OP_QUERY_PROJ 6  /* csa_query_proj over B*nq tokens (n_max ignored) */
+#define CSA_OP_OUTPUT_PROJ 7 /* csa_output_proj over B*nq tokens (n_max ignored) */
 
 /* Layer configuration, passed by pointer (read during the call only).
  * Supported set (CSA_ERR_INVALID_ARG otherwise):
@@ -85,6 +87,12 @@ typedef struct csa_config {
                                  p * rope_inv_freq[i] (base 160000 for compressed layers; any
                                  table, e.g. YaRN-scaled, may be passed) */
   int32_t idx_key_format;     /* CSA_IDX_E4M3 (0) or CSA_IDX_MXFP4 (1); CSA only */
+  /* Projections on either side of attention (csa_query_proj / csa_output_proj only):
+   * query LoRA rank r_q (1024 Flash, 1536 Pro), output groups g (8 / 16), output rank r_o
+   * (1024).  Book, chapter "Attention": configuration table and section "注意力实现细节". */
+  int32_t q_rank;
+  int32_t out_groups;
+  int32_t out_rank;
 } csa_config_t;
 
 /* Caller-owned per-sequence attention state for B sequences (all device pointers).
@@ -251,6 +259,55 @@ int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H
                 const uint8_t* qi, const float* qi_scale, const float* wi, const float* sink,
                 uint16_t* out, int32_t* idx_out, void* workspace, size_t ws_bytes,
                 void* stream);
+
+/* Weights of the query-side projections (device, bf16 unless noted; one row per output
+ * column, like w_cat):
+ *  w_dq  [q_rank, hidden]            W^DQ  (c^Q = h W^DQ)
+ *  w_w   [idx_heads, hidden]         W_w   (w^I = h W_w; CSA, NULL for HCA)
+ *  w_uq  [n_heads*head_dim, q_rank]  W^UQ  (attention query before its per-head RMSNorm)
+ *  w_iuq [idx_heads*idx_dim, q_rank] W^IUQ (q^I = c^Q W^IUQ; CSA, NULL for HCA)
+ *  gamma_q fp32 [head_dim]           RMSNorm gain of every attention-query head */
+typedef struct csa_qproj_weights {
+  const uint16_t* w_dq;
+  const uint16_t* w_w;
+  const uint16_t* w_uq;
+  const uint16_t* w_iuq;
+  const float* gamma_q;
+} csa_qproj_weights_t;
+
+/* Weights of the grouped output projection (device, bf16, one row per output column):
+ *  w_down [out_groups, out_rank, (n_heads/out_groups)*head_dim]  W^[u]_down of group u
+ *  w_proj [hidden, out_groups*out_rank]                         Proj */
+typedef struct csa_oproj_weights {
+  const uint16_t* w_down;
+  const uint16_t* w_proj;
+} csa_oproj_weights_t;
+
+/* csa_query_proj - the queries of T tokens of B sequences from their hidden states.
+ * Book, chapter "Attention", section "CSA 的完整路径": c^Q = h W^DQ, q^I = c^Q W^IUQ split
+ * into idx_heads heads, w^I = h W_w; section "注意力实现细节": queries are RMS-normalised.
+ *  H bf16 [B, T, hidden];
+ *  q_out bf16 [B, T, n_heads, head_dim]: c^Q W^UQ, each head RMS-normalised over head_dim with
+ *        gain gamma_q (eps = rms_eps), not rotated (the attention calls rotate it at t);
+ *  qi_out e4m3 [B, T, idx_heads, idx_dim], qi_scale_out fp32 [B, T, idx_heads] (max|x|/448 per
+ *        head), wi_out fp32 [B, T, idx_heads]: the csa_index_topk inputs (CSA; NULL for HCA).
+ * c^Q is kept in bf16 between the two products; all products accumulate in fp32.
+ * Requires hidden and q_rank multiples of 64. */
+int csa_query_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,
+                   const csa_qproj_weights_t* w, uint16_t* q_out, uint8_t* qi_out,
+                   float* qi_scale_out, float* wi_out, void* workspace, size_t ws_bytes,
+                   void* stream);
+
+/* csa_output_proj - grouped output projection of T tokens of B sequences.
+ * Book, chapter "Attention", section "注意力实现细节" and its component table:
+ * O = Concat_u O^[u] (group u = heads u*n_heads/g .. (u+1)*n_heads/g-1), z^[u] = O^[u] W^[u]_down,
+ * y = Proj(Concat_u z^[u]).
+ *  O bf16 [B, T, n_heads, head_dim] (the attention output); y_out bf16 [B, T, hidden].
+ * z is kept in bf16 between the two products.  Requires out_groups dividing n_heads and
+ * (n_heads/out_groups)*head_dim, out_groups*out_rank multiples of 64. */
+int csa_output_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* O,
+                    const csa_oproj_weights_t* w, uint16_t* y_out, void* workspace,
+                    size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

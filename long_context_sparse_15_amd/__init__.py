@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
 MODE_CSA, MODE_HCA = 0, 1
 IDX_E4M3, IDX_MXFP4 = 0, 1
-OP_COMPRESS, OP_INDEX_TOPK, OP_SPARSE_MQA, OP_HCA_MQA, OP_DECODE, OP_PREFILL = range(6)
+(OP_COMPRESS, OP_INDEX_TOPK, OP_SPARSE_MQA, OP_HCA_MQA, OP_DECODE, OP_PREFILL, OP_QUERY_PROJ,
+ OP_OUTPUT_PROJ) = range(8)
 
 
 class CsaError(RuntimeError):
@@ -28,7 +29,8 @@ class Config(ctypes.Structure):
                 ("idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("rope_inv_freq", ctypes.c_void_p),
-                ("idx_key_format", ctypes.c_int32)]
+                ("idx_key_format", ctypes.c_int32), ("q_rank", ctypes.c_int32),
+                ("out_groups", ctypes.c_int32), ("out_rank", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -36,6 +38,15 @@ class Cache(ctypes.Structure):
                 ("entries", ctypes.c_void_p), ("idx_keys", ctypes.c_void_p),
                 ("idx_scale", ctypes.c_void_p), ("window", ctypes.c_void_p),
                 ("tail", ctypes.c_void_p), ("n_entries", ctypes.c_void_p)]
+
+
+class QProjWeights(ctypes.Structure):
+    _fields_ = [("w_dq", ctypes.c_void_p), ("w_w", ctypes.c_void_p), ("w_uq", ctypes.c_void_p),
+                ("w_iuq", ctypes.c_void_p), ("gamma_q", ctypes.c_void_p)]
+
+
+class OProjWeights(ctypes.Structure):
+    _fields_ = [("w_down", ctypes.c_void_p), ("w_proj", ctypes.c_void_p)]
 
 
 class KernelTime(ctypes.Structure):
@@ -69,6 +80,8 @@ _SIGS = {
                    ctypes.c_int),
     "csa_prefill": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
                     ctypes.c_int),
+    "csa_query_proj": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "csa_output_proj": ([_P, _I, _I, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -133,11 +146,12 @@ def _stream(stream):
 
 def make_config(mode, m, n_heads, head_dim, rope_dim, inv_freq, top_k=0, n_win=128,
                 idx_heads=0, idx_dim=0, hidden=0, softmax_scale=None, rms_eps=1e-6,
-                idx_key_format=0):
+                idx_key_format=0, q_rank=0, out_groups=0, out_rank=0):
     """A Config; keeps a reference to the device inv_freq tensor for the config's lifetime."""
     cfg = Config(mode, m, top_k, n_win, n_heads, head_dim, rope_dim, idx_heads, idx_dim, hidden,
                  float(softmax_scale if softmax_scale is not None else head_dim ** -0.5),
-                 float(rms_eps), _ptr(inv_freq).value, int(idx_key_format))
+                 float(rms_eps), _ptr(inv_freq).value, int(idx_key_format), int(q_rank),
+                 int(out_groups), int(out_rank))
     cfg._keep = inv_freq
     return cfg
 
@@ -156,6 +170,38 @@ def make_weights(w_cat, bias_a, gamma, gamma_win, bias_b=None, bias_ia=None, bia
     w = Weights(v(w_cat), v(bias_a), v(bias_b), v(bias_ia), v(bias_ib), v(gamma), v(gamma_win))
     w._keep = (w_cat, bias_a, bias_b, bias_ia, bias_ib, gamma, gamma_win)
     return w
+
+
+def make_qproj_weights(w_dq, w_uq, gamma_q, w_w=None, w_iuq=None):
+    v = lambda t: _ptr(t) and _ptr(t).value
+    w = QProjWeights(v(w_dq), v(w_w), v(w_uq), v(w_iuq), v(gamma_q))
+    w._keep = (w_dq, w_w, w_uq, w_iuq, gamma_q)
+    return w
+
+
+def make_oproj_weights(w_down, w_proj):
+    w = OProjWeights(_ptr(w_down).value, _ptr(w_proj).value)
+    w._keep = (w_down, w_proj)
+    return w
+
+
+def query_proj(cfg, H, weights, q_out, ws, qi_out=None, qi_scale_out=None, wi_out=None,
+               stream=None):
+    """csa_query_proj: H [B, T, hidden] -> q_out [B, T, n_heads, head_dim] (and the indexer
+    query, its scales and head weights in CSA mode)."""
+    B, T = H.shape[0], H.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib().csa_query_proj(ctypes.byref(cfg), B, T, _ptr(H), ctypes.byref(weights),
+                                _ptr(q_out), _ptr(qi_out), _ptr(qi_scale_out), _ptr(wi_out), wp,
+                                wn, _stream(stream)), "csa_query_proj")
+
+
+def output_proj(cfg, O, weights, y_out, ws, stream=None):
+    """csa_output_proj: O [B, T, n_heads, head_dim] -> y_out [B, T, hidden]."""
+    B, T = O.shape[0], O.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib().csa_output_proj(ctypes.byref(cfg), B, T, _ptr(O), ctypes.byref(weights),
+                                 _ptr(y_out), wp, wn, _stream(stream)), "csa_output_proj")
 
 
 def weight_cols(cfg):

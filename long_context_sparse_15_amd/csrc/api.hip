@@ -237,6 +237,28 @@ int run_attend(const csa_config_t* c, int B, int nq, const uint16_t* q, const cs
   return e == hipSuccess ? CSA_OK : hip_fail(e, "attention launch");
 }
 
+int check_qproj_config(const csa_config_t* c) {
+  if (c->hidden < 64 || c->hidden % 64)
+    return fail(CSA_ERR_INVALID_ARG, "hidden=%d must be a positive multiple of 64", c->hidden);
+  if (c->q_rank < 64 || c->q_rank % 64)
+    return fail(CSA_ERR_INVALID_ARG, "q_rank=%d must be a positive multiple of 64", c->q_rank);
+  return CSA_OK;
+}
+
+int check_oproj_config(const csa_config_t* c) {
+  if (c->hidden < 1) return fail(CSA_ERR_INVALID_ARG, "hidden=%d < 1", c->hidden);
+  if (c->out_groups < 1 || c->n_heads % c->out_groups)
+    return fail(CSA_ERR_INVALID_ARG, "out_groups=%d must divide n_heads=%d", c->out_groups,
+                c->n_heads);
+  if ((c->n_heads / c->out_groups * c->head_dim) % 64)
+    return fail(CSA_ERR_INVALID_ARG, "a group's width (n_heads/out_groups*head_dim) must be a "
+                "multiple of 64");
+  if (c->out_rank < 1 || (c->out_groups * c->out_rank) % 64)
+    return fail(CSA_ERR_INVALID_ARG, "out_groups*out_rank=%d must be a positive multiple of 64",
+                c->out_groups * c->out_rank);
+  return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -294,6 +316,15 @@ int csa_workspace_size(const csa_config_t* cfg, int32_t op, int32_t B, int32_t n
     case CSA_OP_HCA_MQA: *bytes = ws_mqa(cfg, B * nq, max_list_dense(cfg, n_max)); break;
     case CSA_OP_DECODE: *bytes = ws_layer(cfg, B, 1, n_max, false, true); break;
     case CSA_OP_PREFILL: *bytes = ws_layer(cfg, B, nq, n_max, true, true); break;
+    case CSA_OP_QUERY_PROJ:
+      if ((rc = check_qproj_config(cfg))) return rc;
+      *bytes = csa::query_proj_workspace(B * nq, cfg->q_rank, cfg->n_heads, cfg->head_dim,
+                                         is_csa(cfg) ? cfg->idx_heads : 0, cfg->idx_dim);
+      break;
+    case CSA_OP_OUTPUT_PROJ:
+      if ((rc = check_oproj_config(cfg))) return rc;
+      *bytes = csa::output_proj_workspace(B * nq, cfg->out_groups, cfg->out_rank);
+      break;
     default: return fail(CSA_ERR_INVALID_ARG, "unknown op %d", op);
   }
   return CSA_OK;
@@ -431,6 +462,77 @@ int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H
     return run_attend(cfg, B, T, q, cache, idx, nullptr, sink, out, nullptr, p, s);
   }
   return run_attend(cfg, B, T, q, cache, nullptr, nullptr, sink, out, nullptr, p, s);
+}
+
+int csa_query_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,
+                   const csa_qproj_weights_t* w, uint16_t* q_out, uint8_t* qi_out,
+                   float* qi_scale_out, float* wi_out, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  int rc = check_config(cfg, false);
+  if (rc) return rc;
+  if ((rc = check_qproj_config(cfg))) return rc;
+  if (B < 1 || T < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, T=%d must be >= 1", B, T);
+  if (!H || !w || !w->w_dq || !w->w_uq || !w->gamma_q || !q_out)
+    return fail(CSA_ERR_INVALID_ARG, "H, weights (w_dq, w_uq, gamma_q) or q_out is NULL");
+  const bool csa_mode = is_csa(cfg);
+  if (csa_mode && (!w->w_w || !w->w_iuq || !qi_out || !qi_scale_out || !wi_out))
+    return fail(CSA_ERR_INVALID_ARG, "CSA needs w_w, w_iuq, qi_out, qi_scale_out and wi_out");
+  const int BT = B * T;
+  const size_t need = csa::query_proj_workspace(BT, cfg->q_rank, cfg->n_heads, cfg->head_dim,
+                                                csa_mode ? cfg->idx_heads : 0, cfg->idx_dim);
+  if (!workspace || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  csa::QueryProjArgs a;
+  a.BT = BT;
+  a.D = cfg->hidden;
+  a.r_q = cfg->q_rank;
+  a.n_h = cfg->n_heads;
+  a.c = cfg->head_dim;
+  a.H_I = csa_mode ? cfg->idx_heads : 0;
+  a.d_I = csa_mode ? cfg->idx_dim : 0;
+  a.eps = cfg->rms_eps;
+  a.H = H;
+  a.w_dq = w->w_dq;
+  a.w_w = csa_mode ? w->w_w : nullptr;
+  a.w_uq = w->w_uq;
+  a.w_iuq = csa_mode ? w->w_iuq : nullptr;
+  a.gamma_q = w->gamma_q;
+  a.q = q_out;
+  a.qi = csa_mode ? qi_out : nullptr;
+  a.qi_scale = csa_mode ? qi_scale_out : nullptr;
+  a.wi = csa_mode ? wi_out : nullptr;
+  a.ws = workspace;
+  const hipError_t e = csa::launch_query_proj(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_query_proj");
+}
+
+int csa_output_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* O,
+                    const csa_oproj_weights_t* w, uint16_t* y_out, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg, false);
+  if (rc) return rc;
+  if ((rc = check_oproj_config(cfg))) return rc;
+  if (B < 1 || T < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, T=%d must be >= 1", B, T);
+  if (!O || !w || !w->w_down || !w->w_proj || !y_out)
+    return fail(CSA_ERR_INVALID_ARG, "O, w_down, w_proj or y_out is NULL");
+  const int BT = B * T;
+  const size_t need = csa::output_proj_workspace(BT, cfg->out_groups, cfg->out_rank);
+  if (!workspace || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  csa::OutputProjArgs a;
+  a.BT = BT;
+  a.D = cfg->hidden;
+  a.n_h = cfg->n_heads;
+  a.c = cfg->head_dim;
+  a.g = cfg->out_groups;
+  a.r_o = cfg->out_rank;
+  a.O = O;
+  a.w_down = w->w_down;
+  a.w_proj = w->w_proj;
+  a.y = y_out;
+  a.ws = workspace;
+  const hipError_t e = csa::launch_output_proj(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_output_proj");
 }
 
 }  // extern "C"

@@ -28,6 +28,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
 }
+// E4M3 ("fn") encoding with round-to-nearest-even and saturation to +-448, from the format's
+// bit fields (bias 7, 3 mantissa bits, subnormal quantum 2^-9).
+__device__ __forceinline__ uint8_t e4m3_rne(float x) {
+  const uint8_t sign = (__float_as_uint(x) >> 24) & 0x80;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (!(a < 448.f)) {
+    code = 0x7e;
+  } else if (a < 0.015625f) {  // below 2^-6: subnormal quantum 2^-9
+    code = static_cast<uint32_t>(rintf(a * 512.f));  // 8 -> 0x08 = 2^-6, still correct
+  } else {
+    int ex;
+    const float f = frexpf(a, &ex);  // a = f * 2^ex, f in [0.5, 1)
+    uint32_t mant = static_cast<uint32_t>(rintf((f * 2.f - 1.f) * 8.f));
+    uint32_t field = static_cast<uint32_t>(ex + 6);
+    if (mant == 8) {
+      mant = 0;
+      ++field;
+    }
+    code = (field << 3) | mant;
+    if (code > 0x7e) code = 0x7e;
+  }
+  return static_cast<uint8_t>(code | sign);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }

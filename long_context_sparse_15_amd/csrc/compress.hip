@@ -115,9 +115,12 @@ constexpr size_t kGemm2Lds = 2 * (G2M + G2N) * G2K * sizeof(uint16_t);  // 128 K
 
 __device__ __forceinline__ int g2_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// C[m, n] = sum_k A[m, k] W[n, k] with row strides lda, ldw, ldc (elements); OutT = float, or
+// uint16_t for a bf16 result (round to nearest even).
+template <typename OutT>
 __global__ __launch_bounds__(G2_THREADS) void gemm_tn_bf16_256_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, float* __restrict__ Cst,
-    int M, int N, int K, int tiles_m, int tiles_n, int per_xcd) {
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, OutT* __restrict__ Cst,
+    int M, int N, int K, int lda, int ldw, int ldc, int tiles_m, int tiles_n, int per_xcd) {
   extern __shared__ __align__(16) unsigned char smem[];
   typedef __attribute__((address_space(3))) void lds_void;
   const int bid = blockIdx.x;
@@ -144,8 +147,8 @@ __global__ __launch_bounds__(G2_THREADS) void gemm_tn_bf16_256_kernel(
   for (int q = 0; q < 4; ++q) {
     const int r = (4 * wave + q) * 8 + (l >> 3);
     const int c = (l & 7) ^ g2_swz(r);
-    asrc[q] = A + static_cast<size_t>(min(m0 + r, M - 1)) * K + c * 8;
-    bsrc[q] = Bw + static_cast<size_t>(min(n0 + r, N - 1)) * K + c * 8;
+    asrc[q] = A + static_cast<size_t>(min(m0 + r, M - 1)) * lda + c * 8;
+    bsrc[q] = Bw + static_cast<size_t>(min(n0 + r, N - 1)) * ldw + c * 8;
   }
   auto issue = [&](int kt, int stage) {
     unsigned char* sa = smem + stage * 65536 + (4 * wave) * 8 * 128;
@@ -211,38 +214,48 @@ __global__ __launch_bounds__(G2_THREADS) void gemm_tn_bf16_256_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int m = m0 + wm * 128 + mi * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (m < M) Cst[static_cast<size_t>(m) * N + n] = acc[mi][ni][i];
+        if (m < M) {
+          if constexpr (sizeof(OutT) == 2)
+            Cst[static_cast<size_t>(m) * ldc + n] = f32_to_bf16(acc[mi][ni][i]);
+          else
+            Cst[static_cast<size_t>(m) * ldc + n] = acc[mi][ni][i];
+        }
       }
     }
 }
 
-
-// ============================================================================ helpers
-// E4M3 ("fn") encoding with round-to-nearest-even and saturation to +-448, from the format's
-// bit fields (bias 7, 3 mantissa bits, subnormal quantum 2^-9).
-__device__ __forceinline__ uint8_t e4m3_rne(float x) {
-  const uint8_t sign = (__float_as_uint(x) >> 24) & 0x80;
-  const float a = fabsf(x);
-  uint32_t code;
-  if (!(a < 448.f)) {
-    code = 0x7e;
-  } else if (a < 0.015625f) {  // below 2^-6: subnormal quantum 2^-9
-    code = static_cast<uint32_t>(rintf(a * 512.f));  // 8 -> 0x08 = 2^-6, still correct
-  } else {
-    int ex;
-    const float f = frexpf(a, &ex);  // a = f * 2^ex, f in [0.5, 1)
-    uint32_t mant = static_cast<uint32_t>(rintf((f * 2.f - 1.f) * 8.f));
-    uint32_t field = static_cast<uint32_t>(ex + 6);
-    if (mant == 8) {
-      mant = 0;
-      ++field;
-    }
-    code = (field << 3) | mant;
-    if (code > 0x7e) code = 0x7e;
+// One launch of the large-tile GEMM (K % 64 == 0): tiles in XCD order, LDS attribute set once
+// per output type.
+template <typename OutT>
+static hipError_t launch_gemm_256(const uint16_t* A, int lda, const uint16_t* W, int ldw, OutT* C,
+                                  int ldc, int M, int N, int K, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tn_bf16_256_kernel<OutT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(kGemm2Lds));
+    if (e != hipSuccess) return e;
+    attr = true;
   }
-  return static_cast<uint8_t>(code | sign);
+  const int tm2 = (M + G2M - 1) / G2M, tn2 = (N + G2N - 1) / G2N;
+  const int per_xcd = (tm2 * tn2 + 7) / 8;
+  gemm_tn_bf16_256_kernel<OutT><<<8 * per_xcd, G2_THREADS, kGemm2Lds, s>>>(
+      A, W, C, M, N, K, lda, ldw, ldc, tm2, tn2, per_xcd);
+  return hipGetLastError();
 }
 
+hipError_t launch_gemm_tn(const GemmArgs& g, hipStream_t s) {
+  if (g.K % G2K != 0 || g.M < 1 || g.N < 1) return hipErrorInvalidValue;
+  ProfScope ps(g.name, s);
+  if (g.bf16_out)
+    return launch_gemm_256(g.A, g.lda, g.W, g.ldw, static_cast<uint16_t*>(g.C), g.ldc, g.M, g.N,
+                           g.K, s);
+  return launch_gemm_256(g.A, g.lda, g.W, g.ldw, static_cast<float*>(g.C), g.ldc, g.M, g.N, g.K,
+                         s);
+}
+
+
+// ============================================================================ helpers
 // E2M1 (OCP MXFP4 element: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to x, ties to the even
 // code, saturating at 6; the sign bit (bit 3) follows x's sign bit.
 __device__ __forceinline__ uint32_t e2m1_rne(float x) {
@@ -474,19 +487,20 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   const int M = a.B * a.T;
   const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (a.n_cols + GBN - 1) / GBN;
   if (a.D % G2K == 0) {
-    static bool attr = false;
-    if (!attr) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tn_bf16_256_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(kGemm2Lds));
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
-    const int tm2 = (M + G2M - 1) / G2M, tn2 = (a.n_cols + G2N - 1) / G2N;
-    const int per_xcd = (tm2 * tn2 + 7) / 8;
-    ProfScope ps("compress_gemm", s);
-    gemm_tn_bf16_256_kernel<<<8 * per_xcd, G2_THREADS, kGemm2Lds, s>>>(
-        a.H, a.W, a.proj, M, a.n_cols, a.D, tm2, tn2, per_xcd);
+    GemmArgs g;
+    g.A = a.H;
+    g.lda = a.D;
+    g.W = a.W;
+    g.ldw = a.D;
+    g.C = a.proj;
+    g.ldc = a.n_cols;
+    g.M = M;
+    g.N = a.n_cols;
+    g.K = a.D;
+    g.bf16_out = false;
+    g.name = "compress_gemm";
+    hipError_t e = launch_gemm_tn(g, s);
+    if (e != hipSuccess) return e;
   } else {
     ProfScope ps("compress_gemm", s);
     gemm_tn_bf16_kernel<<<tiles_m * tiles_n, 256, 0, s>>>(a.H, a.W, a.proj, M, a.n_cols, a.D,

@@ -87,6 +87,50 @@ struct CompressArgs {
 size_t compress_workspace(int B, int T, int n_cols);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- dense projections
+// C[M, N] = A[M, K] W[N, K]^T, bf16 operands, fp32 accumulation, K % 64 == 0.
+struct GemmArgs {
+  const uint16_t* A;
+  int lda;
+  const uint16_t* W;
+  int ldw;
+  void* C;          // fp32, or bf16 when bf16_out
+  int ldc;
+  int M, N, K;
+  bool bf16_out;
+  const char* name;  // label for launch timing
+};
+hipError_t launch_gemm_tn(const GemmArgs& g, hipStream_t s);
+
+struct QueryProjArgs {
+  int BT, D, r_q, n_h, c, H_I, d_I;
+  float eps;
+  const uint16_t* H;      // [BT, D]
+  const uint16_t* w_dq;   // [r_q, D]
+  const uint16_t* w_w;    // [H_I, D] or nullptr
+  const uint16_t* w_uq;   // [n_h * c, r_q]
+  const uint16_t* w_iuq;  // [H_I * d_I, r_q] or nullptr
+  const float* gamma_q;   // [c]
+  uint16_t* q;            // [BT, n_h, c]
+  uint8_t* qi;            // [BT, H_I, d_I] or nullptr
+  float* qi_scale;        // [BT, H_I] or nullptr
+  float* wi;              // [BT, H_I] or nullptr
+  void* ws;
+};
+size_t query_proj_workspace(int BT, int r_q, int n_h, int c, int H_I, int d_I);
+hipError_t launch_query_proj(const QueryProjArgs& a, hipStream_t s);
+
+struct OutputProjArgs {
+  int BT, D, n_h, c, g, r_o;
+  const uint16_t* O;       // [BT, n_h, c]
+  const uint16_t* w_down;  // [g, r_o, (n_h / g) * c]
+  const uint16_t* w_proj;  // [D, g * r_o]
+  uint16_t* y;             // [BT, D]
+  void* ws;
+};
+size_t output_proj_workspace(int BT, int g, int r_o);
+hipError_t launch_output_proj(const OutputProjArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- misc
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 

@@ -36,7 +36,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
         assert n in csa._SIGS, n
@@ -98,3 +98,18 @@ def test_null_arguments_are_rejected(L):
     assert "cache" in csa.last_error()
     assert L.hca_dense_mqa(ctypes.byref(_cfg(csa.MODE_HCA)), 1, 1, None, None, None, None,
                            None, None, None, 0, None) == -1
+
+
+def test_projection_configs_are_checked(L):
+    c = _cfg(hidden=4096, q_rank=1024, out_groups=8, out_rank=1024)
+    q = csa.workspace_size(c, csa.OP_QUERY_PROJ, 1, 4096, 1)
+    o = csa.workspace_size(c, csa.OP_OUTPUT_PROJ, 1, 4096, 1)
+    assert q >= 4096 * 1024 * 2 and o >= 4096 * 8 * 1024 * 2
+    for bad in (dict(q_rank=1000), dict(hidden=4000)):
+        with pytest.raises(csa.CsaError):
+            csa.workspace_size(_cfg(**dict(dict(hidden=4096, q_rank=1024), **bad)),
+                               csa.OP_QUERY_PROJ, 1, 16, 1)
+    for bad in (dict(out_groups=3), dict(out_rank=10)):
+        with pytest.raises(csa.CsaError):
+            csa.workspace_size(_cfg(**dict(dict(hidden=4096, out_groups=8, out_rank=1024), **bad)),
+                               csa.OP_OUTPUT_PROJ, 1, 16, 1)

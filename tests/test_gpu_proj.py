@@ -1,0 +1,104 @@
+"""GPU parity of the projections on either side of attention (csa_query_proj,
+csa_output_proj) against the oracle: a tiny layer shape, the V4-Flash shape (hidden 4096,
+r_q 1024, 64 heads x 512, indexer 64 x 128, 8 output groups of rank 1024) on sampled tokens,
+HCA mode (no indexer query), and a token count that spans two row chunks of the query
+up-projection's fp32 buffer."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_15_amd as csa
+import oracle as O
+from synth import inputs as S
+from gpu_common import DEV, check_close, dev, host_bits, say, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _e4m3_steps(a, b):
+    mag = lambda c: np.where(c & 0x80, -(c & 0x7F).astype(np.int32), (c & 0x7F).astype(np.int32))
+    return np.abs(mag(a.astype(np.uint8)) - mag(b.astype(np.uint8)))
+
+
+def _cfg(mode, D, r_q, n_h, c, H_I, d_I, g=1, r_o=64):
+    inv = dev(S.rope_inv_freq(64, 160000.0))
+    return csa.make_config(mode, 4 if mode == csa.MODE_CSA else 128, n_h, c, 64, inv, top_k=64,
+                           idx_heads=H_I, idx_dim=d_I, hidden=D, q_rank=r_q, out_groups=g,
+                           out_rank=r_o)
+
+
+@pytest.mark.parametrize("case", [
+    # (mode, B, T, D, r_q, n_h, c, H_I, d_I, sampled rows or None = all)
+    ("csa", 1, 37, 512, 128, 8, 128, 4, 64, None),
+    ("hca", 2, 20, 512, 192, 8, 128, 0, 0, None),
+    ("csa", 2, 300, 4096, 1024, 64, 512, 64, 128, [0, 1, 150, 299, 300, 451, 599]),
+    ("csa", 1, 1600, 4096, 1024, 64, 512, 64, 128, [0, 1535, 1536, 1599]),  # two row chunks
+])
+def test_query_proj_parity(case):
+    mode, B, T, D, r_q, n_h, c, H_I, d_I, rows = case
+    say("query proj", case)
+    rng = np.random.default_rng(41)
+    csa_mode = mode == "csa"
+    h = S.bf16_normal(rng, (B, T, D))
+    w_dq = S.bf16_normal(rng, (r_q, D), std=D ** -0.5)
+    w_uq = S.bf16_normal(rng, (n_h * c, r_q), std=r_q ** -0.5)
+    gamma = (1.0 + 0.1 * rng.standard_normal(c)).astype(np.float32)
+    w_w = S.bf16_normal(rng, (H_I, D), std=D ** -0.5) if csa_mode else None
+    w_iuq = S.bf16_normal(rng, (H_I * d_I, r_q), std=r_q ** -0.5) if csa_mode else None
+    cfg = _cfg(csa.MODE_CSA if csa_mode else csa.MODE_HCA, D, r_q, n_h, c, max(H_I, 1),
+               max(d_I, 32))
+    w = csa.make_qproj_weights(dev(w_dq), dev(w_uq), dev(gamma), w_w=dev(w_w) if csa_mode else None,
+                               w_iuq=dev(w_iuq) if csa_mode else None)
+    q = torch.empty((B, T, n_h, c), dtype=torch.int16, device=DEV)
+    kw = {}
+    if csa_mode:
+        kw = dict(qi_out=torch.empty((B, T, H_I, d_I), dtype=torch.uint8, device=DEV),
+                  qi_scale_out=torch.empty((B, T, H_I), dtype=torch.float32, device=DEV),
+                  wi_out=torch.empty((B, T, H_I), dtype=torch.float32, device=DEV))
+    ws = workspace(csa.workspace_size(cfg, csa.OP_QUERY_PROJ, B, T, 1))
+    csa.query_proj(cfg, dev(h), w, q, ws, **kw)
+    torch.cuda.synchronize()
+    hh = h.reshape(B * T, D)
+    sel = np.arange(B * T) if rows is None else np.array(rows)
+    ref = O.query_projections(hh[sel], w_dq, w_w if csa_mode else np.zeros((0, D), np.uint16),
+                              w_uq, w_iuq if csa_mode else np.zeros((0, r_q), np.uint16), gamma,
+                              n_h, c, H_I, max(d_I, 1), 1e-6)
+    q_h = O.bf16_bits_to_f64(host_bits(q).reshape(B * T, n_h, c)[sel])
+    check_close(q_h, O.bf16_bits_to_f64(ref["q"]), "q")
+    if csa_mode:
+        qi = kw["qi_out"].cpu().numpy().reshape(B * T, H_I, d_I)[sel]
+        qs = kw["qi_scale_out"].cpu().numpy().reshape(B * T, H_I)[sel]
+        wi = kw["wi_out"].cpu().numpy().reshape(B * T, H_I)[sel]
+        check_close(wi, ref["wi"], "w^I", atol=1e-5, rtol=1e-4)
+        check_close(qs, ref["qi_scale"], "q^I scales", atol=0, rtol=2e-2)
+        # c^Q is stored in bf16 on both sides: a one-ulp difference there moves q^I slightly,
+        # so codes may differ by a step and the scales by the same relative amount
+        dec_g = O.e4m3_decode(qi) * qs[..., None].astype(np.float64)
+        dec_r = O.e4m3_decode(ref["qi"]) * ref["qi_scale"][..., None].astype(np.float64)
+        check_close(dec_g, dec_r, "q^I values", atol=2e-2 * np.abs(dec_r).max(), rtol=0.13)
+
+
+@pytest.mark.parametrize("case", [
+    # (B, T, D, n_h, c, g, r_o, sampled rows or None)
+    (1, 45, 512, 8, 128, 2, 64, None),
+    (2, 300, 4096, 64, 512, 8, 1024, [0, 7, 299, 300, 599]),
+    (1, 64, 512, 8, 128, 1, 128, None),
+])
+def test_output_proj_parity(case):
+    B, T, D, n_h, c, g, r_o, rows = case
+    say("output proj", case)
+    rng = np.random.default_rng(42)
+    o = S.bf16_normal(rng, (B, T, n_h, c))
+    width = n_h // g * c
+    w_down = S.bf16_normal(rng, (g, r_o, width), std=width ** -0.5)
+    w_proj = S.bf16_normal(rng, (D, g * r_o), std=(g * r_o) ** -0.5)
+    cfg = _cfg(csa.MODE_CSA, D, 64, n_h, c, 4, 64, g, r_o)
+    w = csa.make_oproj_weights(dev(w_down), dev(w_proj))
+    y = torch.empty((B, T, D), dtype=torch.int16, device=DEV)
+    ws = workspace(csa.workspace_size(cfg, csa.OP_OUTPUT_PROJ, B, T, 1))
+    csa.output_proj(cfg, dev(o), w, y, ws)
+    torch.cuda.synchronize()
+    sel = np.arange(B * T) if rows is None else np.array(rows)
+    _, y_ref = O.grouped_output_projection(o.reshape(B * T, n_h, c)[sel], w_down, w_proj, g)
+    y_h = O.bf16_bits_to_f64(host_bits(y).reshape(B * T, D)[sel])
+    check_close(y_h, O.bf16_bits_to_f64(y_ref), "y")
