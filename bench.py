@@ -15,9 +15,10 @@ Infinity Cache.  A second, profiled pass of K steps brackets every kernel launch
 
 Also measured (one line, under "also"): CSA decode at 1M context (B=4, 262144 entries, 128
 heads, k=2048), HCA dense decode at 1M context (B=16, 8192 entries, 128 heads), the 64K-token
-CSA prefill, and the 128K / 1M decodes and the prefill again with MXFP4 indexer keys (E2M1 codes
-with an E8M0 scale per 32 dims instead of E4M3 codes with a per-entry fp32 scale).  The CPU
-oracle is timed on a bounded sample of the headline workload.
+CSA prefill, the 128K / 1M decodes and the prefill again with MXFP4 indexer keys (E2M1 codes
+with an E8M0 scale per 32 dims instead of E4M3 codes with a per-entry fp32 scale), and the
+query-side and grouped output projections of the 64K-token prefill.  The CPU oracle is timed on
+a bounded sample of the headline workload.
 
 Prints ONE JSON line.
 """
@@ -239,6 +240,61 @@ def prefill_workload(name, K, W):
     return res
 
 
+def proj_workload(name, K, W):
+    """Query-side projections and grouped output projection of the 64K-token prefill at the
+    V4-Flash shape (hidden 4096, r_q 1024, 64 heads x 512, indexer 64 x 128, 8 groups of rank
+    1024): one csa_query_proj and one csa_output_proj per step."""
+    import torch
+    import long_context_sparse_15_amd as csa
+    from synth import inputs as S
+    from synth import gpu as G
+
+    w = S.WORKLOADS["csa_prefill_64k"]
+    dev = "cuda"
+    T, D, n_h, c, H_I, d_I, r_q, g, r_o = w.T, w.D, w.n_h, w.c, w.H_I, w.d_I, 1024, 8, 1024
+    gen = G._gen(w.seed + 100, dev)
+    H = G.bf16_normal(gen, (1, T, D), dev)
+    Oatt = G.bf16_normal(gen, (1, T, n_h, c), dev)
+    wq = csa.make_qproj_weights(G.bf16_normal(gen, (r_q, D), dev, std=D ** -0.5),
+                                G.bf16_normal(gen, (n_h * c, r_q), dev, std=r_q ** -0.5),
+                                torch.ones(c, device=dev),
+                                w_w=G.bf16_normal(gen, (H_I, D), dev, std=D ** -0.5),
+                                w_iuq=G.bf16_normal(gen, (H_I * d_I, r_q), dev, std=r_q ** -0.5))
+    width = n_h // g * c
+    wo = csa.make_oproj_weights(G.bf16_normal(gen, (g, r_o, width), dev, std=width ** -0.5),
+                                G.bf16_normal(gen, (D, g * r_o), dev, std=(g * r_o) ** -0.5))
+    inv = torch.from_numpy(S.rope_inv_freq(w.r, w.rope_base)).to(dev)
+    cfg = csa.make_config(csa.MODE_CSA, w.m, n_h, c, w.r, inv, top_k=w.k, idx_heads=H_I,
+                          idx_dim=d_I, hidden=D, q_rank=r_q, out_groups=g, out_rank=r_o)
+    q = torch.empty((1, T, n_h, c), dtype=torch.int16, device=dev)
+    qi = torch.empty((1, T, H_I, d_I), dtype=torch.uint8, device=dev)
+    qs = torch.empty((1, T, H_I), dtype=torch.float32, device=dev)
+    wi = torch.empty((1, T, H_I), dtype=torch.float32, device=dev)
+    y = torch.empty((1, T, D), dtype=torch.int16, device=dev)
+    ws = torch.empty(max(csa.workspace_size(cfg, csa.OP_QUERY_PROJ, 1, T, 1),
+                         csa.workspace_size(cfg, csa.OP_OUTPUT_PROJ, 1, T, 1)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        csa.query_proj(cfg, H, wq, q, ws, qi_out=qi, qi_scale_out=qs, wi_out=wi)
+        csa.output_proj(cfg, Oatt, wo, y, ws)
+
+    ms = _time_steps(step, K, W, stream)
+    prof = _profiled(step, K, W)
+    flops = 2.0 * T * (D * (r_q + H_I) + r_q * (n_h * c + H_I * d_I) + n_h * c * r_o +
+                       g * r_o * D)
+    ach = flops / (ms / 1e3) / 1e12
+    res = {"workload": name, "value": T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+           "kernels_ms_per_step": {k: v[1] / K for k, v in prof.items()},
+           "roofline": {"kernel": "all projections", "bound": "mfma", "achieved": ach,
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": ach / BF16_PEAK_TFLOPS, "traffic": None, "flops_per_step": flops}}
+    del H, Oatt, q, qi, qs, wi, y, ws, wq, wo
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, budget_s=10.0):
     """The CPU oracle on a bounded sample of the same workload: decode steps of sampled
     sequences (same shapes and recipe, numpy generator), timed on the host cores."""
@@ -282,7 +338,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode_128k")
     ap.add_argument("--extra", default="csa_decode_1m,hca_decode_1m,csa_prefill_64k,"
-                    "csa_decode_128k_mxfp4,csa_decode_1m_mxfp4,csa_prefill_64k_mxfp4",
+                    "csa_decode_128k_mxfp4,csa_decode_1m_mxfp4,csa_prefill_64k_mxfp4,"
+                    "qo_proj_64k",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
@@ -309,6 +366,8 @@ def main():
         print("[bench] extra %s" % name, file=sys.stderr, flush=True)
         if name.startswith("csa_prefill"):
             also.append(prefill_workload(name, max(2, args.steps // 10), 1))
+        elif name.startswith("qo_proj"):
+            also.append(proj_workload(name, max(2, args.steps // 10), 1))
         else:
             also.append(decode_workload(name, args.steps, args.warmup, args.rotate))
     if args.calib_copy:

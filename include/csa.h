@@ -14,7 +14,8 @@
  *  - No call allocates device memory and no call synchronizes: work is enqueued on the HIP
  *    stream passed as `stream` (a hipStream_t, NULL = the default stream) and the call returns.
  *  - Every tensor argument is a caller-owned DEVICE pointer to contiguous row-major memory,
- *    unless marked "host".  The library keeps no pointer after a call returns.
+ *    unless marked "host", 16-byte aligned (the kernels move 16-byte vectors).  The library
+ *    keeps no pointer after a call returns.
  *  - Scratch memory comes from the caller's `workspace` (device, 256-byte aligned) of
  *    `ws_bytes` bytes; csa_workspace_size() returns the bytes an operation needs.  Workspace
  *    contents on entry are irrelevant and are clobbered.

@@ -3,9 +3,11 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "../../include/csa.h"
+
 #include "kernels.h"
 
 namespace {
@@ -235,6 +237,14 @@ int run_attend(const csa_config_t* c, int B, int nq, const uint16_t* q, const cs
   const csa::MqaPlan p = csa::plan_mqa(B * nq, c->n_heads, c->head_dim, max_list);
   hipError_t e = csa::launch_mqa(a, p, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "attention launch");
+}
+
+// CSA_ERR_INVALID_ARG unless every non-NULL pointer is 16-byte aligned.
+int check_aligned(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 15)
+      return fail(CSA_ERR_INVALID_ARG, "device pointer %p is not 16-byte aligned", p);
+  return CSA_OK;
 }
 
 int check_qproj_config(const csa_config_t* c) {
@@ -477,6 +487,9 @@ int csa_query_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t
   const bool csa_mode = is_csa(cfg);
   if (csa_mode && (!w->w_w || !w->w_iuq || !qi_out || !qi_scale_out || !wi_out))
     return fail(CSA_ERR_INVALID_ARG, "CSA needs w_w, w_iuq, qi_out, qi_scale_out and wi_out");
+  if ((rc = check_aligned({H, w->w_dq, w->w_w, w->w_uq, w->w_iuq, w->gamma_q, q_out, qi_out,
+                           qi_scale_out, wi_out, workspace})))
+    return rc;
   const int BT = B * T;
   const size_t need = csa::query_proj_workspace(BT, cfg->q_rank, cfg->n_heads, cfg->head_dim,
                                                 csa_mode ? cfg->idx_heads : 0, cfg->idx_dim);
@@ -515,6 +528,7 @@ int csa_output_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_
   if (B < 1 || T < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, T=%d must be >= 1", B, T);
   if (!O || !w || !w->w_down || !w->w_proj || !y_out)
     return fail(CSA_ERR_INVALID_ARG, "O, w_down, w_proj or y_out is NULL");
+  if ((rc = check_aligned({O, w->w_down, w->w_proj, y_out, workspace}))) return rc;
   const int BT = B * T;
   const size_t need = csa::output_proj_workspace(BT, cfg->out_groups, cfg->out_rank);
   if (!workspace || ws_bytes < need)

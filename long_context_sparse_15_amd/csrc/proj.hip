@@ -10,9 +10,12 @@
 // fp32 scale per (token, head), max|x| / 448; w^I in fp32.
 //
 // Every product is the large-tile bf16 MFMA GEMM (launch_gemm_tn, fp32 accumulation).  The
-// fp32 results of the query up-projection are produced in row chunks sized to a bounded
-// workspace and finished by one pass: a wave per head reads the head's row, normalises it (or
-// takes its max for the E4M3 scale) with wave-wide reductions and stores the result.
+// query up-projection writes its bf16 result straight into q (the attention-query heads) and a
+// small bf16 buffer (the indexer-query heads); one pass then finishes them: a wave per head
+// reads the head's row, normalises it in place (or takes its max for the E4M3 scale) with
+// wave-wide reductions.  The normalisation thus reads the product rounded to bf16 (one bf16
+// rounding more than a normalisation of the fp32 product; an fp32 buffer of the product cost
+// 10.7 GB of extra traffic at 64K tokens).
 #include <cmath>
 
 #include "common.h"
@@ -33,93 +36,119 @@ int chunk_rows(int BT, size_t row_bytes) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// v summed over the wave: quad permutes, the mirrored half-row and row (DPP), then l^16 and l^32
+// (lane swaps).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));
+  return wave_sum_xor16_32(v);
 }
 
-// One workgroup (4 waves) per token row of the chunk; wave w takes "heads" w, w+4, ... of the
-// row: the first n_h are attention-query heads (c floats each: RMSNorm with gain gamma, bf16),
-// the next H_I are indexer-query heads (d_I floats each: E4M3 with max|x|/448 scale).
+template <int N>
+struct alignas(4 * N) Words {
+  uint32_t v[N];
+};
+
+// One workgroup (4 waves) per token row.  Attention-query heads (c values of q each, normalised
+// in place with gain gamma): a wave takes a head per pass, lane l the c/64 consecutive values
+// from c/64*l, loaded as one vector; each wave keeps UNR heads' loads in flight before it
+// reduces.  Indexer-query heads (d_I values of P each, E4M3 with max|x|/448 scale): d_I/8 lanes
+// per head, 8 values (16 bytes) per lane, 64/(d_I/8) heads per wave pass.
 template <int C, int DI>
 __global__ __launch_bounds__(256) void query_finish_kernel(
-    const float* __restrict__ P, int ldp, int n_h, int H_I, const float* __restrict__ gamma,
+    const uint16_t* __restrict__ P, int ldp, int n_h, int H_I, const float* __restrict__ gamma,
     float eps, uint16_t* __restrict__ q, uint8_t* __restrict__ qi, float* __restrict__ qi_scale) {
-  constexpr int PERQ = C / 64, PERI = DI / 64 > 0 ? DI / 64 : 1;
+  constexpr int V = C / 64, QW = V / 2, UNR = 4;
+  constexpr int LPH = DI / 8, HPW = 64 / LPH;
+  static_assert(C % 128 == 0 && DI % 8 == 0 && LPH <= 64, "head widths");
   const int row = blockIdx.x;
   const int l = lane_id(), wave = threadIdx.x >> 6;
-  const float* src = P + static_cast<size_t>(row) * ldp;
-  for (int hd = wave; hd < n_h + H_I; hd += 4) {
-    if (hd < n_h) {
-      float x[PERQ];
+  float g[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) g[i] = gamma[l * V + i];
+  uint16_t* qrow = q + static_cast<size_t>(row) * n_h * C + l * V;
+  for (int h0 = wave * UNR; h0 < n_h; h0 += 4 * UNR) {
+    Words<QW> w[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int hd = h0 + u < n_h ? h0 + u : n_h - 1;
+      w[u] = *reinterpret_cast<const Words<QW>*>(qrow + static_cast<size_t>(hd) * C);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float x[V];
       float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < PERQ; ++i) {
-        x[i] = src[hd * C + i * 64 + l];
-        ss += x[i] * x[i];
+      for (int j = 0; j < QW; ++j) {
+        x[2 * j] = __uint_as_float(w[u].v[j] << 16);
+        x[2 * j + 1] = __uint_as_float(w[u].v[j] & 0xffff0000u);
+        ss += x[2 * j] * x[2 * j] + x[2 * j + 1] * x[2 * j + 1];
       }
       const float inv = rsqrtf(wave_sum(ss) / C + eps);
-      uint16_t* dst = q + (static_cast<size_t>(row) * n_h + hd) * C;
+      Words<QW> o;
 #pragma unroll
-      for (int i = 0; i < PERQ; ++i) dst[i * 64 + l] = f32_to_bf16(x[i] * inv * gamma[i * 64 + l]);
-    } else {
-      const int h = hd - n_h;
-      const float* s2 = src + n_h * C + h * DI;
-      float x[PERI];
-      float am = 0.f;
-#pragma unroll
-      for (int i = 0; i < PERI; ++i) {
-        const int d = i * 64 + l;
-        x[i] = d < DI ? s2[d] : 0.f;
-        am = fmaxf(am, fabsf(x[i]));
-      }
-      am = wave_max(am);
-      const float scale = am > 0.f ? am / 448.f : 1.f;
-      uint8_t* dst = qi + (static_cast<size_t>(row) * H_I + h) * DI;
-#pragma unroll
-      for (int i = 0; i < PERI; ++i) {
-        const int d = i * 64 + l;
-        if (d < DI) dst[d] = e4m3_rne(x[i] / scale);
-      }
-      if (l == 0) qi_scale[static_cast<size_t>(row) * H_I + h] = scale;
+      for (int j = 0; j < QW; ++j)
+        o.v[j] = pack_bf16x2(x[2 * j] * inv * g[2 * j], x[2 * j + 1] * inv * g[2 * j + 1]);
+      if (h0 + u < n_h)
+        *reinterpret_cast<Words<QW>*>(qrow + static_cast<size_t>(h0 + u) * C) = o;
     }
+  }
+  const int sub = l % LPH;
+  for (int pass = wave; pass * HPW < H_I; pass += 4) {
+    const int h = pass * HPW + l / LPH;
+    if (h >= H_I) continue;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(P + static_cast<size_t>(row) * ldp + h * DI +
+                                                    sub * 8);
+    float x[8];
+    float am = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      am = fmaxf(am, fmaxf(fabsf(x[2 * j]), fabsf(x[2 * j + 1])));
+    }
+#pragma unroll
+    for (int off = LPH / 2; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+    const float scale = am > 0.f ? am / 448.f : 1.f;
+    uint32_t c[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      c[j] = static_cast<uint32_t>(e4m3_rne(x[4 * j] / scale)) |
+             (static_cast<uint32_t>(e4m3_rne(x[4 * j + 1] / scale)) << 8) |
+             (static_cast<uint32_t>(e4m3_rne(x[4 * j + 2] / scale)) << 16) |
+             (static_cast<uint32_t>(e4m3_rne(x[4 * j + 3] / scale)) << 24);
+    uint8_t* dst = qi + (static_cast<size_t>(row) * H_I + h) * DI + sub * 8;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(c[0], c[1]);
+    if (sub == 0) qi_scale[static_cast<size_t>(row) * H_I + h] = scale;
   }
 }
 
 template <int C, int DI>
-hipError_t launch_finish(const float* P, int ldp, int rows, const QueryProjArgs& a, int r0,
-                         hipStream_t s) {
+hipError_t launch_finish(const uint16_t* P, int ldp, const QueryProjArgs& a, hipStream_t s) {
   ProfScope ps("qproj_finish", s);
-  query_finish_kernel<C, DI><<<rows, 256, 0, s>>>(
-      P, ldp, a.n_h, a.qi ? a.H_I : 0, a.gamma_q, a.eps,
-      a.q + static_cast<size_t>(r0) * a.n_h * a.c,
-      a.qi ? a.qi + static_cast<size_t>(r0) * a.H_I * a.d_I : nullptr,
-      a.qi ? a.qi_scale + static_cast<size_t>(r0) * a.H_I : nullptr);
+  query_finish_kernel<C, DI><<<a.BT, 256, 0, s>>>(P, ldp, a.n_h, a.qi ? a.H_I : 0, a.gamma_q,
+                                                   a.eps, a.q, a.qi, a.qi_scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t query_proj_workspace(int BT, int r_q, int n_h, int c, int H_I, int d_I) {
-  const size_t width = static_cast<size_t>(n_h) * c + static_cast<size_t>(H_I) * d_I;
-  const int rows = chunk_rows(BT, width * sizeof(float));
+  (void)n_h;
+  (void)c;
   return align256(static_cast<size_t>(BT) * r_q * sizeof(uint16_t)) +
-         align256(static_cast<size_t>(rows) * width * sizeof(float));
+         align256(static_cast<size_t>(BT) * H_I * d_I * sizeof(uint16_t));
 }
 
 hipError_t launch_query_proj(const QueryProjArgs& a, hipStream_t s) {
   const bool idx = a.qi != nullptr;
   const int H_I = idx ? a.H_I : 0;
-  const int width = a.n_h * a.c + H_I * a.d_I;
+  const int iw = H_I * a.d_I;  // indexer-query width
   unsigned char* p = static_cast<unsigned char*>(a.ws);
   uint16_t* cq = reinterpret_cast<uint16_t*>(p);
-  float* buf = reinterpret_cast<float*>(p + align256(static_cast<size_t>(a.BT) * a.r_q * 2));
+  uint16_t* qib = reinterpret_cast<uint16_t*>(p + align256(static_cast<size_t>(a.BT) * a.r_q * 2));
   GemmArgs g;
   // c^Q = h W^DQ (bf16) and w^I = h W_w (fp32, straight into the output)
   g = GemmArgs{a.H, a.D, a.w_dq, a.D, cq, a.r_q, a.BT, a.r_q, a.D, true, "qproj_down"};
@@ -130,38 +159,29 @@ hipError_t launch_query_proj(const QueryProjArgs& a, hipStream_t s) {
     e = launch_gemm_tn(g, s);
     if (e != hipSuccess) return e;
   }
-  const int rows = chunk_rows(a.BT, static_cast<size_t>(width) * sizeof(float));
-  for (int r0 = 0; r0 < a.BT; r0 += rows) {
-    const int m = a.BT - r0 < rows ? a.BT - r0 : rows;
-    const uint16_t* A = cq + static_cast<size_t>(r0) * a.r_q;
-    g = GemmArgs{A, a.r_q, a.w_uq, a.r_q, buf, width, m, a.n_h * a.c, a.r_q, false, "qproj_up"};
+  // c^Q W^UQ into q (bf16, normalised below) and c^Q W^IUQ into the indexer-query buffer
+  g = GemmArgs{cq, a.r_q, a.w_uq, a.r_q, a.q, a.n_h * a.c, a.BT, a.n_h * a.c, a.r_q, true,
+               "qproj_up"};
+  e = launch_gemm_tn(g, s);
+  if (e != hipSuccess) return e;
+  if (idx) {
+    g = GemmArgs{cq, a.r_q, a.w_iuq, a.r_q, qib, iw, a.BT, iw, a.r_q, true, "qproj_up"};
     e = launch_gemm_tn(g, s);
     if (e != hipSuccess) return e;
-    if (idx) {
-      g = GemmArgs{A, a.r_q, a.w_iuq, a.r_q, buf + a.n_h * a.c, width, m, H_I * a.d_I, a.r_q,
-                   false, "qproj_up"};
-      e = launch_gemm_tn(g, s);
-      if (e != hipSuccess) return e;
-    }
-#define CSA_FINISH_CASE(C_, DI_)                                         \
-    if (a.c == C_ && (!idx || a.d_I == DI_)) {                           \
-      e = launch_finish<C_, DI_>(buf, width, m, a, r0, s);               \
-      if (e != hipSuccess) return e;                                     \
-      continue;                                                          \
-    }
-    CSA_FINISH_CASE(512, 128)
-    CSA_FINISH_CASE(512, 64)
-    CSA_FINISH_CASE(512, 32)
-    CSA_FINISH_CASE(256, 128)
-    CSA_FINISH_CASE(256, 64)
-    CSA_FINISH_CASE(256, 32)
-    CSA_FINISH_CASE(128, 128)
-    CSA_FINISH_CASE(128, 64)
-    CSA_FINISH_CASE(128, 32)
-#undef CSA_FINISH_CASE
-    return hipErrorInvalidValue;
   }
-  return hipSuccess;
+#define CSA_FINISH_CASE(C_, DI_) \
+  if (a.c == C_ && (!idx || a.d_I == DI_)) return launch_finish<C_, DI_>(qib, iw, a, s);
+  CSA_FINISH_CASE(512, 128)
+  CSA_FINISH_CASE(512, 64)
+  CSA_FINISH_CASE(512, 32)
+  CSA_FINISH_CASE(256, 128)
+  CSA_FINISH_CASE(256, 64)
+  CSA_FINISH_CASE(256, 32)
+  CSA_FINISH_CASE(128, 128)
+  CSA_FINISH_CASE(128, 64)
+  CSA_FINISH_CASE(128, 32)
+#undef CSA_FINISH_CASE
+  return hipErrorInvalidValue;
 }
 
 size_t output_proj_workspace(int BT, int g, int r_o) {
