@@ -111,14 +111,17 @@ def _profiled(step, K, W):
 
 def decode_workload(name, K, W, rotate):
     """One decode step per iteration of a named workload; a "_mxfp4" suffix runs the same
-    workload with MXFP4 indexer keys (the E4M3 keys are the configured default)."""
+    workload with MXFP4 indexer keys (the E4M3 keys are the configured default), a "_paged"
+    suffix with the entries, keys and scales in block pools (blocks of 128 tokens, 128/m
+    entries) placed in a random order and addressed through a block table."""
     import torch
     import long_context_sparse_15_amd as csa
     from synth import inputs as S
     from synth import gpu as G
 
-    key_fmt = "mxfp4" if name.endswith("_mxfp4") else "e4m3"
-    base = name[:-len("_mxfp4")] if key_fmt == "mxfp4" else name
+    key_fmt = "mxfp4" if "_mxfp4" in name else "e4m3"
+    paged = "_paged" in name
+    base = name.replace("_paged", "").replace("_mxfp4", "")
     w = S.WORKLOADS[base]
     dev = "cuda"
     x = G.decode_cache_inputs(w, dev, key_fmt=key_fmt)
@@ -133,8 +136,25 @@ def decode_workload(name, K, W, rotate):
                           w.r, x["inv_freq"], top_k=w.k, n_win=w.n_win, idx_heads=w.H_I,
                           idx_dim=w.d_I, softmax_scale=w.scale,
                           idx_key_format=csa.IDX_MXFP4 if key_fmt == "mxfp4" else csa.IDX_E4M3)
+    pg = {}
+    if paged:
+        be = 128 // w.m
+        n_blocks = w.B * (w.N // be)
+        gen = torch.Generator().manual_seed(w.seed)
+        table = torch.randperm(n_blocks, generator=gen).view(w.B, w.N // be).to(torch.int32)
+        table = table.to(dev)
+        rows = (table.long()[:, :, None] * be + torch.arange(be, device=dev)).reshape(-1)
+        for y in copies:
+            for k in ("entries", "ikeys", "iscale"):
+                if k in y:
+                    pool = torch.empty((n_blocks * be,) + tuple(y[k].shape[2:]), dtype=y[k].dtype,
+                                       device=dev)
+                    pool[rows] = y[k].reshape((-1,) + tuple(y[k].shape[2:]))
+                    y[k] = pool
+        pg = dict(block_table=table, block_entries=be, n_blocks=n_blocks)
     caches = [csa.make_cache(w.N, w.n_win, y["entries"], y["window"], y["n_entries"],
-                             idx_keys=y.get("ikeys"), idx_scale=y.get("iscale")) for y in copies]
+                             idx_keys=y.get("ikeys"), idx_scale=y.get("iscale"), **pg)
+              for y in copies]
     ws = torch.empty(csa.workspace_size(cfg, csa.OP_DECODE, w.B, 1, w.N), dtype=torch.uint8,
                      device=dev)
     out = torch.empty((w.B, w.n_h, w.c), dtype=torch.bfloat16, device=dev)
@@ -339,7 +359,7 @@ def main():
     ap.add_argument("--workload", default="csa_decode_128k")
     ap.add_argument("--extra", default="csa_decode_1m,hca_decode_1m,csa_prefill_64k,"
                     "csa_decode_128k_mxfp4,csa_decode_1m_mxfp4,csa_prefill_64k_mxfp4,"
-                    "qo_proj_64k",
+                    "qo_proj_64k,csa_decode_128k_paged,csa_decode_1m_paged,hca_decode_1m_paged",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")

@@ -107,7 +107,20 @@ typedef struct csa_config {
  *  tail      fp32 [B, tail_rows, tail_cols] compressor projections of the last tail_rows tokens
  *            (row u % tail_rows); only used by the compressor (csa_tail_shape gives the shape)
  *  n_entries int32 [B]                   closed entries per sequence (read; the compressor
- *                                        updates it) */
+ *                                        updates it)
+ *
+ * Block layout (the hybrid cache of Book "DeepSeek V4 模型技术大全", chapter "Attention":
+ * compressed entries in fixed-size blocks of lcm(m, 128) tokens, i.e. 128/m entries for m = 4
+ * and one entry for m' = 128; the window ring and compressor tail stay per-sequence state).
+ * block_entries = 0 selects the contiguous layout above.  block_entries > 0 (a power of two;
+ * CSA: >= 16) makes entries, idx_keys and idx_scale pools of n_blocks physical blocks of
+ * block_entries entries ([n_blocks, block_entries, ...], same per-entry widths), and puts
+ * logical entry i of sequence b in row i % block_entries of physical block
+ * block_table[b * blocks_per_seq + i / block_entries].  Requires n_max = blocks_per_seq *
+ * block_entries and n_blocks * block_entries < 2^31.  Table values outside 0..n_blocks-1 are
+ * clamped into the pool (wrong results, never an access outside it).  Sequences may map the
+ * same physical blocks (a shared prefix): readers never write entries, and csa_compress writes
+ * only blocks i >= n_entries[b]. */
 typedef struct csa_cache {
   int32_t n_max;
   int32_t win_slots;
@@ -117,6 +130,10 @@ typedef struct csa_cache {
   uint16_t* window;
   float* tail;
   int32_t* n_entries;
+  int32_t block_entries;       /* 0: contiguous; else entries per block */
+  int32_t blocks_per_seq;      /* block_table row length */
+  int32_t n_blocks;            /* physical blocks in each pool */
+  const int32_t* block_table;  /* device int32 [B, blocks_per_seq] */
 } csa_cache_t;
 
 /* Compressor parameters (device pointers).
@@ -176,10 +193,16 @@ int csa_workspace_size(const csa_config_t* cfg, int32_t op, int32_t B, int32_t n
  *
  *  H     bf16 [B, T, hidden]: T new tokens of each sequence, sequence b's at positions
  *        pos0[b] .. pos0[b]+T-1.
- *  pos0  int32 [B] device: first new position per sequence; n_entries[b] must equal
- *        floor(pos0[b]/m) and the tail ring must hold the previous call's last tokens.
- *  Effects per sequence: every block i that closes inside the call (m(i+1)-1 within the new
- *  tokens) is written to entries[b,i] (bf16, RMSNorm*gamma, RoPE at m*i) and, for CSA, to
+ *  pos0  int32 [B] device: first new position per sequence, with floor(pos0[b]/m) <=
+ *        n_entries[b] <= floor((pos0[b]+T)/m); the tail ring must hold the projections of the
+ *        tokens before pos0[b] that the first new block reads (none for a fresh sequence).
+ *        n_entries[b] > floor(pos0[b]/m) rebuilds state only: with entries 0..n_entries[b]-1
+ *        already in the cache (e.g. blocks shared with another sequence), re-running the last
+ *        max(n_win, 2m) tokens before position m*n_entries[b] refills the window ring and the
+ *        tail ring and writes no entry (prefix reuse with tail recompute).
+ *  Effects per sequence: every block i >= n_entries[b] that closes inside the call
+ *  (m(i+1)-1 within the new tokens) is written to entries[b,i] (bf16, RMSNorm*gamma, RoPE at
+ *  m*i) and, for CSA, to
  *  idx_keys/idx_scale[b,i] (E4M3 with per-entry scale max|x|/448, no norm, no RoPE);
  *  window rows of the new tokens (RMSNorm(h W_win)*gamma_win, RoPE at u); the tail ring;
  *  n_entries[b] = floor((pos0[b]+T)/m).  Requires floor((pos0[b]+T)/m) <= n_max.

@@ -37,7 +37,9 @@ class Cache(ctypes.Structure):
     _fields_ = [("n_max", ctypes.c_int32), ("win_slots", ctypes.c_int32),
                 ("entries", ctypes.c_void_p), ("idx_keys", ctypes.c_void_p),
                 ("idx_scale", ctypes.c_void_p), ("window", ctypes.c_void_p),
-                ("tail", ctypes.c_void_p), ("n_entries", ctypes.c_void_p)]
+                ("tail", ctypes.c_void_p), ("n_entries", ctypes.c_void_p),
+                ("block_entries", ctypes.c_int32), ("blocks_per_seq", ctypes.c_int32),
+                ("n_blocks", ctypes.c_int32), ("block_table", ctypes.c_void_p)]
 
 
 class QProjWeights(ctypes.Structure):
@@ -157,11 +159,18 @@ def make_config(mode, m, n_heads, head_dim, rope_dim, inv_freq, top_k=0, n_win=1
 
 
 def make_cache(n_max, win_slots, entries, window, n_entries, idx_keys=None, idx_scale=None,
-               tail=None):
+               tail=None, block_table=None, block_entries=0, n_blocks=0):
+    """Contiguous cache, or (block_table [B, blocks_per_seq] int32 given) the block layout:
+    entries / idx_keys / idx_scale are then pools of n_blocks blocks of block_entries rows and
+    n_max must be blocks_per_seq * block_entries."""
+    bps = int(block_table.shape[-1]) if block_table is not None else 0
     c = Cache(n_max, win_slots, _ptr(entries).value, _ptr(idx_keys) and _ptr(idx_keys).value,
               _ptr(idx_scale) and _ptr(idx_scale).value, _ptr(window).value,
-              _ptr(tail) and _ptr(tail).value, _ptr(n_entries).value)
-    c._keep = (entries, window, n_entries, idx_keys, idx_scale, tail)
+              _ptr(tail) and _ptr(tail).value, _ptr(n_entries).value,
+              block_entries if block_table is not None else 0, bps,
+              n_blocks if block_table is not None else 0,
+              _ptr(block_table) and _ptr(block_table).value)
+    c._keep = (entries, window, n_entries, idx_keys, idx_scale, tail, block_table)
     return c
 
 

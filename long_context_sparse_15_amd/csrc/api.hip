@@ -81,6 +81,14 @@ void tail_shape(const csa_config_t* c, int* rows, int* cols) {
   }
 }
 
+// CSA_ERR_INVALID_ARG unless every non-NULL pointer is 16-byte aligned.
+int check_aligned(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 15)
+      return fail(CSA_ERR_INVALID_ARG, "device pointer %p is not 16-byte aligned", p);
+  return CSA_OK;
+}
+
 int check_cache(const csa_config_t* c, const csa_cache_t* k, bool need_keys, bool need_tail) {
   if (!k) return fail(CSA_ERR_INVALID_ARG, "cache is NULL");
   if (k->n_max < 1) return fail(CSA_ERR_INVALID_ARG, "cache n_max=%d < 1", k->n_max);
@@ -91,7 +99,36 @@ int check_cache(const csa_config_t* c, const csa_cache_t* k, bool need_keys, boo
   if (need_keys && (!k->idx_keys || !k->idx_scale))
     return fail(CSA_ERR_INVALID_ARG, "cache idx_keys/idx_scale is NULL");
   if (need_tail && !k->tail) return fail(CSA_ERR_INVALID_ARG, "cache tail is NULL");
+  if (k->block_entries != 0) {
+    const int be = k->block_entries;
+    if (be < 0 || (be & (be - 1)))
+      return fail(CSA_ERR_INVALID_ARG, "block_entries=%d must be 0 or a power of two", be);
+    if (is_csa(c) && be < 16)
+      return fail(CSA_ERR_INVALID_ARG, "CSA caches need block_entries >= 16 (got %d)", be);
+    if (!k->block_table || k->blocks_per_seq < 1 || k->n_blocks < 1)
+      return fail(CSA_ERR_INVALID_ARG, "paged cache needs block_table, blocks_per_seq >= 1 "
+                  "and n_blocks >= 1");
+    if (static_cast<long long>(k->blocks_per_seq) * be != k->n_max)
+      return fail(CSA_ERR_INVALID_ARG, "n_max=%d != blocks_per_seq*block_entries=%lld",
+                  k->n_max, static_cast<long long>(k->blocks_per_seq) * be);
+    if (static_cast<long long>(k->n_blocks) * be >= (1LL << 31))
+      return fail(CSA_ERR_INVALID_ARG, "pool of %d blocks x %d entries exceeds 2^31 rows",
+                  k->n_blocks, be);
+  }
   return CSA_OK;
+}
+
+csa::PageMap page_map(const csa_cache_t* k) {
+  csa::PageMap pm;
+  if (k->block_entries > 0) {
+    pm.table = k->block_table;
+    pm.stride = k->blocks_per_seq;
+    int sh = 0;
+    while ((1 << sh) < k->block_entries) ++sh;
+    pm.shift = sh;
+    pm.n_blocks = k->n_blocks;
+  }
+  return pm;
 }
 
 int check_weights(const csa_config_t* c, const csa_weights_t* w) {
@@ -149,6 +186,7 @@ void fill_index_args(csa::IndexArgs& a, const csa_config_t* c, int B, int nq, co
   a.m = c->m;
   a.k = c->top_k;
   a.key_fmt = c->idx_key_format;
+  a.pages = page_map(k);
   a.idx_out = idx_out;
   a.score_out = score_out;
   csa::index_topk_layout(a, ws, B * nq);
@@ -175,6 +213,7 @@ void fill_mqa_args(csa::MqaArgs& a, const csa_config_t* c, int B, int nq, const 
   a.n_win = c->n_win;
   a.win_slots = k->win_slots;
   a.n_max = k->n_max;
+  a.pages = page_map(k);
   a.scale = c->softmax_scale;
   a.out = out;
   a.lse_out = lse_out;
@@ -214,6 +253,7 @@ int run_compress(const csa_config_t* c, int B, int T, const uint16_t* H, const i
   a.window = k->window;
   a.tail = k->tail;
   a.n_entries = k->n_entries;
+  a.pages = page_map(k);
   a.proj = static_cast<float*>(ws);
   hipError_t e = csa::launch_compress(a, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "compress launch");
@@ -237,14 +277,6 @@ int run_attend(const csa_config_t* c, int B, int nq, const uint16_t* q, const cs
   const csa::MqaPlan p = csa::plan_mqa(B * nq, c->n_heads, c->head_dim, max_list);
   hipError_t e = csa::launch_mqa(a, p, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "attention launch");
-}
-
-// CSA_ERR_INVALID_ARG unless every non-NULL pointer is 16-byte aligned.
-int check_aligned(std::initializer_list<const void*> ptrs) {
-  for (const void* p : ptrs)
-    if (reinterpret_cast<uintptr_t>(p) & 15)
-      return fail(CSA_ERR_INVALID_ARG, "device pointer %p is not 16-byte aligned", p);
-  return CSA_OK;
 }
 
 int check_qproj_config(const csa_config_t* c) {
@@ -273,7 +305,7 @@ int check_oproj_config(const csa_config_t* c) {
 
 extern "C" {
 
-int csa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int csa_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
 int csa_profile_start(void) {
   csa::profile_start();

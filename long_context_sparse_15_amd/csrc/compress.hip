@@ -308,6 +308,8 @@ struct PoolParams {
   uint16_t* entries;
   uint8_t* ikeys;
   float* iscale;
+  PageMap pages;               // layout of entries, ikeys and iscale
+  const int32_t* n_entries;    // [B] entries already in the cache: blocks below are kept
 };
 
 __device__ __forceinline__ const float* proj_row(const PoolParams& p, int b, int p0, int u) {
@@ -350,6 +352,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   const int i = p0 / p.m + blockIdx.x % p.nblk;
   if (i > (p0 + p.T) / p.m - 1) return;  // block does not close in this call
   if (i >= p.n_max) return;               // never write past the cache
+  if (i < p.n_entries[b]) return;         // already in the cache (rebuilding the state only)
+  const size_t erow = entry_row(p.pages, p.n_max, b, i);
   const int tid = threadIdx.x;
   const int c = p.c;
   const bool csa = p.mode == 0;
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   }
   const float tot = block_sum(ss, s_red);  // includes the barrier that publishes s_val
   const float inv_rms = rsqrtf(tot / c + p.eps);
-  uint16_t* dst = p.entries + (static_cast<size_t>(b) * p.n_max + i) * c;
+  uint16_t* dst = p.entries + erow * c;
   const int pos = p.m * i;
   for (int pp = tid; pp < c / 2; pp += 256) {
     const int d = 2 * pp;
@@ -410,17 +414,17 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     const int se = am > 0.f ? min(max(ex - 3, -127), 127) : -127;
     const uint32_t code = e2m1_rne(ldexpf(v, -se));
     const uint32_t hi = static_cast<uint32_t>(__shfl_down(static_cast<int>(code), 1, 64));
-    uint8_t* kd = p.ikeys + (static_cast<size_t>(b) * p.n_max + i) * (dI / 2);
+    uint8_t* kd = p.ikeys + erow * (dI / 2);
     if (has && (tid & 1) == 0) kd[tid >> 1] = static_cast<uint8_t>(code | (hi << 4));
-    uint8_t* sd = reinterpret_cast<uint8_t*>(p.iscale) + (static_cast<size_t>(b) * p.n_max + i) * 4;
+    uint8_t* sd = reinterpret_cast<uint8_t*>(p.iscale) + erow * 4;
     if (tid < 128 && (tid & 31) == 0) sd[tid >> 5] = static_cast<uint8_t>(has ? se + 127 : 127);
     return;
   }
   amax = block_max(amax, s_red);
   const float scale = amax > 0.f ? amax / 448.f : 1.f;
-  uint8_t* kd = p.ikeys + (static_cast<size_t>(b) * p.n_max + i) * dI;
+  uint8_t* kd = p.ikeys + erow * dI;
   for (int ch = tid; ch < dI; ch += 256) kd[ch] = e4m3_rne(s_val[ch] / scale);
-  if (tid == 0) p.iscale[static_cast<size_t>(b) * p.n_max + i] = scale;
+  if (tid == 0) p.iscale[erow] = scale;
 }
 
 // Window KV of every new token: RMSNorm(h_u W_win) * gamma_win, RoPE at u.
@@ -535,6 +539,8 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   p.ikeys = a.ikeys;
   p.iscale = a.iscale;
   p.key_fmt = a.key_fmt;
+  p.pages = a.pages;
+  p.n_entries = a.n_entries;
   {
     ProfScope ps("compress_pool", s);
     pool_kernel<<<a.B * p.nblk, 256, 0, s>>>(p);

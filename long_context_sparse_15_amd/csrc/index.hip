@@ -43,13 +43,15 @@ __device__ __forceinline__ int visible(const int32_t* n_entries, const int32_t* 
 // the query as E4M3 and the keys as FP4 with each lane's block scale; its FP4 operand gives
 // lane group g the 32 dims 32g..32g+31 (16 contiguous bytes of the packed key), while its FP8
 // operand gives lane group g dims 16g..16g+15 and 64+16g..64+16g+15 (both checked on the GPU).
-template <int DI, int HT, int TPW, bool MX = false>
+// PAGED: keys and scales live in a block pool (blocks of >= 16 entries, so a 16-entry tile lies
+// in one block); each tile's block comes from one scalar-cache load of the block table.
+template <int DI, int HT, int TPW, bool MX = false, bool PAGED = false>
 __global__ __launch_bounds__(256) void index_score_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ wi, const uint8_t* __restrict__ keys,
     const float* __restrict__ kscale, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int n_max, int H_I, int m, int chunk,
-    float* __restrict__ scores, int sstride, int nchunks) {
+    float* __restrict__ scores, int sstride, int nchunks, PageMap pm) {
   constexpr int KB = DI / 4;   // key bytes per lane (its lane group's K slice)
   constexpr int KK = DI / 32;  // 8-byte MFMA steps per slice
 
@@ -95,8 +97,9 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     }
   }
 
-  const uint8_t* kbase = keys + static_cast<size_t>(b) * n_max * KROW + (kWide ? 0 : g * KB);
-  const float* sbase = kscale + static_cast<size_t>(b) * n_max;
+  const size_t seq0 = PAGED ? 0 : static_cast<size_t>(b) * n_max;  // row of entry 0
+  const uint8_t* kbase = keys + seq0 * KROW + (kWide ? 0 : g * KB);
+  const float* sbase = kscale + seq0;
   const uint32_t* swbase = reinterpret_cast<const uint32_t*>(sbase);  // MXFP4 scale bytes
   float* srow = scores + static_cast<size_t>(row) * sstride;
 
@@ -112,7 +115,12 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     uint32_t sw;
   };
   auto load = [&](int t, KeyTile& kt, int emax) {
-    const int e = min(tile_entry(t), emax);
+    const int el = min(tile_entry(t), emax);
+    size_t e = el;
+    if constexpr (PAGED) {  // the tile's entries (clamped ones included) share one block
+      const int tb = min(e0 + (wave + 4 * t) * 16, emax & ~15);
+      e = block_base_uniform(pm, b, tb >> pm.shift) + (el & ((1 << pm.shift) - 1));
+    }
     if constexpr (MX) {
       const u32x4* src = reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(e) * KROW);
       const u32x4 v = g < NBLK ? CSA_STREAM_LOAD(src + g) : u32x4{0, 0, 0, 0};
@@ -206,13 +214,15 @@ __device__ __forceinline__ int qswz(int q) { return (q >> 1) & 7; }
 // MX = true: MXFP4 keys as the FP4 A operand (lane group g: dims 32g..32g+31, the lane's block
 // scale); the query codes then go in the FP8 operand's order (lane group g: dims 16g..16g+15 and
 // 64+16g..64+16g+15, i.e. 16-byte chunks g and 4+g of the query row).
-template <bool MX>
+// PAGED: keys and scales in a block pool (blocks of >= 16 entries); each 16-entry block's pool
+// block comes from a scalar-cache load of the block table.
+template <bool MX, bool PAGED = false>
 __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ wi, const uint8_t* __restrict__ keys,
     const float* __restrict__ kscale, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int n_max, int H_I, int m, int qtiles,
-    float* __restrict__ scores, int sstride) {
+    float* __restrict__ scores, int sstride, PageMap pm) {
   constexpr int DI = kGemmDI;
   constexpr int KROW = MX ? DI / 2 : DI;  // key bytes per entry
   extern __shared__ __align__(16) unsigned char smem[];
@@ -248,8 +258,9 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
   const int ngroups = (nv_max + 63) / 64;
   if (wave >= ngroups) return;
 
-  const uint8_t* kb = keys + static_cast<size_t>(b) * n_max * KROW + g * (MX ? 16 : 32);
-  const float* sb = kscale + static_cast<size_t>(b) * n_max;
+  const size_t seq0 = PAGED ? 0 : static_cast<size_t>(b) * n_max;  // row of entry 0
+  const uint8_t* kb = keys + seq0 * KROW + g * (MX ? 16 : 32);
+  const float* sb = kscale + seq0;
   const uint32_t* swb = reinterpret_cast<const uint32_t*>(sb);  // MXFP4 scale bytes
   float* srow = scores + static_cast<size_t>(b * nq + t0 + c16) * sstride;
   const bool row_ok = t0 + c16 < nq;
@@ -258,7 +269,17 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
   auto load = [&](int G, i32x8 (&a)[4], f32x4 (&ks)[4], int (&sa)[4]) {
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      const int e = min(G * 64 + blk * 16 + c16, nv_max - 1);
+      // entry of this lane and pool row of entry 0 of its 16-entry block (the block's clamped
+      // entries, scale loads included, stay in the block holding nv_max - 1)
+      const int el = min(G * 64 + blk * 16 + c16, nv_max - 1);
+      long long r0 = 0;
+      int e = el;
+      if constexpr (PAGED) {
+        const int tb = min(G * 64 + blk * 16, (nv_max - 1) & ~15);
+        r0 = static_cast<long long>(block_base_uniform(pm, b, tb >> pm.shift)) +
+             (tb & ((1 << pm.shift) - 1)) - tb;
+        e = static_cast<int>(r0 + el);
+      }
       if constexpr (MX) {  // 16 bytes of codes and this lane's block scale; no entry scale
         const u32x4 v = *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(e) * KROW);
         a[blk] = i32x8{static_cast<int>(v[0]), static_cast<int>(v[1]), static_cast<int>(v[2]),
@@ -274,7 +295,8 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
                      static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
                      static_cast<int>(hi[2]), static_cast<int>(hi[3])};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ks[blk][i] = sb[min(G * 64 + blk * 16 + 4 * g + i, nv_max - 1)];
+      for (int i = 0; i < 4; ++i)
+        ks[blk][i] = sb[r0 + min(G * 64 + blk * 16 + 4 * g + i, nv_max - 1)];
     }
   };
   const uint8_t* qb = s_q + c16 * DI;
@@ -1140,18 +1162,28 @@ void index_topk_layout(IndexArgs& a, void* ws, int rows) {
 constexpr int kScoreTPW = CSA_SCORE_TPW;       // tiles of 16 entries per wave
 constexpr int kScoreChunk = 4 * kScoreTPW * 16;  // entries per workgroup
 
+template <int DI, int HT, bool MX, bool PAGED>
+static void launch_scores_k(const IndexArgs& a, int chunk, int nchunks, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(nchunks) * static_cast<unsigned>(a.B * a.nq);
+  index_score_kernel<DI, HT, kScoreTPW, MX, PAGED><<<grid, 256, 0, s>>>(
+      a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
+      chunk, a.scores, a.sstride, nchunks, a.pages);
+}
 template <int DI, int HT>
 static void launch_scores_t(const IndexArgs& a, int chunk, int nchunks, hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>(nchunks) * static_cast<unsigned>(a.B * a.nq);
   ProfScope ps("index_score", s);
-  if (a.key_fmt == 1)
-    index_score_kernel<DI, HT, kScoreTPW, true><<<grid, 256, 0, s>>>(
-        a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
-        chunk, a.scores, a.sstride, nchunks);
-  else
-    index_score_kernel<DI, HT, kScoreTPW><<<grid, 256, 0, s>>>(
-        a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
-        chunk, a.scores, a.sstride, nchunks);
+  const bool paged = a.pages.table != nullptr;
+  if (a.key_fmt == 1) {
+    if (paged)
+      launch_scores_k<DI, HT, true, true>(a, chunk, nchunks, s);
+    else
+      launch_scores_k<DI, HT, true, false>(a, chunk, nchunks, s);
+  } else {
+    if (paged)
+      launch_scores_k<DI, HT, false, true>(a, chunk, nchunks, s);
+    else
+      launch_scores_k<DI, HT, false, false>(a, chunk, nchunks, s);
+  }
 }
 
 static hipError_t launch_scores(const IndexArgs& a, int chunk, hipStream_t s) {
@@ -1202,26 +1234,31 @@ static bool use_gemm_scores(const IndexArgs& a) {
   return a.nq >= kGemmQ && a.d_I == kGemmDI && a.H_I <= kGemmH;
 }
 
-template <bool MX>
+template <bool MX, bool PAGED>
 static hipError_t launch_gemm_scores_t(const IndexArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(index_gemm_kernel<MX>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(kGemmLds));
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(index_gemm_kernel<MX, PAGED>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemmLds));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int qtiles = (a.nq + kGemmQ - 1) / kGemmQ;
   ProfScope ps("index_score", s);
-  index_gemm_kernel<MX><<<static_cast<unsigned>(a.B) * qtiles, kGemmThreads, kGemmLds, s>>>(
-      a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
-      qtiles, a.scores, a.sstride);
+  index_gemm_kernel<MX, PAGED>
+      <<<static_cast<unsigned>(a.B) * qtiles, kGemmThreads, kGemmLds, s>>>(
+          a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I,
+          a.m, qtiles, a.scores, a.sstride, a.pages);
   return hipGetLastError();
 }
 
 static hipError_t launch_gemm_scores(const IndexArgs& a, hipStream_t s) {
-  return a.key_fmt == 1 ? launch_gemm_scores_t<true>(a, s) : launch_gemm_scores_t<false>(a, s);
+  if (a.pages.table)
+    return a.key_fmt == 1 ? launch_gemm_scores_t<true, true>(a, s)
+                          : launch_gemm_scores_t<false, true>(a, s);
+  return a.key_fmt == 1 ? launch_gemm_scores_t<true, false>(a, s)
+                        : launch_gemm_scores_t<false, false>(a, s);
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {

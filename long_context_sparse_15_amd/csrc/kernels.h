@@ -13,6 +13,35 @@ constexpr int kMaxTopK = 4096;
 constexpr int kRowTopkMaxN = 16384; // row select with 256 threads holds this many keys in LDS
 constexpr int kRowTopkBigN = 32768; // row select with 1024 threads holds this many keys
 
+// ---------------------------------------------------------------- cache layout
+// Where the per-sequence entry arrays (compressed entries, indexer keys, key scales) keep
+// logical entry e of sequence b.  table == nullptr: contiguous, row b * n_max + e.  Otherwise
+// the arrays are pools of n_blocks physical blocks of 2^shift entries each, and e lives in row
+// e & (2^shift - 1) of block table[b * stride + (e >> shift)] (clamped into the pool, so a bad
+// table entry gives wrong values, never an access outside the pool).  Callers keep e < n_max.
+struct PageMap {
+  const int32_t* table = nullptr;
+  int stride = 0;    // table entries per sequence
+  int shift = 0;     // log2(entries per block)
+  int n_blocks = 0;  // physical blocks in the pools
+};
+__device__ __forceinline__ size_t entry_row(const PageMap& pm, int n_max, int b, int e) {
+  if (!pm.table) return static_cast<size_t>(b) * n_max + e;
+  int blk = pm.table[static_cast<size_t>(b) * pm.stride + (e >> pm.shift)];
+  blk = blk < 0 ? 0 : (blk >= pm.n_blocks ? pm.n_blocks - 1 : blk);
+  return (static_cast<size_t>(blk) << pm.shift) + (e & ((1 << pm.shift) - 1));
+}
+// First row of the physical block of logical block j of sequence b, for wave-uniform b and j:
+// one scalar-cache load (counted apart from the vector loads, so waiting for it never waits
+// for key loads in flight).
+__device__ __forceinline__ size_t block_base_uniform(const PageMap& pm, int b, int j) {
+  const int i = __builtin_amdgcn_readfirstlane(b * pm.stride + j);
+  typedef const __attribute__((address_space(4))) int32_t* ctab;
+  int blk = reinterpret_cast<ctab>(reinterpret_cast<uintptr_t>(pm.table))[i];
+  blk = blk < 0 ? 0 : (blk >= pm.n_blocks ? pm.n_blocks - 1 : blk);
+  return static_cast<size_t>(blk) << pm.shift;
+}
+
 // ---------------------------------------------------------------- indexer + top-k
 struct IndexArgs {
   const uint8_t* qi;      // [rows, H_I, d_I]
@@ -24,6 +53,7 @@ struct IndexArgs {
   const int32_t* pos;     // [rows] or nullptr (t = query index within its sequence)
   int B, nq, n_max, H_I, d_I, m, k;
   int key_fmt;            // 0 e4m3 + fp32 scale, 1 MXFP4
+  PageMap pages;          // layout of keys and kscale (paged: blocks of >= 16 entries)
   float* scores;          // workspace [rows, sstride]
   int sstride;
   uint32_t* counters;     // workspace [rows, chunks, 2]: candidates and threshold of each chunk
@@ -48,6 +78,7 @@ struct MqaArgs {
   const float* sink;        // [n_heads]
   const float* inv_freq;    // [r/2]
   int B, nq, n_heads, c, r, k, m, n_win, win_slots, n_max;
+  PageMap pages;            // layout of entries
   float scale;
   uint16_t* out;            // [rows, n_heads, c]
   float* lse_out;           // [rows, n_heads] or nullptr
@@ -70,6 +101,7 @@ struct CompressArgs {
   int mode;                 // 0 CSA, 1 HCA
   int B, T, D, c, d_I, m, r, n_cols, tail_rows, tail_cols, win_slots, n_max;
   int key_fmt;              // indexer keys: 0 e4m3 + fp32 scale, 1 MXFP4
+  PageMap pages;            // layout of entries, ikeys and iscale
   const uint16_t* H;        // [B, T, D]
   const int32_t* pos0;      // [B] or nullptr (all 0)
   const uint16_t* W;        // [n_cols, D]

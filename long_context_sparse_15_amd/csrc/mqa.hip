@@ -22,6 +22,7 @@
 // spans per query each workgroup writes (max, sum, unnormalised O) and a combine kernel merges
 // them in a fixed order, adds the sink and normalises; with one span the same epilogue runs in
 // place.  Spans are fixed by the plan, not by timing, so results are run-to-run deterministic.
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -40,6 +41,7 @@ struct MqaParams {
   const float* sink;
   const float* inv_freq;
   int nq, n_heads, r, k, m, n_win, win_slots, n_max;
+  PageMap pages;  // entries in a block pool (PAGED kernels)
   float scale_log2;
   int split_rows, n_splits, head_groups, n_work;
   float* part;  // span partials, unnormalised O in the MFMA lane order (see mqa_kernel)
@@ -125,7 +127,10 @@ struct MqaShape {
   static constexpr size_t lds_fixed() { return lds_freq() + (C / 2) * sizeof(float); }
 };
 
-template <int C, int HP>
+// PAGED: entries live in a block pool; the span's entry list (selected indices, or the visible
+// range for the dense case) is translated to pool rows once, into LDS, and those rows are
+// gathered (-1: masked).
+template <int C, int HP, bool PAGED = false>
 __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p) {
   using SH = MqaShape<C, HP>;
   constexpr int DS = SH::DS, NW = SH::NW, NT = SH::NT, CS = SH::CS, KK = SH::KK, DT = SH::DT;
@@ -178,6 +183,16 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
   const int head = (hg * HP + hp) * 32 + n32;
   const bool head_ok = head < p.n_heads;
   const int dbase = slice * CS;
+  // pool row of logical entry e (-1 if e is not a closed entry)
+  auto xlate = [&](int e) {
+    return (e >= 0 && e < n_ent) ? static_cast<int>(entry_row(p.pages, p.n_max, b, e)) : -1;
+  };
+  if constexpr (PAGED) {
+    if (l < 32) {
+      pre0 = xlate(p.idx ? pre0 : j0 + l);
+      pre1 = xlate(p.idx ? pre1 : j0 + 32 + l);
+    }
+  }
 
   // Row pointers of the tile starting at list row jt, computed by lanes 0..31 (one row each).
   // Rows that are masked (past the span, an index outside the visible entries) point at the
@@ -191,9 +206,14 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
     bool ok = false;
     if (l < 32 && j < j1) {
       if (j < n_sel) {
-        const int e = p.idx ? (pre >= -1 ? pre : s_idx[j - j0]) : j;
-        ok = e >= 0 && e < n_ent;
-        if (ok) pr = p.entries + (static_cast<size_t>(b) * p.n_max + e) * C;
+        const int e = (p.idx || PAGED) ? (pre >= -1 ? pre : s_idx[j - j0]) : j;
+        if constexpr (PAGED) {
+          ok = e >= 0;
+          if (ok) pr = p.entries + static_cast<size_t>(e) * C;
+        } else {
+          ok = e >= 0 && e < n_ent;
+          if (ok) pr = p.entries + (static_cast<size_t>(b) * p.n_max + e) * C;
+        }
       } else {
         const int u = wlo + (j - n_sel);
         ok = true;
@@ -256,7 +276,7 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
   }
   const float sink_v = (p.sink && head_ok) ? p.sink[head] : 0.f;
   const float freq_v = tid < (p.r >> 1) ? p.inv_freq[tid] : 0.f;  // r/2 <= C/2 <= NT
-  if (p.idx) {
+  if (p.idx || PAGED) {
     constexpr int IPT = 8;  // indices per thread and pass, all loaded before any is stored
     const int e1 = min(j1, n_sel);
     for (int base = j0; base < e1; base += NT * IPT) {
@@ -264,7 +284,11 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
 #pragma unroll
       for (int i = 0; i < IPT; ++i) {
         const int j = base + tid + i * NT;
-        v[i] = j < e1 ? p.idx[static_cast<size_t>(row) * p.k + j] : 0;
+        v[i] = j < e1 ? (p.idx ? p.idx[static_cast<size_t>(row) * p.k + j] : j) : 0;
+      }
+      if constexpr (PAGED) {
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) v[i] = xlate(v[i]);
       }
 #pragma unroll
       for (int i = 0; i < IPT; ++i) {
@@ -553,7 +577,8 @@ __device__ __forceinline__ float sum_over_xor8_16_32(float x) {
   return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
 
-template <int C, bool SPARSE>
+// PAGED: as mqa_kernel's, the span's entries are translated to pool rows in the prologue.
+template <int C, bool SPARSE, bool PAGED = false>
 __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaParams p) {
   using SH = MqaWideShape<C>;
   constexpr int HP = SH::HP, DS = SH::DS, NW = SH::NW, NT = SH::NT, CS = SH::CS, KK = SH::KK,
@@ -570,7 +595,8 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   float* SA = reinterpret_cast<float*>(smem + SH::off_sa);
   float2* SL = reinterpret_cast<float2*>(smem + SH::off_sl);
   float2* s_cs = reinterpret_cast<float2*>(smem + SH::off_cs);  // cos, sin of pair i at t
-  int* s_idx = reinterpret_cast<int*>(smem + SH::lds_fixed());  // [split_rows] (sparse)
+  int* s_idx = reinterpret_cast<int*>(smem + SH::lds_fixed());  // [split_rows] (LIST)
+  constexpr bool LIST = SPARSE || PAGED;  // rows come from the span's list in s_idx
 
   const int tid = threadIdx.x;
   const int l = lane_id();
@@ -629,13 +655,16 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   // Masked rows (past the span, an index outside the visible entries) read the window row of t.
   // Branch-free: the index is always read (clamped into the span's index list) and both
   // candidate pointers are formed, then selected.
-  const uint16_t* const ent_base = p.entries + static_cast<size_t>(b) * p.n_max * C;
+  const uint16_t* const ent_base =
+      PAGED ? p.entries : p.entries + static_cast<size_t>(b) * p.n_max * C;
   const uint16_t* const win_base = p.window + static_cast<size_t>(b) * p.win_slots * C;
   const uint16_t* const safe_row = win_base + static_cast<size_t>(t % p.win_slots) * C;
+  // PAGED lists hold pool rows, already checked against the visible entries (-1: masked)
+  const int e_lim = PAGED ? 0x7fffffff : n_ent;
   auto resolve_e = [&](int j, int e, const uint16_t*& ptr, uint32_t& mask) {
     const bool in_span = l < 32 && j < j1;
     const bool sel = j < n_sel;
-    const bool ok_e = e >= 0 && e < n_ent;
+    const bool ok_e = e >= 0 && e < e_lim;
     const int u = max(wlo + (j - n_sel), 0);
     const uint16_t* pe = ent_base + static_cast<size_t>(ok_e ? e : 0) * C;
     const uint16_t* pw = win_base + static_cast<size_t>(u % p.win_slots) * C;
@@ -646,7 +675,7 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   auto resolve = [&](int jt, const uint16_t*& ptr, uint32_t& mask) {
     const int j = jt + l;
     int e = j;
-    if constexpr (SPARSE) e = s_idx[min(max(j - j0, 0), p.split_rows - 1)];
+    if constexpr (LIST) e = s_idx[min(max(j - j0, 0), p.split_rows - 1)];
     resolve_e(j, e, ptr, mask);
   };
   // wave `wave` loads rows wave, wave+8, wave+16, wave+24 of the tile, 16 bytes per lane
@@ -668,21 +697,32 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   // (an empty span gathers masked rows, the window row of t, and never uses them)
   u32x4 stage0[LOADS], stage1[LOADS];
   uint32_t mq0 = 0, mq1 = 0, mq2 = 0, mq3 = 0;  // valid masks of tiles i .. i+3
+  // pool row of logical entry e (-1 if e is not a closed entry)
+  auto xlate = [&](int e) {
+    return (e >= 0 && e < n_ent) ? static_cast<int>(entry_row(p.pages, p.n_max, b, e)) : -1;
+  };
   {
     const uint16_t* p0;
     const uint16_t* p1;
-    resolve_e(j0 + l, SPARSE ? pre0 : j0 + l, p0, mq0);
-    resolve_e(j0 + 32 + l, SPARSE ? pre1 : j0 + 32 + l, p1, mq1);
+    int f0 = SPARSE ? pre0 : j0 + l, f1 = SPARSE ? pre1 : j0 + 32 + l;
+    if constexpr (PAGED) {
+      f0 = xlate(f0);
+      f1 = xlate(f1);
+    }
+    resolve_e(j0 + l, f0, p0, mq0);
+    resolve_e(j0 + 32 + l, f1, p1, mq1);
     gload(p0, stage0);
     gload(p1, stage1);
   }
 
-  if constexpr (SPARSE) {
+  if constexpr (LIST) {
     const int e1 = min(j1, n_sel);
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int j = j0 + i * NT + tid;
-      if (j < e1) s_idx[j - j0] = iv[i];
+      int v = SPARSE ? iv[i] : j;
+      if constexpr (PAGED) v = j < e1 ? xlate(v) : -1;
+      if (j < e1) s_idx[j - j0] = v;
     }
   }
   if (tid < (p.r >> 1)) {
@@ -1076,10 +1116,12 @@ MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list) {
   double best = 1e30;
   pl.split_rows = round_up(list, 32);
   pl.n_splits = 1;
+  pl.split_rows = std::min(pl.split_rows, kMaxTopK);  // a span's list fits its LDS slots
+  pl.n_splits = (list + pl.split_rows - 1) / pl.split_rows;
   for (int s = 1; s <= 64; ++s) {
     const int sr = round_up((list + s - 1) / s, 32);
     const int ns = (list + sr - 1) / sr;
-    if (ns != s) continue;
+    if (ns != s || sr > kMaxTopK) continue;
     // tile counts are padded: even for the eight-wave kernel (c = 512), odd otherwise
     const int tiles = c == 512 ? ((sr + 63) / 64) * 2 : ((sr / 32) | 1);
     const double rounds = std::ceil(base * ns / slots);
@@ -1103,22 +1145,22 @@ size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c) {
   return (o + ml) * sizeof(float);
 }
 
-template <int C, class SH, bool WIDE>
+template <int C, class SH, bool WIDE, bool PAGED>
 static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
-  const size_t lds =
-      SH::lds_fixed() + (prm.idx ? static_cast<size_t>(prm.split_rows) * sizeof(int) : 0);
+  const size_t lds = SH::lds_fixed() + ((prm.idx || PAGED)
+                                            ? static_cast<size_t>(prm.split_rows) * sizeof(int)
+                                            : 0);
   static size_t attr = 0;
   if (attr < lds) {
-    const void* kfn;
     hipError_t e;
     if constexpr (WIDE) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_wide_kernel<C, true>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_wide_kernel<C, true, PAGED>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_wide_kernel<C, false>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_wide_kernel<C, false, PAGED>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     } else {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_kernel<C, SH::HP>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_kernel<C, SH::HP, PAGED>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     }
     if (e != hipSuccess) return e;
@@ -1130,10 +1172,10 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   {
     ProfScope ps(prm.idx ? "mqa_sparse" : "mqa_dense", s);
     if constexpr (WIDE) {
-      if (prm.idx) mqa_wide_kernel<C, true><<<grid, SH::NT, lds, s>>>(q);
-      else mqa_wide_kernel<C, false><<<grid, SH::NT, lds, s>>>(q);
+      if (prm.idx) mqa_wide_kernel<C, true, PAGED><<<grid, SH::NT, lds, s>>>(q);
+      else mqa_wide_kernel<C, false, PAGED><<<grid, SH::NT, lds, s>>>(q);
     }
-    else mqa_kernel<C, SH::HP><<<grid, SH::NT, lds, s>>>(q);
+    else mqa_kernel<C, SH::HP, PAGED><<<grid, SH::NT, lds, s>>>(q);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || prm.n_splits == 1) return e;
@@ -1146,8 +1188,14 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
 template <int C>
 static hipError_t launch_c(const MqaParams& prm, const MqaPlan& pl, int rows, hipStream_t s) {
   if (pl.head_pairs != 2) return hipErrorInvalidValue;
-  if constexpr (C == 512) return launch_t<C, MqaWideShape<C>, true>(prm, rows, s);
-  else return launch_t<C, MqaShape<C, 2>, false>(prm, rows, s);
+  const bool paged = prm.pages.table != nullptr;
+  if constexpr (C == 512) {
+    return paged ? launch_t<C, MqaWideShape<C>, true, true>(prm, rows, s)
+                 : launch_t<C, MqaWideShape<C>, true, false>(prm, rows, s);
+  } else {
+    return paged ? launch_t<C, MqaShape<C, 2>, false, true>(prm, rows, s)
+                 : launch_t<C, MqaShape<C, 2>, false, false>(prm, rows, s);
+  }
 }
 
 hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& pl, hipStream_t s) {
@@ -1168,6 +1216,7 @@ hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& pl, hipStream_t s) {
   p.n_win = a.n_win;
   p.win_slots = a.win_slots;
   p.n_max = a.n_max;
+  p.pages = a.pages;
   p.scale_log2 = a.scale * kLog2e;
   p.split_rows = pl.split_rows;
   p.n_splits = pl.n_splits;

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_helpers(L):
-    assert csa.version() == 10000
+    assert csa.version() == 10100
     c = _cfg()
     assert csa.weight_cols(c) == 5 * 512 + 4 * 128
     assert csa.tail_shape(c) == (8, 4 * 512 + 4 * 128)
@@ -113,3 +113,23 @@ def test_projection_configs_are_checked(L):
         with pytest.raises(csa.CsaError):
             csa.workspace_size(_cfg(**dict(dict(hidden=4096, out_groups=8, out_rank=1024), **bad)),
                                csa.OP_OUTPUT_PROJ, 1, 16, 1)
+
+
+@pytest.mark.parametrize("mode,be,bps,nb,n_max,msg", [
+    (csa.MODE_CSA, 24, 4, 8, 96, "power of two"),
+    (csa.MODE_CSA, 8, 4, 8, 32, ">= 16"),
+    (csa.MODE_CSA, 32, 4, 8, 100, "n_max"),
+    (csa.MODE_CSA, 32, 4, 0, 128, "n_blocks"),
+    (csa.MODE_HCA, 1, 0, 8, 1, "blocks_per_seq"),
+    (csa.MODE_HCA, 1 << 20, 1, 1 << 12, 1 << 20, "2^31"),
+    (csa.MODE_HCA, 1, 64, 8, 64, None),  # valid: the next check (NULL q) fails instead
+])
+def test_paged_cache_layout_is_checked(L, mode, be, bps, nb, n_max, msg):
+    c = _cfg(mode)
+    k = csa.Cache(n_max, 128, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, be, bps, nb,
+                  0x7000)
+    rc = L.hca_dense_mqa(ctypes.byref(c), 1, 1, None, ctypes.byref(k), None, None, None, None,
+                         None, 0, None)
+    assert rc == -1
+    err = csa.last_error()
+    assert ("NULL" if msg is None else msg) in err, err
