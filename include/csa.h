@@ -333,6 +333,50 @@ int csa_output_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_
                     const csa_oproj_weights_t* w, uint16_t* y_out, void* workspace,
                     size_t ws_bytes, void* stream);
 
+/* ---- Block manager (host only; no device work) ------------------------------------------
+ * Book "DeepSeek V4 模型技术大全", chapter "Attention": the hybrid cache keeps compressed entries
+ * in blocks of lcm(m, 128) = 128 tokens and reuses the blocks of a shared token prefix.  One
+ * block id names the same 128 tokens in every pool of the block layout (CSA entries, indexer
+ * keys and scales, HCA entries), so one manager serves all of a model's CSA and HCA layers when
+ * their pools hold the same n_blocks.
+ *
+ * The manager tracks, per block id 0..n_blocks-1, a reference count (sequences whose table maps
+ * it) and a registry of full blocks under a 64-bit key naming the token prefix they end
+ * (csa_blocks_chain_keys).  A registered block whose count reaches zero stays registered
+ * ("idle") until a lookup takes it back or an allocation finds no never-registered block free;
+ * allocation then recycles the least recently released idle block and unregisters it.
+ * A manager is used by one thread at a time.  Errors: CSA_ERR_INVALID_ARG (NULL, out-of-range
+ * or unreferenced block, over-release; nothing changes), CSA_ERR_UNSUPPORTED (not enough free
+ * blocks; nothing allocated). */
+typedef struct csa_block_manager csa_block_manager_t;
+int csa_blocks_create(int32_t n_blocks, csa_block_manager_t** out /* host */);
+int csa_blocks_destroy(csa_block_manager_t* m);
+/* *n_free = blocks allocatable now (free + idle), *n_idle = idle registered blocks (either
+ * pointer may be NULL). */
+int csa_blocks_counts(const csa_block_manager_t* m, int32_t* n_free, int32_t* n_idle);
+int csa_blocks_refcount(const csa_block_manager_t* m, int32_t block, int32_t* count);
+/* n fresh blocks into blocks[0..n) (host), each with count 1; all or nothing. */
+int csa_blocks_alloc(csa_block_manager_t* m, int32_t n, int32_t* blocks);
+/* One more reference to each listed block (a sequence mapping another's blocks). */
+int csa_blocks_share(csa_block_manager_t* m, int32_t n, const int32_t* blocks);
+/* One reference less per listing; a block reaching zero becomes free (idle if registered). */
+int csa_blocks_release(csa_block_manager_t* m, int32_t n, const int32_t* blocks);
+/* Register a block in use, now holding the entries of the whole prefix named by key.  A key
+ * already registered keeps its first block (the call succeeds and changes nothing). */
+int csa_blocks_publish(csa_block_manager_t* m, uint64_t key, int32_t block);
+/* Longest run of leading keys[0..n_keys) that are registered: their blocks go to
+ * blocks[0..*n_hit) (host) with one more reference each (idle blocks come back into use).  The
+ * caller then maps them, rebuilds the sequence's window and compressor tail from the last
+ * max(n_win, 2m) prefix tokens (csa_compress with n_entries preset) and continues. */
+int csa_blocks_lookup(csa_block_manager_t* m, int32_t n_keys, const uint64_t* keys,
+                      int32_t* blocks, int32_t* n_hit);
+/* Prefix keys of the floor(n_tokens / block_tokens) whole blocks of a token-id sequence (host
+ * arrays): key j depends on seed and on tokens 0 .. (j+1)*block_tokens-1 only, through a chain
+ * of 64-bit mixes (the splitmix64 finaliser).  Equal prefixes give equal keys; any differing
+ * token changes its block's key and every later one. */
+int csa_blocks_chain_keys(const int32_t* tokens, int32_t n_tokens, int32_t block_tokens,
+                          uint64_t seed, uint64_t* keys);
+
 #ifdef __cplusplus
 }
 #endif

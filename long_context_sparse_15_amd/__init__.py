@@ -84,6 +84,16 @@ _SIGS = {
                     ctypes.c_int),
     "csa_query_proj": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "csa_output_proj": ([_P, _I, _I, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "csa_blocks_create": ([_I, _P], ctypes.c_int),
+    "csa_blocks_destroy": ([_P], ctypes.c_int),
+    "csa_blocks_counts": ([_P, _P, _P], ctypes.c_int),
+    "csa_blocks_refcount": ([_P, _I, _P], ctypes.c_int),
+    "csa_blocks_alloc": ([_P, _I, _P], ctypes.c_int),
+    "csa_blocks_share": ([_P, _I, _P], ctypes.c_int),
+    "csa_blocks_release": ([_P, _I, _P], ctypes.c_int),
+    "csa_blocks_publish": ([_P, ctypes.c_uint64, _I], ctypes.c_int),
+    "csa_blocks_lookup": ([_P, _I, _P, _P, _P], ctypes.c_int),
+    "csa_blocks_chain_keys": ([_P, _I, _I, ctypes.c_uint64, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -288,3 +298,75 @@ def prefill(cfg, H, weights, cache, q, sink, out, ws, qi=None, qi_scale=None, wi
                              ctypes.byref(cache), _ptr(q), _ptr(qi), _ptr(qi_scale), _ptr(wi),
                              _ptr(sink), _ptr(out), _ptr(idx_out), wp, wn, _stream(stream)),
            "csa_prefill")
+
+
+class BlockManager:
+    """Host-side block manager of the block cache layout (csa_blocks_*): reference counts, free
+    blocks, and a registry of full blocks by token-prefix key for prefix reuse."""
+
+    def __init__(self, n_blocks):
+        self._m = ctypes.c_void_p()
+        _check(lib().csa_blocks_create(int(n_blocks), ctypes.byref(self._m)), "csa_blocks_create")
+
+    def close(self):
+        if self._m:
+            lib().csa_blocks_destroy(self._m)
+            self._m = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _ids(blocks):
+        a = (ctypes.c_int32 * len(blocks))(*[int(b) for b in blocks])
+        return a, len(blocks)
+
+    def counts(self):
+        f, i = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().csa_blocks_counts(self._m, ctypes.byref(f), ctypes.byref(i)),
+               "csa_blocks_counts")
+        return f.value, i.value
+
+    def refcount(self, block):
+        c = ctypes.c_int32()
+        _check(lib().csa_blocks_refcount(self._m, int(block), ctypes.byref(c)),
+               "csa_blocks_refcount")
+        return c.value
+
+    def alloc(self, n):
+        a = (ctypes.c_int32 * max(n, 1))()
+        _check(lib().csa_blocks_alloc(self._m, int(n), a), "csa_blocks_alloc")
+        return list(a[:n])
+
+    def share(self, blocks):
+        a, n = self._ids(blocks)
+        _check(lib().csa_blocks_share(self._m, n, a), "csa_blocks_share")
+
+    def release(self, blocks):
+        a, n = self._ids(blocks)
+        _check(lib().csa_blocks_release(self._m, n, a), "csa_blocks_release")
+
+    def publish(self, key, block):
+        _check(lib().csa_blocks_publish(self._m, ctypes.c_uint64(key), int(block)),
+               "csa_blocks_publish")
+
+    def lookup(self, keys):
+        k = (ctypes.c_uint64 * max(len(keys), 1))(*[int(x) for x in keys])
+        b = (ctypes.c_int32 * max(len(keys), 1))()
+        h = ctypes.c_int32()
+        _check(lib().csa_blocks_lookup(self._m, len(keys), k, b, ctypes.byref(h)),
+               "csa_blocks_lookup")
+        return list(b[:h.value])
+
+
+def chain_keys(tokens, block_tokens=128, seed=0):
+    """Prefix keys of the whole blocks of a token-id sequence (csa_blocks_chain_keys)."""
+    t = (ctypes.c_int32 * max(len(tokens), 1))(*[int(x) for x in tokens])
+    nb = len(tokens) // block_tokens
+    k = (ctypes.c_uint64 * max(nb, 1))()
+    _check(lib().csa_blocks_chain_keys(t, len(tokens), int(block_tokens), ctypes.c_uint64(seed),
+                                       k), "csa_blocks_chain_keys")
+    return list(k[:nb])

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libcsa.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "index.hip", "mqa.hip", "compress.hip", "proj.hip", "profile.hip"]
+SOURCES = ["api.hip", "index.hip", "mqa.hip", "compress.hip", "proj.hip", "profile.hip",
+           "blocks.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -14,15 +14,36 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int code, const char* fmt, ...) {
+int vfail(int code, const char* fmt, va_list ap) {
   char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
   vsnprintf(buf, sizeof(buf), fmt, ap);
-  va_end(ap);
   g_last_error = buf;
   return code;
 }
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int rc = vfail(code, fmt, ap);
+  va_end(ap);
+  return rc;
+}
+
+}  // namespace
+
+namespace csa {
+// Records the calling thread's last error (csa_last_error) and returns `code`; for the other
+// host-side parts of the library.
+int api_fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int rc = vfail(code, fmt, ap);
+  va_end(ap);
+  return rc;
+}
+}  // namespace csa
+
+namespace {
 
 int hip_fail(hipError_t e, const char* where) {
   return fail(CSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));

@@ -36,7 +36,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(L, n), n
         assert n in csa._SIGS, n
