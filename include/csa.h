@@ -273,7 +273,8 @@ int csa_decode(const csa_config_t* cfg, int32_t B, const uint16_t* h_new,
                size_t ws_bytes, void* stream);
 
 /* csa_prefill - causal layer over the first T tokens of B sequences (positions 0..T-1):
- * csa_compress (pos0 = 0; n_entries must be 0), then for every token t as a query the
+ * csa_compress (pos0 = 0; every block is written whatever n_entries holds on entry, and
+ * n_entries ends as floor(T/m)), then for every token t as a query the
  * causal csa_index_topk and csa_sparse_mqa (HCA mode: hca_dense_mqa).
  * Requires cache->win_slots >= T.  q bf16 [B, T, n_heads, head_dim]; qi/qi_scale/wi as
  * csa_index_topk with nq=T; out bf16 [B, T, n_heads, head_dim]; idx_out int32

@@ -242,7 +242,8 @@ void fill_mqa_args(csa::MqaArgs& a, const csa_config_t* c, int B, int nq, const 
 }
 
 int run_compress(const csa_config_t* c, int B, int T, const uint16_t* H, const int32_t* pos0,
-                 const csa_weights_t* w, const csa_cache_t* k, void* ws, hipStream_t s) {
+                 const csa_weights_t* w, const csa_cache_t* k, void* ws, hipStream_t s,
+                 bool keep_existing = true) {
   csa::CompressArgs a;
   a.mode = c->mode;
   a.B = B;
@@ -275,6 +276,7 @@ int run_compress(const csa_config_t* c, int B, int T, const uint16_t* H, const i
   a.tail = k->tail;
   a.n_entries = k->n_entries;
   a.pages = page_map(k);
+  a.keep_existing = keep_existing;
   a.proj = static_cast<float*>(ws);
   hipError_t e = csa::launch_compress(a, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "compress launch");
@@ -518,7 +520,7 @@ int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H
     idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p);
     p += align256(static_cast<size_t>(B) * T * cfg->top_k * 4);
   }
-  if ((rc = run_compress(cfg, B, T, H, nullptr, w, cache, p, s))) return rc;
+  if ((rc = run_compress(cfg, B, T, H, nullptr, w, cache, p, s, false))) return rc;
   if (is_csa(cfg)) {
     if ((rc = run_index(cfg, B, T, qi, qi_scale, wi, cache, nullptr, idx, nullptr, p, s)))
       return rc;

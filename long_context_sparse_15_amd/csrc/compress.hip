@@ -309,7 +309,7 @@ struct PoolParams {
   uint8_t* ikeys;
   float* iscale;
   PageMap pages;               // layout of entries, ikeys and iscale
-  const int32_t* n_entries;    // [B] entries already in the cache: blocks below are kept
+  const int32_t* n_keep;       // [B] entries already in the cache, kept as they are (or null)
 };
 
 __device__ __forceinline__ const float* proj_row(const PoolParams& p, int b, int p0, int u) {
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   const int i = p0 / p.m + blockIdx.x % p.nblk;
   if (i > (p0 + p.T) / p.m - 1) return;  // block does not close in this call
   if (i >= p.n_max) return;               // never write past the cache
-  if (i < p.n_entries[b]) return;         // already in the cache (rebuilding the state only)
+  if (p.n_keep && i < p.n_keep[b]) return;  // already in the cache (rebuilding state only)
   const size_t erow = entry_row(p.pages, p.n_max, b, i);
   const int tid = threadIdx.x;
   const int c = p.c;
@@ -540,7 +540,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   p.iscale = a.iscale;
   p.key_fmt = a.key_fmt;
   p.pages = a.pages;
-  p.n_entries = a.n_entries;
+  p.n_keep = a.keep_existing ? a.n_entries : nullptr;
   {
     ProfScope ps("compress_pool", s);
     pool_kernel<<<a.B * p.nblk, 256, 0, s>>>(p);

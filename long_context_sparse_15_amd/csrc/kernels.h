@@ -102,6 +102,7 @@ struct CompressArgs {
   int B, T, D, c, d_I, m, r, n_cols, tail_rows, tail_cols, win_slots, n_max;
   int key_fmt;              // indexer keys: 0 e4m3 + fp32 scale, 1 MXFP4
   PageMap pages;            // layout of entries, ikeys and iscale
+  bool keep_existing;       // blocks below n_entries[b] (on entry) are not written
   const uint16_t* H;        // [B, T, D]
   const int32_t* pos0;      // [B] or nullptr (all 0)
   const uint16_t* W;        // [n_cols, D]

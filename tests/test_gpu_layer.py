@@ -148,3 +148,31 @@ def test_compress_ragged_batch_positions():
         assert _e4m3_steps(keys, comp["ikeys"]).max() <= 1
         win = host_bits(ct["window"][b])[:Hs.shape[0]]
         check_close(O.bf16_bits_to_f64(win), O.bf16_bits_to_f64(comp["win"]), "seq %d win" % b)
+
+
+def test_prefill_rewrites_entries_whatever_n_entries_holds():
+    """csa_prefill starts at position 0: a second prefill on a cache whose n_entries already
+    counts every block (the first prefill's) still writes every entry, key and scale."""
+    w = S.WORKLOADS["tiny_csa"]
+    T = 512
+    say("prefill twice", w.name, T)
+    x = S.layer_inputs(w, T=T)
+    cfg, cache, ct, weights, d, n_max, slots = _build(w, x, x["T_total"])
+    ws = workspace(csa.workspace_size(cfg, csa.OP_PREFILL, 1, T, n_max))
+    out = torch.empty((1, T, w.n_h, w.c), dtype=torch.bfloat16, device=DEV)
+    args = (cfg, d["H"][:, :T].contiguous(), weights, cache, d["q"][:, :T].contiguous(),
+            d["sink"], out, ws)
+    kw = dict(qi=d["qi"][:, :T].contiguous(), qi_scale=d["qi_scale"][:, :T].contiguous(),
+              wi=d["wi"][:, :T].contiguous())
+    csa.prefill(*args, **kw)
+    torch.cuda.synchronize()
+    first = {k: ct[k].clone() for k in ("entries", "idx_keys", "idx_scale")}
+    out1 = out.clone()
+    for k in first:
+        ct[k].zero_()
+    assert int(ct["n_entries"][0]) == T // w.m
+    csa.prefill(*args, **kw)
+    torch.cuda.synchronize()
+    for k in first:
+        assert torch.equal(ct[k], first[k]), k
+    assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
