@@ -111,6 +111,7 @@ __global__ __launch_bounds__(256) void gemm_tn_bf16_kernel(const uint16_t* __res
 // on XCD b % 8), so the 32 workgroups resident on an XCD share 8 A panels and 4 B panels
 // through its L2.
 constexpr int G2M = 256, G2N = 256, G2K = 64, G2_THREADS = 512;
+constexpr int kEpiPitch = G2N + 8;  // fp32 row pitch of the epilogue staging (64 rows: 66 KiB)
 constexpr size_t kGemm2Lds = 2 * (G2M + G2N) * G2K * sizeof(uint16_t);  // 128 KiB
 
 __device__ __forceinline__ int g2_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -120,7 +121,8 @@ __device__ __forceinline__ int g2_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); 
 template <typename OutT>
 __global__ __launch_bounds__(G2_THREADS) void gemm_tn_bf16_256_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, OutT* __restrict__ Cst,
-    int M, int N, int K, int lda, int ldw, int ldc, int tiles_m, int tiles_n, int per_xcd) {
+    int M, int N, int K, int lda, int ldw, int ldc, int tiles_m, int tiles_n, int per_xcd,
+    bool vec_ok) {
   extern __shared__ __align__(16) unsigned char smem[];
   typedef __attribute__((address_space(3))) void lds_void;
   const int bid = blockIdx.x;
@@ -204,24 +206,66 @@ __global__ __launch_bounds__(G2_THREADS) void gemm_tn_bf16_256_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next stage has landed
     __syncthreads();                                   // and every wave is done with this one
   }
-  // D of a 32x32 tile: lane l holds column l%32, rows 8*(i/4) + 4h + i%4
+  // Epilogue through LDS (free after the last barrier), 64 tile rows per pass: the waves that
+  // own them write their accumulators as fp32 rows (pitch kEpiPitch: rows 4 apart land 32 banks
+  // apart, so the two half-waves' rows do not collide), then every wave reads whole rows back,
+  // 32 bytes per lane, and stores them as full-width row segments.
+  // D of a 32x32 tile: lane l holds column l%32, rows 8*(i/4) + 4h + i%4.
+  float* stage = reinterpret_cast<float*>(smem);
+  const bool full_n = vec_ok && n0 + G2N <= N;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int pass = 0; pass < 4; ++pass) {
+    if (wm == (pass >> 1)) {
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int n = n0 + wn * 64 + ni * 32 + n32;
-      if (n >= N) continue;
+      for (int mh = 0; mh < 2; ++mh) {
+        const int mi = 2 * (pass & 1) + mh;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * 128 + mi * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (m < M) {
-          if constexpr (sizeof(OutT) == 2)
-            Cst[static_cast<size_t>(m) * ldc + n] = f32_to_bf16(acc[mi][ni][i]);
-          else
-            Cst[static_cast<size_t>(m) * ldc + n] = acc[mi][ni][i];
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = mh * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+            stage[r * kEpiPitch + wn * 64 + ni * 32 + n32] = acc[mi][ni][i];
+          }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = it * 16 + wave * 2 + (l >> 5);  // tile row within the pass
+      const int c = (l & 31) * 8;                    // first of 8 columns
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(stage + r * kEpiPitch + c);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(stage + r * kEpiPitch + c + 4);
+      const int m = m0 + pass * 64 + r;
+      if (m < M) {
+        OutT* dst = Cst + static_cast<size_t>(m) * ldc + n0 + c;
+        if (full_n) {
+          if constexpr (sizeof(OutT) == 2) {
+            u32x4 o;
+            o[0] = pack_bf16x2(v0[0], v0[1]);
+            o[1] = pack_bf16x2(v0[2], v0[3]);
+            o[2] = pack_bf16x2(v1[0], v1[1]);
+            o[3] = pack_bf16x2(v1[2], v1[3]);
+            *reinterpret_cast<u32x4*>(dst) = o;
+          } else {
+            reinterpret_cast<f32x4*>(dst)[0] = v0;
+            reinterpret_cast<f32x4*>(dst)[1] = v1;
+          }
+        } else {
+          const float vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (n0 + c + j < N) {
+              if constexpr (sizeof(OutT) == 2)
+                dst[j] = f32_to_bf16(vv[j]);
+              else
+                dst[j] = vv[j];
+            }
+          }
         }
       }
     }
+    __syncthreads();
+  }
 }
 
 // One launch of the large-tile GEMM (K % 64 == 0): tiles in XCD order, LDS attribute set once
@@ -239,8 +283,10 @@ static hipError_t launch_gemm_256(const uint16_t* A, int lda, const uint16_t* W,
   }
   const int tm2 = (M + G2M - 1) / G2M, tn2 = (N + G2N - 1) / G2N;
   const int per_xcd = (tm2 * tn2 + 7) / 8;
+  // full-row vector stores need 8-element aligned rows (16 or 32 bytes)
+  const bool vec_ok = ldc % 8 == 0 && reinterpret_cast<uintptr_t>(C) % (8 * sizeof(OutT)) == 0;
   gemm_tn_bf16_256_kernel<OutT><<<8 * per_xcd, G2_THREADS, kGemm2Lds, s>>>(
-      A, W, C, M, N, K, lda, ldw, ldc, tm2, tn2, per_xcd);
+      A, W, C, M, N, K, lda, ldw, ldc, tm2, tn2, per_xcd, vec_ok);
   return hipGetLastError();
 }
 
