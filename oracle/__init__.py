@@ -17,7 +17,7 @@ and section:
   components in words; partial RoPE; learnable sink logit).
 
 Every function states the passage it follows.  Where the pages are silent the reading taken
-is named in the function's docstring (R1..R21); the same list is in the design notes.
+is named in the function's docstring (R1..R22); the same list is in the design notes.
 
 Parity pins: every public function is pinned by tests that do not reuse its own formula
 (closed forms, textbook special cases computed with torch, hand-computed fixtures under
@@ -29,7 +29,8 @@ from .numerics import (bf16_bits_to_f64, f64_to_bf16_bits, e4m3_table, e4m3_deco
 from .csa import (project, pool_overlap, pool_plain, rms_norm, rope_rotate, split_columns,
                   compress_tokens, index_scores, index_scores_mxfp4, topk_select,
                   visible_entries, window_tokens, attend, csa_query, hca_query, csa_layer,
-                  hca_layer, query_projections, grouped_output_projection)
+                  hca_layer, query_projections, grouped_output_projection,
+                  quantize_entries_mixed, decode_entries_mixed)
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "e4m3_table", "e4m3_decode", "e4m3_encode",
@@ -37,5 +38,6 @@ __all__ = [
     "quantize_rows_mxfp4", "mxfp4_decode", "index_scores_mxfp4", "project", "pool_overlap",
     "pool_plain", "rms_norm", "rope_rotate", "split_columns", "compress_tokens", "index_scores", "topk_select", "visible_entries",
     "window_tokens", "attend", "csa_query", "hca_query", "csa_layer", "hca_layer",
-    "query_projections", "grouped_output_projection",
+    "query_projections", "grouped_output_projection", "quantize_entries_mixed",
+    "decode_entries_mixed",
 ]

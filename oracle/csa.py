@@ -37,11 +37,17 @@ Readings taken where the pages are silent (also listed in the design notes):
       the heads, stored bf16 and not rotated (R18); q^I = c^Q W^IUQ is stored as R5; w^I = h W_w
       stays fp32;
   R21 grouped output projection: group u holds the consecutive heads u*n_h/g .. (u+1)*n_h/g-1,
-      z^[u] is stored in bf16, Proj is a plain linear map from g*r_o to D (no bias), y in bf16.
+      z^[u] is stored in bf16, Proj is a plain linear map from g*r_o to D (no bias), y in bf16;
+  R22 mixed-precision entries (optional): the pages keep the RoPE dims of a KV entry in BF16 and
+      the other dims in FP8 without naming a scale: dims 0..c-r-1 are stored as E4M3 codes of
+      the normalised, gain-scaled value itself (RNE, saturating at 448, no scale: RMS-normalised
+      entries stay far inside E4M3's range), dims c-r..c-1 (rotated) as bf16; window rows stay
+      bf16.  E4M3 values are exact in bf16, so a decoded entry is a bf16 row.
 """
 import numpy as np
 
-from .numerics import (bf16_bits_to_f64, f64_to_bf16_bits, e4m3_decode, quantize_rows_e4m3,
+from .numerics import (bf16_bits_to_f64, f64_to_bf16_bits, e4m3_decode, e4m3_encode,
+                       quantize_rows_e4m3,
                        quantize_rows_mxfp4, mxfp4_decode)
 
 
@@ -164,7 +170,25 @@ def rope_rotate(x, positions, inv_freq, sign=1.0):
     return x
 
 
-def compress_tokens(h_bits, w_bits, params, mode, m, c, d_i, inv_freq, eps, idx_format="e4m3"):
+def quantize_entries_mixed(values, r):
+    """Mixed-precision storage of compressed entries (reading R22; Book, chapter "Attention",
+    section "注意力实现细节": RoPE dims in BF16, the rest in FP8).  values float64 [n, c]
+    (normalised and rotated).  Returns (codes uint8 [n, c-r]: E4M3 of dims 0..c-r-1, rope
+    uint16 [n, r]: bf16 bits of dims c-r..c-1)."""
+    values = np.asarray(values, np.float64)
+    c = values.shape[1]
+    return e4m3_encode(values[:, :c - r]), f64_to_bf16_bits(values[:, c - r:])
+
+
+def decode_entries_mixed(codes, rope_bits):
+    """bf16 bits [n, c] of the real values of mixed-precision entries (reading R22): the E4M3
+    dims decoded (exactly representable in bf16), then the bf16 RoPE dims."""
+    vals = np.concatenate([e4m3_decode(codes), bf16_bits_to_f64(rope_bits)], axis=1)
+    return f64_to_bf16_bits(vals)
+
+
+def compress_tokens(h_bits, w_bits, params, mode, m, c, d_i, inv_freq, eps, idx_format="e4m3",
+                    entry_format="bf16"):
     """Run the compressor on a whole token prefix H[0:T] (a1 + a2 + epilogue).
 
     Returns a dict with
@@ -175,6 +199,7 @@ def compress_tokens(h_bits, w_bits, params, mode, m, c, d_i, inv_freq, eps, idx_
       iscale   float32 [floor(T/m)], or uint8 [floor(T/m), d_I/32] E8M0 block scales (mxfp4)
       ipre     float64 [floor(T/m), d_I]
       win      uint16 [T, c] bf16 bits of RoPE(RMSNorm(h_u W_win) * gamma_win, u) (reading R10)
+      ecodes, erope  (entry_format "mixed") quantize_entries_mixed of the same values (R22)
     params: dict with Ba, Bb, BIa, BIb (CSA) or B (HCA), gamma, gamma_win.
     Book, chapter "Attention": "CSA 的完整路径" (compressor; K^IComp from the same
     compression operation), "HCA 的完整路径" (m' compressor), "注意力实现细节" (RMSNorm and
@@ -199,6 +224,8 @@ def compress_tokens(h_bits, w_bits, params, mode, m, c, d_i, inv_freq, eps, idx_
     normed = rms_norm(pre, params["gamma"], eps)
     rotated = rope_rotate(normed, m * np.arange(n), inv_freq)
     out["entries"] = f64_to_bf16_bits(rotated)
+    if entry_format == "mixed":
+        out["ecodes"], out["erope"] = quantize_entries_mixed(rotated, 2 * len(inv_freq))
     out["pre"] = pre
     win = rope_rotate(rms_norm(s["Win"], params["gamma_win"], eps), np.arange(T), inv_freq)
     out["win"] = f64_to_bf16_bits(win)

@@ -624,3 +624,56 @@ def test_grouped_output_projection_closed_forms():
     # one group with identity weights is a plain projection
     z1, y1 = O.grouped_output_projection(o, _bf16(np.eye(n_h * c))[None], _bf16(np.eye(n_h * c)), 1)
     assert np.array_equal(z1, o.reshape(T, -1)) and np.array_equal(y1, z1)
+
+
+# ---------------------------------------------------------------- mixed-precision entries (R22)
+
+def test_mixed_entries_split_and_hand_values():
+    """One-hot rows put their value on the right side of the split at c - r: 1.0 in the last
+    non-RoPE dim is E4M3 0x38 (exponent field 7, bias 7); 1.0 in the first RoPE dim is bf16
+    0x3F80.  Values past the E4M3 range saturate at 448 (0x7E), signs are kept."""
+    c, r = 16, 8
+    x = np.zeros((4, c))
+    x[0, c - r - 1] = 1.0
+    x[1, c - r] = 1.0
+    x[2, 0] = 1000.0
+    x[3, 1] = -0.5
+    codes, rope = O.quantize_entries_mixed(x, r)
+    assert codes.shape == (4, c - r) and rope.shape == (4, r)
+    assert codes[0, c - r - 1] == 0x38 and np.all(rope[0] == 0)
+    assert np.all(codes[1] == 0) and rope[1, 0] == 0x3F80 and np.all(rope[1, 1:] == 0)
+    assert codes[2, 0] == 0x7E
+    assert codes[3, 1] == 0xB0  # -0.5: sign, exponent field 6, mantissa 0
+
+
+def test_mixed_entries_round_trip_on_representable_values():
+    """Values that E4M3 (first dims) and bf16 (RoPE dims) hold exactly come back exactly; the
+    E4M3 values are taken from the OCP point table, not from the oracle's own decoder."""
+    g = _gold("e4m3_points.json")
+    pts = np.array([v for _, v in g["points"]], dtype=np.float64)
+    rng = np.random.default_rng(3)
+    c, r = 64, 16
+    x = np.empty((5, c))
+    x[:, :c - r] = rng.choice(np.concatenate([pts, -pts]), size=(5, c - r))
+    x[:, c - r:] = rng.integers(-128, 128, size=(5, r)) / 16.0   # 7 significant bits: exact in bf16
+    codes, rope = O.quantize_entries_mixed(x, r)
+    back = O.bf16_bits_to_f64(O.decode_entries_mixed(codes, rope))
+    assert np.array_equal(back, x)
+
+
+def test_mixed_entries_error_bound_and_compressor():
+    """The compressor's mixed entries (reading R22) decode to within half an E4M3 step of the
+    bf16 entries' values on the non-RoPE dims (relative 2^-4, or 2^-10 absolute below the
+    normal range) and equal them on the RoPE dims."""
+    w = S.WORKLOADS["tiny_csa"]
+    x = S.layer_inputs(w, T=256)
+    params = {k: x[k] for k in ("Ba", "Bb", "BIa", "BIb", "gamma", "gamma_win")}
+    comp = O.compress_tokens(x["H"][0], x["W"], params, "csa", w.m, w.c, w.d_I, x["inv_freq"],
+                             1e-6, entry_format="mixed")
+    dec = O.bf16_bits_to_f64(O.decode_entries_mixed(comp["ecodes"], comp["erope"]))
+    ref = O.bf16_bits_to_f64(comp["entries"])
+    k = w.c - w.r
+    assert np.array_equal(dec[:, k:], ref[:, k:])
+    err = np.abs(dec[:, :k] - ref[:, :k])
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(ref[:, :k]), 2.0 ** -10) * 1.01)
+    assert err.max() > 0  # the quantisation is not a no-op
