@@ -43,16 +43,18 @@ def _key_bytes(w, key_fmt):
     return (w.d_I // 2 if key_fmt == "mxfp4" else w.d_I) + 4
 
 
-def _decode_bytes(w, n_vis, key_fmt="e4m3"):
+def _decode_bytes(w, n_vis, key_fmt="e4m3", mixed=False):
     """Algorithmic HBM bytes of one decode token (what the method must move): indexer keys and
     their scales over the visible entries, the top-k gathered entries (CSA) or every visible
-    entry (HCA), the window rows, the query and the output, the indexer query."""
+    entry (HCA), the window rows, the query and the output, the indexer query.  Mixed entries
+    take c + r bytes (E4M3 unrotated dims, bf16 RoPE dims) instead of 2c."""
     c2 = w.c * 2
+    e2 = w.c + w.r if mixed else c2
     b = w.n_win * c2 + 2 * w.n_h * c2
     if w.mode == "csa":
-        b += n_vis * _key_bytes(w, key_fmt) + min(w.k, n_vis) * c2 + w.H_I * (w.d_I + 8)
+        b += n_vis * _key_bytes(w, key_fmt) + min(w.k, n_vis) * e2 + w.H_I * (w.d_I + 8)
     else:
-        b += n_vis * c2
+        b += n_vis * e2
     return b
 
 
@@ -121,10 +123,11 @@ def decode_workload(name, K, W, rotate):
 
     key_fmt = "mxfp4" if "_mxfp4" in name else "e4m3"
     paged = "_paged" in name
-    base = name.replace("_paged", "").replace("_mxfp4", "")
+    mixed = "_mixed" in name
+    base = name.replace("_paged", "").replace("_mxfp4", "").replace("_mixed", "")
     w = S.WORKLOADS[base]
     dev = "cuda"
-    x = G.decode_cache_inputs(w, dev, key_fmt=key_fmt)
+    x = G.decode_cache_inputs(w, dev, key_fmt=key_fmt, entry_fmt="mixed" if mixed else "bf16")
     heavy = ["entries", "window"] + (["ikeys", "iscale"] if w.mode == "csa" else [])
     copies = [x]
     for r in range(1, rotate):
@@ -135,7 +138,8 @@ def decode_workload(name, K, W, rotate):
     cfg = csa.make_config(csa.MODE_CSA if w.mode == "csa" else csa.MODE_HCA, w.m, w.n_h, w.c,
                           w.r, x["inv_freq"], top_k=w.k, n_win=w.n_win, idx_heads=w.H_I,
                           idx_dim=w.d_I, softmax_scale=w.scale,
-                          idx_key_format=csa.IDX_MXFP4 if key_fmt == "mxfp4" else csa.IDX_E4M3)
+                          idx_key_format=csa.IDX_MXFP4 if key_fmt == "mxfp4" else csa.IDX_E4M3,
+                          entry_format=csa.ENT_MIXED if mixed else csa.ENT_BF16)
     pg = {}
     if paged:
         be = 128 // w.m
@@ -172,7 +176,7 @@ def decode_workload(name, K, W, rotate):
     ms = _time_steps(step, K, W, stream)
     prof = _profiled(step, K, W)
     n_vis = min(w.N, (w.t + 1) // w.m)
-    step_bytes = w.B * _decode_bytes(w, n_vis, key_fmt)
+    step_bytes = w.B * _decode_bytes(w, n_vis, key_fmt, mixed)
     res = {"workload": name, "value": w.B / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
            "hbm_gbs": step_bytes / (ms / 1e3) / 1e9,
            "hbm_frac": step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
@@ -182,7 +186,8 @@ def decode_workload(name, K, W, rotate):
         kbytes = w.B * _score_kernel_bytes(w, n_vis, key_fmt)
     else:
         kname = "mqa_dense"
-        kbytes = w.B * ((n_vis + w.n_win) * w.c * 2 + 2 * w.n_h * w.c * 2)
+        kbytes = w.B * (n_vis * (w.c + w.r if mixed else 2 * w.c) + w.n_win * w.c * 2 +
+                        2 * w.n_h * w.c * 2)
     launches, tot = prof[kname]
     kdur = tot / launches
     ach = kbytes / (kdur / 1e3) / 1e9
@@ -359,7 +364,8 @@ def main():
     ap.add_argument("--workload", default="csa_decode_128k")
     ap.add_argument("--extra", default="csa_decode_1m,hca_decode_1m,csa_prefill_64k,"
                     "csa_decode_128k_mxfp4,csa_decode_1m_mxfp4,csa_prefill_64k_mxfp4,"
-                    "qo_proj_64k,csa_decode_128k_paged,csa_decode_1m_paged,hca_decode_1m_paged",
+                    "qo_proj_64k,csa_decode_128k_paged,csa_decode_1m_paged,hca_decode_1m_paged,"
+                    "csa_decode_128k_mixed,csa_decode_1m_mixed,hca_decode_1m_mixed",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")

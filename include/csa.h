@@ -53,6 +53,14 @@ extern "C" {
                            low nibble of byte i) + one E8M0 scale byte per 32 dims (shared
                            exponent floor(log2 max|k|) - 2); the query stays e4m3 */
 
+/* Storage of the compressed entries (csa_config_t.entry_format). */
+#define CSA_ENT_BF16 0  /* head_dim bf16 values per entry */
+#define CSA_ENT_MIXED 1 /* head_dim - rope_dim E4M3 codes of the unrotated dims (no scale), then
+                           rope_dim bf16 rotated dims: head_dim + rope_dim bytes per entry.  The
+                           pages keep the RoPE dims in BF16 and the rest in FP8 ("DeepSeek V4
+                           模型技术大全", chapter "Attention", section "注意力实现细节").  Requires
+                           head_dim 512 and rope_dim a multiple of 16; window rows stay bf16. */
+
 /* Operation ids for csa_workspace_size(). */
 #define CSA_OP_COMPRESS 0
 #define CSA_OP_INDEX_TOPK 1
@@ -94,10 +102,12 @@ typedef struct csa_config {
   int32_t q_rank;
   int32_t out_groups;
   int32_t out_rank;
+  int32_t entry_format; /* CSA_ENT_BF16 (0) or CSA_ENT_MIXED (1) */
 } csa_config_t;
 
 /* Caller-owned per-sequence attention state for B sequences (all device pointers).
- *  entries   bf16 [B, n_max, head_dim]  compressed entries, RMS-normalised and rotated
+ *  entries   bf16 [B, n_max, head_dim]  compressed entries, RMS-normalised and rotated; with
+ *            CSA_ENT_MIXED uint8 [B, n_max, head_dim + rope_dim] (see CSA_ENT_MIXED)
  *  idx_keys  e4m3 [B, n_max, idx_dim]   indexer keys K^IComp (CSA; NULL for HCA); with
  *            CSA_IDX_MXFP4: uint8 [B, n_max, idx_dim/2] packed E2M1 codes
  *  idx_scale fp32 [B, n_max]            per-entry scale of idx_keys (CSA; NULL for HCA); with

@@ -82,6 +82,12 @@ int check_config(const csa_config_t* c, bool need_compressor) {
       return fail(CSA_ERR_INVALID_ARG, "idx_key_format=%d is neither E4M3 nor MXFP4",
                   c->idx_key_format);
   }
+  if (c->entry_format != CSA_ENT_BF16 && c->entry_format != CSA_ENT_MIXED)
+    return fail(CSA_ERR_INVALID_ARG, "entry_format=%d is neither BF16 nor MIXED",
+                c->entry_format);
+  if (c->entry_format == CSA_ENT_MIXED && (c->head_dim != 512 || c->rope_dim % 16))
+    return fail(CSA_ERR_UNSUPPORTED, "mixed entries need head_dim 512 and rope_dim a multiple "
+                "of 16 (head_dim=%d, rope_dim=%d)", c->head_dim, c->rope_dim);
   if (need_compressor) {
     if (c->hidden < 32 || (c->hidden % 32))
       return fail(CSA_ERR_INVALID_ARG, "hidden=%d must be a positive multiple of 32", c->hidden);
@@ -235,6 +241,7 @@ void fill_mqa_args(csa::MqaArgs& a, const csa_config_t* c, int B, int nq, const 
   a.win_slots = k->win_slots;
   a.n_max = k->n_max;
   a.pages = page_map(k);
+  a.entry_mixed = c->entry_format == CSA_ENT_MIXED;
   a.scale = c->softmax_scale;
   a.out = out;
   a.lse_out = lse_out;
@@ -277,6 +284,7 @@ int run_compress(const csa_config_t* c, int B, int T, const uint16_t* H, const i
   a.n_entries = k->n_entries;
   a.pages = page_map(k);
   a.keep_existing = keep_existing;
+  a.entry_mixed = c->entry_format == CSA_ENT_MIXED;
   a.proj = static_cast<float*>(ws);
   hipError_t e = csa::launch_compress(a, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "compress launch");
@@ -328,7 +336,7 @@ int check_oproj_config(const csa_config_t* c) {
 
 extern "C" {
 
-int csa_version(void) { return 1 * 10000 + 1 * 100 + 0; }
+int csa_version(void) { return 1 * 10000 + 2 * 100 + 0; }
 
 int csa_profile_start(void) {
   csa::profile_start();

@@ -356,6 +356,7 @@ struct PoolParams {
   float* iscale;
   PageMap pages;               // layout of entries, ikeys and iscale
   const int32_t* n_keep;       // [B] entries already in the cache, kept as they are (or null)
+  bool entry_mixed;            // entries as [c-r E4M3 codes | r bf16] rows (c + r bytes)
 };
 
 __device__ __forceinline__ const float* proj_row(const PoolParams& p, int b, int p0, int u) {
@@ -417,7 +418,9 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   }
   const float tot = block_sum(ss, s_red);  // includes the barrier that publishes s_val
   const float inv_rms = rsqrtf(tot / c + p.eps);
-  uint16_t* dst = p.entries + erow * c;
+  // bf16 row of c values, or (mixed) c - r E4M3 codes of the unrotated dims then r bf16
+  unsigned char* dst = reinterpret_cast<unsigned char*>(p.entries) +
+                       erow * static_cast<size_t>(p.entry_mixed ? c + p.r : 2 * c);
   const int pos = p.m * i;
   for (int pp = tid; pp < c / 2; pp += 256) {
     const int d = 2 * pp;
@@ -430,7 +433,13 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
       x0 = y0;
       x1 = y1;
     }
-    *reinterpret_cast<uint32_t*>(dst + d) = pack_bf16x2(x0, x1);
+    if (!p.entry_mixed)
+      *reinterpret_cast<uint32_t*>(dst + 2 * d) = pack_bf16x2(x0, x1);
+    else if (d < c - p.r)
+      *reinterpret_cast<uint16_t*>(dst + d) =
+          static_cast<uint16_t>(e4m3_rne(x0) | (static_cast<uint32_t>(e4m3_rne(x1)) << 8));
+    else
+      *reinterpret_cast<uint32_t*>(dst + (c - p.r) + 2 * (d - (c - p.r))) = pack_bf16x2(x0, x1);
   }
   if (!csa) return;
   // indexer keys: same pooling on their own streams, then per-entry E4M3 quantisation or
@@ -587,6 +596,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   p.key_fmt = a.key_fmt;
   p.pages = a.pages;
   p.n_keep = a.keep_existing ? a.n_entries : nullptr;
+  p.entry_mixed = a.entry_mixed;
   {
     ProfScope ps("compress_pool", s);
     pool_kernel<<<a.B * p.nblk, 256, 0, s>>>(p);

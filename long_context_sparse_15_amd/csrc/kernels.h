@@ -79,6 +79,7 @@ struct MqaArgs {
   const float* inv_freq;    // [r/2]
   int B, nq, n_heads, c, r, k, m, n_win, win_slots, n_max;
   PageMap pages;            // layout of entries
+  bool entry_mixed;         // entries as [c-r E4M3 codes | r bf16] rows (c + r bytes)
   float scale;
   uint16_t* out;            // [rows, n_heads, c]
   float* lse_out;           // [rows, n_heads] or nullptr
@@ -103,6 +104,7 @@ struct CompressArgs {
   int key_fmt;              // indexer keys: 0 e4m3 + fp32 scale, 1 MXFP4
   PageMap pages;            // layout of entries, ikeys and iscale
   bool keep_existing;       // blocks below n_entries[b] (on entry) are not written
+  bool entry_mixed;         // entries as [c-r E4M3 codes | r bf16] rows (c + r bytes)
   const uint16_t* H;        // [B, T, D]
   const int32_t* pos0;      // [B] or nullptr (all 0)
   const uint16_t* W;        // [n_cols, D]

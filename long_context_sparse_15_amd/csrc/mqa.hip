@@ -578,7 +578,10 @@ __device__ __forceinline__ float sum_over_xor8_16_32(float x) {
 }
 
 // PAGED: as mqa_kernel's, the span's entries are translated to pool rows in the prologue.
-template <int C, bool SPARSE, bool PAGED = false>
+// MIXED: entries are rows of c + r bytes, the c - r unrotated dims as E4M3 codes then the r RoPE
+// dims in bf16; a gathered entry row is widened to bf16 (exact) as it is stored to LDS, so the
+// tiles and everything after them are unchanged.  Window rows stay bf16.
+template <int C, bool SPARSE, bool PAGED = false, bool MIXED = false>
 __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaParams p) {
   using SH = MqaWideShape<C>;
   constexpr int HP = SH::HP, DS = SH::DS, NW = SH::NW, NT = SH::NT, CS = SH::CS, KK = SH::KK,
@@ -655,31 +658,37 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   // Masked rows (past the span, an index outside the visible entries) read the window row of t.
   // Branch-free: the index is always read (clamped into the span's index list) and both
   // candidate pointers are formed, then selected.
+  const int ES = MIXED ? (C + p.r) / 2 : C;  // entry row stride in 16-bit units
   const uint16_t* const ent_base =
-      PAGED ? p.entries : p.entries + static_cast<size_t>(b) * p.n_max * C;
+      PAGED ? p.entries : p.entries + static_cast<size_t>(b) * p.n_max * ES;
   const uint16_t* const win_base = p.window + static_cast<size_t>(b) * p.win_slots * C;
   const uint16_t* const safe_row = win_base + static_cast<size_t>(t % p.win_slots) * C;
   // PAGED lists hold pool rows, already checked against the visible entries (-1: masked)
   const int e_lim = PAGED ? 0x7fffffff : n_ent;
-  auto resolve_e = [&](int j, int e, const uint16_t*& ptr, uint32_t& mask) {
+  // em (MIXED): which rows of the tile are entry rows (the rest are bf16 window rows)
+  auto resolve_e = [&](int j, int e, const uint16_t*& ptr, uint32_t& mask, uint32_t& em) {
     const bool in_span = l < 32 && j < j1;
     const bool sel = j < n_sel;
     const bool ok_e = e >= 0 && e < e_lim;
     const int u = max(wlo + (j - n_sel), 0);
-    const uint16_t* pe = ent_base + static_cast<size_t>(ok_e ? e : 0) * C;
+    const uint16_t* pe = ent_base + static_cast<size_t>(ok_e ? e : 0) * ES;
     const uint16_t* pw = win_base + static_cast<size_t>(u % p.win_slots) * C;
     const bool ok = in_span && (!sel || ok_e);
     ptr = ok ? (sel ? pe : pw) : safe_row;
     mask = static_cast<uint32_t>(__ballot(ok));
+    if constexpr (MIXED) em = static_cast<uint32_t>(__ballot(ok && sel));
   };
-  auto resolve = [&](int jt, const uint16_t*& ptr, uint32_t& mask) {
+  auto resolve = [&](int jt, const uint16_t*& ptr, uint32_t& mask, uint32_t& em) {
     const int j = jt + l;
     int e = j;
     if constexpr (LIST) e = s_idx[min(max(j - j0, 0), p.split_rows - 1)];
-    resolve_e(j, e, ptr, mask);
+    resolve_e(j, e, ptr, mask, em);
   };
-  // wave `wave` loads rows wave, wave+8, wave+16, wave+24 of the tile, 16 bytes per lane
-  auto gload = [&](const uint16_t* ptr, u32x4 (&st)[LOADS]) {
+  const int ncc = (C - p.r) >> 4;  // MIXED: 16-byte chunks of codes, then r/8 of RoPE dims
+  const int ebc = ncc + (p.r >> 3);
+  // wave `wave` loads rows wave, wave+8, wave+16, wave+24 of the tile, 16 bytes per lane (an
+  // entry row of a MIXED tile has ebc chunks: the lanes past them reload its last chunk)
+  auto gload = [&](const uint16_t* ptr, uint32_t em, u32x4 (&st)[LOADS]) {
     const uint64_t pv = reinterpret_cast<uint64_t>(ptr);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -687,7 +696,9 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
       const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv), rr);
       const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv >> 32), rr);
       const uint64_t rp = (static_cast<uint64_t>(hi) << 32) | lo;
-      st[i] = *(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(rp) + l);
+      int ch = l;
+      if constexpr (MIXED) ch = ((em >> rr) & 1u) ? min(l, ebc - 1) : l;
+      st[i] = *(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(rp) + ch);
     }
   };
 
@@ -697,6 +708,7 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   // (an empty span gathers masked rows, the window row of t, and never uses them)
   u32x4 stage0[LOADS], stage1[LOADS];
   uint32_t mq0 = 0, mq1 = 0, mq2 = 0, mq3 = 0;  // valid masks of tiles i .. i+3
+  uint32_t em0 = 0, em1 = 0, em2 = 0, em3 = 0;  // entry-row masks of the same tiles (MIXED)
   // pool row of logical entry e (-1 if e is not a closed entry)
   auto xlate = [&](int e) {
     return (e >= 0 && e < n_ent) ? static_cast<int>(entry_row(p.pages, p.n_max, b, e)) : -1;
@@ -709,10 +721,10 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
       f0 = xlate(f0);
       f1 = xlate(f1);
     }
-    resolve_e(j0 + l, f0, p0, mq0);
-    resolve_e(j0 + 32 + l, f1, p1, mq1);
-    gload(p0, stage0);
-    gload(p1, stage1);
+    resolve_e(j0 + l, f0, p0, mq0, em0);
+    resolve_e(j0 + 32 + l, f1, p1, mq1, em1);
+    gload(p0, em0, stage0);
+    gload(p1, em1, stage1);
   }
 
   if constexpr (LIST) {
@@ -792,9 +804,37 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     tb_off[dt] = static_cast<uint32_t>(rb * C + dbase + ((low ^ swz(rb)) << 3) + 4 * (q4 & 1)) * 2u;
   }
 
-  auto store_tile = [&](const u32x4 (&st)[LOADS], uint32_t bo) {
+  auto store_tile = [&](const u32x4 (&st)[LOADS], uint32_t em, uint32_t bo) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4*>(smem + st_off[i] + bo) = st[i];
+    for (int i = 0; i < LOADS; ++i) {
+      if constexpr (MIXED) {
+        const int rr = wave + i * NW;
+        if ((em >> rr) & 1u) {  // entry row: 16 codes -> two bf16 chunks, or one RoPE chunk
+          unsigned char* row = smem + bo + static_cast<uint32_t>(rr * C * 2);
+          const int sw = swz(rr);
+          if (l < ncc) {
+            u32x4 lo, hi;
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              lo[2 * w] = __builtin_bit_cast(
+                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(st[i][w], 1.f, false));
+              lo[2 * w + 1] = __builtin_bit_cast(
+                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(st[i][w], 1.f, true));
+              hi[2 * w] = __builtin_bit_cast(
+                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(st[i][2 + w], 1.f, false));
+              hi[2 * w + 1] = __builtin_bit_cast(
+                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(st[i][2 + w], 1.f, true));
+            }
+            *reinterpret_cast<u32x4*>(row + (((2 * l) ^ sw) << 4)) = lo;
+            *reinterpret_cast<u32x4*>(row + (((2 * l + 1) ^ sw) << 4)) = hi;
+          } else if (l < ebc) {
+            *reinterpret_cast<u32x4*>(row + (((l + ncc) ^ sw) << 4)) = st[i];
+          }
+          continue;
+        }
+      }
+      *reinterpret_cast<u32x4*>(smem + st_off[i] + bo) = st[i];
+    }
   };
   auto s_phase = [&](uint32_t bo) -> f32x16 {
     const unsigned char* Eb = smem + bo;
@@ -872,11 +912,11 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     const uint16_t* pnext;
     {
       const uint16_t* p2;
-      resolve(j0 + 64, p2, mq2);
-      resolve(j0 + 96, pnext, mq3);
-      store_tile(stage0, 0);
+      resolve(j0 + 64, p2, mq2, em2);
+      resolve(j0 + 96, pnext, mq3, em3);
+      store_tile(stage0, em0, 0);
       __syncthreads();
-      gload(p2, stage0);
+      gload(p2, em2, stage0);
     }
     f32x16 sacc = s_phase(0);
     bf16x8 bp[2];
@@ -884,9 +924,9 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     auto step = [&](int i, u32x4 (&st)[LOADS]) {
       const int par = i & 1;
       // phase A: tile i+1 to LDS, S partial of tile i out, gathers of tile i+3
-      store_tile(st, bo_next);
+      store_tile(st, em1, bo_next);
       x_write(sacc);
-      gload(pnext, st);
+      gload(pnext, em3, st);
       __syncthreads();
       // phase B
       {
@@ -900,12 +940,16 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
       softmax(mq0, par);
       pv_phase(bo_prev, bp);
       sacc = s_phase(bo_next);
-      uint32_t mn;
-      resolve(j0 + (i + 4) * 32, pnext, mn);
+      uint32_t mn, en = 0;
+      resolve(j0 + (i + 4) * 32, pnext, mn, en);
       mq0 = mq1;
       mq1 = mq2;
       mq2 = mq3;
       mq3 = mn;
+      em0 = em1;
+      em1 = em2;
+      em2 = em3;
+      em3 = en;
       __syncthreads();
       bo_prev = bo_prev == 2 * TB ? 0 : bo_prev + TB;  // tile i, i.e. i-1 of the next step
       bo_next = bo_next == 2 * TB ? 0 : bo_next + TB;
@@ -1145,7 +1189,7 @@ size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c) {
   return (o + ml) * sizeof(float);
 }
 
-template <int C, class SH, bool WIDE, bool PAGED>
+template <int C, class SH, bool WIDE, bool PAGED, bool MIXED = false>
 static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   const size_t lds = SH::lds_fixed() + ((prm.idx || PAGED)
                                             ? static_cast<size_t>(prm.split_rows) * sizeof(int)
@@ -1154,11 +1198,13 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   if (attr < lds) {
     hipError_t e;
     if constexpr (WIDE) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_wide_kernel<C, true, PAGED>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(mqa_wide_kernel<C, true, PAGED, MIXED>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_wide_kernel<C, false, PAGED>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(mqa_wide_kernel<C, false, PAGED, MIXED>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     } else {
       e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_kernel<C, SH::HP, PAGED>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -1172,8 +1218,8 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   {
     ProfScope ps(prm.idx ? "mqa_sparse" : "mqa_dense", s);
     if constexpr (WIDE) {
-      if (prm.idx) mqa_wide_kernel<C, true, PAGED><<<grid, SH::NT, lds, s>>>(q);
-      else mqa_wide_kernel<C, false, PAGED><<<grid, SH::NT, lds, s>>>(q);
+      if (prm.idx) mqa_wide_kernel<C, true, PAGED, MIXED><<<grid, SH::NT, lds, s>>>(q);
+      else mqa_wide_kernel<C, false, PAGED, MIXED><<<grid, SH::NT, lds, s>>>(q);
     }
     else mqa_kernel<C, SH::HP, PAGED><<<grid, SH::NT, lds, s>>>(q);
   }
@@ -1186,13 +1232,19 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
 }
 
 template <int C>
-static hipError_t launch_c(const MqaParams& prm, const MqaPlan& pl, int rows, hipStream_t s) {
+static hipError_t launch_c(const MqaParams& prm, const MqaPlan& pl, int rows, bool mixed,
+                           hipStream_t s) {
   if (pl.head_pairs != 2) return hipErrorInvalidValue;
   const bool paged = prm.pages.table != nullptr;
   if constexpr (C == 512) {
-    return paged ? launch_t<C, MqaWideShape<C>, true, true>(prm, rows, s)
-                 : launch_t<C, MqaWideShape<C>, true, false>(prm, rows, s);
+    using W = MqaWideShape<C>;
+    if (mixed)
+      return paged ? launch_t<C, W, true, true, true>(prm, rows, s)
+                   : launch_t<C, W, true, false, true>(prm, rows, s);
+    return paged ? launch_t<C, W, true, true>(prm, rows, s)
+                 : launch_t<C, W, true, false>(prm, rows, s);
   } else {
+    if (mixed) return hipErrorInvalidValue;  // mixed entries: head dim 512 only
     return paged ? launch_t<C, MqaShape<C, 2>, false, true>(prm, rows, s)
                  : launch_t<C, MqaShape<C, 2>, false, false>(prm, rows, s);
   }
@@ -1228,9 +1280,9 @@ hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& pl, hipStream_t s) {
   p.lse_out = a.lse_out;
   const int rows = a.B * a.nq;
   switch (a.c) {
-    case 128: return launch_c<128>(p, pl, rows, s);
-    case 256: return launch_c<256>(p, pl, rows, s);
-    case 512: return launch_c<512>(p, pl, rows, s);
+    case 128: return launch_c<128>(p, pl, rows, a.entry_mixed, s);
+    case 256: return launch_c<256>(p, pl, rows, a.entry_mixed, s);
+    case 512: return launch_c<512>(p, pl, rows, a.entry_mixed, s);
   }
   return hipErrorInvalidValue;
 }

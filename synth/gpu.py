@@ -70,12 +70,24 @@ def mxfp4_normalish(g, rows_shape, d, device, chunk=1 << 24):
     return packed.view(*rows_shape, d // 2), scales.view(*rows_shape, 4)
 
 
-def decode_cache_inputs(w, device="cuda", seed=None, key_fmt="e4m3"):
-    """As synth.inputs.decode_cache_inputs, on the device."""
+def mixed_entries(g, shape, c, r, device):
+    """Entry rows of c + r bytes: c - r E4M3 codes (as e4m3_normalish) then r bf16 values
+    (N(0,1)), the mixed-precision entry layout."""
+    codes = e4m3_normalish(g, tuple(shape) + (c - r,), device)
+    rope = bf16_normal(g, tuple(shape) + (r,), device).contiguous().view(torch.uint8)
+    return torch.cat([codes, rope], dim=-1).contiguous()
+
+
+def decode_cache_inputs(w, device="cuda", seed=None, key_fmt="e4m3", entry_fmt="bf16"):
+    """As synth.inputs.decode_cache_inputs, on the device (entry_fmt "mixed": entries as
+    mixed_entries rows)."""
     g = _gen(w.seed if seed is None else seed, device)
     B, N = w.B, w.N
     out = {"B": B, "N": N}
-    out["entries"] = bf16_normal(g, (B, N, w.c), device)
+    if entry_fmt == "mixed":
+        out["entries"] = mixed_entries(g, (B, N), w.c, w.r, device)
+    else:
+        out["entries"] = bf16_normal(g, (B, N, w.c), device)
     if w.mode == "csa" and key_fmt == "mxfp4":
         out["ikeys"], out["iscale"] = mxfp4_normalish(g, (B, N), w.d_I, device)
     elif w.mode == "csa":

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_helpers(L):
-    assert csa.version() == 10100
+    assert csa.version() == 10200
     c = _cfg()
     assert csa.weight_cols(c) == 5 * 512 + 4 * 128
     assert csa.tail_shape(c) == (8, 4 * 512 + 4 * 128)
