@@ -684,10 +684,12 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     if constexpr (LIST) e = s_idx[min(max(j - j0, 0), p.split_rows - 1)];
     resolve_e(j, e, ptr, mask, em);
   };
-  const int ncc = (C - p.r) >> 4;  // MIXED: 16-byte chunks of codes, then r/8 of RoPE dims
-  const int ebc = ncc + (p.r >> 3);
-  // wave `wave` loads rows wave, wave+8, wave+16, wave+24 of the tile, 16 bytes per lane (an
-  // entry row of a MIXED tile has ebc chunks: the lanes past them reload its last chunk)
+  // MIXED: an entry row holds ncc 16-byte chunks of codes, then r/8 chunks of RoPE dims.  Lane l
+  // fills bf16 chunk l of the LDS row either way: lanes below 2*ncc load the code chunk l/2 and
+  // widen its half l%2 (8 codes), the others load RoPE chunk l - ncc as is.
+  const int ncc = (C - p.r) >> 4;
+  const int mixed_ch = l < 2 * ncc ? (l >> 1) : l - ncc;
+  // wave `wave` loads rows wave, wave+8, wave+16, wave+24 of the tile, 16 bytes per lane
   auto gload = [&](const uint16_t* ptr, uint32_t em, u32x4 (&st)[LOADS]) {
     const uint64_t pv = reinterpret_cast<uint64_t>(ptr);
 #pragma unroll
@@ -697,7 +699,7 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
       const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv >> 32), rr);
       const uint64_t rp = (static_cast<uint64_t>(hi) << 32) | lo;
       int ch = l;
-      if constexpr (MIXED) ch = ((em >> rr) & 1u) ? min(l, ebc - 1) : l;
+      if constexpr (MIXED) ch = ((em >> rr) & 1u) ? mixed_ch : l;
       st[i] = *(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(rp) + ch);
     }
   };
@@ -807,33 +809,19 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   auto store_tile = [&](const u32x4 (&st)[LOADS], uint32_t em, uint32_t bo) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      if constexpr (MIXED) {
+      u32x4 v = st[i];
+      if constexpr (MIXED) {  // entry-row code lanes: 8 codes of dwords 2(l%2), 2(l%2)+1
         const int rr = wave + i * NW;
-        if ((em >> rr) & 1u) {  // entry row: 16 codes -> two bf16 chunks, or one RoPE chunk
-          unsigned char* row = smem + bo + static_cast<uint32_t>(rr * C * 2);
-          const int sw = swz(rr);
-          if (l < ncc) {
-            u32x4 lo, hi;
-#pragma unroll
-            for (int w = 0; w < 2; ++w) {
-              lo[2 * w] = __builtin_bit_cast(
-                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(st[i][w], 1.f, false));
-              lo[2 * w + 1] = __builtin_bit_cast(
-                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(st[i][w], 1.f, true));
-              hi[2 * w] = __builtin_bit_cast(
-                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(st[i][2 + w], 1.f, false));
-              hi[2 * w + 1] = __builtin_bit_cast(
-                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(st[i][2 + w], 1.f, true));
-            }
-            *reinterpret_cast<u32x4*>(row + (((2 * l) ^ sw) << 4)) = lo;
-            *reinterpret_cast<u32x4*>(row + (((2 * l + 1) ^ sw) << 4)) = hi;
-          } else if (l < ebc) {
-            *reinterpret_cast<u32x4*>(row + (((l + ncc) ^ sw) << 4)) = st[i];
-          }
-          continue;
-        }
+        const bool widen = ((em >> rr) & 1u) && l < 2 * ncc;
+        const uint32_t w0 = (l & 1) ? v[2] : v[0], w1 = (l & 1) ? v[3] : v[1];
+        const u32x4 wv = {
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
+        v = widen ? wv : v;
       }
-      *reinterpret_cast<u32x4*>(smem + st_off[i] + bo) = st[i];
+      *reinterpret_cast<u32x4*>(smem + st_off[i] + bo) = v;
     }
   };
   auto s_phase = [&](uint32_t bo) -> f32x16 {
