@@ -7,8 +7,9 @@ per-sequence state.
   and on a paged cache whose blocks are a random permutation of a larger pool gives identical
   bits: outputs, selected indices, and every entry, key and scale (read back through the table);
   the paged run is also checked stage-wise against the oracle.
-* Full-size decodes (128K CSA with E4M3 and MXFP4 keys, 1M CSA, 1M HCA) on paged copies of the
-  cache give the contiguous run's bits, with sequences of different lengths.
+* Full-size decodes (128K CSA with E4M3 and MXFP4 keys, 1M CSA, 1M HCA; bf16 and mixed-precision
+  entries) on paged copies of the cache give the contiguous run's bits, with sequences of
+  different lengths.
 * Prefix reuse: a second sequence maps the first sequence's leading blocks, rebuilds its window
   and compressor tail by re-running the last 128 prefix tokens (no entry is written, the shared
   blocks keep their bits), then continues with tokens of its own; its entries match a
@@ -197,15 +198,17 @@ def test_paged_layer_matches_contiguous(name, key_fmt, T):
                           keys, ksc, mx, out_p, idx_p, qs)
 
 
-@pytest.mark.parametrize("name,key_fmt,B", [("csa_decode_128k", "e4m3", 4),
-                                            ("csa_decode_128k", "mxfp4", 4),
-                                            ("csa_decode_1m", "e4m3", 1),
-                                            ("hca_decode_1m", None, 4)])
-def test_paged_decode_matches_contiguous(name, key_fmt, B):
+@pytest.mark.parametrize("name,key_fmt,B,ent", [("csa_decode_128k", "e4m3", 4, "bf16"),
+                                                ("csa_decode_128k", "mxfp4", 4, "bf16"),
+                                                ("csa_decode_1m", "e4m3", 1, "bf16"),
+                                                ("hca_decode_1m", None, 4, "bf16"),
+                                                ("csa_decode_128k", "e4m3", 4, "mixed"),
+                                                ("hca_decode_1m", None, 4, "mixed")])
+def test_paged_decode_matches_contiguous(name, key_fmt, B, ent):
     w = dataclasses.replace(S.WORKLOADS[name], B=B)
-    say("paged decode", name, key_fmt, "B=%d N=%d" % (B, w.N))
+    say("paged decode", name, key_fmt, ent, "B=%d N=%d" % (B, w.N))
     mx = key_fmt == "mxfp4"
-    x = G.decode_cache_inputs(w, DEV, key_fmt=key_fmt or "e4m3")
+    x = G.decode_cache_inputs(w, DEV, key_fmt=key_fmt or "e4m3", entry_fmt=ent)
     # sequences of different lengths, not multiples of the block size
     x["n_entries"] = torch.tensor([w.N - 37 * b - (5 if b else 0) for b in range(B)],
                                   dtype=torch.int32, device=DEV)
@@ -216,7 +219,8 @@ def test_paged_decode_matches_contiguous(name, key_fmt, B):
     cfg = csa.make_config(csa.MODE_CSA if csa_mode else csa.MODE_HCA, w.m, w.n_h, w.c, w.r,
                           x["inv_freq"], top_k=w.k, n_win=w.n_win, idx_heads=w.H_I,
                           idx_dim=w.d_I, softmax_scale=w.scale,
-                          idx_key_format=csa.IDX_MXFP4 if mx else csa.IDX_E4M3)
+                          idx_key_format=csa.IDX_MXFP4 if mx else csa.IDX_E4M3,
+                          entry_format=csa.ENT_MIXED if ent == "mixed" else csa.ENT_BF16)
     ws = workspace(csa.workspace_size(cfg, csa.OP_DECODE, B, 1, w.N))
     q = x["q"][:, 0].contiguous()
 
