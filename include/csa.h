@@ -14,8 +14,10 @@
  *  - No call allocates device memory and no call synchronizes: work is enqueued on the HIP
  *    stream passed as `stream` (a hipStream_t, NULL = the default stream) and the call returns.
  *  - Every tensor argument is a caller-owned DEVICE pointer to contiguous row-major memory,
- *    unless marked "host", 16-byte aligned (the kernels move 16-byte vectors).  The library
- *    keeps no pointer after a call returns.
+ *    unless marked "host".  Tensors the kernels move as 16-byte vectors must be 16-byte aligned
+ *    (CSA_ERR_INVALID_ARG otherwise): hidden states, weights, queries, indexer queries,
+ *    outputs, and the cache's entries, keys, window and tail.  The library keeps no pointer
+ *    after a call returns.
  *  - Scratch memory comes from the caller's `workspace` (device, 256-byte aligned) of
  *    `ws_bytes` bytes; csa_workspace_size() returns the bytes an operation needs.  Workspace
  *    contents on entry are irrelevant and are clobbered.

@@ -126,6 +126,7 @@ int check_cache(const csa_config_t* c, const csa_cache_t* k, bool need_keys, boo
   if (need_keys && (!k->idx_keys || !k->idx_scale))
     return fail(CSA_ERR_INVALID_ARG, "cache idx_keys/idx_scale is NULL");
   if (need_tail && !k->tail) return fail(CSA_ERR_INVALID_ARG, "cache tail is NULL");
+  if (int rc = check_aligned({k->entries, k->idx_keys, k->window, k->tail})) return rc;
   if (k->block_entries != 0) {
     const int be = k->block_entries;
     if (be < 0 || (be & (be - 1)))
@@ -412,6 +413,7 @@ int csa_compress(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* 
   if ((rc = check_weights(cfg, w))) return rc;
   if (B < 1 || T < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, T=%d must be >= 1", B, T);
   if (!H || !pos0) return fail(CSA_ERR_INVALID_ARG, "H or pos0 is NULL");
+  if ((rc = check_aligned({H, w ? w->w_cat : nullptr}))) return rc;
   const size_t need = ws_compress(cfg, B, T);
   if (!workspace || ws_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -430,6 +432,7 @@ int csa_index_topk(const csa_config_t* cfg, int32_t B, int32_t nq, const uint8_t
   if (B < 1 || nq < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, nq=%d must be >= 1", B, nq);
   if (!qi || !qi_scale || !wi || !pos || !idx_out)
     return fail(CSA_ERR_INVALID_ARG, "qi/qi_scale/wi/pos/idx_out is NULL");
+  if ((rc = check_aligned({qi}))) return rc;
   const size_t need = ws_index(cfg, B * nq, cache->n_max);
   if (!workspace || ws_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -447,6 +450,7 @@ int csa_sparse_mqa(const csa_config_t* cfg, int32_t B, int32_t nq, const uint16_
   if (B < 1 || nq < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, nq=%d must be >= 1", B, nq);
   if (!q || !idx || !pos || !sink || !out)
     return fail(CSA_ERR_INVALID_ARG, "q/idx/pos/sink/out is NULL");
+  if ((rc = check_aligned({q, out}))) return rc;
   if (cfg->top_k < 1 || cfg->top_k > csa::kMaxTopK)
     return fail(CSA_ERR_INVALID_ARG, "top_k=%d not in 1..%d", cfg->top_k, csa::kMaxTopK);
   const size_t need = ws_mqa(cfg, B * nq, max_list_sparse(cfg));
@@ -464,6 +468,7 @@ int hca_dense_mqa(const csa_config_t* cfg, int32_t B, int32_t nq, const uint16_t
   if ((rc = check_cache(cfg, cache, false, false))) return rc;
   if (B < 1 || nq < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, nq=%d must be >= 1", B, nq);
   if (!q || !pos || !sink || !out) return fail(CSA_ERR_INVALID_ARG, "q/pos/sink/out is NULL");
+  if ((rc = check_aligned({q, out}))) return rc;
   const size_t need = ws_mqa(cfg, B * nq, max_list_dense(cfg, cache->n_max));
   if (need && (!workspace || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -482,6 +487,7 @@ int csa_decode(const csa_config_t* cfg, int32_t B, const uint16_t* h_new, const 
   if (comp && (rc = check_weights(cfg, w))) return rc;
   if (B < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
   if (!pos || !q || !sink || !out) return fail(CSA_ERR_INVALID_ARG, "pos/q/sink/out is NULL");
+  if ((rc = check_aligned({h_new, q, qi, out, w ? w->w_cat : nullptr}))) return rc;
   if (is_csa(cfg) && (!qi || !qi_scale || !wi))
     return fail(CSA_ERR_INVALID_ARG, "CSA decode needs qi, qi_scale and wi");
   const size_t need = ws_layer(cfg, B, 1, cache->n_max, false, comp);
@@ -512,6 +518,7 @@ int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H
   if ((rc = check_weights(cfg, w))) return rc;
   if (B < 1 || T < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, T=%d must be >= 1", B, T);
   if (!H || !q || !sink || !out) return fail(CSA_ERR_INVALID_ARG, "H/q/sink/out is NULL");
+  if ((rc = check_aligned({H, q, qi, out, w ? w->w_cat : nullptr}))) return rc;
   if (is_csa(cfg) && (!qi || !qi_scale || !wi))
     return fail(CSA_ERR_INVALID_ARG, "CSA prefill needs qi, qi_scale and wi");
   if (cache->win_slots < T)
