@@ -19,7 +19,7 @@
 //   from the S^T accumulator layout).
 // LDS rows are unpadded with 16-byte chunks XOR-swizzled by row, which keeps both the row reads
 // of the S phase and the transposed reads of the PV phase free of bank conflicts.  With several
-// spans per query each workgroup writes (max, sum, unnormalised O) and a combine kernel merges
+// spans per query each workgroup writes (max, sum, O / sum in fp16) and a combine kernel merges
 // them in a fixed order, adds the sink and normalises; with one span the same epilogue runs in
 // place.  Spans are fixed by the plan, not by timing, so results are run-to-run deterministic.
 #include <algorithm>
@@ -44,7 +44,7 @@ struct MqaParams {
   PageMap pages;  // entries in a block pool (PAGED kernels)
   float scale_log2;
   int split_rows, n_splits, head_groups, n_work;
-  float* part;  // span partials, unnormalised O in the MFMA lane order (see mqa_kernel)
+  float* part;  // span partials: fp16 O / l of each span in the MFMA lane order (see mqa_kernel)
   float* ml;    // [rows, n_splits, n_heads, 2]: (max, sum) of each span
   uint16_t* out;
   float* lse_out;
@@ -64,6 +64,19 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // RNE
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two fp32 values as fp16 (round to nearest even), packed low first.
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ f32x4 unpack_h4(uint2 v) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const h4 x = __builtin_bit_cast(h4, v);
+  return f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+               static_cast<float>(x[3])};
 }
 
 // As store_out4, with cos/sin of the rotation angles of position t read from a table (pair i of
@@ -508,15 +521,19 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
       p.lse_out[orow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     // span partials in the MFMA lane order: per (row, span, head group, wave) DT*4 chunks of
-    // 64 lanes x 4 floats, so every store instruction writes 1 KiB contiguous
-    float* pw = p.part + ((((static_cast<size_t>(row) * p.n_splits + split) * p.head_groups + hg) *
-                            NW + wave) * (DT * 4) * 256);
+    // 64 lanes x 4 values, so every store instruction writes 512 bytes contiguous; the values
+    // are O / l of the span (|O / l| <= max |entry|) in fp16
+    uint16_t* pw = reinterpret_cast<uint16_t*>(p.part) +
+                   ((((static_cast<size_t>(row) * p.n_splits + split) * p.head_groups + hg) * NW +
+                     wave) * (DT * 4) * 256);
+    const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<f32x4*>(pw + ((dt * 4 + g4) * 64 + l) * 4) =
-            f32x4{acc[dt][4 * g4], acc[dt][4 * g4 + 1], acc[dt][4 * g4 + 2], acc[dt][4 * g4 + 3]};
+        *reinterpret_cast<uint2*>(pw + ((dt * 4 + g4) * 64 + l) * 4) =
+            uint2{pack_h2(acc[dt][4 * g4] * il, acc[dt][4 * g4 + 1] * il),
+                  pack_h2(acc[dt][4 * g4 + 2] * il, acc[dt][4 * g4 + 3] * il)};
     if (h == 0 && slice == 0) {
       float* mlp = p.ml + ((static_cast<size_t>(row) * p.n_splits + split) * p.n_heads + head) * 2;
       mlp[0] = m_ref;
@@ -1004,14 +1021,18 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     }
   } else {
     if (!head_ok) return;
-    float* pw = p.part + ((((static_cast<size_t>(row) * p.n_splits + split) * p.head_groups + hg) *
-                            NW + wave) * (DT * 4) * 256);
+    // span partials as in mqa_kernel: O / l of the span in fp16, MFMA lane order
+    uint16_t* pw = reinterpret_cast<uint16_t*>(p.part) +
+                   ((((static_cast<size_t>(row) * p.n_splits + split) * p.head_groups + hg) * NW +
+                     wave) * (DT * 4) * 256);
+    const float il = l_fin > 0.f ? 1.f / l_fin : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<f32x4*>(pw + ((dt * 4 + g4) * 64 + l) * 4) =
-            f32x4{acc[dt][4 * g4], acc[dt][4 * g4 + 1], acc[dt][4 * g4 + 2], acc[dt][4 * g4 + 3]};
+        *reinterpret_cast<uint2*>(pw + ((dt * 4 + g4) * 64 + l) * 4) =
+            uint2{pack_h2(acc[dt][4 * g4] * il, acc[dt][4 * g4 + 1] * il),
+                  pack_h2(acc[dt][4 * g4 + 2] * il, acc[dt][4 * g4 + 3] * il)};
     if (h == 0 && slice == 0) {
       float* mlp = p.ml + ((static_cast<size_t>(row) * p.n_splits + split) * p.n_heads + head) * 2;
       mlp[0] = m_fin;
@@ -1046,8 +1067,9 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
   const int t = p.pos ? p.pos[row] : (row % p.nq);
   const int dbase = slice * CS;
   const size_t span_stride = static_cast<size_t>(p.head_groups) * NW * (DT * 4) * 256;
-  const float* pw0 = p.part + (((static_cast<size_t>(row) * p.n_splits) * p.head_groups + hg) * NW +
-                               wave) * (DT * 4) * 256 + (cgp * CPT * 64 + l) * 4;
+  const uint16_t* pw0 = reinterpret_cast<const uint16_t*>(p.part) +
+                        (((static_cast<size_t>(row) * p.n_splits) * p.head_groups + hg) * NW +
+                         wave) * (DT * 4) * 256 + (cgp * CPT * 64 + l) * 4;
   const float* ml0 = p.ml + (static_cast<size_t>(row) * p.n_splits * p.n_heads + head) * 2;
   const size_t ml_stride = static_cast<size_t>(p.n_heads) * 2;
 
@@ -1069,7 +1091,7 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
       lv[j] = ml0[sp * ml_stride + 1];
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
-        ov[j][c] = *reinterpret_cast<const f32x4*>(pw0 + sp * span_stride + c * 256);
+        ov[j][c] = unpack_h4(*reinterpret_cast<const uint2*>(pw0 + sp * span_stride + c * 256));
     }
     float Mn = M;
 #pragma unroll
@@ -1087,7 +1109,7 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
       const float f = exp2f(mv[j] - M);
       lsum += lv[j] * f;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) o[c] += ov[j][c] * f;
+      for (int c = 0; c < CPT; ++c) o[c] += ov[j][c] * (lv[j] * f);  // partials are O / l
     }
   }
   const float den = lsum + ((p.sink && M != -INFINITY) ? exp2f(sink2 - M) : 0.f);
@@ -1130,7 +1152,7 @@ static int round_up(int x, int a) { return (x + a - 1) / a * a; }
 // workgroups sit on the same XCD and share the gathered rows through its L2.  Spans: chosen by
 // a small cost model with one resident workgroup of four waves per CU (fewer waves: several):
 // rounds of workgroups x (tiles x per-tile time + fixed cost), plus writing and re-reading the
-// fp32 partials when a query's list is split.
+// fp16 partials when a query's list is split.
 MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list) {
   MqaPlan pl;
   pl.head_pairs = 2;  // one instantiation: 64 heads (fewer heads leave waves idle)
@@ -1158,7 +1180,7 @@ MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list) {
     const int tiles = c == 512 ? ((sr + 63) / 64) * 2 : ((sr / 32) | 1);
     const double rounds = std::ceil(base * ns / slots);
     double tm = rounds * (tiles * t_tile + t_fixed);
-    if (ns > 1) tm += 2.0 * rows * ns * static_cast<double>(n_heads) * (c + 4) * 4.0 / bw + t_comb;
+    if (ns > 1) tm += 2.0 * rows * ns * static_cast<double>(n_heads) * (2.0 * c + 8.0) / bw + t_comb;
     if (tm < best * 0.97) {
       best = tm;
       pl.split_rows = sr;
@@ -1174,7 +1196,7 @@ size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c) {
   if (p.n_splits <= 1) return 0;
   const size_t o = static_cast<size_t>(rows) * p.n_splits * p.head_groups * p.heads_per_wg * c;
   const size_t ml = static_cast<size_t>(rows) * p.n_splits * n_heads * 2;
-  return (o + ml) * sizeof(float);
+  return o * sizeof(uint16_t) + ml * sizeof(float);  // fp16 partials, then fp32 (max, sum)
 }
 
 template <int C, class SH, bool WIDE, bool PAGED, bool MIXED = false>
@@ -1263,7 +1285,7 @@ hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& pl, hipStream_t s) {
   p.head_groups = pl.head_groups;
   p.part = a.part;
   p.ml = a.part + static_cast<size_t>(a.B) * a.nq * pl.n_splits * pl.head_groups *
-                      pl.heads_per_wg * a.c;
+                      pl.heads_per_wg * a.c / 2;  // after the fp16 partials
   p.out = a.out;
   p.lse_out = a.lse_out;
   const int rows = a.B * a.nq;
