@@ -133,3 +133,18 @@ def test_paged_cache_layout_is_checked(L, mode, be, bps, nb, n_max, msg):
     assert rc == -1
     err = csa.last_error()
     assert ("NULL" if msg is None else msg) in err, err
+
+
+def test_entry_format_is_checked(L):
+    b = ctypes.c_size_t()
+    ok = _cfg(entry_format=csa.ENT_MIXED)
+    assert L.csa_workspace_size(ctypes.byref(ok), csa.OP_DECODE, 1, 1, 16, ctypes.byref(b)) == 0
+    bad_dim = _cfg(entry_format=csa.ENT_MIXED, head_dim=256)
+    assert L.csa_workspace_size(ctypes.byref(bad_dim), csa.OP_DECODE, 1, 1, 16,
+                                ctypes.byref(b)) == -2  # CSA_ERR_UNSUPPORTED
+    assert "mixed" in csa.last_error()
+    bad_rope = _cfg(entry_format=csa.ENT_MIXED, rope_dim=40)
+    assert L.csa_workspace_size(ctypes.byref(bad_rope), csa.OP_DECODE, 1, 1, 16,
+                                ctypes.byref(b)) == -2
+    bad = _cfg(entry_format=5)
+    assert L.csa_workspace_size(ctypes.byref(bad), csa.OP_DECODE, 1, 1, 16, ctypes.byref(b)) == -1
