@@ -236,6 +236,8 @@ int csa_compress(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* 
  *            than top_k entries are visible all of them are selected and the rest is -1.
  *            Ties at the k-th score go to the lower index.
  *  score_out fp32 [B, nq, top_k] or NULL: I_{t,s} of each selected index (-inf for -1 pads).
+ * Caches of more than 32768 entries (n_max) take at most 4096 query rows (B*nq) per call
+ * (CSA_ERR_UNSUPPORTED otherwise; the same holds for csa_decode's B and csa_prefill's B*T).
  */
 int csa_index_topk(const csa_config_t* cfg, int32_t B, int32_t nq, const uint8_t* qi,
                    const float* qi_scale, const float* wi, const csa_cache_t* cache,

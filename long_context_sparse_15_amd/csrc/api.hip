@@ -168,6 +168,16 @@ int check_weights(const csa_config_t* c, const csa_weights_t* w) {
   return CSA_OK;
 }
 
+// Selection over rows longer than kRowTopkBigN entries runs on the multi-workgroup path, whose
+// per-call row count is bounded; longer rows in bigger batches are refused, not truncated.
+int check_index_rows(const csa_config_t* c, long long rows, int n_max) {
+  if (is_csa(c) && n_max > csa::kRowTopkBigN && rows > csa::kMultiMaxRows)
+    return fail(CSA_ERR_UNSUPPORTED, "%lld query rows over caches of n_max=%d > %d entries: "
+                "call with at most %d query rows at a time", rows, n_max, csa::kRowTopkBigN,
+                csa::kMultiMaxRows);
+  return CSA_OK;
+}
+
 // --- workspace layouts ----------------------------------------------------------------------
 size_t ws_compress(const csa_config_t* c, int B, int T) {
   return csa::compress_workspace(B, T, weight_cols(c));
@@ -380,6 +390,12 @@ int csa_workspace_size(const csa_config_t* cfg, int32_t op, int32_t B, int32_t n
   if (rc) return rc;
   if (!bytes) return fail(CSA_ERR_INVALID_ARG, "bytes is NULL");
   if (B < 1 || nq < 1 || n_max < 1) return fail(CSA_ERR_INVALID_ARG, "B, nq, n_max must be >= 1");
+  if (op == CSA_OP_INDEX_TOPK || op == CSA_OP_PREFILL || op == CSA_OP_DECODE) {
+    if ((rc = check_index_rows(cfg, op == CSA_OP_DECODE ? static_cast<long long>(B)
+                                                        : static_cast<long long>(B) * nq,
+                               n_max)))
+      return rc;
+  }
   switch (op) {
     case CSA_OP_COMPRESS: *bytes = ws_compress(cfg, B, nq); break;
     case CSA_OP_INDEX_TOPK:
@@ -433,6 +449,7 @@ int csa_index_topk(const csa_config_t* cfg, int32_t B, int32_t nq, const uint8_t
   if (!qi || !qi_scale || !wi || !pos || !idx_out)
     return fail(CSA_ERR_INVALID_ARG, "qi/qi_scale/wi/pos/idx_out is NULL");
   if ((rc = check_aligned({qi}))) return rc;
+  if ((rc = check_index_rows(cfg, static_cast<long long>(B) * nq, cache->n_max))) return rc;
   const size_t need = ws_index(cfg, B * nq, cache->n_max);
   if (!workspace || ws_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -486,6 +503,7 @@ int csa_decode(const csa_config_t* cfg, int32_t B, const uint16_t* h_new, const 
   if ((rc = check_cache(cfg, cache, is_csa(cfg), comp))) return rc;
   if (comp && (rc = check_weights(cfg, w))) return rc;
   if (B < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if ((rc = check_index_rows(cfg, B, cache->n_max))) return rc;
   if (!pos || !q || !sink || !out) return fail(CSA_ERR_INVALID_ARG, "pos/q/sink/out is NULL");
   if ((rc = check_aligned({h_new, q, qi, out, w ? w->w_cat : nullptr}))) return rc;
   if (is_csa(cfg) && (!qi || !qi_scale || !wi))
@@ -525,6 +543,7 @@ int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H
     return fail(CSA_ERR_INVALID_ARG, "prefill needs win_slots=%d >= T=%d", cache->win_slots, T);
   if (T / cfg->m > cache->n_max)
     return fail(CSA_ERR_INVALID_ARG, "T/m=%d entries exceed n_max=%d", T / cfg->m, cache->n_max);
+  if ((rc = check_index_rows(cfg, static_cast<long long>(B) * T, cache->n_max))) return rc;
   const size_t need = ws_layer(cfg, B, T, cache->n_max, true, true);
   if (!workspace || ws_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

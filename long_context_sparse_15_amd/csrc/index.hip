@@ -1166,7 +1166,9 @@ static int score_stride(int n_max) { return (n_max + 63) & ~63; }
 
 // Rows longer than the 1024-thread sampled select holds (and not too many of them) use the
 // multi-workgroup select (measured slower than the one-workgroup select at 32K entries).
-bool index_use_multi(int rows, int n_max) { return n_max > kRowTopkBigN && rows <= 4096; }
+bool index_use_multi(int rows, int n_max) {
+  return n_max > kRowTopkBigN && rows <= kMultiMaxRows;
+}
 
 static int collect_chunks(int n_max) { return (n_max + kCollectChunk - 1) / kCollectChunk; }
 

@@ -62,6 +62,7 @@ struct IndexArgs {
   float* score_out;       // [rows, k] or nullptr
 };
 // Rows longer than kRowTopkBigN (and not too many) use the multi-workgroup select.
+constexpr int kMultiMaxRows = 4096;
 bool index_use_multi(int rows, int n_max);
 size_t index_topk_workspace(int rows, int n_max, int k);
 void index_topk_layout(IndexArgs& a, void* ws, int rows);  // needs a.n_max and a.k set

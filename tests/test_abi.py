@@ -148,3 +148,18 @@ def test_entry_format_is_checked(L):
                                 ctypes.byref(b)) == -2
     bad = _cfg(entry_format=5)
     assert L.csa_workspace_size(ctypes.byref(bad), csa.OP_DECODE, 1, 1, 16, ctypes.byref(b)) == -1
+
+
+def test_long_rows_in_big_batches_are_refused(L):
+    """Selection over caches of more than 32768 entries takes at most 4096 query rows a call."""
+    c = _cfg()
+    b = ctypes.c_size_t()
+    assert L.csa_workspace_size(ctypes.byref(c), csa.OP_INDEX_TOPK, 1, 4096, 65536,
+                                ctypes.byref(b)) == 0
+    assert L.csa_workspace_size(ctypes.byref(c), csa.OP_INDEX_TOPK, 1, 4097, 65536,
+                                ctypes.byref(b)) == -2
+    assert "4096" in csa.last_error()
+    assert L.csa_workspace_size(ctypes.byref(c), csa.OP_PREFILL, 2, 4096, 65536,
+                                ctypes.byref(b)) == -2
+    assert L.csa_workspace_size(ctypes.byref(c), csa.OP_INDEX_TOPK, 1, 65536, 32768,
+                                ctypes.byref(b)) == 0   # rows of at most 32768 entries: any count
