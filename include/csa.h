@@ -80,7 +80,11 @@ extern "C" {
  *   1 <= n_heads <= 128;  n_win in 1..1024;
  *   CSA: idx_dim in {32, 64, 128}, 1 <= idx_heads <= 64, 1 <= top_k <= 4096, m >= 1,
  *        idx_key_format CSA_IDX_E4M3 or CSA_IDX_MXFP4;
- *   HCA: m >= 1;  hidden (compressor only) a positive multiple of 32. */
+ *   HCA: m >= 1;  hidden (compressor only) a positive multiple of 32;
+ *   entry_format CSA_ENT_BF16 or CSA_ENT_MIXED (the latter: head_dim 512 and rope_dim a multiple
+ *   of 16, CSA_ERR_UNSUPPORTED otherwise);
+ *   projections only: hidden and q_rank multiples of 64; out_groups dividing n_heads with
+ *   (n_heads/out_groups)*head_dim and out_groups*out_rank multiples of 64. */
 typedef struct csa_config {
   int32_t mode;       /* CSA_MODE_CSA or CSA_MODE_HCA */
   int32_t m;          /* compression ratio: 4 in CSA layers, 128 (m') in HCA layers */
