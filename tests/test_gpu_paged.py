@@ -351,3 +351,64 @@ def test_prefix_reuse_with_tail_recompute(name):
     qs = sorted(set([P, P + 1, TB - 1] + list(rng.integers(P, TB, 10))))
     _check_against_oracle(w, xb, TB, n_ent, host_bits(ent_b), host_bits(ct_b["window"][0]),
                           slots, keys, ksc, False, full_out, full_idx, qs)
+
+
+def test_paged_ragged_batch_matches_contiguous():
+    """Three sequences on one block table, appended by csa_compress at different positions (one
+    restarting from 0), then one csa_decode step each at its own position: the paged cache
+    gives the contiguous cache's entries, keys, scales, window rows and outputs bit for bit."""
+    w = S.shrink(S.WORKLOADS["tiny_csa"], B=3)
+    say("paged ragged batch", w.name)
+    x = S.layer_inputs(w, T=200)
+    d = {k: dev(x[k]) for k in x if isinstance(x[k], np.ndarray)}
+    cfg = config_for(w, d["inv_freq"])
+    be = _block_entries(w)
+    bps = (216 // w.m + be) // be + 1
+    n_max = bps * be
+    slots = 256
+    table, n_blocks = _perm_table(3, bps, 4, seed=9)
+    tr, tc = csa.tail_shape(cfg)
+
+    def make(paged):
+        lead = (n_blocks * be,) if paged else (3, n_max)
+        ct = dict(entries=torch.zeros(lead + (w.c,), dtype=torch.int16, device=DEV),
+                  window=torch.zeros((3, slots, w.c), dtype=torch.int16, device=DEV),
+                  n_entries=torch.zeros(3, dtype=torch.int32, device=DEV),
+                  tail=torch.zeros((3, tr, tc), dtype=torch.float32, device=DEV),
+                  idx_keys=torch.zeros(lead + (w.d_I,), dtype=torch.uint8, device=DEV),
+                  idx_scale=torch.zeros(lead, dtype=torch.float32, device=DEV))
+        kw = dict(block_table=dev(table), block_entries=be, n_blocks=n_blocks) if paged else {}
+        return csa.make_cache(n_max, slots, **ct, **kw), ct
+
+    weights = _weights(w, d)
+    ws = workspace(max(csa.workspace_size(cfg, csa.OP_COMPRESS, 3, 120, n_max),
+                       csa.workspace_size(cfg, csa.OP_DECODE, 3, 1, n_max)))
+    runs = []
+    for paged in (False, True):
+        cache, ct = make(paged)
+        pos0 = torch.zeros(3, dtype=torch.int32, device=DEV)
+        csa.compress(cfg, d["H"][:, :120].contiguous(), pos0, weights, cache, ws)
+        ct["n_entries"][1] = 0                       # sequence 1 restarts from position 0
+        pos0 = torch.tensor([120, 0, 120], dtype=torch.int32, device=DEV)
+        csa.compress(cfg, d["H"][:, 120:200].contiguous(), pos0, weights, cache, ws)
+        pos = torch.tensor([199, 79, 199], dtype=torch.int32, device=DEV)
+        out = torch.empty((3, w.n_h, w.c), dtype=torch.bfloat16, device=DEV)
+        idx = torch.full((3, w.k), -7, dtype=torch.int32, device=DEV)
+        csa.decode(cfg, cache, pos, d["q"][:, 199].contiguous(), d["sink"], out, ws,
+                   qi=d["qi"][:, 199].contiguous(), qi_scale=d["qi_scale"][:, 199].contiguous(),
+                   wi=d["wi"][:, 199].contiguous(), idx_out=idx)
+        torch.cuda.synchronize()
+        runs.append((ct, out, idx))
+    (cc, oc, ic), (cp, op, ip) = runs
+    assert torch.equal(cp["n_entries"], cc["n_entries"])
+    for k in ("entries", "idx_keys", "idx_scale"):
+        logical = _from_pool(cp[k], table, be)
+        for b in range(3):
+            n = int(cc["n_entries"][b])
+            got, ref = logical[b, :n], cc[k][b, :n]
+            if k == "idx_scale":
+                got, ref = got.view(torch.int32), ref.view(torch.int32)
+            assert torch.equal(got, ref), (k, b)
+    assert torch.equal(cp["window"], cc["window"])
+    assert torch.equal(op.view(torch.int16), oc.view(torch.int16))
+    assert torch.equal(ip, ic)
