@@ -1,8 +1,8 @@
 """GPU parity of the projections on either side of attention (csa_query_proj,
 csa_output_proj) against the oracle: a tiny layer shape, the V4-Flash shape (hidden 4096,
 r_q 1024, 64 heads x 512, indexer 64 x 128, 8 output groups of rank 1024) on sampled tokens,
-HCA mode (no indexer query), and a token count that spans two row chunks of the query
-up-projection's fp32 buffer."""
+HCA mode (no indexer query), and a longer token run (1600 rows: several GEMM row tiles and a
+ragged last one)."""
 import numpy as np
 import pytest
 import torch
@@ -32,7 +32,7 @@ def _cfg(mode, D, r_q, n_h, c, H_I, d_I, g=1, r_o=64):
     ("csa", 1, 37, 512, 128, 8, 128, 4, 64, None),
     ("hca", 2, 20, 512, 192, 8, 128, 0, 0, None),
     ("csa", 2, 300, 4096, 1024, 64, 512, 64, 128, [0, 1, 150, 299, 300, 451, 599]),
-    ("csa", 1, 1600, 4096, 1024, 64, 512, 64, 128, [0, 1535, 1536, 1599]),  # two row chunks
+    ("csa", 1, 1600, 4096, 1024, 64, 512, 64, 128, [0, 1535, 1536, 1599]),  # ragged last tile
 ])
 def test_query_proj_parity(case):
     mode, B, T, D, r_q, n_h, c, H_I, d_I, rows = case
