@@ -83,6 +83,8 @@ def test_query_proj_parity(case):
     (1, 45, 512, 8, 128, 2, 64, None),
     (2, 300, 4096, 64, 512, 8, 1024, [0, 7, 299, 300, 599]),
     (1, 64, 512, 8, 128, 1, 128, None),
+    # 16 groups of rank 1024: the z buffer takes 8192 rows per chunk, so 9000 rows run in two
+    (1, 9000, 512, 16, 512, 16, 1024, [0, 8191, 8192, 8999]),
 ])
 def test_output_proj_parity(case):
     B, T, D, n_h, c, g, r_o, rows = case
