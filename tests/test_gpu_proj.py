@@ -10,7 +10,7 @@ import torch
 import long_context_sparse_15_amd as csa
 import oracle as O
 from synth import inputs as S
-from gpu_common import DEV, check_close, dev, host_bits, say, workspace
+from gpu_common import DEV, check_close, check_selection, dev, host_bits, say, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +104,88 @@ def test_output_proj_parity(case):
     _, y_ref = O.grouped_output_projection(o.reshape(B * T, n_h, c)[sel], w_down, w_proj, g)
     y_h = O.bf16_bits_to_f64(host_bits(y).reshape(B * T, D)[sel])
     check_close(y_h, O.bf16_bits_to_f64(y_ref), "y")
+
+
+def test_layer_from_hidden_states_to_output():
+    """The projections around the attention path, chained: hidden states -> csa_query_proj ->
+    csa_prefill (compressor, indexer, top-k, sparse MQA) -> csa_output_proj -> layer output, at
+    the production head shape.  Each stage is checked against the oracle on the GPU's own
+    inputs to that stage (sampled tokens)."""
+    import dataclasses
+    w = dataclasses.replace(S.WORKLOADS["tiny_csa"], name="tiny_csa_wide", c=512, n_h=64,
+                            H_I=64, d_I=128, T=512)
+    T, D, r_q, g, r_o = 512, w.D, 256, 8, 128
+    say("hidden states to layer output", T)
+    x = S.layer_inputs(w, T=T)
+    rng = np.random.default_rng(43)
+    w_dq = S.bf16_normal(rng, (r_q, D), std=D ** -0.5)
+    w_uq = S.bf16_normal(rng, (w.n_h * w.c, r_q), std=r_q ** -0.5)
+    w_w = S.bf16_normal(rng, (w.H_I, D), std=D ** -0.5)
+    w_iuq = S.bf16_normal(rng, (w.H_I * w.d_I, r_q), std=r_q ** -0.5)
+    gamma_q = (1.0 + 0.1 * rng.standard_normal(w.c)).astype(np.float32)
+    width = w.n_h // g * w.c
+    w_down = S.bf16_normal(rng, (g, r_o, width), std=width ** -0.5)
+    w_proj = S.bf16_normal(rng, (D, g * r_o), std=(g * r_o) ** -0.5)
+    inv = dev(x["inv_freq"])
+    cfg = csa.make_config(csa.MODE_CSA, w.m, w.n_h, w.c, w.r, inv, top_k=w.k, n_win=w.n_win,
+                          idx_heads=w.H_I, idx_dim=w.d_I, hidden=D, softmax_scale=w.scale,
+                          q_rank=r_q, out_groups=g, out_rank=r_o)
+    H = dev(x["H"][:, :T])
+    # 1. queries from the hidden states
+    q = torch.empty((1, T, w.n_h, w.c), dtype=torch.int16, device=DEV)
+    qi = torch.empty((1, T, w.H_I, w.d_I), dtype=torch.uint8, device=DEV)
+    qs = torch.empty((1, T, w.H_I), dtype=torch.float32, device=DEV)
+    wi = torch.empty((1, T, w.H_I), dtype=torch.float32, device=DEV)
+    wq = csa.make_qproj_weights(dev(w_dq), dev(w_uq), dev(gamma_q), w_w=dev(w_w),
+                                w_iuq=dev(w_iuq))
+    n_max = T // w.m + 32
+    ws = workspace(max(csa.workspace_size(cfg, csa.OP_QUERY_PROJ, 1, T, n_max),
+                       csa.workspace_size(cfg, csa.OP_PREFILL, 1, T, n_max),
+                       csa.workspace_size(cfg, csa.OP_OUTPUT_PROJ, 1, T, n_max)))
+    csa.query_proj(cfg, H, wq, q, ws, qi_out=qi, qi_scale_out=qs, wi_out=wi)
+    # 2. the attention layer on those queries
+    tr, tc = csa.tail_shape(cfg)
+    ct = dict(entries=torch.zeros((1, n_max, w.c), dtype=torch.int16, device=DEV),
+              window=torch.zeros((1, T, w.c), dtype=torch.int16, device=DEV),
+              n_entries=torch.zeros(1, dtype=torch.int32, device=DEV),
+              tail=torch.zeros((1, tr, tc), dtype=torch.float32, device=DEV),
+              idx_keys=torch.zeros((1, n_max, w.d_I), dtype=torch.uint8, device=DEV),
+              idx_scale=torch.zeros((1, n_max), dtype=torch.float32, device=DEV))
+    cache = csa.make_cache(n_max, T, **ct)
+    d = {k: dev(x[k]) for k in ("W", "Ba", "Bb", "BIa", "BIb", "gamma", "gamma_win", "sink")}
+    weights = csa.make_weights(d["W"], d["Ba"], d["gamma"], d["gamma_win"], bias_b=d["Bb"],
+                               bias_ia=d["BIa"], bias_ib=d["BIb"])
+    out = torch.empty((1, T, w.n_h, w.c), dtype=torch.int16, device=DEV)
+    idx = torch.full((1, T, w.k), -7, dtype=torch.int32, device=DEV)
+    csa.prefill(cfg, H, weights, cache, q, d["sink"], out, ws, qi=qi, qi_scale=qs, wi=wi,
+                idx_out=idx)
+    # 3. the layer output
+    y = torch.empty((1, T, D), dtype=torch.int16, device=DEV)
+    csa.output_proj(cfg, out, csa.make_oproj_weights(dev(w_down), dev(w_proj)), y, ws)
+    torch.cuda.synchronize()
+
+    sel = np.array([0, 3, 4, 130, 255, 256, 400, T - 1])
+    hh = x["H"][0, :T]
+    ref = O.query_projections(hh[sel], w_dq, w_w, w_uq, w_iuq, gamma_q, w.n_h, w.c, w.H_I,
+                              w.d_I, 1e-6)
+    q_h = host_bits(q)[0]
+    check_close(O.bf16_bits_to_f64(q_h[sel]), O.bf16_bits_to_f64(ref["q"]), "q")
+    qi_h, qs_h, wi_h = qi.cpu().numpy()[0], qs.cpu().numpy()[0], wi.cpu().numpy()[0]
+    check_close(wi_h[sel], ref["wi"], "w^I", atol=1e-5, rtol=1e-4)
+    n_ent = T // w.m
+    ent = host_bits(ct["entries"][0])
+    win = host_bits(ct["window"][0])
+    keys = ct["idx_keys"][0].cpu().numpy()[:n_ent]
+    ksc = ct["idx_scale"][0].cpu().numpy()[:n_ent]
+    idx_h = idx[0].cpu().numpy()
+    out_h = host_bits(out)[0]
+    for t in sel:
+        n_vis = O.visible_entries(int(t), w.m, n_ent)
+        sc = O.index_scores(qi_h[t], qs_h[t], wi_h[t], keys, ksc, n_vis)
+        check_selection(idx_h[t], sc, w.k, "token %d selection" % t)
+        rows = np.concatenate([ent[idx_h[t][:min(w.k, n_vis)]],
+                               win[O.window_tokens(int(t), w.n_win)]])
+        att, _ = O.attend(q_h[t], rows, x["sink"], w.scale, int(t), x["inv_freq"])
+        check_close(O.bf16_bits_to_f64(out_h[t]), att, "token %d attention" % t)
+    _, y_ref = O.grouped_output_projection(out_h[sel], w_down, w_proj, g)
+    check_close(O.bf16_bits_to_f64(host_bits(y)[0][sel]), O.bf16_bits_to_f64(y_ref), "y")
