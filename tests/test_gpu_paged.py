@@ -412,3 +412,50 @@ def test_paged_ragged_batch_matches_contiguous():
     assert torch.equal(cp["window"], cc["window"])
     assert torch.equal(op.view(torch.int16), oc.view(torch.int16))
     assert torch.equal(ip, ic)
+
+
+@pytest.mark.parametrize("name", ["csa_decode_128k", "hca_decode_1m"])
+def test_paged_decode_short_and_empty_sequences(name):
+    """Sequences with no closed entry, fewer visible entries than k, a partial last block and a
+    full cache, decoded from a paged cache: bit-equal to the contiguous cache."""
+    w = dataclasses.replace(S.WORKLOADS[name], B=4, N=4096)
+    say("paged short/empty sequences", name)
+    x = G.decode_cache_inputs(w, DEV)
+    x["n_entries"] = torch.tensor([0, 5, 300, w.N], dtype=torch.int32, device=DEV)
+    csa_mode = w.mode == "csa"
+    be = _block_entries(w)
+    table, n_blocks = _perm_table(4, w.N // be, 2, seed=21)
+    cfg = csa.make_config(csa.MODE_CSA if csa_mode else csa.MODE_HCA, w.m, w.n_h, w.c, w.r,
+                          x["inv_freq"], top_k=w.k, n_win=w.n_win, idx_heads=w.H_I,
+                          idx_dim=w.d_I, softmax_scale=w.scale)
+    ws = workspace(csa.workspace_size(cfg, csa.OP_DECODE, 4, 1, w.N))
+    q = x["q"][:, 0].contiguous()
+    pools = {"entries": _to_pool(x["entries"], table, n_blocks, be)}
+    if csa_mode:
+        pools["idx_keys"] = _to_pool(x["ikeys"], table, n_blocks, be)
+        pools["idx_scale"] = _to_pool(x["iscale"], table, n_blocks, be)
+    caches = [csa.make_cache(w.N, w.n_win, x["entries"], x["window"], x["n_entries"],
+                             idx_keys=x.get("ikeys"), idx_scale=x.get("iscale")),
+              csa.make_cache(w.N, w.n_win, pools["entries"], x["window"], x["n_entries"],
+                             idx_keys=pools.get("idx_keys"), idx_scale=pools.get("idx_scale"),
+                             block_table=dev(table), block_entries=be, n_blocks=n_blocks)]
+    res = []
+    for cache in caches:
+        out = torch.empty((4, w.n_h, w.c), dtype=torch.bfloat16, device=DEV)
+        idx = torch.full((4, max(w.k, 1)), -7, dtype=torch.int32, device=DEV)
+        if csa_mode:
+            csa.decode(cfg, cache, x["pos"], q, x["sink"], out, ws, qi=x["qi"],
+                       qi_scale=x["qi_scale"], wi=x["wi"], idx_out=idx)
+        else:
+            csa.decode(cfg, cache, x["pos"], q, x["sink"], out, ws)
+        torch.cuda.synchronize()
+        res.append((out, idx))
+    (oc, ic), (op, ip) = res
+    assert torch.equal(op.view(torch.int16), oc.view(torch.int16))
+    if csa_mode:
+        assert torch.equal(ip, ic)
+        ih = ic.cpu().numpy()
+        assert np.all(ih[0] == -1)                                  # nothing visible
+        assert np.array_equal(ih[1, :5], np.arange(5)) and np.all(ih[1, 5:] == -1)
+        assert np.array_equal(ih[2, :300], np.arange(300)) and np.all(ih[2, 300:] == -1)
+    assert torch.isfinite(oc.float()).all()
