@@ -116,6 +116,17 @@ int check_aligned(std::initializer_list<const void*> ptrs) {
   return CSA_OK;
 }
 
+// The caller's workspace: at least `need` bytes (CSA_ERR_WORKSPACE) and 256-byte aligned as
+// documented (the kernels move scores and partials in 16-byte vectors from 256-byte aligned
+// sub-buffers).  A NULL workspace is accepted when the operation needs none.
+int check_workspace(const void* ws, size_t ws_bytes, size_t need) {
+  if (need && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return fail(CSA_ERR_INVALID_ARG, "workspace %p is not 256-byte aligned", ws);
+  return CSA_OK;
+}
+
 int check_cache(const csa_config_t* c, const csa_cache_t* k, bool need_keys, bool need_tail) {
   if (!k) return fail(CSA_ERR_INVALID_ARG, "cache is NULL");
   if (k->n_max < 1) return fail(CSA_ERR_INVALID_ARG, "cache n_max=%d < 1", k->n_max);
@@ -185,22 +196,23 @@ size_t ws_compress(const csa_config_t* c, int B, int T) {
 size_t ws_index(const csa_config_t* c, int rows, int n_max) {
   return csa::index_topk_workspace(rows, n_max, c->top_k);
 }
-size_t ws_mqa(const csa_config_t* c, int rows, int max_list) {
-  const csa::MqaPlan p = csa::plan_mqa(rows, c->n_heads, c->head_dim, max_list);
-  return csa::mqa_workspace(p, rows, c->n_heads, c->head_dim);
+size_t ws_mqa(const csa_config_t* c, int B, int nq, int max_list) {
+  const csa::MqaPlan p = csa::plan_mqa(nq, c->n_heads, c->head_dim, max_list);
+  return csa::mqa_workspace(p, B * nq, c->n_heads, c->head_dim);
 }
 int max_list_sparse(const csa_config_t* c) { return c->top_k + c->n_win; }
 int max_list_dense(const csa_config_t* c, int n_max) { return n_max + c->n_win; }
 
-size_t ws_attend(const csa_config_t* c, int rows, int n_max) {
-  return is_csa(c) ? ws_mqa(c, rows, max_list_sparse(c)) : ws_mqa(c, rows, max_list_dense(c, n_max));
+size_t ws_attend(const csa_config_t* c, int B, int nq, int n_max) {
+  return is_csa(c) ? ws_mqa(c, B, nq, max_list_sparse(c))
+                   : ws_mqa(c, B, nq, max_list_dense(c, n_max));
 }
 
 // decode / prefill: [idx buffer (CSA)] + union(compress, index, attend)
 size_t ws_layer(const csa_config_t* c, int B, int T, int n_max, bool prefill, bool compress) {
   const int rows = B * T;
   size_t idx = is_csa(c) ? align256(static_cast<size_t>(rows) * c->top_k * 4) : 0;
-  size_t u = ws_attend(c, rows, n_max);
+  size_t u = ws_attend(c, B, T, n_max);
   if (is_csa(c)) u = std::max(u, ws_index(c, rows, n_max));
   if (compress) u = std::max(u, ws_compress(c, B, prefill ? T : 1));
   return idx + u;
@@ -316,7 +328,7 @@ int run_attend(const csa_config_t* c, int B, int nq, const uint16_t* q, const cs
   csa::MqaArgs a;
   fill_mqa_args(a, c, B, nq, q, k, idx, pos, sink, out, lse_out, ws);
   const int max_list = idx ? max_list_sparse(c) : max_list_dense(c, k->n_max);
-  const csa::MqaPlan p = csa::plan_mqa(B * nq, c->n_heads, c->head_dim, max_list);
+  const csa::MqaPlan p = csa::plan_mqa(nq, c->n_heads, c->head_dim, max_list);
   hipError_t e = csa::launch_mqa(a, p, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "attention launch");
 }
@@ -402,8 +414,8 @@ int csa_workspace_size(const csa_config_t* cfg, int32_t op, int32_t B, int32_t n
       if (!is_csa(cfg)) return fail(CSA_ERR_INVALID_ARG, "index_topk needs CSA mode");
       *bytes = ws_index(cfg, B * nq, n_max);
       break;
-    case CSA_OP_SPARSE_MQA: *bytes = ws_mqa(cfg, B * nq, max_list_sparse(cfg)); break;
-    case CSA_OP_HCA_MQA: *bytes = ws_mqa(cfg, B * nq, max_list_dense(cfg, n_max)); break;
+    case CSA_OP_SPARSE_MQA: *bytes = ws_mqa(cfg, B, nq, max_list_sparse(cfg)); break;
+    case CSA_OP_HCA_MQA: *bytes = ws_mqa(cfg, B, nq, max_list_dense(cfg, n_max)); break;
     case CSA_OP_DECODE: *bytes = ws_layer(cfg, B, 1, n_max, false, true); break;
     case CSA_OP_PREFILL: *bytes = ws_layer(cfg, B, nq, n_max, true, true); break;
     case CSA_OP_QUERY_PROJ:
@@ -431,8 +443,7 @@ int csa_compress(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* 
   if (!H || !pos0) return fail(CSA_ERR_INVALID_ARG, "H or pos0 is NULL");
   if ((rc = check_aligned({H, w ? w->w_cat : nullptr}))) return rc;
   const size_t need = ws_compress(cfg, B, T);
-  if (!workspace || ws_bytes < need)
-    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   return run_compress(cfg, B, T, H, pos0, w, cache, workspace,
                       reinterpret_cast<hipStream_t>(stream));
 }
@@ -451,8 +462,7 @@ int csa_index_topk(const csa_config_t* cfg, int32_t B, int32_t nq, const uint8_t
   if ((rc = check_aligned({qi}))) return rc;
   if ((rc = check_index_rows(cfg, static_cast<long long>(B) * nq, cache->n_max))) return rc;
   const size_t need = ws_index(cfg, B * nq, cache->n_max);
-  if (!workspace || ws_bytes < need)
-    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   return run_index(cfg, B, nq, qi, qi_scale, wi, cache, pos, idx_out, score_out, workspace,
                    reinterpret_cast<hipStream_t>(stream));
 }
@@ -470,9 +480,8 @@ int csa_sparse_mqa(const csa_config_t* cfg, int32_t B, int32_t nq, const uint16_
   if ((rc = check_aligned({q, out}))) return rc;
   if (cfg->top_k < 1 || cfg->top_k > csa::kMaxTopK)
     return fail(CSA_ERR_INVALID_ARG, "top_k=%d not in 1..%d", cfg->top_k, csa::kMaxTopK);
-  const size_t need = ws_mqa(cfg, B * nq, max_list_sparse(cfg));
-  if (need && (!workspace || ws_bytes < need))
-    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const size_t need = ws_mqa(cfg, B, nq, max_list_sparse(cfg));
+  if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   return run_attend(cfg, B, nq, q, cache, idx, pos, sink, out, lse_out, workspace,
                     reinterpret_cast<hipStream_t>(stream));
 }
@@ -486,9 +495,8 @@ int hca_dense_mqa(const csa_config_t* cfg, int32_t B, int32_t nq, const uint16_t
   if (B < 1 || nq < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, nq=%d must be >= 1", B, nq);
   if (!q || !pos || !sink || !out) return fail(CSA_ERR_INVALID_ARG, "q/pos/sink/out is NULL");
   if ((rc = check_aligned({q, out}))) return rc;
-  const size_t need = ws_mqa(cfg, B * nq, max_list_dense(cfg, cache->n_max));
-  if (need && (!workspace || ws_bytes < need))
-    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const size_t need = ws_mqa(cfg, B, nq, max_list_dense(cfg, cache->n_max));
+  if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   return run_attend(cfg, B, nq, q, cache, nullptr, pos, sink, out, lse_out, workspace,
                     reinterpret_cast<hipStream_t>(stream));
 }
@@ -509,8 +517,7 @@ int csa_decode(const csa_config_t* cfg, int32_t B, const uint16_t* h_new, const 
   if (is_csa(cfg) && (!qi || !qi_scale || !wi))
     return fail(CSA_ERR_INVALID_ARG, "CSA decode needs qi, qi_scale and wi");
   const size_t need = ws_layer(cfg, B, 1, cache->n_max, false, comp);
-  if (!workspace || ws_bytes < need)
-    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   unsigned char* p = static_cast<unsigned char*>(workspace);
   int32_t* idx = nullptr;
@@ -545,8 +552,7 @@ int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H
     return fail(CSA_ERR_INVALID_ARG, "T/m=%d entries exceed n_max=%d", T / cfg->m, cache->n_max);
   if ((rc = check_index_rows(cfg, static_cast<long long>(B) * T, cache->n_max))) return rc;
   const size_t need = ws_layer(cfg, B, T, cache->n_max, true, true);
-  if (!workspace || ws_bytes < need)
-    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   unsigned char* p = static_cast<unsigned char*>(workspace);
   int32_t* idx = nullptr;
@@ -577,13 +583,12 @@ int csa_query_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t
   if (csa_mode && (!w->w_w || !w->w_iuq || !qi_out || !qi_scale_out || !wi_out))
     return fail(CSA_ERR_INVALID_ARG, "CSA needs w_w, w_iuq, qi_out, qi_scale_out and wi_out");
   if ((rc = check_aligned({H, w->w_dq, w->w_w, w->w_uq, w->w_iuq, w->gamma_q, q_out, qi_out,
-                           qi_scale_out, wi_out, workspace})))
+                           qi_scale_out, wi_out})))
     return rc;
   const int BT = B * T;
   const size_t need = csa::query_proj_workspace(BT, cfg->q_rank, cfg->n_heads, cfg->head_dim,
                                                 csa_mode ? cfg->idx_heads : 0, cfg->idx_dim);
-  if (!workspace || ws_bytes < need)
-    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   csa::QueryProjArgs a;
   a.BT = BT;
   a.D = cfg->hidden;
@@ -617,11 +622,10 @@ int csa_output_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_
   if (B < 1 || T < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d, T=%d must be >= 1", B, T);
   if (!O || !w || !w->w_down || !w->w_proj || !y_out)
     return fail(CSA_ERR_INVALID_ARG, "O, w_down, w_proj or y_out is NULL");
-  if ((rc = check_aligned({O, w->w_down, w->w_proj, y_out, workspace}))) return rc;
+  if ((rc = check_aligned({O, w->w_down, w->w_proj, y_out}))) return rc;
   const int BT = B * T;
   const size_t need = csa::output_proj_workspace(BT, cfg->out_groups, cfg->out_rank);
-  if (!workspace || ws_bytes < need)
-    return fail(CSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   csa::OutputProjArgs a;
   a.BT = BT;
   a.D = cfg->hidden;

@@ -273,14 +273,9 @@ __global__ __launch_bounds__(G2_THREADS) void gemm_tn_bf16_256_kernel(
 template <typename OutT>
 static hipError_t launch_gemm_256(const uint16_t* A, int lda, const uint16_t* W, int ldw, OutT* C,
                                   int ldc, int M, int N, int K, hipStream_t s) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tn_bf16_256_kernel<OutT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(kGemm2Lds));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  if (hipError_t e = ensure_max_lds(
+          reinterpret_cast<const void*>(gemm_tn_bf16_256_kernel<OutT>), kGemm2Lds))
+    return e;
   const int tm2 = (M + G2M - 1) / G2M, tn2 = (N + G2N - 1) / G2N;
   const int per_xcd = (tm2 * tn2 + 7) / 8;
   // full-row vector stores need 8-element aligned rows (16 or 32 bytes)

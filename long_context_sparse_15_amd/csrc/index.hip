@@ -1255,14 +1255,9 @@ static hipError_t launch_scores(const IndexArgs& a, int chunk, hipStream_t s) {
 template <int THREADS, int CAP>
 static hipError_t launch_row_topk(const IndexArgs& a, int rows, hipStream_t s) {
   const size_t lds = (static_cast<size_t>(CAP) + kHistBins) * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_row_kernel<THREADS, CAP>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(topk_row_kernel<THREADS, CAP>),
+                                    lds))
+    return e;
   ProfScope ps("topk_row", s);
   topk_row_kernel<THREADS, CAP><<<rows, THREADS, lds, s>>>(a.scores, a.sstride, a.n_entries,
                                                            a.pos, a.nq, a.m, a.k, a.n_max,
@@ -1278,14 +1273,9 @@ static bool use_gemm_scores(const IndexArgs& a) {
 
 template <bool MX, bool PAGED>
 static hipError_t launch_gemm_scores_t(const IndexArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(index_gemm_kernel<MX, PAGED>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemmLds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_gemm_kernel<MX, PAGED>),
+                                    kGemmLds))
+    return e;
   const int qtiles = (a.nq + kGemmQ - 1) / kGemmQ;
   ProfScope ps("index_score", s);
   index_gemm_kernel<MX, PAGED>
@@ -1335,14 +1325,8 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static bool attr_set = false;
-  if (!attr_set) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_finalize_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(kMultiLds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if ((e = ensure_max_lds(reinterpret_cast<const void*>(topk_finalize_kernel), kMultiLds)))
+    return e;
   ProfScope ps("topk_finalize", s);
   topk_finalize_kernel<<<rows, 1024, kMultiLds, s>>>(a.scores, a.sstride, a.n_entries, a.pos,
                                                      a.nq, a.m, a.k, a.n_max, ncc, a.counters,

@@ -94,7 +94,9 @@ struct MqaPlan {
   int split_rows;     // rows of the key list per workgroup (multiple of 32)
   int n_splits;
 };
-MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list);
+// nq = queries per sequence in the call; the batch size is deliberately not an input (the plan
+// fixes the order of every query's softmax sums, see mqa.hip)
+MqaPlan plan_mqa(int nq, int n_heads, int c, int max_list);
 size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c);
 hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& p, hipStream_t s);
 
@@ -169,6 +171,10 @@ hipError_t launch_output_proj(const OutputProjArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- misc
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
+// Raises kernel fn's dynamic-LDS limit to at least `bytes` (never lowers it).  Thread-safe: the
+// limits already set are kept per function under one lock, so concurrent first launches from
+// several threads each see the attribute in place before they launch.
+hipError_t ensure_max_lds(const void* fn, size_t bytes);
 
 // ---------------------------------------------------------------- launch timing (opt-in)
 struct ProfTotal {

@@ -19,9 +19,11 @@
 //   from the S^T accumulator layout).
 // LDS rows are unpadded with 16-byte chunks XOR-swizzled by row, which keeps both the row reads
 // of the S phase and the transposed reads of the PV phase free of bank conflicts.  With several
-// spans per query each workgroup writes (max, sum, O / sum in fp16) and a combine kernel merges
-// them in a fixed order, adds the sink and normalises; with one span the same epilogue runs in
-// place.  Spans are fixed by the plan, not by timing, so results are run-to-run deterministic.
+// spans per query each workgroup writes (max, sum, O / sum in bf16) and a combine kernel merges
+// them in a fixed order, adds the sink and normalises; with one span the workgroup runs the same
+// merge on its own partial in place.  The span size depends on the key list's length and on
+// whether the call brings one query per sequence or a run of them, never on the batch size, so a
+// sequence's output bits do not depend on which other sequences share the call.
 #include <algorithm>
 #include <cmath>
 
@@ -44,7 +46,7 @@ struct MqaParams {
   PageMap pages;  // entries in a block pool (PAGED kernels)
   float scale_log2;
   int split_rows, n_splits, head_groups, n_work;
-  float* part;  // span partials: fp16 O / l of each span in the MFMA lane order (see mqa_kernel)
+  float* part;  // span partials: bf16 O / l of each span in the MFMA lane order (see mqa_kernel)
   float* ml;    // [rows, n_splits, n_heads, 2]: (max, sum) of each span
   uint16_t* out;
   float* lse_out;
@@ -66,17 +68,56 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Two fp32 values as fp16 (round to nearest even), packed low first.
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const h2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
-  return __builtin_bit_cast(uint32_t, v);
+// fp32 rounded to bf16 (nearest even) and back: the value a span partial holds
+__device__ __forceinline__ float bf16_round(float x) {
+  return static_cast<float>(static_cast<__bf16>(x));
 }
-__device__ __forceinline__ f32x4 unpack_h4(uint2 v) {
-  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-  const h4 x = __builtin_bit_cast(h4, v);
-  return f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
-               static_cast<float>(x[3])};
+// four bf16 values packed low first (as pack2 writes them) to fp32
+__device__ __forceinline__ f32x4 unpack_b4(uint2 v) {
+  return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+}
+
+// Merge of a query's span partials, in span order, plus the sink, in the log2 domain.  A span
+// contributes its maximum m, its sum l of exp2(z - m) and O / l stored in bf16.  Every list, split
+// into one span or many, is normalised by exactly these operations (contraction off, so the
+// rounding is the same wherever they are inlined): the combine kernel folds the stored partials,
+// a single-span workgroup folds its own partial, rounded to bf16 as it would have been stored.
+struct SpanMerge {
+  float M;     // running reference: the sink logit, raised to the spans' maxima
+  float lsum;  // sum over merged spans of l * exp2(m - M)
+};
+__device__ __forceinline__ SpanMerge sm_start(float sink2) { return SpanMerge{sink2, 0.f}; }
+// raise the reference to Mn >= M; returns the factor the merged O must be multiplied by
+__device__ __forceinline__ float sm_raise(SpanMerge& st, float Mn) {
+#pragma clang fp contract(off)
+  if (Mn == st.M) return 1.f;
+  const float a = (st.M == -INFINITY) ? 0.f : exp2f(st.M - Mn);
+  st.lsum *= a;
+  st.M = Mn;
+  return a;
+}
+// adds a span (maximum m <= M, sum l); returns the weight of its O / l (0 for an empty span)
+__device__ __forceinline__ float sm_add(SpanMerge& st, float m, float l) {
+#pragma clang fp contract(off)
+  if (m == -INFINITY) return 0.f;
+  const float w = l * exp2f(m - st.M);
+  st.lsum += w;
+  return w;
+}
+__device__ __forceinline__ float sm_fold(float o, float ov, float w) {
+#pragma clang fp contract(off)
+  return o + ov * w;
+}
+// 1 / (sum + the sink's term); 0 when nothing is attended and there is no sink
+__device__ __forceinline__ float sm_inv(const SpanMerge& st, bool has_sink, float sink2) {
+#pragma clang fp contract(off)
+  const float den = st.lsum + ((has_sink && st.M != -INFINITY) ? exp2f(sink2 - st.M) : 0.f);
+  return den > 0.f ? 1.f / den : 0.f;
+}
+// natural-log sum of exp(z) without the sink
+__device__ __forceinline__ float sm_lse(const SpanMerge& st) {
+  return st.lsum > 0.f ? (st.M + log2f(st.lsum)) * kLn2 : -INFINITY;
 }
 
 // As store_out4, with cos/sin of the rotation angles of position t read from a table (pair i of
@@ -502,38 +543,40 @@ __global__ __launch_bounds__((MqaShape<C, HP>::NT)) void mqa_kernel(MqaParams p)
   const size_t orow = static_cast<size_t>(row) * p.n_heads + head;
   if (!head_ok) return;
   // output element i of acc[dt]: head l%32, dim dbase + 32dt + 8*(i/4) + 4h + i%4
+  const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;  // the partial is O / l of the span
   if (p.n_splits == 1) {
+    // the combine's merge of this one partial (rounded to bf16 as it would have been stored)
     const float a2 = p.sink ? sink_v * kLog2e : -INFINITY;
-    const float M = fmaxf(m_ref, a2);
-    const float f = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - M);
-    const float den = l_tot * f + ((a2 == -INFINITY) ? 0.f : exp2f(a2 - M));
-    const float inv = den > 0.f ? f / den : 0.f;
+    SpanMerge sm = sm_start(a2);
+    sm_raise(sm, fmaxf(sm.M, m_ref));
+    const float wgt = sm_add(sm, m_ref, l_tot);
+    const float inv = sm_inv(sm, p.sink != nullptr, a2);
+    auto fin = [&](float v) { return sm_fold(0.f, bf16_round(v * il), wgt) * inv; };
     uint16_t* orow_p = p.out + orow * C;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = dbase + dt * 32 + g4 * 8 + 4 * h;
-        store_out4(orow_p + d0, acc[dt][4 * g4] * inv, acc[dt][4 * g4 + 1] * inv,
-                   acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv, d0, C, p.r, t, s_freq);
+        store_out4(orow_p + d0, fin(acc[dt][4 * g4]), fin(acc[dt][4 * g4 + 1]),
+                   fin(acc[dt][4 * g4 + 2]), fin(acc[dt][4 * g4 + 3]), d0, C, p.r, t, s_freq);
       }
-    if (p.lse_out && h == 0 && slice == 0)
-      p.lse_out[orow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (p.lse_out && h == 0 && slice == 0) p.lse_out[orow] = sm_lse(sm);
   } else {
     // span partials in the MFMA lane order: per (row, span, head group, wave) DT*4 chunks of
     // 64 lanes x 4 values, so every store instruction writes 512 bytes contiguous; the values
-    // are O / l of the span (|O / l| <= max |entry|) in fp16
+    // are O / l of the span (|O / l| <= max |entry|) in bf16 (fp32's exponent range: no
+    // overflow whatever the entries' magnitudes)
     uint16_t* pw = reinterpret_cast<uint16_t*>(p.part) +
                    ((((static_cast<size_t>(row) * p.n_splits + split) * p.head_groups + hg) * NW +
                      wave) * (DT * 4) * 256);
-    const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
         *reinterpret_cast<uint2*>(pw + ((dt * 4 + g4) * 64 + l) * 4) =
-            uint2{pack_h2(acc[dt][4 * g4] * il, acc[dt][4 * g4 + 1] * il),
-                  pack_h2(acc[dt][4 * g4 + 2] * il, acc[dt][4 * g4 + 3] * il)};
+            uint2{pack2(acc[dt][4 * g4] * il, acc[dt][4 * g4 + 1] * il),
+                  pack2(acc[dt][4 * g4 + 2] * il, acc[dt][4 * g4 + 3] * il)};
     if (h == 0 && slice == 0) {
       float* mlp = p.ml + ((static_cast<size_t>(row) * p.n_splits + split) * p.n_heads + head) * 2;
       mlp[0] = m_ref;
@@ -985,12 +1028,15 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   const float m_fin = mlv.x, l_fin = mlv.y;
   const size_t orow = static_cast<size_t>(row) * p.n_heads + head;
   // output element i of acc[dt]: head n32, dim dbase + 32dt + 8*(i/4) + 4h + i%4
+  const float il = l_fin > 0.f ? 1.f / l_fin : 0.f;  // the partial is O / l of the span
   if (p.n_splits == 1) {
+    // the combine's merge of this one partial (rounded to bf16 as it would have been stored)
     const float a2 = (p.sink && head_ok) ? sink_raw * kLog2e : -INFINITY;
-    const float M = fmaxf(m_fin, a2);
-    const float f = (m_fin == -INFINITY) ? 0.f : exp2f(m_fin - M);
-    const float den = l_fin * f + ((a2 == -INFINITY) ? 0.f : exp2f(a2 - M));
-    const float inv = den > 0.f ? f / den : 0.f;
+    SpanMerge sm = sm_start(a2);
+    sm_raise(sm, fmaxf(sm.M, m_fin));
+    const float wgt = sm_add(sm, m_fin, l_fin);
+    const float inv = sm_inv(sm, p.sink != nullptr, a2);
+    auto fin = [&](float v) { return sm_fold(0.f, bf16_round(v * il), wgt) * inv; };
     // The normalised, rotated rows of the workgroup's heads are assembled in LDS (the tile ring
     // is free after the barrier above; a row pitch of C + 8 elements spreads consecutive heads
     // over the banks) and leave as whole rows: each store instruction writes 1 KiB contiguous.
@@ -1003,11 +1049,10 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = dbase + dt * 32 + g4 * 8 + 4 * h;
-        store_out4_tab(so_row + d0, acc[dt][4 * g4] * inv, acc[dt][4 * g4 + 1] * inv,
-                       acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv, d0, C, p.r, s_cs);
+        store_out4_tab(so_row + d0, fin(acc[dt][4 * g4]), fin(acc[dt][4 * g4 + 1]),
+                       fin(acc[dt][4 * g4 + 2]), fin(acc[dt][4 * g4 + 3]), d0, C, p.r, s_cs);
       }
-    if (p.lse_out && head_ok && h == 0 && slice == 0)
-      p.lse_out[orow] = l_fin > 0.f ? (m_fin + log2f(l_fin)) * kLn2 : -INFINITY;
+    if (p.lse_out && head_ok && h == 0 && slice == 0) p.lse_out[orow] = sm_lse(sm);
     __syncthreads();
     const int head0 = hg * HP * 32;
     uint16_t* obase = p.out + (static_cast<size_t>(row) * p.n_heads + head0) * C;
@@ -1021,18 +1066,17 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     }
   } else {
     if (!head_ok) return;
-    // span partials as in mqa_kernel: O / l of the span in fp16, MFMA lane order
+    // span partials as in mqa_kernel: O / l of the span in bf16, MFMA lane order
     uint16_t* pw = reinterpret_cast<uint16_t*>(p.part) +
                    ((((static_cast<size_t>(row) * p.n_splits + split) * p.head_groups + hg) * NW +
                      wave) * (DT * 4) * 256);
-    const float il = l_fin > 0.f ? 1.f / l_fin : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
         *reinterpret_cast<uint2*>(pw + ((dt * 4 + g4) * 64 + l) * 4) =
-            uint2{pack_h2(acc[dt][4 * g4] * il, acc[dt][4 * g4 + 1] * il),
-                  pack_h2(acc[dt][4 * g4 + 2] * il, acc[dt][4 * g4 + 3] * il)};
+            uint2{pack2(acc[dt][4 * g4] * il, acc[dt][4 * g4 + 1] * il),
+                  pack2(acc[dt][4 * g4 + 2] * il, acc[dt][4 * g4 + 3] * il)};
     if (h == 0 && slice == 0) {
       float* mlp = p.ml + ((static_cast<size_t>(row) * p.n_splits + split) * p.n_heads + head) * 2;
       mlp[0] = m_fin;
@@ -1076,8 +1120,7 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
   // one pass per kCombineMax spans: their (max, sum) and O loads go out together, and the
   // running reference M moves (rescaling what was merged) only between passes
   const float sink2 = p.sink ? p.sink[head] * kLog2e : -INFINITY;
-  float M = sink2;
-  float lsum = 0.f;
+  SpanMerge sm = sm_start(sink2);
   f32x4 o[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1091,29 +1134,25 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
       lv[j] = ml0[sp * ml_stride + 1];
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
-        ov[j][c] = unpack_h4(*reinterpret_cast<const uint2*>(pw0 + sp * span_stride + c * 256));
+        ov[j][c] = unpack_b4(*reinterpret_cast<const uint2*>(pw0 + sp * span_stride + c * 256));
     }
-    float Mn = M;
+    float Mn = sm.M;
 #pragma unroll
     for (int j = 0; j < kCombineMax; ++j) Mn = fmaxf(Mn, mv[j]);
-    if (Mn != M) {
-      const float a = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
-      lsum *= a;
+    const float a = sm_raise(sm, Mn);
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) o[c] *= a;
-      M = Mn;
-    }
+    for (int c = 0; c < CPT; ++c) o[c] *= a;
 #pragma unroll
     for (int j = 0; j < kCombineMax; ++j) {
-      if (mv[j] == -INFINITY) continue;
-      const float f = exp2f(mv[j] - M);
-      lsum += lv[j] * f;
+      const float wgt = sm_add(sm, mv[j], lv[j]);  // partials are O / l
+      if (wgt == 0.f && mv[j] == -INFINITY) continue;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) o[c] += ov[j][c] * (lv[j] * f);  // partials are O / l
+      for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[c][e] = sm_fold(o[c][e], ov[j][c][e], wgt);
     }
   }
-  const float den = lsum + ((p.sink && M != -INFINITY) ? exp2f(sink2 - M) : 0.f);
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float inv = sm_inv(sm, p.sink != nullptr, sink2);
   // chunk cc = dt*4 + g4 holds dims dbase + 32dt + 8g4 + 4h .. +3; all rotations before stores
   uint2 packed[CPT];
   int dpos[CPT];
@@ -1141,53 +1180,41 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
 #pragma unroll
   for (int c = 0; c < CPT; ++c) *reinterpret_cast<uint2*>(dst + dpos[c]) = packed[c];
   if (p.lse_out && cgp == 0 && h == 0 && slice == 0)
-    p.lse_out[static_cast<size_t>(row) * p.n_heads + head] =
-        lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
+    p.lse_out[static_cast<size_t>(row) * p.n_heads + head] = sm_lse(sm);
 }
 
 // ---------------------------------------------------------------- planning and launch
 static int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
 // Heads: up to 64 per workgroup (two 32-head pairs), more as separate head groups whose
-// workgroups sit on the same XCD and share the gathered rows through its L2.  Spans: chosen by
-// a small cost model with one resident workgroup of four waves per CU (fewer waves: several):
-// rounds of workgroups x (tiles x per-tile time + fixed cost), plus writing and re-reading the
-// fp16 partials when a query's list is split.
-MqaPlan plan_mqa(int rows, int n_heads, int c, int max_list) {
+// workgroups sit on the same XCD and share the gathered rows through its L2.
+//
+// Spans.  How a query's key list is cut into spans decides the order in which its softmax terms
+// are summed, so it must not depend on the batch: the plan reads the list's length (top_k +
+// n_win for CSA, the cache's n_max + n_win for HCA) and whether the call brings one query per
+// sequence (decode) or a run of kManyQueries or more (prefill), never the number of sequences.
+// A sequence decoded alone or inside any batch, at any slot, gets the same bits.
+//  * runs of queries: one span per query (lists up to kMaxTopK rows) -- the rows already fill
+//    the device, and a split would only add the partials' round trip;
+//  * decode, lists up to kMaxTopK rows (every CSA decode): spans of kDecodeSpan rows;
+//  * decode, longer lists (HCA over a long cache): eight spans.
+constexpr int kManyQueries = 16;
+constexpr int kDecodeSpan = 128;
+constexpr int kLongListSpans = 8;
+
+MqaPlan plan_mqa(int nq, int n_heads, int c, int max_list) {
   MqaPlan pl;
   pl.head_pairs = 2;  // one instantiation: 64 heads (fewer heads leave waves idle)
   pl.slices = c == 512 ? 4 : 1;  // eight waves of 128-dim slices for c = 512
   pl.heads_per_wg = 32 * pl.head_pairs;
   pl.head_groups = (n_heads + pl.heads_per_wg - 1) / pl.heads_per_wg;
-  const int waves = pl.head_pairs * pl.slices;
-  const double slots = 256.0 * (waves >= 4 ? 1 : 4 / waves);
-  const double base = static_cast<double>(rows) * pl.head_groups;
   const int list = max_list > 0 ? max_list : 1;
-  // measured on MI355X: a 32-row tile step, the per-workgroup fixed cost, the partials' round
-  // trip and the combine launch
-  const double t_tile = 1.0e-6 * (c >= 256 ? 1.0 : 0.6), t_fixed = 5.0e-6, bw = 5.0e12,
-               t_comb = 3.0e-6;
-  double best = 1e30;
-  pl.split_rows = round_up(list, 32);
-  pl.n_splits = 1;
-  pl.split_rows = std::min(pl.split_rows, kMaxTopK);  // a span's list fits its LDS slots
+  int sr;
+  if (nq >= kManyQueries) sr = round_up(list, 32);
+  else if (list <= kMaxTopK) sr = kDecodeSpan;
+  else sr = round_up((list + kLongListSpans - 1) / kLongListSpans, 64);
+  pl.split_rows = std::min(sr, kMaxTopK);  // a span's list fits its LDS slots
   pl.n_splits = (list + pl.split_rows - 1) / pl.split_rows;
-  for (int s = 1; s <= 64; ++s) {
-    const int sr = round_up((list + s - 1) / s, 32);
-    const int ns = (list + sr - 1) / sr;
-    if (ns != s || sr > kMaxTopK) continue;
-    // tile counts are padded: even for the eight-wave kernel (c = 512), odd otherwise
-    const int tiles = c == 512 ? ((sr + 63) / 64) * 2 : ((sr / 32) | 1);
-    const double rounds = std::ceil(base * ns / slots);
-    double tm = rounds * (tiles * t_tile + t_fixed);
-    if (ns > 1) tm += 2.0 * rows * ns * static_cast<double>(n_heads) * (2.0 * c + 8.0) / bw + t_comb;
-    if (tm < best * 0.97) {
-      best = tm;
-      pl.split_rows = sr;
-      pl.n_splits = ns;
-    }
-    if (sr <= 32) break;
-  }
   return pl;
 }
 
@@ -1196,7 +1223,7 @@ size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c) {
   if (p.n_splits <= 1) return 0;
   const size_t o = static_cast<size_t>(rows) * p.n_splits * p.head_groups * p.heads_per_wg * c;
   const size_t ml = static_cast<size_t>(rows) * p.n_splits * n_heads * 2;
-  return o * sizeof(uint16_t) + ml * sizeof(float);  // fp16 partials, then fp32 (max, sum)
+  return o * sizeof(uint16_t) + ml * sizeof(float);  // bf16 partials, then fp32 (max, sum)
 }
 
 template <int C, class SH, bool WIDE, bool PAGED, bool MIXED = false>
@@ -1204,23 +1231,17 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   const size_t lds = SH::lds_fixed() + ((prm.idx || PAGED)
                                             ? static_cast<size_t>(prm.split_rows) * sizeof(int)
                                             : 0);
-  static size_t attr = 0;
-  if (attr < lds) {
+  {
     hipError_t e;
     if constexpr (WIDE) {
-      e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(mqa_wide_kernel<C, true, PAGED, MIXED>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(mqa_wide_kernel<C, false, PAGED, MIXED>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      e = prm.idx ? ensure_max_lds(
+                        reinterpret_cast<const void*>(mqa_wide_kernel<C, true, PAGED, MIXED>), lds)
+                  : ensure_max_lds(
+                        reinterpret_cast<const void*>(mqa_wide_kernel<C, false, PAGED, MIXED>), lds);
     } else {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(mqa_kernel<C, SH::HP, PAGED>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      e = ensure_max_lds(reinterpret_cast<const void*>(mqa_kernel<C, SH::HP, PAGED>), lds);
     }
     if (e != hipSuccess) return e;
-    attr = lds;
   }
   MqaParams q = prm;
   q.n_work = rows * prm.n_splits;
@@ -1285,7 +1306,7 @@ hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& pl, hipStream_t s) {
   p.head_groups = pl.head_groups;
   p.part = a.part;
   p.ml = a.part + static_cast<size_t>(a.B) * a.nq * pl.n_splits * pl.head_groups *
-                      pl.heads_per_wg * a.c / 2;  // after the fp16 partials
+                      pl.heads_per_wg * a.c / 2;  // after the bf16 partials
   p.out = a.out;
   p.lse_out = a.lse_out;
   const int rows = a.B * a.nq;

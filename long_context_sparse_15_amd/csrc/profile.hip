@@ -4,6 +4,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "kernels.h"
@@ -94,6 +95,18 @@ int profile_stop(ProfTotal* out, int max, int* n) {
   for (int i = 0; i < cnt; ++i) out[i] = tot[i];
   *n = cnt;
   return err == hipSuccess ? 0 : -1;
+}
+
+hipError_t ensure_max_lds(const void* fn, size_t bytes) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, size_t> set;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = set.find(fn);
+  if (it != set.end() && it->second >= bytes) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(bytes));
+  if (e == hipSuccess) set[fn] = bytes;
+  return e;
 }
 
 }  // namespace csa

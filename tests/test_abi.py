@@ -163,3 +163,38 @@ def test_long_rows_in_big_batches_are_refused(L):
                                 ctypes.byref(b)) == -2
     assert L.csa_workspace_size(ctypes.byref(c), csa.OP_INDEX_TOPK, 1, 65536, 32768,
                                 ctypes.byref(b)) == 0   # rows of at most 32768 entries: any count
+
+
+def test_misaligned_workspace_is_rejected(L):
+    """Every compute entry point checks the workspace's documented 256-byte alignment before
+    anything is launched (the other pointers here are aligned stand-ins that are never used)."""
+    c = _cfg()
+    h = _cfg(csa.MODE_HCA)
+    k = csa.Cache(8192, 128, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0, 0, 0, 0)
+    ws, n = 0x10010, 1 << 40
+    P = 0x20000
+    calls = [
+        lambda: L.csa_index_topk(ctypes.byref(c), 1, 1, P, P, P, ctypes.byref(k), P, P, None, ws,
+                                 n, None),
+        lambda: L.csa_sparse_mqa(ctypes.byref(c), 1, 1, P, ctypes.byref(k), P, P, P, P, None, ws,
+                                 n, None),
+        lambda: L.hca_dense_mqa(ctypes.byref(h), 1, 1, P, ctypes.byref(k), P, P, P, None, ws, n,
+                                None),
+        lambda: L.csa_decode(ctypes.byref(c), 1, None, None, ctypes.byref(k), P, P, P, P, P, P, P,
+                             None, ws, n, None),
+    ]
+    for f in calls:
+        assert f() == -1
+        assert "256-byte aligned" in csa.last_error(), csa.last_error()
+
+
+def test_attention_plan_does_not_depend_on_the_batch(L):
+    """The attention workspace (span partials) grows exactly linearly with the batch: the number
+    of spans a query's list is cut into is the same for every batch size."""
+    for cfg, op, n_max in ((_cfg(), csa.OP_SPARSE_MQA, 32768),
+                           (_cfg(n_heads=128, top_k=2048), csa.OP_SPARSE_MQA, 262144),
+                           (_cfg(csa.MODE_HCA, n_heads=128), csa.OP_HCA_MQA, 8192)):
+        one = csa.workspace_size(cfg, op, 1, 1, n_max)
+        assert one > 0
+        for B in (2, 5, 16, 32, 128):
+            assert csa.workspace_size(cfg, op, B, 1, n_max) == B * one
