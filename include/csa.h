@@ -290,6 +290,24 @@ int csa_decode(const csa_config_t* cfg, int32_t B, const uint16_t* h_new,
                const float* sink, uint16_t* out, int32_t* idx_out, void* workspace,
                size_t ws_bytes, void* stream);
 
+/* csa_decode_noalloc - csa_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, effects and errors as csa_decode, minus workspace/ws_bytes.  Scratch comes from
+ * a static device array of CSA_NOALLOC_SCRATCH_BYTES inside the library: each GPU the library
+ * runs on holds its own copy until the process ends, and its address is looked up once per
+ * device, on the first call with that device current.  A step needing more scratch than that
+ * (csa_workspace_size(cfg, CSA_OP_DECODE, B, 1, n_max, ...)) returns CSA_ERR_UNSUPPORTED and
+ * launches nothing; the configured workloads need at most about 17 MiB (1M-context HCA, B=16).
+ * The call allocates nothing: no hipMalloc, hipFree or allocating library routine (with the
+ * opt-in launch timer off).  All calls on one GPU share its array, so calls that overlap on one
+ * GPU (different streams or threads without ordering between them) race: serialise them. */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int csa_decode_noalloc(const csa_config_t* cfg, int32_t B, const uint16_t* h_new,
+                       const csa_weights_t* w, const csa_cache_t* cache, const int32_t* pos,
+                       const uint16_t* q, const uint8_t* qi, const float* qi_scale,
+                       const float* wi, const float* sink, uint16_t* out, int32_t* idx_out,
+                       void* stream);
+
 /* csa_prefill - causal layer over the first T tokens of B sequences (positions 0..T-1):
  * csa_compress (pos0 = 0; every block is written whatever n_entries holds on entry, and
  * n_entries ends as floor(T/m)), then for every token t as a query the

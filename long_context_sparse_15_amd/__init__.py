@@ -17,6 +17,7 @@ IDX_E4M3, IDX_MXFP4 = 0, 1
 ENT_BF16, ENT_MIXED = 0, 1
 (OP_COMPRESS, OP_INDEX_TOPK, OP_SPARSE_MQA, OP_HCA_MQA, OP_DECODE, OP_PREFILL, OP_QUERY_PROJ,
  OP_OUTPUT_PROJ) = range(8)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CSA_NOALLOC_SCRATCH_BYTES
 
 
 class CsaError(RuntimeError):
@@ -84,6 +85,8 @@ _SIGS = {
                    ctypes.c_int),
     "csa_prefill": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
                     ctypes.c_int),
+    "csa_decode_noalloc": ([_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+                           ctypes.c_int),
     "csa_query_proj": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "csa_output_proj": ([_P, _I, _I, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "csa_blocks_create": ([_I, _P], ctypes.c_int),
@@ -290,6 +293,18 @@ def decode(cfg, cache, pos, q, sink, out, ws, h_new=None, weights=None, qi=None,
                             ctypes.byref(cache), _ptr(pos), _ptr(q), _ptr(qi), _ptr(qi_scale),
                             _ptr(wi), _ptr(sink), _ptr(out), _ptr(idx_out), wp, wn,
                             _stream(stream)), "csa_decode")
+
+
+def decode_noalloc(cfg, cache, pos, q, sink, out, h_new=None, weights=None, qi=None,
+                   qi_scale=None, wi=None, idx_out=None, stream=None):
+    """csa_decode_noalloc: csa_decode with the library's static device scratch instead of a
+    workspace (for callers that cannot allocate; calls overlapping on one GPU race)."""
+    B = q.shape[0]
+    _check(lib().csa_decode_noalloc(ctypes.byref(cfg), B, _ptr(h_new),
+                                    ctypes.byref(weights) if weights is not None else None,
+                                    ctypes.byref(cache), _ptr(pos), _ptr(q), _ptr(qi),
+                                    _ptr(qi_scale), _ptr(wi), _ptr(sink), _ptr(out),
+                                    _ptr(idx_out), _stream(stream)), "csa_decode_noalloc")
 
 
 def prefill(cfg, H, weights, cache, q, sink, out, ws, qi=None, qi_scale=None, wi=None,

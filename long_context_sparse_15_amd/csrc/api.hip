@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "../../include/csa.h"
@@ -42,6 +43,9 @@ int api_fail(int code, const char* fmt, ...) {
   return rc;
 }
 }  // namespace csa
+
+// Static scratch of csa_decode_noalloc (see scratch_of_current_device below).
+static __device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -355,11 +359,82 @@ int check_oproj_config(const csa_config_t* c) {
   return CSA_OK;
 }
 
+// Validation shared by csa_decode and csa_decode_noalloc; *need receives the scratch bytes the
+// step uses (index buffer, then the union of the compressor, scorer and attention buffers).
+int decode_check(const csa_config_t* cfg, int32_t B, const uint16_t* h_new,
+                 const csa_weights_t* w, const csa_cache_t* cache, const int32_t* pos,
+                 const uint16_t* q, const uint8_t* qi, const float* qi_scale, const float* wi,
+                 const float* sink, const uint16_t* out, size_t* need) {
+  const bool comp = h_new != nullptr;
+  int rc = check_config(cfg, comp);
+  if (rc) return rc;
+  if ((rc = check_cache(cfg, cache, is_csa(cfg), comp))) return rc;
+  if (comp && (rc = check_weights(cfg, w))) return rc;
+  if (B < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if ((rc = check_index_rows(cfg, B, cache->n_max))) return rc;
+  if (!pos || !q || !sink || !out) return fail(CSA_ERR_INVALID_ARG, "pos/q/sink/out is NULL");
+  if ((rc = check_aligned({h_new, q, qi, out, w ? w->w_cat : nullptr}))) return rc;
+  if (is_csa(cfg) && (!qi || !qi_scale || !wi))
+    return fail(CSA_ERR_INVALID_ARG, "CSA decode needs qi, qi_scale and wi");
+  *need = ws_layer(cfg, B, 1, cache->n_max, false, comp);
+  return CSA_OK;
+}
+
+// One decode step on already validated arguments, with scratch ws.
+int decode_run(const csa_config_t* cfg, int32_t B, const uint16_t* h_new,
+               const csa_weights_t* w, const csa_cache_t* cache, const int32_t* pos,
+               const uint16_t* q, const uint8_t* qi, const float* qi_scale, const float* wi,
+               const float* sink, uint16_t* out, int32_t* idx_out, void* ws, hipStream_t s) {
+  int rc = CSA_OK;
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  int32_t* idx = nullptr;
+  if (is_csa(cfg)) {
+    idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p);
+    p += align256(static_cast<size_t>(B) * cfg->top_k * 4);
+  }
+  if (h_new && (rc = run_compress(cfg, B, 1, h_new, pos, w, cache, p, s))) return rc;
+  if (is_csa(cfg)) {
+    if ((rc = run_index(cfg, B, 1, qi, qi_scale, wi, cache, pos, idx, nullptr, p, s))) return rc;
+    return run_attend(cfg, B, 1, q, cache, idx, pos, sink, out, nullptr, p, s);
+  }
+  return run_attend(cfg, B, 1, q, cache, nullptr, pos, sink, out, nullptr, p, s);
+}
+
+// ---- static scratch of csa_decode_noalloc ---------------------------------------------------
+// One file-scope device array: every GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  Host code never passes the array's name to a kernel (on the
+// host it only names the symbol); it takes each device's address once, with that device current,
+// through hipGetSymbolAddress and uses that pointer.  No decode buffer has to start zeroed:
+// every scratch byte a kernel reads was written earlier in the same call.
+constexpr size_t kScratchBytes = CSA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(CSA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch "
+                "tracks", dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(CSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int csa_version(void) { return 1 * 10000 + 2 * 100 + 0; }
+int csa_version(void) { return 1 * 10000 + 3 * 100 + 0; }
 
 int csa_profile_start(void) {
   csa::profile_start();
@@ -505,32 +580,30 @@ int csa_decode(const csa_config_t* cfg, int32_t B, const uint16_t* h_new, const 
                const csa_cache_t* cache, const int32_t* pos, const uint16_t* q, const uint8_t* qi,
                const float* qi_scale, const float* wi, const float* sink, uint16_t* out,
                int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
-  const bool comp = h_new != nullptr;
-  int rc = check_config(cfg, comp);
+  size_t need = 0;
+  int rc = decode_check(cfg, B, h_new, w, cache, pos, q, qi, qi_scale, wi, sink, out, &need);
   if (rc) return rc;
-  if ((rc = check_cache(cfg, cache, is_csa(cfg), comp))) return rc;
-  if (comp && (rc = check_weights(cfg, w))) return rc;
-  if (B < 1) return fail(CSA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
-  if ((rc = check_index_rows(cfg, B, cache->n_max))) return rc;
-  if (!pos || !q || !sink || !out) return fail(CSA_ERR_INVALID_ARG, "pos/q/sink/out is NULL");
-  if ((rc = check_aligned({h_new, q, qi, out, w ? w->w_cat : nullptr}))) return rc;
-  if (is_csa(cfg) && (!qi || !qi_scale || !wi))
-    return fail(CSA_ERR_INVALID_ARG, "CSA decode needs qi, qi_scale and wi");
-  const size_t need = ws_layer(cfg, B, 1, cache->n_max, false, comp);
   if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  unsigned char* p = static_cast<unsigned char*>(workspace);
-  int32_t* idx = nullptr;
-  if (is_csa(cfg)) {
-    idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p);
-    p += align256(static_cast<size_t>(B) * cfg->top_k * 4);
-  }
-  if (comp && (rc = run_compress(cfg, B, 1, h_new, pos, w, cache, p, s))) return rc;
-  if (is_csa(cfg)) {
-    if ((rc = run_index(cfg, B, 1, qi, qi_scale, wi, cache, pos, idx, nullptr, p, s))) return rc;
-    return run_attend(cfg, B, 1, q, cache, idx, pos, sink, out, nullptr, p, s);
-  }
-  return run_attend(cfg, B, 1, q, cache, nullptr, pos, sink, out, nullptr, p, s);
+  return decode_run(cfg, B, h_new, w, cache, pos, q, qi, qi_scale, wi, sink, out, idx_out,
+                    workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+int csa_decode_noalloc(const csa_config_t* cfg, int32_t B, const uint16_t* h_new,
+                       const csa_weights_t* w, const csa_cache_t* cache, const int32_t* pos,
+                       const uint16_t* q, const uint8_t* qi, const float* qi_scale,
+                       const float* wi, const float* sink, uint16_t* out, int32_t* idx_out,
+                       void* stream) {
+  size_t need = 0;
+  int rc = decode_check(cfg, B, h_new, w, cache, pos, q, qi, qi_scale, wi, sink, out, &need);
+  if (rc) return rc;
+  if (need > kScratchBytes)
+    return fail(CSA_ERR_UNSUPPORTED, "this decode needs %zu bytes of scratch, more than the %zu "
+                "bytes of csa_decode_noalloc's static scratch (use csa_decode with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  return decode_run(cfg, B, h_new, w, cache, pos, q, qi, qi_scale, wi, sink, out, idx_out, ws,
+                    reinterpret_cast<hipStream_t>(stream));
 }
 
 int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,

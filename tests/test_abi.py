@@ -36,14 +36,14 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(L, n), n
         assert n in csa._SIGS, n
 
 
 def test_version_and_helpers(L):
-    assert csa.version() == 10200
+    assert csa.version() == 10300
     c = _cfg()
     assert csa.weight_cols(c) == 5 * 512 + 4 * 128
     assert csa.tail_shape(c) == (8, 4 * 512 + 4 * 128)
