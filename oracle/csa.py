@@ -31,7 +31,15 @@ Readings taken where the pages are silent (also listed in the design notes):
       rotated: the attention step applies RoPE at the query position t;
   R19 optional FP4 indexer keys are OCP MXFP4: 32 consecutive dims share one E8M0 scale
       (shared exponent floor(log2 max|v|) - 2, all-zero block -127), elements E2M1 with ties to
-      even and saturation; the query stays E4M3;
+      even and saturation.  Paired with an E4M3 query this is a labelled variant of this
+      library (index_scores_mxfp4), not the pages' path, which R24 gives;
+  R24 the pages' FP4 indexer QK path: the indexer query is FP4 too, quantised like the keys
+      (MXFP4, blocks of 32 dims of one (token, head) row, one E8M0 scale per block), so both
+      operands of every q^I . K dot product are MXFP4 values (index_scores_fp4);
+  R25 optional BF16 index scores: each score I_{t,s} is rounded to bf16 (nearest, ties to even)
+      before TopK, and TopK runs on the rounded values with the lower index winning the (now
+      frequent) ties (round_scores_bf16); index sets are then compared outside a band of one
+      bf16 ulp of the k-th score instead of 1e-3;
   R20 query side: c^Q = h W^DQ is stored in bf16 between the two projections; the attention
       query is c^Q W^UQ RMS-normalised over each head's c dims with one gain vector shared by
       the heads, stored bf16 and not rotated (R18); q^I = c^Q W^IUQ is stored as R5; w^I = h W_w
@@ -275,6 +283,28 @@ def index_scores_mxfp4(qi_codes, qi_scale, wi, ki_packed, ki_scales, n_vis):
     return np.maximum(dots, 0.0) @ np.asarray(wi, np.float64)
 
 
+def index_scores_fp4(qi_packed, qi_scales, wi, ki_packed, ki_scales, n_vis):
+    """index_scores with both indexer operands FP4 (reading R24: the pages run the indexer's QK
+    product in FP4, query and keys alike - Deep dive "论文专题讲解：DeepSeek-V4", section "FP4
+    QAT", table row "CSA indexer QK path"; Analysis "DeepSeek-V4 技术报告深度解读" §5.4).  The query
+    of each head is one MXFP4 row: its real values are E2M1 codes times the power-of-two scale
+    of their 32-dim block, as are the keys', and the dot products, ReLU and the head sum run in
+    float64 on those values.  qi_packed [H_I, d_I/2] u8, qi_scales [H_I, d_I/32] u8 (E8M0),
+    wi [H_I] f32, ki_packed [N, d_I/2] u8, ki_scales [N, d_I/32] u8.  Returns float64 [n_vis]."""
+    q = mxfp4_decode(qi_packed, qi_scales)                                  # [H_I, d_I]
+    k = mxfp4_decode(ki_packed[:n_vis], ki_scales[:n_vis])                 # [n_vis, d_I]
+    dots = k @ q.T
+    return np.maximum(dots, 0.0) @ np.asarray(wi, np.float64)
+
+
+def round_scores_bf16(scores):
+    """Index scores stored in BF16 before the top-k (reading R25; Deep dive "论文专题讲解：
+    DeepSeek-V4", section "FP4 QAT", table row "index scores": FP32 -> BF16, which the pages
+    credit with a 2x faster top-k selector).  Each score is rounded to the nearest bf16 number
+    (ties to even); returns the float64 values of those numbers."""
+    return bf16_bits_to_f64(f64_to_bf16_bits(scores))
+
+
 def topk_select(scores, k):
     """TopK_k over the visible scores (book, chapter "Attention", section "CSA 的完整路径",
     I_t = TopK_k{I_{t,s} | s < floor((t+1)/m)}).  Ties: lower index wins; fewer than k
@@ -314,18 +344,31 @@ def attend(q_bits, rows_bits, sink, scale, t, inv_freq):
     return rope_rotate(o, t, inv_freq, sign=-1.0), lse
 
 
+def score_function(idx_format="e4m3", qi_format="e4m3"):
+    """The index-score function of a key format (idx_format "e4m3" or "mxfp4") and query format
+    (qi_format "e4m3" or "mxfp4"; an MXFP4 query needs MXFP4 keys, reading R24)."""
+    if qi_format == "mxfp4":
+        assert idx_format == "mxfp4", "an FP4 query is paired with FP4 keys"
+        return index_scores_fp4
+    return index_scores_mxfp4 if idx_format == "mxfp4" else index_scores
+
+
 def csa_query(t, q_bits, qi_codes, qi_scale, wi, sink, entries, ikeys, iscale, n_entries, win,
-              win_pos_to_row, m, k, n_win, scale, inv_freq, idx_format="e4m3"):
+              win_pos_to_row, m, k, n_win, scale, inv_freq, idx_format="e4m3", qi_format="e4m3",
+              score_format="fp32"):
     """One CSA query token t: score the visible entries, select the top-k, attend over the
     selected entries plus the sliding window plus the sink.
 
     entries [N, c] bf16 bits, ikeys [N, d_I], iscale [N]; win: bf16 rows of uncompressed KV and
-    win_pos_to_row(u) -> row index into win for token u.
+    win_pos_to_row(u) -> row index into win for token u.  score_format "bf16" rounds the scores
+    to bf16 before the top-k (reading R25).
     Returns dict(sel, scores, out, lse).
     """
     n_vis = visible_entries(t, m, n_entries)
-    score_fn = index_scores_mxfp4 if idx_format == "mxfp4" else index_scores
+    score_fn = score_function(idx_format, qi_format)
     scores = score_fn(qi_codes, qi_scale, wi, ikeys, iscale, n_vis)
+    if score_format == "bf16":
+        scores = round_scores_bf16(scores)
     sel = topk_select(scores, k)
     rows = [entries[sel]]
     wt = window_tokens(t, n_win)
@@ -347,7 +390,8 @@ def hca_query(t, q_bits, sink, entries, n_entries, win, win_pos_to_row, m, n_win
 
 
 def csa_layer(h_bits, w_bits, params, q_bits, qi_codes, qi_scale, wi, sink, m, c, d_i, k,
-              n_win, scale, inv_freq, eps, queries, idx_format="e4m3"):
+              n_win, scale, inv_freq, eps, queries, idx_format="e4m3", qi_format="e4m3",
+              score_format="fp32"):
     """Whole CSA layer from hidden states, for the listed query tokens (prefill rows or decode
     steps alike: a decode step at position t is the prefill row t of the longer prefix, since
     every quantity depends only on tokens <= t).  q_bits etc. are indexed by token.
@@ -359,7 +403,8 @@ def csa_layer(h_bits, w_bits, params, q_bits, qi_codes, qi_scale, wi, sink, m, c
         # them from the whole prefix once and lets visibility mask the rest.
         res[t] = csa_query(t, q_bits[t], qi_codes[t], qi_scale[t], wi[t], sink, comp["entries"],
                            comp["ikeys"], comp["iscale"], comp["entries"].shape[0], comp["win"],
-                           lambda u: u, m, k, n_win, scale, inv_freq, idx_format)
+                           lambda u: u, m, k, n_win, scale, inv_freq, idx_format, qi_format,
+                           score_format)
     return comp, res
 
 
@@ -377,7 +422,7 @@ def hca_layer(h_bits, w_bits, params, q_bits, sink, m, c, n_win, scale, inv_freq
 # projections (the steps on either side of the attention path)
 
 def query_projections(h_bits, w_dq_bits, w_w_bits, w_uq_bits, w_iuq_bits, gamma_q, n_h, c,
-                      H_I, d_I, eps):
+                      H_I, d_I, eps, qi_format="e4m3"):
     """Indexer query, indexer head weights and attention query of every token.
 
     Book, chapter "Attention", section "CSA 的完整路径": c^Q_t = h_t W^DQ,
@@ -386,7 +431,9 @@ def query_projections(h_bits, w_dq_bits, w_w_bits, w_uq_bits, w_iuq_bits, gamma_
     h_bits [T, D] bf16; weights bf16, one row per output column: w_dq [r_q, D], w_w [H_I, D],
     w_uq [n_h*c, r_q], w_iuq [H_I*d_I, r_q]; gamma_q [c].
     Returns dict(cq bf16 [T, r_q], q bf16 [T, n_h, c], qi u8 [T, H_I, d_I], qi_scale f32
-    [T, H_I], wi f32 [T, H_I], qpre f64 [T, n_h, c], qi_pre f64 [T, H_I, d_I]).
+    [T, H_I], wi f32 [T, H_I], qpre f64 [T, n_h, c], qi_pre f64 [T, H_I, d_I]); with qi_format
+    "mxfp4" (reading R24) qi is u8 [T, H_I, d_I/2] packed MXFP4 and qi_scale u8 [T, H_I, d_I/32]
+    its E8M0 block scales.
     """
     H = bf16_bits_to_f64(h_bits)
     T = H.shape[0]
@@ -394,7 +441,10 @@ def query_projections(h_bits, w_dq_bits, w_w_bits, w_uq_bits, w_iuq_bits, gamma_
     CQ = bf16_bits_to_f64(cq)
     wi = (H @ bf16_bits_to_f64(w_w_bits).T).astype(np.float32)
     qi_pre = (CQ @ bf16_bits_to_f64(w_iuq_bits).T).reshape(T, H_I, d_I)
-    qi, qi_scale = quantize_rows_e4m3(qi_pre)
+    if qi_format == "mxfp4":
+        qi, qi_scale = quantize_rows_mxfp4(qi_pre)
+    else:
+        qi, qi_scale = quantize_rows_e4m3(qi_pre)
     qpre = (CQ @ bf16_bits_to_f64(w_uq_bits).T).reshape(T, n_h, c)
     q = f64_to_bf16_bits(rms_norm(qpre, gamma_q, eps))
     return {"cq": cq, "q": q, "qi": qi, "qi_scale": qi_scale, "wi": wi, "qpre": qpre,

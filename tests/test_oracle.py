@@ -677,3 +677,147 @@ def test_mixed_entries_error_bound_and_compressor():
     err = np.abs(dec[:, :k] - ref[:, :k])
     assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(ref[:, :k]), 2.0 ** -10) * 1.01)
     assert err.max() > 0  # the quantisation is not a no-op
+
+
+# ----------------------------------------------------------------------------- FP4 query, BF16 scores
+
+def _fp4_row(byte0, d=32):
+    """A packed MXFP4 row of d dims with only byte 0 (dims 0 and 1) non-zero."""
+    r = np.zeros(d // 2, np.uint8)
+    r[0] = byte0
+    return r
+
+
+def test_index_score_fp4_hand_fixture():
+    g = _gold("index_score_fp4_hand.json")
+    qp = np.stack([_fp4_row(b) for b in g["qi_byte0"]])
+    kp = np.stack([_fp4_row(b) for b in g["ki_byte0"]])
+    qs = np.array(g["qi_scale"], np.uint8)[:, None]
+    ks = np.array(g["ki_scale"], np.uint8)[:, None]
+    got = O.index_scores_fp4(qp, qs, np.array(g["wi"], np.float32), kp, ks, 2)
+    assert np.array_equal(got, np.array(g["expect"]))
+
+
+def test_index_score_fp4_brute_force_loops():
+    """Brute force with an E2M1 magnitude table written out here and E8M0 scales 2^(byte-127)."""
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    rng = np.random.default_rng(41)
+    HI, dI, N = 3, 64, 7
+    qcodes = rng.integers(0, 16, (HI, dI))
+    kcodes = rng.integers(0, 16, (N, dI))
+    qsb = rng.integers(120, 132, (HI, dI // 32)).astype(np.uint8)
+    ksb = rng.integers(120, 132, (N, dI // 32)).astype(np.uint8)
+    pack = lambda c: (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+    w = rng.standard_normal(HI).astype(np.float32)
+    got = O.index_scores_fp4(pack(qcodes), qsb, w, pack(kcodes), ksb, 6)
+
+    def val(code, sb):
+        v = mags[code & 7] * 2.0 ** (int(sb) - 127)
+        return -v if code & 8 else v
+    for s in range(6):
+        tot = 0.0
+        for h in range(HI):
+            dot = sum(val(qcodes[h, d], qsb[h, d // 32]) * val(kcodes[s, d], ksb[s, d // 32])
+                      for d in range(dI))
+            tot += float(w[h]) * max(dot, 0.0)
+        assert abs(got[s] - tot) <= 1e-12 * (1 + abs(tot))
+
+
+def test_index_scores_fp4_equals_e4m3_path_on_shared_values():
+    """Queries and keys whose real values both formats hold exactly (E2M1 magnitudes times a
+    power of two per 32-dim block): the FP4 x FP4 scorer, the E4M3 x MXFP4 variant and the E4M3
+    scorer give identical scores."""
+    rng = np.random.default_rng(42)
+    H, d, N = 4, 128, 40
+
+    def shared(rows):
+        codes = rng.integers(0, 16, (rows, d)).astype(np.uint8)
+        codes[:, ::32] = 7  # every block holds its largest magnitude, 6 x 2^e
+        se = rng.integers(-3, 5, (rows, d // 32))
+        return O.e2m1_decode(codes) * np.repeat(np.exp2(se.astype(np.float64)), 32, axis=1)
+    qv, kv = shared(H), shared(N)
+    qp, qs = O.quantize_rows_mxfp4(qv)
+    kp, ks = O.quantize_rows_mxfp4(kv)
+    assert np.array_equal(O.mxfp4_decode(qp, qs), qv) and np.array_equal(O.mxfp4_decode(kp, ks), kv)
+    qe, ke = O.e4m3_encode(qv), O.e4m3_encode(kv)
+    assert np.array_equal(O.e4m3_decode(qe), qv) and np.array_equal(O.e4m3_decode(ke), kv)
+    wi = rng.standard_normal(H).astype(np.float32)
+    one_q, one_k = np.ones(H, np.float32), np.ones(N, np.float32)
+    a = O.index_scores(qe, one_q, wi, ke, one_k, N - 5)
+    b = O.index_scores_mxfp4(qe, one_q, wi, kp, ks, N - 5)
+    c = O.index_scores_fp4(qp, qs, wi, kp, ks, N - 5)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    assert O.score_function("mxfp4", "mxfp4") is O.index_scores_fp4
+    assert O.score_function("mxfp4", "e4m3") is O.index_scores_mxfp4
+    assert O.score_function() is O.index_scores
+
+
+def test_round_scores_bf16_hand_fixture_and_topk():
+    g = _gold("bf16_scores_topk_hand.json")
+    sc = np.array(g["scores"])
+    r = O.round_scores_bf16(sc)
+    assert np.array_equal(r, np.array(g["rounded"]))
+    assert list(O.topk_select(r, g["k"])) == g["expect_bf16"]
+    assert list(O.topk_select(sc, g["k"])) == g["expect_full"]
+
+
+def test_round_scores_bf16_against_torch_and_order():
+    """float32 inputs (one rounding step, so torch's conversion is a single RNE too), exact
+    bf16 values kept, monotone non-decreasing."""
+    rng = np.random.default_rng(43)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000)).astype(np.float32)
+    got = O.round_scores_bf16(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(O.round_scores_bf16(got), got)
+    srt = np.sort(x.astype(np.float64))
+    assert np.all(np.diff(O.round_scores_bf16(srt)) >= 0)
+
+
+def test_csa_query_bf16_scores_select_on_rounded_values():
+    """csa_query with BF16 scores: the selection is the top-k of the rounded scores with the
+    lower index winning ties (brute force with Python's sorted)."""
+    rng = np.random.default_rng(44)
+    w = S.shrink(S.WORKLOADS["tiny_csa"])
+    x = S.decode_cache_inputs(w, B=1, N=400)
+    t = 4 * 400
+    r = O.csa_query(t, x["q"][0, 0], x["qi"][0, 0], x["qi_scale"][0, 0], x["wi"][0, 0], x["sink"],
+                    x["entries"][0], x["ikeys"][0], x["iscale"][0], 400, x["window"][0],
+                    lambda u: u % w.n_win, w.m, w.k, w.n_win, w.scale, x["inv_freq"],
+                    score_format="bf16")
+    full = O.index_scores(x["qi"][0, 0], x["qi_scale"][0, 0], x["wi"][0, 0], x["ikeys"][0],
+                          x["iscale"][0], 400)
+    rounded = O.round_scores_bf16(full)
+    assert np.array_equal(r["scores"], rounded)
+    ref = sorted(sorted(range(400), key=lambda i: (-rounded[i], i))[:w.k])
+    assert list(r["sel"]) == ref
+    assert len(np.unique(rounded)) < 400  # bf16 rounding does create ties here
+    del rng
+
+
+def test_query_projections_mxfp4_query():
+    """qi_format "mxfp4": the indexer query is the MXFP4 quantisation of the same pre-quantised
+    values, each element within half an E2M1 step (times its block scale) of them, or clamped
+    at 6 times the block scale."""
+    rng = np.random.default_rng(45)
+    T, D, n_h, c, H_I, d_I = 4, 64, 2, 32, 2, 64
+    r_q = 64
+    bf = lambda a: O.f64_to_bf16_bits(a)
+    h = bf(rng.standard_normal((T, D)))
+    w_dq = bf(rng.standard_normal((r_q, D)) / 8)
+    w_w = bf(rng.standard_normal((H_I, D)) / 8)
+    w_uq = bf(rng.standard_normal((n_h * c, r_q)) / 8)
+    w_iuq = bf(rng.standard_normal((H_I * d_I, r_q)) / 8)
+    a = O.query_projections(h, w_dq, w_w, w_uq, w_iuq, np.ones(c), n_h, c, H_I, d_I, 1e-6)
+    b = O.query_projections(h, w_dq, w_w, w_uq, w_iuq, np.ones(c), n_h, c, H_I, d_I, 1e-6,
+                            qi_format="mxfp4")
+    assert np.array_equal(a["qi_pre"], b["qi_pre"]) and np.array_equal(a["q"], b["q"])
+    assert b["qi"].shape == (T, H_I, d_I // 2) and b["qi_scale"].shape == (T, H_I, d_I // 32)
+    p, sc = O.quantize_rows_mxfp4(b["qi_pre"])
+    assert np.array_equal(p, b["qi"]) and np.array_equal(sc, b["qi_scale"])
+    dec = O.mxfp4_decode(b["qi"], b["qi_scale"])
+    X = np.repeat(np.exp2(b["qi_scale"].astype(np.float64) - 127), 32, axis=-1)
+    y = b["qi_pre"] / X
+    step = np.where(np.abs(y) < 2, 0.5, np.where(np.abs(y) < 4, 1.0, 2.0))
+    clamp = np.maximum(np.abs(y) - 6.0, 0.0)  # a block's largest values may saturate at 6
+    assert np.all(np.abs(dec - b["qi_pre"]) / X <= 0.5 * step + clamp + 1e-12)
