@@ -53,7 +53,14 @@ extern "C" {
 #define CSA_IDX_E4M3 0  /* e4m3 codes [idx_dim] + one fp32 scale per entry (max|k|/448) */
 #define CSA_IDX_MXFP4 1 /* OCP MXFP4: E2M1 codes packed two per byte [idx_dim/2] (dim 2i in the
                            low nibble of byte i) + one E8M0 scale byte per 32 dims (shared
-                           exponent floor(log2 max|k|) - 2); the query stays e4m3 */
+                           exponent floor(log2 max|k|) - 2) */
+
+/* Index-score storage before the top-k (csa_config_t.score_format).  The pages store the
+ * indexer's scores in BF16 for a faster selector (Deep dive "论文专题讲解：DeepSeek-V4", section
+ * "FP4 QAT", table row "index scores": FP32 -> BF16). */
+#define CSA_SCORE_FP32 0 /* fp32 scores; selection exact on them */
+#define CSA_SCORE_BF16 1 /* each score rounded to bf16 (nearest even), top-k on the bf16 values,
+                            the lower index winning the ties this creates */
 
 /* Storage of the compressed entries (csa_config_t.entry_format). */
 #define CSA_ENT_BF16 0  /* head_dim bf16 values per entry */
@@ -79,7 +86,9 @@ extern "C" {
  *   rope_dim even, 2 <= rope_dim <= min(head_dim, 128);
  *   1 <= n_heads <= 128;  n_win in 1..1024;
  *   CSA: idx_dim in {32, 64, 128}, 1 <= idx_heads <= 64, 1 <= top_k <= 4096, m >= 1,
- *        idx_key_format CSA_IDX_E4M3 or CSA_IDX_MXFP4;
+ *        idx_key_format CSA_IDX_E4M3 or CSA_IDX_MXFP4; idx_query_format CSA_IDX_E4M3 or
+ *        CSA_IDX_MXFP4, the latter only with MXFP4 keys (CSA_ERR_UNSUPPORTED otherwise);
+ *        score_format CSA_SCORE_FP32 or CSA_SCORE_BF16;
  *   HCA: m >= 1;  hidden (compressor only) a positive multiple of 32;
  *   entry_format CSA_ENT_BF16 or CSA_ENT_MIXED (the latter: head_dim 512 and rope_dim a multiple
  *   of 16, CSA_ERR_UNSUPPORTED otherwise);
@@ -109,6 +118,14 @@ typedef struct csa_config {
   int32_t out_groups;
   int32_t out_rank;
   int32_t entry_format; /* CSA_ENT_BF16 (0) or CSA_ENT_MIXED (1) */
+  /* Format of the indexer query q^I (CSA).  CSA_IDX_E4M3: qi e4m3 [.., idx_heads, idx_dim] with
+   * qi_scale fp32 [.., idx_heads] (max|q|/448).  CSA_IDX_MXFP4 (the pages' FP4 QK path: query
+   * and keys both FP4, Deep dive "论文专题讲解：DeepSeek-V4", section "FP4 QAT", table row "CSA
+   * indexer QK path"): qi uint8 [.., idx_heads, idx_dim/2] packed E2M1 codes as the keys', and
+   * qi_scale the same 4 bytes per (token, head) holding its idx_dim/32 E8M0 block scales, block
+   * b in byte b (unused bytes are ignored). */
+  int32_t idx_query_format;
+  int32_t score_format;  /* CSA_SCORE_FP32 (0) or CSA_SCORE_BF16 (1); CSA only */
 } csa_config_t;
 
 /* Caller-owned per-sequence attention state for B sequences (all device pointers).
@@ -239,7 +256,8 @@ int csa_compress(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* 
  *  idx_out   int32 [B, nq, top_k]  selected entry indices in ascending order; when fewer
  *            than top_k entries are visible all of them are selected and the rest is -1.
  *            Ties at the k-th score go to the lower index.
- *  score_out fp32 [B, nq, top_k] or NULL: I_{t,s} of each selected index (-inf for -1 pads).
+ *  score_out fp32 [B, nq, top_k] or NULL: I_{t,s} of each selected index (-inf for -1 pads);
+ *            with CSA_SCORE_BF16 the bf16 value the selection ranked, widened to fp32.
  * Caches of more than 32768 entries (n_max) take at most 4096 query rows (B*nq) per call
  * (CSA_ERR_UNSUPPORTED otherwise; the same holds for csa_decode's B and csa_prefill's B*T).
  */
@@ -351,7 +369,9 @@ typedef struct csa_oproj_weights {
  *  q_out bf16 [B, T, n_heads, head_dim]: c^Q W^UQ, each head RMS-normalised over head_dim with
  *        gain gamma_q (eps = rms_eps), not rotated (the attention calls rotate it at t);
  *  qi_out e4m3 [B, T, idx_heads, idx_dim], qi_scale_out fp32 [B, T, idx_heads] (max|x|/448 per
- *        head), wi_out fp32 [B, T, idx_heads]: the csa_index_topk inputs (CSA; NULL for HCA).
+ *        head), wi_out fp32 [B, T, idx_heads]: the csa_index_topk inputs (CSA; NULL for HCA);
+ *        with idx_query_format CSA_IDX_MXFP4, qi_out packed MXFP4 [B, T, idx_heads, idx_dim/2]
+ *        and qi_scale_out its E8M0 block-scale bytes, 4 per head (as csa_config_t describes).
  * c^Q is kept in bf16 between the two products; all products accumulate in fp32.
  * Requires hidden and q_rank multiples of 64. */
 int csa_query_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,

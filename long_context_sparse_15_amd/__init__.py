@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
 MODE_CSA, MODE_HCA = 0, 1
 IDX_E4M3, IDX_MXFP4 = 0, 1
+SCORE_FP32, SCORE_BF16 = 0, 1
 ENT_BF16, ENT_MIXED = 0, 1
 (OP_COMPRESS, OP_INDEX_TOPK, OP_SPARSE_MQA, OP_HCA_MQA, OP_DECODE, OP_PREFILL, OP_QUERY_PROJ,
  OP_OUTPUT_PROJ) = range(8)
@@ -33,7 +34,8 @@ class Config(ctypes.Structure):
                 ("rms_eps", ctypes.c_float), ("rope_inv_freq", ctypes.c_void_p),
                 ("idx_key_format", ctypes.c_int32), ("q_rank", ctypes.c_int32),
                 ("out_groups", ctypes.c_int32), ("out_rank", ctypes.c_int32),
-                ("entry_format", ctypes.c_int32)]
+                ("entry_format", ctypes.c_int32), ("idx_query_format", ctypes.c_int32),
+                ("score_format", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -163,12 +165,14 @@ def _stream(stream):
 
 def make_config(mode, m, n_heads, head_dim, rope_dim, inv_freq, top_k=0, n_win=128,
                 idx_heads=0, idx_dim=0, hidden=0, softmax_scale=None, rms_eps=1e-6,
-                idx_key_format=0, q_rank=0, out_groups=0, out_rank=0, entry_format=0):
+                idx_key_format=0, q_rank=0, out_groups=0, out_rank=0, entry_format=0,
+                idx_query_format=0, score_format=0):
     """A Config; keeps a reference to the device inv_freq tensor for the config's lifetime."""
     cfg = Config(mode, m, top_k, n_win, n_heads, head_dim, rope_dim, idx_heads, idx_dim, hidden,
                  float(softmax_scale if softmax_scale is not None else head_dim ** -0.5),
                  float(rms_eps), _ptr(inv_freq).value, int(idx_key_format), int(q_rank),
-                 int(out_groups), int(out_rank), int(entry_format))
+                 int(out_groups), int(out_rank), int(entry_format), int(idx_query_format),
+                 int(score_format))
     cfg._keep = inv_freq
     return cfg
 

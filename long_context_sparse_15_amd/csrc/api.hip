@@ -85,6 +85,14 @@ int check_config(const csa_config_t* c, bool need_compressor) {
     if (c->idx_key_format != CSA_IDX_E4M3 && c->idx_key_format != CSA_IDX_MXFP4)
       return fail(CSA_ERR_INVALID_ARG, "idx_key_format=%d is neither E4M3 nor MXFP4",
                   c->idx_key_format);
+    if (c->idx_query_format != CSA_IDX_E4M3 && c->idx_query_format != CSA_IDX_MXFP4)
+      return fail(CSA_ERR_INVALID_ARG, "idx_query_format=%d is neither E4M3 nor MXFP4",
+                  c->idx_query_format);
+    if (c->idx_query_format == CSA_IDX_MXFP4 && c->idx_key_format != CSA_IDX_MXFP4)
+      return fail(CSA_ERR_UNSUPPORTED, "an MXFP4 indexer query needs MXFP4 keys");
+    if (c->score_format != CSA_SCORE_FP32 && c->score_format != CSA_SCORE_BF16)
+      return fail(CSA_ERR_INVALID_ARG, "score_format=%d is neither FP32 nor BF16",
+                  c->score_format);
   }
   if (c->entry_format != CSA_ENT_BF16 && c->entry_format != CSA_ENT_MIXED)
     return fail(CSA_ERR_INVALID_ARG, "entry_format=%d is neither BF16 nor MIXED",
@@ -198,7 +206,7 @@ size_t ws_compress(const csa_config_t* c, int B, int T) {
   return csa::compress_workspace(B, T, weight_cols(c));
 }
 size_t ws_index(const csa_config_t* c, int rows, int n_max) {
-  return csa::index_topk_workspace(rows, n_max, c->top_k);
+  return csa::index_topk_workspace(rows, n_max, c->top_k, c->score_format == CSA_SCORE_BF16);
 }
 size_t ws_mqa(const csa_config_t* c, int B, int nq, int max_list) {
   const csa::MqaPlan p = csa::plan_mqa(nq, c->n_heads, c->head_dim, max_list);
@@ -240,6 +248,8 @@ void fill_index_args(csa::IndexArgs& a, const csa_config_t* c, int B, int nq, co
   a.m = c->m;
   a.k = c->top_k;
   a.key_fmt = c->idx_key_format;
+  a.q_fmt = c->idx_query_format;
+  a.score_bf16 = c->score_format == CSA_SCORE_BF16;
   a.pages = page_map(k);
   a.idx_out = idx_out;
   a.score_out = score_out;
@@ -680,6 +690,7 @@ int csa_query_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t
   a.q = q_out;
   a.qi = csa_mode ? qi_out : nullptr;
   a.qi_scale = csa_mode ? qi_scale_out : nullptr;
+  a.qi_mx = csa_mode && cfg->idx_query_format == CSA_IDX_MXFP4;
   a.wi = csa_mode ? wi_out : nullptr;
   a.ws = workspace;
   const hipError_t e = csa::launch_query_proj(a, reinterpret_cast<hipStream_t>(stream));

@@ -53,6 +53,21 @@ __device__ __forceinline__ uint8_t e4m3_rne(float x) {
   return static_cast<uint8_t>(code | sign);
 }
 
+// E2M1 (OCP MXFP4 element: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to x, ties to the even
+// code, saturating at 6; the sign bit (bit 3) follows x's sign bit.
+__device__ __forceinline__ uint32_t e2m1_rne(float x) {
+  const float a = fabsf(x);
+  const uint32_t mag = a > 5.f     ? 7u
+                       : a >= 3.5f ? 6u
+                       : a > 2.5f  ? 5u
+                       : a >= 1.75f ? 4u
+                       : a > 1.25f ? 3u
+                       : a >= 0.75f ? 2u
+                       : a > 0.25f ? 1u
+                                   : 0u;
+  return mag | ((__float_as_uint(x) >> 28) & 8u);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }

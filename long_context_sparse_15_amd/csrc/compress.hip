@@ -297,21 +297,6 @@ hipError_t launch_gemm_tn(const GemmArgs& g, hipStream_t s) {
 
 
 // ============================================================================ helpers
-// E2M1 (OCP MXFP4 element: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to x, ties to the even
-// code, saturating at 6; the sign bit (bit 3) follows x's sign bit.
-__device__ __forceinline__ uint32_t e2m1_rne(float x) {
-  const float a = fabsf(x);
-  const uint32_t mag = a > 5.f     ? 7u
-                       : a >= 3.5f ? 6u
-                       : a > 2.5f  ? 5u
-                       : a >= 1.75f ? 4u
-                       : a > 1.25f ? 3u
-                       : a >= 0.75f ? 2u
-                       : a > 0.25f ? 1u
-                                   : 0u;
-  return mag | ((__float_as_uint(x) >> 28) & 8u);
-}
-
 __device__ float block_sum(float v, float* s_red) {
   const int tid = threadIdx.x;
   v = wave_sum_xor(v, 48);

@@ -7,6 +7,10 @@
 //   w_h ReLU(sq_h sk_s x) = sk_s (w_h sq_h) ReLU(x),
 // so the MFMA works on raw codes and the epilogue applies (w_h sq_h) per head and sk_s per entry.
 //
+// The indexer query may be MXFP4 too (both operands FP4: E2M1 codes with an E8M0 scale per 32
+// dims on each side, applied inside the scaled MFMA).  Scores may be stored as fp32 or, rounded
+// to nearest even, as bf16 ("index scores FP32 -> BF16"); the top-k then ranks the bf16 values.
+//
 // Top-k is exact with the lower index winning ties.  Scores become order-preserving 32-bit
 // keys.  Rows of up to 32768 entries use one workgroup per row with the keys in registers or
 // LDS: a sampled threshold, an exact select among the few candidates above it (or a radix
@@ -35,6 +39,39 @@ __device__ __forceinline__ int visible(const int32_t* n_entries, const int32_t* 
   return static_cast<int>(v < 0 ? 0 : v);
 }
 
+// Score rows in the workspace: fp32, or bf16 bit patterns (ST = uint16_t).  at() reads one score
+// as fp32 (bf16 widens exactly), four() the four scores from element e (e % 4 == 0: one 16-byte
+// or 8-byte load), put() stores one (bf16: nearest even).
+template <typename ST> struct Scores;
+template <> struct Scores<float> {
+  static __device__ __forceinline__ float at(const float* r, int e) { return r[e]; }
+  static __device__ __forceinline__ void four(const float* r, int e, float (&f)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(r + e);
+    f[0] = v.x;
+    f[1] = v.y;
+    f[2] = v.z;
+    f[3] = v.w;
+  }
+  static __device__ __forceinline__ void put(float* r, int e, float v) { r[e] = v; }
+  static __device__ __forceinline__ void put4(float* r, int e, f32x4 v) {
+    *reinterpret_cast<f32x4*>(r + e) = v;
+  }
+};
+template <> struct Scores<uint16_t> {
+  static __device__ __forceinline__ float at(const uint16_t* r, int e) { return bf16_to_f32(r[e]); }
+  static __device__ __forceinline__ void four(const uint16_t* r, int e, float (&f)[4]) {
+    const uint2 v = *reinterpret_cast<const uint2*>(r + e);
+    f[0] = __uint_as_float(v.x << 16);
+    f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16);
+    f[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+  static __device__ __forceinline__ void put(uint16_t* r, int e, float v) { r[e] = f32_to_bf16(v); }
+  static __device__ __forceinline__ void put4(uint16_t* r, int e, f32x4 v) {
+    *reinterpret_cast<uint2*>(r + e) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+};
+
 // ============================================================================ scoring
 // One workgroup scores `chunk` consecutive entries of one query row.  Each wave takes 16-entry
 // tiles; a tile is an MFMA with the indexer heads as the M dimension (A operand, resident in
@@ -45,13 +82,18 @@ __device__ __forceinline__ int visible(const int32_t* n_entries, const int32_t* 
 // operand gives lane group g dims 16g..16g+15 and 64+16g..64+16g+15 (both checked on the GPU).
 // PAGED: keys and scales live in a block pool (blocks of >= 16 entries, so a 16-entry tile lies
 // in one block); each tile's block comes from one scalar-cache load of the block table.
-template <int DI, int HT, int TPW, bool MX = false, bool PAGED = false>
+// QX (with MX): the query is MXFP4 too, the scaled MFMA's FP4 A operand: lane group g takes dims
+// 32g..32g+31 of its head (16 bytes of the packed row) and that block's E8M0 scale byte.
+// ST: the score type written (float, or uint16_t for bf16 scores).
+template <int DI, int HT, int TPW, bool MX = false, bool PAGED = false, bool QX = false,
+          typename ST = float>
 __global__ __launch_bounds__(256) void index_score_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ wi, const uint8_t* __restrict__ keys,
     const float* __restrict__ kscale, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int n_max, int H_I, int m, int chunk,
-    float* __restrict__ scores, int sstride, int nchunks, PageMap pm) {
+    ST* __restrict__ scores, int sstride, int nchunks, PageMap pm) {
+  static_assert(!QX || MX, "an FP4 query is paired with FP4 keys");
   constexpr int KB = DI / 4;   // key bytes per lane (its lane group's K slice)
   constexpr int KK = DI / 32;  // 8-byte MFMA steps per slice
 
@@ -77,9 +119,28 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   i32x8 aw[HT];
   long aq[HT][KK];
   float wq[HT][4];
+  int sq[HT];  // QX: this lane's query block scale (E8M0)
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const int head = ht * 16 + c16;
+    sq[ht] = 127;
+    if constexpr (QX) {  // packed E2M1 row of DI/2 bytes; blocks past DI are zero codes
+      const size_t rh = static_cast<size_t>(row) * H_I + (head < H_I ? head : 0);
+      const u32x4 v = (head < H_I && g < NBLK)
+                          ? reinterpret_cast<const u32x4*>(qi + rh * (DI / 2))[g]
+                          : u32x4{0, 0, 0, 0};
+      aw[ht] = i32x8{static_cast<int>(v[0]), static_cast<int>(v[1]), static_cast<int>(v[2]),
+                     static_cast<int>(v[3]), 0, 0, 0, 0};
+      if (head < H_I && g < NBLK)
+        sq[ht] = static_cast<int>((reinterpret_cast<const uint32_t*>(qi_scale)[rh] >> (8 * g)) &
+                                  0xffu);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = ht * 16 + g * 4 + i;
+        wq[ht][i] = hh < H_I ? wi[static_cast<size_t>(row) * H_I + hh] : 0.f;  // scale in MFMA
+      }
+      continue;
+    }
     const uint8_t* qrow = qi + (static_cast<size_t>(row) * H_I + (head < H_I ? head : 0)) * DI;
     const uint8_t* src = qrow + g * KB;
     if constexpr (kWide) {  // dims past DI (MXFP4 with DI < 128) are zero
@@ -110,7 +171,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const uint8_t* kbase = keys + seq0 * KROW + (kWide ? 0 : g * KB);
   const float* sbase = kscale + seq0;
   const uint32_t* swbase = reinterpret_cast<const uint32_t*>(sbase);  // MXFP4 scale bytes
-  float* srow = scores + static_cast<size_t>(row) * sstride;
+  ST* srow = scores + static_cast<size_t>(row) * sstride;
 
   // Wave `wave` scores tiles wave, wave+4, ... (TPW tiles of 16 entries).  The sequence is
   // fully unrolled straight-line code with PD tiles in flight; loads are unconditional (past
@@ -180,7 +241,13 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       // this lane's block scale (unit for the zero blocks past DI)
       const int sb = g < NBLK ? static_cast<int>((kt.sw >> (8 * g)) & 0xffu) : 127;
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_fp8_fp4_16x16x128(aw[ht], kt.w, acc[ht], sb);
+      for (int ht = 0; ht < HT; ++ht) {
+        if constexpr (QX)
+          acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[ht], kt.w, acc[ht], 4, 4,
+                                                                     0, sq[ht], 0, sb);
+        else
+          acc[ht] = mfma_fp8_fp4_16x16x128(aw[ht], kt.w, acc[ht], sb);
+      }
     } else if constexpr (kLine) {
       i32x8 w;
 #pragma unroll
@@ -210,7 +277,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     const int e = tile_entry(t);
     if (g == 0 && e < e1) {
       const float sc = MX ? part : part * kt.ks;  // MXFP4 scales act inside the MFMA
-      srow[e] = sc;
+      Scores<ST>::put(srow, e, sc);
     }
   };
   // The first tiles are loaded before the row's visible length is known (clamped to the
@@ -245,7 +312,9 @@ constexpr int kGemmWaves = 8;  // two waves per SIMD: one's epilogue overlaps an
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kGemmH = 64;   // largest head count held in LDS
 constexpr int kGemmDI = 128;
-constexpr size_t kGemmLds = kGemmH * kGemmQ * kGemmDI + kGemmH * kGemmQ * 4 + kGemmQ * 4;
+// LDS: query codes [h][q][128 B], head factors [h][q] fp32, query block scales [h][q] (4 E8M0
+// bytes, FP4 queries), visible counts [q]
+constexpr size_t kGemmLds = kGemmH * kGemmQ * kGemmDI + 2 * kGemmH * kGemmQ * 4 + kGemmQ * 4;
 
 // 16-byte chunk swizzle of the query rows in LDS: the 16 queries read at one chunk position
 // land in 16 distinct bank groups (rows are 128 bytes apart).
@@ -256,37 +325,50 @@ __device__ __forceinline__ int qswz(int q) { return (q >> 1) & 7; }
 // 64+16g..64+16g+15, i.e. 16-byte chunks g and 4+g of the query row).
 // PAGED: keys and scales in a block pool (blocks of >= 16 entries); each 16-entry block's pool
 // block comes from a scalar-cache load of the block table.
-template <bool MX, bool PAGED = false>
+// QX (with MX): the queries are MXFP4 too, the scaled MFMA's FP4 B operand (lane group g: dims
+// 32g..32g+31 of the query's head, i.e. 16-byte chunk g of its 64-byte packed row, and that
+// block's E8M0 scale byte).  ST: the score type written (float, or uint16_t for bf16 scores).
+template <bool MX, bool PAGED = false, bool QX = false, typename ST = float>
 __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ wi, const uint8_t* __restrict__ keys,
     const float* __restrict__ kscale, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int n_max, int H_I, int m, int qtiles,
-    float* __restrict__ scores, int sstride, PageMap pm) {
+    ST* __restrict__ scores, int sstride, PageMap pm) {
+  static_assert(!QX || MX, "an FP4 query is paired with FP4 keys");
   constexpr int DI = kGemmDI;
   constexpr int KROW = MX ? DI / 2 : DI;  // key bytes per entry
+  constexpr int QROW = QX ? DI / 2 : DI;  // query bytes per head
   extern __shared__ __align__(16) unsigned char smem[];
   uint8_t* s_q = smem;                                                   // [h][q][128] swizzled
   float* s_c = reinterpret_cast<float*>(smem + kGemmH * kGemmQ * DI);    // [h][q]: w * sq
-  int* s_nv = reinterpret_cast<int*>(s_c + kGemmH * kGemmQ);             // [q]: visible entries
+  uint32_t* s_qs = reinterpret_cast<uint32_t*>(s_c + kGemmH * kGemmQ);   // [h][q]: E8M0 x 4
+  int* s_nv = reinterpret_cast<int*>(s_qs + kGemmH * kGemmQ);            // [q]: visible entries
   // causal rows: the last query tiles carry the most entries and are dispatched first
   const int b = blockIdx.x / qtiles;
   const int t0 = (qtiles - 1 - blockIdx.x % qtiles) * kGemmQ;
   const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
   const int g = l >> 4, c16 = l & 15;
 
-  for (int ch = tid; ch < H_I * kGemmQ * 8; ch += kGemmThreads) {
-    const int h = ch / (kGemmQ * 8), q = (ch / 8) % kGemmQ, c = ch % 8;
+  constexpr int QCH = QROW / 16;  // 16-byte chunks of a query head
+  for (int ch = tid; ch < H_I * kGemmQ * QCH; ch += kGemmThreads) {
+    const int h = ch / (kGemmQ * QCH), q = (ch / QCH) % kGemmQ, c = ch % QCH;
     u32x4 v = u32x4{0, 0, 0, 0};
     if (t0 + q < nq)
       v = *reinterpret_cast<const u32x4*>(
-          qi + (static_cast<size_t>(b * nq + t0 + q) * H_I + h) * DI + c * 16);
+          qi + (static_cast<size_t>(b * nq + t0 + q) * H_I + h) * QROW + c * 16);
     *reinterpret_cast<u32x4*>(s_q + (h * kGemmQ + q) * DI + ((c ^ qswz(q)) << 4)) = v;
   }
   for (int i = tid; i < H_I * kGemmQ; i += kGemmThreads) {
     const int h = i / kGemmQ, q = i % kGemmQ;
     const size_t rh = static_cast<size_t>(b * nq + t0 + q) * H_I + h;
-    s_c[i] = (t0 + q < nq) ? wi[rh] * qi_scale[rh] : 0.f;
+    const bool ok = t0 + q < nq;
+    if constexpr (QX) {  // the scales act inside the MFMA; s_c is the head weight alone
+      s_c[i] = ok ? wi[rh] : 0.f;
+      s_qs[i] = ok ? reinterpret_cast<const uint32_t*>(qi_scale)[rh] : 0x7f7f7f7fu;
+    } else {
+      s_c[i] = ok ? wi[rh] * qi_scale[rh] : 0.f;
+    }
   }
   if (tid < kGemmQ)
     s_nv[tid] = (t0 + tid < nq) ? visible(n_entries, pos, b * nq + t0 + tid, nq, m, n_max) : 0;
@@ -302,7 +384,7 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
   const uint8_t* kb = keys + seq0 * KROW + g * (MX ? 16 : 32);
   const float* sb = kscale + seq0;
   const uint32_t* swb = reinterpret_cast<const uint32_t*>(sb);  // MXFP4 scale bytes
-  float* srow = scores + static_cast<size_t>(b * nq + t0 + c16) * sstride;
+  ST* srow = scores + static_cast<size_t>(b * nq + t0 + c16) * sstride;
   const bool row_ok = t0 + c16 < nq;
   // A operands of group G: entry G*64 + 16blk + c16 (clamped into the visible range), bytes
   // 32g..32g+31; entry scales of the 4 entries G*64 + 16blk + 4g + i this lane's D holds
@@ -354,23 +436,35 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
     // heads are software-pipelined: the four MFMAs of head h+1 are issued before the epilogue
     // of head h reads its results, and each head's query codes are read from LDS one step
     // before its MFMAs
+    // head h's B operand (and, FP4 queries, this lane's block scale in bq[4])
     auto readq = [&](int h, i32x8& bq, float& ch) {
       const uint8_t* qh = qb + min(h, H_I - 1) * kGemmQ * DI;
       const u32x4 lo = *reinterpret_cast<const u32x4*>(qh + ch0);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(qh + ch1);
-      bq = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
-                 static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
-                 static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+      if constexpr (QX) {
+        const uint32_t sw = s_qs[min(h, H_I - 1) * kGemmQ + c16];
+        bq = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                   static_cast<int>(lo[3]), static_cast<int>((sw >> (8 * g)) & 0xffu), 0, 0, 0};
+      } else {
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(qh + ch1);
+        bq = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                   static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                   static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+      }
       ch = s_c[min(h, H_I - 1) * kGemmQ + c16];
     };
     auto issue = [&](const i32x8& bq, f32x4 (&d)[4]) {
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        if constexpr (MX)
+        if constexpr (QX) {
+          const i32x8 b4 = i32x8{bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
+          d[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a[blk], b4, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa[blk], 0, bq[4]);
+        } else if constexpr (MX) {
           d[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               a[blk], bq, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, sa[blk], 0, 127);
-        else
+        } else {
           d[blk] = mfma_fp8_16x16x128(a[blk], bq, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
       }
     };
     // acc += max(d, 0) * ch; the ReLU is a signed integer max of the float's bits with 0
@@ -411,9 +505,9 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
     for (int blk = 0; blk < 4; ++blk) {
       const int e = G * 64 + blk * 16 + 4 * g;
       if (row_ok && e < my_nv)
-        *reinterpret_cast<f32x4*>(srow + e) =
-            f32x4{acc[blk][0] * ks[blk][0], acc[blk][1] * ks[blk][1], acc[blk][2] * ks[blk][2],
-                  acc[blk][3] * ks[blk][3]};
+        Scores<ST>::put4(srow, e,
+                         f32x4{acc[blk][0] * ks[blk][0], acc[blk][1] * ks[blk][1],
+                               acc[blk][2] * ks[blk][2], acc[blk][3] * ks[blk][3]});
       a[blk] = an[blk];
       ks[blk] = ksn[blk];
       sa[blk] = san[blk];
@@ -551,13 +645,13 @@ __device__ void ordered_emit_fn(KeyFn key, int n, uint32_t T, int need_eq, int c
 }
 
 // Emission straight into a row of the output (and its scores), padded with -1 / -inf.
-template <int THREADS, typename KeyFn>
+template <int THREADS, typename KeyFn, typename ST>
 __device__ void ordered_emit(KeyFn key, int n, uint32_t T, int need_eq, int kk, int k,
-                             const float* __restrict__ srow, int32_t* __restrict__ out,
+                             const ST* __restrict__ srow, int32_t* __restrict__ out,
                              float* __restrict__ sout, uint32_t* s_tmp) {
   ordered_emit_fn<THREADS>(key, n, T, need_eq, k, [&](int slot, int e) {
     out[slot] = e;
-    if (sout) sout[slot] = srow[e];
+    if (sout) sout[slot] = Scores<ST>::at(srow, e);
   });
   for (int j = kk + threadIdx.x; j < k; j += THREADS) {
     out[j] = -1;
@@ -699,9 +793,9 @@ __device__ void select_kth(KeyFn key, int n, int kk, uint32_t lo, uint32_t hi,
 // ============================================================================ per-row top-k
 // One workgroup per query row; the row's keys live in LDS when n_vis <= CAP, otherwise they are
 // re-read from the score row in global memory on every pass (exact, slower).
-template <int THREADS, int CAP>
+template <int THREADS, int CAP, typename ST>
 __global__ __launch_bounds__(THREADS) void topk_row_kernel(
-    const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const ST* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -715,11 +809,11 @@ __global__ __launch_bounds__(THREADS) void topk_row_kernel(
   const int kk = min(k, n_vis);
   int32_t* out = idx_out + static_cast<size_t>(row) * k;
   float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
-  const float* srow = scores + static_cast<size_t>(row) * sstride;
+  const ST* srow = scores + static_cast<size_t>(row) * sstride;
   if (n_vis <= k) {
     for (int j = tid; j < k; j += THREADS) {
       out[j] = j < n_vis ? j : -1;
-      if (sout) sout[j] = j < n_vis ? srow[j] : -INFINITY;
+      if (sout) sout[j] = j < n_vis ? Scores<ST>::at(srow, j) : -INFINITY;
     }
     return;
   }
@@ -727,21 +821,19 @@ __global__ __launch_bounds__(THREADS) void topk_row_kernel(
   int need_eq;
   if (n_vis <= CAP) {
     const int n4 = n_vis >> 2;
-    const float4* s4 = reinterpret_cast<const float4*>(srow);
     for (int i = tid; i < n4; i += THREADS) {
-      const float4 v = s4[i];
-      keys[4 * i + 0] = order_key(v.x);
-      keys[4 * i + 1] = order_key(v.y);
-      keys[4 * i + 2] = order_key(v.z);
-      keys[4 * i + 3] = order_key(v.w);
+      float v[4];
+      Scores<ST>::four(srow, 4 * i, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) keys[4 * i + j] = order_key(v[j]);
     }
-    for (int e = 4 * n4 + tid; e < n_vis; e += THREADS) keys[e] = order_key(srow[e]);
+    for (int e = 4 * n4 + tid; e < n_vis; e += THREADS) keys[e] = order_key(Scores<ST>::at(srow, e));
     __syncthreads();
     auto kf = [&](int e) { return keys[e]; };
     radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
     ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
   } else {
-    auto kf = [&](int e) { return order_key(srow[e]); };
+    auto kf = [&](int e) { return order_key(Scores<ST>::at(srow, e)); };
     radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
     ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
   }
@@ -762,9 +854,9 @@ __global__ __launch_bounds__(THREADS) void topk_row_kernel(
 //  4. the index-ordered emission over the candidate list writes the keys above T and the first
 //     ties, so the selection comes out sorted with the lowest indices winning ties.
 // If the count misses [kk, kCandCap] (ties, adversarial data) the exact streaming select runs.
-template <int THREADS, int PER>
+template <int THREADS, int PER, typename ST>
 __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
-    const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const ST* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
   constexpr int CH = PER / 4;             // chunks per thread
@@ -788,11 +880,11 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
   const int kk = min(k, n_vis);
   int32_t* out = idx_out + static_cast<size_t>(row) * k;
   float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
-  const float* srow = scores + static_cast<size_t>(row) * sstride;
+  const ST* srow = scores + static_cast<size_t>(row) * sstride;
   if (n_vis <= k) {
     for (int j = tid; j < k; j += THREADS) {
       out[j] = j < n_vis ? j : -1;
-      if (sout) sout[j] = j < n_vis ? srow[j] : -INFINITY;
+      if (sout) sout[j] = j < n_vis ? Scores<ST>::at(srow, j) : -INFINITY;
     }
     return;
   }
@@ -804,8 +896,8 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
     const int base = (i * THREADS + tid) * 4;
     // the address depends only on the row length, not on n_vis, so the loads need not wait for
     // the row's position and entry count
-    const float4 v = *reinterpret_cast<const float4*>(srow + min(base, sstride - 4));
-    const float f[4] = {v.x, v.y, v.z, v.w};
+    float f[4];
+    Scores<ST>::four(srow, min(base, sstride - 4), f);
 #pragma unroll
     for (int j = 0; j < 4; ++j) kr[i * 4 + j] = (base + j < n_vis) ? order_key(f[j]) : 0u;
   }
@@ -819,7 +911,7 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
         if ((i * THREADS + tid) * 4 == last) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (last + j < n_vis) kr[i * 4 + j] = order_key(srow[last + j]);
+            if (last + j < n_vis) kr[i * 4 + j] = order_key(Scores<ST>::at(srow, last + j));
         }
     }
   }
@@ -930,7 +1022,7 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
     ordered_emit_fn<THREADS>(cf, static_cast<int>(cnt), T, need_eq, k, [&](int o, int j) {
       const int e = s_cidx[j];
       out[o] = e;
-      if (sout) sout[o] = srow[e];
+      if (sout) sout[o] = Scores<ST>::at(srow, e);
     });
     for (int j = kk + tid; j < k; j += THREADS) {
       out[j] = -1;
@@ -940,7 +1032,7 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
   }
   uint32_t T;
   int need_eq;
-  auto gk = [&](int e) { return order_key(srow[e]); };
+  auto gk = [&](int e) { return order_key(Scores<ST>::at(srow, e)); };
   radix_select<THREADS>(gk, n_vis, kk, s_hist, s_tmp, s_res, T, need_eq);
   ordered_emit<THREADS>(gk, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
 }
@@ -981,8 +1073,9 @@ constexpr int kCandPerChunk = 1024;
 constexpr int kSCandCap = 8192;  // candidates of a row held by its finalize workgroup
 constexpr size_t kMultiLds = static_cast<size_t>(kSCandCap) * 8 + kHistBins * 4;
 
+template <typename ST>
 __global__ __launch_bounds__(1024) void topk_collect_kernel(
-    const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const ST* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int nchunks,
     uint32_t* __restrict__ ccount, uint64_t* __restrict__ cand) {
   constexpr int THREADS = 1024, PER = kCollectChunk / THREADS;
@@ -996,7 +1089,7 @@ __global__ __launch_bounds__(1024) void topk_collect_kernel(
   const int tid = threadIdx.x;
   const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
   const int kk = min(k, n_vis);
-  const float* srow = scores + static_cast<size_t>(row) * sstride;
+  const ST* srow = scores + static_cast<size_t>(row) * sstride;
   if (n_vis <= k) return;  // everything is selected; finalize does not read the regions
   const int used = (n_vis + kCollectChunk - 1) / kCollectChunk;  // chunks holding visible keys
   if (chunk >= used) return;
@@ -1009,8 +1102,8 @@ __global__ __launch_bounds__(1024) void topk_collect_kernel(
   uint32_t key[PER];
   {
     const int base = e0 + tid * PER;
-    const float4 v = *reinterpret_cast<const float4*>(srow + min(base, sstride - 4));
-    const float f[4] = {v.x, v.y, v.z, v.w};
+    float f[4];
+    Scores<ST>::four(srow, min(base, sstride - 4), f);
 #pragma unroll
     for (int j = 0; j < 4; ++j) key[j] = base + j < n_vis ? order_key(f[j]) : 0u;
   }
@@ -1056,8 +1149,9 @@ __global__ __launch_bounds__(1024) void topk_collect_kernel(
   }
 }
 
+template <typename ST>
 __global__ __launch_bounds__(1024) void topk_finalize_kernel(
-    const float* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const ST* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int nchunks,
     const uint32_t* __restrict__ ccount, const uint64_t* __restrict__ cand,
     int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
@@ -1077,11 +1171,11 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   const int kk = min(k, n_vis);
   int32_t* out = idx_out + static_cast<size_t>(row) * k;
   float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
-  const float* srow = scores + static_cast<size_t>(row) * sstride;
+  const ST* srow = scores + static_cast<size_t>(row) * sstride;
   if (n_vis <= k) {  // everything is selected
     for (int j = tid; j < k; j += THREADS) {
       out[j] = j < n_vis ? j : -1;
-      if (sout) sout[j] = j < n_vis ? srow[j] : -INFINITY;
+      if (sout) sout[j] = j < n_vis ? Scores<ST>::at(srow, j) : -INFINITY;
     }
     return;
   }
@@ -1111,7 +1205,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   if (s_flag) {
     uint32_t T;
     int need_eq;
-    auto kf = [&](int e) { return order_key(srow[e]); };
+    auto kf = [&](int e) { return order_key(Scores<ST>::at(srow, e)); };
     radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
     ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
     return;
@@ -1143,7 +1237,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   auto ck = [&](int j) { return ckey[j]; };
   select_kth<THREADS>(ck, nc, kk, s_lo, s_hi, hist, s_tmp, s_res, T, need_eq);
   if (T < s_tmax) {  // some chunk's threshold cut keys that reach T: exact streaming select
-    auto kf = [&](int e) { return order_key(srow[e]); };
+    auto kf = [&](int e) { return order_key(Scores<ST>::at(srow, e)); };
     radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
     ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
     return;
@@ -1151,7 +1245,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   // the candidate list is in ascending index order
   ordered_emit_fn<THREADS>(ck, nc, T, need_eq, k, [&](int slot, int j) {
     out[slot] = cidx[j];
-    if (sout) sout[slot] = srow[cidx[j]];
+    if (sout) sout[slot] = Scores<ST>::at(srow, cidx[j]);
   });
   for (int j = kk + tid; j < k; j += THREADS) {
     out[j] = -1;
@@ -1172,8 +1266,9 @@ bool index_use_multi(int rows, int n_max) {
 
 static int collect_chunks(int n_max) { return (n_max + kCollectChunk - 1) / kCollectChunk; }
 
-size_t index_topk_workspace(int rows, int n_max, int k) {
-  size_t b = align256(static_cast<size_t>(rows) * score_stride(n_max) * sizeof(float));
+size_t index_topk_workspace(int rows, int n_max, int k, bool score_bf16) {
+  const size_t sb = score_bf16 ? 2 : 4;
+  size_t b = align256(static_cast<size_t>(rows) * score_stride(n_max) * sb);
   if (index_use_multi(rows, n_max)) {
     const size_t rc = static_cast<size_t>(rows) * collect_chunks(n_max);
     b += align256(rc * 8);  // (count, threshold) per chunk
@@ -1186,8 +1281,8 @@ size_t index_topk_workspace(int rows, int n_max, int k) {
 void index_topk_layout(IndexArgs& a, void* ws, int rows) {
   unsigned char* p = static_cast<unsigned char*>(ws);
   a.sstride = score_stride(a.n_max);
-  a.scores = reinterpret_cast<float*>(p);
-  p += align256(static_cast<size_t>(rows) * a.sstride * sizeof(float));
+  a.scores = p;
+  p += align256(static_cast<size_t>(rows) * a.sstride * (a.score_bf16 ? 2 : 4));
   a.counters = nullptr;
   a.cand = nullptr;
   if (index_use_multi(rows, a.n_max)) {
@@ -1204,36 +1299,40 @@ void index_topk_layout(IndexArgs& a, void* ws, int rows) {
 constexpr int kScoreTPW = CSA_SCORE_TPW;       // tiles of 16 entries per wave
 constexpr int kScoreChunk = 4 * kScoreTPW * 16;  // entries per workgroup
 
-template <int DI, int HT, bool MX, bool PAGED>
+template <int DI, int HT, bool MX, bool PAGED, bool QX, typename ST>
 static void launch_scores_k(const IndexArgs& a, int chunk, int nchunks, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(nchunks) * static_cast<unsigned>(a.B * a.nq);
-  index_score_kernel<DI, HT, kScoreTPW, MX, PAGED><<<grid, 256, 0, s>>>(
+  index_score_kernel<DI, HT, kScoreTPW, MX, PAGED, QX, ST><<<grid, 256, 0, s>>>(
       a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
-      chunk, a.scores, a.sstride, nchunks, a.pages);
+      chunk, static_cast<ST*>(a.scores), a.sstride, nchunks, a.pages);
 }
-template <int DI, int HT>
+template <int DI, int HT, bool MX, bool QX, typename ST>
+static void launch_scores_p(const IndexArgs& a, int chunk, int nchunks, hipStream_t s) {
+  if (a.pages.table != nullptr)
+    launch_scores_k<DI, HT, MX, true, QX, ST>(a, chunk, nchunks, s);
+  else
+    launch_scores_k<DI, HT, MX, false, QX, ST>(a, chunk, nchunks, s);
+}
+template <int DI, int HT, typename ST>
 static void launch_scores_t(const IndexArgs& a, int chunk, int nchunks, hipStream_t s) {
   ProfScope ps("index_score", s);
-  const bool paged = a.pages.table != nullptr;
   if (a.key_fmt == 1) {
-    if (paged)
-      launch_scores_k<DI, HT, true, true>(a, chunk, nchunks, s);
+    if (a.q_fmt == 1)
+      launch_scores_p<DI, HT, true, true, ST>(a, chunk, nchunks, s);
     else
-      launch_scores_k<DI, HT, true, false>(a, chunk, nchunks, s);
+      launch_scores_p<DI, HT, true, false, ST>(a, chunk, nchunks, s);
   } else {
-    if (paged)
-      launch_scores_k<DI, HT, false, true>(a, chunk, nchunks, s);
-    else
-      launch_scores_k<DI, HT, false, false>(a, chunk, nchunks, s);
+    launch_scores_p<DI, HT, false, false, ST>(a, chunk, nchunks, s);
   }
 }
 
+template <typename ST>
 static hipError_t launch_scores(const IndexArgs& a, int chunk, hipStream_t s) {
   const int nchunks = (a.n_max + chunk - 1) / chunk;
   const int ht = (a.H_I + 15) / 16;
 #define CSA_SCORE_CASE(DI_, HT_)                            \
   if (a.d_I == DI_ && ht == HT_) {                         \
-    launch_scores_t<DI_, HT_>(a, chunk, nchunks, s);              \
+    launch_scores_t<DI_, HT_, ST>(a, chunk, nchunks, s);    \
     return hipGetLastError();                              \
   }
   CSA_SCORE_CASE(128, 4)
@@ -1252,16 +1351,16 @@ static hipError_t launch_scores(const IndexArgs& a, int chunk, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int THREADS, int CAP>
+template <int THREADS, int CAP, typename ST>
 static hipError_t launch_row_topk(const IndexArgs& a, int rows, hipStream_t s) {
   const size_t lds = (static_cast<size_t>(CAP) + kHistBins) * 4;
-  if (hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(topk_row_kernel<THREADS, CAP>),
-                                    lds))
+  if (hipError_t e =
+          ensure_max_lds(reinterpret_cast<const void*>(topk_row_kernel<THREADS, CAP, ST>), lds))
     return e;
   ProfScope ps("topk_row", s);
-  topk_row_kernel<THREADS, CAP><<<rows, THREADS, lds, s>>>(a.scores, a.sstride, a.n_entries,
-                                                           a.pos, a.nq, a.m, a.k, a.n_max,
-                                                           a.idx_out, a.score_out);
+  topk_row_kernel<THREADS, CAP, ST><<<rows, THREADS, lds, s>>>(
+      static_cast<const ST*>(a.scores), a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max,
+      a.idx_out, a.score_out);
   return hipGetLastError();
 }
 
@@ -1271,67 +1370,78 @@ static bool use_gemm_scores(const IndexArgs& a) {
   return a.nq >= kGemmQ && a.d_I == kGemmDI && a.H_I <= kGemmH;
 }
 
-template <bool MX, bool PAGED>
+template <bool MX, bool PAGED, bool QX, typename ST>
 static hipError_t launch_gemm_scores_t(const IndexArgs& a, hipStream_t s) {
-  if (hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_gemm_kernel<MX, PAGED>),
-                                    kGemmLds))
+  if (hipError_t e = ensure_max_lds(
+          reinterpret_cast<const void*>(index_gemm_kernel<MX, PAGED, QX, ST>), kGemmLds))
     return e;
   const int qtiles = (a.nq + kGemmQ - 1) / kGemmQ;
   ProfScope ps("index_score", s);
-  index_gemm_kernel<MX, PAGED>
+  index_gemm_kernel<MX, PAGED, QX, ST>
       <<<static_cast<unsigned>(a.B) * qtiles, kGemmThreads, kGemmLds, s>>>(
           a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I,
-          a.m, qtiles, a.scores, a.sstride, a.pages);
+          a.m, qtiles, static_cast<ST*>(a.scores), a.sstride, a.pages);
   return hipGetLastError();
 }
 
-static hipError_t launch_gemm_scores(const IndexArgs& a, hipStream_t s) {
-  if (a.pages.table)
-    return a.key_fmt == 1 ? launch_gemm_scores_t<true, true>(a, s)
-                          : launch_gemm_scores_t<false, true>(a, s);
-  return a.key_fmt == 1 ? launch_gemm_scores_t<true, false>(a, s)
-                        : launch_gemm_scores_t<false, false>(a, s);
+template <bool MX, bool QX, typename ST>
+static hipError_t launch_gemm_scores_p(const IndexArgs& a, hipStream_t s) {
+  return a.pages.table ? launch_gemm_scores_t<MX, true, QX, ST>(a, s)
+                       : launch_gemm_scores_t<MX, false, QX, ST>(a, s);
 }
 
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
+template <typename ST>
+static hipError_t launch_gemm_scores(const IndexArgs& a, hipStream_t s) {
+  if (a.key_fmt != 1) return launch_gemm_scores_p<false, false, ST>(a, s);
+  return a.q_fmt == 1 ? launch_gemm_scores_p<true, true, ST>(a, s)
+                      : launch_gemm_scores_p<true, false, ST>(a, s);
+}
+
+template <typename ST>
+static hipError_t launch_index_topk_t(const IndexArgs& a, hipStream_t s) {
   const int rows = a.B * a.nq;
   const bool multi = index_use_multi(rows, a.n_max);
-  hipError_t e = (!multi && use_gemm_scores(a)) ? launch_gemm_scores(a, s)
-                                                : launch_scores(a, kScoreChunk, s);
+  hipError_t e = (!multi && use_gemm_scores(a)) ? launch_gemm_scores<ST>(a, s)
+                                                : launch_scores<ST>(a, kScoreChunk, s);
   if (e != hipSuccess) return e;
+  const ST* sc = static_cast<const ST*>(a.scores);
   if (!multi) {
-    if (a.n_max <= 4096) return launch_row_topk<256, kRowTopkMaxN>(a, rows, s);
+    if (a.n_max <= 4096) return launch_row_topk<256, kRowTopkMaxN, ST>(a, rows, s);
     if (a.n_max <= 16384) {
       ProfScope ps("topk_sample", s);
       // 512 threads x 32 keys (measured 1.83 ms against 2.89 ms for 256 x 64 and 3.68 ms for
       // 1024 x 32 on the 64K-token prefill rows)
-      topk_sample_kernel<512, 32><<<rows, 512, 0, s>>>(a.scores, a.sstride, a.n_entries, a.pos,
-                                                      a.nq, a.m, a.k, a.n_max, a.idx_out,
-                                                      a.score_out);
+      topk_sample_kernel<512, 32, ST><<<rows, 512, 0, s>>>(sc, a.sstride, a.n_entries, a.pos,
+                                                          a.nq, a.m, a.k, a.n_max, a.idx_out,
+                                                          a.score_out);
       return hipGetLastError();
     }
     ProfScope ps("topk_sample", s);
-    topk_sample_kernel<1024, 32><<<rows, 1024, 0, s>>>(a.scores, a.sstride, a.n_entries, a.pos,
-                                                      a.nq, a.m, a.k, a.n_max, a.idx_out,
-                                                      a.score_out);
+    topk_sample_kernel<1024, 32, ST><<<rows, 1024, 0, s>>>(sc, a.sstride, a.n_entries, a.pos,
+                                                          a.nq, a.m, a.k, a.n_max, a.idx_out,
+                                                          a.score_out);
     return hipGetLastError();
   }
   const int ncc = collect_chunks(a.n_max);
   {
     ProfScope ps("topk_collect", s);
-    topk_collect_kernel<<<static_cast<unsigned>(ncc) * rows, 1024, 0, s>>>(
-        a.scores, a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, ncc, a.counters,
-        a.cand);
+    topk_collect_kernel<ST><<<static_cast<unsigned>(ncc) * rows, 1024, 0, s>>>(
+        sc, a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, ncc, a.counters, a.cand);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = ensure_max_lds(reinterpret_cast<const void*>(topk_finalize_kernel), kMultiLds)))
+  if ((e = ensure_max_lds(reinterpret_cast<const void*>(topk_finalize_kernel<ST>), kMultiLds)))
     return e;
   ProfScope ps("topk_finalize", s);
-  topk_finalize_kernel<<<rows, 1024, kMultiLds, s>>>(a.scores, a.sstride, a.n_entries, a.pos,
-                                                     a.nq, a.m, a.k, a.n_max, ncc, a.counters,
-                                                     a.cand, a.idx_out, a.score_out);
+  topk_finalize_kernel<ST><<<rows, 1024, kMultiLds, s>>>(sc, a.sstride, a.n_entries, a.pos,
+                                                         a.nq, a.m, a.k, a.n_max, ncc,
+                                                         a.counters, a.cand, a.idx_out,
+                                                         a.score_out);
   return hipGetLastError();
+}
+
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
+  return a.score_bf16 ? launch_index_topk_t<uint16_t>(a, s) : launch_index_topk_t<float>(a, s);
 }
 
 }  // namespace csa

@@ -53,8 +53,11 @@ struct IndexArgs {
   const int32_t* pos;     // [rows] or nullptr (t = query index within its sequence)
   int B, nq, n_max, H_I, d_I, m, k;
   int key_fmt;            // 0 e4m3 + fp32 scale, 1 MXFP4
+  int q_fmt;              // 0 e4m3 + fp32 scale per head, 1 MXFP4 (qi [rows, H_I, d_I/2], qi_scale
+                          // 4 E8M0 bytes per head); 1 needs key_fmt 1
+  bool score_bf16;        // scores stored as bf16 (nearest even) instead of fp32
   PageMap pages;          // layout of keys and kscale (paged: blocks of >= 16 entries)
-  float* scores;          // workspace [rows, sstride]
+  void* scores;           // workspace [rows, sstride] fp32 or bf16
   int sstride;
   uint32_t* counters;     // workspace [rows, chunks, 2]: candidates and threshold of each chunk
   uint64_t* cand;         // workspace [rows, chunks, candidates per chunk]: (key, index)
@@ -64,7 +67,7 @@ struct IndexArgs {
 // Rows longer than kRowTopkBigN (and not too many) use the multi-workgroup select.
 constexpr int kMultiMaxRows = 4096;
 bool index_use_multi(int rows, int n_max);
-size_t index_topk_workspace(int rows, int n_max, int k);
+size_t index_topk_workspace(int rows, int n_max, int k, bool score_bf16);
 void index_topk_layout(IndexArgs& a, void* ws, int rows);  // needs a.n_max and a.k set
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
 
@@ -150,8 +153,9 @@ struct QueryProjArgs {
   const uint16_t* w_iuq;  // [H_I * d_I, r_q] or nullptr
   const float* gamma_q;   // [c]
   uint16_t* q;            // [BT, n_h, c]
-  uint8_t* qi;            // [BT, H_I, d_I] or nullptr
-  float* qi_scale;        // [BT, H_I] or nullptr
+  uint8_t* qi;            // [BT, H_I, d_I] (MXFP4: [BT, H_I, d_I/2]) or nullptr
+  float* qi_scale;        // [BT, H_I] fp32 (MXFP4: 4 E8M0 bytes per head) or nullptr
+  bool qi_mx;             // indexer query as MXFP4
   float* wi;              // [BT, H_I] or nullptr
   void* ws;
 };

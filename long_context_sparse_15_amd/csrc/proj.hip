@@ -7,7 +7,8 @@
 //   O = Concat_u O^[u],  z^[u] = O^[u] W^[u]_down (rank r_o),  y = Proj(Concat_u z^[u]).
 // The attention query is c^Q W^UQ normalised per head.  Intermediates: c^Q and z are stored in
 // bf16; q in bf16 (unrotated; RoPE happens in the attention kernels); q^I as E4M3 codes with one
-// fp32 scale per (token, head), max|x| / 448; w^I in fp32.
+// fp32 scale per (token, head), max|x| / 448, or (FP4 indexer query) as MXFP4: E2M1 codes with
+// one E8M0 scale per 32 dims, shared exponent floor(log2 max|x|) - 2; w^I in fp32.
 //
 // Every product is the large-tile bf16 MFMA GEMM (launch_gemm_tn, fp32 accumulation).  The
 // query up-projection writes its bf16 result straight into q (the attention-query heads) and a
@@ -55,8 +56,10 @@ struct alignas(4 * N) Words {
 // in place with gain gamma): a wave takes a head per pass, lane l the c/64 consecutive values
 // from c/64*l, loaded as one vector; each wave keeps UNR heads' loads in flight before it
 // reduces.  Indexer-query heads (d_I values of P each, E4M3 with max|x|/448 scale): d_I/8 lanes
-// per head, 8 values (16 bytes) per lane, 64/(d_I/8) heads per wave pass.
-template <int C, int DI>
+// per head, 8 values (16 bytes) per lane, 64/(d_I/8) heads per wave pass.  MX: MXFP4 instead,
+// four lanes per 32-dim block: the block's max from two lane swaps, E8M0 byte from its binary
+// exponent, 8 E2M1 codes (one dword) per lane.
+template <int C, int DI, bool MX>
 __global__ __launch_bounds__(256) void query_finish_kernel(
     const uint16_t* __restrict__ P, int ldp, int n_h, int H_I, const float* __restrict__ gamma,
     float eps, uint16_t* __restrict__ q, uint8_t* __restrict__ qi, float* __restrict__ qi_scale) {
@@ -109,6 +112,21 @@ __global__ __launch_bounds__(256) void query_finish_kernel(
       x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
       am = fmaxf(am, fmaxf(fabsf(x[2 * j]), fabsf(x[2 * j + 1])));
     }
+    if constexpr (MX) {
+      am = fmaxf(am, __shfl_xor(am, 1, 64));
+      am = fmaxf(am, __shfl_xor(am, 2, 64));
+      int ex;
+      (void)frexpf(am, &ex);  // am = f 2^ex, f in [0.5, 1): floor(log2 am) = ex - 1
+      const int se = am > 0.f ? min(max(ex - 3, -127), 127) : -127;
+      uint32_t code = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) code |= e2m1_rne(ldexpf(x[j], -se)) << (4 * j);
+      const size_t rh = static_cast<size_t>(row) * H_I + h;
+      *reinterpret_cast<uint32_t*>(qi + rh * (DI / 2) + sub * 4) = code;
+      if ((sub & 3) == 0)
+        reinterpret_cast<uint8_t*>(qi_scale)[rh * 4 + (sub >> 2)] = static_cast<uint8_t>(se + 127);
+      continue;
+    }
 #pragma unroll
     for (int off = LPH / 2; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
     const float scale = am > 0.f ? am / 448.f : 1.f;
@@ -128,8 +146,14 @@ __global__ __launch_bounds__(256) void query_finish_kernel(
 template <int C, int DI>
 hipError_t launch_finish(const uint16_t* P, int ldp, const QueryProjArgs& a, hipStream_t s) {
   ProfScope ps("qproj_finish", s);
-  query_finish_kernel<C, DI><<<a.BT, 256, 0, s>>>(P, ldp, a.n_h, a.qi ? a.H_I : 0, a.gamma_q,
-                                                   a.eps, a.q, a.qi, a.qi_scale);
+  if (a.qi_mx)
+    query_finish_kernel<C, DI, true><<<a.BT, 256, 0, s>>>(P, ldp, a.n_h, a.qi ? a.H_I : 0,
+                                                          a.gamma_q, a.eps, a.q, a.qi,
+                                                          a.qi_scale);
+  else
+    query_finish_kernel<C, DI, false><<<a.BT, 256, 0, s>>>(P, ldp, a.n_h, a.qi ? a.H_I : 0,
+                                                           a.gamma_q, a.eps, a.q, a.qi,
+                                                           a.qi_scale);
   return hipGetLastError();
 }
 

@@ -3,7 +3,8 @@
 Same recipe as synth.inputs (bf16 = normal draws truncated to their upper 16 bits; E4M3 codes
 assembled from sign/exponent of a normal draw plus uniform mantissa bits; uniform scales),
 drawn from torch's device generator instead of numpy PCG64 so that gigabyte-sized workloads
-are produced in milliseconds.  Parity tests use synth.inputs; these tensors are only timed.
+are produced in milliseconds: the benchmark times them, and the full-size parity tests check
+the kernels on them against the oracle (fed host copies of the same tensors).
 """
 import torch
 
@@ -78,7 +79,8 @@ def mixed_entries(g, shape, c, r, device):
     return torch.cat([codes, rope], dim=-1).contiguous()
 
 
-def decode_cache_inputs(w, device="cuda", seed=None, key_fmt="e4m3", entry_fmt="bf16"):
+def decode_cache_inputs(w, device="cuda", seed=None, key_fmt="e4m3", entry_fmt="bf16",
+                        qi_fmt="e4m3"):
     """As synth.inputs.decode_cache_inputs, on the device (entry_fmt "mixed": entries as
     mixed_entries rows)."""
     g = _gen(w.seed if seed is None else seed, device)
@@ -97,15 +99,18 @@ def decode_cache_inputs(w, device="cuda", seed=None, key_fmt="e4m3", entry_fmt="
     out["inv_freq"] = torch.from_numpy(rope_inv_freq(w.r, w.rope_base)).to(device)
     out["pos"] = torch.full((B,), w.t, dtype=torch.int32, device=device)
     out["n_entries"] = torch.full((B,), N, dtype=torch.int32, device=device)
-    _queries(g, w, 1, out, device)
+    _queries(g, w, 1, out, device, qi_fmt)
     return out
 
 
-def _queries(g, w, nq, out, device):
+def _queries(g, w, nq, out, device, qi_fmt="e4m3"):
     out["q"] = bf16_normal(g, (w.B, nq, w.n_h, w.c), device)
     if w.mode == "csa":
-        out["qi"] = e4m3_normalish(g, (w.B, nq, w.H_I, w.d_I), device)
-        out["qi_scale"] = _uniform(g, (w.B, nq, w.H_I), device, 0.5, 1.5) / 16
+        if qi_fmt == "mxfp4":
+            out["qi"], out["qi_scale"] = mxfp4_normalish(g, (w.B, nq, w.H_I), w.d_I, device)
+        else:
+            out["qi"] = e4m3_normalish(g, (w.B, nq, w.H_I, w.d_I), device)
+            out["qi_scale"] = _uniform(g, (w.B, nq, w.H_I), device, 0.5, 1.5) / 16
         out["wi"] = torch.randn(w.B, nq, w.H_I, generator=g, device=device) / 8
     if w.sink is None:
         out["sink"] = torch.randn(w.n_h, generator=g, device=device)
@@ -113,7 +118,7 @@ def _queries(g, w, nq, out, device):
         out["sink"] = torch.full((w.n_h,), w.sink, device=device)
 
 
-def layer_inputs(w, device="cuda", seed=None):
+def layer_inputs(w, device="cuda", seed=None, qi_fmt="e4m3"):
     """As synth.inputs.layer_inputs (prefill of w.T tokens, no decode tokens), on the device."""
     g = _gen(w.seed if seed is None else seed, device)
     T = w.T
@@ -128,5 +133,5 @@ def layer_inputs(w, device="cuda", seed=None):
     out["gamma"] = 1.0 + 0.1 * torch.randn(w.c, generator=g, device=device)
     out["gamma_win"] = 1.0 + 0.1 * torch.randn(w.c, generator=g, device=device)
     out["inv_freq"] = torch.from_numpy(rope_inv_freq(w.r, w.rope_base)).to(device)
-    _queries(g, w, T, out, device)
+    _queries(g, w, T, out, device, qi_fmt)
     return out

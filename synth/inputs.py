@@ -109,11 +109,14 @@ def tail_shape(w):
     return w.m, 2 * w.c
 
 
-def _queries(rng, w, nq, out):
+def _queries(rng, w, nq, out, qi_fmt="e4m3"):
     out["q"] = bf16_normal(rng, (w.B, nq, w.n_h, w.c))
     if w.mode == "csa":
-        out["qi"] = e4m3_normalish(rng, (w.B, nq, w.H_I, w.d_I))
-        out["qi_scale"] = rng.uniform(0.5, 1.5, size=(w.B, nq, w.H_I)).astype(np.float32) / 16
+        if qi_fmt == "mxfp4":  # packed codes [.., H_I, d_I/2] and 4 E8M0 bytes per head
+            out["qi"], out["qi_scale"] = mxfp4_normalish(rng, (w.B, nq, w.H_I), w.d_I)
+        else:
+            out["qi"] = e4m3_normalish(rng, (w.B, nq, w.H_I, w.d_I))
+            out["qi_scale"] = rng.uniform(0.5, 1.5, size=(w.B, nq, w.H_I)).astype(np.float32) / 16
         out["wi"] = (rng.standard_normal((w.B, nq, w.H_I), dtype=np.float32) / 8)
     if w.sink is None:
         out["sink"] = rng.standard_normal(w.n_h, dtype=np.float32)
@@ -121,7 +124,7 @@ def _queries(rng, w, nq, out):
         out["sink"] = np.full(w.n_h, w.sink, dtype=np.float32)
 
 
-def layer_inputs(w, seed=None, T=None):
+def layer_inputs(w, seed=None, T=None, qi_fmt="e4m3"):
     """Inputs of a whole layer run from hidden states: prefill of T tokens (default w.T) plus
     w.decode_steps decode tokens.  Arrays are indexed [B, token, ...]; the compressor weight is
     [cols, D] (one row per output column)."""
@@ -141,7 +144,7 @@ def layer_inputs(w, seed=None, T=None):
     out["gamma"] = (1.0 + 0.1 * rng.standard_normal(w.c)).astype(np.float32)
     out["gamma_win"] = (1.0 + 0.1 * rng.standard_normal(w.c)).astype(np.float32)
     out["inv_freq"] = rope_inv_freq(w.r, w.rope_base)
-    _queries(rng, w, tt, out)
+    _queries(rng, w, tt, out, qi_fmt)
     return out
 
 
@@ -165,10 +168,11 @@ def mxfp4_normalish(rng, rows_shape, d):
     return packed.reshape(tuple(rows_shape) + (d // 2,)), scales.reshape(tuple(rows_shape) + (4,))
 
 
-def decode_cache_inputs(w, seed=None, B=None, N=None, key_fmt="e4m3"):
+def decode_cache_inputs(w, seed=None, B=None, N=None, key_fmt="e4m3", qi_fmt="e4m3"):
     """Inputs of one decode step over a resident cache: N entries per sequence (bf16 ~N(0,1)),
     indexer keys (CSA: E4M3 with per-entry scales, or MXFP4 with key_fmt "mxfp4"), a 128-row
-    window ring (token u in row u mod 128) and one query per sequence at position w.t."""
+    window ring (token u in row u mod 128) and one query per sequence at position w.t (the
+    indexer query E4M3 with a scale per head, or MXFP4 with qi_fmt "mxfp4")."""
     rng = _rng(w.seed if seed is None else seed)
     B = w.B if B is None else B
     N = w.N if N is None else N
@@ -184,5 +188,5 @@ def decode_cache_inputs(w, seed=None, B=None, N=None, key_fmt="e4m3"):
     out["inv_freq"] = rope_inv_freq(w.r, w.rope_base)
     out["pos"] = np.full(B, w.t, dtype=np.int32)
     out["n_entries"] = np.full(B, N, dtype=np.int32)
-    _queries(rng, w, 1, out)
+    _queries(rng, w, 1, out, qi_fmt)
     return out

@@ -1,7 +1,8 @@
 """GPU parity of csa_index_topk with many query rows per sequence (the prefill shape: rows are
 scored 16 at a time as a product over indexer heads) against the oracle's float64 scores:
 ragged row counts, fewer heads than the LDS tile holds, partially filled caches, rows with
-nothing visible, and arbitrary positions; with E4M3 keys and with MXFP4 keys."""
+nothing visible, and arbitrary positions; with E4M3 keys, with MXFP4 keys (E4M3 query), with
+MXFP4 keys and query (reading R24), and with bf16 scores (reading R25)."""
 import numpy as np
 import pytest
 import torch
@@ -9,24 +10,31 @@ import torch
 import long_context_sparse_15_amd as csa
 import oracle as O
 from synth import inputs as S
-from gpu_common import DEV, check_close, check_selection, dev, say, workspace
+from gpu_common import (DEV, check_close, check_scores_bf16, check_selection, check_selection_bf16,
+                        dev, say, workspace)
 
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(seed, B, nq, n_max, n_ent, H_I, d_I, pos, key_fmt="e4m3"):
+def _inputs(seed, B, nq, n_max, n_ent, H_I, d_I, pos, key_fmt="e4m3", qi_fmt="e4m3"):
     rng = np.random.Generator(np.random.PCG64(seed))
     if key_fmt == "mxfp4":
         keys, ksc = S.mxfp4_normalish(rng, (B, n_max), d_I)
     else:
         keys = S.e4m3_normalish(rng, (B, n_max, d_I))
         ksc = (rng.uniform(0.5, 1.5, size=(B, n_max)) / 16).astype(np.float32)
+    if qi_fmt == "mxfp4":
+        qi, qsc = S.mxfp4_normalish(rng, (B, nq, H_I), d_I)
+    else:
+        qi = S.e4m3_normalish(rng, (B, nq, H_I, d_I))
+        qsc = (rng.uniform(0.5, 1.5, size=(B, nq, H_I)) / 16).astype(np.float32)
     x = {
         "key_fmt": key_fmt,
+        "qi_fmt": qi_fmt,
         "ikeys": keys,
         "iscale": ksc,
-        "qi": S.e4m3_normalish(rng, (B, nq, H_I, d_I)),
-        "qi_scale": (rng.uniform(0.5, 1.5, size=(B, nq, H_I)) / 16).astype(np.float32),
+        "qi": qi,
+        "qi_scale": qsc,
         "wi": (rng.standard_normal((B, nq, H_I), dtype=np.float32) / 8),
         "n_entries": np.asarray(n_ent, dtype=np.int32),
         "pos": None if pos is None else np.asarray(pos, dtype=np.int32).reshape(B, nq),
@@ -34,11 +42,14 @@ def _inputs(seed, B, nq, n_max, n_ent, H_I, d_I, pos, key_fmt="e4m3"):
     return x
 
 
-def _run(x, B, nq, n_max, H_I, d_I, k, m=4):
+def _run(x, B, nq, n_max, H_I, d_I, k, m=4, bf16=False):
     inv = dev(S.rope_inv_freq(64, 160000.0))
     mx = x["key_fmt"] == "mxfp4"
+    qx = x["qi_fmt"] == "mxfp4"
     cfg = csa.make_config(csa.MODE_CSA, m, 64, 512, 64, inv, top_k=k, n_win=128, idx_heads=H_I,
-                          idx_dim=d_I, idx_key_format=csa.IDX_MXFP4 if mx else csa.IDX_E4M3)
+                          idx_dim=d_I, idx_key_format=csa.IDX_MXFP4 if mx else csa.IDX_E4M3,
+                          idx_query_format=csa.IDX_MXFP4 if qx else csa.IDX_E4M3,
+                          score_format=csa.SCORE_BF16 if bf16 else csa.SCORE_FP32)
     d = {key: dev(x[key]) for key in ("ikeys", "iscale", "qi", "qi_scale", "wi", "n_entries")}
     pos = dev(x["pos"]) if x["pos"] is not None else None
     entries = torch.zeros((B, n_max, 512), dtype=torch.int16, device=DEV)
@@ -55,18 +66,20 @@ def _run(x, B, nq, n_max, H_I, d_I, k, m=4):
         for q in range(nq):
             t = int(x["pos"][b, q]) if x["pos"] is not None else q
             n_vis = O.visible_entries(t, m, int(x["n_entries"][b]))
-            if mx:
-                ref = O.index_scores_mxfp4(x["qi"][b, q], x["qi_scale"][b, q], x["wi"][b, q],
-                                           x["ikeys"][b], x["iscale"][b][:, :d_I // 32], n_vis)
-            else:
-                ref = O.index_scores(x["qi"][b, q], x["qi_scale"][b, q], x["wi"][b, q],
-                                     x["ikeys"][b], x["iscale"][b], n_vis)
+            fn = O.score_function(x["key_fmt"], x["qi_fmt"])
+            qs = x["qi_scale"][b, q][:, :d_I // 32] if qx else x["qi_scale"][b, q]
+            ks = x["iscale"][b][:, :d_I // 32] if mx else x["iscale"][b]
+            ref = fn(x["qi"][b, q], qs, x["wi"][b, q], x["ikeys"][b], ks, n_vis)
             what = "seq %d row %d (t=%d, n_vis=%d)" % (b, q, t, n_vis)
-            check_selection(idx_h[b, q], ref, k, what)
             kk = min(k, n_vis)
             sel = idx_h[b, q, :kk]
-            check_close(sc_h[b, q, :kk], ref[sel], what + " scores",
-                        atol=1e-5 * max(1.0, np.abs(ref).max(initial=0.0)), rtol=1e-5)
+            if bf16:
+                check_selection_bf16(idx_h[b, q], ref, k, what)
+                check_scores_bf16(sc_h[b, q, :kk], ref[sel], what + " scores", full_ref=ref)
+            else:
+                check_selection(idx_h[b, q], ref, k, what)
+                check_close(sc_h[b, q, :kk], ref[sel], what + " scores",
+                            atol=1e-5 * max(1.0, np.abs(ref).max(initial=0.0)), rtol=1e-5)
             assert np.all(np.isneginf(sc_h[b, q, kk:])), what + " padding scores"
 
 
@@ -80,14 +93,16 @@ def _run(x, B, nq, n_max, H_I, d_I, k, m=4):
     # one full tile of 16 rows over long rows (several 64-entry groups per wave)
     (14, 1, 16, 9000, [8800], 64, 256, "spread"),
 ])
-@pytest.mark.parametrize("key_fmt", ["e4m3", "mxfp4"])
-def test_index_rows_parity(case, key_fmt):
+@pytest.mark.parametrize("fmt", ["e4m3", "mxfp4", "fp4q", "e4m3-bf16", "fp4q-bf16"])
+def test_index_rows_parity(case, fmt):
     seed, B, nq, n_max, n_ent, H_I, k, posmode = case
-    say("index rows", key_fmt, case)
+    say("index rows", fmt, case)
+    key_fmt = "e4m3" if fmt.startswith("e4m3") else "mxfp4"
+    qi_fmt = "mxfp4" if fmt.startswith("fp4q") else "e4m3"
     if posmode == "spread":
         rng = np.random.Generator(np.random.PCG64(seed + 100))
         pos = rng.integers(0, 4 * n_max + 8, size=(B, nq))
     else:  # positions 0..nq-1
         pos = np.tile(np.arange(nq), (B, 1))
-    x = _inputs(seed, B, nq, n_max, n_ent, H_I, 128, pos, key_fmt)
-    _run(x, B, nq, n_max, H_I, 128, k)
+    x = _inputs(seed, B, nq, n_max, n_ent, H_I, 128, pos, key_fmt, qi_fmt)
+    _run(x, B, nq, n_max, H_I, 128, k, bf16=fmt.endswith("bf16"))
