@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libcsa.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "index.hip", "mqa.hip", "compress.hip", "proj.hip", "profile.hip",
+SOURCES = ["api.hip", "index.hip", "topk.hip", "mqa.hip", "compress.hip", "proj.hip", "profile.hip",
            "blocks.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -27,6 +27,7 @@ FLAGS = [
 # Per-file flags.  The indexer's MFMA results feed VALU epilogues directly, so they are produced
 # in VGPRs; the attention kernels keep their accumulators in VGPRs too, one register pool.
 FILE_FLAGS = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "mqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
@@ -39,7 +40,7 @@ def _run(cmd):
     return out
 
 
-def build(jobs=4, verbose=False):
+def build(jobs=8, verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     cmds = []

@@ -69,7 +69,8 @@ constexpr int kMultiMaxRows = 4096;
 bool index_use_multi(int rows, int n_max);
 size_t index_topk_workspace(int rows, int n_max, int k, bool score_bf16);
 void index_topk_layout(IndexArgs& a, void* ws, int rows);  // needs a.n_max and a.k set
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);  // a.scores only
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);    // scores, then selection
 
 // ---------------------------------------------------------------- attention
 struct MqaArgs {
@@ -174,7 +175,6 @@ size_t output_proj_workspace(int BT, int g, int r_o);
 hipError_t launch_output_proj(const OutputProjArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- misc
-hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 // Raises kernel fn's dynamic-LDS limit to at least `bytes` (never lowers it).  Thread-safe: the
 // limits already set are kept per function under one lock, so concurrent first launches from
 // several threads each see the attribute in place before they launch.

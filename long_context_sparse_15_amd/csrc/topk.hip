@@ -1,0 +1,837 @@
+// Exact top-k selection of the indexer scores for gfx950.
+//
+// Method: "DeepSeek V4 模型技术大全", chapter "Attention", section "CSA 的完整路径":
+//   I_t = TopK_k { I_{t,s} | s < floor((t+1)/m) }.
+//
+// Top-k is exact with the lower index winning ties.  Scores (fp32, or bf16 widened exactly)
+// become order-preserving 32-bit keys.  Rows of up to 32768 entries use one workgroup per row
+// with the keys in registers or LDS: a sampled threshold, an exact select among the few
+// candidates above it (or a radix select) and an index-ordered compaction that emits the
+// selection sorted.  Longer rows (decode at long context, few rows) are cut into 4096-entry
+// chunks, one workgroup each, that take thresholds of their own and write their candidates; a
+// finalize workgroup per row selects among them and emits the selection in ascending index
+// order.
+#include "index_common.h"
+
+namespace csa {
+
+// ============================================================================ block helpers
+// Block-wide search over a histogram of `nbins` counts for the bin d with
+//   sum(bins > d) < remaining <= sum(bins >= d).
+// Writes d to s_res[0] and remaining - sum(bins > d) to s_res[1].  All THREADS threads call it.
+template <int THREADS>
+__device__ void block_find_crossing(const uint32_t* bins, int nbins, uint32_t remaining,
+                                    uint32_t* s_tmp, int* s_res) {
+  constexpr int NWAVE = THREADS / 64;
+  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
+  const int per = nbins / THREADS;  // nbins is a multiple of THREADS
+  uint32_t own = 0;
+  for (int j = 0; j < per; ++j) own += bins[tid * per + j];
+  // inclusive suffix sum inside the wave (lane l: sum over lanes >= l) from the prefix sum
+  const uint32_t inc = wave_incl_scan(own);
+  const uint32_t wtot = __builtin_amdgcn_readlane(inc, 63);
+  const uint32_t suf = wtot - inc + own;
+  if (l == 0) s_tmp[wave] = wtot;
+  __syncthreads();
+  uint32_t later = 0;
+  for (int w2 = wave + 1; w2 < NWAVE; ++w2) later += s_tmp[w2];
+  const uint32_t above = suf - own + later;
+  if (above < remaining && remaining <= above + own) {
+    uint32_t cum = above;
+    for (int j = per - 1; j >= 0; --j) {
+      const uint32_t c = bins[tid * per + j];
+      if (cum + c >= remaining) {
+        s_res[0] = tid * per + j;
+        s_res[1] = static_cast<int>(remaining - cum);
+        break;
+      }
+      cum += c;
+    }
+  }
+  __syncthreads();
+}
+
+// Exclusive block scan of one uint32 per thread; returns the thread's prefix, *total the sum.
+template <int THREADS>
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
+  constexpr int NWAVE = THREADS / 64;
+  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
+  const uint32_t inc = wave_incl_scan(v);
+  if (l == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+  for (int w2 = 0; w2 < NWAVE; ++w2) {
+    const uint32_t x = s_tmp[w2];
+    if (w2 < wave) before += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + inc - v;
+}
+
+template <typename T, bool kDescending, int THREADS>
+__device__ void bitonic_sort(T* a, int n) {  // n power of two
+  for (int k2 = 2; k2 <= n; k2 <<= 1) {
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += THREADS) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const bool up = ((i & k2) == 0) == kDescending;  // this pair wants a[i] >= a[ixj]
+          const T x = a[i], y = a[ixj];
+          if (up ? (x < y) : (x > y)) {
+            a[i] = y;
+            a[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Index-ordered emission of a row's selection: every key > T, then the first need_eq keys == T
+// in index order; indices come out ascending.  key(e) reads the row's key of entry e.  Each wave
+// owns a contiguous segment of the row: a counting pass (ballots), one exchange of per-wave
+// counts, and an emitting pass whose slots come from ballot prefix counts.
+template <int THREADS, typename KeyFn, typename EmitFn>
+__device__ void ordered_emit_fn(KeyFn key, int n, uint32_t T, int need_eq, int cap, EmitFn emit) {
+  constexpr int NWAVE = THREADS / 64;
+  __shared__ uint32_t s_gt[NWAVE], s_eq[NWAVE];
+  const int l = lane_id(), wave = threadIdx.x >> 6;
+  const unsigned long long lower = (l == 0) ? 0ull : ((1ull << l) - 1ull);
+  const int seg = ((n + NWAVE - 1) / NWAVE + 63) & ~63;
+  const int s0 = min(n, wave * seg), s1 = min(n, s0 + seg);
+  uint32_t cgt = 0, ceq = 0;
+  for (int base = s0; base < s1; base += 64) {
+    const int e = base + l;
+    const uint32_t kv = e < s1 ? key(e) : 0u;
+    cgt += __popcll(__ballot(e < s1 && kv > T));
+    ceq += __popcll(__ballot(e < s1 && kv == T));
+  }
+  if (l == 0) {
+    s_gt[wave] = cgt;
+    s_eq[wave] = ceq;
+  }
+  __syncthreads();
+  int eq_seen = 0, slot_base = 0;
+  for (int w2 = 0; w2 < wave; ++w2) {
+    const int eqb = eq_seen;
+    int take_eq = need_eq - eqb;
+    take_eq = take_eq < 0 ? 0 : (take_eq > static_cast<int>(s_eq[w2]) ? static_cast<int>(s_eq[w2]) : take_eq);
+    slot_base += static_cast<int>(s_gt[w2]) + take_eq;
+    eq_seen += static_cast<int>(s_eq[w2]);
+  }
+  for (int base = s0; base < s1; base += 64) {
+    const int e = base + l;
+    const uint32_t kv = e < s1 ? key(e) : 0u;
+    const bool eq = e < s1 && kv == T;
+    const bool gt = e < s1 && kv > T;
+    const unsigned long long meq = __ballot(eq);
+    const bool take = gt || (eq && eq_seen + __popcll(meq & lower) < need_eq);
+    const unsigned long long mt = __ballot(take);
+    const int slot = slot_base + __popcll(mt & lower);
+    if (take && slot < cap) emit(slot, e);
+    slot_base += __popcll(mt);
+    eq_seen += __popcll(meq);
+  }
+  __syncthreads();  // s_gt / s_eq are reused by the next call
+}
+
+// Emission straight into a row of the output (and its scores), padded with -1 / -inf.
+template <int THREADS, typename KeyFn, typename ST>
+__device__ void ordered_emit(KeyFn key, int n, uint32_t T, int need_eq, int kk, int k,
+                             const ST* __restrict__ srow, int32_t* __restrict__ out,
+                             float* __restrict__ sout, uint32_t* s_tmp) {
+  ordered_emit_fn<THREADS>(key, n, T, need_eq, k, [&](int slot, int e) {
+    out[slot] = e;
+    if (sout) sout[slot] = Scores<ST>::at(srow, e);
+  });
+  for (int j = kk + threadIdx.x; j < k; j += THREADS) {
+    out[j] = -1;
+    if (sout) sout[j] = -INFINITY;
+  }
+  (void)s_tmp;
+}
+
+// Radix select of the kk-th largest key among n keys with 12 + 12 + 8 bit passes over a 4096-bin
+// histogram.  Returns T (the kk-th largest key) and need_eq (how many keys == T are taken).
+template <int THREADS, typename KeyFn>
+__device__ void radix_select(KeyFn key, int n, int kk, uint32_t* hist /*4096*/, uint32_t* s_tmp,
+                             int* s_res, uint32_t& T, int& need_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  uint32_t remaining = static_cast<uint32_t>(kk);
+  const int shifts[3] = {20, 8, 0};
+  const int widths[3] = {12, 12, 8};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = shifts[pass];
+    const int nb = 1 << widths[pass];
+    for (int i = tid; i < nb; i += THREADS) hist[i] = 0;
+    __syncthreads();
+    for (int e = tid; e < n; e += THREADS) {
+      const uint32_t kv = key(e);
+      if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    if (nb >= THREADS) {
+      block_find_crossing<THREADS>(hist, nb, remaining, s_tmp, s_res);
+    } else {  // 256 bins with more than 256 threads: first 256 threads only
+      if (tid < 64) {
+        const int l = tid;
+        uint32_t c4[4], own = 0;
+        for (int j = 0; j < 4; ++j) {
+          c4[j] = hist[l * 4 + j];
+          own += c4[j];
+        }
+        const uint32_t inc = wave_incl_scan(own);
+        const uint32_t above = __builtin_amdgcn_readlane(inc, 63) - inc;
+        if (above < remaining && remaining <= above + own) {
+          uint32_t cum = above;
+          for (int j = 3; j >= 0; --j) {
+            if (cum + c4[j] >= remaining) {
+              s_res[0] = l * 4 + j;
+              s_res[1] = static_cast<int>(remaining - cum);
+              break;
+            }
+            cum += c4[j];
+          }
+        }
+      }
+      __syncthreads();
+    }
+    const uint32_t d = static_cast<uint32_t>(s_res[0]);
+    remaining = static_cast<uint32_t>(s_res[1]);
+    prefix |= d << shift;
+    mask |= static_cast<uint32_t>(nb - 1) << shift;
+    __syncthreads();
+  }
+  T = prefix;
+  need_eq = static_cast<int>(remaining);
+}
+
+// One histogram pass of radix select: counts keys matching (prefix, mask) into nb bins of the
+// bits at `shift`, then finds the crossing bin of `remaining` (s_res[0], s_res[1]); returns the
+// crossing bin's count.
+template <int THREADS, typename KeyFn>
+__device__ uint32_t radix_pass(KeyFn key, int n, uint32_t prefix, uint32_t mask, int shift,
+                               int nb, uint32_t remaining, uint32_t* hist, uint32_t* s_tmp,
+                               int* s_res, bool zeroed = false) {
+  const int tid = threadIdx.x;
+  if (!zeroed) {  // a caller that cleared hist before its last barrier skips this
+    for (int i = tid; i < nb; i += THREADS) hist[i] = 0;
+    __syncthreads();
+  }
+  for (int e = tid; e < n; e += THREADS) {
+    const uint32_t kv = key(e);
+    if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & (nb - 1)], 1u);
+  }
+  __syncthreads();
+  block_find_crossing<THREADS>(hist, nb, remaining, s_tmp, s_res);
+  return hist[s_res[0]];
+}
+
+// Exact kk-th largest key (T) among n keys that all lie in [lo, hi], and how many keys equal
+// to T are taken (need_eq).  One 12-bit histogram over the bits just below the common prefix of
+// lo and hi (so the bins split the keys' actual range); if the crossing bin holds at most 64
+// keys they are gathered into a small list and ranked by pairwise comparison in one wave,
+// otherwise the full radix select runs.
+template <int THREADS, typename KeyFn>
+__device__ void select_kth(KeyFn key, int n, int kk, uint32_t lo, uint32_t hi,
+                           uint32_t* hist /*4096*/, uint32_t* s_tmp, int* s_res, uint32_t& T,
+                           int& need_eq, bool zeroed = false) {
+  __shared__ uint32_t s_bin[64];
+  __shared__ uint32_t s_nb;
+  const int tid = threadIdx.x;
+  const uint32_t diff = lo ^ hi;
+  const int top = diff ? 32 - __clz(diff) : 0;  // bits below the common prefix
+  const int shift = top > 12 ? top - 12 : 0;
+  const uint32_t pmask = top >= 32 ? 0u : ~((1u << top) - 1u);
+  const uint32_t prefix = lo & pmask;
+  const uint32_t c1 = radix_pass<THREADS>(key, n, prefix, pmask, shift, 4096,
+                                          static_cast<uint32_t>(kk), hist, s_tmp, s_res, zeroed);
+  const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
+  const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
+  __syncthreads();
+  if (c1 > 64) {
+    radix_select<THREADS>(key, n, kk, hist, s_tmp, s_res, T, need_eq);
+    return;
+  }
+  if (tid == 0) s_nb = 0;
+  __syncthreads();
+  for (int e = tid; e < n; e += THREADS) {
+    const uint32_t kv = key(e);
+    if ((kv & pmask) == prefix && ((kv >> shift) & 4095u) == d1) s_bin[atomicAdd(&s_nb, 1u)] = kv;
+  }
+  __syncthreads();
+  if (tid < 64) {  // wave 0: rank the bin's keys; the r1-th largest is T
+    const int nbk = static_cast<int>(s_nb);
+    const uint32_t mine = tid < nbk ? s_bin[tid] : 0u;
+    int gt = 0, eq = 0;
+    for (int j = 0; j < nbk; ++j) {
+      const uint32_t o = s_bin[j];
+      gt += o > mine;
+      eq += o == mine;
+    }
+    if (tid < nbk && gt < static_cast<int>(r1) && static_cast<int>(r1) <= gt + eq) {
+      s_res[0] = static_cast<int>(mine);  // every lane holding T writes the same values
+      s_res[1] = static_cast<int>(r1) - gt;
+    }
+  }
+  __syncthreads();
+  T = static_cast<uint32_t>(s_res[0]);
+  need_eq = s_res[1];
+  __syncthreads();
+}
+
+// ============================================================================ per-row top-k
+// One workgroup per query row; the row's keys live in LDS when n_vis <= CAP, otherwise they are
+// re-read from the score row in global memory on every pass (exact, slower).
+template <int THREADS, int CAP, typename ST>
+__global__ __launch_bounds__(THREADS) void topk_row_kernel(
+    const ST* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem);  // CAP
+  uint32_t* hist = keys + CAP;                          // 4096
+  __shared__ uint32_t s_tmp[THREADS / 64];
+  __shared__ int s_res[2];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  const int kk = min(k, n_vis);
+  int32_t* out = idx_out + static_cast<size_t>(row) * k;
+  float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
+  const ST* srow = scores + static_cast<size_t>(row) * sstride;
+  if (n_vis <= k) {
+    for (int j = tid; j < k; j += THREADS) {
+      out[j] = j < n_vis ? j : -1;
+      if (sout) sout[j] = j < n_vis ? Scores<ST>::at(srow, j) : -INFINITY;
+    }
+    return;
+  }
+  uint32_t T;
+  int need_eq;
+  if (n_vis <= CAP) {
+    const int n4 = n_vis >> 2;
+    for (int i = tid; i < n4; i += THREADS) {
+      float v[4];
+      Scores<ST>::four(srow, 4 * i, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) keys[4 * i + j] = order_key(v[j]);
+    }
+    for (int e = 4 * n4 + tid; e < n_vis; e += THREADS) keys[e] = order_key(Scores<ST>::at(srow, e));
+    __syncthreads();
+    auto kf = [&](int e) { return keys[e]; };
+    radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
+    ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+  } else {
+    auto kf = [&](int e) { return order_key(Scores<ST>::at(srow, e)); };
+    radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
+    ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+  }
+}
+
+// ============================================================================ sampled row top-k
+// One workgroup per row; thread t holds in registers the keys of the row's 16-byte chunks
+// i*THREADS + t, i < PER/4 (coalesced loads), so chunk column i of all threads precedes column
+// i+1 in index order.
+//  1. the first key of every fourth chunk is a sample (1 in 16); the lower edge of the 12-bit
+//     bin holding the r-th largest sample (r a little above kk/16 with a margin of 4 standard
+//     deviations; refined by a second pass when that bin is crowded) is a threshold T_lo that
+//     almost surely has between kk and kCandCap keys at or above it;
+//  2. each thread counts its candidates (keys >= T_lo) per chunk column, two 16-bit counts to a
+//     word; one block prefix sum over those words places every candidate (key, index) in LDS in
+//     ascending index order;
+//  3. select_kth finds the kk-th candidate key T and how many keys equal to T are taken;
+//  4. the index-ordered emission over the candidate list writes the keys above T and the first
+//     ties, so the selection comes out sorted with the lowest indices winning ties.
+// If the count misses [kk, kCandCap] (ties, adversarial data) the exact streaming select runs.
+template <int THREADS, int PER, typename ST>
+__global__ __launch_bounds__(THREADS) void topk_sample_kernel(
+    const ST* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
+  constexpr int CH = PER / 4;             // chunks per thread
+  constexpr int SPT = CH / 4;             // samples per thread
+  constexpr int NS = THREADS * SPT;       // sample slots
+  constexpr int NWAVE = THREADS / 64;
+  constexpr int CW = CH / 2;              // count words per thread, two chunk columns each
+  static_assert(CH % 4 == 0 && CW <= 4, "chunk and count layout");
+  static_assert(THREADS * 4 <= 0xffff, "a column's candidate count fits 16 bits");
+  __shared__ uint32_t s_samp[NS];
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_ckey[kCandCap];
+  __shared__ int32_t s_cidx[kCandCap];
+  __shared__ u32x4 s_wcnt[NWAVE];
+  __shared__ uint32_t s_tmp[NWAVE];
+  __shared__ int s_res[2];
+  __shared__ uint32_t s_max;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
+  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  const int kk = min(k, n_vis);
+  int32_t* out = idx_out + static_cast<size_t>(row) * k;
+  float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
+  const ST* srow = scores + static_cast<size_t>(row) * sstride;
+  if (n_vis <= k) {
+    for (int j = tid; j < k; j += THREADS) {
+      out[j] = j < n_vis ? j : -1;
+      if (sout) sout[j] = j < n_vis ? Scores<ST>::at(srow, j) : -INFINITY;
+    }
+    return;
+  }
+  // keys; every chunk load is issued (clamped into the row) and masked, the row's last partial
+  // chunk is read element by element
+  uint32_t kr[PER];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int base = (i * THREADS + tid) * 4;
+    // the address depends only on the row length, not on n_vis, so the loads need not wait for
+    // the row's position and entry count
+    float f[4];
+    Scores<ST>::four(srow, min(base, sstride - 4), f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kr[i * 4 + j] = (base + j < n_vis) ? order_key(f[j]) : 0u;
+  }
+  // the first histogram pass finds it cleared (written while the loads are in flight)
+  for (int i = tid; i < kHistBins; i += THREADS) s_hist[i] = 0u;
+  {
+    const int last = (n_vis - 1) & ~3;  // start of the chunk holding the last visible entry
+    if (n_vis & 3) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+        if ((i * THREADS + tid) * 4 == last) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (last + j < n_vis) kr[i * 4 + j] = order_key(Scores<ST>::at(srow, last + j));
+        }
+    }
+  }
+  // samples: slot (i/4)*THREADS + t holds the first key of chunk i*THREADS + t (i % 4 == 0);
+  // entries grow with the slot, so the visible samples are a prefix of ns slots
+#pragma unroll
+  for (int i = 0; i < CH; i += 4) {
+    const int base = (i * THREADS + tid) * 4;
+    s_samp[(i / 4) * THREADS + tid] = base < n_vis ? kr[i * 4] : 0u;
+  }
+  const int qch = (n_vis + 3) / 4;  // chunks that start below n_vis
+  int ns = 0;
+#pragma unroll
+  for (int g = 0; g < SPT; ++g) ns += max(0, min(THREADS, qch - 4 * g * THREADS));
+  if (tid == 0) s_max = 0u;
+  __syncthreads();
+  const float expect = static_cast<float>(kk) * static_cast<float>(ns) / static_cast<float>(n_vis);
+  int r = static_cast<int>(ceilf(expect + 4.f * sqrtf(expect) + 4.f));
+  if (r > ns) r = ns;
+  // T_lo: the lower edge of the 12-bit bin that holds the r-th largest sample (refined by a
+  // second 12-bit pass when that bin holds more than 64 samples)
+  auto sf = [&](int j) { return s_samp[j]; };
+  uint32_t Tlo;
+  {
+    const uint32_t cb = radix_pass<THREADS>(sf, ns, 0u, 0u, 20, 4096, static_cast<uint32_t>(r),
+                                            s_hist, s_tmp, s_res, /*zeroed=*/true);
+    const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
+    const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
+    __syncthreads();
+    Tlo = d1 << 20;
+    if (cb > 64) {
+      radix_pass<THREADS>(sf, ns, d1 << 20, 0xfff00000u, 8, 4096, r1, s_hist, s_tmp, s_res);
+      Tlo |= static_cast<uint32_t>(s_res[0]) << 8;
+      __syncthreads();
+    }
+  }
+  // candidates (visible keys >= T_lo) per chunk column, packed two columns to a word, and the
+  // largest candidate key
+  uint32_t cw[CW], kmax = 0;
+#pragma unroll
+  for (int w = 0; w < CW; ++w) cw[w] = 0u;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = (i * THREADS + tid) * 4 + j < n_vis && kr[i * 4 + j] >= Tlo;
+      c += in ? 1u : 0u;
+      kmax = in ? max(kmax, kr[i * 4 + j]) : kmax;
+    }
+    cw[i / 2] += c << (16 * (i & 1));
+  }
+  uint32_t inc[CW];
+#pragma unroll
+  for (int w = 0; w < CW; ++w) inc[w] = wave_incl_scan(cw[w]);
+  kmax = wave_max_u32(kmax);
+  if (l == 63) {
+    u32x4 t4 = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < CW; ++w) t4[w] = inc[w];
+    s_wcnt[wave] = t4;
+  }
+  if (l == 0 && kmax) atomicMax(&s_max, kmax);
+  // select_kth's histogram pass finds it cleared
+  for (int i = tid; i < kHistBins; i += THREADS) s_hist[i] = 0u;
+  __syncthreads();
+  // lane j < NWAVE takes wave j's totals; a scan across those lanes gives every wave the words
+  // of the waves before it and the block totals
+  uint32_t before[CW], tot[CW];
+  {
+    const int uw = __builtin_amdgcn_readfirstlane(wave);
+    const u32x4 mine = l < NWAVE ? s_wcnt[l] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < CW; ++w) {
+      const uint32_t sc = wave_incl_scan(mine[w]);
+      tot[w] = __builtin_amdgcn_readlane(sc, NWAVE - 1);
+      const uint32_t prev = uw > 0 ? __builtin_amdgcn_readlane(sc, uw > 0 ? uw - 1 : 0) : 0u;
+      before[w] = inc[w] - cw[w] + prev;
+    }
+  }
+  uint32_t cnt = 0;
+  uint32_t slot[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    slot[i] = cnt + ((before[i / 2] >> (16 * (i & 1))) & 0xffffu);
+    cnt += (tot[i / 2] >> (16 * (i & 1))) & 0xffffu;
+  }
+  if (cnt >= static_cast<uint32_t>(kk) && cnt <= static_cast<uint32_t>(kCandCap)) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      uint32_t sl = slot[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = (i * THREADS + tid) * 4 + j;
+        if (e < n_vis && kr[i * 4 + j] >= Tlo) {
+          s_ckey[sl] = kr[i * 4 + j];
+          s_cidx[sl] = e;
+          ++sl;
+        }
+      }
+    }
+    __syncthreads();
+    uint32_t T;
+    int need_eq;
+    auto cf = [&](int j) { return s_ckey[j]; };
+    select_kth<THREADS>(cf, static_cast<int>(cnt), kk, Tlo, s_max, s_hist, s_tmp, s_res, T,
+                        need_eq, /*zeroed=*/true);
+    ordered_emit_fn<THREADS>(cf, static_cast<int>(cnt), T, need_eq, k, [&](int o, int j) {
+      const int e = s_cidx[j];
+      out[o] = e;
+      if (sout) sout[o] = Scores<ST>::at(srow, e);
+    });
+    for (int j = kk + tid; j < k; j += THREADS) {
+      out[j] = -1;
+      if (sout) sout[j] = -INFINITY;
+    }
+    return;
+  }
+  uint32_t T;
+  int need_eq;
+  auto gk = [&](int e) { return order_key(Scores<ST>::at(srow, e)); };
+  radix_select<THREADS>(gk, n_vis, kk, s_hist, s_tmp, s_res, T, need_eq);
+  ordered_emit<THREADS>(gk, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+}
+
+// ============================================================================ multi-WG top-k
+// For rows longer than one workgroup's register file (decode at long context).  A row is cut
+// into chunks of kCollectChunk entries, one 1024-thread workgroup each.  A workgroup selects its
+// chunk's candidates with a threshold of its own: T_c, the lower edge of the 12-bit bin (refined
+// by 12 more bits when crowded) holding its r-th largest key, r = the chunk's expected share of
+// the row's top kk plus four standard deviations.  It writes the (key, index) pairs >= T_c in
+// ascending index order into its own region (block prefix sum, no global atomics) with the
+// count and T_c.  A finalize workgroup per row (a second launch: a device-scope handoff inside
+// one launch costs an L2 write-back per workgroup on this multi-XCD part) concatenates the
+// regions (a list in ascending index order), finds the kk-th key T of the list with one
+// histogram pass over its actual range and emits the keys above it plus the first ties in index
+// order.  The list holds every key >= T of the row exactly when T >= every chunk's T_c (a key
+// >= T is then >= its chunk's threshold); otherwise (a chunk holding far more than its share
+// of the top keys), and on a region overflow or too few candidates, the exact streaming select
+// of the row runs instead.
+constexpr int kCollectChunk = 4096;
+constexpr int kCandPerChunk = 1024;
+constexpr int kSCandCap = 8192;  // candidates of a row held by its finalize workgroup
+constexpr size_t kMultiLds = static_cast<size_t>(kSCandCap) * 8 + kHistBins * 4;
+
+template <typename ST>
+__global__ __launch_bounds__(1024) void topk_collect_kernel(
+    const ST* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int nchunks,
+    uint32_t* __restrict__ ccount, uint64_t* __restrict__ cand) {
+  constexpr int THREADS = 1024, PER = kCollectChunk / THREADS;
+  static_assert(PER == 4, "one 16-byte load of keys per thread");
+  __shared__ uint32_t s_key[kCollectChunk];
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t s_tmp[THREADS / 64];
+  __shared__ int s_res[2];
+  const int row = blockIdx.x / nchunks;
+  const int chunk = blockIdx.x % nchunks;
+  const int tid = threadIdx.x;
+  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  const int kk = min(k, n_vis);
+  const ST* srow = scores + static_cast<size_t>(row) * sstride;
+  if (n_vis <= k) return;  // everything is selected; finalize does not read the regions
+  const int used = (n_vis + kCollectChunk - 1) / kCollectChunk;  // chunks holding visible keys
+  if (chunk >= used) return;
+  const size_t rc = static_cast<size_t>(row) * nchunks + chunk;
+  const int e0 = chunk * kCollectChunk;
+  const int len = min(kCollectChunk, n_vis - e0);
+
+  // this chunk's keys (one 16-byte load per thread, clamped into the row), also to LDS for the
+  // histogram pass; the histogram is cleared while the loads are in flight
+  uint32_t key[PER];
+  {
+    const int base = e0 + tid * PER;
+    float f[4];
+    Scores<ST>::four(srow, min(base, sstride - 4), f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) key[j] = base + j < n_vis ? order_key(f[j]) : 0u;
+  }
+  for (int i = tid; i < kHistBins; i += THREADS) hist[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) s_key[tid * PER + j] = key[j];
+  __syncthreads();
+  const float expect = static_cast<float>(kk) * static_cast<float>(len) / static_cast<float>(n_vis);
+  const int r = static_cast<int>(ceilf(expect + 4.f * sqrtf(expect) + 4.f));
+  uint32_t Tc = 0u;  // keep the whole chunk when it holds no more than r keys
+  if (r < len) {
+    auto kf = [&](int e) { return s_key[e]; };
+    const uint32_t cb = radix_pass<THREADS>(kf, len, 0u, 0u, 20, 4096, static_cast<uint32_t>(r),
+                                            hist, s_tmp, s_res, /*zeroed=*/true);
+    const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
+    const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
+    __syncthreads();
+    Tc = d1 << 20;
+    if (cb > 64) {  // crowded bin: refine by the next 12 bits
+      radix_pass<THREADS>(kf, len, d1 << 20, 0xfff00000u, 8, 4096, r1, hist, s_tmp, s_res);
+      Tc |= static_cast<uint32_t>(s_res[0]) << 8;
+      __syncthreads();
+    }
+  }
+  uint32_t own = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) own += (e0 + tid * PER + i < n_vis && key[i] >= Tc) ? 1u : 0u;
+  uint32_t total;
+  uint32_t off = block_excl_scan<THREADS>(own, s_tmp, &total);
+  uint64_t* cdst = cand + rc * kCandPerChunk;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = e0 + tid * PER + i;
+    if (e < n_vis && key[i] >= Tc) {
+      if (off < static_cast<uint32_t>(kCandPerChunk))
+        cdst[off] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(e);
+      ++off;
+    }
+  }
+  if (tid == 0) {
+    ccount[2 * rc] = total;
+    ccount[2 * rc + 1] = Tc;
+  }
+}
+
+template <typename ST>
+__global__ __launch_bounds__(1024) void topk_finalize_kernel(
+    const ST* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int nchunks,
+    const uint32_t* __restrict__ ccount, const uint64_t* __restrict__ cand,
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+  constexpr int THREADS = 1024;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(smem);              // kSCandCap
+  int32_t* cidx = reinterpret_cast<int32_t*>(ckey + kSCandCap);    // kSCandCap
+  uint32_t* hist = reinterpret_cast<uint32_t*>(cidx + kSCandCap);  // kHistBins
+  __shared__ uint32_t s_off[1025];
+  __shared__ uint32_t s_tmp[THREADS / 64];
+  __shared__ int s_res[2];
+  __shared__ int s_flag;
+  __shared__ uint32_t s_lo, s_hi, s_tmax;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  const int kk = min(k, n_vis);
+  int32_t* out = idx_out + static_cast<size_t>(row) * k;
+  float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
+  const ST* srow = scores + static_cast<size_t>(row) * sstride;
+  if (n_vis <= k) {  // everything is selected
+    for (int j = tid; j < k; j += THREADS) {
+      out[j] = j < n_vis ? j : -1;
+      if (sout) sout[j] = j < n_vis ? Scores<ST>::at(srow, j) : -INFINITY;
+    }
+    return;
+  }
+  const int used = (n_vis + kCollectChunk - 1) / kCollectChunk;  // <= nchunks
+  if (tid == 0) {
+    s_flag = used > THREADS ? 1 : 0;  // 1 = take the exact fallback
+    s_lo = 0xffffffffu;
+    s_hi = 0u;
+    s_tmax = 0u;
+  }
+  __syncthreads();
+  if (!s_flag) {
+    const size_t rc = static_cast<size_t>(row) * nchunks + tid;
+    const uint32_t c = tid < used ? ccount[2 * rc] : 0u;
+    const uint32_t tc = wave_max_u32(tid < used ? ccount[2 * rc + 1] : 0u);
+    if (lane_id() == 0) atomicMax(&s_tmax, tc);
+    if (c > static_cast<uint32_t>(kCandPerChunk)) s_flag = 1;
+    uint32_t tot;
+    const uint32_t o = block_excl_scan<THREADS>(c, s_tmp, &tot);
+    if (tid < used) s_off[tid] = o;
+    if (tid == 0) {
+      s_off[used] = tot;
+      if (tot > static_cast<uint32_t>(kSCandCap) || tot < static_cast<uint32_t>(kk)) s_flag = 1;
+    }
+    __syncthreads();
+  }
+  if (s_flag) {
+    uint32_t T;
+    int need_eq;
+    auto kf = [&](int e) { return order_key(Scores<ST>::at(srow, e)); };
+    radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
+    ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+    return;
+  }
+  const int nc = static_cast<int>(s_off[used]);
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  // 16 threads per region, each region's pairs to its place in the concatenated list
+  for (int c = tid >> 4; c < used; c += THREADS / 16) {
+    const uint32_t o = s_off[c], n = s_off[c + 1] - o;
+    const uint64_t* src = cand + (static_cast<size_t>(row) * nchunks + c) * kCandPerChunk;
+    for (uint32_t j = tid & 15; j < n; j += 16) {
+      const uint64_t v = src[j];
+      const uint32_t kv = static_cast<uint32_t>(v >> 32);
+      ckey[o + j] = kv;
+      cidx[o + j] = static_cast<int32_t>(v & 0xffffffffu);
+      lo = min(lo, kv);
+      hi = max(hi, kv);
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane_id() == 0) {
+    atomicMin(&s_lo, lo);
+    atomicMax(&s_hi, hi);
+  }
+  __syncthreads();
+  uint32_t T;
+  int need_eq;
+  auto ck = [&](int j) { return ckey[j]; };
+  select_kth<THREADS>(ck, nc, kk, s_lo, s_hi, hist, s_tmp, s_res, T, need_eq);
+  if (T < s_tmax) {  // some chunk's threshold cut keys that reach T: exact streaming select
+    auto kf = [&](int e) { return order_key(Scores<ST>::at(srow, e)); };
+    radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
+    ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+    return;
+  }
+  // the candidate list is in ascending index order
+  ordered_emit_fn<THREADS>(ck, nc, T, need_eq, k, [&](int slot, int j) {
+    out[slot] = cidx[j];
+    if (sout) sout[slot] = Scores<ST>::at(srow, cidx[j]);
+  });
+  for (int j = kk + tid; j < k; j += THREADS) {
+    out[j] = -1;
+    if (sout) sout[j] = -INFINITY;
+  }
+}
+
+// ============================================================================ launchers
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Rows longer than the 1024-thread sampled select holds (and not too many of them) use the
+// multi-workgroup select (measured slower than the one-workgroup select at 32K entries).
+bool index_use_multi(int rows, int n_max) {
+  return n_max > kRowTopkBigN && rows <= kMultiMaxRows;
+}
+
+static int collect_chunks(int n_max) { return (n_max + kCollectChunk - 1) / kCollectChunk; }
+
+size_t index_topk_workspace(int rows, int n_max, int k, bool score_bf16) {
+  const size_t sb = score_bf16 ? 2 : 4;
+  size_t b = align256(static_cast<size_t>(rows) * score_stride(n_max) * sb);
+  if (index_use_multi(rows, n_max)) {
+    const size_t rc = static_cast<size_t>(rows) * collect_chunks(n_max);
+    b += align256(rc * 8);  // (count, threshold) per chunk
+    b += align256(rc * kCandPerChunk * 8);
+  }
+  (void)k;
+  return b;
+}
+
+void index_topk_layout(IndexArgs& a, void* ws, int rows) {
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  a.sstride = score_stride(a.n_max);
+  a.scores = p;
+  p += align256(static_cast<size_t>(rows) * a.sstride * (a.score_bf16 ? 2 : 4));
+  a.counters = nullptr;
+  a.cand = nullptr;
+  if (index_use_multi(rows, a.n_max)) {
+    const size_t rc = static_cast<size_t>(rows) * collect_chunks(a.n_max);
+    a.counters = reinterpret_cast<uint32_t*>(p);
+    p += align256(rc * 8);
+    a.cand = reinterpret_cast<uint64_t*>(p);
+  }
+}
+
+template <int THREADS, int CAP, typename ST>
+static hipError_t launch_row_topk(const IndexArgs& a, int rows, hipStream_t s) {
+  const size_t lds = (static_cast<size_t>(CAP) + kHistBins) * 4;
+  if (hipError_t e =
+          ensure_max_lds(reinterpret_cast<const void*>(topk_row_kernel<THREADS, CAP, ST>), lds))
+    return e;
+  ProfScope ps("topk_row", s);
+  topk_row_kernel<THREADS, CAP, ST><<<rows, THREADS, lds, s>>>(
+      static_cast<const ST*>(a.scores), a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max,
+      a.idx_out, a.score_out);
+  return hipGetLastError();
+}
+
+template <typename ST>
+static hipError_t launch_index_topk_t(const IndexArgs& a, hipStream_t s) {
+  const int rows = a.B * a.nq;
+  const bool multi = index_use_multi(rows, a.n_max);
+  hipError_t e = launch_index_scores(a, s);
+  if (e != hipSuccess) return e;
+  const ST* sc = static_cast<const ST*>(a.scores);
+  if (!multi) {
+    if (a.n_max <= 4096) return launch_row_topk<256, kRowTopkMaxN, ST>(a, rows, s);
+    if (a.n_max <= 16384) {
+      ProfScope ps("topk_sample", s);
+      // 512 threads x 32 keys (measured 1.83 ms against 2.89 ms for 256 x 64 and 3.68 ms for
+      // 1024 x 32 on the 64K-token prefill rows)
+      topk_sample_kernel<512, 32, ST><<<rows, 512, 0, s>>>(sc, a.sstride, a.n_entries, a.pos,
+                                                          a.nq, a.m, a.k, a.n_max, a.idx_out,
+                                                          a.score_out);
+      return hipGetLastError();
+    }
+    ProfScope ps("topk_sample", s);
+    topk_sample_kernel<1024, 32, ST><<<rows, 1024, 0, s>>>(sc, a.sstride, a.n_entries, a.pos,
+                                                          a.nq, a.m, a.k, a.n_max, a.idx_out,
+                                                          a.score_out);
+    return hipGetLastError();
+  }
+  const int ncc = collect_chunks(a.n_max);
+  {
+    ProfScope ps("topk_collect", s);
+    topk_collect_kernel<ST><<<static_cast<unsigned>(ncc) * rows, 1024, 0, s>>>(
+        sc, a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, ncc, a.counters, a.cand);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = ensure_max_lds(reinterpret_cast<const void*>(topk_finalize_kernel<ST>), kMultiLds)))
+    return e;
+  ProfScope ps("topk_finalize", s);
+  topk_finalize_kernel<ST><<<rows, 1024, kMultiLds, s>>>(sc, a.sstride, a.n_entries, a.pos,
+                                                         a.nq, a.m, a.k, a.n_max, ncc,
+                                                         a.counters, a.cand, a.idx_out,
+                                                         a.score_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
+  return a.score_bf16 ? launch_index_topk_t<uint16_t>(a, s) : launch_index_topk_t<float>(a, s);
+}
+
+}  // namespace csa
