@@ -163,6 +163,84 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+# ---- argument checks: the library sees raw device pointers only, so every tensor's dtype and
+# size is checked here against the config, the batch and the query count before the call (an
+# undersized tensor would otherwise be read or written out of bounds on the device).
+
+def _bytes(t):
+    return t.numel() * t.element_size()
+
+
+def _want(t, name, dtypes, numel=None, min_numel=None, min_bytes=None):
+    """Raise CsaError unless t is a tensor of one of `dtypes` (names, e.g. "bfloat16") holding
+    exactly `numel` elements / at least `min_numel` elements / at least `min_bytes` bytes."""
+    if t is None:
+        raise CsaError("%s is required" % name)
+    dt = str(t.dtype).replace("torch.", "")
+    if dtypes and dt not in dtypes:
+        raise CsaError("%s has dtype %s, expected one of %s" % (name, dt, ", ".join(dtypes)))
+    if numel is not None and t.numel() != numel:
+        raise CsaError("%s holds %d elements, expected %d" % (name, t.numel(), numel))
+    if min_numel is not None and t.numel() < min_numel:
+        raise CsaError("%s holds %d elements, needs at least %d" % (name, t.numel(), min_numel))
+    if min_bytes is not None and _bytes(t) < min_bytes:
+        raise CsaError("%s holds %d bytes, needs at least %d" % (name, _bytes(t), min_bytes))
+
+
+_BF16 = ("bfloat16", "int16", "uint16")
+_U8 = ("uint8", "float8_e4m3fn", "int8")
+_F32 = ("float32",)
+_I32 = ("int32",)
+_ANY4 = ("float32", "int32", "uint8", "uint32")  # 4-byte scale words (fp32, or 4 E8M0 bytes)
+
+
+def _qi_width(cfg):
+    """Bytes per indexer-query head: E4M3 codes, or packed MXFP4 codes."""
+    return cfg.idx_dim // 2 if cfg.idx_query_format == IDX_MXFP4 else cfg.idx_dim
+
+
+def _check_indexer_query(cfg, rows, qi, qi_scale, wi):
+    _want(qi, "qi", _U8, numel=rows * cfg.idx_heads * _qi_width(cfg))
+    _want(qi_scale, "qi_scale", _ANY4, min_bytes=rows * cfg.idx_heads * 4)
+    if _bytes(qi_scale) != rows * cfg.idx_heads * 4:
+        raise CsaError("qi_scale holds %d bytes, expected %d (4 per head)" %
+                       (_bytes(qi_scale), rows * cfg.idx_heads * 4))
+    _want(wi, "wi", _F32, numel=rows * cfg.idx_heads)
+
+
+def _check_cache(cfg, cache, B, keys=False, tail=False):
+    """The cache's tensors hold what B sequences of n_max entries (or the block pools) and their
+    window rings need."""
+    entries, window, n_entries, idx_keys, idx_scale, tail_t, table = cache._keep
+    rows = (cache.n_blocks * cache.block_entries if cache.block_entries
+            else B * cache.n_max)
+    row_bytes = (cfg.head_dim + cfg.rope_dim if cfg.entry_format == ENT_MIXED
+                 else 2 * cfg.head_dim)
+    _want(entries, "cache entries", None, min_bytes=rows * row_bytes)
+    _want(window, "cache window", _BF16, min_numel=B * cache.win_slots * cfg.head_dim)
+    _want(n_entries, "cache n_entries", _I32, min_numel=B)
+    if cache.block_entries:
+        _want(table, "cache block_table", _I32, min_numel=B * cache.blocks_per_seq)
+    if keys:
+        kb = cfg.idx_dim // 2 if cfg.idx_key_format == IDX_MXFP4 else cfg.idx_dim
+        _want(idx_keys, "cache idx_keys", _U8, min_bytes=rows * kb)
+        _want(idx_scale, "cache idx_scale", None, min_bytes=rows * 4)
+    if tail and tail_t is not None:
+        r, c = tail_shape(cfg)
+        _want(tail_t, "cache tail", _F32, min_numel=B * r * c)
+
+
+def _check_attention(cfg, B, nq, q, pos, sink, out, lse_out=None):
+    n = B * nq * cfg.n_heads * cfg.head_dim
+    _want(q, "q", _BF16, numel=n)
+    _want(out, "out", _BF16, numel=n)
+    if pos is not None:
+        _want(pos, "pos", _I32, numel=B * nq)
+    _want(sink, "sink", _F32, numel=cfg.n_heads)
+    if lse_out is not None:
+        _want(lse_out, "lse_out", _F32, min_numel=B * nq * cfg.n_heads)
+
+
 def make_config(mode, m, n_heads, head_dim, rope_dim, inv_freq, top_k=0, n_win=128,
                 idx_heads=0, idx_dim=0, hidden=0, softmax_scale=None, rms_eps=1e-6,
                 idx_key_format=0, q_rank=0, out_groups=0, out_rank=0, entry_format=0,
@@ -218,6 +296,10 @@ def query_proj(cfg, H, weights, q_out, ws, qi_out=None, qi_scale_out=None, wi_ou
     """csa_query_proj: H [B, T, hidden] -> q_out [B, T, n_heads, head_dim] (and the indexer
     query, its scales and head weights in CSA mode)."""
     B, T = H.shape[0], H.shape[1]
+    _want(H, "H", _BF16, numel=B * T * cfg.hidden)
+    _want(q_out, "q_out", _BF16, numel=B * T * cfg.n_heads * cfg.head_dim)
+    if cfg.mode == MODE_CSA:
+        _check_indexer_query(cfg, B * T, qi_out, qi_scale_out, wi_out)
     wp, wn = _ws(ws)
     _check(lib().csa_query_proj(ctypes.byref(cfg), B, T, _ptr(H), ctypes.byref(weights),
                                 _ptr(q_out), _ptr(qi_out), _ptr(qi_scale_out), _ptr(wi_out), wp,
@@ -227,6 +309,8 @@ def query_proj(cfg, H, weights, q_out, ws, qi_out=None, qi_scale_out=None, wi_ou
 def output_proj(cfg, O, weights, y_out, ws, stream=None):
     """csa_output_proj: O [B, T, n_heads, head_dim] -> y_out [B, T, hidden]."""
     B, T = O.shape[0], O.shape[1]
+    _want(O, "O", _BF16, numel=B * T * cfg.n_heads * cfg.head_dim)
+    _want(y_out, "y_out", _BF16, numel=B * T * cfg.hidden)
     wp, wn = _ws(ws)
     _check(lib().csa_output_proj(ctypes.byref(cfg), B, T, _ptr(O), ctypes.byref(weights),
                                  _ptr(y_out), wp, wn, _stream(stream)), "csa_output_proj")
@@ -258,6 +342,9 @@ def _ws(ws):
 
 def compress(cfg, H, pos0, weights, cache, ws, stream=None):
     B, T = H.shape[0], H.shape[1]
+    _want(H, "H", _BF16, numel=B * T * cfg.hidden)
+    _want(pos0, "pos0", _I32, numel=B)
+    _check_cache(cfg, cache, B, keys=cfg.mode == MODE_CSA, tail=True)
     wp, wn = _ws(ws)
     _check(lib().csa_compress(ctypes.byref(cfg), B, T, _ptr(H), _ptr(pos0),
                               ctypes.byref(weights), ctypes.byref(cache), wp, wn,
@@ -266,6 +353,12 @@ def compress(cfg, H, pos0, weights, cache, ws, stream=None):
 
 def index_topk(cfg, qi, qi_scale, wi, cache, pos, idx_out, ws, score_out=None, stream=None):
     B, nq = qi.shape[0], qi.shape[1]
+    _check_indexer_query(cfg, B * nq, qi, qi_scale, wi)
+    _want(pos, "pos", _I32, numel=B * nq)
+    _want(idx_out, "idx_out", _I32, min_numel=B * nq * cfg.top_k)
+    if score_out is not None:
+        _want(score_out, "score_out", _F32, min_numel=B * nq * cfg.top_k)
+    _check_cache(cfg, cache, B, keys=True)
     wp, wn = _ws(ws)
     _check(lib().csa_index_topk(ctypes.byref(cfg), B, nq, _ptr(qi), _ptr(qi_scale), _ptr(wi),
                                 ctypes.byref(cache), _ptr(pos), _ptr(idx_out), _ptr(score_out),
@@ -274,6 +367,10 @@ def index_topk(cfg, qi, qi_scale, wi, cache, pos, idx_out, ws, score_out=None, s
 
 def sparse_mqa(cfg, q, cache, idx, pos, sink, out, ws, lse_out=None, stream=None):
     B, nq = q.shape[0], q.shape[1]
+    _check_attention(cfg, B, nq, q, pos, sink, out, lse_out)
+    _want(pos, "pos", _I32, numel=B * nq)
+    _want(idx, "idx", _I32, min_numel=B * nq * cfg.top_k)
+    _check_cache(cfg, cache, B)
     wp, wn = _ws(ws)
     _check(lib().csa_sparse_mqa(ctypes.byref(cfg), B, nq, _ptr(q), ctypes.byref(cache),
                                 _ptr(idx), _ptr(pos), _ptr(sink), _ptr(out), _ptr(lse_out),
@@ -282,15 +379,32 @@ def sparse_mqa(cfg, q, cache, idx, pos, sink, out, ws, lse_out=None, stream=None
 
 def hca_dense_mqa(cfg, q, cache, pos, sink, out, ws, lse_out=None, stream=None):
     B, nq = q.shape[0], q.shape[1]
+    _check_attention(cfg, B, nq, q, pos, sink, out, lse_out)
+    _want(pos, "pos", _I32, numel=B * nq)
+    _check_cache(cfg, cache, B)
     wp, wn = _ws(ws)
     _check(lib().hca_dense_mqa(ctypes.byref(cfg), B, nq, _ptr(q), ctypes.byref(cache),
                                _ptr(pos), _ptr(sink), _ptr(out), _ptr(lse_out), wp, wn,
                                _stream(stream)), "hca_dense_mqa")
 
 
+def _check_decode(cfg, B, cache, pos, q, sink, out, h_new, qi, qi_scale, wi, idx_out):
+    _check_attention(cfg, B, 1, q, pos, sink, out)
+    _want(pos, "pos", _I32, numel=B)
+    if h_new is not None:
+        _want(h_new, "h_new", _BF16, numel=B * cfg.hidden)
+    csa_mode = cfg.mode == MODE_CSA
+    if csa_mode:
+        _check_indexer_query(cfg, B, qi, qi_scale, wi)
+        if idx_out is not None:
+            _want(idx_out, "idx_out", _I32, min_numel=B * cfg.top_k)
+    _check_cache(cfg, cache, B, keys=csa_mode, tail=h_new is not None)
+
+
 def decode(cfg, cache, pos, q, sink, out, ws, h_new=None, weights=None, qi=None, qi_scale=None,
            wi=None, idx_out=None, stream=None):
     B = q.shape[0]
+    _check_decode(cfg, B, cache, pos, q, sink, out, h_new, qi, qi_scale, wi, idx_out)
     wp, wn = _ws(ws)
     _check(lib().csa_decode(ctypes.byref(cfg), B, _ptr(h_new),
                             ctypes.byref(weights) if weights is not None else None,
@@ -304,6 +418,7 @@ def decode_noalloc(cfg, cache, pos, q, sink, out, h_new=None, weights=None, qi=N
     """csa_decode_noalloc: csa_decode with the library's static device scratch instead of a
     workspace (for callers that cannot allocate; calls overlapping on one GPU race)."""
     B = q.shape[0]
+    _check_decode(cfg, B, cache, pos, q, sink, out, h_new, qi, qi_scale, wi, idx_out)
     _check(lib().csa_decode_noalloc(ctypes.byref(cfg), B, _ptr(h_new),
                                     ctypes.byref(weights) if weights is not None else None,
                                     ctypes.byref(cache), _ptr(pos), _ptr(q), _ptr(qi),
@@ -314,6 +429,14 @@ def decode_noalloc(cfg, cache, pos, q, sink, out, h_new=None, weights=None, qi=N
 def prefill(cfg, H, weights, cache, q, sink, out, ws, qi=None, qi_scale=None, wi=None,
             idx_out=None, stream=None):
     B, T = H.shape[0], H.shape[1]
+    _want(H, "H", _BF16, numel=B * T * cfg.hidden)
+    _check_attention(cfg, B, T, q, None, sink, out)
+    csa_mode = cfg.mode == MODE_CSA
+    if csa_mode:
+        _check_indexer_query(cfg, B * T, qi, qi_scale, wi)
+        if idx_out is not None:
+            _want(idx_out, "idx_out", _I32, min_numel=B * T * cfg.top_k)
+    _check_cache(cfg, cache, B, keys=csa_mode, tail=True)
     wp, wn = _ws(ws)
     _check(lib().csa_prefill(ctypes.byref(cfg), B, T, _ptr(H), ctypes.byref(weights),
                              ctypes.byref(cache), _ptr(q), _ptr(qi), _ptr(qi_scale), _ptr(wi),
