@@ -54,8 +54,10 @@ FLAGS = ("mxfp4", "fp4q", "bf16s", "paged", "mixed")
 
 # source files whose hash a committed counter summary records, per kernel
 KERNEL_SOURCES = {"index_score": ("index.hip", "index_common.h", "common.h", "kernels.h"),
-                  "mqa_dense": ("mqa.hip", "common.h", "kernels.h"),
-                  "mqa_sparse": ("mqa.hip", "common.h", "kernels.h"),
+                  "mqa_dense": ("mqa.hip", "mqa_hb.hip", "mqa_common.h", "common.h",
+                                "kernels.h"),
+                  "mqa_sparse": ("mqa.hip", "mqa_hb.hip", "mqa_common.h", "common.h",
+                                 "kernels.h"),
                   "all_projections": ("proj.hip", "compress.hip", "common.h", "kernels.h")}
 
 

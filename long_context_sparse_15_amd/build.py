@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libcsa.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "index.hip", "topk.hip", "mqa.hip", "compress.hip", "proj.hip", "profile.hip",
+SOURCES = ["api.hip", "index.hip", "topk.hip", "mqa.hip", "mqa_hb.hip", "compress.hip", "proj.hip",
+           "profile.hip",
            "blocks.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -25,10 +26,13 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 # Per-file flags.  The indexer's MFMA results feed VALU epilogues directly, so they are produced
-# in VGPRs; the attention kernels keep their accumulators in VGPRs too, one register pool.
+# in VGPRs; the sliced attention kernels keep their accumulators in VGPRs too, one register pool.
+# The head-block kernel (mqa_hb.hip) is built the same way for its logits and writes its output
+# MFMAs out with accumulation-register operands (256 output accumulators a wave).
 FILE_FLAGS = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "mqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "mqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "mqa_hb.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):

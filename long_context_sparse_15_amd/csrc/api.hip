@@ -209,7 +209,7 @@ size_t ws_index(const csa_config_t* c, int rows, int n_max) {
   return csa::index_topk_workspace(rows, n_max, c->top_k, c->score_format == CSA_SCORE_BF16);
 }
 size_t ws_mqa(const csa_config_t* c, int B, int nq, int max_list) {
-  const csa::MqaPlan p = csa::plan_mqa(nq, c->n_heads, c->head_dim, max_list);
+  const csa::MqaPlan p = csa::plan_mqa(nq, c->n_heads, c->head_dim, max_list, c->entry_format == CSA_ENT_MIXED);
   return csa::mqa_workspace(p, B * nq, c->n_heads, c->head_dim);
 }
 int max_list_sparse(const csa_config_t* c) { return c->top_k + c->n_win; }
@@ -342,7 +342,7 @@ int run_attend(const csa_config_t* c, int B, int nq, const uint16_t* q, const cs
   csa::MqaArgs a;
   fill_mqa_args(a, c, B, nq, q, k, idx, pos, sink, out, lse_out, ws);
   const int max_list = idx ? max_list_sparse(c) : max_list_dense(c, k->n_max);
-  const csa::MqaPlan p = csa::plan_mqa(nq, c->n_heads, c->head_dim, max_list);
+  const csa::MqaPlan p = csa::plan_mqa(nq, c->n_heads, c->head_dim, max_list, c->entry_format == CSA_ENT_MIXED);
   hipError_t e = csa::launch_mqa(a, p, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "attention launch");
 }

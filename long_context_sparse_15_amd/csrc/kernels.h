@@ -91,6 +91,7 @@ struct MqaArgs {
   float* part;              // workspace partials
 };
 struct MqaPlan {
+  int kind;           // kMqaSliced (mqa.hip) or kMqaHeadBlock (mqa_hb.hip)
   int head_pairs;     // 32-head groups per workgroup (one wave each per dim slice)
   int slices;         // dim slices (waves) per head pair
   int heads_per_wg;   // 32 * head_pairs
@@ -98,9 +99,11 @@ struct MqaPlan {
   int split_rows;     // rows of the key list per workgroup (multiple of 32)
   int n_splits;
 };
+constexpr int kMqaSliced = 0;     // waves own 32 heads x a dim slice, logits summed through LDS
+constexpr int kMqaHeadBlock = 1;  // waves own 32 heads x all 512 dims, 128 heads a workgroup
 // nq = queries per sequence in the call; the batch size is deliberately not an input (the plan
 // fixes the order of every query's softmax sums, see mqa.hip)
-MqaPlan plan_mqa(int nq, int n_heads, int c, int max_list);
+MqaPlan plan_mqa(int nq, int n_heads, int c, int max_list, bool mixed);
 size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c);
 hipError_t launch_mqa(const MqaArgs& a, const MqaPlan& p, hipStream_t s);
 

@@ -27,142 +27,9 @@
 #include <algorithm>
 #include <cmath>
 
-#include "common.h"
-#include "kernels.h"
+#include "mqa_common.h"
 
 namespace csa {
-
-
-struct MqaParams {
-  const uint16_t* q;
-  const uint16_t* entries;
-  const uint16_t* window;
-  const int32_t* idx;
-  const int32_t* n_entries;
-  const int32_t* pos;
-  const float* sink;
-  const float* inv_freq;
-  int nq, n_heads, r, k, m, n_win, win_slots, n_max;
-  PageMap pages;  // entries in a block pool (PAGED kernels)
-  float scale_log2;
-  int split_rows, n_splits, head_groups, n_work;
-  float* part;  // span partials: bf16 O / l of each span in the MFMA lane order (see mqa_kernel)
-  float* ml;    // [rows, n_splits, n_heads, 2]: (max, sum) of each span
-  uint16_t* out;
-  float* lse_out;
-};
-
-__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Physical 16-byte chunk of logical chunk c in LDS row `row`: the low four bits of the chunk
-// index are XORed with a permutation of row % 16 (bits of row&3 and (row>>2)&3 swapped).
-// 16 consecutive rows at one logical chunk land in 16 distinct bank groups, and so do the
-// 4 rows x 4 chunks addressed by 32 lanes of a transposed read.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // RNE
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// fp32 rounded to bf16 (nearest even) and back: the value a span partial holds
-__device__ __forceinline__ float bf16_round(float x) {
-  return static_cast<float>(static_cast<__bf16>(x));
-}
-// four bf16 values packed low first (as pack2 writes them) to fp32
-__device__ __forceinline__ f32x4 unpack_b4(uint2 v) {
-  return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
-}
-
-// Merge of a query's span partials, in span order, plus the sink, in the log2 domain.  A span
-// contributes its maximum m, its sum l of exp2(z - m) and O / l stored in bf16.  Every list, split
-// into one span or many, is normalised by exactly these operations (contraction off, so the
-// rounding is the same wherever they are inlined): the combine kernel folds the stored partials,
-// a single-span workgroup folds its own partial, rounded to bf16 as it would have been stored.
-struct SpanMerge {
-  float M;     // running reference: the sink logit, raised to the spans' maxima
-  float lsum;  // sum over merged spans of l * exp2(m - M)
-};
-__device__ __forceinline__ SpanMerge sm_start(float sink2) { return SpanMerge{sink2, 0.f}; }
-// raise the reference to Mn >= M; returns the factor the merged O must be multiplied by
-__device__ __forceinline__ float sm_raise(SpanMerge& st, float Mn) {
-#pragma clang fp contract(off)
-  if (Mn == st.M) return 1.f;
-  const float a = (st.M == -INFINITY) ? 0.f : exp2f(st.M - Mn);
-  st.lsum *= a;
-  st.M = Mn;
-  return a;
-}
-// adds a span (maximum m <= M, sum l); returns the weight of its O / l (0 for an empty span)
-__device__ __forceinline__ float sm_add(SpanMerge& st, float m, float l) {
-#pragma clang fp contract(off)
-  if (m == -INFINITY) return 0.f;
-  const float w = l * exp2f(m - st.M);
-  st.lsum += w;
-  return w;
-}
-__device__ __forceinline__ float sm_fold(float o, float ov, float w) {
-#pragma clang fp contract(off)
-  return o + ov * w;
-}
-// 1 / (sum + the sink's term); 0 when nothing is attended and there is no sink
-__device__ __forceinline__ float sm_inv(const SpanMerge& st, bool has_sink, float sink2) {
-#pragma clang fp contract(off)
-  const float den = st.lsum + ((has_sink && st.M != -INFINITY) ? exp2f(sink2 - st.M) : 0.f);
-  return den > 0.f ? 1.f / den : 0.f;
-}
-// natural-log sum of exp(z) without the sink
-__device__ __forceinline__ float sm_lse(const SpanMerge& st) {
-  return st.lsum > 0.f ? (st.M + log2f(st.lsum)) * kLn2 : -INFINITY;
-}
-
-// As store_out4, with cos/sin of the rotation angles of position t read from a table (pair i of
-// the RoPE dims at entry i).
-__device__ __forceinline__ void store_out4_tab(uint16_t* dst, float o0, float o1, float o2,
-                                               float o3, int d0, int c, int r,
-                                               const float2* cs_tab) {
-  float o[4] = {o0, o1, o2, o3};
-#pragma unroll
-  for (int pr = 0; pr < 2; ++pr) {
-    const int d = d0 + 2 * pr;
-    if (d >= c - r) {
-      const float2 e = cs_tab[(d - (c - r)) >> 1];
-      const float x0 = o[2 * pr], x1 = o[2 * pr + 1];
-      o[2 * pr] = x0 * e.x + x1 * e.y;       // rotation by -angle
-      o[2 * pr + 1] = -x0 * e.y + x1 * e.x;
-    }
-  }
-  uint2 v;
-  v.x = pack2(o[0], o[1]);
-  v.y = pack2(o[2], o[3]);
-  *reinterpret_cast<uint2*>(dst) = v;
-}
-
-// Epilogue shared by the in-place path and the combine kernel: o (4 consecutive dims d0..d0+3
-// of one head) is rotated back by -t on the RoPE dims and stored as bf16.
-__device__ __forceinline__ void store_out4(uint16_t* dst, float o0, float o1, float o2, float o3,
-                                           int d0, int c, int r, int t, const float* inv_freq) {
-  float o[4] = {o0, o1, o2, o3};
-#pragma unroll
-  for (int pr = 0; pr < 2; ++pr) {
-    const int d = d0 + 2 * pr;
-    if (d >= c - r) {
-      float cs, sn;
-      rope_cos_sin(t, inv_freq[(d - (c - r)) >> 1], cs, sn);
-      const float x0 = o[2 * pr], x1 = o[2 * pr + 1];
-      o[2 * pr] = x0 * cs + x1 * sn;       // rotation by -angle
-      o[2 * pr + 1] = -x0 * sn + x1 * cs;
-    }
-  }
-  uint2 v;
-  v.x = pack2(o[0], o[1]);
-  v.y = pack2(o[2], o[3]);
-  *reinterpret_cast<uint2*>(dst) = v;
-}
 
 template <int C, int HP_>
 struct MqaShape {
@@ -1186,8 +1053,13 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
 // ---------------------------------------------------------------- planning and launch
 static int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
-// Heads: up to 64 per workgroup (two 32-head pairs), more as separate head groups whose
-// workgroups sit on the same XCD and share the gathered rows through its L2.
+// Heads.  Sliced kernels: up to 64 heads per workgroup (two 32-head pairs), more heads as
+// separate 64-head groups whose workgroups sit on the same XCD and share the gathered rows
+// through its L2.  Decode over a long list (more than kMaxTopK rows, HCA over a long cache) with
+// more than 64 heads, c = 512 and bf16 entries: the head-block kernel (mqa_hb.hip), 128 heads
+// per workgroup, so every gathered row serves all of a query's heads in one pass.  Its fixed
+// cost per workgroup (about 10 us of prologue and epilogue on MI355X) pays off only over long
+// spans, so shorter lists stay on the sliced kernels.
 //
 // Spans.  How a query's key list is cut into spans decides the order in which its softmax terms
 // are summed, so it must not depend on the batch: the plan reads the list's length (top_k +
@@ -1197,32 +1069,43 @@ static int round_up(int x, int a) { return (x + a - 1) / a * a; }
 //  * runs of queries: one span per query (lists up to kMaxTopK rows) -- the rows already fill
 //    the device, and a split would only add the partials' round trip;
 //  * decode, lists up to kMaxTopK rows (every CSA decode): spans of kDecodeSpan rows;
-//  * decode, longer lists (HCA over a long cache): eight spans.
+//  * decode, longer lists (HCA over a long cache): eight spans, sixteen for the head-block
+//    kernel (each of its workgroups covers twice the heads, so twice the spans fill the device;
+//    it always runs several spans).
 constexpr int kManyQueries = 16;
 constexpr int kDecodeSpan = 128;
 constexpr int kLongListSpans = 8;
+constexpr int kLongListSpansHb = 16;
 
-MqaPlan plan_mqa(int nq, int n_heads, int c, int max_list) {
+MqaPlan plan_mqa(int nq, int n_heads, int c, int max_list, bool mixed) {
   MqaPlan pl;
-  pl.head_pairs = 2;  // one instantiation: 64 heads (fewer heads leave waves idle)
-  pl.slices = c == 512 ? 4 : 1;  // eight waves of 128-dim slices for c = 512
+  const int list0 = max_list > 0 ? max_list : 1;
+  const bool hb =
+      c == 512 && !mixed && n_heads > 64 && nq < kManyQueries && list0 > kMaxTopK;
+  pl.kind = hb ? kMqaHeadBlock : kMqaSliced;
+  pl.head_pairs = hb ? 4 : 2;  // sliced: one instantiation, 64 heads (fewer leave waves idle)
+  pl.slices = hb ? 1 : (c == 512 ? 4 : 1);  // eight waves of 128-dim slices for c = 512
   pl.heads_per_wg = 32 * pl.head_pairs;
   pl.head_groups = (n_heads + pl.heads_per_wg - 1) / pl.heads_per_wg;
   const int list = max_list > 0 ? max_list : 1;
+  const int long_spans = hb ? kLongListSpansHb : kLongListSpans;
   int sr;
   if (nq >= kManyQueries) sr = round_up(list, 32);
   else if (list <= kMaxTopK) sr = kDecodeSpan;
-  else sr = round_up((list + kLongListSpans - 1) / kLongListSpans, 64);
+  else sr = round_up((list + long_spans - 1) / long_spans, hb ? 32 : 64);
   pl.split_rows = std::min(sr, kMaxTopK);  // a span's list fits its LDS slots
   pl.n_splits = (list + pl.split_rows - 1) / pl.split_rows;
   return pl;
 }
 
-// partials: rows x spans x head groups x (32 * head_pairs heads) x c floats, then (max, sum)
+// partials: rows x spans x head groups x heads_per_wg heads x c bf16, then (max, sum) floats
+// for rows x spans x heads (the head-block kernel indexes them by its padded head count)
 size_t mqa_workspace(const MqaPlan& p, int rows, int n_heads, int c) {
   if (p.n_splits <= 1) return 0;
-  const size_t o = static_cast<size_t>(rows) * p.n_splits * p.head_groups * p.heads_per_wg * c;
-  const size_t ml = static_cast<size_t>(rows) * p.n_splits * n_heads * 2;
+  const size_t heads = static_cast<size_t>(p.head_groups) * p.heads_per_wg;
+  const size_t o = static_cast<size_t>(rows) * p.n_splits * heads * c;
+  const size_t ml = static_cast<size_t>(rows) * p.n_splits *
+                    (p.kind == kMqaHeadBlock ? heads : static_cast<size_t>(n_heads)) * 2;
   return o * sizeof(uint16_t) + ml * sizeof(float);  // bf16 partials, then fp32 (max, sum)
 }
 
@@ -1265,9 +1148,13 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
 template <int C>
 static hipError_t launch_c(const MqaParams& prm, const MqaPlan& pl, int rows, bool mixed,
                            hipStream_t s) {
-  if (pl.head_pairs != 2) return hipErrorInvalidValue;
   const bool paged = prm.pages.table != nullptr;
   if constexpr (C == 512) {
+    if (pl.kind == kMqaHeadBlock) {
+      if (mixed || pl.head_pairs != 4) return hipErrorInvalidValue;
+      return launch_mqa_hb(prm, rows, s);
+    }
+    if (pl.head_pairs != 2) return hipErrorInvalidValue;
     using W = MqaWideShape<C>;
     if (mixed)
       return paged ? launch_t<C, W, true, true, true>(prm, rows, s)
@@ -1275,7 +1162,7 @@ static hipError_t launch_c(const MqaParams& prm, const MqaPlan& pl, int rows, bo
     return paged ? launch_t<C, W, true, true>(prm, rows, s)
                  : launch_t<C, W, true, false>(prm, rows, s);
   } else {
-    if (mixed) return hipErrorInvalidValue;  // mixed entries: head dim 512 only
+    if (mixed || pl.kind != kMqaSliced || pl.head_pairs != 2) return hipErrorInvalidValue;
     return paged ? launch_t<C, MqaShape<C, 2>, false, true>(prm, rows, s)
                  : launch_t<C, MqaShape<C, 2>, false, false>(prm, rows, s);
   }

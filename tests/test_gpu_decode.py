@@ -150,11 +150,16 @@ def test_csa_decode_clustered_top_keys_multi_workgroup_fallback():
 @pytest.mark.parametrize("case", [
     ("hca_decode_1m", 3, 300, [128 * 300 + 5, 128 * 100 + 127, 60]),
     ("tiny_hca", 2, 40, [128 * 40, 127]),
+    # lists longer than 4096 rows with 128 heads: the head-block kernel, sixteen spans; positions
+    # that fill the list, leave a ragged last tile, leave most spans empty, and leave no entry
+    ("hca_decode_1m", 4, 4500, [128 * 4500 + 5, 128 * 3001 + 77, 128 * 40, 1000]),
+    # 96 heads: the last 32-head block of the workgroup is empty
+    ("hca_decode_1m", 2, 4200, [128 * 4200 + 127, 128 * 2222], 96),
 ])
 def test_hca_dense_parity(case):
-    name, B, N, positions = case
+    name, B, N, positions = case[:4]
     say("hca dense", case)
-    w = _w(name)
+    w = _w(name, **({"n_h": case[4]} if len(case) > 4 else {}))
     x = S.decode_cache_inputs(w, B=B, N=N)
     x["pos"] = np.array(positions, dtype=np.int32)
     cfg, cache, d = _setup(w, x)

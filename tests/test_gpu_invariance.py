@@ -10,7 +10,8 @@ The magnitude cases scale entries and window rows by 2^17 (beyond fp16's range) 
 (below its normal range), and the query by the inverse power of two so that the logits stay
 exactly those of the unscaled rows, and check both a one-span plan (a run of 16 queries per sequence) and
 the split plan (one query per sequence, several spans merged by the combine kernel) against
-the oracle, with the tolerance scaled by the magnitude."""
+the oracle, with the tolerance scaled by the magnitude, for 64 and 128 heads; and the same for
+an HCA decode over a list longer than 4096 rows with 128 heads (the head-block kernel)."""
 import numpy as np
 import pytest
 import torch
@@ -85,11 +86,11 @@ def _scaled_bits(bits, e):
     return O.f64_to_bf16_bits(O.bf16_bits_to_f64(bits) * 2.0 ** e)
 
 
-@pytest.mark.parametrize("e", [17, -20])
-def test_span_partials_extreme_magnitudes(e):
-    w = S.shrink(S.WORKLOADS["csa_decode_128k"])
+@pytest.mark.parametrize("e,n_h", [(17, 64), (-20, 64), (17, 128), (-20, 128)])
+def test_span_partials_extreme_magnitudes(e, n_h):
+    w = S.shrink(S.WORKLOADS["csa_decode_128k"], n_h=n_h)
     B, N = 16, 3000
-    say("span partials at magnitude 2^%d" % e)
+    say("span partials at magnitude 2^%d, %d heads" % (e, n_h))
     x = S.decode_cache_inputs(w, B=B, N=N)
     x["pos"] = (4 * N - 37 * np.arange(B)).astype(np.int32)
     x["entries"] = _scaled_bits(x["entries"], e)
@@ -139,3 +140,31 @@ def test_span_partials_extreme_magnitudes(e):
         ref0, _ = O.attend(x["q"][b, 0], np.concatenate([x["entries"][0][sel], win0]),
                            x["sink"], w.scale, t, x["inv_freq"])
         check_close(got_one[0, b], ref0, "2^%d one span, query %d" % (e, b), atol=1e-2 * mag)
+
+
+@pytest.mark.parametrize("e", [17, -20])
+def test_head_block_partials_extreme_magnitudes(e):
+    w = S.shrink(S.WORKLOADS["hca_decode_1m"])
+    B, N = 3, 4300
+    say("head-block span partials at magnitude 2^%d" % e)
+    x = S.decode_cache_inputs(w, B=B, N=N)
+    x["pos"] = np.array([128 * N + 3, 128 * 2500 + 9, 128 * 4100], dtype=np.int32)
+    x["entries"] = _scaled_bits(x["entries"], e)
+    x["window"] = _scaled_bits(x["window"], e)
+    x["q"] = _scaled_bits(x["q"], -e)
+    d = {k: dev(x[k]) for k in ("entries", "window", "pos", "n_entries", "q", "sink", "inv_freq")}
+    cfg = config_for(w, d["inv_freq"])
+    cache = csa.make_cache(N, w.n_win, d["entries"], d["window"], d["n_entries"])
+    ws = workspace(csa.workspace_size(cfg, csa.OP_DECODE, B, 1, N))
+    out = torch.empty((B, 1, w.n_h, w.c), dtype=torch.bfloat16, device=DEV)
+    csa.hca_dense_mqa(cfg, d["q"], cache, d["pos"], d["sink"], out, ws)
+    torch.cuda.synchronize()
+    got = O.bf16_bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    mag = 2.0 ** e
+    for b in range(B):
+        t = int(x["pos"][b])
+        n_vis = O.visible_entries(t, w.m, N)
+        win = window_rows_ring(x["window"][b], t, w.n_win, w.n_win)
+        ref, _ = O.attend(x["q"][b, 0], np.concatenate([x["entries"][b][:n_vis], win]), x["sink"],
+                          w.scale, t, x["inv_freq"])
+        check_close(got[b, 0], ref, "2^%d seq %d" % (e, b), atol=1e-2 * mag)

@@ -56,12 +56,16 @@ def _case(seed, nq, k, N, n_ent, n_h=64, c=512, r=64, n_win=128):
 
 
 @pytest.mark.parametrize("case", [
-    # (seed, rows, k, entries, visible entries)
-    (21, 1100, 160, 600, 560),
+    # (seed, rows, k, entries, visible entries, heads)
+    (21, 1100, 160, 600, 560, 64),
     # 512-entry lists (the prefill top-k)
-    (22, 1309, 512, 1500, 1500),
+    (22, 1309, 512, 1500, 1500, 64),
+    # more than 64 heads: two 64-head groups of workgroups, also with a head count that leaves
+    # part of the last group empty
+    (23, 300, 512, 1500, 1400, 128),
+    (24, 270, 160, 600, 560, 96),
 ])
 def test_many_row_sparse_attention_parity(case):
     say("many-row attention", case)
-    seed, nq, k, N, n_ent = case
-    _case(seed, nq, k, N, n_ent)
+    seed, nq, k, N, n_ent, n_h = case
+    _case(seed, nq, k, N, n_ent, n_h=n_h)
