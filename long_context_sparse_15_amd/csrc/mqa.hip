@@ -534,12 +534,18 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   const int hp = wave % HP, slice = wave / HP;
   const int h = l >> 5, n32 = l & 31;
   const int r4 = l >> 3, hh = 8 * slice + (l & 7);  // softmax share: head hh, rows 4r4..4r4+3
+  // every launch parameter is requested at once: scalar loads complete out of order, so each
+  // later batch the compiler would issue on demand costs a full wait on all of them
+  asm volatile("" ::"s"(p.q), "s"(p.entries), "s"(p.window), "s"(p.idx), "s"(p.n_entries),
+               "s"(p.pos), "s"(p.sink), "s"(p.inv_freq), "s"(p.nq), "s"(p.n_heads), "s"(p.r),
+               "s"(p.k), "s"(p.m), "s"(p.n_win), "s"(p.win_slots), "s"(p.n_max));
+  asm volatile("" ::"s"(p.pages.table), "s"(p.pages.stride), "s"(p.pages.shift),
+               "s"(p.scale_log2), "s"(p.split_rows), "s"(p.n_splits), "s"(p.head_groups),
+               "s"(p.n_work), "s"(p.part), "s"(p.ml), "s"(p.out), "s"(p.lse_out));
   const int bid = blockIdx.x;
-  const int w = (bid / (8 * p.head_groups)) * 8 + (bid & 7);
-  const int hg = (bid >> 3) % p.head_groups;
-  if (w >= p.n_work) return;
-  const int split = w % p.n_splits;
-  const int row = w / p.n_splits;
+  int hg, split, row;
+  mqa_work_item(p, bid, hg, split, row);
+  if (row < 0) return;
   const int b = row / p.nq;
   const int j0 = split * p.split_rows;
   const int head = (hg * HP + hp) * 32 + n32;
@@ -549,6 +555,13 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   // covers only what it needs (vector loads complete in order): the span's first indices, its
   // index list, sink and RoPE frequencies; then the query slice; the first gathers last.
   constexpr int IPT = (kMaxTopK + NT - 1) / NT;  // index-list entries per thread: any span
+  // position and entry count first, through the vector path (one round trip, waited for once
+  // below, not two scalar round trips each behind a wait for every scalar load)
+  int rv = p.pos ? row : b, bv = b;
+  asm volatile("" : "+v"(rv), "+v"(bv));
+  int t_vec = (p.pos ? p.pos : p.n_entries)[rv];
+  int ne_vec = p.n_entries[bv];
+  asm volatile("" ::: "memory");
   int pre0 = 0, pre1 = 0;
   int iv[IPT];
   if constexpr (SPARSE) {
@@ -567,8 +580,9 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
     for (int kk = 0; kk < KK; ++kk)
       qraw[kk] = *reinterpret_cast<const u32x4*>(qrow + dbase + kk * 16 + h * 8);
   }
-  const int t = p.pos ? p.pos[row] : (row % p.nq);
-  const int n_ent = max(0, min(p.n_entries[b], p.n_max));
+  asm volatile("" : "+v"(t_vec), "+v"(ne_vec) : : "memory");  // after Q is requested
+  const int t = p.pos ? __builtin_amdgcn_readfirstlane(t_vec) : (row % p.nq);
+  const int n_ent = max(0, min(__builtin_amdgcn_readfirstlane(ne_vec), p.n_max));
   const int n_w = min(p.n_win, t + 1);
   const int wlo = t - n_w + 1;
   int n_sel;
@@ -1128,7 +1142,7 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   }
   MqaParams q = prm;
   q.n_work = rows * prm.n_splits;
-  const unsigned grid = static_cast<unsigned>((q.n_work + 7) / 8 * 8) * prm.head_groups;
+  const unsigned grid = mqa_grid(rows, prm.n_splits, prm.head_groups);
   {
     ProfScope ps(prm.idx ? "mqa_sparse" : "mqa_dense", s);
     if constexpr (WIDE) {

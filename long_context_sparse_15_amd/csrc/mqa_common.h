@@ -157,6 +157,33 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup -> (head group, span, query row); row = -1 for a workgroup past the work.  Workgroups
+// are dealt round-robin over the 8 XCDs (bid % 8).  With at least 8 rows every span and head
+// group of a row runs on the XCD row % 8, so the row's query (and, for head groups, its gathered
+// rows) is fetched into one L2.  With fewer rows that would leave XCDs idle, so the work items
+// (row, span) are spread over the XCDs instead, a work item's head groups still on one XCD.
+// mqa_grid gives the matching grid size.
+__device__ __forceinline__ void mqa_work_item(const MqaParams& p, int bid, int& hg, int& split,
+                                             int& row) {
+  const int rows = p.n_work / p.n_splits;
+  const int xcd = bid & 7, k8 = bid >> 3;
+  hg = k8 % p.head_groups;
+  if (rows >= 8) {
+    split = (k8 / p.head_groups) % p.n_splits;
+    row = (k8 / p.head_groups / p.n_splits) * 8 + xcd;
+    if (row >= rows) row = -1;
+  } else {
+    const int w = (k8 / p.head_groups) * 8 + xcd;
+    split = w % p.n_splits;
+    row = w < p.n_work ? w / p.n_splits : -1;
+  }
+}
+inline unsigned mqa_grid(int rows, int n_splits, int head_groups) {
+  const long n = rows >= 8 ? static_cast<long>((rows + 7) / 8 * 8) * n_splits
+                           : static_cast<long>((rows * n_splits + 7) / 8 * 8);
+  return static_cast<unsigned>(n * head_groups);
+}
+
 // Head-block attention for c = 512 (mqa_hb.hip): launches the kernel and, with several spans,
 // its combine.
 hipError_t launch_mqa_hb(const MqaParams& prm, int rows, hipStream_t s);

@@ -136,15 +136,10 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
   asm volatile("" ::"s"(p.pages.table), "s"(p.pages.stride), "s"(p.pages.shift),
                "s"(p.scale_log2), "s"(p.split_rows), "s"(p.n_splits), "s"(p.head_groups),
                "s"(p.n_work), "s"(p.part), "s"(p.ml));
-  // workgroup -> (query row, span, head group): every span and head group of a row runs on the
-  // XCD bid % 8 (workgroups are dealt round-robin over the 8 XCDs), so the row's query is
-  // fetched into one L2 and read from there by all of them
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, k8 = bid >> 3;
-  const int hg = k8 % p.head_groups;
-  const int split = (k8 / p.head_groups) % p.n_splits;
-  const int row = (k8 / p.head_groups / p.n_splits) * 8 + xcd;
-  if (row >= p.n_work / p.n_splits) return;
+  int hg, split, row;
+  mqa_work_item(p, bid, hg, split, row);
+  if (row < 0) return;
   const int b = row / p.nq;
   const int j0 = split * p.split_rows;
   const int head = hg * SH::HPG + wave * SH::HPW + n32;
@@ -474,61 +469,53 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
   // (Stores of 8 bytes a lane straight from the registers took 70% longer: 32 rows a store.)
   const float l_tot = sum_xor32(l_part);
   const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;  // the partial is O / l of the span
-  unsigned char* so = smem + wave * TB;
-  const int sw_c = (n32 >> 1) & 15, sw_h = h ^ (n32 & 1);
-  auto stage = [&](int c, const float (&x)[4]) {
-    *reinterpret_cast<uint2*>(so + n32 * (C * 2) + ((c ^ sw_c) << 4) + (sw_h << 3)) =
-        uint2{pack2(x[0], x[1]), pack2(x[2], x[3])};
-  };
   const size_t hrow = static_cast<size_t>(p.head_groups) * SH::HPG;  // padded heads of a row
+  // block (row, span, head group, wave) of the partials: [dt][i][lane][4 dims], every store
+  // 512 contiguous bytes; element e of lane l in (dt, i) is head 32 wave + l % 32 of the group,
+  // dim 32 dt + 8 i + 4 (l / 32) + e
+  uint16_t* pw = reinterpret_cast<uint16_t*>(p.part) +
+                 ((((static_cast<size_t>(row) * p.n_splits + split) * p.head_groups + hg) * NW +
+                   wave) * (SH::HPW * C));
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) {
     if (dt > 0) asm volatile("" : "+a"(acc[dt - 1]), "+a"(acc[dt]));  // one block at a time
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = acc[dt][4 * i + e] * il;
-      stage(4 * dt + i, x);
-    }
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint2*>(pw + ((dt * 4 + i) * 64 + l) * 4) =
+          uint2{pack2(acc[dt][4 * i] * il, acc[dt][4 * i + 1] * il),
+                pack2(acc[dt][4 * i + 2] * il, acc[dt][4 * i + 3] * il)};
   }
   if (h == 0) {
     float* mlp = p.ml + ((static_cast<size_t>(row) * p.n_splits + split) * hrow + head) * 2;
     mlp[0] = m_ref;
     mlp[1] = l_tot;
   }
-  __syncthreads();
-  const int head0 = hg * SH::HPG + wave * SH::HPW;
-  const int n_rows = min(SH::HPW, p.n_heads - head0);
-  uint16_t* obase = reinterpret_cast<uint16_t*>(p.part) +
-                    ((static_cast<size_t>(row) * p.n_splits + split) * hrow + head0) * C;
-#pragma unroll 1
-  for (int n = 0; n < n_rows; ++n) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(so + n * (C * 2) + ((l ^ ((n >> 1) & 15)) << 4));
-    if (n & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-    *reinterpret_cast<u32x4*>(obase + static_cast<size_t>(n) * C + l * 8) = v;
-  }
 }
 
-// Merge of the span partials of the head-block kernel (natural layout: row, span, head, dim): a
-// thread takes 8 consecutive dims of one (row, head), merges the spans in order, adds the sink
-// once, normalises, rotates back and stores bf16.  Loads of up to kHbCombineMax spans are in
-// flight together.
+// Merge of the span partials of the head-block kernel: a thread takes dims 8c..8c+7 of one
+// (row, head), i.e. the words of lanes n and n + 32 at step c = 4 dt + i of its partial blocks
+// (consecutive threads take consecutive lanes, so a wave's loads are two 256-byte runs), merges
+// the spans in order, adds the sink once, normalises, rotates back and stores bf16.  Loads of up
+// to kHbCombineMax spans are in flight together.
 constexpr int kHbCombineMax = 8;
 
 __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int rows) {
-  constexpr int C = MqaHbShape::C, CH = C / 8;
-  const size_t hrow = static_cast<size_t>(p.head_groups) * MqaHbShape::HPG;
+  constexpr int C = MqaHbShape::C, HPW = MqaHbShape::HPW, BLK = HPW * C;
+  const int nblk = p.head_groups * MqaHbShape::NW;  // 32-head blocks of a row
+  const size_t hrow = static_cast<size_t>(nblk) * HPW;
   const size_t gid = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int chunk = static_cast<int>(gid % CH);
-  const int head = static_cast<int>((gid / CH) % hrow);
-  const int row = static_cast<int>(gid / (CH * hrow));
+  const int n = static_cast<int>(gid % HPW);
+  const int c = static_cast<int>((gid / HPW) % (C / 8));
+  const int blk = static_cast<int>((gid / (HPW * (C / 8))) % nblk);
+  const int row = static_cast<int>(gid / (static_cast<size_t>(HPW) * (C / 8) * nblk));
+  const int head = blk * HPW + n;
   if (row >= rows || head >= p.n_heads) return;
   const int t = p.pos ? p.pos[row] : (row % p.nq);
   const uint16_t* pw = reinterpret_cast<const uint16_t*>(p.part) +
-                       (static_cast<size_t>(row) * p.n_splits * hrow + head) * C + chunk * 8;
+                       (static_cast<size_t>(row) * p.n_splits * nblk + blk) * BLK +
+                       (c * 64 + n) * 4;
   const float* ml = p.ml + (static_cast<size_t>(row) * p.n_splits * hrow + head) * 2;
-  const size_t pstride = hrow * C, mstride = hrow * 2;
+  const size_t pstride = static_cast<size_t>(nblk) * BLK, mstride = hrow * 2;
   const float sink2 = p.sink ? p.sink[head] * kLog2e : -INFINITY;
   SpanMerge sm = sm_start(sink2);
   float o[8];
@@ -536,13 +523,14 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
   for (int s0 = 0; s0 < p.n_splits; s0 += kHbCombineMax) {
     float mv[kHbCombineMax], lv[kHbCombineMax];
-    u32x4 ov[kHbCombineMax];
+    uint2 ova[kHbCombineMax], ovb[kHbCombineMax];
 #pragma unroll
     for (int j = 0; j < kHbCombineMax; ++j) {
       const int sp = min(s0 + j, p.n_splits - 1);
       mv[j] = s0 + j < p.n_splits ? ml[sp * mstride] : -INFINITY;
       lv[j] = ml[sp * mstride + 1];
-      ov[j] = *reinterpret_cast<const u32x4*>(pw + sp * pstride);
+      ova[j] = *reinterpret_cast<const uint2*>(pw + sp * pstride);
+      ovb[j] = *reinterpret_cast<const uint2*>(pw + sp * pstride + 32 * 4);
     }
     float Mn = sm.M;
 #pragma unroll
@@ -554,10 +542,11 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
     for (int j = 0; j < kHbCombineMax; ++j) {
       const float wgt = sm_add(sm, mv[j], lv[j]);  // partials are O / l
       if (mv[j] == -INFINITY) continue;
+      const f32x4 va = unpack_b4(ova[j]), vb = unpack_b4(ovb[j]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o[2 * e] = sm_fold(o[2 * e], __uint_as_float(ov[j][e] << 16), wgt);
-        o[2 * e + 1] = sm_fold(o[2 * e + 1], __uint_as_float(ov[j][e] & 0xffff0000u), wgt);
+        o[e] = sm_fold(o[e], va[e], wgt);
+        o[4 + e] = sm_fold(o[4 + e], vb[e], wgt);
       }
     }
   }
@@ -565,7 +554,7 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
   float x[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = o[e] * inv;
-  const int d0 = chunk * 8;
+  const int d0 = c * 8;
 #pragma unroll
   for (int pr2 = 0; pr2 < 4; ++pr2) {
     const int d = d0 + 2 * pr2;
@@ -577,7 +566,7 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
   }
   *reinterpret_cast<u32x4*>(p.out + (static_cast<size_t>(row) * p.n_heads + head) * C + d0) =
       u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
-  if (p.lse_out && chunk == 0) p.lse_out[static_cast<size_t>(row) * p.n_heads + head] = sm_lse(sm);
+  if (p.lse_out && c == 0) p.lse_out[static_cast<size_t>(row) * p.n_heads + head] = sm_lse(sm);
 }
 
 template <bool SPARSE, bool PAGED>
@@ -590,8 +579,7 @@ static hipError_t launch_hb_t(const MqaParams& prm, int rows, hipStream_t s) {
   if (e != hipSuccess) return e;
   MqaParams q = prm;
   q.n_work = rows * prm.n_splits;
-  const unsigned grid =
-      static_cast<unsigned>((rows + 7) / 8 * 8) * prm.n_splits * prm.head_groups;
+  const unsigned grid = mqa_grid(rows, prm.n_splits, prm.head_groups);
   {
     ProfScope ps(SPARSE ? "mqa_sparse" : "mqa_dense", s);
     mqa_hb_kernel<SPARSE, PAGED><<<grid, SH::NT, lds, s>>>(q);
