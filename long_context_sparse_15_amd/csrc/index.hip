@@ -43,11 +43,22 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   constexpr int KB = DI / 4;   // key bytes per lane (its lane group's K slice)
   constexpr int KK = DI / 32;  // 8-byte MFMA steps per slice
 
+  // every launch parameter is requested at once (scalar loads complete out of order, so each
+  // later batch the compiler would issue on demand costs a full wait on all of them)
+  asm volatile("" ::"s"(qi), "s"(qi_scale), "s"(wi), "s"(keys), "s"(kscale), "s"(n_entries),
+               "s"(pos), "s"(nq), "s"(n_max), "s"(H_I), "s"(m), "s"(chunk), "s"(scores),
+               "s"(sstride), "s"(nchunks), "s"(pm.table), "s"(pm.stride), "s"(pm.shift));
   const int row = blockIdx.x / nchunks;
   const int b = row / nq;
   const int e0 = (blockIdx.x % nchunks) * chunk;
   const int tid = threadIdx.x;
   const int l = lane_id(), g = l >> 4, c16 = l & 15, wave = tid >> 6;
+  // position and entry count of the row through the vector path, first: one round trip,
+  // waited for only where the visible length is needed
+  int rv = pos ? row : b, bv = b;
+  asm volatile("" : "+v"(rv), "+v"(bv));
+  int t_vec = (pos ? pos : n_entries)[rv];
+  int ne_vec = n_entries[bv];
 
   // A operand: query codes of head ht*16 + c16, K slice g.  For DI = 128 (one 16x16x128 MFMA
   // per head tile) lane group g holds bytes 16g..16g+15 and 64+16g..64+16g+15 of the row, and
@@ -83,7 +94,8 @@ __global__ __launch_bounds__(256) void index_score_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = ht * 16 + g * 4 + i;
-        wq[ht][i] = hh < H_I ? wi[static_cast<size_t>(row) * H_I + hh] : 0.f;  // scale in MFMA
+        const float wv = wi[static_cast<size_t>(row) * H_I + (hh < H_I ? hh : 0)];
+        wq[ht][i] = hh < H_I ? wv : 0.f;  // the query scale acts inside the MFMA
       }
       continue;
     }
@@ -104,12 +116,14 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       for (int kk = 0; kk < KK; ++kk)
         aq[ht][kk] = head < H_I ? reinterpret_cast<const long*>(src)[kk] : 0;
     }
+    // (loads unconditional, from a clamped head, then selected: guarded loads went out one
+    // pair at a time, each behind a wait)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = ht * 16 + g * 4 + i;
-      wq[ht][i] = hh < H_I ? wi[static_cast<size_t>(row) * H_I + hh] *
-                                 qi_scale[static_cast<size_t>(row) * H_I + hh]
-                           : 0.f;
+      const size_t hi = static_cast<size_t>(row) * H_I + (hh < H_I ? hh : 0);
+      const float wv = wi[hi], sv = qi_scale[hi];
+      wq[ht][i] = hh < H_I ? wv * sv : 0.f;
     }
   }
 
@@ -233,7 +247,15 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   KeyTile kb[NB];                      // is computed
 #pragma unroll
   for (int t = 0; t < PD; ++t) load(t, kb[t], n_max - 1);
-  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  asm volatile("" : "+v"(t_vec), "+v"(ne_vec) : : "memory");  // after the first tiles' loads
+  int n_vis;
+  {
+    const long tt = pos ? __builtin_amdgcn_readfirstlane(t_vec) : (row % nq);
+    long v = (tt + 1) / m;
+    const int n = min(__builtin_amdgcn_readfirstlane(ne_vec), n_max);
+    if (v > n) v = n;
+    n_vis = static_cast<int>(v < 0 ? 0 : v);  // as visible(): min(n_entries, (t+1)/m) in [0, n_max]
+  }
   const int e1 = min(n_vis, e0 + chunk);
   if (e0 < e1) {
 #pragma unroll
