@@ -534,14 +534,7 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   const int hp = wave % HP, slice = wave / HP;
   const int h = l >> 5, n32 = l & 31;
   const int r4 = l >> 3, hh = 8 * slice + (l & 7);  // softmax share: head hh, rows 4r4..4r4+3
-  // every launch parameter is requested at once: scalar loads complete out of order, so each
-  // later batch the compiler would issue on demand costs a full wait on all of them
-  asm volatile("" ::"s"(p.q), "s"(p.entries), "s"(p.window), "s"(p.idx), "s"(p.n_entries),
-               "s"(p.pos), "s"(p.sink), "s"(p.inv_freq), "s"(p.nq), "s"(p.n_heads), "s"(p.r),
-               "s"(p.k), "s"(p.m), "s"(p.n_win), "s"(p.win_slots), "s"(p.n_max));
-  asm volatile("" ::"s"(p.pages.table), "s"(p.pages.stride), "s"(p.pages.shift),
-               "s"(p.scale_log2), "s"(p.split_rows), "s"(p.n_splits), "s"(p.head_groups),
-               "s"(p.n_work), "s"(p.part), "s"(p.ml), "s"(p.out), "s"(p.lse_out));
+  mqa_preload_params(p);
   const int bid = blockIdx.x;
   int hg, split, row;
   mqa_work_item(p, bid, hg, split, row);
@@ -988,8 +981,9 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
   const int hp = wave % HP, slice = wave / HP;
   const int h = l >> 5, n32 = l & 31;
   const int head = (hg * HP + hp) * 32 + n32;
+  mqa_preload_params(p);
   if (head >= p.n_heads) return;
-  const int t = p.pos ? p.pos[row] : (row % p.nq);
+  const int t_vec = mqa_position_request(p, row);  // needed only for the rotation at the end
   const int dbase = slice * CS;
   const size_t span_stride = static_cast<size_t>(p.head_groups) * NW * (DT * 4) * 256;
   const uint16_t* pw0 = reinterpret_cast<const uint16_t*>(p.part) +
@@ -1000,8 +994,10 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
 
   // one pass per kCombineMax spans: their (max, sum) and O loads go out together, and the
   // running reference M moves (rescaling what was merged) only between passes
-  const float sink2 = p.sink ? p.sink[head] * kLog2e : -INFINITY;
-  SpanMerge sm = sm_start(sink2);
+  // the sink is requested now and taken after the first pass's loads are out
+  float sink_raw = *(p.sink ? p.sink + head : p.inv_freq);
+  float sink2 = -INFINITY;
+  SpanMerge sm = sm_start(-INFINITY);
   f32x4 o[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1016,6 +1012,11 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
         ov[j][c] = unpack_b4(*reinterpret_cast<const uint2*>(pw0 + sp * span_stride + c * 256));
+    }
+    if (s0 == 0) {
+      asm volatile("" : "+v"(sink_raw) : : "memory");
+      sink2 = p.sink ? sink_raw * kLog2e : -INFINITY;
+      sm = sm_start(sink2);
     }
     float Mn = sm.M;
 #pragma unroll
@@ -1034,6 +1035,7 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
     }
   }
   const float inv = sm_inv(sm, p.sink != nullptr, sink2);
+  const int t = mqa_position_take(p, row, t_vec);
   // chunk cc = dt*4 + g4 holds dims dbase + 32dt + 8g4 + 4h .. +3; all rotations before stores
   uint2 packed[CPT];
   int dpos[CPT];

@@ -157,6 +157,29 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Every launch parameter requested in one batch at kernel entry: scalar loads complete out of
+// order, so each later batch the compiler would issue on demand costs a full wait on all of them.
+__device__ __forceinline__ void mqa_preload_params(const MqaParams& p) {
+  asm volatile("" ::"s"(p.q), "s"(p.entries), "s"(p.window), "s"(p.idx), "s"(p.n_entries),
+               "s"(p.pos), "s"(p.sink), "s"(p.inv_freq), "s"(p.nq), "s"(p.n_heads), "s"(p.r),
+               "s"(p.k), "s"(p.m), "s"(p.n_win), "s"(p.win_slots), "s"(p.n_max));
+  asm volatile("" ::"s"(p.pages.table), "s"(p.pages.stride), "s"(p.pages.shift),
+               "s"(p.scale_log2), "s"(p.split_rows), "s"(p.n_splits), "s"(p.head_groups),
+               "s"(p.n_work), "s"(p.part), "s"(p.ml), "s"(p.out), "s"(p.lse_out));
+}
+
+// The position of query row `row` requested through the vector path (a valid address when there
+// is no position array); take it with mqa_position_take after the loads that do not need it.
+__device__ __forceinline__ int mqa_position_request(const MqaParams& p, int row) {
+  int rv = p.pos ? row : 0;
+  asm volatile("" : "+v"(rv));
+  return (p.pos ? p.pos : p.n_entries)[rv];
+}
+__device__ __forceinline__ int mqa_position_take(const MqaParams& p, int row, int t_vec) {
+  asm volatile("" : "+v"(t_vec) : : "memory");
+  return p.pos ? __builtin_amdgcn_readfirstlane(t_vec) : (row % p.nq);
+}
+
 // Workgroup -> (head group, span, query row); row = -1 for a workgroup past the work.  Workgroups
 // are dealt round-robin over the 8 XCDs (bid % 8).  With at least 8 rows every span and head
 // group of a row runs on the XCD row % 8, so the row's query (and, for head groups, its gathered

@@ -128,14 +128,7 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
   const int l = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = l >> 5, n32 = l & 31;
-  // every launch parameter is requested at once: scalar loads complete out of order, so each
-  // later batch the compiler would issue on demand costs a full wait on all of them
-  asm volatile("" ::"s"(p.q), "s"(p.entries), "s"(p.window), "s"(p.idx), "s"(p.n_entries),
-               "s"(p.pos), "s"(p.inv_freq), "s"(p.nq), "s"(p.n_heads), "s"(p.r), "s"(p.k),
-               "s"(p.m), "s"(p.n_win), "s"(p.win_slots), "s"(p.n_max));
-  asm volatile("" ::"s"(p.pages.table), "s"(p.pages.stride), "s"(p.pages.shift),
-               "s"(p.scale_log2), "s"(p.split_rows), "s"(p.n_splits), "s"(p.head_groups),
-               "s"(p.n_work), "s"(p.part), "s"(p.ml));
+  mqa_preload_params(p);
   const int bid = blockIdx.x;
   int hg, split, row;
   mqa_work_item(p, bid, hg, split, row);
@@ -509,15 +502,18 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
   const int blk = static_cast<int>((gid / (HPW * (C / 8))) % nblk);
   const int row = static_cast<int>(gid / (static_cast<size_t>(HPW) * (C / 8) * nblk));
   const int head = blk * HPW + n;
+  mqa_preload_params(p);
   if (row >= rows || head >= p.n_heads) return;
-  const int t = p.pos ? p.pos[row] : (row % p.nq);
+  const int t_vec = mqa_position_request(p, row);  // needed only for the rotation at the end
   const uint16_t* pw = reinterpret_cast<const uint16_t*>(p.part) +
                        (static_cast<size_t>(row) * p.n_splits * nblk + blk) * BLK +
                        (c * 64 + n) * 4;
   const float* ml = p.ml + (static_cast<size_t>(row) * p.n_splits * hrow + head) * 2;
   const size_t pstride = static_cast<size_t>(nblk) * BLK, mstride = hrow * 2;
-  const float sink2 = p.sink ? p.sink[head] * kLog2e : -INFINITY;
-  SpanMerge sm = sm_start(sink2);
+  // the sink is requested now and taken after the first pass's loads are out
+  float sink_raw = *(p.sink ? p.sink + head : p.inv_freq);
+  float sink2 = -INFINITY;
+  SpanMerge sm = sm_start(-INFINITY);
   float o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
@@ -531,6 +527,11 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
       lv[j] = ml[sp * mstride + 1];
       ova[j] = *reinterpret_cast<const uint2*>(pw + sp * pstride);
       ovb[j] = *reinterpret_cast<const uint2*>(pw + sp * pstride + 32 * 4);
+    }
+    if (s0 == 0) {
+      asm volatile("" : "+v"(sink_raw) : : "memory");
+      sink2 = p.sink ? sink_raw * kLog2e : -INFINITY;
+      sm = sm_start(sink2);
     }
     float Mn = sm.M;
 #pragma unroll
@@ -551,6 +552,7 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
     }
   }
   const float inv = sm_inv(sm, p.sink != nullptr, sink2);
+  const int t = mqa_position_take(p, row, t_vec);
   float x[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = o[e] * inv;

@@ -376,11 +376,20 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
   __shared__ uint32_t s_max;
   const int row = blockIdx.x;
   const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
+  const ST* srow = scores + static_cast<size_t>(row) * sstride;
+  // keys; every chunk load is issued (clamped into the row) and masked, the row's last partial
+  // chunk is read element by element.  The addresses depend only on the row length, so the
+  // loads go out first, before the row's position and entry count are known, and all of them
+  // before any is used (pinned: otherwise the compiler splits them and sinks the pieces into
+  // per-element branches, each behind a wait).
+  float f[CH][4];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) Scores<ST>::four(srow, min((i * THREADS + tid) * 4, sstride - 4), f[i]);
+  asm volatile("" ::: "memory");
   const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
   const int kk = min(k, n_vis);
   int32_t* out = idx_out + static_cast<size_t>(row) * k;
   float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
-  const ST* srow = scores + static_cast<size_t>(row) * sstride;
   if (n_vis <= k) {
     for (int j = tid; j < k; j += THREADS) {
       out[j] = j < n_vis ? j : -1;
@@ -388,18 +397,17 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
     }
     return;
   }
-  // keys; every chunk load is issued (clamped into the row) and masked, the row's last partial
-  // chunk is read element by element
   uint32_t kr[PER];
+  {
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int base = (i * THREADS + tid) * 4;
-    // the address depends only on the row length, not on n_vis, so the loads need not wait for
-    // the row's position and entry count
-    float f[4];
-    Scores<ST>::four(srow, min(base, sstride - 4), f);
+    for (int i = 0; i < CH; ++i)
+      asm volatile("" : "+v"(f[i][0]), "+v"(f[i][1]), "+v"(f[i][2]), "+v"(f[i][3]) : : "memory");
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kr[i * 4 + j] = (base + j < n_vis) ? order_key(f[j]) : 0u;
+    for (int i = 0; i < CH; ++i) {
+      const int base = (i * THREADS + tid) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kr[i * 4 + j] = (base + j < n_vis) ? order_key(f[i][j]) : 0u;
+    }
   }
   // the first histogram pass finds it cleared (written while the loads are in flight)
   for (int i = tid; i < kHistBins; i += THREADS) s_hist[i] = 0u;
@@ -588,6 +596,7 @@ __global__ __launch_bounds__(1024) void topk_collect_kernel(
     const int base = e0 + tid * PER;
     float f[4];
     Scores<ST>::four(srow, min(base, sstride - 4), f);
+    asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]) : : "memory");  // one load
 #pragma unroll
     for (int j = 0; j < 4; ++j) key[j] = base + j < n_vis ? order_key(f[j]) : 0u;
   }
