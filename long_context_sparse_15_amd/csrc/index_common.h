@@ -9,12 +9,17 @@ namespace csa {
 
 // Visible entries of a query row: min(n_entries[b], floor((t+1)/m)), clamped to [0, n_max]
 // so a bad n_entries can never send a read past the cache.
+// Both loads go out together (one memory round trip, not two dependent ones).  `row` may
+// differ between lanes.
 __device__ __forceinline__ int visible(const int32_t* n_entries, const int32_t* pos, int row,
                                        int nq, int m, int n_max) {
   const int b = row / nq;
-  const long t = pos ? pos[row] : (row % nq);
+  int ne = n_entries[b];
+  int tp = *(pos ? pos + row : n_entries + b);
+  asm volatile("" : "+v"(ne), "+v"(tp) : : "memory");
+  const long t = pos ? tp : (row % nq);
   long v = (t + 1) / m;
-  const int n = min(n_entries[b], n_max);
+  const int n = min(ne, n_max);
   if (v > n) v = n;
   return static_cast<int>(v < 0 ? 0 : v);
 }

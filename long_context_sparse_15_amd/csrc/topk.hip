@@ -576,26 +576,29 @@ __global__ __launch_bounds__(1024) void topk_collect_kernel(
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t s_tmp[THREADS / 64];
   __shared__ int s_res[2];
+  asm volatile("" ::"s"(scores), "s"(sstride), "s"(n_entries), "s"(pos), "s"(nq), "s"(m), "s"(k),
+               "s"(n_max), "s"(nchunks), "s"(ccount), "s"(cand));  // all parameters at once
   const int row = blockIdx.x / nchunks;
   const int chunk = blockIdx.x % nchunks;
   const int tid = threadIdx.x;
+  const ST* srow = scores + static_cast<size_t>(row) * sstride;
+  const int e0 = chunk * kCollectChunk;
+  // this chunk's keys (one 16-byte load per thread, clamped into the row) go out first, before
+  // the row's position and entry count are known; also to LDS for the histogram pass, which is
+  // cleared while the loads are in flight
+  float f[4];
+  Scores<ST>::four(srow, min(e0 + tid * PER, sstride - 4), f);
+  asm volatile("" ::: "memory");
   const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
   const int kk = min(k, n_vis);
-  const ST* srow = scores + static_cast<size_t>(row) * sstride;
   if (n_vis <= k) return;  // everything is selected; finalize does not read the regions
   const int used = (n_vis + kCollectChunk - 1) / kCollectChunk;  // chunks holding visible keys
   if (chunk >= used) return;
   const size_t rc = static_cast<size_t>(row) * nchunks + chunk;
-  const int e0 = chunk * kCollectChunk;
   const int len = min(kCollectChunk, n_vis - e0);
-
-  // this chunk's keys (one 16-byte load per thread, clamped into the row), also to LDS for the
-  // histogram pass; the histogram is cleared while the loads are in flight
   uint32_t key[PER];
   {
     const int base = e0 + tid * PER;
-    float f[4];
-    Scores<ST>::four(srow, min(base, sstride - 4), f);
     asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]) : : "memory");  // one load
 #pragma unroll
     for (int j = 0; j < 4; ++j) key[j] = base + j < n_vis ? order_key(f[j]) : 0u;
@@ -658,8 +661,20 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   __shared__ int s_res[2];
   __shared__ int s_flag;
   __shared__ uint32_t s_lo, s_hi, s_tmax;
+  asm volatile("" ::"s"(scores), "s"(sstride), "s"(n_entries), "s"(pos), "s"(nq), "s"(m), "s"(k),
+               "s"(n_max), "s"(nchunks), "s"(ccount), "s"(cand), "s"(idx_out),
+               "s"(score_out));  // all parameters at once
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  // this thread's chunk (count, threshold) goes out first, before the row's position and entry
+  // count are known (it is used only for chunks that hold visible keys)
+  uint32_t cc_raw = 0u, ct_raw = 0u;
+  {
+    const size_t rc = static_cast<size_t>(row) * nchunks + min(tid, nchunks - 1);
+    cc_raw = ccount[2 * rc];
+    ct_raw = ccount[2 * rc + 1];
+  }
+  asm volatile("" ::: "memory");
   const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
   const int kk = min(k, n_vis);
   int32_t* out = idx_out + static_cast<size_t>(row) * k;
@@ -681,9 +696,8 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   }
   __syncthreads();
   if (!s_flag) {
-    const size_t rc = static_cast<size_t>(row) * nchunks + tid;
-    const uint32_t c = tid < used ? ccount[2 * rc] : 0u;
-    const uint32_t tc = wave_max_u32(tid < used ? ccount[2 * rc + 1] : 0u);
+    const uint32_t c = tid < used ? cc_raw : 0u;
+    const uint32_t tc = wave_max_u32(tid < used ? ct_raw : 0u);
     if (lane_id() == 0) atomicMax(&s_tmax, tc);
     if (c > static_cast<uint32_t>(kCandPerChunk)) s_flag = 1;
     uint32_t tot;
