@@ -101,6 +101,7 @@ struct MqaPlan {
 };
 constexpr int kMqaSliced = 0;     // waves own 32 heads x a dim slice, logits summed through LDS
 constexpr int kMqaHeadBlock = 1;  // waves own 32 heads x all 512 dims, 128 heads a workgroup
+constexpr int kMqaHeadBlockQ = 2; // the same per wave, two queries of 64 heads a workgroup
 // nq = queries per sequence in the call; the batch size is deliberately not an input (the plan
 // fixes the order of every query's softmax sums, see mqa.hip)
 MqaPlan plan_mqa(int nq, int n_heads, int c, int max_list, bool mixed);

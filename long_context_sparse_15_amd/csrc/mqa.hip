@@ -1069,6 +1069,9 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
 // ---------------------------------------------------------------- planning and launch
 static int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
+// Runs of queries (prefill) with up to 64 heads, c = 512, bf16 entries and lists of up to
+// kHbqMaxList rows: the two-query head-block kernel (mqa_hb.hip), one span per query.
+//
 // Heads.  Sliced kernels: up to 64 heads per workgroup (two 32-head pairs), more heads as
 // separate 64-head groups whose workgroups sit on the same XCD and share the gathered rows
 // through its L2.  Decode over a long list (more than kMaxTopK rows, HCA over a long cache) with
@@ -1098,7 +1101,9 @@ MqaPlan plan_mqa(int nq, int n_heads, int c, int max_list, bool mixed) {
   const int list0 = max_list > 0 ? max_list : 1;
   const bool hb =
       c == 512 && !mixed && n_heads > 64 && nq < kManyQueries && list0 > kMaxTopK;
-  pl.kind = hb ? kMqaHeadBlock : kMqaSliced;
+  const bool hbq = c == 512 && !mixed && n_heads <= 64 && nq >= kManyQueries &&
+                   round_up(list0, 32) <= kHbqMaxList;
+  pl.kind = hb ? kMqaHeadBlock : (hbq ? kMqaHeadBlockQ : kMqaSliced);
   pl.head_pairs = hb ? 4 : 2;  // sliced: one instantiation, 64 heads (fewer leave waves idle)
   pl.slices = hb ? 1 : (c == 512 ? 4 : 1);  // eight waves of 128-dim slices for c = 512
   pl.heads_per_wg = 32 * pl.head_pairs;
@@ -1169,6 +1174,10 @@ static hipError_t launch_c(const MqaParams& prm, const MqaPlan& pl, int rows, bo
     if (pl.kind == kMqaHeadBlock) {
       if (mixed || pl.head_pairs != 4) return hipErrorInvalidValue;
       return launch_mqa_hb(prm, rows, s);
+    }
+    if (pl.kind == kMqaHeadBlockQ) {
+      if (mixed || pl.n_splits != 1) return hipErrorInvalidValue;
+      return launch_mqa_hbq(prm, rows, s);
     }
     if (pl.head_pairs != 2) return hipErrorInvalidValue;
     using W = MqaWideShape<C>;

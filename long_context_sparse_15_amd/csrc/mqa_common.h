@@ -210,5 +210,9 @@ inline unsigned mqa_grid(int rows, int n_splits, int head_groups) {
 // Head-block attention for c = 512 (mqa_hb.hip): launches the kernel and, with several spans,
 // its combine.
 hipError_t launch_mqa_hb(const MqaParams& prm, int rows, hipStream_t s);
+// Runs of queries (prefill) with up to 64 heads, c = 512, one span per query of up to
+// kHbqMaxList rows: two queries per workgroup (mqa_hb.hip).
+constexpr int kHbqMaxList = 1024;  // key-list rows a query may bring (its index list in LDS)
+hipError_t launch_mqa_hbq(const MqaParams& prm, int rows, hipStream_t s);
 
 }  // namespace csa

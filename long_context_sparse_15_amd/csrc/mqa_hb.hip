@@ -571,6 +571,369 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
   if (p.lse_out && c == 0) p.lse_out[static_cast<size_t>(row) * p.n_heads + head] = sm_lse(sm);
 }
 
+// ---------------------------------------------------------------- runs of queries (prefill)
+// Two query rows per workgroup, one span each (the whole key list, up to kHbqMaxList rows):
+// waves 2s and 2s+1 own heads 0..31 and 32..63 of query slot s over all 512 dims, with the same
+// MFMA layout as the kernel above.  Each query has a ring of two tiles in LDS (tile i+1 is
+// requested while tile i is computed: S^T, softmax, PV), so four waves work on two independent
+// key lists with one barrier per step.  A query whose list has fewer tiles computes fully
+// masked tiles in the remaining steps (no effect on its sums).  The output is merged with the
+// sink, normalised and rotated back in place (the span-merge arithmetic of the combine, applied
+// to one span) and leaves as whole 1 KiB rows.
+struct MqaHbqShape {
+  static constexpr int NW = 4, NT = 64 * NW, HPW = 32, QPW = 2, HPQ = 64;
+  static constexpr int C = 512;
+  static constexpr uint32_t TB = 32 * C * 2;   // bytes per tile
+  static constexpr int RPW = 32 / 2;           // rows each wave requests per tile (2 a query)
+  static constexpr size_t off_cs = 4 * TB;     // [2][64] cos/sin of the RoPE pairs at t
+  static constexpr size_t lds_fixed() { return off_cs + 2 * 64 * sizeof(float2); }
+};
+
+template <bool SPARSE, bool PAGED>
+__global__ __launch_bounds__(MqaHbqShape::NT) void mqa_hbq_kernel(MqaParams p) {
+  using SH = MqaHbqShape;
+  constexpr int NT = SH::NT, C = SH::C, RPW = SH::RPW;
+  constexpr uint32_t TB = SH::TB;
+  constexpr bool LIST = SPARSE || PAGED;
+  typedef __attribute__((address_space(3))) unsigned char lds_uchar;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int l = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qs = wave >> 1, hb = wave & 1;  // query slot, head block
+  const int tq = tid & 127;                 // thread within the query slot's two waves
+  const int h = l >> 5, n32 = l & 31;
+  mqa_preload_params(p);
+  const int rows = p.n_work;  // one span per query
+  const int row0 = blockIdx.x * 2;
+  if (row0 >= rows) return;
+  const bool live = row0 + qs < rows;  // the slot past an odd row count mirrors the last row
+  const int row = min(row0 + qs, rows - 1);
+  const int b = row / p.nq;
+  const int head = hb * SH::HPW + n32;
+  const bool head_ok = head < p.n_heads;
+  float2* s_cs = reinterpret_cast<float2*>(smem + SH::off_cs) + qs * 64;
+  int* s_idx = reinterpret_cast<int*>(smem + SH::lds_fixed()) + qs * p.split_rows;
+
+  int pre0 = 0;
+  if constexpr (SPARSE) pre0 = p.idx[static_cast<size_t>(row) * p.k + min(n32, p.k - 1)];
+  // position and entry count of both rows of the workgroup (the step count is the larger of
+  // the two lists'), sink and RoPE frequency, then the query slice
+  const int rowo = min(row0 + (qs ^ 1), rows - 1);
+  int t_vec = mqa_position_request(p, row), to_vec = mqa_position_request(p, rowo);
+  int ne_vec = p.n_entries[b], neo_vec = p.n_entries[rowo / p.nq];
+  float sink_raw = *(p.sink ? p.sink + (head_ok ? head : 0) : p.inv_freq);
+  float freq_v = p.inv_freq[min(tq, (p.r >> 1) - 1)];
+  asm volatile("" ::: "memory");
+  u32x4 qv[32];
+  {
+    const uint16_t* qrow = p.q + (static_cast<size_t>(row) * p.n_heads + (head_ok ? head : 0)) * C;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk)
+      qv[kk] = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + h * 8);
+  }
+  asm volatile("" : "+v"(ne_vec), "+v"(neo_vec), "+v"(sink_raw), "+v"(freq_v) : : "memory");
+  const int t = mqa_position_take(p, row, t_vec);
+  const int to = mqa_position_take(p, rowo, to_vec);
+  auto list_len = [&](int tt, int ne_raw) {  // n_sel + n_w of a row at position tt
+    const int ne = max(0, min(ne_raw, p.n_max));
+    int ns;
+    if (SPARSE) {
+      ns = p.k;
+    } else {
+      const long v = (static_cast<long>(tt) + 1) / p.m;
+      ns = static_cast<int>(v < ne ? v : ne);
+    }
+    return ns + min(p.n_win, tt + 1);
+  };
+  const int n_ent = max(0, min(__builtin_amdgcn_readfirstlane(ne_vec), p.n_max));
+  const int n_w = min(p.n_win, t + 1);
+  const int wlo = t - n_w + 1;
+  int n_sel;
+  if (SPARSE) {
+    n_sel = p.k;
+  } else {
+    const long v = (static_cast<long>(t) + 1) / p.m;
+    n_sel = static_cast<int>(v < n_ent ? v : n_ent);
+  }
+  const int R = min(n_sel + n_w, p.split_rows);
+  const int R_o = min(list_len(to, __builtin_amdgcn_readfirstlane(neo_vec)), p.split_rows);
+  const int ntiles = (max(R, R_o) + 31) / 32;  // steps of the workgroup
+
+  const uint16_t* const ent_base =
+      PAGED ? p.entries : p.entries + static_cast<size_t>(b) * p.n_max * C;
+  const uint16_t* const win_base = p.window + static_cast<size_t>(b) * p.win_slots * C;
+  const uint16_t* const safe_row = win_base + static_cast<size_t>(t % p.win_slots) * C;
+  const int e_lim = PAGED ? 0x7fffffff : n_ent;
+  auto xlate = [&](int e) {
+    return (e >= 0 && e < n_ent) ? static_cast<int>(entry_row(p.pages, p.n_max, b, e)) : -1;
+  };
+  auto resolve_e = [&](int j, int e, const uint16_t*& ptr, uint32_t& mask) {
+    const bool in_span = l < 32 && j < R;
+    const bool sel = j < n_sel;
+    const bool ok_e = e >= 0 && e < e_lim;
+    const int u = max(wlo + (j - n_sel), 0);
+    const uint16_t* pe = ent_base + static_cast<size_t>(ok_e ? e : 0) * C;
+    const uint16_t* pw = win_base + static_cast<size_t>(u % p.win_slots) * C;
+    const bool ok = in_span && (!sel || ok_e);
+    ptr = ok ? (sel ? pe : pw) : safe_row;
+    mask = static_cast<uint32_t>(__ballot(ok));
+  };
+  auto resolve = [&](int jt, const uint16_t*& ptr, uint32_t& mask) {
+    const int j = jt + n32;
+    int e = j;
+    if constexpr (LIST) e = s_idx[min(max(j, 0), p.split_rows - 1)];
+    resolve_e(j, e, ptr, mask);
+  };
+  // rows hb, hb + 2, .. of the slot's tile into the slot's buffer buf (rows of one query
+  // split over its two waves)
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_uchar*)smem));
+  auto gload = [&](const uint16_t* ptr, int buf) {
+    const uint64_t pv = reinterpret_cast<uint64_t>(ptr);
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const int rr = hb + 2 * q;
+      const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv), rr);
+      const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv >> 32), rr);
+      lds_dma16((static_cast<uint64_t>(hi) << 32) | lo, static_cast<uint32_t>(l ^ swz(rr)) << 4,
+                lds_base + static_cast<uint32_t>(qs * 2 + buf) * TB +
+                    static_cast<uint32_t>(rr) * (C * 2));
+    }
+  };
+
+  uint32_t mk = 0;  // valid mask of the tile being computed
+  if (ntiles > 0) {
+    const uint16_t* p0;
+    int f0 = SPARSE ? pre0 : n32;
+    if constexpr (PAGED) f0 = xlate(f0);
+    resolve_e(n32, f0, p0, mk);
+    gload(p0, 0);
+  }
+  if constexpr (LIST) {
+    const int e1 = min(R, n_sel);
+    for (int j = tq; j < e1; j += 128) {
+      int v = SPARSE ? p.idx[static_cast<size_t>(row) * p.k + j] : j;
+      if constexpr (PAGED) v = xlate(v);
+      s_idx[j] = v;
+    }
+  }
+  if (tq < (p.r >> 1)) {
+    float cs, sn;
+    rope_cos_sin(t, freq_v, cs, sn);
+    s_cs[tq] = float2{cs, sn};
+  }
+  __syncthreads();  // s_idx, s_cs
+
+  bf16x8 bq[32];
+#pragma unroll
+  for (int kk = 0; kk < 32; ++kk) {
+    u32x4 raw = qv[kk];
+    if (kk >= 24) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = kk * 16 + h * 8 + 2 * jj;
+        const int rel = d - (C - p.r);
+        const float2 e = s_cs[max(rel, 0) >> 1];
+        const float x0 = bf16_to_f32(static_cast<uint16_t>(raw[jj] & 0xffff));
+        const float x1 = bf16_to_f32(static_cast<uint16_t>(raw[jj] >> 16));
+        const uint32_t rot = pack2(x0 * e.x - x1 * e.y, x0 * e.y + x1 * e.x);
+        raw[jj] = rel >= 0 ? rot : raw[jj];
+      }
+    }
+    bq[kk] = as_bf16x8(raw);
+  }
+
+  uint32_t sa_off[8];
+#pragma unroll
+  for (int kr = 0; kr < 8; ++kr)
+    sa_off[kr] = static_cast<uint32_t>(n32 * C + (((2 * kr + h) ^ swz(n32)) << 3)) * 2u;
+  const int G = l >> 4, i0 = (l & 15) >> 2, q4 = l & 3;
+  const int ra = 4 * h + i0, rb = ra + 8;
+  uint32_t ta_off[4], tb_off[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int low = 4 * d + 2 * (G & 1) + (q4 >> 1);
+    ta_off[d] = static_cast<uint32_t>(ra * C + ((low ^ swz(ra)) << 3) + 4 * (q4 & 1)) * 2u;
+    tb_off[d] = static_cast<uint32_t>(rb * C + ((low ^ swz(rb)) << 3) + 4 * (q4 & 1)) * 2u;
+  }
+  constexpr uint32_t kStep16 = 16u * C * 2u;
+
+  f32x16 acc[16];
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) acc[dt] = f32x16{};
+  hb_acc_fence_before_mfma(acc);
+  float m_ref = -INFINITY, l_part = 0.f;
+
+  auto read_s = [&](const unsigned char* Eb, int kk) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(Eb + sa_off[kk & 7] + (kk >> 3) * 256));
+  };
+  auto read_pv = [&](const unsigned char* Eb, int k) {
+    const int dt = k & 15, kb = k >> 4;
+    const uint32_t o = (dt >> 2) * 256 + kb * kStep16;
+    const bf16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Eb + ta_off[dt & 3] + o));
+    const bf16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Eb + tb_off[dt & 3] + o));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  for (int i = 0; i < ntiles; ++i) {
+    const unsigned char* Eb = smem + static_cast<uint32_t>(qs * 2 + (i & 1)) * TB;
+    wait_vm<0>();     // this wave's rows of tile i have landed
+    __syncthreads();  // both waves' rows of tile i are in LDS; tile i-1's buffer is free
+    uint32_t mk_next = 0;
+    if (i + 1 < ntiles) {
+      const uint16_t* pn;
+      resolve((i + 1) * 32, pn, mk_next);
+      gload(pn, (i + 1) & 1);
+    }
+    // S^T of tile i, operands two steps ahead
+    f32x16 sacc;
+    {
+      bf16x8 s0 = read_s(Eb, 0), s1 = read_s(Eb, 1);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        bf16x8 s2 = s1;
+        if (k + 2 < 32) s2 = read_s(Eb, k + 2);
+        if (k == 0) mfma_32x32x16_v0(sacc, s0, bq[0]);
+        else mfma_32x32x16_v(sacc, s0, bq[k]);
+        s0 = s1;
+        s1 = s2;
+      }
+      hb_v_fence_after_mfma(sacc);
+    }
+    // the first PV operands go out while the softmax runs
+    bf16x8 t0 = read_pv(Eb, 0), t1 = read_pv(Eb, 1);
+    float v[16], pr[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = sacc[e];
+    if (mk != 0xffffffffu) {  // a tile with masked rows (wave-uniform)
+      const uint32_t mh = mk >> (4 * h);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[4 * r + e] = ((mh >> (8 * r + e)) & 1u) ? v[4 * r + e] : -INFINITY;
+    }
+    float mx = v[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[e]);
+    mx = max_xor32(mx) * p.scale_log2;
+    const bool move = mx > m_ref + 8.f;
+    const float m_new = move ? mx : m_ref;
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+    const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(v[e], p.scale_log2, -mu));
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ls += pr[e];
+    l_part = l_part * alpha + ls;
+    m_ref = m_new;
+    bf16x8 P[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      P[kb] = as_bf16x8(u32x4{pack2(pr[8 * kb], pr[8 * kb + 1]), pack2(pr[8 * kb + 2], pr[8 * kb + 3]),
+                              pack2(pr[8 * kb + 4], pr[8 * kb + 5]),
+                              pack2(pr[8 * kb + 6], pr[8 * kb + 7])});
+    if (__ballot(alpha != 1.f)) {  // some head's reference moved up: rescale what was summed
+      hb_acc_fence_after_mfma(acc);
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        acc[dt] *= alpha;
+        if (dt + 1 < 16) asm volatile("" : "+a"(acc[dt]), "+a"(acc[dt + 1]));
+      }
+      hb_acc_fence_before_mfma(acc);
+    }
+    // PV of tile i (kb-major: the two MFMAs into one block are 16 apart)
+    hb_nops_valu_to_mfma();  // P was just written by VALU code
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      bf16x8 t2 = t1;
+      if (k + 2 < 32) t2 = read_pv(Eb, k + 2);
+      mfma_32x32x16_agpr(acc[k & 15], t0, P[k >> 4]);
+      t0 = t1;
+      t1 = t2;
+    }
+    mk = mk_next;
+  }
+  hb_acc_fence_after_mfma(acc);
+  __syncthreads();  // every wave is done with the rings before it stages its outputs
+
+  // ---- epilogue: the merge of this one span with the sink (as the combine would merge it),
+  // the rotation back on the RoPE dims (the last four blocks: rope_dim <= 128), staged in tile
+  // buffer `wave` (chunk c of head row n at c ^ ((n >> 1) & 15), halves swapped for odd n) and
+  // written as whole 1 KiB rows
+  const float l_tot = sum_xor32(l_part);
+  const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float a2 = (p.sink && head_ok) ? sink_raw * kLog2e : -INFINITY;
+  SpanMerge sm = sm_start(a2);
+  sm_raise(sm, fmaxf(sm.M, m_ref));
+  const float wgt = sm_add(sm, m_ref, l_tot);
+  const float inv = sm_inv(sm, p.sink != nullptr, a2);
+  const int rope0 = C - p.r;
+  unsigned char* so = smem + wave * TB;
+  const int sw_c = (n32 >> 1) & 15, sw_h = h ^ (n32 & 1);
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) {
+    if (dt > 0) asm volatile("" : "+a"(acc[dt - 1]), "+a"(acc[dt]));  // one block at a time
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x[e] = sm_fold(0.f, bf16_round(acc[dt][4 * i + e] * il), wgt) * inv;
+      if (dt >= 12) {
+#pragma unroll
+        for (int pr2 = 0; pr2 < 2; ++pr2) {
+          const int d = dt * 32 + i * 8 + 4 * h + 2 * pr2;
+          const float2 e = s_cs[max(d - rope0, 0) >> 1];
+          float y0 = x[2 * pr2], y1 = x[2 * pr2 + 1];
+          rot_back(y0, y1, e.x, e.y);
+          x[2 * pr2] = d >= rope0 ? y0 : x[2 * pr2];
+          x[2 * pr2 + 1] = d >= rope0 ? y1 : x[2 * pr2 + 1];
+        }
+      }
+      const int c = 4 * dt + i;
+      *reinterpret_cast<uint2*>(so + n32 * (C * 2) + ((c ^ sw_c) << 4) + (sw_h << 3)) =
+          uint2{pack2(x[0], x[1]), pack2(x[2], x[3])};
+    }
+  }
+  if (live && p.lse_out && head_ok && h == 0)
+    p.lse_out[static_cast<size_t>(row) * p.n_heads + head] = sm_lse(sm);
+  __syncthreads();
+  const int head0 = hb * SH::HPW;
+  const int n_rows = live ? min(SH::HPW, p.n_heads - head0) : 0;
+  uint16_t* obase = p.out + (static_cast<size_t>(row) * p.n_heads + head0) * C;
+#pragma unroll 1
+  for (int n = 0; n < n_rows; ++n) {
+    u32x4 w4 = *reinterpret_cast<const u32x4*>(so + n * (C * 2) + ((l ^ ((n >> 1) & 15)) << 4));
+    if (n & 1) w4 = u32x4{w4[2], w4[3], w4[0], w4[1]};
+    *reinterpret_cast<u32x4*>(obase + static_cast<size_t>(n) * C + l * 8) = w4;
+  }
+}
+
+template <bool SPARSE, bool PAGED>
+static hipError_t launch_hbq_t(const MqaParams& prm, int rows, hipStream_t s) {
+  using SH = MqaHbqShape;
+  if (prm.n_splits != 1 || prm.split_rows > kHbqMaxList || prm.n_heads > SH::HPQ)
+    return hipErrorInvalidValue;
+  const size_t lds = SH::lds_fixed() +
+                     ((SPARSE || PAGED) ? 2 * static_cast<size_t>(prm.split_rows) * sizeof(int) : 0);
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(mqa_hbq_kernel<SPARSE, PAGED>), lds);
+  if (e != hipSuccess) return e;
+  MqaParams q = prm;
+  q.n_work = rows;
+  ProfScope ps(SPARSE ? "mqa_sparse" : "mqa_dense", s);
+  mqa_hbq_kernel<SPARSE, PAGED><<<static_cast<unsigned>((rows + 1) / 2), SH::NT, lds, s>>>(q);
+  return hipGetLastError();
+}
+
+hipError_t launch_mqa_hbq(const MqaParams& prm, int rows, hipStream_t s) {
+  const bool paged = prm.pages.table != nullptr;
+  if (prm.idx) return paged ? launch_hbq_t<true, true>(prm, rows, s) : launch_hbq_t<true, false>(prm, rows, s);
+  return paged ? launch_hbq_t<false, true>(prm, rows, s) : launch_hbq_t<false, false>(prm, rows, s);
+}
+
 template <bool SPARSE, bool PAGED>
 static hipError_t launch_hb_t(const MqaParams& prm, int rows, hipStream_t s) {
   using SH = MqaHbShape;
