@@ -326,18 +326,32 @@ int csa_decode_noalloc(const csa_config_t* cfg, int32_t B, const uint16_t* h_new
                        const float* wi, const float* sink, uint16_t* out, int32_t* idx_out,
                        void* stream);
 
-/* csa_prefill - causal layer over the first T tokens of B sequences (positions 0..T-1):
- * csa_compress (pos0 = 0; every block is written whatever n_entries holds on entry, and
- * n_entries ends as floor(T/m)), then for every token t as a query the
- * causal csa_index_topk and csa_sparse_mqa (HCA mode: hca_dense_mqa).
- * Requires cache->win_slots >= T.  q bf16 [B, T, n_heads, head_dim]; qi/qi_scale/wi as
- * csa_index_topk with nq=T; out bf16 [B, T, n_heads, head_dim]; idx_out int32
- * [B, T, top_k] or NULL. */
+/* csa_prefill - causal layer over T new tokens of each of B sequences: csa_compress, then for
+ * every new token t as a query the causal csa_index_topk and csa_sparse_mqa (HCA mode:
+ * hca_dense_mqa).
+ *  pos0  NULL: every sequence starts at position 0 (tokens 0..T-1); every block is written
+ *        whatever n_entries holds on entry, and n_entries ends as floor(T/m).  Requires
+ *        cache->win_slots >= T.
+ *        int32 [B] device: chunked prefill.  Sequence b continues at pos0[b] (tokens
+ *        pos0[b]..pos0[b]+T-1) on a cache that holds its earlier chunks: the compressor
+ *        continues exactly as csa_compress with the same pos0 (n_entries[b] = floor(pos0[b]/m)
+ *        on entry, the tail ring holding the earlier tokens' projections), and query i of
+ *        sequence b sits at position pos0[b]+i.  The window ring must keep the last n_win-1
+ *        rows of the earlier chunks while this chunk's rows are written: requires
+ *        cache->win_slots >= T + n_win - 1, the same ring size for every chunk of a sequence
+ *        (row u lives in slot u % win_slots).  Book "DeepSeek V4 模型技术大全", section "1M
+ *        context 推理策略", row "chunked prefill" (a long prompt enters in chunks that write the
+ *        cache as they go; closed compressed entries advance at each chunk's end, the window
+ *        rolls, and causality, positions and the compressor's state carry across the
+ *        boundary).  A sequence prefilled in chunks of 16 or more tokens gets the bits of a
+ *        single call over the whole prompt.
+ * q bf16 [B, T, n_heads, head_dim]; qi/qi_scale/wi as csa_index_topk with nq=T; out bf16
+ * [B, T, n_heads, head_dim]; idx_out int32 [B, T, top_k] or NULL. */
 int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,
-                const csa_weights_t* w, const csa_cache_t* cache, const uint16_t* q,
-                const uint8_t* qi, const float* qi_scale, const float* wi, const float* sink,
-                uint16_t* out, int32_t* idx_out, void* workspace, size_t ws_bytes,
-                void* stream);
+                const int32_t* pos0, const csa_weights_t* w, const csa_cache_t* cache,
+                const uint16_t* q, const uint8_t* qi, const float* qi_scale, const float* wi,
+                const float* sink, uint16_t* out, int32_t* idx_out, void* workspace,
+                size_t ws_bytes, void* stream);
 
 /* Weights of the query-side projections (device, bf16 unless noted; one row per output
  * column, like w_cat):

@@ -85,7 +85,7 @@ _SIGS = {
     "hca_dense_mqa": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "csa_decode": ([_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
                    ctypes.c_int),
-    "csa_prefill": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "csa_prefill": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
                     ctypes.c_int),
     "csa_decode_noalloc": ([_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
                            ctypes.c_int),
@@ -427,9 +427,13 @@ def decode_noalloc(cfg, cache, pos, q, sink, out, h_new=None, weights=None, qi=N
 
 
 def prefill(cfg, H, weights, cache, q, sink, out, ws, qi=None, qi_scale=None, wi=None,
-            idx_out=None, stream=None):
+            idx_out=None, pos0=None, stream=None):
+    """pos0=None: tokens 0..T-1 of every sequence; an int32 [B] device tensor: a chunk that
+    continues sequence b at position pos0[b] (chunked prefill)."""
     B, T = H.shape[0], H.shape[1]
     _want(H, "H", _BF16, numel=B * T * cfg.hidden)
+    if pos0 is not None:
+        _want(pos0, "pos0", _I32, numel=B)
     _check_attention(cfg, B, T, q, None, sink, out)
     csa_mode = cfg.mode == MODE_CSA
     if csa_mode:
@@ -438,7 +442,7 @@ def prefill(cfg, H, weights, cache, q, sink, out, ws, qi=None, qi_scale=None, wi
             _want(idx_out, "idx_out", _I32, min_numel=B * T * cfg.top_k)
     _check_cache(cfg, cache, B, keys=csa_mode, tail=True)
     wp, wn = _ws(ws)
-    _check(lib().csa_prefill(ctypes.byref(cfg), B, T, _ptr(H), ctypes.byref(weights),
+    _check(lib().csa_prefill(ctypes.byref(cfg), B, T, _ptr(H), _ptr(pos0), ctypes.byref(weights),
                              ctypes.byref(cache), _ptr(q), _ptr(qi), _ptr(qi_scale), _ptr(wi),
                              _ptr(sink), _ptr(out), _ptr(idx_out), wp, wn, _stream(stream)),
            "csa_prefill")

@@ -49,6 +49,21 @@ static __device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES
 
 namespace {
 
+// Positions of a chunk's queries: pos[b][i] = pos0[b] + i.
+__global__ __launch_bounds__(256) void chunk_positions_kernel(const int32_t* __restrict__ pos0,
+                                                              int T, int32_t* __restrict__ pos) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < T) pos[static_cast<size_t>(b) * T + i] = pos0[b] + i;
+}
+
+hipError_t launch_chunk_positions(const int32_t* pos0, int B, int T, int32_t* pos,
+                                  hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((T + 255) / 256), static_cast<unsigned>(B));
+  chunk_positions_kernel<<<grid, 256, 0, s>>>(pos0, T, pos);
+  return hipGetLastError();
+}
+
 int hip_fail(hipError_t e, const char* where) {
   return fail(CSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
@@ -220,10 +235,12 @@ size_t ws_attend(const csa_config_t* c, int B, int nq, int n_max) {
                    : ws_mqa(c, B, nq, max_list_dense(c, n_max));
 }
 
-// decode / prefill: [idx buffer (CSA)] + union(compress, index, attend)
+// decode / prefill: [idx buffer (CSA)] + [query positions (prefill)] + union(compress, index,
+// attend)
 size_t ws_layer(const csa_config_t* c, int B, int T, int n_max, bool prefill, bool compress) {
   const int rows = B * T;
   size_t idx = is_csa(c) ? align256(static_cast<size_t>(rows) * c->top_k * 4) : 0;
+  if (prefill) idx += align256(static_cast<size_t>(rows) * 4);  // query positions (chunked)
   size_t u = ws_attend(c, B, T, n_max);
   if (is_csa(c)) u = std::max(u, ws_index(c, rows, n_max));
   if (compress) u = std::max(u, ws_compress(c, B, prefill ? T : 1));
@@ -617,9 +634,10 @@ int csa_decode_noalloc(const csa_config_t* cfg, int32_t B, const uint16_t* h_new
 }
 
 int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,
-                const csa_weights_t* w, const csa_cache_t* cache, const uint16_t* q,
-                const uint8_t* qi, const float* qi_scale, const float* wi, const float* sink,
-                uint16_t* out, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+                const int32_t* pos0, const csa_weights_t* w, const csa_cache_t* cache,
+                const uint16_t* q, const uint8_t* qi, const float* qi_scale, const float* wi,
+                const float* sink, uint16_t* out, int32_t* idx_out, void* workspace,
+                size_t ws_bytes, void* stream) {
   int rc = check_config(cfg, true);
   if (rc) return rc;
   if ((rc = check_cache(cfg, cache, is_csa(cfg), true))) return rc;
@@ -629,9 +647,12 @@ int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H
   if ((rc = check_aligned({H, q, qi, out, w ? w->w_cat : nullptr}))) return rc;
   if (is_csa(cfg) && (!qi || !qi_scale || !wi))
     return fail(CSA_ERR_INVALID_ARG, "CSA prefill needs qi, qi_scale and wi");
-  if (cache->win_slots < T)
+  if (!pos0 && cache->win_slots < T)
     return fail(CSA_ERR_INVALID_ARG, "prefill needs win_slots=%d >= T=%d", cache->win_slots, T);
-  if (T / cfg->m > cache->n_max)
+  if (pos0 && cache->win_slots < static_cast<long long>(T) + cfg->n_win - 1)
+    return fail(CSA_ERR_INVALID_ARG, "chunked prefill needs win_slots=%d >= T + n_win - 1 = %d",
+                cache->win_slots, T + cfg->n_win - 1);
+  if (!pos0 && T / cfg->m > cache->n_max)
     return fail(CSA_ERR_INVALID_ARG, "T/m=%d entries exceed n_max=%d", T / cfg->m, cache->n_max);
   if ((rc = check_index_rows(cfg, static_cast<long long>(B) * T, cache->n_max))) return rc;
   const size_t need = ws_layer(cfg, B, T, cache->n_max, true, true);
@@ -643,13 +664,22 @@ int csa_prefill(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H
     idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p);
     p += align256(static_cast<size_t>(B) * T * cfg->top_k * 4);
   }
-  if ((rc = run_compress(cfg, B, T, H, nullptr, w, cache, p, s, false))) return rc;
-  if (is_csa(cfg)) {
-    if ((rc = run_index(cfg, B, T, qi, qi_scale, wi, cache, nullptr, idx, nullptr, p, s)))
-      return rc;
-    return run_attend(cfg, B, T, q, cache, idx, nullptr, sink, out, nullptr, p, s);
+  // chunked prefill: the queries' positions pos0[b] + i, written once for the scorer, the
+  // selection and the attention
+  int32_t* qpos = nullptr;
+  if (pos0) {
+    qpos = reinterpret_cast<int32_t*>(p);
+    const hipError_t e = launch_chunk_positions(pos0, B, T, qpos, s);
+    if (e != hipSuccess) return hip_fail(e, "chunk positions launch");
   }
-  return run_attend(cfg, B, T, q, cache, nullptr, nullptr, sink, out, nullptr, p, s);
+  p += align256(static_cast<size_t>(B) * T * 4);
+  if ((rc = run_compress(cfg, B, T, H, pos0, w, cache, p, s, pos0 != nullptr))) return rc;
+  if (is_csa(cfg)) {
+    if ((rc = run_index(cfg, B, T, qi, qi_scale, wi, cache, qpos, idx, nullptr, p, s)))
+      return rc;
+    return run_attend(cfg, B, T, q, cache, idx, qpos, sink, out, nullptr, p, s);
+  }
+  return run_attend(cfg, B, T, q, cache, nullptr, qpos, sink, out, nullptr, p, s);
 }
 
 int csa_query_proj(const csa_config_t* cfg, int32_t B, int32_t T, const uint16_t* H,

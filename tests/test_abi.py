@@ -91,7 +91,7 @@ def test_null_arguments_are_rejected(L):
     assert L.csa_decode(None, 1, None, None, None, None, None, None, None, None, None, None,
                         None, None, 0, None) == -1
     assert L.csa_prefill(None, 1, 1, None, None, None, None, None, None, None, None, None, None,
-                         None, 0, None) == -1
+                         None, None, 0, None) == -1
     # a valid config with a NULL cache
     assert L.csa_index_topk(ctypes.byref(c), 1, 1, None, None, None, None, None, None, None,
                             None, 0, None) == -1
@@ -198,3 +198,21 @@ def test_attention_plan_does_not_depend_on_the_batch(L):
         assert one > 0
         for B in (2, 5, 16, 32, 128):
             assert csa.workspace_size(cfg, op, B, 1, n_max) == B * one
+
+
+def test_chunked_prefill_window_ring_is_checked(L):
+    """A chunk that continues a sequence (pos0 given) needs a window ring that still holds the
+    last n_win - 1 rows of the earlier chunks: win_slots >= T + n_win - 1.  Refused before any
+    launch (the pointers are stand-ins that are never used)."""
+    c = _cfg()
+    P = 0x20000
+    wts = csa.Weights(P, P, P, P, P, P, P)
+    T = 1000
+    for slots, ok in ((T, False), (T + c.n_win - 2, False), (T + c.n_win - 1, True)):
+        k = csa.Cache(8192, slots, P, P, P, P, P, P, 0, 0, 0, 0)
+        # a too small workspace makes the valid case stop at the workspace check instead
+        rc = L.csa_prefill(ctypes.byref(c), 1, T, P, P, ctypes.byref(wts), ctypes.byref(k), P, P,
+                           P, P, P, P, None, 0x100000, 16, None)
+        err = csa.last_error()
+        assert rc == (-3 if ok else -1), err
+        assert ("T + n_win - 1" in err) != ok, err
