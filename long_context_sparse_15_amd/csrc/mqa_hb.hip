@@ -93,10 +93,33 @@ __device__ __forceinline__ void hb_nops_valu_to_mfma() { asm volatile("s_nop 2")
 // M0 holds the LDS address (one wait state between its write and the DMA); M0 is reserved to
 // the compiler and cannot be declared clobbered, and nothing else in these kernels uses it (the
 // LDS instructions of gfx950 do not read it).
-__device__ __forceinline__ void lds_dma16(uint64_t base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(lds_addr));
+//
+// The row's base address comes from a lane of a vector register (v_readlane into an SGPR pair),
+// and a vector memory instruction may read an SGPR written by a VALU instruction only 5 wait
+// states later.  The compiler does not see the DMA's read, so the callers take every address
+// (row_addr, which pins it in place) before the previous DMA of the sequence is issued: that
+// DMA's three instructions and this one's M0 write and wait state make the 5.  The first DMA of
+// a sequence has only the next address's two readlanes in between and waits 3 more (FIRST).
+struct RowAddr {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ RowAddr row_addr(uint64_t pv, int rr) {
+  RowAddr a{static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(pv), rr)),
+            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(pv >> 32), rr))};
+  asm volatile("" : : "s"(a.lo), "s"(a.hi));  // read here, ahead of the DMAs that precede its own
+  return a;
+}
+template <bool FIRST = false>
+__device__ __forceinline__ void lds_dma16(RowAddr a, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t base = (static_cast<uint64_t>(a.hi) << 32) | a.lo;
+  if constexpr (FIRST)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_addr));
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_addr));
 }
 __device__ __forceinline__ void hb_acc_fence_after_mfma(f32x16 (&acc)[16]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
@@ -207,17 +230,27 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
   // this wave's rows of a tile (rows wave, wave + NW, ...) straight into LDS buffer buf; logical
   // chunk c of row rr lands at chunk c ^ swz(rr)
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_uchar*)smem));
-  auto gload_row = [&](const uint16_t* ptr, int q, int buf) {  // row wave + NW q of a tile
-    const uint64_t pv = reinterpret_cast<uint64_t>(ptr);
+  auto addr_of = [&](const uint16_t* ptr, int q) {  // row wave + NW q of a tile
+    return row_addr(reinterpret_cast<uint64_t>(ptr), wave + q * NW);
+  };
+  auto dma_row = [&](RowAddr a, int q, int buf) {
     const int rr = wave + q * NW;
-    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv), rr);
-    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv >> 32), rr);
-    lds_dma16((static_cast<uint64_t>(hi) << 32) | lo, static_cast<uint32_t>(l ^ swz(rr)) << 4,
+    lds_dma16(a, static_cast<uint32_t>(l ^ swz(rr)) << 4,
               lds_base + static_cast<uint32_t>(buf) * TB + static_cast<uint32_t>(rr) * (C * 2));
   };
-  auto gload = [&](const uint16_t* ptr, int buf) {
+  auto gload = [&](const uint16_t* ptr, int buf) {  // all of this wave's rows of a tile
+    RowAddr a = addr_of(ptr, 0);
 #pragma unroll
-    for (int q = 0; q < RPW; ++q) gload_row(ptr, q, buf);
+    for (int q = 0; q < RPW; ++q) {
+      RowAddr nx = a;
+      if (q + 1 < RPW) nx = addr_of(ptr, q + 1);
+      const int rr = wave + q * NW;
+      const uint32_t voff = static_cast<uint32_t>(l ^ swz(rr)) << 4;
+      const uint32_t la = lds_base + static_cast<uint32_t>(buf) * TB + static_cast<uint32_t>(rr) * (C * 2);
+      if (q == 0) lds_dma16<true>(a, voff, la);
+      else lds_dma16(a, voff, la);
+      a = nx;
+    }
   };
 
   // tiles 0 and 1 are requested first (their indices read straight from global memory)
@@ -370,9 +403,11 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
         __builtin_amdgcn_sched_barrier(0);
       };
       // phase 1: the 32 K steps of S^T, PV blocks 0..15 after the odd steps, one row of tile
-      // i+2 requested after steps 2, 6, .., 30
+      // i+2 requested after steps 2, 6, .., 30 (each row's address read one DMA ahead)
       f32x16 sacc;
       {
+        RowAddr ra{0u, 0u};
+        if (dma) ra = addr_of(pn2, 0);
         bf16x8 s0 = read_s(Eb, 0), s1 = read_s(Eb, 1);
         hb_nops_valu_to_mfma();  // P was written by VALU code
 #pragma unroll
@@ -384,7 +419,11 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
           s0 = s1;
           s1 = s2;
           if (k & 1) pv_step(k >> 1);
-          if ((k & 3) == 2 && dma) gload_row(pn2, k >> 2, dbuf);
+          if ((k & 3) == 2 && dma) {
+            const RowAddr cur = ra;
+            if ((k >> 2) + 1 < RPW) ra = addr_of(pn2, (k >> 2) + 1);
+            dma_row(cur, k >> 2, dbuf);
+          }
         }
         hb_v_fence_after_mfma(sacc);
       }
@@ -691,14 +730,18 @@ __global__ __launch_bounds__(MqaHbqShape::NT) void mqa_hbq_kernel(MqaParams p) {
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_uchar*)smem));
   auto gload = [&](const uint16_t* ptr, int buf) {
     const uint64_t pv = reinterpret_cast<uint64_t>(ptr);
+    RowAddr a = row_addr(pv, hb);
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
       const int rr = hb + 2 * q;
-      const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv), rr);
-      const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(pv >> 32), rr);
-      lds_dma16((static_cast<uint64_t>(hi) << 32) | lo, static_cast<uint32_t>(l ^ swz(rr)) << 4,
-                lds_base + static_cast<uint32_t>(qs * 2 + buf) * TB +
-                    static_cast<uint32_t>(rr) * (C * 2));
+      RowAddr nx = a;
+      if (q + 1 < RPW) nx = row_addr(pv, rr + 2);  // one DMA ahead of its own
+      const uint32_t voff = static_cast<uint32_t>(l ^ swz(rr)) << 4;
+      const uint32_t la = lds_base + static_cast<uint32_t>(qs * 2 + buf) * TB +
+                          static_cast<uint32_t>(rr) * (C * 2);
+      if (q == 0) lds_dma16<true>(a, voff, la);
+      else lds_dma16(a, voff, la);
+      a = nx;
     }
   };
 
