@@ -451,7 +451,8 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
       mx = max_xor32(mx) * p.scale_log2;
       const bool move = mx > m_ref + 8.f;
       const float m_new = move ? mx : m_ref;
-      float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+      // nothing summed yet (reference still -inf): the accumulators are zero, no rescale
+      float alpha = (move && m_ref != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
       float mu = (m_new == -INFINITY) ? 0.f : m_new;
       asm volatile("" : "+v"(alpha), "+v"(mu));
       pv_step(17);
@@ -617,8 +618,8 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
 // requested while tile i is computed: S^T, softmax, PV), so four waves work on two independent
 // key lists with one barrier per step.  A query whose list has fewer tiles computes fully
 // masked tiles in the remaining steps (no effect on its sums).  The output is merged with the
-// sink, normalised and rotated back in place (the span-merge arithmetic of the combine, applied
-// to one span) and leaves as whole 1 KiB rows.
+// sink and normalised (the combine's span-merge arithmetic for one span, folded into one factor
+// per head), rotated back in place and leaves as whole 1 KiB rows.
 struct MqaHbqShape {
   static constexpr int NW = 4, NT = 64 * NW, HPW = 32, QPW = 2, HPQ = 64;
   static constexpr int C = 512;
@@ -658,10 +659,17 @@ __global__ __launch_bounds__(MqaHbqShape::NT) void mqa_hbq_kernel(MqaParams p) {
   int pre0 = 0;
   if constexpr (SPARSE) pre0 = p.idx[static_cast<size_t>(row) * p.k + min(n32, p.k - 1)];
   // position and entry count of both rows of the workgroup (the step count is the larger of
-  // the two lists'), sink and RoPE frequency, then the query slice
+  // the two lists'), the query's index list (every load issued now, clamped into its k
+  // indices, and stored to LDS once the list length is known: one round trip instead of one
+  // per 128 indices), sink and RoPE frequency, then the query slice
   const int rowo = min(row0 + (qs ^ 1), rows - 1);
   int t_vec = mqa_position_request(p, row), to_vec = mqa_position_request(p, rowo);
   int ne_vec = p.n_entries[b], neo_vec = p.n_entries[rowo / p.nq];
+  constexpr int IPT = kHbqMaxList / 128;  // index-list entries per thread of a query slot
+  int idxv[IPT];
+#pragma unroll
+  for (int u = 0; u < IPT; ++u)
+    idxv[u] = SPARSE ? p.idx[static_cast<size_t>(row) * p.k + min(tq + 128 * u, p.k - 1)] : 0;
   float sink_raw = *(p.sink ? p.sink + (head_ok ? head : 0) : p.inv_freq);
   float freq_v = p.inv_freq[min(tq, (p.r >> 1) - 1)];
   asm volatile("" ::: "memory");
@@ -673,6 +681,8 @@ __global__ __launch_bounds__(MqaHbqShape::NT) void mqa_hbq_kernel(MqaParams p) {
       qv[kk] = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + h * 8);
   }
   asm volatile("" : "+v"(ne_vec), "+v"(neo_vec), "+v"(sink_raw), "+v"(freq_v) : : "memory");
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) asm volatile("" : "+v"(idxv[u]) : : "memory");
   const int t = mqa_position_take(p, row, t_vec);
   const int to = mqa_position_take(p, rowo, to_vec);
   auto list_len = [&](int tt, int ne_raw) {  // n_sel + n_w of a row at position tt
@@ -755,10 +765,14 @@ __global__ __launch_bounds__(MqaHbqShape::NT) void mqa_hbq_kernel(MqaParams p) {
   }
   if constexpr (LIST) {
     const int e1 = min(R, n_sel);
-    for (int j = tq; j < e1; j += 128) {
-      int v = SPARSE ? p.idx[static_cast<size_t>(row) * p.k + j] : j;
-      if constexpr (PAGED) v = xlate(v);
-      s_idx[j] = v;
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int j = tq + 128 * u;
+      if (j < e1) {
+        int v = SPARSE ? idxv[u] : j;
+        if constexpr (PAGED) v = xlate(v);
+        s_idx[j] = v;
+      }
     }
   }
   if (tq < (p.r >> 1)) {
@@ -863,7 +877,8 @@ __global__ __launch_bounds__(MqaHbqShape::NT) void mqa_hbq_kernel(MqaParams p) {
     mx = max_xor32(mx) * p.scale_log2;
     const bool move = mx > m_ref + 8.f;
     const float m_new = move ? mx : m_ref;
-    const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+    // nothing summed yet (reference still -inf): the accumulators are zero, no rescale
+    const float alpha = (move && m_ref != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
     const float mu = (m_new == -INFINITY) ? 0.f : m_new;
 #pragma unroll
     for (int e = 0; e < 16; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(v[e], p.scale_log2, -mu));
@@ -902,10 +917,11 @@ __global__ __launch_bounds__(MqaHbqShape::NT) void mqa_hbq_kernel(MqaParams p) {
   hb_acc_fence_after_mfma(acc);
   __syncthreads();  // every wave is done with the rings before it stages its outputs
 
-  // ---- epilogue: the merge of this one span with the sink (as the combine would merge it),
-  // the rotation back on the RoPE dims (the last four blocks: rope_dim <= 128), staged in tile
-  // buffer `wave` (chunk c of head row n at c ^ ((n >> 1) & 15), halves swapped for odd n) and
-  // written as whole 1 KiB rows
+  // ---- epilogue: the span merged with the sink (the combine's arithmetic for one span: the
+  // weight of the span and the normalisation by the sum with the sink's term, folded into one
+  // factor per head), the rotation back on the RoPE dims (the last four blocks: rope_dim <=
+  // 128), staged in tile buffer `wave` (chunk c of head row n at c ^ ((n >> 1) & 15), halves
+  // swapped for odd n) and written as whole 1 KiB rows
   const float l_tot = sum_xor32(l_part);
   const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float a2 = (p.sink && head_ok) ? sink_raw * kLog2e : -INFINITY;
@@ -913,6 +929,7 @@ __global__ __launch_bounds__(MqaHbqShape::NT) void mqa_hbq_kernel(MqaParams p) {
   sm_raise(sm, fmaxf(sm.M, m_ref));
   const float wgt = sm_add(sm, m_ref, l_tot);
   const float inv = sm_inv(sm, p.sink != nullptr, a2);
+  const float fsc = il * wgt * inv;  // O -> output
   const int rope0 = C - p.r;
   unsigned char* so = smem + wave * TB;
   const int sw_c = (n32 >> 1) & 15, sw_h = h ^ (n32 & 1);
@@ -923,8 +940,7 @@ __global__ __launch_bounds__(MqaHbqShape::NT) void mqa_hbq_kernel(MqaParams p) {
     for (int i = 0; i < 4; ++i) {
       float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        x[e] = sm_fold(0.f, bf16_round(acc[dt][4 * i + e] * il), wgt) * inv;
+      for (int e = 0; e < 4; ++e) x[e] = acc[dt][4 * i + e] * fsc;
       if (dt >= 12) {
 #pragma unroll
         for (int pr2 = 0; pr2 < 2; ++pr2) {
@@ -947,11 +963,20 @@ __global__ __launch_bounds__(MqaHbqShape::NT) void mqa_hbq_kernel(MqaParams p) {
   const int head0 = hb * SH::HPW;
   const int n_rows = live ? min(SH::HPW, p.n_heads - head0) : 0;
   uint16_t* obase = p.out + (static_cast<size_t>(row) * p.n_heads + head0) * C;
+  // eight rows at a time: their LDS reads all issued before the first store
 #pragma unroll 1
-  for (int n = 0; n < n_rows; ++n) {
-    u32x4 w4 = *reinterpret_cast<const u32x4*>(so + n * (C * 2) + ((l ^ ((n >> 1) & 15)) << 4));
-    if (n & 1) w4 = u32x4{w4[2], w4[3], w4[0], w4[1]};
-    *reinterpret_cast<u32x4*>(obase + static_cast<size_t>(n) * C + l * 8) = w4;
+  for (int n0 = 0; n0 < n_rows; n0 += 8) {
+    u32x4 w4[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int n = min(n0 + u, n_rows - 1);
+      w4[u] = *reinterpret_cast<const u32x4*>(so + n * (C * 2) + ((l ^ ((n >> 1) & 15)) << 4));
+      if (n & 1) w4[u] = u32x4{w4[u][2], w4[u][3], w4[u][0], w4[u][1]};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (n0 + u < n_rows)
+        *reinterpret_cast<u32x4*>(obase + static_cast<size_t>(n0 + u) * C + l * 8) = w4[u];
   }
 }
 
