@@ -233,11 +233,6 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
   auto addr_of = [&](const uint16_t* ptr, int q) {  // row wave + NW q of a tile
     return row_addr(reinterpret_cast<uint64_t>(ptr), wave + q * NW);
   };
-  auto dma_row = [&](RowAddr a, int q, int buf) {
-    const int rr = wave + q * NW;
-    lds_dma16(a, static_cast<uint32_t>(l ^ swz(rr)) << 4,
-              lds_base + static_cast<uint32_t>(buf) * TB + static_cast<uint32_t>(rr) * (C * 2));
-  };
   auto gload = [&](const uint16_t* ptr, int buf) {  // all of this wave's rows of a tile
     RowAddr a = addr_of(ptr, 0);
 #pragma unroll
@@ -402,12 +397,12 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
         t1 = t2;
         __builtin_amdgcn_sched_barrier(0);
       };
-      // phase 1: the 32 K steps of S^T, PV blocks 0..15 after the odd steps, one row of tile
-      // i+2 requested after steps 2, 6, .., 30 (each row's address read one DMA ahead)
+      // phase 1: tile i+2 requested, then the 32 K steps of S^T with PV blocks 0..15 after the
+      // odd steps (the requests issued together at the start of the phase measured 4% faster per
+      // tile than one after every fourth step)
       f32x16 sacc;
       {
-        RowAddr ra{0u, 0u};
-        if (dma) ra = addr_of(pn2, 0);
+        if (dma) gload(pn2, dbuf);
         bf16x8 s0 = read_s(Eb, 0), s1 = read_s(Eb, 1);
         hb_nops_valu_to_mfma();  // P was written by VALU code
 #pragma unroll
@@ -419,11 +414,6 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
           s0 = s1;
           s1 = s2;
           if (k & 1) pv_step(k >> 1);
-          if ((k & 3) == 2 && dma) {
-            const RowAddr cur = ra;
-            if ((k >> 2) + 1 < RPW) ra = addr_of(pn2, (k >> 2) + 1);
-            dma_row(cur, k >> 2, dbuf);
-          }
         }
         hb_v_fence_after_mfma(sacc);
       }
