@@ -402,11 +402,14 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
 #pragma unroll
     for (int i = 0; i < CH; ++i)
       asm volatile("" : "+v"(f[i][0]), "+v"(f[i][1]), "+v"(f[i][2]), "+v"(f[i][3]) : : "memory");
+    // keys past n_vis are 0, below every key of a finite score (order_key >= 0x007fffff), so
+    // the candidate passes below compare keys only; one bound check per chunk (the row's partial
+    // last chunk is filled in below)
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int base = (i * THREADS + tid) * 4;
+      const bool full = (i * THREADS + tid) * 4 + 4 <= n_vis;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kr[i * 4 + j] = (base + j < n_vis) ? order_key(f[i][j]) : 0u;
+      for (int j = 0; j < 4; ++j) kr[i * 4 + j] = full ? order_key(f[i][j]) : 0u;
     }
   }
   // the first histogram pass finds it cleared (written while the loads are in flight)
@@ -456,8 +459,9 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
       __syncthreads();
     }
   }
-  // candidates (visible keys >= T_lo) per chunk column, packed two columns to a word, and the
-  // largest candidate key
+  // candidates (visible keys >= T_lo; past n_vis every key is 0 < Tc) per chunk column, packed
+  // two columns to a word, and the largest key (a candidate whenever any key is one)
+  const uint32_t Tc = max(Tlo, 1u);
   uint32_t cw[CW], kmax = 0;
 #pragma unroll
   for (int w = 0; w < CW; ++w) cw[w] = 0u;
@@ -466,9 +470,8 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
     uint32_t c = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool in = (i * THREADS + tid) * 4 + j < n_vis && kr[i * 4 + j] >= Tlo;
-      c += in ? 1u : 0u;
-      kmax = in ? max(kmax, kr[i * 4 + j]) : kmax;
+      c += kr[i * 4 + j] >= Tc ? 1u : 0u;
+      kmax = max(kmax, kr[i * 4 + j]);
     }
     cw[i / 2] += c << (16 * (i & 1));
   }
@@ -513,10 +516,9 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
       uint32_t sl = slot[i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int e = (i * THREADS + tid) * 4 + j;
-        if (e < n_vis && kr[i * 4 + j] >= Tlo) {
+        if (kr[i * 4 + j] >= Tc) {
           s_ckey[sl] = kr[i * 4 + j];
-          s_cidx[sl] = e;
+          s_cidx[sl] = (i * THREADS + tid) * 4 + j;
           ++sl;
         }
       }
