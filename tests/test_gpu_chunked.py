@@ -5,7 +5,8 @@ prompt when every chunk has 16 or more tokens; chunk boundaries fall inside comp
 (the compressor's tail ring carries the open block) and the window ring carries the last
 n_win - 1 rows across them.  Shorter chunks (decode-sized runs of queries take the decode span
 plan) and a batch whose sequences sit at different positions are checked against the oracle,
-stage-wise on the GPU's stored state."""
+stage-wise on the GPU's stored state; chunks written into the block cache layout leave the bits
+of one contiguous call."""
 import dataclasses
 
 import numpy as np
@@ -15,7 +16,8 @@ import torch
 import long_context_sparse_15_amd as csa
 import oracle as O
 from synth import inputs as S
-from gpu_common import (DEV, bf16_f64, check_close, check_selection, host_bits, say, workspace)
+from gpu_common import (DEV, bf16_f64, check_close, check_selection, config_for, dev, host_bits,
+                        say, workspace)
 from test_gpu_layer import _build
 
 pytestmark = pytest.mark.gpu
@@ -173,3 +175,54 @@ def test_chunked_prefill_short_chunks_and_ragged_positions():
                              x["inv_freq"], 1e-6)
     ent = host_bits(ct["entries"][1])[:500 // w.m]
     check_close(O.bf16_bits_to_f64(ent), O.bf16_bits_to_f64(comp["entries"]), "seq 1 entries")
+
+
+@pytest.mark.parametrize("name,T,chunks", [
+    ("tiny_csa", 2048, [700, 1000, 348]),
+    ("tiny_hca", 2040, [1000, 1040]),
+    ("wide", 1024, [333, 500, 191]),
+])
+def test_chunked_prefill_on_block_cache_equals_one_call(name, T, chunks):
+    """Chunked prefill on the block cache layout (entries, keys and scales in randomly placed
+    pool blocks) leaves the bits of one contiguous call: entries and keys read back through the
+    block table, window rows, selections and outputs."""
+    from test_gpu_paged import _block_entries, _from_pool, _layer_cache, _perm_table, _weights
+    w = _workload(name)
+    say("chunked prefill, block cache", name, T, chunks)
+    x = S.layer_inputs(w, T=T)
+    d = {k: dev(x[k]) for k in x if isinstance(x[k], np.ndarray)}
+    cfg = config_for(w, d["inv_freq"])
+    be = _block_entries(w)
+    bps = (x["T_total"] // w.m + 1 + be - 1) // be
+    n_max = bps * be
+    slots = 1 << (x["T_total"] - 1).bit_length()
+    assert slots >= max(chunks) + w.n_win - 1
+    table, n_blocks = _perm_table(1, bps, 3, seed=T + 7)
+    weights = _weights(w, d)
+    cache_c, ct_c = _layer_cache(w, cfg, n_max, slots, False)
+    cache_p, ct_p = _layer_cache(w, cfg, n_max, slots, False, table, n_blocks)
+    ws = workspace(csa.workspace_size(cfg, csa.OP_PREFILL, 1, T, n_max))
+    shape = (1, T, w.n_h, w.c)
+    out1 = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    out2 = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    idx1 = torch.full((1, T, max(w.k, 1)), -7, dtype=torch.int32, device=DEV)
+    idx2 = idx1.clone()
+    _prefill(w, x, cfg, cache_c, weights, d, ws, out1, idx1, 0, T)
+    t0 = 0
+    for n in chunks:
+        pos0 = torch.full((1,), t0, dtype=torch.int32, device=DEV)
+        _prefill(w, x, cfg, cache_p, weights, d, ws, out2, idx2, t0, n, pos0=pos0)
+        t0 += n
+    torch.cuda.synchronize()
+    n_ent = T // w.m
+    assert int(ct_p["n_entries"][0]) == n_ent
+    assert torch.equal(_from_pool(ct_p["entries"], table, be)[0, :n_ent],
+                       ct_c["entries"][0, :n_ent]), "entries differ"
+    assert torch.equal(ct_p["window"][:, :T], ct_c["window"][:, :T]), "window rows differ"
+    if w.mode == "csa":
+        assert torch.equal(_from_pool(ct_p["idx_keys"], table, be)[0, :n_ent],
+                           ct_c["idx_keys"][0, :n_ent]), "indexer keys differ"
+        assert torch.equal(_from_pool(ct_p["idx_scale"], table, be)[0, :n_ent].view(torch.int32),
+                           ct_c["idx_scale"][0, :n_ent].view(torch.int32)), "key scales differ"
+        assert torch.equal(idx1, idx2), "selections differ"
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), "outputs differ"
