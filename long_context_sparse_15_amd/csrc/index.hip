@@ -575,11 +575,11 @@ static hipError_t launch_gemm_scores(const IndexArgs& a, hipStream_t s) {
                       : launch_gemm_scores_p<true, false, ST>(a, s);
 }
 
+// (Both scorers write the same score rows, so either selection path reads them: rows of a
+// cache over 32768 entries -- the chunks of a long prompt -- are scored as a product too.)
 template <typename ST>
 static hipError_t launch_index_scores_t(const IndexArgs& a, hipStream_t s) {
-  const bool multi = index_use_multi(a.B * a.nq, a.n_max);
-  return (!multi && use_gemm_scores(a)) ? launch_gemm_scores<ST>(a, s)
-                                        : launch_scores<ST>(a, kScoreChunk, s);
+  return use_gemm_scores(a) ? launch_gemm_scores<ST>(a, s) : launch_scores<ST>(a, kScoreChunk, s);
 }
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {

@@ -75,21 +75,24 @@ def _check_oracle(w, x, ct, out, idx, slots, n_ent, b, ts, what):
         check_close(out_h[t], ref, "%s query %d output" % (what, t))
 
 
-@pytest.mark.parametrize("name,T,chunks", [
-    ("tiny_csa", 2048, [700, 1000, 348]),
-    ("tiny_csa", 2046, [16, 17, 1013, 1000]),
-    ("tiny_hca", 2040, [1000, 1040]),
-    ("wide", 1024, [333, 500, 191]),
+@pytest.mark.parametrize("name,T,chunks,n_max", [
+    ("tiny_csa", 2048, [700, 1000, 348], None),
+    ("tiny_csa", 2046, [16, 17, 1013, 1000], None),
+    ("tiny_hca", 2040, [1000, 1040], None),
+    ("wide", 1024, [333, 500, 191], None),
+    # a cache of more than 32768 entries, as the chunks of a long prompt see: the selection
+    # takes the multi-workgroup path
+    ("wide", 1024, [333, 500, 191], 40000),
 ])
-def test_chunked_prefill_equals_one_call(name, T, chunks):
+def test_chunked_prefill_equals_one_call(name, T, chunks, n_max):
     assert sum(chunks) == T and min(chunks) >= 16
     w = _workload(name)
-    say("chunked prefill", name, T, chunks)
+    say("chunked prefill", name, T, chunks, n_max)
     x = S.layer_inputs(w, T=T)
     # one cache filled by a single call, one by the chunks (same ring size: row u in slot
     # u % slots)
-    cfg, cache1, ct1, weights, d, n_max, slots = _build(w, x, x["T_total"])
-    _, cache2, ct2, _, _, _, _ = _build(w, x, x["T_total"])
+    cfg, cache1, ct1, weights, d, n_max, slots = _build(w, x, x["T_total"], n_max)
+    _, cache2, ct2, _, _, _, _ = _build(w, x, x["T_total"], n_max)
     assert slots >= max(chunks) + w.n_win - 1
     ws = workspace(csa.workspace_size(cfg, csa.OP_PREFILL, w.B, T, n_max))
     shape = (w.B, T, w.n_h, w.c)

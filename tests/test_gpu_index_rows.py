@@ -92,6 +92,9 @@ def _run(x, B, nq, n_max, H_I, d_I, k, m=4, bf16=False):
     (13, 1, 48, 512, [512], 64, 16, "prefix"),
     # one full tile of 16 rows over long rows (several 64-entry groups per wave)
     (14, 1, 16, 9000, [8800], 64, 256, "spread"),
+    # a cache of more than 32768 entries (a chunk of a long prompt): rows scored as a product
+    # over heads, selected by the multi-workgroup path
+    (15, 1, 20, 40000, [39000], 64, 512, "spread"),
 ])
 @pytest.mark.parametrize("fmt", ["e4m3", "mxfp4", "fp4q", "e4m3-bf16", "fp4q-bf16"])
 def test_index_rows_parity(case, fmt):

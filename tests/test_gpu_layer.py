@@ -24,10 +24,10 @@ def _e4m3_steps(a, b):
     return np.abs(mag(a) - mag(b))
 
 
-def _build(w, x, T_total):
+def _build(w, x, T_total, n_max=None):
     d = {k: dev(x[k]) for k in x if isinstance(x[k], np.ndarray)}
     cfg = config_for(w, d["inv_freq"])
-    n_max = T_total // w.m + 1
+    n_max = n_max or T_total // w.m + 1
     win_slots = 1 << (T_total - 1).bit_length()
     tr, tc = csa.tail_shape(cfg)
     B = w.B
