@@ -49,8 +49,9 @@ DEFAULT_EXTRA = ",".join([
     "qo_proj_64k",
     "csa_decode_128k_paged", "csa_decode_1m_paged", "hca_decode_1m_paged",
     "csa_decode_128k_mixed", "csa_decode_1m_mixed", "hca_decode_1m_mixed",
+    "csa_prefill_64k_chunk8k",
 ])
-FLAGS = ("mxfp4", "fp4q", "bf16s", "paged", "mixed")
+FLAGS = ("mxfp4", "fp4q", "bf16s", "paged", "mixed", "chunk8k")
 
 # source files whose hash a committed counter summary records, per kernel
 KERNEL_SOURCES = {"index_score": ("index.hip", "index_common.h", "common.h", "kernels.h"),
@@ -334,10 +335,23 @@ def prefill_workload(name, K, W):
                      device=dev)
     out = torch.empty((B, T, w.n_h, w.c), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
+    # "chunk8k": the same prompt as consecutive csa_prefill calls of 8192 tokens, each chunk
+    # continuing the cache at its start position (the first from position 0)
+    chunk = 8192 if "chunk8k" in flags else T
+    parts = []
+    for c0 in range(0, T, chunk):
+        sl = slice(c0, c0 + chunk)
+        parts.append(dict(H=x["H"][:, sl].contiguous(), q=x["q"][:, sl].contiguous(),
+                          out=out[:, sl], qi=x["qi"][:, sl].contiguous(),
+                          qi_scale=x["qi_scale"][:, sl].contiguous(),
+                          wi=x["wi"][:, sl].contiguous(),
+                          pos0=None if c0 == 0 else
+                          torch.full((B,), c0, dtype=torch.int32, device=dev)))
 
     def step(i):
-        csa.prefill(cfg, x["H"], weights, cache, x["q"], x["sink"], out, ws, qi=x["qi"],
-                    qi_scale=x["qi_scale"], wi=x["wi"])
+        for pt in parts:
+            csa.prefill(cfg, pt["H"], weights, cache, pt["q"], x["sink"], pt["out"], ws,
+                        qi=pt["qi"], qi_scale=pt["qi_scale"], wi=pt["wi"], pos0=pt["pos0"])
 
     ms, per = _time_steps(step, K, W, stream)
     prof = _profiled(step, K, W)
@@ -349,12 +363,15 @@ def prefill_workload(name, K, W):
            "step_ms": _step_stats(per), "mfma_roofline_frac": ideal_ms / ms,
            "kernels_ms_per_step": {k: v[1] / K for k, v in prof.items()},
            # the dominant kernel: sparse + window attention, a bf16 MFMA contraction
-           "roofline": _kernel_roofline(prof, "mqa_sparse", f_mqa, "mfma", BF16_PEAK_TFLOPS,
-                                        "TFLOP/s", name),
+           "roofline": _kernel_roofline(prof, "mqa_sparse", f_mqa / len(parts), "mfma",
+                                        BF16_PEAK_TFLOPS, "TFLOP/s", name),
            # the indexer against its own MFMA peak (fp8, or fp4 for the FP4 query path)
-           "indexer_roofline": _kernel_roofline(prof, "index_score", f_idx, "mfma", idx_peak,
-                                                "TFLOP/s", name)}
-    del x, ws, out, ct, cache
+           "indexer_roofline": _kernel_roofline(prof, "index_score", f_idx / len(parts), "mfma",
+                                                idx_peak, "TFLOP/s", name)}
+    if len(parts) > 1:
+        res["chunks"] = {"tokens": chunk, "calls_per_step": len(parts),
+                         "work_per_launch": "the step's flops / calls (an average chunk)"}
+    del x, ws, out, ct, cache, parts
     torch.cuda.empty_cache()
     return res
 
@@ -555,11 +572,11 @@ def cpu_baseline(name, budget_s=12.0):
     """The CPU oracle as it stands, on a bounded sample of the workload `name` (host cores; the
     thread count is what the BLAS pool actually uses).  The block layout and the mixed entry
     format are invisible to the oracle, which computes the same attention on the same values:
-    those lines reuse their base workload's oracle timing."""
+    those lines reuse their base workload's oracle timing, as does a prefill taken in chunks."""
     threads, model = _host_info()
     base, flags = parse_name(name)
-    layout_only = flags & {"paged", "mixed"}
-    key = base + "".join("_" + f for f in sorted(flags - {"paged", "mixed"}))
+    layout_only = flags & {"paged", "mixed", "chunk8k"}
+    key = base + "".join("_" + f for f in sorted(flags - {"paged", "mixed", "chunk8k"}))
     if key not in _CPU_CACHE:
         if base.startswith("qo_proj"):
             r = _cpu_proj()
@@ -570,9 +587,10 @@ def cpu_baseline(name, budget_s=12.0):
         _CPU_CACHE[key] = r
     r = dict(_CPU_CACHE[key])
     if layout_only:
+        names = {"paged": "block layout", "mixed": "mixed entry format",
+                 "chunk8k": "chunking (the same tokens in one pass)"}
         r["sample"] = "the %s oracle timing (the oracle has no %s): %s" % (
-            key, " / ".join("block layout" if f == "paged" else "mixed entry format"
-                            for f in sorted(layout_only)), r["sample"])
+            key, " / ".join(names[f] for f in sorted(layout_only)), r["sample"])
     r["cores"] = threads
     r["cpu_model"] = model
     return r
