@@ -49,7 +49,7 @@ DEFAULT_EXTRA = ",".join([
     "qo_proj_64k",
     "csa_decode_128k_paged", "csa_decode_1m_paged", "hca_decode_1m_paged",
     "csa_decode_128k_mixed", "csa_decode_1m_mixed", "hca_decode_1m_mixed",
-    "csa_prefill_64k_chunk8k",
+    "csa_prefill_64k_chunk8k", "csa_prefill_1m_chunk",
 ])
 FLAGS = ("mxfp4", "fp4q", "bf16s", "paged", "mixed", "chunk8k")
 
@@ -376,6 +376,77 @@ def prefill_workload(name, K, W):
     return res
 
 
+def chunk_flops(w):
+    """Algorithmic FLOPs of one chunk of a chunked prefill (T tokens at positions t..t+T-1):
+    compressor projections of the chunk, the indexer of every chunk query over its visible
+    entries, sparse + window attention."""
+    n_cols = 5 * w.c + 4 * w.d_I
+    f_comp = 2.0 * w.B * w.T * w.D * n_cols
+    vis = [min(w.N, (u + 1) // w.m) for u in range(w.t, w.t + w.T)]
+    f_idx = 2.0 * w.B * sum(vis) * w.H_I * w.d_I
+    f_mqa = 4.0 * w.B * sum(min(w.k, v) + w.n_win for v in vis) * w.n_h * w.c
+    return f_comp, f_idx, f_mqa
+
+
+def chunk_workload(name, K, W):
+    """One chunk of a long prompt's chunked prefill: csa_prefill of T tokens continuing a
+    sequence at position t over a cache whose first t/m entries are closed (synthetic entries,
+    keys, window rows and compressor tail stand for the earlier chunks).  Each step first
+    restores the entry count to t/m (a one-element fill) so that every step writes the chunk's
+    entries anew."""
+    import torch
+    import long_context_sparse_15_amd as csa
+    from synth import inputs as S
+    from synth import gpu as G
+
+    base, flags = parse_name(name)
+    w = S.WORKLOADS[base]
+    dev = "cuda"
+    x = G.layer_inputs(w, dev)
+    xc = G.decode_cache_inputs(S.shrink(w, B=1), dev)
+    B, T, N = w.B, w.T, w.N
+    cfg = csa.make_config(csa.MODE_CSA, w.m, w.n_h, w.c, w.r, x["inv_freq"], top_k=w.k,
+                          n_win=w.n_win, idx_heads=w.H_I, idx_dim=w.d_I, hidden=w.D,
+                          softmax_scale=w.scale)
+    tr, tc = csa.tail_shape(cfg)
+    slots = 1 << (T + w.n_win - 1 - 1).bit_length()  # >= T + n_win - 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 100)
+    n_pre = w.t // w.m
+    ne = torch.full((B,), n_pre, dtype=torch.int32, device=dev)
+    ct = dict(entries=xc["entries"], idx_keys=xc["ikeys"], idx_scale=xc["iscale"],
+              window=G.bf16_normal(g, (B, slots, w.c), dev), n_entries=ne,
+              tail=torch.randn((B, tr, tc), generator=g, device=dev))
+    cache = csa.make_cache(N, slots, **ct)
+    weights = csa.make_weights(x["W"], x["Ba"], x["gamma"], x["gamma_win"], bias_b=x["Bb"],
+                               bias_ia=x["BIa"], bias_ib=x["BIb"])
+    ws = torch.empty(csa.workspace_size(cfg, csa.OP_PREFILL, B, T, N), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, T, w.n_h, w.c), dtype=torch.bfloat16, device=dev)
+    pos0 = torch.full((B,), w.t, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ne.fill_(n_pre)
+        csa.prefill(cfg, x["H"], weights, cache, x["q"], x["sink"], out, ws, qi=x["qi"],
+                    qi_scale=x["qi_scale"], wi=x["wi"], pos0=pos0)
+
+    ms, per = _time_steps(step, K, W, stream)
+    prof = _profiled(step, K, W)
+    f_comp, f_idx, f_mqa = chunk_flops(w)
+    res = {"workload": name, "value": B * T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+           "step_ms": _step_stats(per), "context": w.t + T,
+           "kernels_ms_per_step": {k: v[1] / K for k, v in prof.items()},
+           # the dominant kernel at this context: the indexer over every visible entry
+           "roofline": _kernel_roofline(prof, "index_score", f_idx, "mfma", FP8_PEAK_TFLOPS,
+                                        "TFLOP/s", name),
+           "attention_roofline": _kernel_roofline(prof, "mqa_sparse", f_mqa, "mfma",
+                                                  BF16_PEAK_TFLOPS, "TFLOP/s", name)}
+    del x, xc, ws, out, ct, cache
+    torch.cuda.empty_cache()
+    return res
+
+
 def proj_workload(name, K, W):
     """Query-side projections and grouped output projection of the 64K-token prefill at the
     V4-Flash shape (hidden 4096, r_q 1024, 64 heads x 512, indexer 64 x 128, 8 groups of rank
@@ -541,6 +612,38 @@ def _cpu_prefill(name):
                          "bf16" if bf16s else "fp32")}
 
 
+def _cpu_chunk(name):
+    """A chunk of a 1M-token prompt, extrapolated from bounded samples: the compressor on 1024
+    of its tokens (x T/1024), indexer + top-k + attention on 4 of its query positions over a
+    synthetic cache of N entries (x T/4; every query of the chunk sees about the same number of
+    entries)."""
+    import numpy as np
+    import oracle as O
+    from synth import inputs as S
+    base, _ = parse_name(name)
+    w = S.WORKLOADS[base]
+    Tc = 1024
+    xl = S.layer_inputs(S.shrink(w, decode_steps=0), T=Tc)
+    params = {k: xl[k] for k in ("Ba", "Bb", "BIa", "BIb", "gamma", "gamma_win")}
+    t0 = time.time()
+    O.compress_tokens(xl["H"][0], xl["W"], params, "csa", w.m, w.c, w.d_I, xl["inv_freq"], 1e-6)
+    t_comp = (time.time() - t0) * (w.T / Tc)
+    x = S.decode_cache_inputs(S.shrink(w, t=w.t + w.T - 1), B=1)
+    win = S.bf16_normal(np.random.default_rng(1), (w.n_win, w.c))
+    n_q = 4
+    t0 = time.time()
+    for t in np.linspace(w.t, w.t + w.T - 1, n_q).astype(int):
+        O.csa_query(int(t), x["q"][0, 0], x["qi"][0, 0], x["qi_scale"][0, 0], x["wi"][0, 0],
+                    x["sink"], x["entries"][0], x["ikeys"][0], x["iscale"][0], w.N, win,
+                    lambda u: u % w.n_win, w.m, w.k, w.n_win, w.scale, x["inv_freq"])
+    t_q = (time.time() - t0) * (w.T / n_q)
+    total = t_comp + t_q
+    return {"value": w.B * w.T / total, "unit": "tokens/s", "kind": "oracle",
+            "sample": "extrapolated, not run whole: compressor timed on %d tokens (x%d: %.1f s), "
+                      "indexer + top-k + attention on %d query positions of the chunk over %d "
+                      "entries (x%d: %.1f s)" % (Tc, w.T // Tc, t_comp, n_q, w.N, w.T // n_q, t_q)}
+
+
 def _cpu_proj():
     """Query-side and output projections at the 64K prefill's shape, timed on 512 tokens and
     extrapolated (x128): every product is per token."""
@@ -580,6 +683,8 @@ def cpu_baseline(name, budget_s=12.0):
     if key not in _CPU_CACHE:
         if base.startswith("qo_proj"):
             r = _cpu_proj()
+        elif base.startswith("csa_prefill_1m_chunk"):
+            r = _cpu_chunk(key)
         elif base.startswith("csa_prefill"):
             r = _cpu_prefill(key)
         else:
@@ -624,6 +729,8 @@ def main():
 
     def run(name, head=False):
         print("[bench] %s%s" % ("" if head else "extra ", name), file=sys.stderr, flush=True)
+        if name.startswith("csa_prefill_1m_chunk"):
+            return chunk_workload(name, args.prefill_steps, max(1, args.prefill_steps // 5))
         if name.startswith("csa_prefill"):
             return prefill_workload(name, args.prefill_steps, max(1, args.prefill_steps // 5))
         if name.startswith("qo_proj"):

@@ -280,6 +280,8 @@ constexpr int kGemmWaves = 8;  // two waves per SIMD: one's epilogue overlaps an
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kGemmH = 64;   // largest head count held in LDS
 constexpr int kGemmDI = 128;
+constexpr int kGemmFillTiles = 256;   // workgroups that fill the device (one per CU)
+constexpr int kGemmPartGroups = 64;   // 64-entry groups of an entry part at the least
 // LDS: query codes [h][q][128 B], head factors [h][q] fp32, query block scales [h][q] (4 E8M0
 // bytes, FP4 queries), visible counts [q]
 constexpr size_t kGemmLds = kGemmH * kGemmQ * kGemmDI + 2 * kGemmH * kGemmQ * 4 + kGemmQ * 4;
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ wi, const uint8_t* __restrict__ keys,
     const float* __restrict__ kscale, const int32_t* __restrict__ n_entries,
-    const int32_t* __restrict__ pos, int nq, int n_max, int H_I, int m, int qtiles,
+    const int32_t* __restrict__ pos, int nq, int n_max, int H_I, int m, int qtiles, int gpp,
     ST* __restrict__ scores, int sstride, PageMap pm) {
   static_assert(!QX || MX, "an FP4 query is paired with FP4 keys");
   constexpr int DI = kGemmDI;
@@ -345,8 +347,11 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
 #pragma unroll
   for (int q = 0; q < kGemmQ; ++q) nv_max = max(nv_max, s_nv[q]);
   const int my_nv = s_nv[c16];
-  const int ngroups = (nv_max + 63) / 64;
-  if (wave >= ngroups) return;
+  // this workgroup's part of the entry groups (blockIdx.y of gridDim.y parts of gpp groups:
+  // few query tiles over a long cache still fill the device)
+  const int g0 = static_cast<int>(blockIdx.y) * gpp;
+  const int ngroups = min((nv_max + 63) / 64, g0 + gpp);
+  if (g0 + wave >= ngroups) return;
 
   const size_t seq0 = PAGED ? 0 : static_cast<size_t>(b) * n_max;  // row of entry 0
   const uint8_t* kb = keys + seq0 * KROW + g * (MX ? 16 : 32);
@@ -395,8 +400,8 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
   i32x8 a[4], an[4];
   f32x4 ks[4], ksn[4];
   int sa[4], san[4];
-  load(wave, a, ks, sa);
-  for (int G = wave; G < ngroups; G += kGemmWaves) {
+  load(g0 + wave, a, ks, sa);
+  for (int G = g0 + wave; G < ngroups; G += kGemmWaves) {
     load(min(G + kGemmWaves, ngroups - 1), an, ksn, san);  // always issued: same order
     f32x4 acc[4];
 #pragma unroll
@@ -554,11 +559,19 @@ static hipError_t launch_gemm_scores_t(const IndexArgs& a, hipStream_t s) {
           reinterpret_cast<const void*>(index_gemm_kernel<MX, PAGED, QX, ST>), kGemmLds))
     return e;
   const int qtiles = (a.nq + kGemmQ - 1) / kGemmQ;
+  // entry parts: enough workgroups to fill the device when there are few query tiles (a
+  // 4096-entry part at the least)
+  const int tiles = a.B * qtiles;
+  const int groups = (a.n_max + 63) / 64;
+  const int parts = std::max(1, std::min((kGemmFillTiles + tiles - 1) / tiles,
+                                         (groups + kGemmPartGroups - 1) / kGemmPartGroups));
+  const int gpp = (groups + parts - 1) / parts;
   ProfScope ps("index_score", s);
   index_gemm_kernel<MX, PAGED, QX, ST>
-      <<<static_cast<unsigned>(a.B) * qtiles, kGemmThreads, kGemmLds, s>>>(
+      <<<dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(parts)), kGemmThreads,
+         kGemmLds, s>>>(
           a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I,
-          a.m, qtiles, static_cast<ST*>(a.scores), a.sstride, a.pages);
+          a.m, qtiles, gpp, static_cast<ST*>(a.scores), a.sstride, a.pages);
   return hipGetLastError();
 }
 

@@ -559,12 +559,14 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
 // regions (a list in ascending index order), finds the kk-th key T of the list with one
 // histogram pass over its actual range and emits the keys above it plus the first ties in index
 // order.  The list holds every key >= T of the row exactly when T >= every chunk's T_c (a key
-// >= T is then >= its chunk's threshold); otherwise (a chunk holding far more than its share
-// of the top keys), and on a region overflow or too few candidates, the exact streaming select
-// of the row runs instead.
+// >= T is then >= its chunk's threshold).  Otherwise (a chunk holding far more than its share
+// of the top keys) the chunks with T_c > T are read again for every key >= T and the list is
+// rebuilt around them (see the finalize); on a region overflow, too few candidates or too many
+// such chunks the exact streaming select of the row runs instead.
 constexpr int kCollectChunk = 4096;
 constexpr int kCandPerChunk = 1024;
 constexpr int kSCandCap = 8192;  // candidates of a row held by its finalize workgroup
+constexpr int kRepairChunks = 16;  // chunks a finalize re-reads when their thresholds cut T
 constexpr size_t kMultiLds = static_cast<size_t>(kSCandCap) * 8 + kHistBins * 4;
 
 template <typename ST>
@@ -663,6 +665,8 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   __shared__ int s_res[2];
   __shared__ int s_flag;
   __shared__ uint32_t s_lo, s_hi, s_tmax;
+  __shared__ int s_rchunk[kRepairChunks];       // chunks re-read for keys >= T
+  __shared__ uint32_t s_rcount[kRepairChunks];  // their counts of such keys
   asm volatile("" ::"s"(scores), "s"(sstride), "s"(n_entries), "s"(pos), "s"(nq), "s"(m), "s"(k),
                "s"(n_max), "s"(nchunks), "s"(ccount), "s"(cand), "s"(idx_out),
                "s"(score_out));  // all parameters at once
@@ -745,14 +749,105 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   int need_eq;
   auto ck = [&](int j) { return ckey[j]; };
   select_kth<THREADS>(ck, nc, kk, s_lo, s_hi, hist, s_tmp, s_res, T, need_eq);
-  if (T < s_tmax) {  // some chunk's threshold cut keys that reach T: exact streaming select
-    auto kf = [&](int e) { return order_key(Scores<ST>::at(srow, e)); };
-    radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
-    ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
-    return;
+  int n_list = nc;
+  if (T < s_tmax) {
+    // Some chunk's threshold cut keys that reach T (a chunk holding far more than its share of
+    // the row's top keys, e.g. the newest entries of a prompt).  Those chunks (T_c > T) are
+    // read again for every key >= T, the others keep their regions (all keys >= T_c, T_c <=
+    // T), and the list is rebuilt in index order: it then holds every key >= T of the row, so
+    // its kk-th key T' >= T is the row's and every key >= T' is in it.  Up to kRepairChunks
+    // chunks are re-read; more, or a list over kSCandCap, take the exact streaming select.
+    const uint32_t Tr = T;
+    const bool aff = tid < used && ct_raw > Tr;
+    uint32_t n_aff;
+    const uint32_t ai = block_excl_scan<THREADS>(aff ? 1u : 0u, s_tmp, &n_aff);
+    if (aff && ai < static_cast<uint32_t>(kRepairChunks)) s_rchunk[ai] = tid;
+    __syncthreads();
+    bool ok = n_aff <= static_cast<uint32_t>(kRepairChunks);
+    if (ok) {
+      // keys >= Tr of each re-read chunk, counted (4 keys a thread, one 16-byte load)
+      for (uint32_t a = 0; a < n_aff; ++a) {
+        const int e = s_rchunk[a] * kCollectChunk + tid * 4;
+        float f[4];
+        Scores<ST>::four(srow, min(e, sstride - 4), f);
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c += (e + j < n_vis && order_key(f[j]) >= Tr) ? 1u : 0u;
+        uint32_t tot;
+        block_excl_scan<THREADS>(c, s_tmp, &tot);
+        if (tid == 0) s_rcount[a] = tot;
+      }
+      __syncthreads();
+      const uint32_t cnew = tid < used ? (aff ? s_rcount[ai] : cc_raw) : 0u;
+      uint32_t tot;
+      const uint32_t o = block_excl_scan<THREADS>(cnew, s_tmp, &tot);
+      if (tid < used) s_off[tid] = o;
+      if (tid == 0) {
+        s_off[used] = tot;
+        s_lo = 0xffffffffu;
+        s_hi = 0u;
+      }
+      ok = tot <= static_cast<uint32_t>(kSCandCap);
+      n_list = static_cast<int>(tot);
+      __syncthreads();
+    }
+    if (!ok) {  // exact streaming select over the row
+      auto kf = [&](int e) { return order_key(Scores<ST>::at(srow, e)); };
+      radix_select<THREADS>(kf, n_vis, kk, hist, s_tmp, s_res, T, need_eq);
+      ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
+      return;
+    }
+    uint32_t lo2 = 0xffffffffu, hi2 = 0u;
+    // regions of the chunks that keep them, 16 threads each
+    for (int c = tid >> 4; c < used; c += THREADS / 16) {
+      if (ccount[2 * (static_cast<size_t>(row) * nchunks + c) + 1] > Tr) continue;
+      const uint32_t o = s_off[c], n = s_off[c + 1] - o;
+      const uint64_t* src = cand + (static_cast<size_t>(row) * nchunks + c) * kCandPerChunk;
+      for (uint32_t j = tid & 15; j < n; j += 16) {
+        const uint64_t v = src[j];
+        const uint32_t kv = static_cast<uint32_t>(v >> 32);
+        ckey[o + j] = kv;
+        cidx[o + j] = static_cast<int32_t>(v & 0xffffffffu);
+        lo2 = min(lo2, kv);
+        hi2 = max(hi2, kv);
+      }
+    }
+    // the re-read chunks' keys >= Tr, in index order
+    for (uint32_t a = 0; a < n_aff; ++a) {
+      const int c = s_rchunk[a];
+      const int e = c * kCollectChunk + tid * 4;
+      float f[4];
+      Scores<ST>::four(srow, min(e, sstride - 4), f);
+      uint32_t kv[4], cnt = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kv[j] = e + j < n_vis ? order_key(f[j]) : 0u;
+        cnt += kv[j] >= Tr && kv[j] != 0u ? 1u : 0u;
+      }
+      uint32_t tot;
+      uint32_t o = s_off[c] + block_excl_scan<THREADS>(cnt, s_tmp, &tot);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (kv[j] >= Tr && kv[j] != 0u) {
+          ckey[o] = kv[j];
+          cidx[o] = e + j;
+          lo2 = min(lo2, kv[j]);
+          hi2 = max(hi2, kv[j]);
+          ++o;
+        }
+      }
+    }
+    lo2 = wave_min_u32(lo2);
+    hi2 = wave_max_u32(hi2);
+    if (lane_id() == 0) {
+      atomicMin(&s_lo, lo2);
+      atomicMax(&s_hi, hi2);
+    }
+    __syncthreads();
+    select_kth<THREADS>(ck, n_list, kk, s_lo, s_hi, hist, s_tmp, s_res, T, need_eq);
   }
   // the candidate list is in ascending index order
-  ordered_emit_fn<THREADS>(ck, nc, T, need_eq, k, [&](int slot, int j) {
+  ordered_emit_fn<THREADS>(ck, n_list, T, need_eq, k, [&](int slot, int j) {
     out[slot] = cidx[j];
     if (sout) sout[slot] = Scores<ST>::at(srow, cidx[j]);
   });

@@ -32,7 +32,8 @@ class Workload:
 
 
 # The five workloads: a tiny whole layer (prefill 2048 + 16 decode steps), CSA decode at 128K
-# and 1M context, HCA dense decode at 1M context, and a 64K-token CSA prefill.
+# and 1M context, HCA dense decode at 1M context, and a 64K-token CSA prefill; and a chunk of a
+# 1M-token prompt's chunked prefill.
 WORKLOADS = {
     "tiny_csa": Workload("tiny_csa", "csa", B=1, m=4, c=128, r=64, n_h=8, k=64, H_I=4, d_I=64,
                          D=512, T=2048, decode_steps=16, sink=0.5, seed=0),
@@ -46,6 +47,12 @@ WORKLOADS = {
                               N=8192, t=1 << 20, seed=4),
     "csa_prefill_64k": Workload("csa_prefill_64k", "csa", B=1, m=4, c=512, r=64, n_h=64, k=512,
                                 H_I=64, d_I=128, D=4096, T=65536, seed=5),
+    # one chunk of a long prompt's chunked prefill: T = 4096 new tokens at positions t..t+T-1
+    # (t = 2^20 - 4096, the last chunk of a 1M-token prompt) over a cache of N = 262144 entries
+    # of which the first t/m are closed
+    "csa_prefill_1m_chunk": Workload("csa_prefill_1m_chunk", "csa", B=1, m=4, c=512, r=64,
+                                     n_h=64, k=512, H_I=64, d_I=128, D=4096, T=4096, N=262144,
+                                     t=(1 << 20) - 4096, seed=6),
 }
 
 

@@ -137,13 +137,29 @@ def test_csa_decode_massive_ties_multi_workgroup_fallback():
 
 def test_csa_decode_clustered_top_keys_multi_workgroup_fallback():
     """The top keys of a long row all sit in its first 4096-entry chunk: that chunk's own
-    threshold cuts keys above the k-th key, the finalize sees it and takes the exact path."""
+    threshold cuts keys above the k-th key; the finalize sees it and reads the chunk again for
+    every key at or above the list's k-th key."""
     say("csa decode clustered top keys, multi-workgroup select")
     w = _w("csa_decode_1m")
     x = S.decode_cache_inputs(w, B=1, N=40000)
     x["iscale"][:, :4096] *= 16.0
     x["pos"] = np.array([4 * 40000], dtype=np.int32)
     # the fp32 sums' rounding scales with their 16x larger terms
+    run_csa_case(w, x, score_atol_mult=16.0)
+
+
+@pytest.mark.parametrize("chunks", [(1, 4, 9), (9,)])
+def test_csa_decode_top_keys_in_several_chunks(chunks):
+    """The top keys of two long rows sit in a few 4096-entry chunks (the last one partial, as
+    the newest entries of a prompt would): each such chunk's threshold cuts keys above the k-th
+    key, and the finalize re-reads exactly those chunks; the second row's top keys are spread
+    evenly (no chunk re-read)."""
+    say("csa decode top keys in chunks", chunks)
+    w = _w("csa_decode_1m")
+    x = S.decode_cache_inputs(w, B=2, N=40000)
+    for c in chunks:
+        x["iscale"][0, 4096 * c:4096 * (c + 1)] *= 16.0
+    x["pos"] = np.array([4 * 40000, 4 * 39000 + 2], dtype=np.int32)
     run_csa_case(w, x, score_atol_mult=16.0)
 
 
