@@ -6,7 +6,8 @@ entry points, shapes and workspace plans), checked against the oracle on sampled
 * HCA dense decode, batch 16, 8192 entries (1M context), 128 heads;
 * CSA prefill of 65536 tokens with hidden size 4096 (compressor, causal indexer, per-query
   top-k 512, sparse MQA with window and sink), checked stage-wise on sampled tokens;
-* the two CSA decodes again with MXFP4 indexer keys.
+* the two CSA decodes again with MXFP4 indexer keys;
+* the last 4096-token chunk of a 1M-token prompt (chunked prefill over 262144 entries).
 
 Inputs come from the seeded device generator (synth.gpu); the oracle receives host copies of the
 same tensors."""
@@ -170,3 +171,59 @@ def test_full_csa_prefill_64k():
         ref, _ = O.attend(h16(x["q"][0, t]), rows, sink, w.scale, t, inv)
         got = O.bf16_bits_to_f64(h16(out[0, t].view(torch.int16)))
         check_close(got, ref, "query %d output" % t)
+
+
+def test_full_csa_prefill_1m_chunk():
+    """The last 4096-token chunk of a 1M-token prompt, as bench.py times it: csa_prefill with a
+    start position over a synthetic cache of 262144 entries whose first 261120 are closed (the
+    chunk writes the last 1024 through the compressor, their keys far larger than the synthetic
+    ones, so the newest entries hold most rows' top keys and the multi-workgroup select re-reads
+    their chunk).  Sampled queries: selection against the oracle's scores over every visible
+    entry on the GPU's stored keys, output against the oracle's attention."""
+    w = S.WORKLOADS["csa_prefill_1m_chunk"]
+    say("full-size prefill chunk", w.name, "T=%d at %d over N=%d" % (w.T, w.t, w.N))
+    x = G.layer_inputs(w, DEV)
+    xc = G.decode_cache_inputs(S.shrink(w, B=1), DEV)
+    B, T, N = w.B, w.T, w.N
+    cfg = csa.make_config(csa.MODE_CSA, w.m, w.n_h, w.c, w.r, x["inv_freq"], top_k=w.k,
+                          n_win=w.n_win, idx_heads=w.H_I, idx_dim=w.d_I, hidden=w.D,
+                          softmax_scale=w.scale)
+    tr, tc = csa.tail_shape(cfg)
+    slots = 1 << (T + w.n_win - 2).bit_length()
+    g = torch.Generator(device=DEV)
+    g.manual_seed(w.seed + 100)
+    n_pre = w.t // w.m
+    ct = dict(entries=xc["entries"], idx_keys=xc["ikeys"], idx_scale=xc["iscale"],
+              window=G.bf16_normal(g, (B, slots, w.c), DEV),
+              n_entries=torch.full((B,), n_pre, dtype=torch.int32, device=DEV),
+              tail=torch.randn((B, tr, tc), generator=g, device=DEV))
+    cache = csa.make_cache(N, slots, **ct)
+    weights = csa.make_weights(x["W"], x["Ba"], x["gamma"], x["gamma_win"], bias_b=x["Bb"],
+                               bias_ia=x["BIa"], bias_ib=x["BIb"])
+    ws = workspace(csa.workspace_size(cfg, csa.OP_PREFILL, B, T, N))
+    out = torch.empty((B, T, w.n_h, w.c), dtype=torch.bfloat16, device=DEV)
+    idx = torch.full((B, T, w.k), -7, dtype=torch.int32, device=DEV)
+    pos0 = torch.full((B,), w.t, dtype=torch.int32, device=DEV)
+    csa.prefill(cfg, x["H"], weights, cache, x["q"], x["sink"], out, ws, qi=x["qi"],
+                qi_scale=x["qi_scale"], wi=x["wi"], idx_out=idx, pos0=pos0)
+    torch.cuda.synchronize()
+    assert int(ct["n_entries"][0]) == (w.t + T) // w.m
+    inv = x["inv_freq"].cpu().numpy()
+    sink = x["sink"].cpu().numpy()
+    keys = ct["idx_keys"][0].cpu().numpy()
+    ksc = ct["idx_scale"][0].cpu().numpy()
+    ent = h16(ct["entries"][0])
+    win_all = h16(ct["window"][0])
+    rng = np.random.default_rng(6)
+    for i in [0, 1, 2047, T - 1] + list(rng.integers(0, T, 2)):
+        t = w.t + int(i)
+        n_vis = O.visible_entries(t, w.m, N)
+        sc = O.index_scores(x["qi"][0, i].cpu().numpy(), x["qi_scale"][0, i].cpu().numpy(),
+                            x["wi"][0, i].cpu().numpy(), keys, ksc, n_vis)
+        row = idx[0, i].cpu().numpy()
+        check_selection(row, sc, w.k, "chunk query %d selection" % i)
+        sel = row[:min(w.k, n_vis)]
+        rows = np.concatenate([ent[sel], win_all[[u % slots for u in O.window_tokens(t, w.n_win)]]])
+        ref, _ = O.attend(h16(x["q"][0, i]), rows, sink, w.scale, t, inv)
+        got = O.bf16_bits_to_f64(h16(out[0, i].view(torch.int16)))
+        check_close(got, ref, "chunk query %d output" % i)
