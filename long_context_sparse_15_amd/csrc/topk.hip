@@ -725,19 +725,36 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   }
   const int nc = static_cast<int>(s_off[used]);
   uint32_t lo = 0xffffffffu, hi = 0u;
-  // 16 threads per region, each region's pairs to its place in the concatenated list
-  for (int c = tid >> 4; c < used; c += THREADS / 16) {
+  // 16 threads per region, each region's pairs to its place in the concatenated list; a
+  // thread's first eight pairs are requested together (one round trip for regions up to 128)
+  auto copy_region = [&](int c) {
     const uint32_t o = s_off[c], n = s_off[c + 1] - o;
     const uint64_t* src = cand + (static_cast<size_t>(row) * nchunks + c) * kCandPerChunk;
-    for (uint32_t j = tid & 15; j < n; j += 16) {
-      const uint64_t v = src[j];
-      const uint32_t kv = static_cast<uint32_t>(v >> 32);
+    const uint32_t j0 = tid & 15, last = n > 0 ? n - 1 : 0;
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[min(j0 + 16u * u, last)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t j = j0 + 16u * u;
+      if (j < n) {
+        const uint32_t kv = static_cast<uint32_t>(v[u] >> 32);
+        ckey[o + j] = kv;
+        cidx[o + j] = static_cast<int32_t>(v[u] & 0xffffffffu);
+        lo = min(lo, kv);
+        hi = max(hi, kv);
+      }
+    }
+    for (uint32_t j = j0 + 128; j < n; j += 16) {
+      const uint64_t w = src[j];
+      const uint32_t kv = static_cast<uint32_t>(w >> 32);
       ckey[o + j] = kv;
-      cidx[o + j] = static_cast<int32_t>(v & 0xffffffffu);
+      cidx[o + j] = static_cast<int32_t>(w & 0xffffffffu);
       lo = min(lo, kv);
       hi = max(hi, kv);
     }
-  }
+  };
+  for (int c = tid >> 4; c < used; c += THREADS / 16) copy_region(c);
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
   if (lane_id() == 0) {
@@ -797,21 +814,12 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
       ordered_emit<THREADS>(kf, n_vis, T, need_eq, kk, k, srow, out, sout, s_tmp);
       return;
     }
-    uint32_t lo2 = 0xffffffffu, hi2 = 0u;
     // regions of the chunks that keep them, 16 threads each
-    for (int c = tid >> 4; c < used; c += THREADS / 16) {
-      if (ccount[2 * (static_cast<size_t>(row) * nchunks + c) + 1] > Tr) continue;
-      const uint32_t o = s_off[c], n = s_off[c + 1] - o;
-      const uint64_t* src = cand + (static_cast<size_t>(row) * nchunks + c) * kCandPerChunk;
-      for (uint32_t j = tid & 15; j < n; j += 16) {
-        const uint64_t v = src[j];
-        const uint32_t kv = static_cast<uint32_t>(v >> 32);
-        ckey[o + j] = kv;
-        cidx[o + j] = static_cast<int32_t>(v & 0xffffffffu);
-        lo2 = min(lo2, kv);
-        hi2 = max(hi2, kv);
-      }
-    }
+    lo = 0xffffffffu;
+    hi = 0u;
+    for (int c = tid >> 4; c < used; c += THREADS / 16)
+      if (ccount[2 * (static_cast<size_t>(row) * nchunks + c) + 1] <= Tr) copy_region(c);
+    uint32_t lo2 = lo, hi2 = hi;
     // the re-read chunks' keys >= Tr, in index order
     for (uint32_t a = 0; a < n_aff; ++a) {
       const int c = s_rchunk[a];
