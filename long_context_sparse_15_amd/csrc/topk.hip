@@ -33,8 +33,10 @@ __device__ void block_find_crossing(const uint32_t* bins, int nbins, uint32_t re
   const uint32_t suf = wtot - inc + own;
   if (l == 0) s_tmp[wave] = wtot;
   __syncthreads();
-  uint32_t later = 0;
-  for (int w2 = wave + 1; w2 < NWAVE; ++w2) later += s_tmp[w2];
+  uint32_t later = 0;  // (a loop of constant length: its reads go out together)
+#pragma unroll
+  for (int w2 = 1; w2 < NWAVE; ++w2)
+    if (w2 > wave) later += s_tmp[w2];
   const uint32_t above = suf - own + later;
   if (above < remaining && remaining <= above + own) {
     uint32_t cum = above;
@@ -120,14 +122,18 @@ __device__ void ordered_emit_fn(KeyFn key, int n, uint32_t T, int need_eq, int c
     s_eq[wave] = ceq;
   }
   __syncthreads();
-  int eq_seen = 0, slot_base = 0;
-  for (int w2 = 0; w2 < wave; ++w2) {
-    const int eqb = eq_seen;
-    int take_eq = need_eq - eqb;
-    take_eq = take_eq < 0 ? 0 : (take_eq > static_cast<int>(s_eq[w2]) ? static_cast<int>(s_eq[w2]) : take_eq);
-    slot_base += static_cast<int>(s_gt[w2]) + take_eq;
-    eq_seen += static_cast<int>(s_eq[w2]);
+  // keys > T and == T in the earlier waves' segments; the == T keys taken before this wave are
+  // the first min(need_eq, eq_seen) of them (a loop of constant length: its reads go out
+  // together)
+  int eq_seen = 0, gt_seen = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < NWAVE - 1; ++w2) {
+    if (w2 < wave) {
+      gt_seen += static_cast<int>(s_gt[w2]);
+      eq_seen += static_cast<int>(s_eq[w2]);
+    }
   }
+  int slot_base = gt_seen + min(need_eq, eq_seen);
   for (int base = s0; base < s1; base += 64) {
     const int e = base + l;
     const uint32_t kv = e < s1 ? key(e) : 0u;
@@ -274,8 +280,8 @@ __device__ void select_kth(KeyFn key, int n, int kk, uint32_t lo, uint32_t hi,
     const int nbk = static_cast<int>(s_nb);
     const uint32_t mine = tid < nbk ? s_bin[tid] : 0u;
     int gt = 0, eq = 0;
-    for (int j = 0; j < nbk; ++j) {
-      const uint32_t o = s_bin[j];
+    for (int j = 0; j < nbk; ++j) {  // key j from lane j's register, no LDS round trip
+      const uint32_t o = __builtin_amdgcn_readlane(mine, j);
       gt += o > mine;
       eq += o == mine;
     }
