@@ -244,10 +244,12 @@ __device__ uint32_t radix_pass(KeyFn key, int n, uint32_t prefix, uint32_t mask,
 }
 
 // Exact kk-th largest key (T) among n keys that all lie in [lo, hi], and how many keys equal
-// to T are taken (need_eq).  One 12-bit histogram over the bits just below the common prefix of
-// lo and hi (so the bins split the keys' actual range); if the crossing bin holds at most 64
-// keys they are gathered into a small list and ranked by pairwise comparison in one wave,
-// otherwise the full radix select runs.
+// to T are taken (need_eq).  A 12-bit histogram over the bits just below the common prefix of
+// lo and hi (so the bins split the keys' actual range); while the crossing bin holds more than
+// 64 keys (crowded or tied scores) the next 12 bits of that bin are histogrammed, until it is
+// small or every bit is fixed.  A small bin's keys are gathered and ranked by pairwise
+// comparison in one wave.  (Each pass after the first counts only the keys in the crossing bin
+// and fixes 12 more bits; the 4096 bins hold the bin's few bits above them at one value.)
 template <int THREADS, typename KeyFn>
 __device__ void select_kth(KeyFn key, int n, int kk, uint32_t lo, uint32_t hi,
                            uint32_t* hist /*4096*/, uint32_t* s_tmp, int* s_res, uint32_t& T,
@@ -257,16 +259,26 @@ __device__ void select_kth(KeyFn key, int n, int kk, uint32_t lo, uint32_t hi,
   const int tid = threadIdx.x;
   const uint32_t diff = lo ^ hi;
   const int top = diff ? 32 - __clz(diff) : 0;  // bits below the common prefix
-  const int shift = top > 12 ? top - 12 : 0;
-  const uint32_t pmask = top >= 32 ? 0u : ~((1u << top) - 1u);
-  const uint32_t prefix = lo & pmask;
-  const uint32_t c1 = radix_pass<THREADS>(key, n, prefix, pmask, shift, 4096,
-                                          static_cast<uint32_t>(kk), hist, s_tmp, s_res, zeroed);
-  const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
-  const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
+  int shift = top > 12 ? top - 12 : 0;
+  uint32_t pmask = top >= 32 ? 0u : ~((1u << top) - 1u);
+  uint32_t prefix = lo & pmask;
+  uint32_t c1 = radix_pass<THREADS>(key, n, prefix, pmask, shift, 4096,
+                                    static_cast<uint32_t>(kk), hist, s_tmp, s_res, zeroed);
+  uint32_t d1 = static_cast<uint32_t>(s_res[0]);
+  uint32_t r1 = static_cast<uint32_t>(s_res[1]);
   __syncthreads();
-  if (c1 > 64) {
-    radix_select<THREADS>(key, n, kk, hist, s_tmp, s_res, T, need_eq);
+  while (c1 > 64 && shift > 0) {  // (uniform: every thread holds the same values)
+    prefix = (prefix | (d1 << shift)) & ~((1u << shift) - 1u);
+    pmask = ~((1u << shift) - 1u);
+    shift = shift > 12 ? shift - 12 : 0;
+    c1 = radix_pass<THREADS>(key, n, prefix, pmask, shift, 4096, r1, hist, s_tmp, s_res);
+    d1 = static_cast<uint32_t>(s_res[0]);
+    r1 = static_cast<uint32_t>(s_res[1]);
+    __syncthreads();
+  }
+  if (c1 > 64) {  // every bit fixed: the bin is one key value, T, of which r1 are taken
+    T = (prefix & pmask) | d1;
+    need_eq = static_cast<int>(r1);
     return;
   }
   if (tid == 0) s_nb = 0;
