@@ -72,32 +72,6 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total
   return before + inc - v;
 }
 
-template <typename T, bool kDescending, int THREADS>
-__device__ void bitonic_sort(T* a, int n) {  // n power of two
-  for (int k2 = 2; k2 <= n; k2 <<= 1) {
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += THREADS) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const bool up = ((i & k2) == 0) == kDescending;  // this pair wants a[i] >= a[ixj]
-          const T x = a[i], y = a[ixj];
-          if (up ? (x < y) : (x > y)) {
-            a[i] = y;
-            a[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-__device__ __forceinline__ int next_pow2(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
-
 // Index-ordered emission of a row's selection: every key > T, then the first need_eq keys == T
 // in index order; indices come out ascending.  key(e) reads the row's key of entry e.  Each wave
 // owns a contiguous segment of the row: a counting pass (ballots), one exchange of per-wave
