@@ -220,8 +220,9 @@ int check_index_rows(const csa_config_t* c, long long rows, int n_max) {
 size_t ws_compress(const csa_config_t* c, int B, int T) {
   return csa::compress_workspace(B, T, weight_cols(c));
 }
-size_t ws_index(const csa_config_t* c, int rows, int n_max) {
-  return csa::index_topk_workspace(rows, n_max, c->top_k, c->score_format == CSA_SCORE_BF16);
+size_t ws_index(const csa_config_t* c, int B, int nq, int n_max) {
+  return csa::index_topk_workspace(B * nq, nq, n_max, c->idx_dim, c->idx_heads,
+                                   c->score_format == CSA_SCORE_BF16);
 }
 size_t ws_mqa(const csa_config_t* c, int B, int nq, int max_list) {
   const csa::MqaPlan p = csa::plan_mqa(nq, c->n_heads, c->head_dim, max_list, c->entry_format == CSA_ENT_MIXED);
@@ -242,7 +243,7 @@ size_t ws_layer(const csa_config_t* c, int B, int T, int n_max, bool prefill, bo
   size_t idx = is_csa(c) ? align256(static_cast<size_t>(rows) * c->top_k * 4) : 0;
   if (prefill) idx += align256(static_cast<size_t>(rows) * 4);  // query positions (chunked)
   size_t u = ws_attend(c, B, T, n_max);
-  if (is_csa(c)) u = std::max(u, ws_index(c, rows, n_max));
+  if (is_csa(c)) u = std::max(u, ws_index(c, B, T, n_max));
   if (compress) u = std::max(u, ws_compress(c, B, prefill ? T : 1));
   return idx + u;
 }
@@ -514,7 +515,7 @@ int csa_workspace_size(const csa_config_t* cfg, int32_t op, int32_t B, int32_t n
     case CSA_OP_COMPRESS: *bytes = ws_compress(cfg, B, nq); break;
     case CSA_OP_INDEX_TOPK:
       if (!is_csa(cfg)) return fail(CSA_ERR_INVALID_ARG, "index_topk needs CSA mode");
-      *bytes = ws_index(cfg, B * nq, n_max);
+      *bytes = ws_index(cfg, B, nq, n_max);
       break;
     case CSA_OP_SPARSE_MQA: *bytes = ws_mqa(cfg, B, nq, max_list_sparse(cfg)); break;
     case CSA_OP_HCA_MQA: *bytes = ws_mqa(cfg, B, nq, max_list_dense(cfg, n_max)); break;
@@ -563,7 +564,7 @@ int csa_index_topk(const csa_config_t* cfg, int32_t B, int32_t nq, const uint8_t
     return fail(CSA_ERR_INVALID_ARG, "qi/qi_scale/wi/pos/idx_out is NULL");
   if ((rc = check_aligned({qi}))) return rc;
   if ((rc = check_index_rows(cfg, static_cast<long long>(B) * nq, cache->n_max))) return rc;
-  const size_t need = ws_index(cfg, B * nq, cache->n_max);
+  const size_t need = ws_index(cfg, B, nq, cache->n_max);
   if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   return run_index(cfg, B, nq, qi, qi_scale, wi, cache, pos, idx_out, score_out, workspace,
                    reinterpret_cast<hipStream_t>(stream));

@@ -10,7 +10,7 @@
 // dims on each side, applied inside the scaled MFMA).  Scores may be stored as fp32 or, rounded
 // to nearest even, as bf16 ("index scores FP32 -> BF16"); the top-k (topk.hip) then ranks the
 // bf16 values.
-#include "index_common.h"
+#include "topk_common.h"
 
 #ifndef CSA_STREAM_LOAD
 #define CSA_STREAM_LOAD(p) __builtin_nontemporal_load(p)
@@ -31,23 +31,35 @@ namespace csa {
 // QX (with MX): the query is MXFP4 too, the scaled MFMA's FP4 A operand: lane group g takes dims
 // 32g..32g+31 of its head (16 bytes of the packed row) and that block's E8M0 scale byte.
 // ST: the score type written (float, or uint16_t for bf16 scores).
+// COL: the workgroup also selects its chunk's top-k candidates for the multi-workgroup select
+// (the order keys of the scores it stores, kept in LDS; collect_candidates): region and (count,
+// threshold) of chunk `blockIdx.x % nchunks` of the row in cand / ccount, as the selection's
+// collect kernel writes them for its own chunks.  Chunks with no visible entry, and rows of no
+// more than k visible entries, write nothing (the finalize does not read them).
 template <int DI, int HT, int TPW, bool MX = false, bool PAGED = false, bool QX = false,
-          typename ST = float>
+          typename ST = float, bool COL = false>
 __global__ __launch_bounds__(256) void index_score_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ wi, const uint8_t* __restrict__ keys,
     const float* __restrict__ kscale, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int n_max, int H_I, int m, int chunk,
-    ST* __restrict__ scores, int sstride, int nchunks, PageMap pm) {
+    ST* __restrict__ scores, int sstride, int nchunks, PageMap pm, int k,
+    uint32_t* __restrict__ ccount, uint64_t* __restrict__ cand) {
   static_assert(!QX || MX, "an FP4 query is paired with FP4 keys");
   constexpr int KB = DI / 4;   // key bytes per lane (its lane group's K slice)
   constexpr int KK = DI / 32;  // 8-byte MFMA steps per slice
+  constexpr int CH = 4 * TPW * 16;  // entries per workgroup (the launch's chunk)
+  __shared__ uint32_t s_key[COL ? CH : 1];          // COL: order keys of the chunk's scores
+  __shared__ uint32_t s_hist[COL ? kHistBins : 1];  // COL: histogram of the collect passes
+  __shared__ uint32_t s_tmp[4];
+  __shared__ int s_res[2];
 
   // every launch parameter is requested at once (scalar loads complete out of order, so each
   // later batch the compiler would issue on demand costs a full wait on all of them)
   asm volatile("" ::"s"(qi), "s"(qi_scale), "s"(wi), "s"(keys), "s"(kscale), "s"(n_entries),
                "s"(pos), "s"(nq), "s"(n_max), "s"(H_I), "s"(m), "s"(chunk), "s"(scores),
                "s"(sstride), "s"(nchunks), "s"(pm.table), "s"(pm.stride), "s"(pm.shift));
+  if constexpr (COL) asm volatile("" ::"s"(k), "s"(ccount), "s"(cand));
   const int row = blockIdx.x / nchunks;
   const int b = row / nq;
   const int e0 = (blockIdx.x % nchunks) * chunk;
@@ -238,6 +250,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     if (g == 0 && e < e1) {
       const float sc = MX ? part : part * kt.ks;  // MXFP4 scales act inside the MFMA
       Scores<ST>::put(srow, e, sc);
+      if constexpr (COL) s_key[e - e0] = order_key(Scores<ST>::stored(sc));
     }
   };
   // The first tiles are loaded before the row's visible length is known (clamped to the
@@ -263,6 +276,20 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       if (t + PD < TPW) load(t + PD, kb[(t + PD) % NB], e1 - 1);
       compute(t, kb[t % NB], e1);
     }
+  }
+  if constexpr (COL) {
+    // (e0, e1 and n_vis are uniform over the workgroup)
+    if (e0 >= e1 || n_vis <= k) return;
+    constexpr int PER = CH / 256;
+    for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
+    __syncthreads();  // every stored key in s_key, s_hist cleared
+    const int len = e1 - e0;
+    uint32_t key[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) key[i] = tid * PER + i < len ? s_key[tid * PER + i] : 0u;
+    const size_t rc = static_cast<size_t>(row) * nchunks + blockIdx.x % nchunks;
+    collect_candidates<256, PER>(key, s_key, e0, len, n_vis, k, s_hist, s_tmp, s_res,
+                                 cand + rc * kCandPerChunk, ccount + 2 * rc);
   }
 }
 // ============================================================================ scoring, many rows
@@ -495,54 +522,57 @@ __global__ __launch_bounds__(kGemmThreads) void index_gemm_kernel(
 constexpr int kScoreTPW = CSA_SCORE_TPW;       // tiles of 16 entries per wave
 constexpr int kScoreChunk = 4 * kScoreTPW * 16;  // entries per workgroup
 
-template <int DI, int HT, bool MX, bool PAGED, bool QX, typename ST>
+template <int DI, int HT, bool MX, bool PAGED, bool QX, typename ST, bool COL>
 static void launch_scores_k(const IndexArgs& a, int chunk, int nchunks, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(nchunks) * static_cast<unsigned>(a.B * a.nq);
-  index_score_kernel<DI, HT, kScoreTPW, MX, PAGED, QX, ST><<<grid, 256, 0, s>>>(
+  index_score_kernel<DI, HT, kScoreTPW, MX, PAGED, QX, ST, COL><<<grid, 256, 0, s>>>(
       a.qi, a.qi_scale, a.wi, a.keys, a.kscale, a.n_entries, a.pos, a.nq, a.n_max, a.H_I, a.m,
-      chunk, static_cast<ST*>(a.scores), a.sstride, nchunks, a.pages);
+      chunk, static_cast<ST*>(a.scores), a.sstride, nchunks, a.pages, a.k, a.counters, a.cand);
 }
-template <int DI, int HT, bool MX, bool QX, typename ST>
+template <int DI, int HT, bool MX, bool QX, typename ST, bool COL>
 static void launch_scores_p(const IndexArgs& a, int chunk, int nchunks, hipStream_t s) {
   if (a.pages.table != nullptr)
-    launch_scores_k<DI, HT, MX, true, QX, ST>(a, chunk, nchunks, s);
+    launch_scores_k<DI, HT, MX, true, QX, ST, COL>(a, chunk, nchunks, s);
   else
-    launch_scores_k<DI, HT, MX, false, QX, ST>(a, chunk, nchunks, s);
+    launch_scores_k<DI, HT, MX, false, QX, ST, COL>(a, chunk, nchunks, s);
 }
-template <int DI, int HT, typename ST>
+template <int DI, int HT, typename ST, bool COL>
 static void launch_scores_t(const IndexArgs& a, int chunk, int nchunks, hipStream_t s) {
   ProfScope ps("index_score", s);
   if (a.key_fmt == 1) {
     if (a.q_fmt == 1)
-      launch_scores_p<DI, HT, true, true, ST>(a, chunk, nchunks, s);
+      launch_scores_p<DI, HT, true, true, ST, COL>(a, chunk, nchunks, s);
     else
-      launch_scores_p<DI, HT, true, false, ST>(a, chunk, nchunks, s);
+      launch_scores_p<DI, HT, true, false, ST, COL>(a, chunk, nchunks, s);
   } else {
-    launch_scores_p<DI, HT, false, false, ST>(a, chunk, nchunks, s);
+    launch_scores_p<DI, HT, false, false, ST, COL>(a, chunk, nchunks, s);
   }
 }
 
-template <typename ST>
+// COL: the scorer also collects its chunks' candidates (index_fused_collect: d_I = 128 only)
+template <typename ST, bool COL = false>
 static hipError_t launch_scores(const IndexArgs& a, int chunk, hipStream_t s) {
   const int nchunks = (a.n_max + chunk - 1) / chunk;
   const int ht = (a.H_I + 15) / 16;
-#define CSA_SCORE_CASE(DI_, HT_)                            \
-  if (a.d_I == DI_ && ht == HT_) {                         \
-    launch_scores_t<DI_, HT_, ST>(a, chunk, nchunks, s);    \
-    return hipGetLastError();                              \
+#define CSA_SCORE_CASE(DI_, HT_)                                 \
+  if (a.d_I == DI_ && ht == HT_) {                              \
+    launch_scores_t<DI_, HT_, ST, COL>(a, chunk, nchunks, s);    \
+    return hipGetLastError();                                   \
   }
   CSA_SCORE_CASE(128, 4)
   CSA_SCORE_CASE(128, 3)
   CSA_SCORE_CASE(128, 2)
   CSA_SCORE_CASE(128, 1)
-  CSA_SCORE_CASE(64, 4)
-  CSA_SCORE_CASE(64, 3)
-  CSA_SCORE_CASE(64, 2)
-  CSA_SCORE_CASE(64, 1)
-  CSA_SCORE_CASE(32, 4)
-  CSA_SCORE_CASE(32, 3)
-  CSA_SCORE_CASE(32, 2)
-  CSA_SCORE_CASE(32, 1)
+  if constexpr (!COL) {
+    CSA_SCORE_CASE(64, 4)
+    CSA_SCORE_CASE(64, 3)
+    CSA_SCORE_CASE(64, 2)
+    CSA_SCORE_CASE(64, 1)
+    CSA_SCORE_CASE(32, 4)
+    CSA_SCORE_CASE(32, 3)
+    CSA_SCORE_CASE(32, 2)
+    CSA_SCORE_CASE(32, 1)
+  }
 #undef CSA_SCORE_CASE
   return hipErrorInvalidValue;
 }
@@ -597,6 +627,25 @@ static hipError_t launch_index_scores_t(const IndexArgs& a, hipStream_t s) {
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   return a.score_bf16 ? launch_index_scores_t<uint16_t>(a, s) : launch_index_scores_t<float>(a, s);
+}
+
+// Rows over caches of more than kFusedMinN entries that the decode scorer takes (fewer than 16
+// query rows a sequence, or more heads than the product's LDS tile) and d_I = 128: the scorer
+// collects each chunk's candidates itself, in the workgroup that has just scored the chunk, and
+// the selection is the finalize alone (no second read of the scores, one launch fewer).  The
+// collection adds about 3 us to the scorer on MI355X: at 1M entries (4 rows) that is less than
+// the collect launch it replaces (decode step 70.0 -> 66.4 us); at 32768 entries (32 rows) the
+// one-workgroup row select is as fast (60 us either way), and rows that short keep it.
+constexpr int kFusedMinN = 32768;
+bool index_fused_collect(int nq, int d_I, int H_I, int rows, int n_max) {
+  const bool gemm = nq >= kGemmQ && d_I == kGemmDI && H_I <= kGemmH;
+  return !gemm && d_I == 128 && n_max > kFusedMinN && rows <= kMultiMaxRows;
+}
+int index_score_chunk() { return kScoreChunk; }
+
+hipError_t launch_index_scores_collect(const IndexArgs& a, hipStream_t s) {
+  return a.score_bf16 ? launch_scores<uint16_t, true>(a, kScoreChunk, s)
+                      : launch_scores<float, true>(a, kScoreChunk, s);
 }
 
 }  // namespace csa

@@ -38,6 +38,7 @@ template <> struct Scores<float> {
     f[3] = v.w;
   }
   static __device__ __forceinline__ void put(float* r, int e, float v) { r[e] = v; }
+  static __device__ __forceinline__ float stored(float v) { return v; }  // what put keeps
   static __device__ __forceinline__ void put4(float* r, int e, f32x4 v) {
     *reinterpret_cast<f32x4*>(r + e) = v;
   }
@@ -52,6 +53,7 @@ template <> struct Scores<uint16_t> {
     f[3] = __uint_as_float(v.y & 0xffff0000u);
   }
   static __device__ __forceinline__ void put(uint16_t* r, int e, float v) { r[e] = f32_to_bf16(v); }
+  static __device__ __forceinline__ float stored(float v) { return bf16_to_f32(f32_to_bf16(v)); }
   static __device__ __forceinline__ void put4(uint16_t* r, int e, f32x4 v) {
     *reinterpret_cast<uint2*>(r + e) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }

@@ -64,12 +64,23 @@ struct IndexArgs {
   int32_t* idx_out;       // [rows, k]
   float* score_out;       // [rows, k] or nullptr
 };
-// Rows longer than kRowTopkBigN (and not too many) use the multi-workgroup select.
+// Rows longer than kRowTopkBigN (and not too many) use the multi-workgroup select: chunks of a
+// row take candidates of their own (regions of kCandPerChunk pairs), a finalize workgroup per
+// row selects among them.  The chunks are kCollectChunk entries when a selection kernel collects
+// them, or the decode scorer's chunks when it collects its own (index_fused_collect).
 constexpr int kMultiMaxRows = 4096;
+constexpr int kCollectChunk = 4096;
+constexpr int kCandPerChunk = 1024;
 bool index_use_multi(int rows, int n_max);
-size_t index_topk_workspace(int rows, int n_max, int k, bool score_bf16);
-void index_topk_layout(IndexArgs& a, void* ws, int rows);  // needs a.n_max and a.k set
+// decode-scorer rows whose chunks' candidates the scorer collects (index.hip)
+bool index_fused_collect(int nq, int d_I, int H_I, int rows, int n_max);
+int index_score_chunk();  // entries a decode-scorer workgroup scores (and collects)
+size_t index_topk_workspace(int rows, int nq, int n_max, int d_I, int H_I, bool score_bf16);
+void index_topk_layout(IndexArgs& a, void* ws, int rows);  // needs a.n_max, nq, d_I, H_I set
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);  // a.scores only
+// the decode scorer with candidate collection (index_fused_collect rows): a.scores, a.counters
+// and a.cand
+hipError_t launch_index_scores_collect(const IndexArgs& a, hipStream_t s);
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);    // scores, then selection
 
 // ---------------------------------------------------------------- attention

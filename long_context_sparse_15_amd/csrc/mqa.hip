@@ -959,18 +959,18 @@ __global__ __launch_bounds__((MqaWideShape<C>::NT)) void mqa_wide_kernel(MqaPara
   }
 }
 
-// Merge of the spans of one (query row, 64-head group): a thread takes kCombineCPT of the DT*4
-// chunks a lane of one wave held (same head, 4 dims each), merges the spans in a fixed order,
-// adds the sink once, normalises, rotates back and stores bf16.  Loads of up to kCombineMax
-// spans are in flight together.  Two chunks per thread (rather than four) double the workgroups
-// of a small decode batch: 9.4 against 10.6 us for 32 rows x 5 spans at 128K.
-constexpr int kCombineMax = 8;
-constexpr int kCombineCPT = 2;
+// Merge of the spans of one (query row, 64-head group): a thread takes CPT of the DT*4 chunks a
+// lane of one wave held (same head, 4 dims each), merges the spans in a fixed order, adds the
+// sink once, normalises, rotates back and stores bf16.  Loads of up to NS spans are in flight
+// together: NS covers every span of a CSA decode list (one pass, one round trip), and the RoPE
+// frequencies of the thread's dims are requested with them, so the rotation at the end waits
+// for nothing.  Fewer (row, head group) pairs than the device has CUs take one chunk per thread
+// (twice the workgroups); larger batches two.
+constexpr int kCombineMax = 24;
 
-template <int C, class SH>
+template <int C, class SH, int NS, int CPT>
 __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
   constexpr int HP = SH::HP, NW = SH::NW, CS = SH::CS, DT = SH::DT;
-  constexpr int CPT = kCombineCPT;       // chunks per thread
   constexpr int GROUPS = DT * 4 / CPT;   // thread groups per (row, head group)
   const int bid = blockIdx.x;
   const int cgp = bid % GROUPS;
@@ -985,6 +985,18 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
   if (head >= p.n_heads) return;
   const int t_vec = mqa_position_request(p, row);  // needed only for the rotation at the end
   const int dbase = slice * CS;
+  // chunk cc = dt*4 + g4 holds dims dbase + 32dt + 8g4 + 4h .. +3: the frequencies of its two
+  // RoPE pairs (a clamped pair for unrotated dims, unused)
+  int dpos[CPT];
+  float fq[CPT][2];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int cc = cgp * CPT + c;
+    dpos[c] = dbase + (cc >> 2) * 32 + (cc & 3) * 8 + 4 * h;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr)
+      fq[c][pr] = p.inv_freq[max(0, min(dpos[c] + 2 * pr - (C - p.r), p.r - 2)) >> 1];
+  }
   const size_t span_stride = static_cast<size_t>(p.head_groups) * NW * (DT * 4) * 256;
   const uint16_t* pw0 = reinterpret_cast<const uint16_t*>(p.part) +
                         (((static_cast<size_t>(row) * p.n_splits) * p.head_groups + hg) * NW +
@@ -992,8 +1004,8 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
   const float* ml0 = p.ml + (static_cast<size_t>(row) * p.n_splits * p.n_heads + head) * 2;
   const size_t ml_stride = static_cast<size_t>(p.n_heads) * 2;
 
-  // one pass per kCombineMax spans: their (max, sum) and O loads go out together, and the
-  // running reference M moves (rescaling what was merged) only between passes
+  // one pass per NS spans: their (max, sum) and O loads go out together, and the running
+  // reference M moves (rescaling what was merged) only between passes
   // the sink is requested now and taken after the first pass's loads are out
   float sink_raw = *(p.sink ? p.sink + head : p.inv_freq);
   float sink2 = -INFINITY;
@@ -1001,17 +1013,17 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
   f32x4 o[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < p.n_splits; s0 += kCombineMax) {
-    float mv[kCombineMax], lv[kCombineMax];
-    f32x4 ov[kCombineMax][CPT];
+  for (int s0 = 0; s0 < p.n_splits; s0 += NS) {
+    float mv[NS], lv[NS];
+    uint2 ov[NS][CPT];
 #pragma unroll
-    for (int j = 0; j < kCombineMax; ++j) {
+    for (int j = 0; j < NS; ++j) {
       const int sp = min(s0 + j, p.n_splits - 1);
       mv[j] = s0 + j < p.n_splits ? ml0[sp * ml_stride] : -INFINITY;
       lv[j] = ml0[sp * ml_stride + 1];
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
-        ov[j][c] = unpack_b4(*reinterpret_cast<const uint2*>(pw0 + sp * span_stride + c * 256));
+        ov[j][c] = *reinterpret_cast<const uint2*>(pw0 + sp * span_stride + c * 256);
     }
     if (s0 == 0) {
       asm volatile("" : "+v"(sink_raw) : : "memory");
@@ -1020,36 +1032,35 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
     }
     float Mn = sm.M;
 #pragma unroll
-    for (int j = 0; j < kCombineMax; ++j) Mn = fmaxf(Mn, mv[j]);
+    for (int j = 0; j < NS; ++j) Mn = fmaxf(Mn, mv[j]);
     const float a = sm_raise(sm, Mn);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) o[c] *= a;
 #pragma unroll
-    for (int j = 0; j < kCombineMax; ++j) {
+    for (int j = 0; j < NS; ++j) {
       const float wgt = sm_add(sm, mv[j], lv[j]);  // partials are O / l
       if (wgt == 0.f && mv[j] == -INFINITY) continue;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c)
+      for (int c = 0; c < CPT; ++c) {
+        const f32x4 v = unpack_b4(ov[j][c]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[c][e] = sm_fold(o[c][e], ov[j][c][e], wgt);
+        for (int e = 0; e < 4; ++e) o[c][e] = sm_fold(o[c][e], v[e], wgt);
+      }
     }
   }
   const float inv = sm_inv(sm, p.sink != nullptr, sink2);
   const int t = mqa_position_take(p, row, t_vec);
-  // chunk cc = dt*4 + g4 holds dims dbase + 32dt + 8g4 + 4h .. +3; all rotations before stores
   uint2 packed[CPT];
-  int dpos[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int cc = cgp * CPT + c;
-    const int d0 = dbase + (cc >> 2) * 32 + (cc & 3) * 8 + 4 * h;
+    const int d0 = dpos[c];
     float x[4] = {o[c][0] * inv, o[c][1] * inv, o[c][2] * inv, o[c][3] * inv};
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
       const int d = d0 + 2 * pr;
       if (d >= C - p.r) {
         float cs, sn;
-        rope_cos_sin(t, p.inv_freq[(d - (C - p.r)) >> 1], cs, sn);
+        rope_cos_sin(t, fq[c][pr], cs, sn);
         const float x0 = x[2 * pr], x1 = x[2 * pr + 1];
         x[2 * pr] = x0 * cs + x1 * sn;
         x[2 * pr + 1] = -x0 * sn + x1 * cs;
@@ -1057,7 +1068,6 @@ __global__ __launch_bounds__((SH::NT)) void mqa_combine_kernel(MqaParams p) {
     }
     packed[c].x = pack2(x[0], x[1]);
     packed[c].y = pack2(x[2], x[3]);
-    dpos[c] = d0;
   }
   uint16_t* dst = p.out + (static_cast<size_t>(row) * p.n_heads + head) * C;
 #pragma unroll
@@ -1161,8 +1171,18 @@ static hipError_t launch_t(const MqaParams& prm, int rows, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || prm.n_splits == 1) return e;
   ProfScope ps("mqa_combine", s);
-  constexpr int groups = SH::DT * 4 / kCombineCPT;
-  mqa_combine_kernel<C, SH><<<static_cast<unsigned>(rows) * prm.head_groups * groups, SH::NT, 0, s>>>(prm);
+  constexpr int G2 = SH::DT * 4 / 2;  // workgroups per (row, head group) at two chunks a thread
+  const unsigned pairs = static_cast<unsigned>(rows) * prm.head_groups;
+  const bool one_chunk = pairs * G2 < 256;
+  const bool wide = prm.n_splits > 8;
+  const unsigned cgrid = pairs * (one_chunk ? 2 * G2 : G2);
+  if (one_chunk) {
+    if (wide) mqa_combine_kernel<C, SH, kCombineMax, 1><<<cgrid, SH::NT, 0, s>>>(prm);
+    else mqa_combine_kernel<C, SH, 8, 1><<<cgrid, SH::NT, 0, s>>>(prm);
+  } else {
+    if (wide) mqa_combine_kernel<C, SH, kCombineMax, 2><<<cgrid, SH::NT, 0, s>>>(prm);
+    else mqa_combine_kernel<C, SH, 8, 2><<<cgrid, SH::NT, 0, s>>>(prm);
+  }
   return hipGetLastError();
 }
 

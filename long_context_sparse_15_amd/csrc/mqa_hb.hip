@@ -519,7 +519,8 @@ __global__ __launch_bounds__(MqaHbShape::NT) void mqa_hb_kernel(MqaParams p) {
 // (row, head), i.e. the words of lanes n and n + 32 at step c = 4 dt + i of its partial blocks
 // (consecutive threads take consecutive lanes, so a wave's loads are two 256-byte runs), merges
 // the spans in order, adds the sink once, normalises, rotates back and stores bf16.  Loads of up
-// to kHbCombineMax spans are in flight together.
+// to kHbCombineMax spans are in flight together, and the RoPE frequencies of the thread's dims go
+// out with the first loads, so the rotation at the end waits for nothing.
 constexpr int kHbCombineMax = 8;
 
 __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int rows) {
@@ -535,6 +536,11 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
   mqa_preload_params(p);
   if (row >= rows || head >= p.n_heads) return;
   const int t_vec = mqa_position_request(p, row);  // needed only for the rotation at the end
+  const int d0 = c * 8;
+  float fq[4];  // frequencies of the thread's RoPE pairs, requested now (clamped, unused if unrotated)
+#pragma unroll
+  for (int pr2 = 0; pr2 < 4; ++pr2)
+    fq[pr2] = p.inv_freq[max(0, min(d0 + 2 * pr2 - (C - p.r), p.r - 2)) >> 1];
   const uint16_t* pw = reinterpret_cast<const uint16_t*>(p.part) +
                        (static_cast<size_t>(row) * p.n_splits * nblk + blk) * BLK +
                        (c * 64 + n) * 4;
@@ -586,13 +592,12 @@ __global__ __launch_bounds__(256) void mqa_combine_hb_kernel(MqaParams p, int ro
   float x[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = o[e] * inv;
-  const int d0 = c * 8;
 #pragma unroll
   for (int pr2 = 0; pr2 < 4; ++pr2) {
     const int d = d0 + 2 * pr2;
     if (d >= C - p.r) {
       float cs, sn;
-      rope_cos_sin(t, p.inv_freq[(d - (C - p.r)) >> 1], cs, sn);
+      rope_cos_sin(t, fq[pr2], cs, sn);
       rot_back(x[2 * pr2], x[2 * pr2 + 1], cs, sn);
     }
   }

@@ -11,66 +11,9 @@
 // chunks, one workgroup each, that take thresholds of their own and write their candidates; a
 // finalize workgroup per row selects among them and emits the selection in ascending index
 // order.
-#include "index_common.h"
+#include "topk_common.h"
 
 namespace csa {
-
-// ============================================================================ block helpers
-// Block-wide search over a histogram of `nbins` counts for the bin d with
-//   sum(bins > d) < remaining <= sum(bins >= d).
-// Writes d to s_res[0] and remaining - sum(bins > d) to s_res[1].  All THREADS threads call it.
-template <int THREADS>
-__device__ void block_find_crossing(const uint32_t* bins, int nbins, uint32_t remaining,
-                                    uint32_t* s_tmp, int* s_res) {
-  constexpr int NWAVE = THREADS / 64;
-  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
-  const int per = nbins / THREADS;  // nbins is a multiple of THREADS
-  uint32_t own = 0;
-  for (int j = 0; j < per; ++j) own += bins[tid * per + j];
-  // inclusive suffix sum inside the wave (lane l: sum over lanes >= l) from the prefix sum
-  const uint32_t inc = wave_incl_scan(own);
-  const uint32_t wtot = __builtin_amdgcn_readlane(inc, 63);
-  const uint32_t suf = wtot - inc + own;
-  if (l == 0) s_tmp[wave] = wtot;
-  __syncthreads();
-  uint32_t later = 0;  // (a loop of constant length: its reads go out together)
-#pragma unroll
-  for (int w2 = 1; w2 < NWAVE; ++w2)
-    if (w2 > wave) later += s_tmp[w2];
-  const uint32_t above = suf - own + later;
-  if (above < remaining && remaining <= above + own) {
-    uint32_t cum = above;
-    for (int j = per - 1; j >= 0; --j) {
-      const uint32_t c = bins[tid * per + j];
-      if (cum + c >= remaining) {
-        s_res[0] = tid * per + j;
-        s_res[1] = static_cast<int>(remaining - cum);
-        break;
-      }
-      cum += c;
-    }
-  }
-  __syncthreads();
-}
-
-// Exclusive block scan of one uint32 per thread; returns the thread's prefix, *total the sum.
-template <int THREADS>
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
-  constexpr int NWAVE = THREADS / 64;
-  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
-  const uint32_t inc = wave_incl_scan(v);
-  if (l == 63) s_tmp[wave] = inc;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-  for (int w2 = 0; w2 < NWAVE; ++w2) {
-    const uint32_t x = s_tmp[w2];
-    if (w2 < wave) before += x;
-    tot += x;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + inc - v;
-}
 
 // Index-ordered emission of a row's selection: every key > T, then the first need_eq keys == T
 // in index order; indices come out ascending.  key(e) reads the row's key of entry e.  Each wave
@@ -194,27 +137,6 @@ __device__ void radix_select(KeyFn key, int n, int kk, uint32_t* hist /*4096*/, 
   }
   T = prefix;
   need_eq = static_cast<int>(remaining);
-}
-
-// One histogram pass of radix select: counts keys matching (prefix, mask) into nb bins of the
-// bits at `shift`, then finds the crossing bin of `remaining` (s_res[0], s_res[1]); returns the
-// crossing bin's count.
-template <int THREADS, typename KeyFn>
-__device__ uint32_t radix_pass(KeyFn key, int n, uint32_t prefix, uint32_t mask, int shift,
-                               int nb, uint32_t remaining, uint32_t* hist, uint32_t* s_tmp,
-                               int* s_res, bool zeroed = false) {
-  const int tid = threadIdx.x;
-  if (!zeroed) {  // a caller that cleared hist before its last barrier skips this
-    for (int i = tid; i < nb; i += THREADS) hist[i] = 0;
-    __syncthreads();
-  }
-  for (int e = tid; e < n; e += THREADS) {
-    const uint32_t kv = key(e);
-    if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & (nb - 1)], 1u);
-  }
-  __syncthreads();
-  block_find_crossing<THREADS>(hist, nb, remaining, s_tmp, s_res);
-  return hist[s_res[0]];
 }
 
 // Exact kk-th largest key (T) among n keys that all lie in [lo, hi], and how many keys equal
@@ -541,8 +463,10 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
 
 // ============================================================================ multi-WG top-k
 // For rows longer than one workgroup's register file (decode at long context).  A row is cut
-// into chunks of kCollectChunk entries, one 1024-thread workgroup each.  A workgroup selects its
-// chunk's candidates with a threshold of its own: T_c, the lower edge of the 12-bit bin (refined
+// into chunks, each of which selects its candidates itself: the decode scorer's workgroups do so
+// for the entries they have just scored (index.hip), otherwise one 1024-thread workgroup per
+// kCollectChunk entries reads them back (topk_collect_kernel).  A chunk selects its
+// candidates with a threshold of its own: T_c, the lower edge of the 12-bit bin (refined
 // by 12 more bits when crowded) holding its r-th largest key, r = the chunk's expected share of
 // the row's top kk plus four standard deviations.  It writes the (key, index) pairs >= T_c in
 // ascending index order into its own region (block prefix sum, no global atomics) with the
@@ -555,8 +479,6 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
 // of the top keys) the chunks with T_c > T are read again for every key >= T and the list is
 // rebuilt around them (see the finalize); on a region overflow, too few candidates or too many
 // such chunks the exact streaming select of the row runs instead.
-constexpr int kCollectChunk = 4096;
-constexpr int kCandPerChunk = 1024;
 constexpr int kSCandCap = 8192;  // candidates of a row held by its finalize workgroup
 constexpr int kRepairChunks = 16;  // chunks a finalize re-reads when their thresholds cut T
 constexpr size_t kMultiLds = static_cast<size_t>(kSCandCap) * 8 + kHistBins * 4;
@@ -603,42 +525,8 @@ __global__ __launch_bounds__(1024) void topk_collect_kernel(
 #pragma unroll
   for (int j = 0; j < PER; ++j) s_key[tid * PER + j] = key[j];
   __syncthreads();
-  const float expect = static_cast<float>(kk) * static_cast<float>(len) / static_cast<float>(n_vis);
-  const int r = static_cast<int>(ceilf(expect + 4.f * sqrtf(expect) + 4.f));
-  uint32_t Tc = 0u;  // keep the whole chunk when it holds no more than r keys
-  if (r < len) {
-    auto kf = [&](int e) { return s_key[e]; };
-    const uint32_t cb = radix_pass<THREADS>(kf, len, 0u, 0u, 20, 4096, static_cast<uint32_t>(r),
-                                            hist, s_tmp, s_res, /*zeroed=*/true);
-    const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
-    const uint32_t r1 = static_cast<uint32_t>(s_res[1]);
-    __syncthreads();
-    Tc = d1 << 20;
-    if (cb > 64) {  // crowded bin: refine by the next 12 bits
-      radix_pass<THREADS>(kf, len, d1 << 20, 0xfff00000u, 8, 4096, r1, hist, s_tmp, s_res);
-      Tc |= static_cast<uint32_t>(s_res[0]) << 8;
-      __syncthreads();
-    }
-  }
-  uint32_t own = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) own += (e0 + tid * PER + i < n_vis && key[i] >= Tc) ? 1u : 0u;
-  uint32_t total;
-  uint32_t off = block_excl_scan<THREADS>(own, s_tmp, &total);
-  uint64_t* cdst = cand + rc * kCandPerChunk;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = e0 + tid * PER + i;
-    if (e < n_vis && key[i] >= Tc) {
-      if (off < static_cast<uint32_t>(kCandPerChunk))
-        cdst[off] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(e);
-      ++off;
-    }
-  }
-  if (tid == 0) {
-    ccount[2 * rc] = total;
-    ccount[2 * rc + 1] = Tc;
-  }
+  collect_candidates<THREADS, PER>(key, s_key, e0, len, n_vis, kk, hist, s_tmp, s_res,
+                                   cand + rc * kCandPerChunk, ccount + 2 * rc);
 }
 
 template <typename ST>
@@ -646,7 +534,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
     const ST* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int nchunks,
     const uint32_t* __restrict__ ccount, const uint64_t* __restrict__ cand,
-    int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out, int cchunk) {
   constexpr int THREADS = 1024;
   extern __shared__ __align__(16) unsigned char smem[];
   uint32_t* ckey = reinterpret_cast<uint32_t*>(smem);              // kSCandCap
@@ -661,7 +549,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   __shared__ uint32_t s_rcount[kRepairChunks];  // their counts of such keys
   asm volatile("" ::"s"(scores), "s"(sstride), "s"(n_entries), "s"(pos), "s"(nq), "s"(m), "s"(k),
                "s"(n_max), "s"(nchunks), "s"(ccount), "s"(cand), "s"(idx_out),
-               "s"(score_out));  // all parameters at once
+               "s"(score_out), "s"(cchunk));  // all parameters at once
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   // this thread's chunk (count, threshold) goes out first, before the row's position and entry
@@ -685,7 +573,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
     }
     return;
   }
-  const int used = (n_vis + kCollectChunk - 1) / kCollectChunk;  // <= nchunks
+  const int used = (n_vis + cchunk - 1) / cchunk;  // <= nchunks
   if (tid == 0) {
     s_flag = used > THREADS ? 1 : 0;  // 1 = take the exact fallback
     s_lo = 0xffffffffu;
@@ -717,18 +605,22 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
   }
   const int nc = static_cast<int>(s_off[used]);
   uint32_t lo = 0xffffffffu, hi = 0u;
-  // 16 threads per region, each region's pairs to its place in the concatenated list; a
-  // thread's first eight pairs are requested together (one round trip for regions up to 128)
+  // tpr threads per region (16; 8 for chunks of up to 2048 entries, whose regions hold about
+  // half as many pairs and are twice as many), each region's pairs to its place in the
+  // concatenated list; a thread's first eight pairs are requested together (one round trip for
+  // regions up to 8 tpr pairs)
+  const int tpr = cchunk <= 2048 ? 8 : 16;
+  const int tsh = cchunk <= 2048 ? 3 : 4;
   auto copy_region = [&](int c) {
     const uint32_t o = s_off[c], n = s_off[c + 1] - o;
     const uint64_t* src = cand + (static_cast<size_t>(row) * nchunks + c) * kCandPerChunk;
-    const uint32_t j0 = tid & 15, last = n > 0 ? n - 1 : 0;
+    const uint32_t j0 = tid & (tpr - 1), last = n > 0 ? n - 1 : 0;
     uint64_t v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[min(j0 + 16u * u, last)];
+    for (int u = 0; u < 8; ++u) v[u] = src[min(j0 + tpr * u, last)];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const uint32_t j = j0 + 16u * u;
+      const uint32_t j = j0 + tpr * u;
       if (j < n) {
         const uint32_t kv = static_cast<uint32_t>(v[u] >> 32);
         ckey[o + j] = kv;
@@ -737,7 +629,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
         hi = max(hi, kv);
       }
     }
-    for (uint32_t j = j0 + 128; j < n; j += 16) {
+    for (uint32_t j = j0 + 8 * tpr; j < n; j += tpr) {
       const uint64_t w = src[j];
       const uint32_t kv = static_cast<uint32_t>(w >> 32);
       ckey[o + j] = kv;
@@ -746,7 +638,7 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
       hi = max(hi, kv);
     }
   };
-  for (int c = tid >> 4; c < used; c += THREADS / 16) copy_region(c);
+  for (int c = tid >> tsh; c < used; c += THREADS >> tsh) copy_region(c);
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
   if (lane_id() == 0) {
@@ -773,15 +665,18 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
     if (aff && ai < static_cast<uint32_t>(kRepairChunks)) s_rchunk[ai] = tid;
     __syncthreads();
     bool ok = n_aff <= static_cast<uint32_t>(kRepairChunks);
+    // a re-read chunk of cchunk <= 4096 entries takes the first cchunk / 4 threads
+    const bool in_chunk = tid * 4 < cchunk;
     if (ok) {
       // keys >= Tr of each re-read chunk, counted (4 keys a thread, one 16-byte load)
       for (uint32_t a = 0; a < n_aff; ++a) {
-        const int e = s_rchunk[a] * kCollectChunk + tid * 4;
+        const int e = s_rchunk[a] * cchunk + tid * 4;
         float f[4];
         Scores<ST>::four(srow, min(e, sstride - 4), f);
         uint32_t c = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) c += (e + j < n_vis && order_key(f[j]) >= Tr) ? 1u : 0u;
+        for (int j = 0; j < 4; ++j)
+          c += (in_chunk && e + j < n_vis && order_key(f[j]) >= Tr) ? 1u : 0u;
         uint32_t tot;
         block_excl_scan<THREADS>(c, s_tmp, &tot);
         if (tid == 0) s_rcount[a] = tot;
@@ -809,19 +704,19 @@ __global__ __launch_bounds__(1024) void topk_finalize_kernel(
     // regions of the chunks that keep them, 16 threads each
     lo = 0xffffffffu;
     hi = 0u;
-    for (int c = tid >> 4; c < used; c += THREADS / 16)
+    for (int c = tid >> tsh; c < used; c += THREADS >> tsh)
       if (ccount[2 * (static_cast<size_t>(row) * nchunks + c) + 1] <= Tr) copy_region(c);
     uint32_t lo2 = lo, hi2 = hi;
     // the re-read chunks' keys >= Tr, in index order
     for (uint32_t a = 0; a < n_aff; ++a) {
       const int c = s_rchunk[a];
-      const int e = c * kCollectChunk + tid * 4;
+      const int e = c * cchunk + tid * 4;
       float f[4];
       Scores<ST>::four(srow, min(e, sstride - 4), f);
       uint32_t kv[4], cnt = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        kv[j] = e + j < n_vis ? order_key(f[j]) : 0u;
+        kv[j] = (in_chunk && e + j < n_vis) ? order_key(f[j]) : 0u;
         cnt += kv[j] >= Tr && kv[j] != 0u ? 1u : 0u;
       }
       uint32_t tot;
@@ -866,17 +761,21 @@ bool index_use_multi(int rows, int n_max) {
   return n_max > kRowTopkBigN && rows <= kMultiMaxRows;
 }
 
-static int collect_chunks(int n_max) { return (n_max + kCollectChunk - 1) / kCollectChunk; }
+// Chunks a row is cut into for the multi-workgroup select: the decode scorer's own chunks when
+// it collects the candidates, kCollectChunk otherwise; 0 when the row selection runs instead.
+static int chunk_entries(int rows, int nq, int n_max, int d_I, int H_I) {
+  if (index_fused_collect(nq, d_I, H_I, rows, n_max)) return index_score_chunk();
+  return index_use_multi(rows, n_max) ? kCollectChunk : 0;
+}
 
-size_t index_topk_workspace(int rows, int n_max, int k, bool score_bf16) {
+size_t index_topk_workspace(int rows, int nq, int n_max, int d_I, int H_I, bool score_bf16) {
   const size_t sb = score_bf16 ? 2 : 4;
   size_t b = align256(static_cast<size_t>(rows) * score_stride(n_max) * sb);
-  if (index_use_multi(rows, n_max)) {
-    const size_t rc = static_cast<size_t>(rows) * collect_chunks(n_max);
+  if (const int ch = chunk_entries(rows, nq, n_max, d_I, H_I)) {
+    const size_t rc = static_cast<size_t>(rows) * ((n_max + ch - 1) / ch);
     b += align256(rc * 8);  // (count, threshold) per chunk
     b += align256(rc * kCandPerChunk * 8);
   }
-  (void)k;
   return b;
 }
 
@@ -887,8 +786,8 @@ void index_topk_layout(IndexArgs& a, void* ws, int rows) {
   p += align256(static_cast<size_t>(rows) * a.sstride * (a.score_bf16 ? 2 : 4));
   a.counters = nullptr;
   a.cand = nullptr;
-  if (index_use_multi(rows, a.n_max)) {
-    const size_t rc = static_cast<size_t>(rows) * collect_chunks(a.n_max);
+  if (const int ch = chunk_entries(rows, a.nq, a.n_max, a.d_I, a.H_I)) {
+    const size_t rc = static_cast<size_t>(rows) * ((a.n_max + ch - 1) / ch);
     a.counters = reinterpret_cast<uint32_t*>(p);
     p += align256(rc * 8);
     a.cand = reinterpret_cast<uint64_t*>(p);
@@ -911,8 +810,9 @@ static hipError_t launch_row_topk(const IndexArgs& a, int rows, hipStream_t s) {
 template <typename ST>
 static hipError_t launch_index_topk_t(const IndexArgs& a, hipStream_t s) {
   const int rows = a.B * a.nq;
-  const bool multi = index_use_multi(rows, a.n_max);
-  hipError_t e = launch_index_scores(a, s);
+  const bool fused = index_fused_collect(a.nq, a.d_I, a.H_I, rows, a.n_max);
+  const bool multi = fused || index_use_multi(rows, a.n_max);
+  hipError_t e = fused ? launch_index_scores_collect(a, s) : launch_index_scores(a, s);
   if (e != hipSuccess) return e;
   const ST* sc = static_cast<const ST*>(a.scores);
   if (!multi) {
@@ -932,21 +832,22 @@ static hipError_t launch_index_topk_t(const IndexArgs& a, hipStream_t s) {
                                                           a.score_out);
     return hipGetLastError();
   }
-  const int ncc = collect_chunks(a.n_max);
-  {
+  const int cch = fused ? index_score_chunk() : kCollectChunk;
+  const int ncc = (a.n_max + cch - 1) / cch;
+  if (!fused) {
     ProfScope ps("topk_collect", s);
     topk_collect_kernel<ST><<<static_cast<unsigned>(ncc) * rows, 1024, 0, s>>>(
         sc, a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, ncc, a.counters, a.cand);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if ((e = ensure_max_lds(reinterpret_cast<const void*>(topk_finalize_kernel<ST>), kMultiLds)))
     return e;
   ProfScope ps("topk_finalize", s);
   topk_finalize_kernel<ST><<<rows, 1024, kMultiLds, s>>>(sc, a.sstride, a.n_entries, a.pos,
                                                          a.nq, a.m, a.k, a.n_max, ncc,
                                                          a.counters, a.cand, a.idx_out,
-                                                         a.score_out);
+                                                         a.score_out, cch);
   return hipGetLastError();
 }
 

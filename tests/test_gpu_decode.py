@@ -92,7 +92,7 @@ def _w(name, **kw):
     ("tiny_csa", 1, 64, [300]),
     # one 1024-thread workgroup per row with every key in LDS (16K < n_vis <= 32K)
     ("csa_decode_128k", 2, 20000, [4 * 20000, 4 * 17000 + 3]),
-    # multi-workgroup select (n_vis > 32K): threshold bin, per-chunk regions, finalize
+    # multi-workgroup select (n_vis > 32K): the scorer's per-chunk thresholds and regions, finalize
     ("csa_decode_1m", 2, 40000, [4 * 40000 + 1, 4 * 33000]),
 ])
 def test_csa_decode_parity(case):
@@ -136,9 +136,10 @@ def test_csa_decode_massive_ties_multi_workgroup_fallback():
 
 
 def test_csa_decode_clustered_top_keys_multi_workgroup_fallback():
-    """The top keys of a long row all sit in its first 4096-entry chunk: that chunk's own
-    threshold cuts keys above the k-th key; the finalize sees it and reads the chunk again for
-    every key at or above the list's k-th key."""
+    """The top keys of a long row all sit in its first 4096 entries (two of the decode scorer's
+    2048-entry chunks, whose candidates it collects itself): those chunks' own thresholds cut
+    keys above the k-th key; the finalize sees it and reads the chunks again for every key at or
+    above the list's k-th key."""
     say("csa decode clustered top keys, multi-workgroup select")
     w = _w("csa_decode_1m")
     x = S.decode_cache_inputs(w, B=1, N=40000)
@@ -150,10 +151,10 @@ def test_csa_decode_clustered_top_keys_multi_workgroup_fallback():
 
 @pytest.mark.parametrize("chunks", [(1, 4, 9), (9,)])
 def test_csa_decode_top_keys_in_several_chunks(chunks):
-    """The top keys of two long rows sit in a few 4096-entry chunks (the last one partial, as
-    the newest entries of a prompt would): each such chunk's threshold cuts keys above the k-th
-    key, and the finalize re-reads exactly those chunks; the second row's top keys are spread
-    evenly (no chunk re-read)."""
+    """The top keys of two long rows sit in a few 4096-entry spans (each two of the decode
+    scorer's 2048-entry chunks; the last one partial, as the newest entries of a prompt would):
+    each such chunk's threshold cuts keys above the k-th key, and the finalize re-reads exactly
+    those chunks; the second row's top keys are spread evenly (no chunk re-read)."""
     say("csa decode top keys in chunks", chunks)
     w = _w("csa_decode_1m")
     x = S.decode_cache_inputs(w, B=2, N=40000)
