@@ -268,7 +268,11 @@ __global__ __launch_bounds__(THREADS) void topk_row_kernel(
 //  4. the index-ordered emission over the candidate list writes the keys above T and the first
 //     ties, so the selection comes out sorted with the lowest indices winning ties.
 // If the count misses [kk, kCandCap] (ties, adversarial data) the exact streaming select runs.
-template <int THREADS, int PER, typename ST>
+// CLAMP (runs of query rows, whose causal lengths vary): the row's visible length is read first
+// and chunk loads past it re-read the row's last visible chunk (a cache hit), so a row moves
+// only its visible scores from HBM; otherwise (decode: full rows, few of them) every chunk load
+// goes out before the length is known, one memory round trip sooner.
+template <int THREADS, int PER, typename ST, bool CLAMP = false>
 __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
     const ST* __restrict__ scores, int sstride, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ pos, int nq, int m, int k, int n_max, int32_t* __restrict__ idx_out,
@@ -297,10 +301,20 @@ __global__ __launch_bounds__(THREADS) void topk_sample_kernel(
   // before any is used (pinned: otherwise the compiler splits them and sinks the pieces into
   // per-element branches, each behind a wait).
   float f[CH][4];
+  int n_vis;
+  if constexpr (CLAMP) {
+    n_vis = visible(n_entries, pos, row, nq, m, n_max);
+    const int last = max(n_vis - 1, 0) & ~3;  // start of the chunk holding the last visible key
 #pragma unroll
-  for (int i = 0; i < CH; ++i) Scores<ST>::four(srow, min((i * THREADS + tid) * 4, sstride - 4), f[i]);
-  asm volatile("" ::: "memory");
-  const int n_vis = visible(n_entries, pos, row, nq, m, n_max);
+    for (int i = 0; i < CH; ++i) Scores<ST>::four(srow, min((i * THREADS + tid) * 4, last), f[i]);
+    asm volatile("" ::: "memory");
+  } else {
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      Scores<ST>::four(srow, min((i * THREADS + tid) * 4, sstride - 4), f[i]);
+    asm volatile("" ::: "memory");
+    n_vis = visible(n_entries, pos, row, nq, m, n_max);
+  }
   const int kk = min(k, n_vis);
   int32_t* out = idx_out + static_cast<size_t>(row) * k;
   float* sout = score_out ? score_out + static_cast<size_t>(row) * k : nullptr;
@@ -817,19 +831,27 @@ static hipError_t launch_index_topk_t(const IndexArgs& a, hipStream_t s) {
   const ST* sc = static_cast<const ST*>(a.scores);
   if (!multi) {
     if (a.n_max <= 4096) return launch_row_topk<256, kRowTopkMaxN, ST>(a, rows, s);
+    // runs of query rows (causal lengths) read only their visible scores
+    const bool clamp = a.nq >= 16;
     if (a.n_max <= 16384) {
       ProfScope ps("topk_sample", s);
       // 512 threads x 32 keys (measured 1.83 ms against 2.89 ms for 256 x 64 and 3.68 ms for
       // 1024 x 32 on the 64K-token prefill rows)
-      topk_sample_kernel<512, 32, ST><<<rows, 512, 0, s>>>(sc, a.sstride, a.n_entries, a.pos,
-                                                          a.nq, a.m, a.k, a.n_max, a.idx_out,
-                                                          a.score_out);
+      if (clamp)
+        topk_sample_kernel<512, 32, ST, true><<<rows, 512, 0, s>>>(
+            sc, a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, a.idx_out, a.score_out);
+      else
+        topk_sample_kernel<512, 32, ST><<<rows, 512, 0, s>>>(
+            sc, a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, a.idx_out, a.score_out);
       return hipGetLastError();
     }
     ProfScope ps("topk_sample", s);
-    topk_sample_kernel<1024, 32, ST><<<rows, 1024, 0, s>>>(sc, a.sstride, a.n_entries, a.pos,
-                                                          a.nq, a.m, a.k, a.n_max, a.idx_out,
-                                                          a.score_out);
+    if (clamp)
+      topk_sample_kernel<1024, 32, ST, true><<<rows, 1024, 0, s>>>(
+          sc, a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, a.idx_out, a.score_out);
+    else
+      topk_sample_kernel<1024, 32, ST><<<rows, 1024, 0, s>>>(
+          sc, a.sstride, a.n_entries, a.pos, a.nq, a.m, a.k, a.n_max, a.idx_out, a.score_out);
     return hipGetLastError();
   }
   const int cch = fused ? index_score_chunk() : kCollectChunk;
