@@ -201,6 +201,7 @@ def test_paged_layer_matches_contiguous(name, key_fmt, T):
 @pytest.mark.parametrize("name,key_fmt,B,ent", [("csa_decode_128k", "e4m3", 4, "bf16"),
                                                 ("csa_decode_128k", "mxfp4", 4, "bf16"),
                                                 ("csa_decode_1m", "e4m3", 1, "bf16"),
+                                                ("csa_decode_1m", "mxfp4", 1, "bf16"),
                                                 ("hca_decode_1m", None, 4, "bf16"),
                                                 ("csa_decode_128k", "e4m3", 4, "mixed"),
                                                 ("hca_decode_1m", None, 4, "mixed")])
