@@ -94,6 +94,9 @@ def _w(name, **kw):
     ("csa_decode_128k", 2, 20000, [4 * 20000, 4 * 17000 + 3]),
     # multi-workgroup select (n_vis > 32K): the scorer's per-chunk thresholds and regions, finalize
     ("csa_decode_1m", 2, 40000, [4 * 40000 + 1, 4 * 33000]),
+    # the same cache with rows of n_vis <= k (no regions written: everything selected), k + 1
+    # and one visible entry past a chunk boundary
+    ("csa_decode_1m", 4, 40000, [4 * 1500 + 3, 4 * 2049, 4 * 2048 * 3 + 4, 4 * 40000]),
 ])
 def test_csa_decode_parity(case):
     name, B, N, positions = case
