@@ -119,6 +119,16 @@ def test_bf16_scores_exact_ties_lower_index_wins(key_fmt, qi_fmt):
     _decode_case(w, 2, 900, [4 * 900, 4 * 500], key_fmt, qi_fmt, "bf16", ties=True)
 
 
+@pytest.mark.parametrize("key_fmt,qi_fmt", [("e4m3", "e4m3"), ("mxfp4", "mxfp4")])
+def test_bf16_scores_exact_ties_multi_workgroup(key_fmt, qi_fmt):
+    """bf16 scores over 40000 entries (the scorer's per-chunk candidates and the finalize), every
+    key from entry 100 on identical: each chunk's candidates overflow its region and the exact
+    select decides; the lowest indices win the ties."""
+    say("bf16 scores, exact ties, multi-workgroup select", key_fmt, qi_fmt)
+    w = S.shrink(S.WORKLOADS["csa_decode_1m"])
+    _decode_case(w, 2, 40000, [4 * 40000, 4 * 35000 + 2], key_fmt, qi_fmt, "bf16", ties=True)
+
+
 def _full(name, score_fmt, sample):
     w = S.WORKLOADS[name]
     say("full-size fp4 x fp4 decode", name, score_fmt)
