@@ -47,12 +47,14 @@ def _check_row(idx_row, sc_row, ref, k, bf16, what):
     return sel
 
 
-def _decode_case(w, B, N, positions, key_fmt, qi_fmt, score_fmt, ties=False):
+def _decode_case(w, B, N, positions, key_fmt, qi_fmt, score_fmt, ties=False, prep=None):
     x = S.decode_cache_inputs(w, B=B, N=N, key_fmt=key_fmt, qi_fmt=qi_fmt)
     x["pos"] = np.array(positions, dtype=np.int32)
     if ties:  # a block of identical keys: exactly equal scores on both sides
         x["ikeys"][:, 100:] = x["ikeys"][:, 100:101]
         x["iscale"][:, 100:] = x["iscale"][:, 100:101]
+    if prep:
+        prep(x)
     d = {k: dev(x[k]) for k in ("entries", "window", "pos", "n_entries", "q", "sink", "inv_freq",
                                 "ikeys", "iscale", "qi", "qi_scale", "wi")}
     bf16 = score_fmt == "bf16"
@@ -127,6 +129,19 @@ def test_bf16_scores_exact_ties_multi_workgroup(key_fmt, qi_fmt):
     say("bf16 scores, exact ties, multi-workgroup select", key_fmt, qi_fmt)
     w = S.shrink(S.WORKLOADS["csa_decode_1m"])
     _decode_case(w, 2, 40000, [4 * 40000, 4 * 35000 + 2], key_fmt, qi_fmt, "bf16", ties=True)
+
+
+def test_bf16_scores_clustered_top_keys_multi_workgroup():
+    """bf16 scores over 40000 entries whose top keys all sit in entries 8192..12287 (two of the
+    scorer's chunks): those chunks' own thresholds cut keys above the k-th key and the finalize
+    re-reads them through the bf16 score rows (the keys it compares are those the scorer ranked)."""
+    say("bf16 scores, clustered top keys, multi-workgroup select")
+    w = S.shrink(S.WORKLOADS["csa_decode_1m"])
+
+    def prep(x):
+        x["iscale"][:, 8192:12288] *= 16.0
+
+    _decode_case(w, 2, 40000, [4 * 40000, 4 * 39000 + 2], "e4m3", "e4m3", "bf16", prep=prep)
 
 
 def _full(name, score_fmt, sample):
